@@ -1,0 +1,240 @@
+"""Activation-sparse transformer FFN (TwELL) on AMD MI355X (gfx950).
+
+Thin Python binding over the C ABI of ``libtwell.so`` (declared in include/twell.h): the
+functions below only check tensors, allocate outputs with torch and pass raw device
+pointers plus the current HIP stream. Every step of the computation runs in the HIP
+kernels of the library; there is no fallback path. If the library is missing, every call
+raises.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
+    "twell_down", "ffn_up_relu_dense", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
+    "nm_prune", "nm_ffn_down", "twell_sync_status", "F32", "BF16",
+]
+
+F32, BF16 = 0, 1
+STATUS = {0: "TWELL_OK", -1: "TWELL_ERR_ARG", -2: "TWELL_ERR_SHAPE", -3: "TWELL_ERR_ALIGN",
+          -4: "TWELL_ERR_WORKSPACE", -5: "TWELL_ERR_OVF_CAPACITY", -6: "TWELL_ERR_HIP",
+          -7: "TWELL_ERR_UNSUPPORTED"}
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtwell.so")
+
+_c = ctypes
+_P, _I, _F, _Z = _c.c_void_p, _c.c_int32, _c.c_float, _c.c_size_t
+
+
+class TwellError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {STATUS.get(status, status)}")
+
+
+class TwellMatrixC(_c.Structure):
+    _fields_ = [("rows", _I), ("cols", _I), ("tile_w", _I), ("slots", _I), ("ovf_cap", _I),
+                ("val_dtype", _I), ("counts", _P), ("col_idx", _P), ("vals", _P), ("ovf_n", _P),
+                ("ovf_rows", _P), ("ovf_slot", _P), ("ovf_dense", _P), ("ovf_bits", _P)]
+
+
+_SIGS = {
+    "twell_abi_version": ([], _I),
+    "twell_status_str": ([_I], _c.c_char_p),
+    "twell_ovf_bits_words": ([_I, _I, _I], _Z),
+    "twell_pack": ([_P, _I, _P, _P], _I),
+    "twell_ffn_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
+    "twell_down": ([_P, _P, _I, _I, _P, _I, _P], _I),
+    "ffn_up_relu_dense": ([_P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
+    "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _P], _Z),
+    "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "nm_prune": ([_P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "nm_ffn_down": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P], _I),
+    "twell_sync_status": ([_P, _P], _I),
+}
+
+_LIB = None
+
+
+def lib():
+    """Load libtwell.so (built in-tree by activation_sparse_transformer_up_amd.build)."""
+    global _LIB
+    if _LIB is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                               "`python -m activation_sparse_transformer_up_amd.build`")
+        L = _c.CDLL(LIB_PATH)
+        for name, (args, res) in _SIGS.items():
+            fn = getattr(L, name)
+            fn.argtypes = args
+            fn.restype = res
+        _LIB = L
+    return _LIB
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise TwellError(status, where)
+
+
+def _dt(t: torch.dtype) -> int:
+    if t == torch.float32:
+        return F32
+    if t == torch.bfloat16:
+        return BF16
+    raise TypeError(f"unsupported dtype {t}")
+
+
+def _tdt(code: int) -> torch.dtype:
+    return torch.float32 if code == F32 else torch.bfloat16
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _stream(device=None):
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def twell_abi_version() -> int:
+    return lib().twell_abi_version()
+
+
+class TwellMatrix:
+    """Device buffers of a TwELL matrix (see twell_matrix_t in include/twell.h)."""
+
+    def __init__(self, rows: int, cols: int, tile_w: int, slots: int, ovf_cap: int,
+                 val_dtype: torch.dtype = torch.float32, device="cuda"):
+        self.rows, self.cols, self.tile_w, self.slots, self.ovf_cap = rows, cols, tile_w, slots, ovf_cap
+        self.val_dtype = val_dtype
+        nt = cols // tile_w
+        i32 = dict(dtype=torch.int32, device=device)
+        self.counts = torch.empty((rows, nt), **i32)
+        self.col_idx = torch.empty((rows, nt, slots), **i32)
+        self.vals = torch.empty((rows, nt, slots), dtype=val_dtype, device=device)
+        self.ovf_n = torch.zeros((1,), **i32)
+        self.ovf_rows = torch.empty((max(ovf_cap, 1),), **i32)
+        self.ovf_slot = torch.empty((rows,), **i32)
+        self.ovf_dense = torch.empty((max(ovf_cap, 1), cols), dtype=val_dtype, device=device)
+        words = lib().twell_ovf_bits_words(rows, cols, tile_w)
+        self.ovf_bits = torch.empty((max(words, 1),), **i32)
+
+    def c(self) -> TwellMatrixC:
+        return TwellMatrixC(self.rows, self.cols, self.tile_w, self.slots, self.ovf_cap,
+                            _dt(self.val_dtype), _ptr(self.counts), _ptr(self.col_idx),
+                            _ptr(self.vals), _ptr(self.ovf_n), _ptr(self.ovf_rows),
+                            _ptr(self.ovf_slot), _ptr(self.ovf_dense), _ptr(self.ovf_bits))
+
+    @property
+    def n_tiles(self) -> int:
+        return self.cols // self.tile_w
+
+
+def twell_pack(h: torch.Tensor, tile_w: int, slots: int, ovf_cap: int,
+               val_dtype: torch.dtype | None = None, out: TwellMatrix | None = None) -> TwellMatrix:
+    R, C = h.shape
+    if out is None:
+        out = TwellMatrix(R, C, tile_w, slots, ovf_cap, val_dtype or h.dtype, h.device)
+    m = out.c()
+    _check(lib().twell_pack(_ptr(h), _dt(h.dtype), _c.byref(m), _stream(h.device)), "twell_pack")
+    return out
+
+
+def twell_ffn_fwd(x, w1t, b1, w2, tile_w: int, slots: int, ovf_cap: int,
+                  val_dtype=torch.float32, y_dtype=torch.float32, h: TwellMatrix | None = None,
+                  y: torch.Tensor | None = None):
+    """y = ReLU(x w1t^T + b1) w2 with the hidden activations packed in TwELL. Returns (y, h)."""
+    T, d = x.shape
+    f = w1t.shape[0]
+    if w1t.dtype != x.dtype or w2.dtype != x.dtype:
+        raise TypeError("x, w1t and w2 must share a dtype")
+    if b1.dtype != torch.float32:
+        raise TypeError("b1 must be float32")
+    if h is None:
+        h = TwellMatrix(T, f, tile_w, slots, ovf_cap, val_dtype, x.device)
+    if y is None:
+        y = torch.empty((T, d), dtype=y_dtype, device=x.device)
+    m = h.c()
+    _check(lib().twell_ffn_fwd(_ptr(x), _ptr(w1t), _ptr(b1), _ptr(w2), _dt(x.dtype), T, d, f,
+                               _c.byref(m), _ptr(y), _dt(y.dtype), _stream(x.device)), "twell_ffn_fwd")
+    return y, h
+
+
+def twell_down(h: TwellMatrix, w2: torch.Tensor, y_dtype=torch.float32, y=None) -> torch.Tensor:
+    d = w2.shape[1]
+    if y is None:
+        y = torch.empty((h.rows, d), dtype=y_dtype, device=w2.device)
+    m = h.c()
+    _check(lib().twell_down(_c.byref(m), _ptr(w2), _dt(w2.dtype), d, _ptr(y), _dt(y.dtype),
+                            _stream(w2.device)), "twell_down")
+    return y
+
+
+def ffn_up_relu_dense(x, w1t, b1, h_dtype=torch.float32, out=None) -> torch.Tensor:
+    T, d = x.shape
+    f = w1t.shape[0]
+    if out is None:
+        out = torch.empty((T, f), dtype=h_dtype, device=x.device)
+    _check(lib().ffn_up_relu_dense(_ptr(x), _ptr(w1t), _ptr(b1), _dt(x.dtype), T, d, f, _ptr(out),
+                                   _dt(out.dtype), _stream(x.device)), "ffn_up_relu_dense")
+    return out
+
+
+def twell_ffn_bwd_workspace_bytes(T: int, d: int, f: int, h: TwellMatrix) -> int:
+    m = h.c()
+    return lib().twell_ffn_bwd_workspace_bytes(T, d, f, _c.byref(m))
+
+
+def twell_ffn_bwd(x, w1t, w2, h: TwellMatrix, dy, l1_coef: float, want_db1: bool = True,
+                  workspace: torch.Tensor | None = None):
+    """Gradients (dx, dw1t, dw2, db1) of <dy, y> + l1_coef * sum(h), fp32."""
+    T, d = x.shape
+    f = w1t.shape[0]
+    dev = x.device
+    dx = torch.empty((T, d), dtype=torch.float32, device=dev)
+    dw1t = torch.empty((f, d), dtype=torch.float32, device=dev)
+    dw2 = torch.empty((f, d), dtype=torch.float32, device=dev)
+    db1 = torch.empty((f,), dtype=torch.float32, device=dev) if want_db1 else None
+    nbytes = twell_ffn_bwd_workspace_bytes(T, d, f, h)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
+    m = h.c()
+    _check(lib().twell_ffn_bwd(_ptr(x), _ptr(w1t), _ptr(w2), _dt(x.dtype), T, d, f, _c.byref(m),
+                               _ptr(dy), float(l1_coef), _ptr(dx), _ptr(dw1t), _ptr(dw2), _ptr(db1),
+                               _ptr(workspace), workspace.numel(), _stream(dev)), "twell_ffn_bwd")
+    return dx, dw1t, dw2, db1
+
+
+def nm_prune(h: torch.Tensor, n: int, m: int):
+    T, f = h.shape
+    vals = torch.empty((T, f // m, n), dtype=h.dtype, device=h.device)
+    idx = torch.empty((T, f // m, n), dtype=torch.uint8, device=h.device)
+    _check(lib().nm_prune(_ptr(h), _dt(h.dtype), T, f, n, m, _ptr(vals), _ptr(idx), _stream(h.device)),
+           "nm_prune")
+    return vals, idx
+
+
+def nm_ffn_down(vals, idx, n: int, m: int, w2t: torch.Tensor, y_dtype=torch.float32, y=None):
+    T, G, _ = vals.shape
+    f = G * m
+    d = w2t.shape[0]
+    if y is None:
+        y = torch.empty((T, d), dtype=y_dtype, device=vals.device)
+    _check(lib().nm_ffn_down(_ptr(vals), _ptr(idx), _dt(vals.dtype), T, f, n, m, _ptr(w2t), d, _ptr(y),
+                             _dt(y.dtype), _stream(vals.device)), "nm_ffn_down")
+    return y
+
+
+def twell_sync_status(h: TwellMatrix) -> int:
+    m = h.c()
+    return lib().twell_sync_status(_c.byref(m), _stream(h.counts.device))

@@ -1,0 +1,214 @@
+// C ABI of the TwELL FFN library: argument validation, then launches on the caller's stream.
+// Declarations, layouts and error contract: include/twell.h.
+#include <string.h>
+
+#include "../../include/twell.h"
+#include "launch.h"
+
+using namespace tw;
+
+namespace {
+
+inline bool al16(const void *p) { return ((uintptr_t)p & 15u) == 0; }
+inline bool al4(const void *p) { return ((uintptr_t)p & 3u) == 0; }
+inline bool dtype_ok(int32_t t) { return t == TWELL_F32 || t == TWELL_BF16; }
+inline hipStream_t S(void *s) { return (hipStream_t)s; }
+inline int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_ERR_HIP; }
+
+#define TW_TRY(expr)                               \
+  do {                                             \
+    hipError_t e_ = (expr);                        \
+    if (e_ != hipSuccess) return TWELL_ERR_HIP;    \
+  } while (0)
+
+// Shape and pointer checks of a TwELL struct used as output (writable) or input.
+int check_matrix(const twell_matrix_t *m, bool need_ovf_bits) {
+  if (!m) return TWELL_ERR_ARG;
+  if (!dtype_ok(m->val_dtype)) return TWELL_ERR_ARG;
+  if (m->rows < 0 || m->cols <= 0 || m->ovf_cap < 0) return TWELL_ERR_SHAPE;
+  if (m->tile_w != 64 && m->tile_w != 128) return TWELL_ERR_UNSUPPORTED;
+  if (m->cols % m->tile_w) return TWELL_ERR_SHAPE;
+  if (m->slots < 1 || m->slots > m->tile_w || m->slots > 64) return TWELL_ERR_SHAPE;
+  if (!m->ovf_n) return TWELL_ERR_ARG;
+  if (m->rows > 0) {
+    if (!m->counts || !m->col_idx || !m->vals || !m->ovf_slot) return TWELL_ERR_ARG;
+    if (need_ovf_bits && !m->ovf_bits) return TWELL_ERR_ARG;
+  }
+  if (m->ovf_cap > 0 && (!m->ovf_rows || !m->ovf_dense)) return TWELL_ERR_ARG;
+  if (!al4(m->counts) || !al4(m->col_idx) || !al4(m->vals) || !al4(m->ovf_n) || !al4(m->ovf_rows) ||
+      !al4(m->ovf_slot) || !al4(m->ovf_bits) || !al16(m->ovf_dense))
+    return TWELL_ERR_ALIGN;
+  return TWELL_OK;
+}
+
+TwellOut out_of(const twell_matrix_t *m) {
+  TwellOut o;
+  o.counts = m->counts;
+  o.col_idx = m->col_idx;
+  o.vals = m->vals;
+  o.ovf_bits = m->ovf_bits;
+  o.n_t = m->cols / m->tile_w;
+  o.S = m->slots;
+  o.words = (m->rows + 31) / 32;
+  o.val_bf16 = m->val_dtype == TWELL_BF16;
+  return o;
+}
+
+TwellIn in_of(const twell_matrix_t *m) {
+  TwellIn h;
+  h.counts = m->counts;
+  h.col_idx = m->col_idx;
+  h.vals = m->vals;
+  h.ovf_slot = m->ovf_slot;
+  h.ovf_dense = m->ovf_dense;
+  h.rows = m->rows;
+  h.cols = m->cols;
+  h.n_t = m->cols / m->tile_w;
+  h.S = m->slots;
+  h.W = m->tile_w;
+  h.val_bf16 = m->val_dtype == TWELL_BF16;
+  return h;
+}
+
+}  // namespace
+
+extern "C" {
+
+int twell_abi_version(void) { return TWELL_ABI_VERSION; }
+
+const char *twell_status_str(int status) {
+  switch (status) {
+    case TWELL_OK: return "TWELL_OK";
+    case TWELL_ERR_ARG: return "TWELL_ERR_ARG: null pointer or invalid enum/struct field";
+    case TWELL_ERR_SHAPE: return "TWELL_ERR_SHAPE: invalid or inconsistent sizes";
+    case TWELL_ERR_ALIGN: return "TWELL_ERR_ALIGN: misaligned pointer or d_model % 8 != 0";
+    case TWELL_ERR_WORKSPACE: return "TWELL_ERR_WORKSPACE: workspace too small";
+    case TWELL_ERR_OVF_CAPACITY: return "TWELL_ERR_OVF_CAPACITY: more overflow rows than ovf_cap";
+    case TWELL_ERR_HIP: return "TWELL_ERR_HIP: HIP runtime or launch failure";
+    case TWELL_ERR_UNSUPPORTED: return "TWELL_ERR_UNSUPPORTED: valid request not implemented";
+    default: return "TWELL_UNKNOWN_STATUS";
+  }
+}
+
+size_t twell_ovf_bits_words(int32_t rows, int32_t cols, int32_t tile_w) {
+  if (rows < 0 || cols <= 0 || tile_w <= 0) return 0;
+  return (size_t)(cols / tile_w) * (size_t)((rows + 31) / 32);
+}
+
+int twell_pack(const void *h, int32_t h_dtype, twell_matrix_t *out, void *stream) {
+  if (!h || !out) return TWELL_ERR_ARG;
+  if (!dtype_ok(h_dtype)) return TWELL_ERR_ARG;
+  int st = check_matrix(out, true);
+  if (st) return st;
+  if (h_dtype == TWELL_F32 && out->val_dtype == TWELL_BF16) return TWELL_ERR_UNSUPPORTED;
+  if (!al16(h)) return TWELL_ERR_ALIGN;
+  const int R = out->rows, C = out->cols;
+  if (R == 0) return hip_status(launch_set_int(out->ovf_n, 0, S(stream)));
+  const TwellOut o = out_of(out);
+  TW_TRY(launch_pack(h, h_dtype == TWELL_BF16, R, C, o, out->tile_w, S(stream)));
+  TW_TRY(launch_ovf_scan(out->ovf_bits, o.n_t, o.words, R, out->ovf_cap, out->ovf_n, out->ovf_rows,
+                         out->ovf_slot, S(stream)));
+  TW_TRY(launch_ovf_copy(h, h_dtype == TWELL_BF16, R, C, out->ovf_n, out->ovf_rows, out->ovf_cap,
+                         out->ovf_dense, out->val_dtype == TWELL_BF16, S(stream)));
+  return TWELL_OK;
+}
+
+static int check_ffn_args(const void *x, const void *w1t, const void *w2, int32_t in_dtype, int32_t T,
+                          int32_t d, int32_t f) {
+  if (!w1t || (T > 0 && !x)) return TWELL_ERR_ARG;
+  if (!dtype_ok(in_dtype)) return TWELL_ERR_ARG;
+  if (T < 0 || d <= 0 || f <= 0) return TWELL_ERR_SHAPE;
+  if (d % 8) return TWELL_ERR_ALIGN;
+  if (!al16(x) || !al16(w1t) || (w2 && !al16(w2))) return TWELL_ERR_ALIGN;
+  return TWELL_OK;
+}
+
+int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w2, int32_t in_dtype,
+                  int32_t T, int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *y, int32_t y_dtype,
+                  void *stream) {
+  if (!b1 || !w2 || !h || (T > 0 && !y)) return TWELL_ERR_ARG;
+  if (!dtype_ok(y_dtype)) return TWELL_ERR_ARG;
+  int st = check_ffn_args(x, w1t, w2, in_dtype, T, d_model, d_ff);
+  if (st) return st;
+  st = check_matrix(h, true);
+  if (st) return st;
+  if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
+  if (!al16(y) || !al4(b1)) return TWELL_ERR_ALIGN;
+  hipStream_t s = S(stream);
+  if (T == 0) return hip_status(launch_set_int(h->ovf_n, 0, s));
+  const int bf = in_dtype == TWELL_BF16;
+  const TwellOut o = out_of(h);
+  TW_TRY(launch_up_twell(bf, x, w1t, b1, T, d_ff, d_model, o, h->tile_w, s));
+  TW_TRY(launch_ovf_scan(h->ovf_bits, o.n_t, o.words, T, h->ovf_cap, h->ovf_n, h->ovf_rows, h->ovf_slot, s));
+  if (h->ovf_cap > 0) {
+    const int M = h->ovf_cap < T ? h->ovf_cap : T;
+    TW_TRY(launch_up_dense(bf, x, w1t, b1, M, d_ff, d_model, h->ovf_rows, h->ovf_n, h->ovf_dense,
+                           h->val_dtype == TWELL_BF16, 1, s));
+  }
+  TW_TRY(launch_twell_down(in_of(h), w2, bf, d_model, y, y_dtype == TWELL_BF16, s));
+  return TWELL_OK;
+}
+
+int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model, void *y,
+               int32_t y_dtype, void *stream) {
+  if (!h || !w2 || !y) return TWELL_ERR_ARG;
+  if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return TWELL_ERR_ARG;
+  int st = check_matrix(h, false);
+  if (st) return st;
+  if (d_model <= 0) return TWELL_ERR_SHAPE;
+  if (d_model % 8) return TWELL_ERR_ALIGN;
+  if (!al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
+  if (h->rows == 0) return TWELL_OK;
+  TW_TRY(launch_twell_down(in_of(h), w2, w_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, S(stream)));
+  return TWELL_OK;
+}
+
+int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                      int32_t d_model, int32_t d_ff, void *h, int32_t h_dtype, void *stream) {
+  if (!b1 || (T > 0 && !h)) return TWELL_ERR_ARG;
+  if (!dtype_ok(h_dtype)) return TWELL_ERR_ARG;
+  int st = check_ffn_args(x, w1t, nullptr, in_dtype, T, d_model, d_ff);
+  if (st) return st;
+  if (!al16(h) || !al4(b1)) return TWELL_ERR_ALIGN;
+  if (T == 0) return TWELL_OK;
+  TW_TRY(launch_up_dense(in_dtype == TWELL_BF16, x, w1t, b1, T, d_ff, d_model, nullptr, nullptr, h,
+                         h_dtype == TWELL_BF16, 1, S(stream)));
+  return TWELL_OK;
+}
+
+size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, const twell_matrix_t *h) {
+  (void)T; (void)d_model; (void)d_ff; (void)h;
+  return 0;
+}
+
+int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dtype, int32_t T,
+                  int32_t d_model, int32_t d_ff, const twell_matrix_t *h, const void *dy, float l1_coef,
+                  float *dx, float *dw1t, float *dw2, float *db1, void *workspace, size_t workspace_bytes,
+                  void *stream) {
+  (void)x; (void)w1t; (void)w2; (void)in_dtype; (void)T; (void)d_model; (void)d_ff; (void)h; (void)dy;
+  (void)l1_coef; (void)dx; (void)dw1t; (void)dw2; (void)db1; (void)workspace; (void)workspace_bytes; (void)stream;
+  return TWELL_ERR_UNSUPPORTED;
+}
+
+int nm_prune(const void *h, int32_t dtype, int32_t T, int32_t d_ff, int32_t n, int32_t m, void *vals,
+             uint8_t *idx, void *stream) {
+  (void)h; (void)dtype; (void)T; (void)d_ff; (void)n; (void)m; (void)vals; (void)idx; (void)stream;
+  return TWELL_ERR_UNSUPPORTED;
+}
+
+int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, int32_t d_ff, int32_t n,
+                int32_t m, const void *w2t, int32_t d_model, void *y, int32_t y_dtype, void *stream) {
+  (void)vals; (void)idx; (void)dtype; (void)T; (void)d_ff; (void)n; (void)m; (void)w2t; (void)d_model;
+  (void)y; (void)y_dtype; (void)stream;
+  return TWELL_ERR_UNSUPPORTED;
+}
+
+int twell_sync_status(const twell_matrix_t *h, void *stream) {
+  if (!h || !h->ovf_n) return TWELL_ERR_ARG;
+  if (hipStreamSynchronize(S(stream)) != hipSuccess) return TWELL_ERR_HIP;
+  int32_t n = 0;
+  if (hipMemcpy(&n, h->ovf_n, sizeof(n), hipMemcpyDeviceToHost) != hipSuccess) return TWELL_ERR_HIP;
+  return n > h->ovf_cap ? TWELL_ERR_OVF_CAPACITY : TWELL_OK;
+}
+
+}  // extern "C"

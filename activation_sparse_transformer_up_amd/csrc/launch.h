@@ -1,0 +1,48 @@
+// Internal launchers shared between the kernel files and the C ABI layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace tw {
+
+// Output side of a TwELL-producing kernel (see twell_matrix_t in include/twell.h).
+struct TwellOut {
+  int32_t *counts;
+  int32_t *col_idx;
+  void *vals;
+  uint32_t *ovf_bits;
+  int n_t, S, words, val_bf16;
+};
+
+// Read side of a TwELL consumer.
+struct TwellIn {
+  const int32_t *counts;
+  const int32_t *col_idx;
+  const void *vals;
+  const int32_t *ovf_slot;
+  const void *ovf_dense;
+  int rows, cols, n_t, S, W, val_bf16;
+};
+
+// gemm.hip
+hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
+                           const TwellOut &o, int W, hipStream_t s);
+hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
+                           const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
+                           hipStream_t s);
+
+// pack.hip
+hipError_t launch_pack(const void *h, int h_bf16, int R, int C, const TwellOut &o, int W, hipStream_t s);
+hipError_t launch_ovf_scan(const uint32_t *bits, int n_t, int words, int R, int cap, int32_t *ovf_n,
+                           int32_t *ovf_rows, int32_t *ovf_slot, hipStream_t s);
+hipError_t launch_ovf_copy(const void *h, int h_bf16, int R, int C, const int32_t *ovf_n, const int32_t *ovf_rows,
+                           int cap, void *dense, int dense_bf16, hipStream_t s);
+hipError_t launch_set_int(int32_t *p, int v, hipStream_t s);
+
+// down.hip
+hipError_t launch_twell_down(const TwellIn &h, const void *w2, int w_bf16, int d, void *y, int y_bf16,
+                             hipStream_t s);
+
+}  // namespace tw

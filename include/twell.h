@@ -1,0 +1,201 @@
+/*
+ * twell.h — C ABI of the activation-sparse transformer feed-forward library (AMD gfx950).
+ *
+ * The layer is y = ReLU(x . W1 + b1) . W2 in which only the nonzero hidden activations
+ * are stored and multiplied ("Sparser, Faster, Lighter Transformer Language Models",
+ * section "1. O Problema", and section "2. Metodologia": "Formato de Dados TwELL",
+ * "Kernels de Inferência", "Formato Híbrido para Treinamento", "Técnicas de Treinamento").
+ * N:M activation pruning follows "Motivating Next-Gen Accelerators with Flexible (N:M)
+ * Activation Sparsity ...", section "2. Metodologia" (magnitude criterion ACT).
+ *
+ * Conventions for every entry point:
+ *   - Array pointers are DEVICE pointers (memory the caller allocated on the current HIP
+ *     device), row-major, contiguous, 16-byte aligned. The caller owns every buffer; the
+ *     library never allocates, frees or keeps a pointer after the call returns.
+ *   - `stream` is a hipStream_t (NULL = the null stream). Work is enqueued on it and the
+ *     call returns without synchronising (except twell_sync_status).
+ *   - Arguments are validated before anything is enqueued; on an error nothing is written
+ *     and a negative twell_status_t is returned. A failed launch returns TWELL_ERR_HIP.
+ *   - Outputs must not alias inputs. Gradients are overwritten, not accumulated.
+ *   - The library holds no mutable global state and is safe to call concurrently on
+ *     different streams with different buffers.
+ *   - Floating-point inputs must be finite; NaN/Inf are outside the contract.
+ *
+ * Layouts (T tokens, d = d_model, f = d_ff):
+ *   x   [T][d]     token activations
+ *   w1t [f][d]     row j = input weights of hidden unit j   (nn.Linear(d, f).weight)
+ *   b1  [f]        fp32 bias
+ *   w2  [f][d]     row j = output weights of hidden unit j  (nn.Linear(f, d).weight^T)
+ *   y   [T][d]
+ */
+#ifndef TWELL_H
+#define TWELL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define TWELL_ABI_VERSION 1
+
+typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype_t;
+
+typedef enum {
+  TWELL_OK = 0,
+  TWELL_ERR_ARG = -1,          /* null pointer, bad enum value, bad struct field          */
+  TWELL_ERR_SHAPE = -2,        /* non-positive size, f % tile_w, slots out of range, ...   */
+  TWELL_ERR_ALIGN = -3,        /* pointer not 16-byte aligned, or d % 8 != 0               */
+  TWELL_ERR_WORKSPACE = -4,    /* workspace too small                                      */
+  TWELL_ERR_OVF_CAPACITY = -5, /* (twell_sync_status only) more overflow rows than ovf_cap */
+  TWELL_ERR_HIP = -6,          /* a HIP call or kernel launch failed                       */
+  TWELL_ERR_UNSUPPORTED = -7   /* valid request this version does not implement           */
+} twell_status_t;
+
+/*
+ * TwELL (Tile-wise ELLPACK) matrix with its row-level dense backup.
+ *
+ * "Formato de Dados TwELL": the columns of an R x C matrix are cut into tiles of tile_w
+ * columns; for every (row, tile) the nonzero values and their column indices are stored
+ * aligned inside that tile's slot block. "Formato Híbrido para Treinamento": rows with
+ * too many nonzeros are routed to a dense backup matrix.
+ *
+ *   counts  [R][C/tile_w]           true nonzero count of the (row, tile); may exceed slots
+ *   col_idx [R][C/tile_w][slots]    global column of the s-th nonzero, ascending; pad = -1
+ *   vals    [R][C/tile_w][slots]    its value (val_dtype); pad = +0.0
+ *   ovf_n   [1]                     true number of overflow rows (may exceed ovf_cap)
+ *   ovf_rows[ovf_cap]               overflow rows in ascending order (first ovf_cap of them)
+ *   ovf_slot[R]                     index into ovf_dense, or -1 (no overflow / no room)
+ *   ovf_dense[ovf_cap][C]           the full row of each listed overflow row (val_dtype)
+ *   ovf_bits[C/tile_w][ceil(R/32)]  library scratch (uint32 words), written and read
+ *                                   inside one call; contents on return are unspecified
+ *
+ * A row overflows iff some tile of it holds more than `slots` nonzeros. A (row, tile)
+ * keeps its first min(count, slots) nonzeros in ascending column order. "Nonzero" is
+ * "not +0 and not -0". The slots of an overflow row are still filled (first `slots` per
+ * tile); consumers take such a row from ovf_dense. Rows that overflow beyond ovf_cap get
+ * ovf_slot = -1 and their products are undefined; twell_sync_status reports the case.
+ *
+ * Supported: tile_w in {64, 128}; 1 <= slots <= min(tile_w, 64); ovf_cap >= 0 (ovf_rows
+ * and ovf_dense may be NULL when ovf_cap == 0); val_dtype TWELL_F32 or TWELL_BF16.
+ */
+typedef struct {
+  int32_t rows, cols, tile_w, slots, ovf_cap;
+  int32_t val_dtype;
+  int32_t *counts;
+  int32_t *col_idx;
+  void *vals;
+  int32_t *ovf_n;
+  int32_t *ovf_rows;
+  int32_t *ovf_slot;
+  void *ovf_dense;
+  uint32_t *ovf_bits;
+} twell_matrix_t;
+
+/* Returns TWELL_ABI_VERSION. */
+int twell_abi_version(void);
+
+/* Static, human-readable name of a status code (never NULL). */
+const char *twell_status_str(int status);
+
+/* Number of uint32 words that twell_matrix_t.ovf_bits must hold. */
+size_t twell_ovf_bits_words(int32_t rows, int32_t cols, int32_t tile_w);
+
+/*
+ * twell_pack — dense h [R][C] (h_dtype) -> TwELL `out` (shape fields set by the caller).
+ * The separate dense-to-sparse conversion that "Formato de Dados TwELL" describes as the
+ * step the fused epilogue removes; kept as a building block and for testing. Values are
+ * copied bit for bit (bf16 -> fp32 widening is exact; fp32 -> bf16 is refused).
+ * Errors: TWELL_ERR_ARG (null), TWELL_ERR_SHAPE (C % tile_w, slots), TWELL_ERR_UNSUPPORTED.
+ */
+int twell_pack(const void *h, int32_t h_dtype, twell_matrix_t *out, void *stream);
+
+/*
+ * twell_ffn_fwd — y = ReLU(x . W1 + b1) . W2 with the hidden activations in TwELL.
+ * "Formato de Dados TwELL": the up projection is a dense GEMM (MFMA) whose epilogue applies
+ * the bias and ReLU and writes the TwELL slots directly; "Kernels de Inferência": the down
+ * projection iterates over the active units only. The TwELL (h_out, shape fields and
+ * buffers from the caller, rows = T, cols = d_ff) is left for the backward pass.
+ * in_dtype: TWELL_F32 (x, w1t, w2 fp32) or TWELL_BF16 (bf16, fp32 accumulation).
+ * y_dtype: TWELL_F32 or TWELL_BF16. T == 0 is allowed (only *ovf_n is written).
+ * Errors: TWELL_ERR_ARG, TWELL_ERR_SHAPE (d, d_ff <= 0, T < 0, d_ff % tile_w, h_out shape
+ * mismatch), TWELL_ERR_ALIGN (d % 8), TWELL_ERR_UNSUPPORTED.
+ */
+int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w2,
+                  int32_t in_dtype, int32_t T, int32_t d_model, int32_t d_ff,
+                  twell_matrix_t *h_out, void *y, int32_t y_dtype, void *stream);
+
+/*
+ * twell_down — y[t] = sum over the nonzero h[t, j] of h[t, j] * w2[j] for an existing
+ * TwELL h (rows = T, cols = d_ff; ovf_slot must be valid), fp32 accumulation.
+ * "Kernels de Inferência": only the active units' rows of W2 are read.
+ */
+int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model,
+               void *y, int32_t y_dtype, void *stream);
+
+/*
+ * ffn_up_relu_dense — h = ReLU(x . W1 + b1) written densely ([T][d_ff], h_dtype = fp32 or
+ * bf16). Same MFMA kernel and accumulation order as the fused TwELL path, so the fp32
+ * output is bit-identical to the values the TwELL epilogue sees.
+ */
+int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t in_dtype,
+                      int32_t T, int32_t d_model, int32_t d_ff, void *h, int32_t h_dtype,
+                      void *stream);
+
+/* Bytes of device workspace twell_ffn_bwd needs for this problem. */
+size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff,
+                                     const twell_matrix_t *h);
+
+/*
+ * twell_ffn_bwd — gradients of <dy, y> + l1_coef * sum(h) for the forward above.
+ * "Formato Híbrido para Treinamento": the backward runs on the sparsity pattern stored in
+ * the TwELL h (slots of normal rows, dense backup of overflow rows); "Técnicas de
+ * Treinamento": the L1 penalty adds l1_coef on every active entry of dh.
+ *   dz   = (dy . W2^T + l1_coef) on the pattern      (ReLU'(0) = 0)
+ *   dx   = dz . w1t                 [T][d]  fp32
+ *   dw1t = dz^T . x                 [f][d]  fp32
+ *   dw2  = h^T . dy                 [f][d]  fp32
+ *   db1  = sum_t dz                 [f]     fp32 (may be NULL)
+ * x, w1t, w2, dy have in_dtype. Requires every overflow row to have a backup slot
+ * (*ovf_n <= ovf_cap); rows without one contribute through their slots only.
+ */
+int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dtype,
+                  int32_t T, int32_t d_model, int32_t d_ff, const twell_matrix_t *h,
+                  const void *dy, float l1_coef, float *dx, float *dw1t, float *dw2,
+                  float *db1, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * nm_prune — N:M activation pruning by magnitude ("Motivating Next-Gen Accelerators ...",
+ * "2. Metodologia", criterion ACT): in every block of m consecutive entries of a row of
+ * h [T][d_ff] keep the n of largest |h| (ties to the lower index), emitted in ascending
+ * index order with their signed values.
+ *   vals [T][d_ff/m][n]  dtype (bit-exact copies)
+ *   idx  [T][d_ff/m][n]  uint8, index inside the block
+ * Supported (n, m): (2,4), (4,8), (8,16), (16,32). dtype: TWELL_BF16 or TWELL_F32.
+ */
+int nm_prune(const void *h, int32_t dtype, int32_t T, int32_t d_ff, int32_t n, int32_t m,
+             void *vals, uint8_t *idx, void *stream);
+
+/*
+ * nm_ffn_down — y = H_nm . W2 for N:M-packed activations (vals, idx from nm_prune, bf16).
+ * gfx950 has no N:M matrix instruction, so each block is expanded to dense bf16 in LDS and
+ * multiplied on MFMA; only the activation bytes shrink. The down weight is given as
+ * w2t [d_model][d_ff] (nn.Linear(d_ff, d_model).weight), the K-contiguous layout the MFMA
+ * operand loads want. y: [T][d_model], y_dtype fp32 or bf16.
+ */
+int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, int32_t d_ff,
+                int32_t n, int32_t m, const void *w2t, int32_t d_model, void *y,
+                int32_t y_dtype, void *stream);
+
+/*
+ * twell_sync_status — waits for `stream`, then reads *ovf_n: TWELL_ERR_OVF_CAPACITY if it
+ * exceeds ovf_cap, TWELL_OK otherwise (TWELL_ERR_HIP if the wait or copy fails).
+ */
+int twell_sync_status(const twell_matrix_t *h, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TWELL_H */

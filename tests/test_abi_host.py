@@ -1,0 +1,116 @@
+"""Host-side checks of the C ABI (no GPU needed): the library loads, exports every function
+include/twell.h declares, and rejects invalid arguments with the documented status codes
+before anything is enqueued. Fake device addresses are used only in calls that fail
+validation; on a machine with a GPU these cases run in the GPU suite with real buffers."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "twell.h")
+
+import activation_sparse_transformer_up_amd as tw  # noqa: E402
+
+ARG, SHAPE, ALIGN, UNSUP = -1, -2, -3, -7
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)))
+
+
+def test_header_declares_expected_entry_points():
+    names = declared_functions()
+    for n in ["twell_pack", "twell_ffn_fwd", "twell_ffn_bwd", "nm_prune", "twell_abi_version",
+              "twell_status_str", "twell_sync_status", "nm_ffn_down", "ffn_up_relu_dense",
+              "twell_down", "twell_ffn_bwd_workspace_bytes", "twell_ovf_bits_words"]:
+        assert n in names, n
+
+
+def test_library_exports_every_declared_symbol():
+    L = tw.lib()
+    for n in declared_functions():
+        assert hasattr(L, n), n
+
+
+def test_version_and_status_strings():
+    assert tw.twell_abi_version() == 1
+    L = tw.lib()
+    for code in [0, -1, -2, -3, -4, -5, -6, -7]:
+        s = L.twell_status_str(code).decode()
+        assert s.startswith(tw.STATUS[code])
+    assert L.twell_status_str(12345).decode() == "TWELL_UNKNOWN_STATUS"
+    assert L.twell_ovf_bits_words(100, 1024, 64) == 16 * 4
+    assert L.twell_ovf_bits_words(-1, 1024, 64) == 0
+
+
+def gpu_present():
+    try:
+        import torch
+        return torch.cuda.is_available()
+    except Exception:
+        return False
+
+
+pytestmark_nogpu = pytest.mark.skipif(gpu_present(), reason="fake-pointer checks run only without a GPU")
+
+FAKE = 0x10000          # 16-byte aligned, never dereferenced: every call below fails validation
+MIS = 0x10004           # misaligned
+
+
+def mat(rows=64, cols=512, W=128, S=8, cap=4, dt=0, **kw):
+    m = tw.TwellMatrixC(rows, cols, W, S, cap, dt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(m, k, v)
+    return m
+
+
+def fwd(m, x=FAKE, w1t=FAKE, b1=FAKE, w2=FAKE, dt=1, T=64, d=256, f=512, y=FAKE, ydt=0):
+    return tw.lib().twell_ffn_fwd(x, w1t, b1, w2, dt, T, d, f, ctypes.byref(m), y, ydt, None)
+
+
+@pytestmark_nogpu
+@pytest.mark.parametrize("kw,want", [
+    (dict(x=None), ARG), (dict(w2=None), ARG), (dict(b1=None), ARG), (dict(y=None), ARG),
+    (dict(dt=7), ARG), (dict(ydt=3), ARG), (dict(T=-1), SHAPE), (dict(d=0), SHAPE),
+    (dict(f=0), SHAPE), (dict(d=100), ALIGN), (dict(x=MIS), ALIGN), (dict(y=MIS), ALIGN),
+    (dict(T=32), SHAPE), (dict(f=1024), SHAPE),
+])
+def test_fwd_rejects(kw, want):
+    assert fwd(mat(), **kw) == want
+
+
+@pytestmark_nogpu
+@pytest.mark.parametrize("mkw,want", [
+    (dict(tile_w=96), UNSUP), (dict(cols=500), SHAPE), (dict(slots=0), SHAPE),
+    (dict(slots=65), SHAPE), (dict(W=64, slots=65), SHAPE), (dict(ovf_cap=-1), SHAPE),
+    (dict(counts=None), ARG), (dict(ovf_n=None), ARG), (dict(ovf_bits=None), ARG),
+    (dict(val_dtype=5), ARG), (dict(ovf_rows=None), ARG), (dict(ovf_dense=MIS), ALIGN),
+    (dict(counts=MIS + 1), ALIGN),
+])
+def test_fwd_rejects_bad_matrix(mkw, want):
+    W = mkw.pop("W", 128)
+    m = mat(W=W)
+    for k, v in mkw.items():
+        setattr(m, k, v)
+    assert fwd(m) == want
+
+
+@pytestmark_nogpu
+def test_pack_and_down_reject():
+    L = tw.lib()
+    m = mat()
+    assert L.twell_pack(None, 0, ctypes.byref(m), None) == ARG
+    assert L.twell_pack(FAKE, 9, ctypes.byref(m), None) == ARG
+    assert L.twell_pack(MIS, 0, ctypes.byref(m), None) == ALIGN
+    m16 = mat(dt=1)
+    assert L.twell_pack(FAKE, 0, ctypes.byref(m16), None) == UNSUP       # fp32 h -> bf16 vals
+    assert L.twell_down(ctypes.byref(m), FAKE, 1, 100, FAKE, 0, None) == ALIGN
+    assert L.twell_down(ctypes.byref(m), None, 1, 256, FAKE, 0, None) == ARG
+    assert L.twell_down(ctypes.byref(m), FAKE, 1, 0, FAKE, 0, None) == SHAPE
+    assert L.ffn_up_relu_dense(FAKE, FAKE, None, 1, 4, 256, 512, FAKE, 0, None) == ARG
+    assert L.ffn_up_relu_dense(FAKE, FAKE, FAKE, 1, 4, 250, 512, FAKE, 0, None) == ALIGN
+    assert L.twell_sync_status(None, None) == ARG
