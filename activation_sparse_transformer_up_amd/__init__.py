@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
-    "twell_down", "ffn_up_relu_dense", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
+    "twell_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
     "nm_prune", "nm_ffn_down", "twell_sync_status", "F32", "BF16",
 ]
 
@@ -48,6 +48,8 @@ _SIGS = {
     "twell_pack": ([_P, _I, _P, _P], _I),
     "twell_ffn_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
     "twell_down": ([_P, _P, _I, _I, _P, _I, _P], _I),
+    "twell_up_gemm": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
+    "twell_up_finish": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "ffn_up_relu_dense": ([_P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
     "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _P], _Z),
     "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
@@ -168,6 +170,24 @@ def twell_ffn_fwd(x, w1t, b1, w2, tile_w: int, slots: int, ovf_cap: int,
     _check(lib().twell_ffn_fwd(_ptr(x), _ptr(w1t), _ptr(b1), _ptr(w2), _dt(x.dtype), T, d, f,
                                _c.byref(m), _ptr(y), _dt(y.dtype), _stream(x.device)), "twell_ffn_fwd")
     return y, h
+
+
+def twell_up_gemm(x, w1t, b1, h: TwellMatrix) -> TwellMatrix:
+    """Stage 1 of twell_ffn_fwd: up GEMM with the fused ReLU + TwELL epilogue."""
+    T, d = x.shape
+    m = h.c()
+    _check(lib().twell_up_gemm(_ptr(x), _ptr(w1t), _ptr(b1), _dt(x.dtype), T, d, w1t.shape[0],
+                               _c.byref(m), _stream(x.device)), "twell_up_gemm")
+    return h
+
+
+def twell_up_finish(x, w1t, b1, h: TwellMatrix) -> TwellMatrix:
+    """Stage 2 of twell_ffn_fwd: overflow list, slots, count and dense backup rows."""
+    T, d = x.shape
+    m = h.c()
+    _check(lib().twell_up_finish(_ptr(x), _ptr(w1t), _ptr(b1), _dt(x.dtype), T, d, w1t.shape[0],
+                                 _c.byref(m), _stream(x.device)), "twell_up_finish")
+    return h
 
 
 def twell_down(h: TwellMatrix, w2: torch.Tensor, y_dtype=torch.float32, y=None) -> torch.Tensor:

@@ -120,32 +120,72 @@ static int check_ffn_args(const void *x, const void *w1t, const void *w2, int32_
   if (T < 0 || d <= 0 || f <= 0) return TWELL_ERR_SHAPE;
   if (d % 8) return TWELL_ERR_ALIGN;
   if (!al16(x) || !al16(w1t) || (w2 && !al16(w2))) return TWELL_ERR_ALIGN;
+  // the GEMM addresses each operand with 32-bit byte offsets
+  const size_t es = in_dtype == TWELL_BF16 ? 2 : 4;
+  if ((size_t)T * d * es >= ((size_t)1 << 31) || (size_t)f * d * es >= ((size_t)1 << 31)) return TWELL_ERR_UNSUPPORTED;
   return TWELL_OK;
+}
+
+static int check_up_args(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                         int32_t d_model, int32_t d_ff, const twell_matrix_t *h) {
+  if (!b1 || !h) return TWELL_ERR_ARG;
+  int st = check_ffn_args(x, w1t, nullptr, in_dtype, T, d_model, d_ff);
+  if (st) return st;
+  st = check_matrix(h, true);
+  if (st) return st;
+  if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
+  if (!al4(b1)) return TWELL_ERR_ALIGN;
+  return TWELL_OK;
+}
+
+static int up_gemm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T, int32_t d_model,
+                   int32_t d_ff, twell_matrix_t *h, hipStream_t s) {
+  if (T == 0) return TWELL_OK;
+  TW_TRY(launch_up_twell(in_dtype == TWELL_BF16, x, w1t, b1, T, d_ff, d_model, out_of(h), h->tile_w, s));
+  return TWELL_OK;
+}
+
+static int up_finish(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                     int32_t d_model, int32_t d_ff, twell_matrix_t *h, hipStream_t s) {
+  if (T == 0) return hip_status(launch_set_int(h->ovf_n, 0, s));
+  const TwellOut o = out_of(h);
+  TW_TRY(launch_ovf_scan(h->ovf_bits, o.n_t, o.words, T, h->ovf_cap, h->ovf_n, h->ovf_rows, h->ovf_slot, s));
+  if (h->ovf_cap > 0) {
+    const int M = h->ovf_cap < T ? h->ovf_cap : T;
+    TW_TRY(launch_up_dense(in_dtype == TWELL_BF16, x, w1t, b1, M, d_ff, d_model, T, h->ovf_rows, h->ovf_n,
+                           h->ovf_dense, h->val_dtype == TWELL_BF16, 1, s));
+  }
+  return TWELL_OK;
+}
+
+int twell_up_gemm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                  int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream) {
+  int st = check_up_args(x, w1t, b1, in_dtype, T, d_model, d_ff, h);
+  if (st) return st;
+  return up_gemm(x, w1t, b1, in_dtype, T, d_model, d_ff, h, S(stream));
+}
+
+int twell_up_finish(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                    int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream) {
+  int st = check_up_args(x, w1t, b1, in_dtype, T, d_model, d_ff, h);
+  if (st) return st;
+  return up_finish(x, w1t, b1, in_dtype, T, d_model, d_ff, h, S(stream));
 }
 
 int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w2, int32_t in_dtype,
                   int32_t T, int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *y, int32_t y_dtype,
                   void *stream) {
-  if (!b1 || !w2 || !h || (T > 0 && !y)) return TWELL_ERR_ARG;
+  if (!w2 || (T > 0 && !y)) return TWELL_ERR_ARG;
   if (!dtype_ok(y_dtype)) return TWELL_ERR_ARG;
-  int st = check_ffn_args(x, w1t, w2, in_dtype, T, d_model, d_ff);
+  int st = check_up_args(x, w1t, b1, in_dtype, T, d_model, d_ff, h);
   if (st) return st;
-  st = check_matrix(h, true);
-  if (st) return st;
-  if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
-  if (!al16(y) || !al4(b1)) return TWELL_ERR_ALIGN;
+  if (!al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
   hipStream_t s = S(stream);
-  if (T == 0) return hip_status(launch_set_int(h->ovf_n, 0, s));
-  const int bf = in_dtype == TWELL_BF16;
-  const TwellOut o = out_of(h);
-  TW_TRY(launch_up_twell(bf, x, w1t, b1, T, d_ff, d_model, o, h->tile_w, s));
-  TW_TRY(launch_ovf_scan(h->ovf_bits, o.n_t, o.words, T, h->ovf_cap, h->ovf_n, h->ovf_rows, h->ovf_slot, s));
-  if (h->ovf_cap > 0) {
-    const int M = h->ovf_cap < T ? h->ovf_cap : T;
-    TW_TRY(launch_up_dense(bf, x, w1t, b1, M, d_ff, d_model, h->ovf_rows, h->ovf_n, h->ovf_dense,
-                           h->val_dtype == TWELL_BF16, 1, s));
-  }
-  TW_TRY(launch_twell_down(in_of(h), w2, bf, d_model, y, y_dtype == TWELL_BF16, s));
+  st = up_gemm(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);
+  if (st) return st;
+  st = up_finish(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);
+  if (st || T == 0) return st;
+  TW_TRY(launch_twell_down(in_of(h), w2, in_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, s));
   return TWELL_OK;
 }
 
@@ -171,7 +211,7 @@ int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t i
   if (st) return st;
   if (!al16(h) || !al4(b1)) return TWELL_ERR_ALIGN;
   if (T == 0) return TWELL_OK;
-  TW_TRY(launch_up_dense(in_dtype == TWELL_BF16, x, w1t, b1, T, d_ff, d_model, nullptr, nullptr, h,
+  TW_TRY(launch_up_dense(in_dtype == TWELL_BF16, x, w1t, b1, T, d_ff, d_model, T, nullptr, nullptr, h,
                          h_dtype == TWELL_BF16, 1, S(stream)));
   return TWELL_OK;
 }

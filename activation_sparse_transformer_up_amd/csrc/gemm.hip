@@ -9,10 +9,13 @@
 // K-contiguous ("NT"). A workgroup computes a BM x BN tile; each wave a WM x WN sub-tile
 // made of 32x32 MFMA blocks with fp32 accumulators in registers.
 //
-// Operand staging: every K step moves 128 bytes of each operand row (64 bf16 or 32 fp32)
-// = 8 chunks of 16 bytes, global -> registers -> LDS, double-buffered (one barrier per
-// step). Chunk c of LDS row r is stored at position c ^ (r & 7) so that the 32 rows an
-// MFMA operand read touches spread over the LDS banks.
+// Operand staging: every K step moves 64 bytes of each operand row (32 bf16 or 16 fp32)
+// = 4 chunks of 16 bytes straight from HBM into LDS (buffer_load ... lds: lane l of a
+// wave writes bytes [16 l, 16 l + 16) of a 1 KB block), through a ring of NS stages, so
+// that NS - 1 K steps of loads are in flight while one is multiplied. Rows past the
+// operand's end and k past K are fetched as zeros by the buffer range check (no
+// branches). Chunk c of LDS row r sits at position c ^ ((r >> 2) & 3): the 16 rows that
+// one quarter-wave reads then start in 16 different bank groups.
 //
 // Accumulation order of one output element depends only on K and the fixed step order,
 // not on the tile shape or the row's position, so every epilogue (TwELL, dense, backup
@@ -29,7 +32,7 @@ template <typename T> struct MfmaOps;
 // bf16: one v_mfma_f32_32x32x16_bf16 per step; lanes 0-31 bring one 16-byte chunk
 // (8 k values), lanes 32-63 the next one.
 template <> struct MfmaOps<uint16_t> {
-  static constexpr int KPT = 64;   // k values per 128-byte row
+  static constexpr int KPT = 32;   // k values per 64-byte row
   static TW_DEV void step(f32x16_t &acc, u32x4_t a, u32x4_t b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a),
                                                   __builtin_bit_cast(bf16x8_t, b), acc, 0, 0, 0);
@@ -39,7 +42,7 @@ template <> struct MfmaOps<uint16_t> {
 // fp32: a 16-byte chunk holds 4 k values; four v_mfma_f32_32x32x2_f32 consume them, lane
 // half h bringing k = 4h + s in the s-th one (A and B use the same assignment).
 template <> struct MfmaOps<float> {
-  static constexpr int KPT = 32;
+  static constexpr int KPT = 16;
   static TW_DEV void step(f32x16_t &acc, u32x4_t a, u32x4_t b) {
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.x), __uint_as_float(b.x), acc, 0, 0, 0);
     acc = __builtin_amdgcn_mfma_f32_32x32x2f32(__uint_as_float(a.y), __uint_as_float(b.y), acc, 0, 0, 0);
@@ -53,10 +56,15 @@ struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32;
-  static constexpr int CH_A = BM * 8 / NT, CH_B = BN * 8 / NT;   // 16-byte chunks / thread
-  static constexpr int LDS_A = BM * 128, LDS_B = BN * 128;
-  static constexpr int LDS_BYTES = 2 * (LDS_A + LDS_B);
-  static_assert(CH_A >= 1 && CH_B >= 1 && (BM * 8) % NT == 0 && (BN * 8) % NT == 0, "tile");
+  static constexpr int RB = 64;                           // bytes of a row per K step
+  static constexpr int NS = 4;                            // pipeline stages
+  static constexpr int STAGE = (BM + BN) * RB;            // bytes per stage (A rows, then B rows)
+  static constexpr int LDS_BYTES = NS * STAGE;
+  static constexpr int LPW = (BM + BN) / 16 / NW;         // 1 KB wave-loads per wave per stage
+  static constexpr int EPI_WAVE = 34816;                  // TwELL epilogue LDS per wave
+  static constexpr int EPI_BYTES = NW * EPI_WAVE;
+  static constexpr int SMEM = LDS_BYTES > EPI_BYTES ? LDS_BYTES : EPI_BYTES;
+  static_assert((BM + BN) % (16 * NW) == 0 && BM % 16 == 0, "tile");
 };
 
 // Large tiles for many tokens, small tiles for few. Waves are 128 columns wide in the
@@ -65,77 +73,92 @@ struct Tile {
 typedef Tile<256, 256, 128, 128> TileL;
 typedef Tile<64, 128, 32, 128> TileS;
 
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
+template <int N> TW_DEV void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt");
+  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
+TW_DEV void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // A operand row r of the tile reads global row arow[m0 + r] (if arow) or m0 + r; rows at or
-// beyond a_rows are zero. B operand rows at or beyond b_rows are zero.
+// beyond a_rows are zero. B operand rows at or beyond b_rows are zero. a_total rows exist
+// in A (bounds of the buffer resource). Operands must be smaller than 2 GiB.
 template <typename T, class G>
-TW_DEV void mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, int a_rows,
+TW_DEV void mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, int a_rows, int a_total,
                      const T *__restrict__ B, int b_rows, int K, int m0, int n0,
                      f32x16_t (&acc)[G::MB][G::NB], char *smem) {
-  constexpr int EPC = 16 / sizeof(T);
-  constexpr int KPT = MfmaOps<T>::KPT;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  constexpr int EPC = 16 / sizeof(T);                     // elements per 16-byte chunk
+  constexpr int KPT = G::RB / sizeof(T);                  // k per stage
+  constexpr uint32_t OOB = 0x80000000u;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / G::NWN, wn = wave % G::NWN;
-  const int cth = tid & 7;                     // this thread's chunk column (NT % 8 == 0)
+  const size_t row_bytes = (size_t)K * sizeof(T);
+  const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)A, (short)0, (int)((size_t)a_total * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)B, (short)0, (int)((size_t)b_rows * row_bytes), 0x00020000);
 
-  const T *pa[G::CH_A];
-  const T *pb[G::CH_B];
-  int oa[G::CH_A], ob[G::CH_B];
-  bool va[G::CH_A], vb[G::CH_B];
+  // This lane's part of each of its wave-loads: LDS row lr16 = l / 4 of a 16-row block,
+  // physical chunk l % 4 holding logical chunk c.
+  const int lrow = lane >> 2;
+  const int cl = (lane & 3) ^ ((lrow >> 2) & 3);
+  uint32_t voff[G::LPW];
+  bool isA[G::LPW];
+  int ldsq[G::LPW];
 #pragma unroll
-  for (int i = 0; i < G::CH_A; ++i) {
-    const int q = tid + i * G::NT, r = q >> 3;
-    const int gr = m0 + r;
-    va[i] = gr < a_rows;
-    const size_t row = va[i] ? (size_t)(arow ? arow[gr] : gr) : 0;
-    pa[i] = A + row * (size_t)K + cth * EPC;
-    oa[i] = r * 128 + ((cth ^ (r & 7)) << 4);
+  for (int i = 0; i < G::LPW; ++i) {
+    const int q = wave + G::NW * i;                       // 16-row block of [A rows; B rows]
+    const int r = q * 16 + lrow;
+    ldsq[i] = q * 1024;
+    isA[i] = q * 16 < G::BM;                              // wave-uniform
+    if (isA[i]) {
+      const int gr = m0 + r;
+      voff[i] = gr < a_rows ? (uint32_t)((size_t)(arow ? arow[gr] : gr) * row_bytes) + cl * 16 : OOB;
+    } else {
+      const int gr = n0 + (r - G::BM);
+      voff[i] = gr < b_rows ? (uint32_t)((size_t)gr * row_bytes) + cl * 16 : OOB;
+    }
   }
-#pragma unroll
-  for (int i = 0; i < G::CH_B; ++i) {
-    const int q = tid + i * G::NT, r = q >> 3;
-    const int gr = n0 + r;
-    vb[i] = gr < b_rows;
-    pb[i] = B + (size_t)(vb[i] ? gr : 0) * (size_t)K + cth * EPC;
-    ob[i] = r * 128 + ((cth ^ (r & 7)) << 4);
-  }
-
-  u32x4_t ra[G::CH_A], rb[G::CH_B];
   const int nk = (K + KPT - 1) / KPT;
-  auto gload = [&](int kt) {
+  const int kc = cl * EPC;                                // this lane's k offset in a stage
+
+  auto issue = [&](int kt) {
     const int k0 = kt * KPT;
-    const bool kin = k0 + cth * EPC < K;
+    char *st = smem + (kt % G::NS) * G::STAGE;
+    const bool kin = k0 + kc < K;
 #pragma unroll
-    for (int i = 0; i < G::CH_A; ++i)
-      ra[i] = (va[i] && kin) ? *(const u32x4_t *)(pa[i] + k0) : u32x4_t{0, 0, 0, 0};
-#pragma unroll
-    for (int i = 0; i < G::CH_B; ++i)
-      rb[i] = (vb[i] && kin) ? *(const u32x4_t *)(pb[i] + k0) : u32x4_t{0, 0, 0, 0};
-  };
-  auto sstore = [&](int buf) {
-    char *sa = smem + buf * (G::LDS_A + G::LDS_B);
-    char *sb = sa + G::LDS_A;
-#pragma unroll
-    for (int i = 0; i < G::CH_A; ++i) *(u32x4_t *)(sa + oa[i]) = ra[i];
-#pragma unroll
-    for (int i = 0; i < G::CH_B; ++i) *(u32x4_t *)(sb + ob[i]) = rb[i];
+    for (int i = 0; i < G::LPW; ++i) {
+      const uint32_t vo = kin ? voff[i] : OOB;
+      lds_void_t *dst = (lds_void_t *)(st + ldsq[i]);
+      if (isA[i]) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vo, k0 * (int)sizeof(T), 0, 0);
+      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vo, k0 * (int)sizeof(T), 0, 0);
+    }
   };
   const int lr = lane & 31, lh = lane >> 5;
-  auto compute = [&](int buf) {
-    const char *sa = smem + buf * (G::LDS_A + G::LDS_B);
-    const char *sb = sa + G::LDS_A;
+  auto compute = [&](int kt) {
+    const char *sa = smem + (kt % G::NS) * G::STAGE;
+    const char *sb = sa + G::BM * G::RB;
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < 2; ++u) {
       const int c = 2 * u + lh;
       u32x4_t a[G::MB], b[G::NB];
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb) {
         const int r = wm * G::WM + mb * 32 + lr;
-        a[mb] = *(const u32x4_t *)(sa + r * 128 + ((c ^ (r & 7)) << 4));
+        a[mb] = *(const u32x4_t *)(sa + r * G::RB + ((c ^ ((r >> 2) & 3)) << 4));
       }
 #pragma unroll
       for (int nb = 0; nb < G::NB; ++nb) {
         const int r = wn * G::WN + nb * 32 + lr;
-        b[nb] = *(const u32x4_t *)(sb + r * 128 + ((c ^ (r & 7)) << 4));
+        b[nb] = *(const u32x4_t *)(sb + r * G::RB + ((c ^ ((r >> 2) & 3)) << 4));
       }
 #pragma unroll
       for (int mb = 0; mb < G::MB; ++mb)
@@ -144,14 +167,15 @@ TW_DEV void mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, 
     }
   };
 
-  gload(0);
-  sstore(0);
-  __syncthreads();
+#pragma unroll
+  for (int s = 0; s < G::NS - 1; ++s)
+    if (s < nk) issue(s);
   for (int kt = 0; kt < nk; ++kt) {
-    if (kt + 1 < nk) gload(kt + 1);
-    compute(kt & 1);
-    if (kt + 1 < nk) sstore((kt + 1) & 1);
-    __syncthreads();
+    if (kt + G::NS - 2 < nk) wait_vmcnt<(G::NS - 2) * G::LPW>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (kt + G::NS - 1 < nk) issue(kt + G::NS - 1);
+    compute(kt);
   }
 }
 
@@ -165,78 +189,123 @@ TW_DEV int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
 // the row 4 below), the popcount is the count, and a lane's slot is the number of set
 // bits of lower columns. Slots below S receive (column, value); the rest are padded.
 // A row-tile with count > S sets its row's bit in ovf_bits[tile][row / 32].
-template <class G, int W>
-TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float *__restrict__ b1, int M, int N,
-                      int m0, int n0, const TwellOut &o) {
+//
+// At one wave per SIMD every instruction costs a full issue slot and scalar<->vector
+// dependencies stall, so the work per 32-column block is a handful of independent vector
+// operations: the lane's half of the ballot, a popcount of the lower bits (slot) and of
+// all bits (running count). Per 32-row block the wave fills its LDS copy of the slot
+// blocks with the pad pattern, writes the active (column, value) pairs into their slots
+// (lanes with nothing to write hit a private junk word, so no branches), and copies the
+// block out with 16-byte stores. Blocks whose ballot is empty are skipped (a scalar test).
+template <class G, int W, typename VT>
+TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB], int M, int N,
+                      int m0, int n0, const TwellOut &o, char *smem) {
   constexpr int BPT = W / 32;                   // 32-column blocks per TwELL tile
   constexpr int TPW = G::WN / W;                // TwELL tiles per wave
   static_assert(G::WN % W == 0, "a TwELL tile must sit inside one wave");
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int wm = wave / G::NWN, wn = wave % G::NWN;
   const int lh = lane >> 5, li = lane & 31;
   const int row0 = m0 + wm * G::WM, col0 = n0 + wn * G::WN;
-  const uint32_t below = (1u << li) - 1u;
   const int S = o.S;
-  float bias[G::NB];
+  const int kt0 = col0 / W;
+  const int tiles = min(TPW, o.n_t - kt0);      // tiles of this wave inside the matrix
+  if (tiles <= 0) return;
+  const int RS = TPW * S;                        // LDS slots per row (all tiles of the wave)
+  // wave-private LDS (<= 32 KB): idx [32][RS] + junk[64] | vals [32][RS] + junk[64] |
+  // counts [32][TPW] + junk[64]
+  char *base = smem + wave * G::EPI_WAVE;
+  int32_t *lidx = (int32_t *)base;
+  VT *lval = (VT *)(lidx + 32 * RS + 64);
+  int32_t *lcnt = (int32_t *)(base + ((4 * (32 * RS + 64) + (int)sizeof(VT) * (32 * RS + 64) + 15) & ~15));
+  const int JI = 32 * RS + lane;                 // this lane's junk element in lidx / lval
+  const uint32_t below = (1u << li) - 1u;
+  const bool vec_ok = (S * (int)sizeof(VT)) % 16 == 0;
 #pragma unroll
-  for (int nb = 0; nb < G::NB; ++nb) {
-    const int col = col0 + nb * 32 + li;
-    bias[nb] = col < N ? b1[col] : 0.f;
-  }
+  for (int mb = 0; mb < G::MB; ++mb) {
+    const int rb0 = row0 + mb * 32;
+    if (rb0 >= M) break;                         // wave-uniform
+    // 1. pad pattern
+    for (int i = lane; i < 32 * RS / 4; i += 64) ((int4 *)lidx)[i] = make_int4(-1, -1, -1, -1);
+    for (int i = lane; i < 32 * RS * (int)sizeof(VT) / 16; i += 64) ((int4 *)lval)[i] = make_int4(0, 0, 0, 0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 2. active units -> slots
+    uint32_t ovfv[TPW];                          // rows of this lane's half that overflow
 #pragma unroll
-  for (int q = 0; q < TPW; ++q) {
-    const int kt = col0 / W + q;
-    if (kt * W >= N) break;
+    for (int q = 0; q < TPW; ++q) ovfv[q] = 0;
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb) {
-      uint32_t ovf_word = 0;
+    for (int q = 0; q < TPW; ++q) {
+      const int kt = kt0 + q;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const int row = row0 + mb * 32 + acc_row(r, lh);
-        const bool rv = row < M;
-        float v[BPT];
-        uint32_t hm[BPT];
-        int pre[BPT];
-        int cnt = 0;
+        const int lrow = 8 * (r >> 2) + (r & 3) + 4 * lh;    // row of this lane in the block
+        int pre = 0;                                          // this lane's row: count so far
 #pragma unroll
         for (int b = 0; b < BPT; ++b) {
           const int nb = q * BPT + b;
-          const float z = acc[mb][nb][r] + bias[nb];
-          v[b] = z;
-          const uint64_t bal = ballot64(z > 0.f);
-          hm[b] = lh ? (uint32_t)(bal >> 32) : (uint32_t)bal;
-          pre[b] = cnt;
-          cnt += __popc(hm[b]);
+          const float zb = acc[mb][nb][r];
+          const bool on = zb > nbias[nb];
+          const uint64_t bal = ballot64(on);
+          if (bal == 0) continue;                             // wave-uniform
+          const uint32_t hm = lh ? (uint32_t)(bal >> 32) : (uint32_t)bal;
+          const int slot = pre + __popc(hm & below);
+          const bool act = on && slot < S;
+          const int e = act ? lrow * RS + q * S + slot : JI;
+          lidx[e] = kt * W + b * 32 + li;
+          Elem<VT>::store(lval, e, zb - nbias[nb]);
+          pre += __popc(hm);
         }
-        if (rv) {
-          const size_t base = ((size_t)row * o.n_t + kt) * (size_t)S;
-#pragma unroll
-          for (int b = 0; b < BPT; ++b) {
-            const int slot = pre[b] + __popc(hm[b] & below);
-            if (v[b] > 0.f && slot < S) {
-              const int col = kt * W + b * 32 + li;
-              o.col_idx[base + slot] = col;
-              if (o.val_bf16) ((uint16_t *)o.vals)[base + slot] = (uint16_t)f32_to_bf16(v[b]);
-              else ((float *)o.vals)[base + slot] = v[b];
-            }
-          }
-          for (int s = li; s < S; s += 32) {
-            if (s >= cnt) {
-              o.col_idx[base + s] = -1;
-              if (o.val_bf16) ((uint16_t *)o.vals)[base + s] = 0;
-              else ((float *)o.vals)[base + s] = 0.f;
-            }
-          }
-          if (li == 0) o.counts[(size_t)row * o.n_t + kt] = cnt;
-        }
-        const uint64_t ob = ballot64(rv && cnt > S);
-        const int bit = 8 * (r >> 2) + (r & 3);
-        if (ob & 1ull) ovf_word |= 1u << bit;
-        if ((ob >> 32) & 1ull) ovf_word |= 1u << (bit + 4);
+        const int e = li == 0 ? lrow * TPW + q : 32 * TPW + lane;
+        lcnt[e] = pre;
+        ovfv[q] |= (pre > S ? 1u : 0u) << lrow;
       }
-      const int w = (row0 + mb * 32) >> 5;
-      if (lane == 0 && w < o.words) o.ovf_bits[(size_t)kt * o.words + w] = ovf_word;
     }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    // 3. copy out rows rb0 .. rb0 + 31: row r's slots of tiles kt0 .. kt0 + tiles - 1 are
+    //    contiguous in the output (tiles * S elements at (row * n_t + kt0) * S)
+    const int nrow = min(32, M - rb0);
+    const int relem = tiles * S;
+    if (vec_ok) {
+      const int ci = relem / 4, cv = relem * (int)sizeof(VT) / 16;   // 16-byte chunks per row
+      for (int i = lane; i < nrow * ci; i += 64) {
+        const int rr = i / ci, c = i - rr * ci;
+        const size_t g = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
+        *(int4 *)(o.col_idx + g + 4 * c) = *(const int4 *)(lidx + rr * RS + 4 * c);
+      }
+      constexpr int EV = 16 / sizeof(VT);
+      for (int i = lane; i < nrow * cv; i += 64) {
+        const int rr = i / cv, c = i - rr * cv;
+        const size_t g = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
+        *(int4 *)((VT *)o.vals + g + EV * c) = *(const int4 *)(lval + rr * RS + EV * c);
+      }
+    } else {
+      for (int i = lane; i < nrow * relem; i += 64) {
+        const int rr = i / relem, c = i - rr * relem;
+        const size_t g = ((size_t)(rb0 + rr) * o.n_t + kt0) * S + c;
+        o.col_idx[g] = lidx[rr * RS + c];
+        ((VT *)o.vals)[g] = lval[rr * RS + c];
+      }
+    }
+    for (int i = lane; i < nrow * tiles; i += 64) {
+      const int rr = i / tiles, c = i - rr * tiles;
+      o.counts[(size_t)(rb0 + rr) * o.n_t + kt0 + c] = lcnt[rr * TPW + c];
+    }
+    // overflow words: lanes 0 / 32 hold the bits of rows 8i+{0..3} / 8i+{4..7}
+    const uint32_t valid = nrow >= 32 ? 0xFFFFFFFFu : ((1u << nrow) - 1u);
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)ovfv[q], 0) |
+                            (uint32_t)__builtin_amdgcn_readlane((int)ovfv[q], 32);
+      if (q < tiles && lane == 0) o.ovf_bits[(size_t)(kt0 + q) * o.words + (rb0 >> 5)] = word & valid;
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   }
 }
 
@@ -272,26 +341,37 @@ TW_DEV void epi_dense(f32x16_t (&acc)[G::MB][G::NB], const float *__restrict__ b
 
 // ------------------------------------------------------------------------ kernels
 
-template <typename T, class G, int W>
+template <typename T, class G, int W, typename VT>
 __global__ __launch_bounds__(G::NT) void k_up_twell(const T *__restrict__ x, const T *__restrict__ w1t,
                                                     const float *__restrict__ b1, int M, int N, int K,
                                                     TwellOut o) {
-  __shared__ __attribute__((aligned(16))) char smem[G::LDS_BYTES];
+  __shared__ __attribute__((aligned(16))) char smem[G::SMEM];
   const int n0 = blockIdx.x * G::BN, m0 = blockIdx.y * G::BM;
+  // -b1 of this lane's columns, fetched before the K loop so its latency is hidden
+  float nbias[G::NB];
+  {
+    const int wn = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % G::NWN;
+#pragma unroll
+    for (int nb = 0; nb < G::NB; ++nb) {
+      const int col = n0 + wn * G::WN + nb * 32 + (threadIdx.x & 31);
+      nbias[nb] = col < N ? -b1[col] : 0.f;
+    }
+  }
   f32x16_t acc[G::MB][G::NB];
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x16_t{};
-  mainloop<T, G>(x, nullptr, M, w1t, N, K, m0, n0, acc, smem);
-  epi_twell<G, W>(acc, b1, M, N, m0, n0, o);
+  mainloop<T, G>(x, nullptr, M, M, w1t, N, K, m0, n0, acc, smem);
+  block_barrier();                      // every wave is done reading the operand stages
+  epi_twell<G, W, VT>(acc, nbias, M, N, m0, n0, o, smem);
 }
 
 // Dense ReLU(x W1 + b1). With arow != NULL the A rows are gathered: tile row i reads x row
 // arow[i] for i < min(*n_rows_dev, M) (the overflow rows of a TwELL), and writes out row i.
 template <typename T, class G>
 __global__ __launch_bounds__(G::NT) void k_up_dense(const T *__restrict__ x, const T *__restrict__ w1t,
-                                                    const float *__restrict__ b1, int M, int N, int K,
+                                                    const float *__restrict__ b1, int M, int N, int K, int x_rows,
                                                     const int32_t *__restrict__ arow,
                                                     const int32_t *__restrict__ n_rows_dev, void *out,
                                                     int out_bf16, int relu) {
@@ -305,7 +385,7 @@ __global__ __launch_bounds__(G::NT) void k_up_dense(const T *__restrict__ x, con
   for (int mb = 0; mb < G::MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x16_t{};
-  mainloop<T, G>(x, arow, rows, w1t, N, K, m0, n0, acc, smem);
+  mainloop<T, G>(x, arow, rows, x_rows, w1t, N, K, m0, n0, acc, smem);
   epi_dense<G>(acc, b1, rows, N, m0, n0, out, out_bf16, relu);
 }
 
@@ -315,8 +395,13 @@ template <typename T, class G>
 static hipError_t launch_twell_t(const T *x, const T *w1t, const float *b1, int M, int N, int K,
                                  const TwellOut &o, int W, hipStream_t s) {
   dim3 grid((N + G::BN - 1) / G::BN, (M + G::BM - 1) / G::BM);
-  if (W == 64) hipLaunchKernelGGL((k_up_twell<T, G, 64>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, o);
-  else hipLaunchKernelGGL((k_up_twell<T, G, 128>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, o);
+  if (o.val_bf16) {
+    if (W == 64) hipLaunchKernelGGL((k_up_twell<T, G, 64, uint16_t>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, o);
+    else hipLaunchKernelGGL((k_up_twell<T, G, 128, uint16_t>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, o);
+  } else {
+    if (W == 64) hipLaunchKernelGGL((k_up_twell<T, G, 64, float>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, o);
+    else hipLaunchKernelGGL((k_up_twell<T, G, 128, float>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, o);
+  }
   return hipGetLastError();
 }
 
@@ -333,26 +418,26 @@ hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float
 }
 
 template <typename T, class G>
-static hipError_t launch_dense_t(const T *x, const T *w1t, const float *b1, int M, int N, int K,
+static hipError_t launch_dense_t(const T *x, const T *w1t, const float *b1, int M, int N, int K, int x_rows,
                                  const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16,
                                  int relu, hipStream_t s) {
   dim3 grid((N + G::BN - 1) / G::BN, (M + G::BM - 1) / G::BM);
-  hipLaunchKernelGGL((k_up_dense<T, G>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev,
+  hipLaunchKernelGGL((k_up_dense<T, G>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, x_rows, arow, n_rows_dev,
                      out, out_bf16, relu);
   return hipGetLastError();
 }
 
 hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
-                           const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16,
+                           int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16,
                            int relu, hipStream_t s) {
   if (bf16) {
     if (use_large(M, N) && !arow)
-      return launch_dense_t<uint16_t, TileL>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, arow,
+      return launch_dense_t<uint16_t, TileL>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
                                              n_rows_dev, out, out_bf16, relu, s);
-    return launch_dense_t<uint16_t, TileS>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, arow,
+    return launch_dense_t<uint16_t, TileS>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
                                            n_rows_dev, out, out_bf16, relu, s);
   }
-  return launch_dense_t<float, TileS>((const float *)x, (const float *)w1t, b1, M, N, K, arow, n_rows_dev,
+  return launch_dense_t<float, TileS>((const float *)x, (const float *)w1t, b1, M, N, K, x_rows, arow, n_rows_dev,
                                       out, out_bf16, relu, s);
 }
 

@@ -30,7 +30,7 @@ struct TwellIn {
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
                            const TwellOut &o, int W, hipStream_t s);
 hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
-                           const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
+                           int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
                            hipStream_t s);
 
 // pack.hip

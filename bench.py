@@ -1,0 +1,189 @@
+"""Benchmark of the activation-sparse (TwELL) FFN forward on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload c2]
+
+A step is one twell_ffn_fwd over one batch of synthetic tokens (the up-projection GEMM
+with the fused ReLU + TwELL epilogue, the overflow bookkeeping, and the sparse down
+projection), enqueued as its three stages with a HIP event after the GEMM so that the
+GEMM's own duration is measured on the stream it runs on. Inputs are resident in HBM
+before timing starts. Prints one JSON line.
+
+Baselines measured in the same run: a dense bf16 FFN (torch, hipBLASLt) on the same GPU
+and shapes, and the CPU oracle on the host cores (a bounded sample of the workload).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3       # MI355X fp32 MFMA / packed VALU
+PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="c2", choices=["c1", "c2", "c3"])
+    ap.add_argument("--T", type=int, default=None, help="override token count (c3: 1, 8 or 64)")
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-dense", action="store_true")
+    ap.add_argument("--ovf-cap", type=int, default=64)
+    return ap.parse_args()
+
+
+def cpu_baseline(g, w, T_sample: int, min_seconds: float = 10.0) -> dict:
+    """Time the oracle forward (fp64 numpy) on the first T_sample tokens, repeated until
+    about min_seconds of CPU work has been done."""
+    import numpy as np
+    from oracle import twell_oracle as orc
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        threads = os.cpu_count() or 1
+    dt = g["dtype"]
+    x = orc.widen(g["x"][:T_sample], dt)
+    w1t = orc.widen(g["w1t"], dt)
+    w2 = orc.widen(g["w2"], dt)
+    b1 = g["b1"].astype(np.float64)
+    reps, t_total = 0, 0.0
+    while t_total < min_seconds and reps < 50:
+        t0 = time.perf_counter()
+        z, h, y = orc.ffn_fwd(x, w1t, b1, w2)
+        orc.twell_pack(h, w.tile_w, w.slots, T_sample)
+        t_total += time.perf_counter() - t0
+        reps += 1
+    return {"value": T_sample * reps / t_total, "unit": "tokens/s", "cores": int(threads),
+            "kind": "oracle",
+            "sample": f"{T_sample} tokens of the {w.name} workload x {reps} repetitions "
+                      f"(fp64 numpy forward + TwELL pack, {t_total:.1f} s)"}
+
+
+def warm(fn, steps: int, min_seconds: float = 0.5):
+    """W untimed steps, continued until at least min_seconds have passed: the GPU's clocks
+    take several milliseconds of sustained load to settle, and kernels timed before that
+    read up to 20 % slow."""
+    import torch
+    t0 = time.perf_counter()
+    n = 0
+    while n < steps or time.perf_counter() - t0 < min_seconds:
+        fn()
+        n += 1
+        if n % 16 == 0:
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()
+
+
+def main():
+    a = parse()
+    if a.gpus != 1:
+        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+                          "n_gpus": a.gpus}))
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+
+    w = synth.WORKLOADS[a.workload]
+    T = a.T or w.T
+    g = synth.generate(w, T=T)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    def up(arr, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+    x, w1t, w2 = up(g["x"], w.dtype), up(g["w1t"], w.dtype), up(g["w2"], w.dtype)
+    b1 = up(g["b1"], "f32")
+    d, f = w.d, w.f
+    h = tw.TwellMatrix(T, f, w.tile_w, w.slots, a.ovf_cap, torch.float32, dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+
+    def step(ev=None):
+        tw.twell_up_gemm(x, w1t, b1, h)
+        if ev is not None:
+            ev.record()
+        tw.twell_up_finish(x, w1t, b1, h)
+        tw.twell_down(h, w2, y=y)
+
+    warm(step, a.warmup)
+    E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
+    starts = [E() for _ in range(a.steps)]
+    gemm_end = [E() for _ in range(a.steps)]
+    t0, t1 = E(), E()
+    torch.cuda.synchronize()
+    t0.record()
+    for i in range(a.steps):
+        starts[i].record()
+        step(gemm_end[i])
+    t1.record()
+    torch.cuda.synchronize()
+    ms = t0.elapsed_time(t1) / a.steps
+    gemm_ms = sum(s.elapsed_time(e) for s, e in zip(starts, gemm_end)) / a.steps
+    nnz = int(h.counts.clamp(max=w.slots).sum().item())
+    ovf_n = int(h.ovf_n.item())
+
+    # the monolithic entry point, same work (sanity: equal time within noise)
+    for _ in range(3):
+        tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, a.ovf_cap, h=h, y=y)
+    torch.cuda.synchronize()
+    t0.record()
+    for _ in range(a.steps):
+        tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, a.ovf_cap, h=h, y=y)
+    t1.record()
+    torch.cuda.synchronize()
+    ms_mono = t0.elapsed_time(t1) / a.steps
+
+    flops_up = 2.0 * T * d * f
+    peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
+    achieved = flops_up / (gemm_ms * 1e-3) / 1e12
+    out = {
+        "metric": "FFN tokens/sec at 1% density (TwELL forward), speedup vs dense bf16, % MFMA peak",
+        "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
+        "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded generator, random-init weights)",
+        "config": {"workload": w.name, "T": T, "d_model": d, "d_ff": f, "tile_w": w.tile_w,
+                   "slots": w.slots, "bias": w.bias, "seed": w.seed, "parallelism": "single GPU"},
+        "roofline": {"kernel": "k_up_twell (up GEMM + fused ReLU/TwELL epilogue)", "bound": "mfma",
+                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+                     "traffic": None, "per_launch_flop": flops_up, "avg_launch_ms": gemm_ms},
+        "measured_density": nnz / (T * f), "ovf_rows": ovf_n, "ms_per_step_monolithic": ms_mono,
+    }
+
+    if not a.no_dense:
+        xb, w1b, w2b = x, w1t, w2
+        bb = b1.to(x.dtype)
+
+        def dense():
+            return torch.relu(torch.addmm(bb, xb, w1b.t())) @ w2b
+        warm(dense, a.warmup)
+        t0.record()
+        for _ in range(a.steps):
+            dense()
+        t1.record()
+        torch.cuda.synchronize()
+        dms = t0.elapsed_time(t1) / a.steps
+        out["dense_baseline"] = {"value": T / (dms * 1e-3), "unit": "tokens/s", "ms_per_step": dms,
+                                 "impl": f"torch relu(addmm) @ w2 in {w.dtype} (hipBLASLt)"}
+        out["speedup_vs_dense"] = dms / ms
+
+    if not a.no_cpu:
+        out["cpu_baseline"] = cpu_baseline(g, w, T_sample=min(T, 4096))
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -127,6 +127,22 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
                   twell_matrix_t *h_out, void *y, int32_t y_dtype, void *stream);
 
 /*
+ * Stages of twell_ffn_fwd, callable one by one (twell_ffn_fwd enqueues exactly
+ * twell_up_gemm, twell_up_finish, twell_down, in that order, on its stream):
+ *   twell_up_gemm   — the up-projection MFMA GEMM with the fused bias + ReLU + TwELL
+ *                     epilogue: writes counts, col_idx, vals and ovf_bits only.
+ *   twell_up_finish — the overflow bookkeeping ("Formato Híbrido para Treinamento"): the
+ *                     ordered overflow list, ovf_slot, *ovf_n, and ovf_dense recomputed by
+ *                     the same GEMM for the listed rows. Must follow twell_up_gemm on the
+ *                     same h. After both, h is the complete TwELL of ReLU(x W1 + b1).
+ * Same arguments, checks and errors as twell_ffn_fwd.
+ */
+int twell_up_gemm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                  int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream);
+int twell_up_finish(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                    int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream);
+
+/*
  * twell_down — y[t] = sum over the nonzero h[t, j] of h[t, j] * w2[j] for an existing
  * TwELL h (rows = T, cols = d_ff; ovf_slot must be valid), fp32 accumulation.
  * "Kernels de Inferência": only the active units' rows of W2 are read.
