@@ -217,30 +217,68 @@ int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t i
 }
 
 size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, const twell_matrix_t *h) {
-  (void)T; (void)d_model; (void)d_ff; (void)h;
-  return 0;
+  if (!h || T < 0 || d_model <= 0 || d_ff <= 0 || h->tile_w <= 0 || h->slots <= 0 || h->ovf_cap < 0) return 0;
+  return bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap);
 }
 
 int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dtype, int32_t T,
                   int32_t d_model, int32_t d_ff, const twell_matrix_t *h, const void *dy, float l1_coef,
                   float *dx, float *dw1t, float *dw2, float *db1, void *workspace, size_t workspace_bytes,
                   void *stream) {
-  (void)x; (void)w1t; (void)w2; (void)in_dtype; (void)T; (void)d_model; (void)d_ff; (void)h; (void)dy;
-  (void)l1_coef; (void)dx; (void)dw1t; (void)dw2; (void)db1; (void)workspace; (void)workspace_bytes; (void)stream;
-  return TWELL_ERR_UNSUPPORTED;
+  if (!h || !w2 || !dw1t || !dw2 || !workspace) return TWELL_ERR_ARG;
+  if (T > 0 && (!dy || !dx)) return TWELL_ERR_ARG;
+  int st = check_ffn_args(x, w1t, w2, in_dtype, T, d_model, d_ff);
+  if (st) return st;
+  st = check_matrix(h, false);
+  if (st) return st;
+  if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
+  if (!al16(dy) || !al16(dx) || !al16(dw1t) || !al16(dw2) || !al4(db1) || !al16(workspace)) return TWELL_ERR_ALIGN;
+  // dy lives in registers (<= 16 chunks of 16 bytes per lane); unit masks of a 32-token
+  // block live in LDS (4 bytes per unit)
+  if (d_model > (in_dtype == TWELL_BF16 ? 8192 : 4096) || d_ff > 16384) return TWELL_ERR_UNSUPPORTED;
+  const size_t need = bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap);
+  if (workspace_bytes < need) return TWELL_ERR_WORKSPACE;
+  BwdArgs a;
+  a.h = in_of(h);
+  a.x = x; a.w1t = w1t; a.w2 = w2; a.dy = dy;
+  a.l1 = l1_coef;
+  a.dx = dx; a.dw1t = dw1t; a.dw2 = dw2; a.db1 = db1;
+  a.ws = workspace;
+  a.d = d_model;
+  a.bf16 = in_dtype == TWELL_BF16;
+  a.cap = h->ovf_cap;
+  TW_TRY(launch_bwd(a, S(stream)));
+  return TWELL_OK;
 }
 
 int nm_prune(const void *h, int32_t dtype, int32_t T, int32_t d_ff, int32_t n, int32_t m, void *vals,
              uint8_t *idx, void *stream) {
-  (void)h; (void)dtype; (void)T; (void)d_ff; (void)n; (void)m; (void)vals; (void)idx; (void)stream;
-  return TWELL_ERR_UNSUPPORTED;
+  if ((T > 0 && (!h || !vals || !idx))) return TWELL_ERR_ARG;
+  if (!dtype_ok(dtype)) return TWELL_ERR_ARG;
+  if (T < 0 || d_ff <= 0) return TWELL_ERR_SHAPE;
+  if (!((n == 2 && m == 4) || (n == 4 && m == 8) || (n == 8 && m == 16) || (n == 16 && m == 32)))
+    return TWELL_ERR_SHAPE;
+  if (d_ff % m) return TWELL_ERR_SHAPE;
+  if (!al16(h) || !al16(vals) || !al16(idx)) return TWELL_ERR_ALIGN;
+  TW_TRY(launch_nm_prune(h, dtype == TWELL_BF16, T, d_ff, n, m, vals, idx, S(stream)));
+  return TWELL_OK;
 }
 
 int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, int32_t d_ff, int32_t n,
                 int32_t m, const void *w2t, int32_t d_model, void *y, int32_t y_dtype, void *stream) {
-  (void)vals; (void)idx; (void)dtype; (void)T; (void)d_ff; (void)n; (void)m; (void)w2t; (void)d_model;
-  (void)y; (void)y_dtype; (void)stream;
-  return TWELL_ERR_UNSUPPORTED;
+  if (!w2t || (T > 0 && (!vals || !idx || !y))) return TWELL_ERR_ARG;
+  if (!dtype_ok(dtype) || !dtype_ok(y_dtype)) return TWELL_ERR_ARG;
+  if (T < 0 || d_ff <= 0 || d_model <= 0) return TWELL_ERR_SHAPE;
+  if (!((n == 8 && m == 16) || (n == 16 && m == 32))) {
+    if ((n == 2 && m == 4) || (n == 4 && m == 8)) return TWELL_ERR_UNSUPPORTED;
+    return TWELL_ERR_SHAPE;
+  }
+  if (dtype != TWELL_BF16) return TWELL_ERR_UNSUPPORTED;
+  if (d_ff % 32) return TWELL_ERR_SHAPE;
+  if (!al16(vals) || !al16(idx) || !al16(w2t) || !al16(y)) return TWELL_ERR_ALIGN;
+  if ((size_t)d_model * d_ff * 2 >= ((size_t)1 << 31)) return TWELL_ERR_UNSUPPORTED;
+  TW_TRY(launch_nm_down(vals, idx, T, d_ff, n, m, w2t, d_model, y, y_dtype == TWELL_BF16, S(stream)));
+  return TWELL_OK;
 }
 
 int twell_sync_status(const twell_matrix_t *h, void *stream) {

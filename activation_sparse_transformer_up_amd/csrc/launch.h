@@ -41,6 +41,24 @@ hipError_t launch_ovf_copy(const void *h, int h_bf16, int R, int C, const int32_
                            int cap, void *dense, int dense_bf16, hipStream_t s);
 hipError_t launch_set_int(int32_t *p, int v, hipStream_t s);
 
+// bwd.hip
+struct BwdArgs {
+  TwellIn h;
+  const void *x, *w1t, *w2, *dy;
+  float l1;
+  float *dx, *dw1t, *dw2, *db1;
+  void *ws;
+  int d, bf16, cap;
+};
+size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap);
+hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
+
+// nm.hip
+hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, void *vals, uint8_t *idx,
+                           hipStream_t s);
+hipError_t launch_nm_down(const void *vals, const uint8_t *idx, int T, int f, int n, int m, const void *w2t, int d,
+                          void *y, int y_bf16, hipStream_t s);
+
 // down.hip
 hipError_t launch_twell_down(const TwellIn &h, const void *w2, int w_bf16, int d, void *y, int y_bf16,
                              hipStream_t s);

@@ -1,0 +1,133 @@
+"""GPU parity of the backward pass (SDDMM dz on the pattern, dx, dW1t, dW2, db1 with the L1
+term) against the oracle's backward, through the C ABI."""
+import sys
+
+import numpy as np
+import pytest
+
+import synth
+from oracle import twell_oracle as orc
+from tests.helpers import from_dev, inputs64, rel_err, to_dev, twell_host
+
+pytestmark = pytest.mark.gpu
+
+torch = pytest.importorskip("torch")
+if not torch.cuda.is_available():
+    pytest.skip("no GPU", allow_module_level=True)
+
+import activation_sparse_transformer_up_amd as tw  # noqa: E402
+
+TOL = {"f32": 1e-5, "bf16": 2e-3}
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def run(g, W, S, cap, lam, val_dtype=torch.float32):
+    dt = g["dtype"]
+    x, w1t, b1, w2 = (to_dev(g["x"], dt), to_dev(g["w1t"], dt), to_dev(g["b1"], "f32"), to_dev(g["w2"], dt))
+    dy = to_dev(g["dy"], dt)
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, cap, val_dtype)
+    dx, dw1t, dw2, db1 = tw.twell_ffn_bwd(x, w1t, w2, h, dy, lam)
+    torch.cuda.synchronize()
+    return h, [from_dev(t) for t in (dx, dw1t, dw2, db1)]
+
+
+def reference(g, h, lam):
+    """Oracle backward on the GPU's own sparsity pattern (the forward's TwELL unpacked)."""
+    xr, w1r, b1r, w2r, dyr = inputs64(g)
+    host = twell_host(h)
+    h64 = orc.twell_unpack(host)
+    return orc.ffn_bwd(xr, w1r, w2r, dyr, lam, h64), h64, (xr, w1r, b1r)
+
+
+@pytest.mark.parametrize("T,d,f,W,S,dt", [(100, 128, 512, 128, 4, "bf16"), (64, 64, 256, 64, 2, "f32"),
+                                          (257, 256, 1024, 128, 8, "bf16")])
+@pytest.mark.parametrize("lam", [0.0, 2.0 ** -10])
+def test_bwd_integer_grid_exact(T, d, f, W, S, dt, lam):
+    say("bwd grid", T, d, f, W, S, dt, lam)
+    g = synth.integer_grid(T, d, f, seed=7 * T + d, dtype=dt, active=0.05)
+    h, got = run(g, W, S, T, lam)
+    ref, h64, (xr, w1r, b1r) = reference(g, h, lam)
+    # on the grid the GPU pattern is the oracle's own
+    assert np.array_equal(h64, orc.relu(orc.preact(xr, w1r, b1r)))
+    assert host_has_overflow(h) or S >= 8
+    for name, a, b in zip(["dx", "dw1t", "dw2", "db1"], got, [ref["dx"], ref["dw1t"], ref["dw2"], ref["db1"]]):
+        assert np.array_equal(a, b), name
+
+
+def host_has_overflow(h):
+    return int(h.ovf_n.item()) > 0
+
+
+def check_close(got, ref, tol):
+    errs = {}
+    for name, a, b in zip(["dx", "dw1t", "dw2", "db1"], got, [ref["dx"], ref["dw1t"], ref["dw2"], ref["db1"]]):
+        errs[name] = rel_err(a, b)
+        assert errs[name] <= tol, (name, errs[name])
+    return errs
+
+
+def test_bwd_c1_fp32():
+    say("bwd c1")
+    w = synth.C1.with_(with_dy=True)
+    g = synth.generate(w)
+    h, got = run(g, w.tile_w, w.slots, 8, 2e-5)
+    ref, _, _ = reference(g, h, 2e-5)
+    say("c1 errs", check_close(got, ref, TOL["f32"]))
+
+
+@pytest.mark.parametrize("vdt", [torch.float32, torch.bfloat16])
+def test_bwd_c5_shaped_sample(vdt):
+    say("bwd c5 sample", vdt)
+    w = synth.C5.with_(T=512, hot_every=128)
+    g = synth.generate(w)
+    h, got = run(g, w.tile_w, w.slots, 64, w.l1_coef, vdt)
+    assert int(h.ovf_n.item()) >= 4        # hot tokens and skewed units overflow
+    ref, _, _ = reference(g, h, w.l1_coef)
+    say("c5 sample errs", check_close(got, ref, TOL["bf16"]))
+
+
+def test_bwd_deterministic_and_dy_zero():
+    w = synth.C5.with_(T=300, d=256, f=1024)
+    g = synth.generate(w)
+    x, w1t, b1, w2 = (to_dev(g["x"], "bf16"), to_dev(g["w1t"], "bf16"), to_dev(g["b1"], "f32"), to_dev(g["w2"], "bf16"))
+    dy = to_dev(g["dy"], "bf16")
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 8, 32)
+    a = tw.twell_ffn_bwd(x, w1t, w2, h, dy, 2e-5)
+    b = tw.twell_ffn_bwd(x, w1t, w2, h, dy, 2e-5)
+    torch.cuda.synchronize()
+    for u, v in zip(a, b):
+        assert torch.equal(u, v)
+    # dy = 0: dw2 = 0, dw1t[j] = l1 * sum of x over the tokens where unit j is active
+    lam = 0.25
+    dx, dw1t, dw2, db1 = tw.twell_ffn_bwd(x, w1t, w2, h, torch.zeros_like(dy), lam)
+    torch.cuda.synchronize()
+    assert torch.count_nonzero(dw2).item() == 0
+    h64 = orc.twell_unpack(twell_host(h))
+    P = (h64 > 0).astype(np.float64)
+    xr = orc.widen(g["x"], "bf16")
+    assert rel_err(from_dev(dw1t), lam * (P.T @ xr)) < 1e-6
+    assert np.allclose(from_dev(db1), lam * P.sum(0), rtol=1e-6)
+
+
+def test_bwd_workspace_too_small():
+    import ctypes
+    w = synth.C1.with_(with_dy=True)
+    g = synth.generate(w)
+    x, w1t, b1, w2 = (to_dev(g["x"], "f32"), to_dev(g["w1t"], "f32"), to_dev(g["b1"], "f32"), to_dev(g["w2"], "f32"))
+    dy = to_dev(g["dy"], "f32")
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, 64, 8, 8)
+    T, d = x.shape
+    f = w1t.shape[0]
+    out = [torch.empty(s, dtype=torch.float32, device="cuda") for s in [(T, d), (f, d), (f, d), (f,)]]
+    ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
+    need = tw.twell_ffn_bwd_workspace_bytes(T, d, f, h)
+    assert need > 4096
+    m = h.c()
+    st = tw.lib().twell_ffn_bwd(x.data_ptr(), w1t.data_ptr(), w2.data_ptr(), 0, T, d, f, ctypes.byref(m),
+                                dy.data_ptr(), 0.0, *[o.data_ptr() for o in out], ws.data_ptr(), 4096, None)
+    assert st == -4
+    torch.cuda.synchronize()
