@@ -38,13 +38,15 @@ class TwellError(RuntimeError):
 class TwellMatrixC(_c.Structure):
     _fields_ = [("rows", _I), ("cols", _I), ("tile_w", _I), ("slots", _I), ("ovf_cap", _I),
                 ("val_dtype", _I), ("counts", _P), ("col_idx", _P), ("vals", _P), ("ovf_n", _P),
-                ("ovf_rows", _P), ("ovf_slot", _P), ("ovf_dense", _P), ("ovf_bits", _P)]
+                ("ovf_rows", _P), ("ovf_slot", _P), ("ovf_dense", _P), ("ovf_bits", _P),
+                ("row_nnz", _P), ("row_list", _P)]
 
 
 _SIGS = {
     "twell_abi_version": ([], _I),
     "twell_status_str": ([_I], _c.c_char_p),
     "twell_ovf_bits_words": ([_I, _I, _I], _Z),
+    "twell_row_list_bytes": ([_I, _I, _I, _I], _Z),
     "twell_pack": ([_P, _I, _P, _P], _I),
     "twell_ffn_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
     "twell_down": ([_P, _P, _I, _I, _P, _I, _P], _I),
@@ -130,12 +132,16 @@ class TwellMatrix:
         self.ovf_dense = torch.empty((max(ovf_cap, 1), cols), dtype=val_dtype, device=device)
         words = lib().twell_ovf_bits_words(rows, cols, tile_w)
         self.ovf_bits = torch.empty((max(words, 1),), **i32)
+        self.row_nnz = torch.empty((max(rows, 1),), **i32)
+        lb = lib().twell_row_list_bytes(rows, cols, tile_w, slots)
+        self.row_list = torch.empty((max(lb // 8, 2),), dtype=torch.int64, device=device)
 
     def c(self) -> TwellMatrixC:
         return TwellMatrixC(self.rows, self.cols, self.tile_w, self.slots, self.ovf_cap,
                             _dt(self.val_dtype), _ptr(self.counts), _ptr(self.col_idx),
                             _ptr(self.vals), _ptr(self.ovf_n), _ptr(self.ovf_rows),
-                            _ptr(self.ovf_slot), _ptr(self.ovf_dense), _ptr(self.ovf_bits))
+                            _ptr(self.ovf_slot), _ptr(self.ovf_dense), _ptr(self.ovf_bits),
+                            _ptr(self.row_nnz), _ptr(self.row_list))
 
     @property
     def n_tiles(self) -> int:

@@ -22,7 +22,7 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_
   } while (0)
 
 // Shape and pointer checks of a TwELL struct used as output (writable) or input.
-int check_matrix(const twell_matrix_t *m, bool need_ovf_bits) {
+int check_matrix(const twell_matrix_t *m, bool need_ovf_bits, bool need_rows = false) {
   if (!m) return TWELL_ERR_ARG;
   if (!dtype_ok(m->val_dtype)) return TWELL_ERR_ARG;
   if (m->rows < 0 || m->cols <= 0 || m->ovf_cap < 0) return TWELL_ERR_SHAPE;
@@ -33,10 +33,11 @@ int check_matrix(const twell_matrix_t *m, bool need_ovf_bits) {
   if (m->rows > 0) {
     if (!m->counts || !m->col_idx || !m->vals || !m->ovf_slot) return TWELL_ERR_ARG;
     if (need_ovf_bits && !m->ovf_bits) return TWELL_ERR_ARG;
+    if (need_rows && (!m->row_nnz || !m->row_list)) return TWELL_ERR_ARG;
   }
   if (m->ovf_cap > 0 && (!m->ovf_rows || !m->ovf_dense)) return TWELL_ERR_ARG;
   if (!al4(m->counts) || !al4(m->col_idx) || !al4(m->vals) || !al4(m->ovf_n) || !al4(m->ovf_rows) ||
-      !al4(m->ovf_slot) || !al4(m->ovf_bits) || !al16(m->ovf_dense))
+      !al4(m->ovf_slot) || !al4(m->ovf_bits) || !al16(m->ovf_dense) || !al4(m->row_nnz) || !al16(m->row_list))
     return TWELL_ERR_ALIGN;
   return TWELL_OK;
 }
@@ -61,6 +62,8 @@ TwellIn in_of(const twell_matrix_t *m) {
   h.vals = m->vals;
   h.ovf_slot = m->ovf_slot;
   h.ovf_dense = m->ovf_dense;
+  h.row_nnz = m->row_nnz;
+  h.row_list = (uint2 *)m->row_list;
   h.rows = m->rows;
   h.cols = m->cols;
   h.n_t = m->cols / m->tile_w;
@@ -93,6 +96,11 @@ const char *twell_status_str(int status) {
 size_t twell_ovf_bits_words(int32_t rows, int32_t cols, int32_t tile_w) {
   if (rows < 0 || cols <= 0 || tile_w <= 0) return 0;
   return (size_t)(cols / tile_w) * (size_t)((rows + 31) / 32);
+}
+
+size_t twell_row_list_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots) {
+  if (rows < 0 || cols <= 0 || tile_w <= 0 || slots <= 0) return 0;
+  return (size_t)rows * (size_t)(cols / tile_w) * (size_t)slots * 8;
 }
 
 int twell_pack(const void *h, int32_t h_dtype, twell_matrix_t *out, void *stream) {
@@ -179,6 +187,8 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
   if (!dtype_ok(y_dtype)) return TWELL_ERR_ARG;
   int st = check_up_args(x, w1t, b1, in_dtype, T, d_model, d_ff, h);
   if (st) return st;
+  st = check_matrix(h, true, true);
+  if (st) return st;
   if (!al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
   hipStream_t s = S(stream);
   st = up_gemm(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);
@@ -193,7 +203,7 @@ int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t
                int32_t y_dtype, void *stream) {
   if (!h || !w2 || !y) return TWELL_ERR_ARG;
   if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return TWELL_ERR_ARG;
-  int st = check_matrix(h, false);
+  int st = check_matrix(h, false, true);
   if (st) return st;
   if (d_model <= 0) return TWELL_ERR_SHAPE;
   if (d_model % 8) return TWELL_ERR_ALIGN;

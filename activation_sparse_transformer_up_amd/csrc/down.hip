@@ -4,11 +4,13 @@
 // "Kernels de Inferência": the down projection iterates over the active units only, so the
 // rows of W2 of inactive units are never read. Accumulation is fp32.
 //
-// Work item = (token t, column chunk c). A chunk is 16 lanes x 16 bytes of a W2 row (128
-// bf16 or 64 fp32 columns); the wave's four 16-lane groups take every fourth entry of the
-// token's active list, so one vector load instruction fetches four different W2 rows.
-// The list (column, value) is staged in LDS: from the TwELL slots of normal rows, or from
-// the nonzeros of the dense backup row of an overflow row.
+// First each normal row's TwELL slots are compacted once into a contiguous list of
+// (column, value) pairs (k_row_list): the gather below is spread over all XCDs by column
+// chunk, and reading the sparse slot blocks from every XCD would fetch whole cache lines
+// for a handful of entries. Work item = (token t, column chunk c). A chunk is 16 lanes x
+// 16 bytes of a W2 row (128 bf16 or 64 fp32 columns); the wave's four 16-lane groups take
+// every fourth entry of the token's list, so one vector load instruction fetches four
+// different W2 rows. Overflow rows take their entries from the dense backup row.
 //
 // XCD-aware order: workgroup b runs on XCD b % 8 (round-robin dispatch), and all chunks
 // handled by one XCD are congruent mod 8, so that XCD's L2 only ever holds its own column
@@ -20,13 +22,42 @@ namespace tw {
 
 template <typename VT> TW_DEV float ldv(const VT *p, size_t i) { return Elem<VT>::load(p, i); }
 
+// Compact list of each normal row: row_list[t][0 .. row_nnz[t]) = (column, fp32 value bits)
+// in ascending column order, read once from the TwELL slots. Rows with a dense backup get
+// row_nnz = -1 (their consumers read the backup row). One wave per row.
+template <typename VT>
+__global__ __launch_bounds__(256) void k_row_list(TwellIn h) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= h.rows) return;
+  const int lane = lane_id();
+  if (h.ovf_slot[t] >= 0) {
+    if (lane == 0) h.row_nnz[t] = -1;
+    return;
+  }
+  const size_t stride = (size_t)h.n_t * h.S;
+  uint2 *out = h.row_list + (size_t)t * stride;
+  const VT *vals = (const VT *)h.vals;
+  int n = 0;
+  for (int k0 = 0; k0 < h.n_t; k0 += 64) {
+    const int k = k0 + lane;
+    const int m = k < h.n_t ? min(h.counts[(size_t)t * h.n_t + k], h.S) : 0;
+    int tot;
+    const int off = wave_excl_scan(m, &tot);
+    const size_t sb = ((size_t)t * h.n_t + k) * h.S;
+    for (int s = 0; s < m; ++s)
+      out[n + off + s] = make_uint2((uint32_t)h.col_idx[sb + s], __float_as_uint(ldv(vals, sb + s)));
+    n += tot;
+  }
+  if (lane == 0) h.row_nnz[t] = n;
+}
+
+// y[t][chunk] from the compact list: batches of 64 (column, value) pairs are staged in LDS
+// (one coalesced 8-byte load per lane); the four 16-lane groups take every fourth entry of
+// a batch and issue all their W2 row loads (up to 16) before the FMAs.
 template <typename WT, typename VT, typename YT>
 __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restrict__ w2, int d,
                                                    YT *__restrict__ y, int nchunk) {
-  extern __shared__ __attribute__((aligned(16))) char lds[];
-  const int LCAP = 64 * h.S;
-  int *lcol = (int *)lds;
-  float *lval = (float *)(lds + (size_t)LCAP * 4);
+  __shared__ uint2 lst[64];
   const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
   const int T = h.rows;
   const int c = xcd + 8 * (i / T), t = i % T;
@@ -36,80 +67,65 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
-  const VT *vals = (const VT *)h.vals;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
 
-  auto flush = [&](int n) {
-    int e = g;
-    for (; e + 12 < n; e += 16) {
-      const int j0 = lcol[e], j1 = lcol[e + 4], j2 = lcol[e + 8], j3 = lcol[e + 12];
-      const float v0 = lval[e], v1 = lval[e + 4], v2 = lval[e + 8], v3 = lval[e + 12];
-      float r0[E], r1[E], r2[E], r3[E];
-      if (cv) {
-        Vec16<WT>::load(w2 + (size_t)j0 * d + col, r0);
-        Vec16<WT>::load(w2 + (size_t)j1 * d + col, r1);
-        Vec16<WT>::load(w2 + (size_t)j2 * d + col, r2);
-        Vec16<WT>::load(w2 + (size_t)j3 * d + col, r3);
+  auto consume = [&](int n) {
+    uint4 raw[16];
+    float vv[16];
 #pragma unroll
-        for (int q = 0; q < E; ++q) {
-          acc[q] = fmaf(v0, r0[q], acc[q]);
-          acc[q] = fmaf(v1, r1[q], acc[q]);
-          acc[q] = fmaf(v2, r2[q], acc[q]);
-          acc[q] = fmaf(v3, r3[q], acc[q]);
-        }
+    for (int j = 0; j < 16; ++j) {
+      const int e = g + 4 * j;
+      vv[j] = 0.f;
+      raw[j] = make_uint4(0, 0, 0, 0);
+      if (e < n) {
+        const uint2 p = lst[e];
+        vv[j] = __uint_as_float(p.y);
+        if (cv) raw[j] = *(const uint4 *)(w2 + (size_t)p.x * d + col);
       }
     }
-    for (; e < n; e += 4) {
-      const int j = lcol[e];
-      const float v = lval[e];
-      float r[E];
-      if (cv) {
-        Vec16<WT>::load(w2 + (size_t)j * d + col, r);
 #pragma unroll
-        for (int q = 0; q < E; ++q) acc[q] = fmaf(v, r[q], acc[q]);
+    for (int j = 0; j < 16; ++j) {
+      float r[E];
+      if constexpr (sizeof(WT) == 2) {
+        const uint32_t w[4] = {raw[j].x, raw[j].y, raw[j].z, raw[j].w};
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          r[2 * q] = __uint_as_float(w[q] << 16);
+          r[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+        }
+      } else {
+        r[0] = __uint_as_float(raw[j].x); r[1] = __uint_as_float(raw[j].y);
+        r[2] = __uint_as_float(raw[j].z); r[3] = __uint_as_float(raw[j].w);
       }
+#pragma unroll
+      for (int q = 0; q < E; ++q) acc[q] = fmaf(vv[j], r[q], acc[q]);
     }
   };
 
-  const int slot = h.ovf_slot[t];
-  if (slot < 0) {
-    for (int k0 = 0; k0 < h.n_t; k0 += 64) {
-      const int k = k0 + lane;
-      int m = 0;
-      if (k < h.n_t) m = min(h.counts[(size_t)t * h.n_t + k], h.S);
-      int tot;
-      const int off = wave_excl_scan(m, &tot);
-      const size_t sbase = ((size_t)t * h.n_t + k) * h.S;
-      for (int s = 0; s < m; ++s) {
-        lcol[off + s] = h.col_idx[sbase + s];
-        lval[off + s] = ldv(vals, sbase + s);
-      }
+  const int nnz = h.row_nnz[t];
+  if (nnz >= 0) {
+    const uint2 *src = h.row_list + (size_t)t * h.n_t * h.S;
+    for (int base = 0; base < nnz; base += 64) {
+      const int n = min(64, nnz - base);
+      if (lane < n) lst[lane] = src[base + lane];
       __syncthreads();
-      flush(tot);
+      consume(n);
       __syncthreads();
     }
   } else {
-    const VT *row = (const VT *)h.ovf_dense + (size_t)slot * h.cols;
-    int n = 0;
+    const VT *row = (const VT *)h.ovf_dense + (size_t)h.ovf_slot[t] * h.cols;
     for (int c0 = 0; c0 < h.cols; c0 += 64) {
       const int j = c0 + lane;
       const float v = j < h.cols ? ldv(row, j) : 0.f;
       const bool nz = v != 0.f;
       const uint64_t m = ballot64(nz);
-      if (nz) {
-        const int pos = n + (int)mbcnt64(m);
-        lcol[pos] = j;
-        lval[pos] = v;
-      }
-      n += __popcll(m);
-      if (n > LCAP - 64 || c0 + 64 >= h.cols) {
-        __syncthreads();
-        flush(n);
-        __syncthreads();
-        n = 0;
-      }
+      if (m == 0) continue;
+      if (nz) lst[mbcnt64(m)] = make_uint2((uint32_t)j, __float_as_uint(v));
+      __syncthreads();
+      consume(__popcll(m));
+      __syncthreads();
     }
   }
 #pragma unroll
@@ -131,8 +147,8 @@ static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, hipStream
   const long long per_xcd = (long long)h.rows * ((nchunk + 7) / 8);
   if (h.rows == 0) return hipSuccess;
   const size_t grid = 8 * (size_t)per_xcd;
-  const size_t lds = (size_t)64 * h.S * 8;
-  hipLaunchKernelGGL((k_twell_down<WT, VT, YT>), dim3((unsigned)grid), dim3(64), lds, s, h, w2, d, y, nchunk);
+  hipLaunchKernelGGL((k_row_list<VT>), dim3((h.rows + 3) / 4), dim3(256), 0, s, h);
+  hipLaunchKernelGGL((k_twell_down<WT, VT, YT>), dim3((unsigned)grid), dim3(64), 0, s, h, w2, d, y, nchunk);
   return hipGetLastError();
 }
 

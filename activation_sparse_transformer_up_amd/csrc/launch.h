@@ -23,6 +23,8 @@ struct TwellIn {
   const void *vals;
   const int32_t *ovf_slot;
   const void *ovf_dense;
+  int32_t *row_nnz;       // scratch: compact list length per row (-1: use the backup row)
+  uint2 *row_list;        // scratch: [rows][n_t * S] (column, fp32 value bits)
   int rows, cols, n_t, S, W, val_bf16;
 };
 

@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--ovf-cap", type=int, default=64)
+    ap.add_argument("--legs", default="c3,c4,c5",
+                    help="extra workloads measured after the headline (comma list, or 'none')")
     return ap.parse_args()
 
 
@@ -81,6 +83,167 @@ def warm(fn, steps: int, min_seconds: float = 0.5):
         if n % 16 == 0:
             torch.cuda.synchronize()
     torch.cuda.synchronize()
+
+
+def _up(arr, dt, dev):
+    import numpy as np
+    import torch
+    if dt == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).view(torch.bfloat16).to(dev)
+    return torch.from_numpy(np.ascontiguousarray(arr)).to(dev)
+
+
+def _time(fn, steps, warmup):
+    import torch
+    warm(fn, warmup, min_seconds=0.2)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        fn()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps
+
+
+def leg_c3(steps, warmup):
+    """Decode-shaped layer, T in {1, 8, 64}, weights cold: three copies of (w1t, w2) are
+    rotated so the 235 MB of weights of a step are not resident in the 256 MB MALL."""
+    import numpy as np
+    import torch
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+    w = synth.C3
+    dev = torch.device("cuda:0")
+    g = synth.generate(w)
+    copies = [(_up(g["w1t"], "bf16", dev), _up(g["w2"], "bf16", dev)) for _ in range(3)]
+    b1 = _up(g["b1"], "f32", dev)
+    out = {}
+    for T in (1, 8, 64):
+        x = _up(g["x"][:T], "bf16", dev)
+        hs = [tw.TwellMatrix(T, w.f, w.tile_w, w.slots, 4, torch.float32, dev) for _ in range(3)]
+        y = torch.empty((T, w.d), device=dev)
+        it = [0]
+
+        def fwd():
+            i = it[0] % 3
+            it[0] += 1
+            w1, w2_ = copies[i]
+            tw.twell_ffn_fwd(x, w1, b1, w2_, w.tile_w, w.slots, 4, h=hs[i], y=y)
+
+        def down():
+            i = it[0] % 3
+            it[0] += 1
+            tw.twell_down(hs[i], copies[i][1], y=y)
+
+        def gemm():
+            i = it[0] % 3
+            it[0] += 1
+            tw.twell_up_gemm(x, copies[i][0], b1, hs[i])
+
+        bb = b1.to(torch.bfloat16)
+
+        def dense():
+            i = it[0] % 3
+            it[0] += 1
+            w1, w2_ = copies[i]
+            torch.relu(torch.addmm(bb, x, w1.t())) @ w2_
+
+        ms = _time(fwd, steps * 4, warmup)
+        ms_down = _time(down, steps * 4, warmup)
+        ms_gemm = _time(gemm, steps * 4, warmup)
+        ms_dense = _time(dense, steps * 4, warmup)
+        # algorithmic bytes of the gather: unique W2 rows touched + y + the compact lists
+        cnt = hs[0].counts.clamp(max=w.slots)
+        nnz = int(cnt.sum().item())
+        ci = hs[0].col_idx.cpu().numpy()
+        uniq = len(np.unique(ci[ci >= 0]))
+        gbytes = uniq * w.d * 2 + T * w.d * 4 + nnz * 8 + T * w.n_tiles * 4
+        ubytes = w.f * w.d * 2 + T * w.d * 2 + T * w.n_tiles * (4 + 8 * w.slots)
+        out[f"T{T}"] = {
+            "tokens_per_s": T / (ms * 1e-3), "ms_per_step": ms, "dense_ms": ms_dense,
+            "speedup_vs_dense": ms_dense / ms, "nnz_per_token": nnz / T, "unique_w2_rows": uniq,
+            "gather": {"ms": ms_down, "algorithmic_bytes": gbytes,
+                       "GB_per_s": gbytes / (ms_down * 1e-3) / 1e9,
+                       "frac_hbm_peak": gbytes / (ms_down * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "up_gemm": {"ms": ms_gemm, "algorithmic_bytes": ubytes,
+                        "GB_per_s": ubytes / (ms_gemm * 1e-3) / 1e9,
+                        "frac_hbm_peak": ubytes / (ms_gemm * 1e-3) / 1e9 / PEAK_HBM_GBS},
+            "cold_weights": "3 rotated copies of w1t+w2 (705 MB)"}
+    return out
+
+
+def leg_c4(steps, warmup):
+    """N:M pruning of the zero-bias layer's activations and the packed down projection."""
+    import torch
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+    w = synth.C4
+    dev = torch.device("cuda:0")
+    g = synth.generate(w)
+    x, w1t, w2 = _up(g["x"], "bf16", dev), _up(g["w1t"], "bf16", dev), _up(g["w2"], "bf16", dev)
+    b1 = _up(g["b1"], "f32", dev)
+    w2t = w2.t().contiguous()
+    h = tw.ffn_up_relu_dense(x, w1t, b1, torch.bfloat16)
+    T, f, d = w.T, w.f, w.d
+    out = {"dense_down_ms": _time(lambda: h @ w2, steps, warmup)}
+    out["up_relu_dense_ms"] = _time(lambda: tw.ffn_up_relu_dense(x, w1t, b1, torch.bfloat16, out=h), steps, warmup)
+    for n, m in w.nm:
+        vals, idx = tw.nm_prune(h, n, m)
+        ms_p = _time(lambda: tw.nm_prune(h, n, m), steps, warmup)
+        y = torch.empty((T, d), device=dev)
+        ms_d = _time(lambda: tw.nm_ffn_down(vals, idx, n, m, w2t, y=y), steps, warmup)
+        pbytes = T * f * 2 + T * (f // m) * n * 3
+        out[f"{n}:{m}"] = {
+            "prune_ms": ms_p, "prune_GB_per_s": pbytes / (ms_p * 1e-3) / 1e9,
+            "prune_frac_hbm_peak": pbytes / (ms_p * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "nm_down_ms": ms_d, "nm_down_TFLOPs": 2.0 * T * f * d / (ms_d * 1e-3) / 1e12,
+            "nm_down_vs_dense_down": out["dense_down_ms"] / ms_d}
+    return out
+
+
+def leg_c5(steps, warmup):
+    """Training step (forward + backward with the L1 term) vs the dense bf16 FFN's
+    forward + backward through autograd (the same six GEMMs a dense layer needs)."""
+    import torch
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+    w = synth.C5
+    dev = torch.device("cuda:0")
+    g = synth.generate(w)
+    x, w1t, w2, dy = (_up(g[k], "bf16", dev) for k in ("x", "w1t", "w2", "dy"))
+    b1 = _up(g["b1"], "f32", dev)
+    T, f, d = w.T, w.f, w.d
+    cap = 1024
+    h = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.float32, dev)
+    y = torch.empty((T, d), device=dev)
+    ws = torch.empty((tw.twell_ffn_bwd_workspace_bytes(T, d, f, h),), dtype=torch.uint8, device=dev)
+
+    def step():
+        tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y)
+        tw.twell_ffn_bwd(x, w1t, w2, h, dy, w.l1_coef, workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    ms_fwd = _time(lambda: tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y), steps, warmup)
+    ovf = int(h.ovf_n.item())
+    dens = float(h.counts.sum().item()) / (T * f)
+    del ws
+    torch.cuda.empty_cache()
+    xd = x.clone().requires_grad_(True)
+    w1d = w1t.clone().requires_grad_(True)
+    w2d = w2.clone().requires_grad_(True)
+    bd = b1.to(torch.bfloat16).requires_grad_(True)
+
+    def dense_step():
+        hh = torch.relu(torch.addmm(bd, xd, w1d.t()))
+        yy = hh @ w2d
+        loss = (yy * dy).sum() + w.l1_coef * hh.float().sum()
+        loss.backward()
+        xd.grad = w1d.grad = w2d.grad = bd.grad = None
+
+    ms_dense = _time(dense_step, steps, warmup)
+    return {"tokens_per_s": T / (ms * 1e-3), "ms_fwd_bwd": ms, "ms_fwd": ms_fwd, "ms_bwd": ms - ms_fwd,
+            "dense_ms_fwd_bwd": ms_dense, "speedup_vs_dense": ms_dense / ms, "density": dens,
+            "overflow_rows": ovf, "slots": w.slots, "tile_w": w.tile_w}
 
 
 def main():
@@ -182,6 +345,20 @@ def main():
 
     if not a.no_cpu:
         out["cpu_baseline"] = cpu_baseline(g, w, T_sample=min(T, 4096))
+    legs = [] if a.legs in ("", "none") else a.legs.split(",")
+    if legs:
+        del x, w1t, w2, h, y
+        torch.cuda.empty_cache()
+        out["legs"] = {}
+        for leg in legs:
+            fn = {"c3": leg_c3, "c4": leg_c4, "c5": leg_c5}.get(leg)
+            if fn is None:
+                continue
+            try:
+                out["legs"][leg] = fn(max(5, a.steps // 5), max(2, a.warmup // 2))
+            except Exception as e:        # a failing extra leg must not hide the headline
+                out["legs"][leg] = {"error": f"{type(e).__name__}: {e}"}
+            torch.cuda.empty_cache()
     print(json.dumps(out), flush=True)
 
 

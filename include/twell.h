@@ -70,6 +70,10 @@ typedef enum {
  *   ovf_dense[ovf_cap][C]           the full row of each listed overflow row (val_dtype)
  *   ovf_bits[C/tile_w][ceil(R/32)]  library scratch (uint32 words), written and read
  *                                   inside one call; contents on return are unspecified
+ *   row_nnz[R]                      library scratch: entries of each row's compact list
+ *   row_list[R][C/tile_w * slots]   library scratch: compact (int32 column, fp32 value)
+ *                                   pairs of each row, written by the consumers of the
+ *                                   matrix (down projection, backward) before use
  *
  * A row overflows iff some tile of it holds more than `slots` nonzeros. A (row, tile)
  * keeps its first min(count, slots) nonzeros in ascending column order. "Nonzero" is
@@ -91,6 +95,8 @@ typedef struct {
   int32_t *ovf_slot;
   void *ovf_dense;
   uint32_t *ovf_bits;
+  int32_t *row_nnz;
+  void *row_list;
 } twell_matrix_t;
 
 /* Returns TWELL_ABI_VERSION. */
@@ -101,6 +107,9 @@ const char *twell_status_str(int status);
 
 /* Number of uint32 words that twell_matrix_t.ovf_bits must hold. */
 size_t twell_ovf_bits_words(int32_t rows, int32_t cols, int32_t tile_w);
+
+/* Bytes that twell_matrix_t.row_list must hold (8 bytes per slot of the matrix). */
+size_t twell_row_list_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots);
 
 /*
  * twell_pack — dense h [R][C] (h_dtype) -> TwELL `out` (shape fields set by the caller).

@@ -26,7 +26,8 @@ def test_header_declares_expected_entry_points():
     names = declared_functions()
     for n in ["twell_pack", "twell_ffn_fwd", "twell_ffn_bwd", "nm_prune", "twell_abi_version",
               "twell_status_str", "twell_sync_status", "nm_ffn_down", "ffn_up_relu_dense",
-              "twell_down", "twell_ffn_bwd_workspace_bytes", "twell_ovf_bits_words"]:
+              "twell_down", "twell_ffn_bwd_workspace_bytes", "twell_ovf_bits_words",
+              "twell_row_list_bytes", "twell_up_gemm", "twell_up_finish"]:
         assert n in names, n
 
 
@@ -62,7 +63,7 @@ MIS = 0x10004           # misaligned
 
 
 def mat(rows=64, cols=512, W=128, S=8, cap=4, dt=0, **kw):
-    m = tw.TwellMatrixC(rows, cols, W, S, cap, dt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    m = tw.TwellMatrixC(rows, cols, W, S, cap, dt, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
     for k, v in kw.items():
         setattr(m, k, v)
     return m
@@ -89,7 +90,7 @@ def test_fwd_rejects(kw, want):
     (dict(slots=65), SHAPE), (dict(W=64, slots=65), SHAPE), (dict(ovf_cap=-1), SHAPE),
     (dict(counts=None), ARG), (dict(ovf_n=None), ARG), (dict(ovf_bits=None), ARG),
     (dict(val_dtype=5), ARG), (dict(ovf_rows=None), ARG), (dict(ovf_dense=MIS), ALIGN),
-    (dict(counts=MIS + 1), ALIGN),
+    (dict(counts=MIS + 1), ALIGN), (dict(row_list=None), ARG), (dict(row_nnz=MIS + 1), ALIGN),
 ])
 def test_fwd_rejects_bad_matrix(mkw, want):
     W = mkw.pop("W", 128)
