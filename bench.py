@@ -37,6 +37,8 @@ def parse():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-dense", action="store_true")
     ap.add_argument("--ovf-cap", type=int, default=64)
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
     ap.add_argument("--legs", default="c3,c4,c5",
                     help="extra workloads measured after the headline (comma list, or 'none')")
     return ap.parse_args()
@@ -68,6 +70,26 @@ def cpu_baseline(g, w, T_sample: int, min_seconds: float = 10.0) -> dict:
             "kind": "oracle",
             "sample": f"{T_sample} tokens of the {w.name} workload x {reps} repetitions "
                       f"(fp64 numpy forward + TwELL pack, {t_total:.1f} s)"}
+
+
+def counter_traffic(workload: str):
+    """HBM bytes per launch of the up GEMM from the committed rocprofv3 counter summary
+    (FETCH_SIZE + WRITE_SIZE, each divided by what the counter reads per byte of a plain
+    device copy), or None if the summary is missing, is for another workload, or was taken
+    on a different version of the GEMM source."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "k_up_twell_c2_counters.json")
+    src = os.path.join(ROOT, "activation_sparse_transformer_up_amd", "csrc", "gemm.hip")
+    try:
+        rec = json.load(open(path))
+        sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    except (OSError, ValueError):
+        return None
+    if rec.get("gemm_source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    fetch = rec["fetch_kib_per_dispatch"] * 1024 / rec["copy_fetch_per_byte"]
+    write = rec["write_kib_per_dispatch"] * 1024 / rec["copy_write_per_byte"]
+    return fetch + write
 
 
 def warm(fn, steps: int, min_seconds: float = 0.5):
@@ -258,6 +280,16 @@ def main():
     import activation_sparse_transformer_up_amd as tw
     import synth
 
+    if a.copy_calibration:
+        src = torch.empty(1 << 28, dtype=torch.float32, device="cuda")      # 1 GiB
+        dst = torch.empty_like(src)
+        src.fill_(1.0)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes": src.numel() * 4, "dispatches": 3}))
+        return
+
     w = synth.WORKLOADS[a.workload]
     T = a.T or w.T
     g = synth.generate(w, T=T)
@@ -311,6 +343,7 @@ def main():
     ms_mono = t0.elapsed_time(t1) / a.steps
 
     flops_up = 2.0 * T * d * f
+    traffic = counter_traffic(w.name)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops_up / (gemm_ms * 1e-3) / 1e12
     out = {
@@ -322,7 +355,7 @@ def main():
                    "slots": w.slots, "bias": w.bias, "seed": w.seed, "parallelism": "single GPU"},
         "roofline": {"kernel": "k_up_twell (up GEMM + fused ReLU/TwELL epilogue)", "bound": "mfma",
                      "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": None, "per_launch_flop": flops_up, "avg_launch_ms": gemm_ms},
+                     "traffic": traffic, "per_launch_flop": flops_up, "avg_launch_ms": gemm_ms},
         "measured_density": nnz / (T * f), "ovf_rows": ovf_n, "ms_per_step_monolithic": ms_mono,
     }
 
