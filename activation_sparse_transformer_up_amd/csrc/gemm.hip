@@ -20,6 +20,8 @@
 // Accumulation order of one output element depends only on K and the fixed step order,
 // not on the tile shape or the row's position, so every epilogue (TwELL, dense, backup
 // rows) sees bit-identical z values.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -51,7 +53,7 @@ template <> struct MfmaOps<float> {
   }
 };
 
-template <int BM_, int BN_, int WM_, int WN_>
+template <int BM_, int BN_, int WM_, int WN_, int EPIW>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
@@ -61,17 +63,26 @@ struct Tile {
   static constexpr int STAGE = (BM + BN) * RB;            // bytes per stage (A rows, then B rows)
   static constexpr int LDS_BYTES = NS * STAGE;
   static constexpr int LPW = (BM + BN) / 16 / NW;         // 1 KB wave-loads per wave per stage
-  static constexpr int EPI_WAVE = 34816;                  // TwELL epilogue LDS per wave
+  static constexpr int EPI_WAVE = EPIW;                   // TwELL epilogue LDS per wave
   static constexpr int EPI_BYTES = NW * EPI_WAVE;
   static constexpr int SMEM = LDS_BYTES > EPI_BYTES ? LDS_BYTES : EPI_BYTES;
   static_assert((BM + BN) % (16 * NW) == 0 && BM % 16 == 0, "tile");
 };
 
-// Large tiles for many tokens, small tiles for few. Waves are 128 columns wide in the
-// large tile and the small one so that a 64- or 128-wide TwELL tile never straddles
-// two waves.
-typedef Tile<256, 256, 128, 128> TileL;
-typedef Tile<64, 128, 32, 128> TileS;
+// TwELL epilogue LDS of one wave: slot indices and values for 32 rows x RS slots (+ one
+// junk element per lane) and the counts. RS = (WN / W) * S slots per row.
+constexpr int epi_wave_bytes(int rs, int tpw, int vbytes) {
+  return ((4 * (32 * rs + 64) + vbytes * (32 * rs + 64) + 15) & ~15) + 4 * (32 * tpw + 64);
+}
+
+// Many tokens: 256 x 256 tiles. TileL8 has 8 waves of 64 x 128 (two per SIMD, so one
+// wave's LDS and memory instructions overlap the other's MFMAs); its epilogue LDS allows
+// up to 64 slots per row per wave. TileL (4 waves of 128 x 128) takes the larger slot
+// counts (W = 64 with S > 32). Few tokens: 64 x 128 tiles. Waves are 128 columns wide so
+// that a 64- or 128-wide TwELL tile never straddles two waves.
+typedef Tile<256, 256, 64, 128, epi_wave_bytes(64, 2, 4)> TileL8;
+typedef Tile<256, 256, 128, 128, epi_wave_bytes(128, 2, 4)> TileL;
+typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4)> TileS;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -87,15 +98,35 @@ TW_DEV void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+// Barrier after this wave's LDS reads have completed (lgkmcnt(0)), so that no read of a
+// stage can still be pending when another wave's loads overwrite it.
+TW_DEV void block_barrier_lds() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
 // A operand row r of the tile reads global row arow[m0 + r] (if arow) or m0 + r; rows at or
 // beyond a_rows are zero. B operand rows at or beyond b_rows are zero. a_total rows exist
 // in A (bounds of the buffer resource). Operands must be smaller than 2 GiB.
+//
+// Software pipeline of one K step (two half-steps u = 0, 1 of 16 (bf16) k each):
+//   read fragments (kt, u=1)    | MFMAs on fragments (kt, u=0)
+//   wait for stage kt+1's loads, barrier
+//   read fragments (kt+1, u=0)  | MFMAs on fragments (kt, u=1), with the loads of stage
+//                                 kt+NS-1 issued between them
+// so LDS reads are always one half-step ahead of the MFMAs that consume them. The stage
+// overwritten by the loads issued after the barrier of step kt is (kt-1) mod NS, whose last
+// fragments every wave has consumed before reaching that barrier.
 template <typename T, class G>
 TW_DEV void mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, int a_rows, int a_total,
                      const T *__restrict__ B, int b_rows, int K, int m0, int n0,
                      f32x16_t (&acc)[G::MB][G::NB], char *smem) {
+  static_assert(G::NS >= 3, "stages");
   constexpr int EPC = 16 / sizeof(T);                     // elements per 16-byte chunk
   constexpr int KPT = G::RB / sizeof(T);                  // k per stage
+  constexpr int NMMA = G::MB * G::NB;
   constexpr uint32_t OOB = 0x80000000u;
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -130,53 +161,81 @@ TW_DEV void mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, 
   const int nk = (K + KPT - 1) / KPT;
   const int kc = cl * EPC;                                // this lane's k offset in a stage
 
-  auto issue = [&](int kt) {
+  auto issue1 = [&](int kt, int i) {
     const int k0 = kt * KPT;
     char *st = smem + (kt % G::NS) * G::STAGE;
-    const bool kin = k0 + kc < K;
-#pragma unroll
-    for (int i = 0; i < G::LPW; ++i) {
-      const uint32_t vo = kin ? voff[i] : OOB;
-      lds_void_t *dst = (lds_void_t *)(st + ldsq[i]);
-      if (isA[i]) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vo, k0 * (int)sizeof(T), 0, 0);
-      else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vo, k0 * (int)sizeof(T), 0, 0);
-    }
+    const uint32_t vo = (k0 + kc < K) ? voff[i] : OOB;
+    lds_void_t *dst = (lds_void_t *)(st + ldsq[i]);
+    if (isA[i]) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vo, k0 * (int)sizeof(T), 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vo, k0 * (int)sizeof(T), 0, 0);
   };
   const int lr = lane & 31, lh = lane >> 5;
-  auto compute = [&](int kt) {
+  typedef u32x4_t FA[G::MB];
+  typedef u32x4_t FB[G::NB];
+  auto read = [&](int kt, int u, FA &a, FB &b) {
     const char *sa = smem + (kt % G::NS) * G::STAGE;
     const char *sb = sa + G::BM * G::RB;
+    const int c = 2 * u + lh;
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = 2 * u + lh;
-      u32x4_t a[G::MB], b[G::NB];
+    for (int mb = 0; mb < G::MB; ++mb) {
+      const int r = wm * G::WM + mb * 32 + lr;
+      a[mb] = *(const u32x4_t *)(sa + r * G::RB + ((c ^ ((r >> 2) & 3)) << 4));
+    }
 #pragma unroll
-      for (int mb = 0; mb < G::MB; ++mb) {
-        const int r = wm * G::WM + mb * 32 + lr;
-        a[mb] = *(const u32x4_t *)(sa + r * G::RB + ((c ^ ((r >> 2) & 3)) << 4));
-      }
-#pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb) {
-        const int r = wn * G::WN + nb * 32 + lr;
-        b[nb] = *(const u32x4_t *)(sb + r * G::RB + ((c ^ ((r >> 2) & 3)) << 4));
-      }
-#pragma unroll
-      for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < G::NB; ++nb) MfmaOps<T>::step(acc[mb][nb], a[mb], b[nb]);
+    for (int nb = 0; nb < G::NB; ++nb) {
+      const int r = wn * G::WN + nb * 32 + lr;
+      b[nb] = *(const u32x4_t *)(sb + r * G::RB + ((c ^ ((r >> 2) & 3)) << 4));
     }
   };
-
+  auto mma = [&](const FA &a, const FB &b) {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) MfmaOps<T>::step(acc[mb][nb], a[mb], b[nb]);
+  };
+  if (nk == 0) return;
 #pragma unroll
   for (int s = 0; s < G::NS - 1; ++s)
-    if (s < nk) issue(s);
-  for (int kt = 0; kt < nk; ++kt) {
-    if (kt + G::NS - 2 < nk) wait_vmcnt<(G::NS - 2) * G::LPW>();
+    if (s < nk)
+#pragma unroll
+      for (int i = 0; i < G::LPW; ++i) issue1(s, i);
+  if (nk >= G::NS - 1) wait_vmcnt<(G::NS - 2) * G::LPW>();
+  else wait_vmcnt<0>();
+  block_barrier();
+  FA a0, a1;
+  FB b0, b1;
+  read(0, 0, a0, b0);
+  // Step kt < nk - 1; LOAD: stage kt + NS - 1 exists and is loaded during this step. The
+  // scheduling barriers keep the compiler from moving MFMAs across the phases.
+  auto step = [&](int kt, auto load_tag) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    read(kt, 1, a1, b1);
+    __builtin_amdgcn_sched_barrier(0);
+    mma(a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+    if (LOAD) wait_vmcnt<(G::NS - 3) * G::LPW>();        // stage kt + 1 has landed
     else wait_vmcnt<0>();
-    block_barrier();
-    if (kt + G::NS - 1 < nk) issue(kt + G::NS - 1);
-    compute(kt);
-  }
+    block_barrier_lds();
+    read(kt + 1, 0, a0, b0);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < NMMA; ++i) {
+      MfmaOps<T>::step(acc[i / G::NB][i % G::NB], a1[i / G::NB], b1[i % G::NB]);
+      if (LOAD && (i & 1) && (i >> 1) < G::LPW) issue1(kt + G::NS - 1, i >> 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+    if (LOAD)
+#pragma unroll
+      for (int i = NMMA / 2; i < G::LPW; ++i) issue1(kt + G::NS - 1, i);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  int kt = 0;
+  for (; kt + G::NS - 1 < nk; ++kt) step(kt, std::integral_constant<bool, true>());
+  for (; kt + 1 < nk; ++kt) step(kt, std::integral_constant<bool, false>());
+  read(kt, 1, a1, b1);
+  __builtin_amdgcn_sched_barrier(0);
+  mma(a0, b0);
+  mma(a1, b1);
 }
 
 // Output position of accumulator register r of a 32x32 block, for this lane:
@@ -394,6 +453,7 @@ __global__ __launch_bounds__(G::NT) void k_up_dense(const T *__restrict__ x, con
 template <typename T, class G>
 static hipError_t launch_twell_t(const T *x, const T *w1t, const float *b1, int M, int N, int K,
                                  const TwellOut &o, int W, hipStream_t s) {
+  static_assert(G::SMEM <= 160 * 1024, "LDS");
   dim3 grid((N + G::BN - 1) / G::BN, (M + G::BM - 1) / G::BM);
   if (o.val_bf16) {
     if (W == 64) hipLaunchKernelGGL((k_up_twell<T, G, 64, uint16_t>), grid, dim3(G::NT), 0, s, x, w1t, b1, M, N, K, o);
@@ -410,6 +470,8 @@ static bool use_large(int M, int N) { return M >= 512 && N >= 1024; }
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N,
                            int K, const TwellOut &o, int W, hipStream_t s) {
   if (bf16) {
+    if (use_large(M, N) && (TileL8::WN / W) * o.S <= 64)
+      return launch_twell_t<uint16_t, TileL8>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
     if (use_large(M, N))
       return launch_twell_t<uint16_t, TileL>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
     return launch_twell_t<uint16_t, TileS>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
@@ -432,7 +494,7 @@ hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float
                            int relu, hipStream_t s) {
   if (bf16) {
     if (use_large(M, N) && !arow)
-      return launch_dense_t<uint16_t, TileL>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
+      return launch_dense_t<uint16_t, TileL8>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
                                              n_rows_dev, out, out_bf16, relu, s);
     return launch_dense_t<uint16_t, TileS>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
                                            n_rows_dev, out, out_bf16, relu, s);
