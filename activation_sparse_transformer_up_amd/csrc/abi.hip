@@ -62,6 +62,9 @@ TwellIn in_of(const twell_matrix_t *m) {
   h.vals = m->vals;
   h.ovf_slot = m->ovf_slot;
   h.ovf_dense = m->ovf_dense;
+  h.ovf_n = m->ovf_n;
+  h.ovf_rows = m->ovf_rows;
+  h.cap = m->ovf_cap;
   h.row_nnz = m->row_nnz;
   h.row_list = (uint2 *)m->row_list;
   h.rows = m->rows;

@@ -5,12 +5,21 @@
 // rows of W2 of inactive units are never read. Accumulation is fp32.
 //
 // First each normal row's TwELL slots are compacted once into a contiguous list of
-// (column, value) pairs (k_row_list): the gather below is spread over all XCDs by column
+// (column, value) pairs (k_row_list): the gathers below are spread over all XCDs by column
 // chunk, and reading the sparse slot blocks from every XCD would fetch whole cache lines
-// for a handful of entries. Work item = (token t, column chunk c). A chunk is 16 lanes x
-// 16 bytes of a W2 row (128 bf16 or 64 fp32 columns); the wave's four 16-lane groups take
-// every fourth entry of the token's list, so one vector load instruction fetches four
-// different W2 rows. Overflow rows take their entries from the dense backup row.
+// for a handful of entries. A chunk is 16 lanes x 16 bytes of a W2 row (128 bf16 or 64
+// fp32 columns), so one vector load instruction fetches four different W2 rows. Three
+// work decompositions, chosen by the number of tokens:
+//   many tokens (k_down_rows4): a wave owns four tokens of one chunk, one per 16-lane
+//     group; each group walks its own list, so no cross-lane reduction is needed. The
+//     rate is set by the texture-address path of each CU (one 16-byte load per lane and
+//     W2 row), which this keeps busiest.
+//   medium (k_twell_down): a wave owns one (token, chunk); its four groups take every
+//     fourth list entry and are summed at the end.
+//   few tokens (k_down_split): a 4-wave workgroup owns one (token, chunk), so sixteen
+//     groups split the list and all W2 row loads of a token leave in one round; this is
+//     the HBM-latency-bound decode case.
+// Overflow rows take their entries from the dense backup row.
 //
 // XCD-aware order: workgroup b runs on XCD b % 8 (round-robin dispatch), and all chunks
 // handled by one XCD are congruent mod 8, so that XCD's L2 only ever holds its own column
@@ -140,15 +149,258 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
   }
 }
 
+
+// Lane j of this lane's 16-lane row (DPP row broadcast); j must fold to a constant.
+TW_DEV uint32_t row_bcast(uint32_t v, int j) {
+  switch (j) {
+#define TW_BC(J) case J: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
+    TW_BC(0) TW_BC(1) TW_BC(2) TW_BC(3) TW_BC(4) TW_BC(5) TW_BC(6) TW_BC(7)
+    TW_BC(8) TW_BC(9) TW_BC(10) TW_BC(11) TW_BC(12) TW_BC(13) TW_BC(14) TW_BC(15)
+#undef TW_BC
+  }
+  return 0;
+}
+
+// acc[0..E) += v * (the E elements of w at p): one 16-byte W2 load, widened to fp32.
+template <typename WT, int E>
+TW_DEV void fma16(float (&acc)[E], float v, uint4 raw) {
+  float r[E];
+  if constexpr (sizeof(WT) == 2) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      r[2 * q] = __uint_as_float(w[q] << 16);
+      r[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    r[0] = __uint_as_float(raw.x); r[1] = __uint_as_float(raw.y);
+    r[2] = __uint_as_float(raw.z); r[3] = __uint_as_float(raw.w);
+  }
+#pragma unroll
+  for (int q = 0; q < E; ++q) acc[q] = fmaf(v, r[q], acc[q]);
+}
+
+TW_DEV void wave_sync_lds() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+// Backup row r of the overflow list, one chunk, by one wave: the dense row's nonzeros are
+// compacted 64 columns at a time into this wave's LDS batch; the four groups take every
+// fourth entry; the group sums are added and written by group 0.
+template <typename WT, typename VT, typename YT>
+TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *__restrict__ y, int r, int c,
+                       uint2 *lst) {
+  constexpr int E = Vec16<WT>::N;
+  constexpr int CW = 16 * E;
+  const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
+  const int col = c * CW + gl * E;
+  const bool cv = col < d;
+  const int t = h.ovf_rows[r];
+  const VT *row = (const VT *)h.ovf_dense + (size_t)r * h.cols;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int c0 = 0; c0 < h.cols; c0 += 64) {
+    const int j = c0 + lane;
+    const float v = j < h.cols ? ldv(row, j) : 0.f;
+    const bool nz = v != 0.f;
+    const uint64_t m = ballot64(nz);
+    if (m == 0) continue;
+    if (nz) lst[mbcnt64(m)] = make_uint2((uint32_t)j, __float_as_uint(v));
+    wave_sync_lds();
+    const int n = __popcll(m);
+    for (int e0 = 0; e0 < n; e0 += 16) {
+      uint4 raw[4];
+      float vv[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int e = e0 + g + 4 * k;
+        vv[k] = 0.f;
+        raw[k] = make_uint4(0, 0, 0, 0);
+        if (e < n) {
+          const uint2 p = lst[e];
+          vv[k] = __uint_as_float(p.y);
+          if (cv) raw[k] = *(const uint4 *)(w2 + (size_t)p.x * d + col);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < 4; ++k) fma16<WT, E>(acc, vv[k], raw[k]);
+    }
+    wave_sync_lds();
+  }
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    acc[q] += __shfl_xor(acc[q], 16, 64);
+    acc[q] += __shfl_xor(acc[q], 32, 64);
+  }
+  if (g == 0 && cv) {
+    const size_t o = (size_t)t * d + col;
+#pragma unroll
+    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+  }
+}
+
+// Many tokens. Workgroups [0, nmain): block b runs on XCD b % 8 and takes chunk
+// c = b % 8 + 8 * ((b / 8) / ntb) and token block (b / 8) % ntb of 16 tokens; wave w, group
+// g owns token 16 * block + 4 w + g. Per round of 16 entries each lane loads one list entry
+// (coalesced), the 16 (column, value) pairs are broadcast within the group, and all 16 W2
+// row loads are issued before their FMAs; the next round's entries are loaded meanwhile.
+// Workgroups [nmain, ...): the backup rows, one (row, chunk) per wave.
+template <typename WT, typename VT, typename YT>
+__global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restrict__ w2, int d,
+                                                    YT *__restrict__ y, int nchunk, int ntb, int nmain) {
+  __shared__ uint2 lst[4][64];
+  constexpr int E = Vec16<WT>::N;
+  constexpr int CW = 16 * E;
+  const int b = blockIdx.x;
+  const int lane = lane_id(), wave = threadIdx.x >> 6;
+  if (b >= nmain) {
+    const int i = b - nmain;
+    const int c = i % nchunk, r = (i / nchunk) * 4 + wave;
+    if (r >= min(*h.ovf_n, h.cap)) return;               // wave-uniform
+    backup_row<WT, VT, YT>(h, w2, d, y, r, c, lst[wave]);
+    return;
+  }
+  const int xcd = b & 7, i = b >> 3;
+  const int c = xcd + 8 * (i / ntb), tb = i % ntb;
+  if (c >= nchunk) return;
+  const int g = lane >> 4, gl = lane & 15;
+  const int t = tb * 16 + wave * 4 + g;
+  const int col = c * CW + gl * E;
+  const bool cv = col < d;
+  int nnz = t < h.rows ? h.row_nnz[t] : 0;
+  const bool normal = nnz >= 0;
+  if (!normal) nnz = 0;
+  int n = max(nnz, __shfl_xor(nnz, 16, 64));
+  n = max(n, __shfl_xor(n, 32, 64));
+  const uint2 *lp = h.row_list + (size_t)(t < h.rows ? t : 0) * h.n_t * h.S;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  uint2 pn = gl < nnz ? lp[gl] : make_uint2(0, 0);
+  for (int base = 0; base < n; base += 16) {
+    const uint2 p = pn;
+    if (base + 16 < n) pn = base + 16 + gl < nnz ? lp[base + 16 + gl] : make_uint2(0, 0);
+    uint4 raw[16];
+    float vv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t cj = row_bcast(p.x, j), vj = row_bcast(p.y, j);
+      const bool ok = base + j < nnz;
+      vv[j] = ok ? __uint_as_float(vj) : 0.f;
+      raw[j] = make_uint4(0, 0, 0, 0);
+      if (ok && cv) raw[j] = *(const uint4 *)(w2 + (size_t)cj * d + col);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
+  }
+  if (normal && t < h.rows && cv) {
+    const size_t o = (size_t)t * d + col;
+#pragma unroll
+    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+  }
+}
+
+// Few tokens: one (token, chunk) per workgroup of 4 waves = 16 groups. The list window of
+// up to 256 entries is read into LDS together with the count (speculatively: the scratch
+// row always holds n_t * S entries); group G takes entries G, G + 16, ..., so its (at most
+// 16) W2 row loads leave at once. Group sums are added across lanes and then across waves.
+template <typename WT, typename VT, typename YT>
+__global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restrict__ w2, int d,
+                                                    YT *__restrict__ y, int nchunk) {
+  constexpr int LW = 256, NG = 16, PER = LW / NG;
+  constexpr int E = Vec16<WT>::N;
+  constexpr int CW = 16 * E;
+  __shared__ uint2 lst[LW];
+  __shared__ float red[3][16 * E];
+  const int T = h.rows;
+  const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
+  const int c = xcd + 8 * (i / T), t = i % T;
+  if (c >= nchunk) return;                                  // uniform for the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int G = wave * 4 + (lane >> 4), gl = lane & 15;
+  const int col = c * CW + gl * E;
+  const bool cv = col < d;
+  const int cap = h.n_t * h.S;
+  const uint2 *src = h.row_list + (size_t)t * cap;
+  if (tid < LW) lst[tid] = tid < cap ? src[tid] : make_uint2(0, 0);
+  const int nnz = h.row_nnz[t];
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  if (nnz < 0) {                                            // backup row: one wave does it
+    if (wave == 0) backup_row<WT, VT, YT>(h, w2, d, y, h.ovf_slot[t], c, lst);
+    return;
+  }
+  __syncthreads();
+  for (int base = 0; base < nnz; base += LW) {
+    if (base > 0) {
+      __syncthreads();
+      if (tid < LW) lst[tid] = base + tid < cap ? src[base + tid] : make_uint2(0, 0);
+      __syncthreads();
+    }
+    const int n = min(LW, nnz - base);
+    uint4 raw[PER];
+    float vv[PER];
+#pragma unroll
+    for (int j = 0; j < PER; ++j) {
+      const int e = G + NG * j;
+      vv[j] = 0.f;
+      raw[j] = make_uint4(0, 0, 0, 0);
+      if (e < n) {
+        const uint2 p = lst[e];
+        vv[j] = __uint_as_float(p.y);
+        if (cv) raw[j] = *(const uint4 *)(w2 + (size_t)p.x * d + col);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PER; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
+  }
+#pragma unroll
+  for (int q = 0; q < E; ++q) {
+    acc[q] += __shfl_xor(acc[q], 16, 64);
+    acc[q] += __shfl_xor(acc[q], 32, 64);
+  }
+  if (wave > 0 && lane < 16)
+#pragma unroll
+    for (int q = 0; q < E; ++q) red[wave - 1][lane * E + q] = acc[q];
+  __syncthreads();
+  if (wave == 0 && lane < 16 && cv) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int q = 0; q < E; ++q) acc[q] += red[w][lane * E + q];
+    const size_t o = (size_t)t * d + col;
+#pragma unroll
+    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+  }
+}
+
+// Token-count thresholds between the three decompositions (measured at d = 2048 and 4096).
+constexpr int kRows4MinT = 512, kSplitMaxT = 16;
+
 template <typename WT, typename VT, typename YT>
 static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, hipStream_t s) {
   constexpr int CW = 16 * Vec16<WT>::N;
   const int nchunk = (d + CW - 1) / CW;
-  const long long per_xcd = (long long)h.rows * ((nchunk + 7) / 8);
+  const size_t per_xcd_chunks = (nchunk + 7) / 8;
   if (h.rows == 0) return hipSuccess;
-  const size_t grid = 8 * (size_t)per_xcd;
   hipLaunchKernelGGL((k_row_list<VT>), dim3((h.rows + 3) / 4), dim3(256), 0, s, h);
-  hipLaunchKernelGGL((k_twell_down<WT, VT, YT>), dim3((unsigned)grid), dim3(64), 0, s, h, w2, d, y, nchunk);
+  if (h.rows >= kRows4MinT) {
+    const int ntb = (h.rows + 15) / 16;
+    const size_t nmain = 8 * per_xcd_chunks * (size_t)ntb;
+    const size_t nback = (size_t)nchunk * ((h.cap + 3) / 4);
+    hipLaunchKernelGGL((k_down_rows4<WT, VT, YT>), dim3((unsigned)(nmain + nback)), dim3(256), 0, s, h, w2, d, y,
+                       nchunk, ntb, (int)nmain);
+  } else if (h.rows <= kSplitMaxT) {
+    hipLaunchKernelGGL((k_down_split<WT, VT, YT>), dim3((unsigned)(8 * per_xcd_chunks * h.rows)), dim3(256), 0, s,
+                       h, w2, d, y, nchunk);
+  } else {
+    hipLaunchKernelGGL((k_twell_down<WT, VT, YT>), dim3((unsigned)(8 * per_xcd_chunks * h.rows)), dim3(64), 0, s,
+                       h, w2, d, y, nchunk);
+  }
   return hipGetLastError();
 }
 

@@ -23,9 +23,11 @@ struct TwellIn {
   const void *vals;
   const int32_t *ovf_slot;
   const void *ovf_dense;
+  const int32_t *ovf_n;   // overflow rows found (may exceed cap)
+  const int32_t *ovf_rows;
   int32_t *row_nnz;       // scratch: compact list length per row (-1: use the backup row)
   uint2 *row_list;        // scratch: [rows][n_t * S] (column, fp32 value bits)
-  int rows, cols, n_t, S, W, val_bf16;
+  int rows, cols, n_t, S, W, val_bf16, cap;
 };
 
 // gemm.hip
