@@ -12,14 +12,18 @@
 //   1. row_nnz + scan        -> row_ptr: per-token entry counts (CSR offsets)
 //   2. csr_fill              -> (col, h) per entry, ascending column within a token
 //   3. sddmm                 -> dz per entry: one wave per token, dy[t] held in registers,
-//                               bf16 dot2 against the W2 rows of its active units
-//   4. list_gather (w1t)     -> dx
+//                               bf16 dot2 against the W2 rows of its active units; writes
+//                               the (unit, dz) pairs of the dx gather
+//   4. gather (w1t rows)     -> dx
 //   5. col_mask, col_tot, scan, col_off, csc_fill -> the same entries by unit (CSC), tokens
 //      ascending inside a unit, positions computed without a serial pass: per 32-token
 //      block every unit keeps the bit mask of its tokens; an entry's rank inside its unit
-//      is the block offset plus the popcount of the mask bits of earlier tokens
-//   6. list_gather dual (dy, x) -> dw2, dw1t; col_sum -> db1
+//      is the block offset plus the popcount of the mask bits of earlier tokens. Writes
+//      the (token, h) and (token, dz) pairs of the two dW gathers
+//   6. gather (dy rows) -> dw2; gather (x rows) -> dw1t, with db1 = sum of dz
+// The three gathers share the 4-lists-per-wave core of the forward down projection.
 #include "common.h"
+#include "gather.h"
 #include "launch.h"
 
 namespace tw {
@@ -134,14 +138,15 @@ __global__ __launch_bounds__(256) void k_csr_fill(TwellIn h, const int32_t *__re
 
 // ------------------------------------------------------------------------ 3. SDDMM
 
-// dz[e] = dy[t] . w2[col[e]] + l1 for the entries e of token t. One wave per token; the
-// token's dy row lives in registers (16-byte chunks, chunk c of lane l covers elements
-// c * 64 * EPC + l * EPC ...), two W2 rows are in flight per step.
+// dz[e] = dy[t] . w2[col[e]] + l1 for the entries e of token t, stored as the pair
+// (col[e], dz[e]). One wave per token; the token's dy row lives in registers (16-byte
+// chunks, chunk c of lane l covers elements c * 64 * EPC + l * EPC ...), two W2 rows are
+// in flight per step.
 template <typename T, int MAXC>
 __global__ __launch_bounds__(256) void k_sddmm(int T_rows, int d, const T *__restrict__ dy,
                                                const T *__restrict__ w2, const int32_t *__restrict__ row_ptr,
                                                const int32_t *__restrict__ col, float l1,
-                                               float *__restrict__ dz) {
+                                               uint2 *__restrict__ dz) {
   constexpr int EPC = 16 / sizeof(T);
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_rows) return;
@@ -188,8 +193,8 @@ __global__ __launch_bounds__(256) void k_sddmm(int T_rows, int d, const T *__res
     s0 = wave_sumf(s0);
     s1 = wave_sumf(s1);
     if (lane == 0) {
-      dz[e] = s0 + l1;
-      dz[e + 1] = s1 + l1;
+      dz[e] = make_uint2((uint32_t)j0, __float_as_uint(s0 + l1));
+      dz[e + 1] = make_uint2((uint32_t)j1, __float_as_uint(s1 + l1));
     }
   }
   if (e < end) {
@@ -201,91 +206,50 @@ __global__ __launch_bounds__(256) void k_sddmm(int T_rows, int d, const T *__res
       if (c < nch && e0 < d) s0 = dot(a[c], *(const uint4 *)(w2 + (size_t)j0 * d + e0), s0);
     }
     s0 = wave_sumf(s0);
-    if (lane == 0) dz[e] = s0 + l1;
+    if (lane == 0) dz[e] = make_uint2((uint32_t)j0, __float_as_uint(s0 + l1));
   }
 }
 
-// ------------------------------------------------------------------ 4/6. list gathers
+// ------------------------------------------------------------------ 4/6. gathers
 
-// out[r][c..] = sum over entries e of list r of val[e] * M[idx[e]][c..] (fp32 accumulation).
-// DUAL: a second value array / matrix / output sharing the same index list.
-// Work item (r, chunk); chunk = 16 lanes x 16 bytes; XCD-aware order as in the forward
-// down projection (chunks congruent mod 8 stay on one XCD).
-template <typename MT, bool DUAL>
-__global__ __launch_bounds__(64) void k_list_gather(int R, int d, int nchunk, const int32_t *__restrict__ ptr,
-                                                    const int32_t *__restrict__ idx,
-                                                    const float *__restrict__ va, const MT *__restrict__ Ma,
-                                                    float *__restrict__ outa, const float *__restrict__ vb,
-                                                    const MT *__restrict__ Mb, float *__restrict__ outb) {
-  const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
-  const int c = xcd + 8 * (i / R), r = i % R;
-  if (c >= nchunk) return;
+// out[r][chunk] = sum over the pairs (i, v) of list r of v * M[i][chunk], lists r given by
+// CSR offsets ptr. Block b runs on XCD b % 8 and takes chunk b % 8 + 8 * ((b / 8) / ntb)
+// and row block (b / 8) % ntb of 16 lists (chunks congruent mod 8 stay on one XCD, whose L2
+// then holds only those column slices of M). Rows without entries are written as zero.
+// rowsum (optional): rowsum[r] = sum of list r's values, written by the chunk-0 blocks.
+template <typename MT>
+__global__ __launch_bounds__(256) void k_gather_csr4(int R, int d, int nchunk, int ntb,
+                                                     const int32_t *__restrict__ ptr,
+                                                     const uint2 *__restrict__ pairs, const MT *__restrict__ M,
+                                                     float *__restrict__ out, float *__restrict__ rowsum) {
   constexpr int E = Vec16<MT>::N;
   constexpr int CW = 16 * E;
+  const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
+  const int c = xcd + 8 * (i / ntb), rb = i % ntb;
+  if (c >= nchunk) return;
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
-  const int colo = c * CW + gl * E;
-  const bool cv = colo < d;
-  float acc_a[E], acc_b[E];
-#pragma unroll
-  for (int q = 0; q < E; ++q) acc_a[q] = acc_b[q] = 0.f;
-  const int start = ptr[r], end = ptr[r + 1];
-  int e = start + g;
-  for (; e + 12 < end; e += 16) {
-    int j[4];
-    float v[4], w[4];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      j[u] = idx[e + 4 * u];
-      v[u] = va[e + 4 * u];
-      if (DUAL) w[u] = vb[e + 4 * u];
-    }
-    if (cv) {
-      float ra[4][E], rb[4][E];
-#pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        Vec16<MT>::load(Ma + (size_t)j[u] * d + colo, ra[u]);
-        if (DUAL) Vec16<MT>::load(Mb + (size_t)j[u] * d + colo, rb[u]);
-      }
-#pragma unroll
-      for (int u = 0; u < 4; ++u)
-#pragma unroll
-        for (int q = 0; q < E; ++q) {
-          acc_a[q] = fmaf(v[u], ra[u][q], acc_a[q]);
-          if (DUAL) acc_b[q] = fmaf(w[u], rb[u][q], acc_b[q]);
-        }
-    }
+  const int r = rb * 16 + (threadIdx.x >> 6) * 4 + g;
+  const int col = c * CW + gl * E;
+  const bool cv = col < d;
+  int start = 0, n = 0;
+  if (r < R) {
+    start = ptr[r];
+    n = ptr[r + 1] - start;
   }
-  for (; e < end; e += 4) {
-    const int jj = idx[e];
-    const float vv = va[e];
-    const float ww = DUAL ? vb[e] : 0.f;
-    if (cv) {
-      float ra[E], rb[E];
-      Vec16<MT>::load(Ma + (size_t)jj * d + colo, ra);
-      if (DUAL) Vec16<MT>::load(Mb + (size_t)jj * d + colo, rb);
+  int nw = max(n, __shfl_xor(n, 16, 64));
+  nw = max(nw, __shfl_xor(nw, 32, 64));
+  float acc[E];
 #pragma unroll
-      for (int q = 0; q < E; ++q) {
-        acc_a[q] = fmaf(vv, ra[q], acc_a[q]);
-        if (DUAL) acc_b[q] = fmaf(ww, rb[q], acc_b[q]);
-      }
-    }
+  for (int q = 0; q < E; ++q) acc[q] = 0.f;
+  const float vs = gather_list16<MT>(pairs + start, n, nw, M, d, col, cv, acc);
+  if (r < R && cv) {
+    const size_t o = (size_t)r * d + col;
+#pragma unroll
+    for (int q = 0; q < E; q += 4) *(float4 *)(out + o + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
   }
-#pragma unroll
-  for (int q = 0; q < E; ++q) {
-    acc_a[q] += __shfl_xor(acc_a[q], 16, 64);
-    acc_a[q] += __shfl_xor(acc_a[q], 32, 64);
-    if (DUAL) {
-      acc_b[q] += __shfl_xor(acc_b[q], 16, 64);
-      acc_b[q] += __shfl_xor(acc_b[q], 32, 64);
-    }
-  }
-  if (g == 0 && cv) {
-    const size_t o = (size_t)r * d + colo;
-#pragma unroll
-    for (int q = 0; q < E; q += 4) {
-      *(float4 *)(outa + o + q) = make_float4(acc_a[q], acc_a[q + 1], acc_a[q + 2], acc_a[q + 3]);
-      if (DUAL) *(float4 *)(outb + o + q) = make_float4(acc_b[q], acc_b[q + 1], acc_b[q + 2], acc_b[q + 3]);
-    }
+  if (rowsum && c == 0) {                        // uniform for the block
+    const float sv = group16_sum(vs);
+    if (gl == 0 && r < R) rowsum[r] = sv;
   }
 }
 
@@ -338,12 +302,13 @@ __global__ __launch_bounds__(256) void k_col_off(int NB, int f, const int32_t *_
   }
 }
 
-// Every CSR entry (t, j) goes to position off[t/32][j] + popc(mask[t/32][j] & lower bits).
+// Every CSR entry (t, j) goes to position off[t/32][j] + popc(mask[t/32][j] & lower bits)
+// of the unit-major lists: (t, h) for dw2, (t, dz) for dw1t.
 __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32_t *__restrict__ row_ptr,
                                                   const int32_t *__restrict__ col, const float *__restrict__ hval,
-                                                  const float *__restrict__ dz, const uint32_t *__restrict__ mask,
-                                                  const int32_t *__restrict__ off, int32_t *__restrict__ tok,
-                                                  float *__restrict__ hv, float *__restrict__ dzv) {
+                                                  const uint2 *__restrict__ dz, const uint32_t *__restrict__ mask,
+                                                  const int32_t *__restrict__ off, uint2 *__restrict__ th,
+                                                  uint2 *__restrict__ tdz) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_rows) return;
   const int lane = lane_id();
@@ -354,20 +319,9 @@ __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32
     const int j = col[k];
     const size_t bj = (size_t)b * f + j;
     const int pos = off[bj] + __popc(mask[bj] & lower);
-    tok[pos] = t;
-    hv[pos] = hval[k];
-    dzv[pos] = dz[k];
+    th[pos] = make_uint2((uint32_t)t, __float_as_uint(hval[k]));
+    tdz[pos] = make_uint2((uint32_t)t, dz[k].y);
   }
-}
-
-// db1[j] = sum of dz over unit j's entries
-__global__ __launch_bounds__(256) void k_col_sum(int f, const int32_t *__restrict__ col_ptr,
-                                                 const float *__restrict__ dzv, float *__restrict__ db1) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= f) return;
-  float s = 0.f;
-  for (int k = col_ptr[j]; k < col_ptr[j + 1]; ++k) s += dzv[k];
-  db1[j] = s;
 }
 
 // ------------------------------------------------------------------ host side
@@ -375,7 +329,7 @@ __global__ __launch_bounds__(256) void k_col_sum(int f, const int32_t *__restric
 // Register-resident dy needs ceil(d / (64 * EPC)) 16-byte chunks per lane (<= 16).
 template <typename T>
 static void sddmm_t(dim3 grid, hipStream_t s, int T_rows, int d, const T *dy, const T *w2, const int32_t *row_ptr,
-                    const int32_t *col, float l1, float *dz) {
+                    const int32_t *col, float l1, uint2 *dz) {
   constexpr int EPC = 16 / sizeof(T);
   const int nch = (d + 64 * EPC - 1) / (64 * EPC);
   if (nch <= 1) hipLaunchKernelGGL((k_sddmm<T, 1>), grid, dim3(256), 0, s, T_rows, d, dy, w2, row_ptr, col, l1, dz);
@@ -393,10 +347,11 @@ size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap) {
   const size_t NB = ((size_t)T + 31) / 32;
   size_t b = 0;
   b += al256(4 * ((size_t)T + 1));          // row_ptr
-  b += 3 * al256(4 * NZ);                   // col, hval, dz
+  b += 2 * al256(4 * NZ);                   // col, hval
+  b += al256(8 * NZ);                       // (col, dz) pairs
   b += 2 * al256(4 * NB * f);               // mask, cnt/off
   b += al256(4 * ((size_t)f + 1));          // col_ptr
-  b += 3 * al256(4 * NZ);                   // tok, hv, dzv
+  b += 2 * al256(8 * NZ);                   // (token, h), (token, dz) pairs
   return b;
 }
 
@@ -410,13 +365,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   int32_t *row_ptr = (int32_t *)take(4 * ((size_t)T + 1));
   int32_t *col = (int32_t *)take(4 * NZ);
   float *hval = (float *)take(4 * NZ);
-  float *dz = (float *)take(4 * NZ);
+  uint2 *dz = (uint2 *)take(8 * NZ);
   uint32_t *mask = (uint32_t *)take(4 * NB * f);
   int32_t *cnt = (int32_t *)take(4 * NB * f);
   int32_t *col_ptr = (int32_t *)take(4 * ((size_t)f + 1));
-  int32_t *tok = (int32_t *)take(4 * NZ);
-  float *hv = (float *)take(4 * NZ);
-  float *dzv = (float *)take(4 * NZ);
+  uint2 *th = (uint2 *)take(8 * NZ);
+  uint2 *tdz = (uint2 *)take(8 * NZ);
   const dim3 rows4((T + 3) / 4);
   if (T > 0) {
     if (h.val_bf16) hipLaunchKernelGGL(k_row_nnz<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr);
@@ -431,14 +385,16 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   }
   const int cw = a.bf16 ? 128 : 64;
   const int nchunk = (d + cw - 1) / cw;
+  auto gather = [&](int R, const int32_t *ptr, const uint2 *pairs, const void *M, float *out, float *rowsum) {
+    const int ntb = (R + 15) / 16;
+    const size_t grid = 8 * (size_t)ntb * ((nchunk + 7) / 8);
+    if (a.bf16) hipLaunchKernelGGL((k_gather_csr4<uint16_t>), dim3((unsigned)grid), dim3(256), 0, s, R, d, nchunk, ntb,
+                                   ptr, pairs, (const uint16_t *)M, out, rowsum);
+    else hipLaunchKernelGGL((k_gather_csr4<float>), dim3((unsigned)grid), dim3(256), 0, s, R, d, nchunk, ntb, ptr,
+                            pairs, (const float *)M, out, rowsum);
+  };
   // dx = dz . w1t
-  if (T > 0) {
-    const size_t grid = 8 * (size_t)T * ((nchunk + 7) / 8);
-    if (a.bf16) hipLaunchKernelGGL((k_list_gather<uint16_t, false>), dim3((unsigned)grid), dim3(64), 0, s, T, d, nchunk,
-                                   row_ptr, col, dz, (const uint16_t *)a.w1t, a.dx, nullptr, nullptr, nullptr);
-    else hipLaunchKernelGGL((k_list_gather<float, false>), dim3((unsigned)grid), dim3(64), 0, s, T, d, nchunk,
-                            row_ptr, col, dz, (const float *)a.w1t, a.dx, nullptr, nullptr, nullptr);
-  }
+  if (T > 0) gather(T, row_ptr, dz, a.w1t, a.dx, nullptr);
   // CSC
   if (T > 0) {
     hipLaunchKernelGGL(k_col_mask, dim3((unsigned)NB), dim3(256), (size_t)f * 4, s, T, f, row_ptr, col, mask, cnt);
@@ -449,17 +405,11 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, col_ptr, f, col_ptr);
   if (T > 0) {
     hipLaunchKernelGGL(k_col_off, dim3((f + 255) / 256), dim3(256), 0, s, (int)NB, f, col_ptr, cnt);
-    hipLaunchKernelGGL(k_csc_fill, rows4, dim3(256), 0, s, T, f, row_ptr, col, hval, dz, mask, cnt, tok, hv, dzv);
+    hipLaunchKernelGGL(k_csc_fill, rows4, dim3(256), 0, s, T, f, row_ptr, col, hval, dz, mask, cnt, th, tdz);
   }
-  // dw2 = h^T dy, dw1t = dz^T x  (every unit row written, zero if it has no entry)
-  {
-    const size_t grid = 8 * (size_t)f * ((nchunk + 7) / 8);
-    if (a.bf16) hipLaunchKernelGGL((k_list_gather<uint16_t, true>), dim3((unsigned)grid), dim3(64), 0, s, f, d, nchunk,
-                                   col_ptr, tok, hv, (const uint16_t *)a.dy, a.dw2, dzv, (const uint16_t *)a.x, a.dw1t);
-    else hipLaunchKernelGGL((k_list_gather<float, true>), dim3((unsigned)grid), dim3(64), 0, s, f, d, nchunk,
-                            col_ptr, tok, hv, (const float *)a.dy, a.dw2, dzv, (const float *)a.x, a.dw1t);
-  }
-  if (a.db1) hipLaunchKernelGGL(k_col_sum, dim3((f + 255) / 256), dim3(256), 0, s, f, col_ptr, dzv, a.db1);
+  // dw2 = h^T dy, dw1t = dz^T x (every unit row written, zero if it has no entry), db1
+  gather(f, col_ptr, th, a.dy, a.dw2, nullptr);
+  gather(f, col_ptr, tdz, a.x, a.dw1t, a.db1);
   return hipGetLastError();
 }
 

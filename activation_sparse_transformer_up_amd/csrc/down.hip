@@ -25,6 +25,7 @@
 // handled by one XCD are congruent mod 8, so that XCD's L2 only ever holds its own column
 // slices of W2; a chunk is finished for all tokens before the XCD moves to its next one.
 #include "common.h"
+#include "gather.h"
 #include "launch.h"
 
 namespace tw {
@@ -150,36 +151,6 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
 }
 
 
-// Lane j of this lane's 16-lane row (DPP row broadcast); j must fold to a constant.
-TW_DEV uint32_t row_bcast(uint32_t v, int j) {
-  switch (j) {
-#define TW_BC(J) case J: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
-    TW_BC(0) TW_BC(1) TW_BC(2) TW_BC(3) TW_BC(4) TW_BC(5) TW_BC(6) TW_BC(7)
-    TW_BC(8) TW_BC(9) TW_BC(10) TW_BC(11) TW_BC(12) TW_BC(13) TW_BC(14) TW_BC(15)
-#undef TW_BC
-  }
-  return 0;
-}
-
-// acc[0..E) += v * (the E elements of w at p): one 16-byte W2 load, widened to fp32.
-template <typename WT, int E>
-TW_DEV void fma16(float (&acc)[E], float v, uint4 raw) {
-  float r[E];
-  if constexpr (sizeof(WT) == 2) {
-    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
-#pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      r[2 * q] = __uint_as_float(w[q] << 16);
-      r[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
-    }
-  } else {
-    r[0] = __uint_as_float(raw.x); r[1] = __uint_as_float(raw.y);
-    r[2] = __uint_as_float(raw.z); r[3] = __uint_as_float(raw.w);
-  }
-#pragma unroll
-  for (int q = 0; q < E; ++q) acc[q] = fmaf(v, r[q], acc[q]);
-}
-
 TW_DEV void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
   __builtin_amdgcn_wave_barrier();
@@ -244,9 +215,7 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
 
 // Many tokens. Workgroups [0, nmain): block b runs on XCD b % 8 and takes chunk
 // c = b % 8 + 8 * ((b / 8) / ntb) and token block (b / 8) % ntb of 16 tokens; wave w, group
-// g owns token 16 * block + 4 w + g. Per round of 16 entries each lane loads one list entry
-// (coalesced), the 16 (column, value) pairs are broadcast within the group, and all 16 W2
-// row loads are issued before their FMAs; the next round's entries are loaded meanwhile.
+// g owns token 16 * block + 4 w + g and walks its list with gather_list16.
 // Workgroups [nmain, ...): the backup rows, one (row, chunk) per wave.
 template <typename WT, typename VT, typename YT>
 __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restrict__ w2, int d,
@@ -279,23 +248,7 @@ __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restr
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  uint2 pn = gl < nnz ? lp[gl] : make_uint2(0, 0);
-  for (int base = 0; base < n; base += 16) {
-    const uint2 p = pn;
-    if (base + 16 < n) pn = base + 16 + gl < nnz ? lp[base + 16 + gl] : make_uint2(0, 0);
-    uint4 raw[16];
-    float vv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t cj = row_bcast(p.x, j), vj = row_bcast(p.y, j);
-      const bool ok = base + j < nnz;
-      vv[j] = ok ? __uint_as_float(vj) : 0.f;
-      raw[j] = make_uint4(0, 0, 0, 0);
-      if (ok && cv) raw[j] = *(const uint4 *)(w2 + (size_t)cj * d + col);
-    }
-#pragma unroll
-    for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
-  }
+  gather_list16<WT>(lp, nnz, n, w2, d, col, cv, acc);
   if (normal && t < h.rows && cv) {
     const size_t o = (size_t)t * d + col;
 #pragma unroll

@@ -1,0 +1,89 @@
+// Shared core of the sparse row gathers: the forward down projection (rows of W2 selected
+// by a token's active units), and the backward dx (rows of w1t) and dW (rows of dy and x
+// selected by a unit's tokens).
+//
+//   out[r][c0 .. c0 + CW) = sum over the entries (i, v) of list r of v * M[i][c0 .. c0 + CW)
+//
+// Lists hold packed (row index, fp32 value bits) pairs. A 16-lane group owns one list and
+// one column chunk: lane l covers 16 bytes (8 bf16 or 4 fp32 elements) of every selected
+// row, so a chunk is 256 bytes of bf16 or fp32 rows and one vector load instruction of the
+// wave fetches four rows of four lists. Per round a lane loads one pair of its group's list
+// (coalesced), the sixteen pairs are broadcast inside the group with a DPP row broadcast,
+// and all sixteen row loads are issued before the FMAs; the next round's pairs are loaded
+// meanwhile. Accumulation is fp32 in list order.
+#pragma once
+#include "common.h"
+
+namespace tw {
+
+// Lane j of this lane's 16-lane row (DPP row broadcast); j must fold to a constant.
+TW_DEV uint32_t row_bcast(uint32_t v, int j) {
+  switch (j) {
+#define TW_BC(J) case J: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
+    TW_BC(0) TW_BC(1) TW_BC(2) TW_BC(3) TW_BC(4) TW_BC(5) TW_BC(6) TW_BC(7)
+    TW_BC(8) TW_BC(9) TW_BC(10) TW_BC(11) TW_BC(12) TW_BC(13) TW_BC(14) TW_BC(15)
+#undef TW_BC
+  }
+  return 0;
+}
+
+// acc[0..E) += v * the E elements in the 16 bytes raw (bf16 widened exactly to fp32).
+template <typename WT, int E>
+TW_DEV void fma16(float (&acc)[E], float v, uint4 raw) {
+  float r[E];
+  if constexpr (sizeof(WT) == 2) {
+    const uint32_t w[4] = {raw.x, raw.y, raw.z, raw.w};
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      r[2 * q] = __uint_as_float(w[q] << 16);
+      r[2 * q + 1] = __uint_as_float(w[q] & 0xFFFF0000u);
+    }
+  } else {
+    r[0] = __uint_as_float(raw.x); r[1] = __uint_as_float(raw.y);
+    r[2] = __uint_as_float(raw.z); r[3] = __uint_as_float(raw.w);
+  }
+#pragma unroll
+  for (int q = 0; q < E; ++q) acc[q] = fmaf(v, r[q], acc[q]);
+}
+
+// The group's list p[0 .. n) against rows of M (row length d); this lane's columns start
+// at col (cv: inside the row). nw = the largest n of the wave's four groups (the loop bound
+// must be wave-uniform). Returns this lane's share of the sum of the list's values (lane l
+// adds entries l, l + 16, ...).
+template <typename WT>
+TW_DEV float gather_list16(const uint2 *__restrict__ p, int n, int nw, const WT *__restrict__ M, int d, int col,
+                           bool cv, float (&acc)[Vec16<WT>::N]) {
+  constexpr int E = Vec16<WT>::N;
+  const int gl = lane_id() & 15;
+  float vs = 0.f;
+  uint2 pn = gl < n ? p[gl] : make_uint2(0, 0);
+  for (int base = 0; base < nw; base += 16) {
+    const uint2 q = pn;
+    if (base + 16 < nw) pn = base + 16 + gl < n ? p[base + 16 + gl] : make_uint2(0, 0);
+    vs += __uint_as_float(q.y);                 // zero for entries past n
+    uint4 raw[16];
+    float vv[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      const uint32_t ij = row_bcast(q.x, j), vj = row_bcast(q.y, j);
+      const bool ok = base + j < n;
+      vv[j] = ok ? __uint_as_float(vj) : 0.f;
+      raw[j] = make_uint4(0, 0, 0, 0);
+      if (ok && cv) raw[j] = *(const uint4 *)(M + (size_t)ij * d + col);
+    }
+#pragma unroll
+    for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
+  }
+  return vs;
+}
+
+// Sum over the 16 lanes of a group.
+TW_DEV float group16_sum(float v) {
+  v += __shfl_xor(v, 1, 64);
+  v += __shfl_xor(v, 2, 64);
+  v += __shfl_xor(v, 4, 64);
+  v += __shfl_xor(v, 8, 64);
+  return v;
+}
+
+}  // namespace tw
