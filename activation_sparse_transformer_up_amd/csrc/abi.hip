@@ -229,9 +229,11 @@ int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t i
   return TWELL_OK;
 }
 
-size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, const twell_matrix_t *h) {
+size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, int32_t in_dtype,
+                                     const twell_matrix_t *h) {
   if (!h || T < 0 || d_model <= 0 || d_ff <= 0 || h->tile_w <= 0 || h->slots <= 0 || h->ovf_cap < 0) return 0;
-  return bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap);
+  if (!dtype_ok(in_dtype)) return 0;
+  return bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap, in_dtype == TWELL_BF16);
 }
 
 int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dtype, int32_t T,
@@ -246,10 +248,10 @@ int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dty
   if (st) return st;
   if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
   if (!al16(dy) || !al16(dx) || !al16(dw1t) || !al16(dw2) || !al4(db1) || !al16(workspace)) return TWELL_ERR_ALIGN;
-  // dy lives in registers (<= 16 chunks of 16 bytes per lane); unit masks of a 32-token
-  // block live in LDS (4 bytes per unit)
-  if (d_model > (in_dtype == TWELL_BF16 ? 8192 : 4096) || d_ff > 16384) return TWELL_ERR_UNSUPPORTED;
-  const size_t need = bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap);
+  // unit masks of a 32-token block live in LDS (4 bytes per unit)
+  if (d_ff > 16384) return TWELL_ERR_UNSUPPORTED;
+  const size_t need =
+      bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap, in_dtype == TWELL_BF16);
   if (workspace_bytes < need) return TWELL_ERR_WORKSPACE;
   BwdArgs a;
   a.h = in_of(h);

@@ -11,9 +11,11 @@
 // Steps (all on the caller's stream, scratch in the caller's workspace):
 //   1. row_nnz + scan        -> row_ptr: per-token entry counts (CSR offsets)
 //   2. csr_fill              -> (col, h) per entry, ascending column within a token
-//   3. sddmm                 -> dz per entry: one wave per token, dy[t] held in registers,
-//                               bf16 dot2 against the W2 rows of its active units; writes
-//                               the (unit, dz) pairs of the dx gather
+//   3. sddmm                 -> dz per entry, in two kernels: per 16-byte-per-lane column
+//                               chunk the partial dot products of dy[t] with the W2 rows of
+//                               its active units (the gathers' decomposition, so each XCD
+//                               reads only its slices of W2), then their sum in chunk order
+//                               plus l1, stored as the (unit, dz) pairs of the dx gather
 //   4. gather (w1t rows)     -> dx
 //   5. col_mask, col_tot, scan, col_off, csc_fill -> the same entries by unit (CSC), tokens
 //      ascending inside a unit, positions computed without a serial pass: per 32-token
@@ -22,6 +24,8 @@
 //      the (token, h) and (token, dz) pairs of the two dW gathers
 //   6. gather (dy rows) -> dw2; gather (x rows) -> dw1t, with db1 = sum of dz
 // The three gathers share the 4-lists-per-wave core of the forward down projection.
+#include <algorithm>
+
 #include "common.h"
 #include "gather.h"
 #include "launch.h"
@@ -138,75 +142,102 @@ __global__ __launch_bounds__(256) void k_csr_fill(TwellIn h, const int32_t *__re
 
 // ------------------------------------------------------------------------ 3. SDDMM
 
-// dz[e] = dy[t] . w2[col[e]] + l1 for the entries e of token t, stored as the pair
-// (col[e], dz[e]). One wave per token; the token's dy row lives in registers (16-byte
-// chunks, chunk c of lane l covers elements c * 64 * EPC + l * EPC ...), two W2 rows are
-// in flight per step.
-template <typename T, int MAXC>
-__global__ __launch_bounds__(256) void k_sddmm(int T_rows, int d, const T *__restrict__ dy,
-                                               const T *__restrict__ w2, const int32_t *__restrict__ row_ptr,
-                                               const int32_t *__restrict__ col, float l1,
-                                               uint2 *__restrict__ dz) {
-  constexpr int EPC = 16 / sizeof(T);
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T_rows) return;
-  const int lane = lane_id();
-  const int nch = (d + 64 * EPC - 1) / (64 * EPC);
-  uint4 a[MAXC];
-#pragma unroll
-  for (int c = 0; c < MAXC; ++c) {
-    const int e0 = c * 64 * EPC + lane * EPC;
-    a[c] = (c < nch && e0 < d) ? *(const uint4 *)(dy + (size_t)t * d + e0) : make_uint4(0, 0, 0, 0);
+// The 16-byte dot product of a chunk of dy with a chunk of a W2 row, fp32 accumulation
+// (bf16 pairs through v_dot2_f32_bf16).
+template <typename T>
+TW_DEV float dot16(const uint4 &x, const uint4 &y) {
+  float acc = 0.f;
+  if constexpr (sizeof(T) == 2) {
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.x), __builtin_bit_cast(bf16x2_t, y.x), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.y), __builtin_bit_cast(bf16x2_t, y.y), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.z), __builtin_bit_cast(bf16x2_t, y.z), acc, false);
+    acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.w), __builtin_bit_cast(bf16x2_t, y.w), acc, false);
+  } else {
+    acc = fmaf(__uint_as_float(x.x), __uint_as_float(y.x), acc);
+    acc = fmaf(__uint_as_float(x.y), __uint_as_float(y.y), acc);
+    acc = fmaf(__uint_as_float(x.z), __uint_as_float(y.z), acc);
+    acc = fmaf(__uint_as_float(x.w), __uint_as_float(y.w), acc);
   }
-  auto dot = [&](const uint4 &x, const uint4 &y, float acc) -> float {
-    if constexpr (sizeof(T) == 2) {
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.x), __builtin_bit_cast(bf16x2_t, y.x), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.y), __builtin_bit_cast(bf16x2_t, y.y), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.z), __builtin_bit_cast(bf16x2_t, y.z), acc, false);
-      acc = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, x.w), __builtin_bit_cast(bf16x2_t, y.w), acc, false);
-    } else {
-      acc = fmaf(__uint_as_float(x.x), __uint_as_float(y.x), acc);
-      acc = fmaf(__uint_as_float(x.y), __uint_as_float(y.y), acc);
-      acc = fmaf(__uint_as_float(x.z), __uint_as_float(y.z), acc);
-      acc = fmaf(__uint_as_float(x.w), __uint_as_float(y.w), acc);
-    }
-    return acc;
-  };
-  const int start = row_ptr[t], end = row_ptr[t + 1];
-  int e = start;
-  for (; e + 1 < end; e += 2) {
-    const int j0 = col[e], j1 = col[e + 1];
-    uint4 b0[MAXC], b1[MAXC];
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int e0 = c * 64 * EPC + lane * EPC;
-      const bool ok = c < nch && e0 < d;
-      b0[c] = ok ? *(const uint4 *)(w2 + (size_t)j0 * d + e0) : make_uint4(0, 0, 0, 0);
-      b1[c] = ok ? *(const uint4 *)(w2 + (size_t)j1 * d + e0) : make_uint4(0, 0, 0, 0);
-    }
-    float s0 = 0.f, s1 = 0.f;
-#pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      s0 = dot(a[c], b0[c], s0);
-      s1 = dot(a[c], b1[c], s1);
-    }
-    s0 = wave_sumf(s0);
-    s1 = wave_sumf(s1);
-    if (lane == 0) {
-      dz[e] = make_uint2((uint32_t)j0, __float_as_uint(s0 + l1));
-      dz[e + 1] = make_uint2((uint32_t)j1, __float_as_uint(s1 + l1));
-    }
+  return acc;
+}
+
+// v[0..16) of the 16 lanes of a group summed across the group, one sum per lane: at step m
+// (8, 4, 2, 1) a lane keeps the half of its remaining values selected by bit m of its lane
+// index and adds the partner's (lane ^ m) copy of that half. Lane l ends with entry l.
+TW_DEV float group16_transpose_sum(float (&v)[16], int gl) {
+  static_for<4>([&](auto S) {
+    constexpr int m = 8 >> decltype(S)::value, half = m;   // values left: 2 * m
+    const bool hi = gl & m;
+    static_for<half>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      const float keep = hi ? v[k + half] : v[k];
+      const float send = hi ? v[k] : v[k + half];
+      v[k] = keep + __shfl_xor(send, m, 64);
+    });
+  });
+  return v[0];
+}
+
+// part[c][e] = dy[t][chunk c] . w2[col[e]][chunk c] for the entries e of token t. Block b
+// runs on XCD b % 8 with chunk b % 8 + 8 * ((b / 8) / ntb) and token block (b / 8) % ntb of
+// 16 tokens, one per 16-lane group; lane l holds 16 bytes of dy[t]. Per round the group
+// loads its next 16 columns (coalesced), broadcasts them, issues the 16 W2 row loads, and
+// the 16 per-lane dot products are summed across the group so that lane l stores entry l
+// (a coalesced 64-byte store per round).
+template <typename T>
+__global__ __launch_bounds__(256) void k_sddmm_part(int T_rows, int d, int nchunk, int ntb, const T *__restrict__ dy,
+                                                    const T *__restrict__ w2, const int32_t *__restrict__ row_ptr,
+                                                    const int32_t *__restrict__ col, size_t nz,
+                                                    float *__restrict__ part) {
+  constexpr int E = Vec16<T>::N;
+  constexpr int CW = 16 * E;
+  const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
+  const int c = xcd + 8 * (i / ntb), tb = i % ntb;
+  if (c >= nchunk) return;
+  const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
+  const int t = tb * 16 + (threadIdx.x >> 6) * 4 + g;
+  const int colo = c * CW + gl * E;
+  const bool cv = colo < d;
+  int start = 0, n = 0;
+  if (t < T_rows) {
+    start = row_ptr[t];
+    n = row_ptr[t + 1] - start;
   }
-  if (e < end) {
-    const int j0 = col[e];
-    float s0 = 0.f;
+  int nw = max(n, __shfl_xor(n, 16, 64));
+  nw = max(nw, __shfl_xor(nw, 32, 64));
+  const uint4 a = (t < T_rows && cv) ? *(const uint4 *)(dy + (size_t)t * d + colo) : make_uint4(0, 0, 0, 0);
+  const int32_t *cp = col + start;
+  float *out = part + (size_t)c * nz + start;
+  int jn = gl < n ? cp[gl] : 0;
+  for (int base = 0; base < nw; base += 16) {
+    const int jq = jn;
+    if (base + 16 < nw) jn = base + 16 + gl < n ? cp[base + 16 + gl] : 0;
+    uint4 raw[16];
+    static_for<16>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const uint32_t jj = row_bcast<j>((uint32_t)jq);
+      raw[j] = make_uint4(0, 0, 0, 0);
+      if (base + j < n && cv) raw[j] = *(const uint4 *)(w2 + (size_t)jj * d + colo);
+    });
+    float v[16];
 #pragma unroll
-    for (int c = 0; c < MAXC; ++c) {
-      const int e0 = c * 64 * EPC + lane * EPC;
-      if (c < nch && e0 < d) s0 = dot(a[c], *(const uint4 *)(w2 + (size_t)j0 * d + e0), s0);
-    }
-    s0 = wave_sumf(s0);
-    if (lane == 0) dz[e] = make_uint2((uint32_t)j0, __float_as_uint(s0 + l1));
+    for (int j = 0; j < 16; ++j) v[j] = dot16<T>(a, raw[j]);
+    const float tot = group16_transpose_sum(v, gl);
+    if (base + gl < n) out[base + gl] = tot;
+  }
+}
+
+// dz[e] = (sum over chunks c of part[c][e], in chunk order) + l1, stored as (col[e], dz),
+// for the row_ptr[T] entries in use (grid-stride over a fixed grid).
+__global__ __launch_bounds__(256) void k_sddmm_sum(int T_rows, const int32_t *__restrict__ row_ptr, size_t nz,
+                                                   int nchunk, const float *__restrict__ part,
+                                                   const int32_t *__restrict__ col, float l1,
+                                                   uint2 *__restrict__ dz) {
+  const size_t total = (size_t)row_ptr[T_rows];
+  for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
+    float s = 0.f;
+    for (int c = 0; c < nchunk; ++c) s += part[(size_t)c * nz + e];
+    dz[e] = make_uint2((uint32_t)col[e], __float_as_uint(s + l1));
   }
 }
 
@@ -326,26 +357,18 @@ __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32
 
 // ------------------------------------------------------------------ host side
 
-// Register-resident dy needs ceil(d / (64 * EPC)) 16-byte chunks per lane (<= 16).
-template <typename T>
-static void sddmm_t(dim3 grid, hipStream_t s, int T_rows, int d, const T *dy, const T *w2, const int32_t *row_ptr,
-                    const int32_t *col, float l1, uint2 *dz) {
-  constexpr int EPC = 16 / sizeof(T);
-  const int nch = (d + 64 * EPC - 1) / (64 * EPC);
-  if (nch <= 1) hipLaunchKernelGGL((k_sddmm<T, 1>), grid, dim3(256), 0, s, T_rows, d, dy, w2, row_ptr, col, l1, dz);
-  else if (nch <= 2) hipLaunchKernelGGL((k_sddmm<T, 2>), grid, dim3(256), 0, s, T_rows, d, dy, w2, row_ptr, col, l1, dz);
-  else if (nch <= 4) hipLaunchKernelGGL((k_sddmm<T, 4>), grid, dim3(256), 0, s, T_rows, d, dy, w2, row_ptr, col, l1, dz);
-  else if (nch <= 8) hipLaunchKernelGGL((k_sddmm<T, 8>), grid, dim3(256), 0, s, T_rows, d, dy, w2, row_ptr, col, l1, dz);
-  else hipLaunchKernelGGL((k_sddmm<T, 16>), grid, dim3(256), 0, s, T_rows, d, dy, w2, row_ptr, col, l1, dz);
-}
-
 static size_t al256(size_t x) { return (x + 255) & ~(size_t)255; }
 
-size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap) {
-  (void)d;
+static int sddmm_chunks(int d, int bf16) {
+  const int cw = bf16 ? 128 : 64;
+  return (d + cw - 1) / cw;
+}
+
+size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf16) {
   const size_t NZ = (size_t)T * n_t * S + (size_t)(cap < T ? cap : T) * f;
   const size_t NB = ((size_t)T + 31) / 32;
   size_t b = 0;
+  b += al256(4 * NZ * (size_t)sddmm_chunks(d, bf16));   // SDDMM partial dot products
   b += al256(4 * ((size_t)T + 1));          // row_ptr
   b += 2 * al256(4 * NZ);                   // col, hval
   b += al256(8 * NZ);                       // (col, dz) pairs
@@ -360,8 +383,10 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const int T = h.rows, f = h.cols, d = a.d;
   const size_t NZ = (size_t)T * h.n_t * h.S + (size_t)(a.cap < T ? a.cap : T) * f;
   const size_t NB = ((size_t)T + 31) / 32;
+  const int nchunk = sddmm_chunks(d, a.bf16);
   char *p = (char *)a.ws;
   auto take = [&](size_t bytes) { char *q = p; p += al256(bytes); return q; };
+  float *part = (float *)take(4 * NZ * (size_t)nchunk);
   int32_t *row_ptr = (int32_t *)take(4 * ((size_t)T + 1));
   int32_t *col = (int32_t *)take(4 * NZ);
   float *hval = (float *)take(4 * NZ);
@@ -380,11 +405,15 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   if (T > 0) {
     if (h.val_bf16) hipLaunchKernelGGL(k_csr_fill<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr, col, hval);
     else hipLaunchKernelGGL(k_csr_fill<float>, rows4, dim3(256), 0, s, h, row_ptr, col, hval);
-    if (a.bf16) sddmm_t<uint16_t>(rows4, s, T, d, (const uint16_t *)a.dy, (const uint16_t *)a.w2, row_ptr, col, a.l1, dz);
-    else sddmm_t<float>(rows4, s, T, d, (const float *)a.dy, (const float *)a.w2, row_ptr, col, a.l1, dz);
+    const int ntb = (T + 15) / 16;
+    const size_t grid = 8 * (size_t)ntb * ((nchunk + 7) / 8);
+    if (a.bf16) hipLaunchKernelGGL((k_sddmm_part<uint16_t>), dim3((unsigned)grid), dim3(256), 0, s, T, d, nchunk, ntb,
+                                   (const uint16_t *)a.dy, (const uint16_t *)a.w2, row_ptr, col, NZ, part);
+    else hipLaunchKernelGGL((k_sddmm_part<float>), dim3((unsigned)grid), dim3(256), 0, s, T, d, nchunk, ntb,
+                            (const float *)a.dy, (const float *)a.w2, row_ptr, col, NZ, part);
+    const unsigned sum_grid = (unsigned)std::min<size_t>((NZ + 255) / 256, 4096);
+    hipLaunchKernelGGL(k_sddmm_sum, dim3(sum_grid), dim3(256), 0, s, T, row_ptr, NZ, nchunk, part, col, a.l1, dz);
   }
-  const int cw = a.bf16 ? 128 : 64;
-  const int nchunk = (d + cw - 1) / cw;
   auto gather = [&](int R, const int32_t *ptr, const uint2 *pairs, const void *M, float *out, float *rowsum) {
     const int ntb = (R + 15) / 16;
     const size_t grid = 8 * (size_t)ntb * ((nchunk + 7) / 8);

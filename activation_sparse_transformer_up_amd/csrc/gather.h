@@ -12,19 +12,27 @@
 // and all sixteen row loads are issued before the FMAs; the next round's pairs are loaded
 // meanwhile. Accumulation is fp32 in list order.
 #pragma once
+#include <type_traits>
+#include <utility>
+
 #include "common.h"
 
 namespace tw {
 
-// Lane j of this lane's 16-lane row (DPP row broadcast); j must fold to a constant.
-TW_DEV uint32_t row_bcast(uint32_t v, int j) {
-  switch (j) {
-#define TW_BC(J) case J: return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
-    TW_BC(0) TW_BC(1) TW_BC(2) TW_BC(3) TW_BC(4) TW_BC(5) TW_BC(6) TW_BC(7)
-    TW_BC(8) TW_BC(9) TW_BC(10) TW_BC(11) TW_BC(12) TW_BC(13) TW_BC(14) TW_BC(15)
-#undef TW_BC
-  }
-  return 0;
+// f(std::integral_constant<int, 0>()), ..., f(std::integral_constant<int, N - 1>()): the
+// index is a constant expression inside f, whatever the inliner and unroller do.
+template <typename F, int... J>
+TW_DEV void static_for_impl(F &&f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>()), ...);
+}
+template <int N, typename F> TW_DEV void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
+
+// Lane J of this lane's 16-lane row (DPP row broadcast).
+template <int J> TW_DEV uint32_t row_bcast(uint32_t v) {
+  static_assert(J >= 0 && J < 16, "row lane");
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
 }
 
 // acc[0..E) += v * the E elements in the 16 bytes raw (bf16 widened exactly to fp32).
@@ -63,14 +71,14 @@ TW_DEV float gather_list16(const uint2 *__restrict__ p, int n, int nw, const WT 
     vs += __uint_as_float(q.y);                 // zero for entries past n
     uint4 raw[16];
     float vv[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const uint32_t ij = row_bcast(q.x, j), vj = row_bcast(q.y, j);
+    static_for<16>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const uint32_t ij = row_bcast<j>(q.x), vj = row_bcast<j>(q.y);
       const bool ok = base + j < n;
       vv[j] = ok ? __uint_as_float(vj) : 0.f;
       raw[j] = make_uint4(0, 0, 0, 0);
       if (ok && cv) raw[j] = *(const uint4 *)(M + (size_t)ij * d + col);
-    }
+    });
 #pragma unroll
     for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
   }

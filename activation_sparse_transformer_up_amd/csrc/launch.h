@@ -54,7 +54,7 @@ struct BwdArgs {
   void *ws;
   int d, bf16, cap;
 };
-size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap);
+size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf16);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 
 // nm.hip
