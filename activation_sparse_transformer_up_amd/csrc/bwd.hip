@@ -180,13 +180,15 @@ TW_DEV float group16_transpose_sum(float (&v)[16], int gl) {
 
 // part[c][e] = dy[t][chunk c] . w2[col[e]][chunk c] for the entries e of token t. Block b
 // runs on XCD b % 8 with chunk b % 8 + 8 * ((b / 8) / ntb) and token block (b / 8) % ntb of
-// 16 tokens, one per 16-lane group; lane l holds 16 bytes of dy[t]. Per round the group
+// 16 tokens (taken in the order perm), one per 16-lane group; lane l holds 16 bytes of
+// dy[t]. Per round the group
 // loads its next 16 columns (coalesced), broadcasts them, issues the 16 W2 row loads, and
 // the 16 per-lane dot products are summed across the group so that lane l stores entry l
 // (a coalesced 64-byte store per round).
 template <typename T>
 __global__ __launch_bounds__(256) void k_sddmm_part(int T_rows, int d, int nchunk, int ntb, const T *__restrict__ dy,
                                                     const T *__restrict__ w2, const int32_t *__restrict__ row_ptr,
+                                                    const int32_t *__restrict__ perm,
                                                     const int32_t *__restrict__ col, size_t nz,
                                                     float *__restrict__ part) {
   constexpr int E = Vec16<T>::N;
@@ -195,7 +197,8 @@ __global__ __launch_bounds__(256) void k_sddmm_part(int T_rows, int d, int nchun
   const int c = xcd + 8 * (i / ntb), tb = i % ntb;
   if (c >= nchunk) return;
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
-  const int t = tb * 16 + (threadIdx.x >> 6) * 4 + g;
+  const int ti = tb * 16 + (threadIdx.x >> 6) * 4 + g;
+  const int t = ti < T_rows ? perm[ti] : T_rows;
   const int colo = c * CW + gl * E;
   const bool cv = colo < d;
   int start = 0, n = 0;
@@ -241,6 +244,34 @@ __global__ __launch_bounds__(256) void k_sddmm_sum(int T_rows, const int32_t *__
   }
 }
 
+// --------------------------------------------------------- list order for the gathers
+
+// perm = the R lists ordered by length, longest first, in 64 buckets of 16 entries (the
+// gathers walk a list 16 entries per round, so the four lists of a wave then take the same
+// number of rounds; lists of 1008 entries and more share the first bucket and start
+// first). The order inside a bucket depends on atomic arrival order; every output row is
+// still summed by one group in list order, so results do not depend on it. One workgroup.
+__global__ __launch_bounds__(1024) void k_order_by_len(int R, const int32_t *__restrict__ ptr, int32_t *__restrict__ perm) {
+  constexpr int NB = 64;
+  __shared__ int hist[NB];
+  const int tid = threadIdx.x;
+  if (tid < NB) hist[tid] = 0;
+  __syncthreads();
+  auto bucket = [&](int r) { return NB - 1 - min(NB - 1, (ptr[r + 1] - ptr[r]) >> 4); };
+  for (int r = tid; r < R; r += 1024) atomicAdd(&hist[bucket(r)], 1);
+  __syncthreads();
+  if (tid == 0) {
+    int run = 0;
+    for (int b = 0; b < NB; ++b) {
+      const int c = hist[b];
+      hist[b] = run;
+      run += c;
+    }
+  }
+  __syncthreads();
+  for (int r = tid; r < R; r += 1024) perm[atomicAdd(&hist[bucket(r)], 1)] = r;
+}
+
 // ------------------------------------------------------------------ 4/6. gathers
 
 // out[r][chunk] = sum over the pairs (i, v) of list r of v * M[i][chunk], lists r given by
@@ -248,9 +279,11 @@ __global__ __launch_bounds__(256) void k_sddmm_sum(int T_rows, const int32_t *__
 // and row block (b / 8) % ntb of 16 lists (chunks congruent mod 8 stay on one XCD, whose L2
 // then holds only those column slices of M). Rows without entries are written as zero.
 // rowsum (optional): rowsum[r] = sum of list r's values, written by the chunk-0 blocks.
+// Rows are taken in the order perm (k_order_by_len).
 template <typename MT>
 __global__ __launch_bounds__(256) void k_gather_csr4(int R, int d, int nchunk, int ntb,
                                                      const int32_t *__restrict__ ptr,
+                                                     const int32_t *__restrict__ perm,
                                                      const uint2 *__restrict__ pairs, const MT *__restrict__ M,
                                                      float *__restrict__ out, float *__restrict__ rowsum) {
   constexpr int E = Vec16<MT>::N;
@@ -259,7 +292,8 @@ __global__ __launch_bounds__(256) void k_gather_csr4(int R, int d, int nchunk, i
   const int c = xcd + 8 * (i / ntb), rb = i % ntb;
   if (c >= nchunk) return;
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
-  const int r = rb * 16 + (threadIdx.x >> 6) * 4 + g;
+  const int ri = rb * 16 + (threadIdx.x >> 6) * 4 + g;
+  const int r = ri < R ? perm[ri] : R;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
   int start = 0, n = 0;
@@ -375,6 +409,7 @@ size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf1
   b += 2 * al256(4 * NB * f);               // mask, cnt/off
   b += al256(4 * ((size_t)f + 1));          // col_ptr
   b += 2 * al256(8 * NZ);                   // (token, h), (token, dz) pairs
+  b += al256(4 * (size_t)T) + al256(4 * (size_t)f);   // list orders
   return b;
 }
 
@@ -396,6 +431,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   int32_t *col_ptr = (int32_t *)take(4 * ((size_t)f + 1));
   uint2 *th = (uint2 *)take(8 * NZ);
   uint2 *tdz = (uint2 *)take(8 * NZ);
+  int32_t *perm_t = (int32_t *)take(4 * (size_t)T);
+  int32_t *perm_u = (int32_t *)take(4 * (size_t)f);
   const dim3 rows4((T + 3) / 4);
   if (T > 0) {
     if (h.val_bf16) hipLaunchKernelGGL(k_row_nnz<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr);
@@ -405,25 +442,27 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   if (T > 0) {
     if (h.val_bf16) hipLaunchKernelGGL(k_csr_fill<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr, col, hval);
     else hipLaunchKernelGGL(k_csr_fill<float>, rows4, dim3(256), 0, s, h, row_ptr, col, hval);
+    hipLaunchKernelGGL(k_order_by_len, dim3(1), dim3(1024), 0, s, T, row_ptr, perm_t);
     const int ntb = (T + 15) / 16;
     const size_t grid = 8 * (size_t)ntb * ((nchunk + 7) / 8);
     if (a.bf16) hipLaunchKernelGGL((k_sddmm_part<uint16_t>), dim3((unsigned)grid), dim3(256), 0, s, T, d, nchunk, ntb,
-                                   (const uint16_t *)a.dy, (const uint16_t *)a.w2, row_ptr, col, NZ, part);
+                                   (const uint16_t *)a.dy, (const uint16_t *)a.w2, row_ptr, perm_t, col, NZ, part);
     else hipLaunchKernelGGL((k_sddmm_part<float>), dim3((unsigned)grid), dim3(256), 0, s, T, d, nchunk, ntb,
-                            (const float *)a.dy, (const float *)a.w2, row_ptr, col, NZ, part);
+                            (const float *)a.dy, (const float *)a.w2, row_ptr, perm_t, col, NZ, part);
     const unsigned sum_grid = (unsigned)std::min<size_t>((NZ + 255) / 256, 4096);
     hipLaunchKernelGGL(k_sddmm_sum, dim3(sum_grid), dim3(256), 0, s, T, row_ptr, NZ, nchunk, part, col, a.l1, dz);
   }
-  auto gather = [&](int R, const int32_t *ptr, const uint2 *pairs, const void *M, float *out, float *rowsum) {
+  auto gather = [&](int R, const int32_t *ptr, const int32_t *perm, const uint2 *pairs, const void *M, float *out,
+                    float *rowsum) {
     const int ntb = (R + 15) / 16;
     const size_t grid = 8 * (size_t)ntb * ((nchunk + 7) / 8);
     if (a.bf16) hipLaunchKernelGGL((k_gather_csr4<uint16_t>), dim3((unsigned)grid), dim3(256), 0, s, R, d, nchunk, ntb,
-                                   ptr, pairs, (const uint16_t *)M, out, rowsum);
+                                   ptr, perm, pairs, (const uint16_t *)M, out, rowsum);
     else hipLaunchKernelGGL((k_gather_csr4<float>), dim3((unsigned)grid), dim3(256), 0, s, R, d, nchunk, ntb, ptr,
-                            pairs, (const float *)M, out, rowsum);
+                            perm, pairs, (const float *)M, out, rowsum);
   };
   // dx = dz . w1t
-  if (T > 0) gather(T, row_ptr, dz, a.w1t, a.dx, nullptr);
+  if (T > 0) gather(T, row_ptr, perm_t, dz, a.w1t, a.dx, nullptr);
   // CSC
   if (T > 0) {
     hipLaunchKernelGGL(k_col_mask, dim3((unsigned)NB), dim3(256), (size_t)f * 4, s, T, f, row_ptr, col, mask, cnt);
@@ -437,8 +476,9 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     hipLaunchKernelGGL(k_csc_fill, rows4, dim3(256), 0, s, T, f, row_ptr, col, hval, dz, mask, cnt, th, tdz);
   }
   // dw2 = h^T dy, dw1t = dz^T x (every unit row written, zero if it has no entry), db1
-  gather(f, col_ptr, th, a.dy, a.dw2, nullptr);
-  gather(f, col_ptr, tdz, a.x, a.dw1t, a.db1);
+  hipLaunchKernelGGL(k_order_by_len, dim3(1), dim3(1024), 0, s, f, col_ptr, perm_u);
+  gather(f, col_ptr, perm_u, th, a.dy, a.dw2, nullptr);
+  gather(f, col_ptr, perm_u, tdz, a.x, a.dw1t, a.db1);
   return hipGetLastError();
 }
 
