@@ -17,7 +17,7 @@
 //                               reads only its slices of W2), then their sum in chunk order
 //                               plus l1, stored as the (unit, dz) pairs of the dx gather
 //   4. gather (w1t rows)     -> dx
-//   5. col_mask, col_tot, scan, col_off, csc_fill -> the same entries by unit (CSC), tokens
+//   5. col_mask, scan, col_off, csc_fill -> the same entries by unit (CSC), tokens
 //      ascending inside a unit, positions computed without a serial pass: per 32-token
 //      block every unit keeps the bit mask of its tokens; an entry's rank inside its unit
 //      is the block offset plus the popcount of the mask bits of earlier tokens. Writes
@@ -38,8 +38,11 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // nnz[t] = entries of row t: the nonzeros of its backup row (counted in that row, so the
 // fill below writes exactly this many), else the stored slots.
+// Also clears tot[0 .. f] (the per-unit totals k_col_mask accumulates into).
 template <typename VT>
-__global__ __launch_bounds__(256) void k_row_nnz(TwellIn h, int32_t *__restrict__ nnz) {
+__global__ __launch_bounds__(256) void k_row_nnz(TwellIn h, int32_t *__restrict__ nnz, int32_t *__restrict__ tot,
+                                                 int f) {
+  for (int j = blockIdx.x * 256 + threadIdx.x; j <= f; j += gridDim.x * 256) tot[j] = 0;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= h.rows) return;
   const int lane = lane_id();
@@ -321,10 +324,11 @@ __global__ __launch_bounds__(256) void k_gather_csr4(int R, int d, int nchunk, i
 // ------------------------------------------------------------------- 5. CSR -> CSC
 
 // Per 32-token block b: mask[b][j] bit (t - 32 b) set iff token t has unit j active;
-// cnt[b][j] = popcount. LDS holds the block's masks for all units.
+// cnt[b][j] = popcount, also added to tot[j] (integer atomics: the sum is exact and
+// independent of order). LDS holds the block's masks for all units.
 __global__ __launch_bounds__(256) void k_col_mask(int T_rows, int f, const int32_t *__restrict__ row_ptr,
                                                   const int32_t *__restrict__ col, uint32_t *__restrict__ mask,
-                                                  int32_t *__restrict__ cnt) {
+                                                  int32_t *__restrict__ cnt, int32_t *__restrict__ tot) {
   extern __shared__ uint32_t lm[];
   const int b = blockIdx.x, tid = threadIdx.x;
   for (int j = tid; j < f; j += 256) lm[j] = 0u;
@@ -341,26 +345,29 @@ __global__ __launch_bounds__(256) void k_col_mask(int T_rows, int f, const int32
     const uint32_t m = lm[j];
     mask[(size_t)b * f + j] = m;
     cnt[(size_t)b * f + j] = __popc(m);
+    if (m) atomicAdd(&tot[j], __popc(m));
   }
 }
 
-// tot[j] = sum_b cnt[b][j]
-__global__ __launch_bounds__(256) void k_col_tot(int NB, int f, const int32_t *__restrict__ cnt,
-                                                 int32_t *__restrict__ tot) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
-  if (j >= f) return;
-  int s = 0;
-  for (int b = 0; b < NB; ++b) s += cnt[(size_t)b * f + j];
-  tot[j] = s;
-}
-
-// cnt[b][j] <- col_ptr[j] + sum_{b' < b} cnt[b'][j]  (first position of block b in unit j)
-__global__ __launch_bounds__(256) void k_col_off(int NB, int f, const int32_t *__restrict__ col_ptr,
-                                                 int32_t *__restrict__ cnt) {
-  const int j = blockIdx.x * 256 + threadIdx.x;
+// cnt[b][j] <- col_ptr[j] + sum_{b' < b} cnt[b'][j]  (first position of block b in unit j).
+// A workgroup owns 64 units; its 16 waves split the NB blocks into consecutive ranges, sum
+// their range, exchange the range sums through LDS, and rewrite their range with offsets.
+__global__ __launch_bounds__(1024) void k_col_off(int NB, int f, const int32_t *__restrict__ col_ptr,
+                                                  int32_t *__restrict__ cnt) {
+  __shared__ int part[16][64];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int j = blockIdx.x * 64 + lane;
+  const int per = (NB + 15) / 16;
+  const int b0 = min(NB, w * per), b1 = min(NB, b0 + per);
+  int sum = 0;
+  if (j < f)
+    for (int b = b0; b < b1; ++b) sum += cnt[(size_t)b * f + j];
+  part[w][lane] = sum;
+  __syncthreads();
   if (j >= f) return;
   int run = col_ptr[j];
-  for (int b = 0; b < NB; ++b) {
+  for (int k = 0; k < w; ++k) run += part[k][lane];
+  for (int b = b0; b < b1; ++b) {
     const int c = cnt[(size_t)b * f + j];
     cnt[(size_t)b * f + j] = run;
     run += c;
@@ -387,6 +394,11 @@ __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32
     th[pos] = make_uint2((uint32_t)t, __float_as_uint(hval[k]));
     tdz[pos] = make_uint2((uint32_t)t, dz[k].y);
   }
+}
+
+__global__ __launch_bounds__(256) void k_fill_zero(int32_t *p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
 }
 
 // ------------------------------------------------------------------ host side
@@ -435,8 +447,10 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   int32_t *perm_u = (int32_t *)take(4 * (size_t)f);
   const dim3 rows4((T + 3) / 4);
   if (T > 0) {
-    if (h.val_bf16) hipLaunchKernelGGL(k_row_nnz<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr);
-    else hipLaunchKernelGGL(k_row_nnz<float>, rows4, dim3(256), 0, s, h, row_ptr);
+    if (h.val_bf16) hipLaunchKernelGGL(k_row_nnz<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr, col_ptr, f);
+    else hipLaunchKernelGGL(k_row_nnz<float>, rows4, dim3(256), 0, s, h, row_ptr, col_ptr, f);
+  } else {
+    hipLaunchKernelGGL(k_fill_zero, dim3((f + 256) / 256), dim3(256), 0, s, col_ptr, f + 1);
   }
   hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, row_ptr, T, row_ptr);
   if (T > 0) {
@@ -464,15 +478,12 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   // dx = dz . w1t
   if (T > 0) gather(T, row_ptr, perm_t, dz, a.w1t, a.dx, nullptr);
   // CSC
-  if (T > 0) {
-    hipLaunchKernelGGL(k_col_mask, dim3((unsigned)NB), dim3(256), (size_t)f * 4, s, T, f, row_ptr, col, mask, cnt);
-    hipLaunchKernelGGL(k_col_tot, dim3((f + 255) / 256), dim3(256), 0, s, (int)NB, f, cnt, col_ptr);
-  } else {
-    hipLaunchKernelGGL(k_col_tot, dim3((f + 255) / 256), dim3(256), 0, s, 0, f, cnt, col_ptr);
-  }
+  if (T > 0)
+    hipLaunchKernelGGL(k_col_mask, dim3((unsigned)NB), dim3(256), (size_t)f * 4, s, T, f, row_ptr, col, mask, cnt,
+                       col_ptr);
   hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, col_ptr, f, col_ptr);
   if (T > 0) {
-    hipLaunchKernelGGL(k_col_off, dim3((f + 255) / 256), dim3(256), 0, s, (int)NB, f, col_ptr, cnt);
+    hipLaunchKernelGGL(k_col_off, dim3((f + 63) / 64), dim3(1024), 0, s, (int)NB, f, col_ptr, cnt);
     hipLaunchKernelGGL(k_csc_fill, rows4, dim3(256), 0, s, T, f, row_ptr, col, hval, dz, mask, cnt, th, tdz);
   }
   // dw2 = h^T dy, dw1t = dz^T x (every unit row written, zero if it has no entry), db1
