@@ -15,7 +15,7 @@ import torch
 
 __all__ = [
     "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
-    "twell_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
+    "twell_down", "twell_fwd_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
     "nm_prune", "nm_ffn_down", "twell_sync_status", "F32", "BF16",
 ]
 
@@ -50,10 +50,11 @@ _SIGS = {
     "twell_pack": ([_P, _I, _P, _P], _I),
     "twell_ffn_fwd": ([_P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
     "twell_down": ([_P, _P, _I, _I, _P, _I, _P], _I),
+    "twell_fwd_down": ([_P, _P, _I, _I, _P, _I, _P], _I),
     "twell_up_gemm": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "twell_up_finish": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "ffn_up_relu_dense": ([_P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
-    "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _P], _Z),
+    "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
     "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
     "nm_prune": ([_P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "nm_ffn_down": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P], _I),
@@ -206,6 +207,17 @@ def twell_down(h: TwellMatrix, w2: torch.Tensor, y_dtype=torch.float32, y=None) 
     return y
 
 
+def twell_fwd_down(h: TwellMatrix, w2: torch.Tensor, y_dtype=torch.float32, y=None) -> torch.Tensor:
+    """Stage 3 of twell_ffn_fwd: the down projection on the row lists twell_up_finish built."""
+    d = w2.shape[1]
+    if y is None:
+        y = torch.empty((h.rows, d), dtype=y_dtype, device=w2.device)
+    m = h.c()
+    _check(lib().twell_fwd_down(_c.byref(m), _ptr(w2), _dt(w2.dtype), d, _ptr(y), _dt(y.dtype),
+                                _stream(w2.device)), "twell_fwd_down")
+    return y
+
+
 def ffn_up_relu_dense(x, w1t, b1, h_dtype=torch.float32, out=None) -> torch.Tensor:
     T, d = x.shape
     f = w1t.shape[0]
@@ -216,9 +228,9 @@ def ffn_up_relu_dense(x, w1t, b1, h_dtype=torch.float32, out=None) -> torch.Tens
     return out
 
 
-def twell_ffn_bwd_workspace_bytes(T: int, d: int, f: int, h: TwellMatrix) -> int:
+def twell_ffn_bwd_workspace_bytes(T: int, d: int, f: int, h: TwellMatrix, dtype=torch.bfloat16) -> int:
     m = h.c()
-    return lib().twell_ffn_bwd_workspace_bytes(T, d, f, _c.byref(m))
+    return lib().twell_ffn_bwd_workspace_bytes(T, d, f, _dt(dtype), _c.byref(m))
 
 
 def twell_ffn_bwd(x, w1t, w2, h: TwellMatrix, dy, l1_coef: float, want_db1: bool = True,
@@ -231,7 +243,7 @@ def twell_ffn_bwd(x, w1t, w2, h: TwellMatrix, dy, l1_coef: float, want_db1: bool
     dw1t = torch.empty((f, d), dtype=torch.float32, device=dev)
     dw2 = torch.empty((f, d), dtype=torch.float32, device=dev)
     db1 = torch.empty((f,), dtype=torch.float32, device=dev) if want_db1 else None
-    nbytes = twell_ffn_bwd_workspace_bytes(T, d, f, h)
+    nbytes = twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype)
     if workspace is None or workspace.numel() < nbytes:
         workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
     m = h.c()

@@ -160,7 +160,7 @@ static int up_finish(const void *x, const void *w1t, const float *b1, int32_t in
                      int32_t d_model, int32_t d_ff, twell_matrix_t *h, hipStream_t s) {
   if (T == 0) return hip_status(launch_set_int(h->ovf_n, 0, s));
   const TwellOut o = out_of(h);
-  TW_TRY(launch_ovf_scan(h->ovf_bits, o.n_t, o.words, T, h->ovf_cap, h->ovf_n, h->ovf_rows, h->ovf_slot, s));
+  TW_TRY(launch_lists_scan(in_of(h), h->ovf_bits, o.words, h->ovf_n, h->ovf_rows, h->ovf_slot, s));
   if (h->ovf_cap > 0) {
     const int M = h->ovf_cap < T ? h->ovf_cap : T;
     TW_TRY(launch_up_dense(in_dtype == TWELL_BF16, x, w1t, b1, M, d_ff, d_model, T, h->ovf_rows, h->ovf_n,
@@ -180,6 +180,8 @@ int twell_up_finish(const void *x, const void *w1t, const float *b1, int32_t in_
                     int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream) {
   int st = check_up_args(x, w1t, b1, in_dtype, T, d_model, d_ff, h);
   if (st) return st;
+  st = check_matrix(h, true, true);
+  if (st) return st;
   return up_finish(x, w1t, b1, in_dtype, T, d_model, d_ff, h, S(stream));
 }
 
@@ -198,12 +200,12 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
   if (st) return st;
   st = up_finish(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);
   if (st || T == 0) return st;
-  TW_TRY(launch_twell_down(in_of(h), w2, in_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, s));
+  TW_TRY(launch_twell_down(in_of(h), w2, in_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, false, s));
   return TWELL_OK;
 }
 
-int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model, void *y,
-               int32_t y_dtype, void *stream) {
+static int down_args(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model, const void *y,
+                     int32_t y_dtype) {
   if (!h || !w2 || !y) return TWELL_ERR_ARG;
   if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return TWELL_ERR_ARG;
   int st = check_matrix(h, false, true);
@@ -211,8 +213,26 @@ int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t
   if (d_model <= 0) return TWELL_ERR_SHAPE;
   if (d_model % 8) return TWELL_ERR_ALIGN;
   if (!al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
+  return TWELL_OK;
+}
+
+int twell_fwd_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model, void *y,
+                   int32_t y_dtype, void *stream) {
+  int st = down_args(h, w2, w_dtype, d_model, y, y_dtype);
+  if (st) return st;
   if (h->rows == 0) return TWELL_OK;
-  TW_TRY(launch_twell_down(in_of(h), w2, w_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, S(stream)));
+  TW_TRY(launch_twell_down(in_of(h), w2, w_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, false,
+                           S(stream)));
+  return TWELL_OK;
+}
+
+int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model, void *y,
+               int32_t y_dtype, void *stream) {
+  int st = down_args(h, w2, w_dtype, d_model, y, y_dtype);
+  if (st) return st;
+  if (h->rows == 0) return TWELL_OK;
+  TW_TRY(launch_twell_down(in_of(h), w2, w_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, true,
+                           S(stream)));
   return TWELL_OK;
 }
 

@@ -4,7 +4,7 @@
 // "Kernels de Inferência": the down projection iterates over the active units only, so the
 // rows of W2 of inactive units are never read. Accumulation is fp32.
 //
-// First each normal row's TwELL slots are compacted once into a contiguous list of
+// First each row's TwELL slots are compacted once into a contiguous list of
 // (column, value) pairs (k_row_list): the gathers below are spread over all XCDs by column
 // chunk, and reading the sparse slot blocks from every XCD would fetch whole cache lines
 // for a handful of entries. A chunk is 16 lanes x 16 bytes of a W2 row (128 bf16 or 64
@@ -27,38 +27,31 @@
 #include "common.h"
 #include "gather.h"
 #include "launch.h"
+#include "rows.h"
 
 namespace tw {
 
 template <typename VT> TW_DEV float ldv(const VT *p, size_t i) { return Elem<VT>::load(p, i); }
 
-// Compact list of each normal row: row_list[t][0 .. row_nnz[t]) = (column, fp32 value bits)
-// in ascending column order, read once from the TwELL slots. Rows with a dense backup get
-// row_nnz = -1 (their consumers read the backup row). One wave per row.
+// The compact list of every row (row_list_wave), 16 rows per workgroup.
 template <typename VT>
-__global__ __launch_bounds__(256) void k_row_list(TwellIn h) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= h.rows) return;
-  const int lane = lane_id();
-  if (h.ovf_slot[t] >= 0) {
-    if (lane == 0) h.row_nnz[t] = -1;
+__global__ __launch_bounds__(1024) void k_row_list(TwellIn h) {
+  const int t = blockIdx.x * 16 + (threadIdx.x >> 6);
+  if (t < h.rows) row_list_wave<VT>(h, t);
+}
+
+// The finish step of the fused forward in one launch: workgroup 0 runs the overflow scan
+// (ovf_scan_block), the others build the row lists, which do not depend on the scan
+// (consumers tell overflow rows by ovf_slot).
+template <typename VT>
+__global__ __launch_bounds__(1024) void k_lists_scan(TwellIn h, const uint32_t *__restrict__ bits, int words,
+                                                     int32_t *ovf_n, int32_t *ovf_rows, int32_t *ovf_slot) {
+  if (blockIdx.x == 0) {
+    ovf_scan_block(bits, h.n_t, words, h.rows, h.cap, ovf_n, ovf_rows, ovf_slot);
     return;
   }
-  const size_t stride = (size_t)h.n_t * h.S;
-  uint2 *out = h.row_list + (size_t)t * stride;
-  const VT *vals = (const VT *)h.vals;
-  int n = 0;
-  for (int k0 = 0; k0 < h.n_t; k0 += 64) {
-    const int k = k0 + lane;
-    const int m = k < h.n_t ? min(h.counts[(size_t)t * h.n_t + k], h.S) : 0;
-    int tot;
-    const int off = wave_excl_scan(m, &tot);
-    const size_t sb = ((size_t)t * h.n_t + k) * h.S;
-    for (int s = 0; s < m; ++s)
-      out[n + off + s] = make_uint2((uint32_t)h.col_idx[sb + s], __float_as_uint(ldv(vals, sb + s)));
-    n += tot;
-  }
-  if (lane == 0) h.row_nnz[t] = n;
+  const int t = (blockIdx.x - 1) * 16 + (threadIdx.x >> 6);
+  if (t < h.rows) row_list_wave<VT>(h, t);
 }
 
 // y[t][chunk] from the compact list: batches of 64 (column, value) pairs are staged in LDS
@@ -114,8 +107,8 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
     }
   };
 
-  const int nnz = h.row_nnz[t];
-  if (nnz >= 0) {
+  if (h.ovf_slot[t] < 0) {
+    const int nnz = h.row_nnz[t];
     const uint2 *src = h.row_list + (size_t)t * h.n_t * h.S;
     for (int base = 0; base < nnz; base += 64) {
       const int n = min(64, nnz - base);
@@ -239,9 +232,8 @@ __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restr
   const int t = tb * 16 + wave * 4 + g;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
-  int nnz = t < h.rows ? h.row_nnz[t] : 0;
-  const bool normal = nnz >= 0;
-  if (!normal) nnz = 0;
+  const bool normal = t < h.rows && h.ovf_slot[t] < 0;
+  const int nnz = normal ? h.row_nnz[t] : 0;
   int n = max(nnz, __shfl_xor(nnz, 16, 64));
   n = max(n, __shfl_xor(n, 32, 64));
   const uint2 *lp = h.row_list + (size_t)(t < h.rows ? t : 0) * h.n_t * h.S;
@@ -279,14 +271,15 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
   const int cap = h.n_t * h.S;
   const uint2 *src = h.row_list + (size_t)t * cap;
   if (tid < LW) lst[tid] = tid < cap ? src[tid] : make_uint2(0, 0);
-  const int nnz = h.row_nnz[t];
+  const int slot = h.ovf_slot[t];
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  if (nnz < 0) {                                            // backup row: one wave does it
-    if (wave == 0) backup_row<WT, VT, YT>(h, w2, d, y, h.ovf_slot[t], c, lst);
+  if (slot >= 0) {                                          // backup row: one wave does it
+    if (wave == 0) backup_row<WT, VT, YT>(h, w2, d, y, slot, c, lst);
     return;
   }
+  const int nnz = h.row_nnz[t];
   __syncthreads();
   for (int base = 0; base < nnz; base += LW) {
     if (base > 0) {
@@ -335,12 +328,12 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
 constexpr int kRows4MinT = 512, kSplitMaxT = 16;
 
 template <typename WT, typename VT, typename YT>
-static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, hipStream_t s) {
+static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, bool build_lists, hipStream_t s) {
   constexpr int CW = 16 * Vec16<WT>::N;
   const int nchunk = (d + CW - 1) / CW;
   const size_t per_xcd_chunks = (nchunk + 7) / 8;
   if (h.rows == 0) return hipSuccess;
-  hipLaunchKernelGGL((k_row_list<VT>), dim3((h.rows + 3) / 4), dim3(256), 0, s, h);
+  if (build_lists) hipLaunchKernelGGL((k_row_list<VT>), dim3((h.rows + 15) / 16), dim3(1024), 0, s, h);
   if (h.rows >= kRows4MinT) {
     const int ntb = (h.rows + 15) / 16;
     const size_t nmain = 8 * per_xcd_chunks * (size_t)ntb;
@@ -358,23 +351,31 @@ static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, hipStream
 }
 
 hipError_t launch_twell_down(const TwellIn &h, const void *w2, int w_bf16, int d, void *y, int y_bf16,
-                             hipStream_t s) {
+                             bool build_lists, hipStream_t s) {
   if (w_bf16) {
     const uint16_t *w = (const uint16_t *)w2;
     if (h.val_bf16) {
-      if (y_bf16) return down_t<uint16_t, uint16_t, uint16_t>(h, w, d, (uint16_t *)y, s);
-      return down_t<uint16_t, uint16_t, float>(h, w, d, (float *)y, s);
+      if (y_bf16) return down_t<uint16_t, uint16_t, uint16_t>(h, w, d, (uint16_t *)y, build_lists, s);
+      return down_t<uint16_t, uint16_t, float>(h, w, d, (float *)y, build_lists, s);
     }
-    if (y_bf16) return down_t<uint16_t, float, uint16_t>(h, w, d, (uint16_t *)y, s);
-    return down_t<uint16_t, float, float>(h, w, d, (float *)y, s);
+    if (y_bf16) return down_t<uint16_t, float, uint16_t>(h, w, d, (uint16_t *)y, build_lists, s);
+    return down_t<uint16_t, float, float>(h, w, d, (float *)y, build_lists, s);
   }
   const float *w = (const float *)w2;
   if (h.val_bf16) {
-    if (y_bf16) return down_t<float, uint16_t, uint16_t>(h, w, d, (uint16_t *)y, s);
-    return down_t<float, uint16_t, float>(h, w, d, (float *)y, s);
+    if (y_bf16) return down_t<float, uint16_t, uint16_t>(h, w, d, (uint16_t *)y, build_lists, s);
+    return down_t<float, uint16_t, float>(h, w, d, (float *)y, build_lists, s);
   }
-  if (y_bf16) return down_t<float, float, uint16_t>(h, w, d, (uint16_t *)y, s);
-  return down_t<float, float, float>(h, w, d, (float *)y, s);
+  if (y_bf16) return down_t<float, float, uint16_t>(h, w, d, (uint16_t *)y, build_lists, s);
+  return down_t<float, float, float>(h, w, d, (float *)y, build_lists, s);
+}
+
+hipError_t launch_lists_scan(const TwellIn &h, const uint32_t *bits, int words, int32_t *ovf_n, int32_t *ovf_rows,
+                            int32_t *ovf_slot, hipStream_t s) {
+  const dim3 grid(1 + (h.rows + 15) / 16);
+  if (h.val_bf16) hipLaunchKernelGGL((k_lists_scan<uint16_t>), grid, dim3(1024), 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot);
+  else hipLaunchKernelGGL((k_lists_scan<float>), grid, dim3(1024), 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot);
+  return hipGetLastError();
 }
 
 }  // namespace tw

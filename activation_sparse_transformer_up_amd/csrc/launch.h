@@ -65,6 +65,9 @@ hipError_t launch_nm_down(const void *vals, const uint8_t *idx, int T, int f, in
 
 // down.hip
 hipError_t launch_twell_down(const TwellIn &h, const void *w2, int w_bf16, int d, void *y, int y_bf16,
-                             hipStream_t s);
+                             bool build_lists, hipStream_t s);
+// overflow scan + row lists in one launch (the finish step of the fused forward)
+hipError_t launch_lists_scan(const TwellIn &h, const uint32_t *bits, int words, int32_t *ovf_n, int32_t *ovf_rows,
+                             int32_t *ovf_slot, hipStream_t s);
 
 }  // namespace tw

@@ -6,11 +6,13 @@
 //    matrix already in memory (the conversion step the fused GEMM epilogue makes
 //    unnecessary; kept as a building block).
 //  - block "Formato Híbrido para Treinamento": rows with too many nonzeros go to a dense
-//    backup. k_ovf_scan turns the per-(tile, 32-row) overflow bit words into the ordered
-//    list of overflow rows, each row's backup slot, and the true overflow count; the
-//    backup rows themselves are copied by k_ovf_copy (or recomputed by the up GEMM).
+//    backup. k_ovf_scan (ovf_scan_block) turns the per-(tile, 32-row) overflow bit words
+//    into the ordered list of overflow rows, each row's backup slot, and the true overflow
+//    count; the backup rows themselves are copied by k_ovf_copy (or recomputed by the up
+//    GEMM).
 #include "common.h"
 #include "launch.h"
+#include "rows.h"
 
 namespace tw {
 
@@ -76,67 +78,10 @@ __global__ __launch_bounds__(256) void k_pack(const HT *__restrict__ h, int R, i
   if (lane == 0 && rb < o.words) o.ovf_bits[(size_t)kt * o.words + rb] = ovf_word;
 }
 
-// One workgroup of 1024 threads. Words are processed in chunks; within a chunk each word
-// is OR-reduced over the n_t tiles by a group of G lanes, its popcount is scanned
-// (exclusive, carried across chunks), and every row's slot is written.
 __global__ __launch_bounds__(1024) void k_ovf_scan(const uint32_t *__restrict__ bits, int n_t, int words,
                                                    int R, int cap, int32_t *ovf_n, int32_t *ovf_rows,
                                                    int32_t *ovf_slot) {
-  __shared__ uint32_t fw[1024];
-  __shared__ int pre[1024];
-  __shared__ int wsum[16];
-  __shared__ int carry_s;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  int G = 1;
-  while (G < 64 && G * 2 * min(words, 1024) <= 1024) G *= 2;
-  const int wpc = 1024 / G;                       // words per chunk
-  if (tid == 0) carry_s = 0;
-  __syncthreads();
-  for (int base = 0; base < words; base += wpc) {
-    const int wi = tid / G, sub = tid % G;
-    const int w = base + wi;
-    uint32_t f = 0;
-    if (w < words) {
-      for (int k = sub; k < n_t; k += G) f |= bits[(size_t)k * words + w];
-    }
-    for (int off = 1; off < G; off <<= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
-    // one value per word: lanes with sub == 0 hold it
-    const int c = (sub == 0 && w < words) ? __popc(f) : 0;
-    int tot;
-    const int ex = wave_excl_scan(c, &tot);
-    if (lane == 0) wsum[wave] = tot;
-    __syncthreads();
-    int wpre = 0, chunk_tot = 0;
-    for (int i = 0; i < 16; ++i) {
-      if (i < wave) wpre += wsum[i];
-      chunk_tot += wsum[i];
-    }
-    const int carry = carry_s;
-    if (sub == 0) {
-      fw[wi] = f;
-      pre[wi] = carry + wpre + ex;
-    }
-    __syncthreads();
-    const int nrows = min(wpc * 32, R - base * 32);
-    for (int i = tid; i < nrows; i += 1024) {
-      const int row = base * 32 + i;
-      const uint32_t ff = fw[i >> 5];
-      const int bit = i & 31;
-      int slot = -1;
-      if ((ff >> bit) & 1u) {
-        const int p = pre[i >> 5] + __popc(ff & ((1u << bit) - 1u));
-        if (p < cap) {
-          slot = p;
-          ovf_rows[p] = row;
-        }
-      }
-      ovf_slot[row] = slot;
-    }
-    __syncthreads();
-    if (tid == 0) carry_s = carry + chunk_tot;
-    __syncthreads();
-  }
-  if (tid == 0) *ovf_n = carry_s;
+  ovf_scan_block(bits, n_t, words, R, cap, ovf_n, ovf_rows, ovf_slot);
 }
 
 // Backup row r < min(*ovf_n, cap) = source row ovf_rows[r], copied (bf16 -> fp32 widening

@@ -1,0 +1,100 @@
+// Per-row bookkeeping of a TwELL matrix, shared by the producers (pack, up-GEMM finish)
+// and the down projection:
+//  - the compact per-row lists of the stored slots, which the row gathers walk;
+//  - the overflow scan of "Sparser, Faster, Lighter Transformer Language Models", section
+//    "2. Metodologia", block "Formato Híbrido para Treinamento": rows with a row-tile count
+//    above the slot budget go to a dense backup, listed in ascending row order.
+#pragma once
+#include "common.h"
+#include "launch.h"
+
+namespace tw {
+
+// row_list[t][0 .. row_nnz[t]) = (column, fp32 value bits) of the stored slots of row t in
+// ascending column order (an overflow row gets its truncated slots; consumers take such
+// rows from the dense backup instead). One wave.
+template <typename VT>
+TW_DEV void row_list_wave(const TwellIn &h, int t) {
+  const int lane = lane_id();
+  const size_t stride = (size_t)h.n_t * h.S;
+  uint2 *out = h.row_list + (size_t)t * stride;
+  const VT *vals = (const VT *)h.vals;
+  int n = 0;
+  for (int k0 = 0; k0 < h.n_t; k0 += 64) {
+    const int k = k0 + lane;
+    const int m = k < h.n_t ? min(h.counts[(size_t)t * h.n_t + k], h.S) : 0;
+    int tot;
+    const int off = wave_excl_scan(m, &tot);
+    const size_t sb = ((size_t)t * h.n_t + k) * h.S;
+    for (int s = 0; s < m; ++s)
+      out[n + off + s] = make_uint2((uint32_t)h.col_idx[sb + s], __float_as_uint(Elem<VT>::load(vals, sb + s)));
+    n += tot;
+  }
+  if (lane == 0) h.row_nnz[t] = n;
+}
+
+// The overflow scan, by one workgroup of 1024 threads: the per-(tile, 32-row) overflow
+// words are OR-reduced over the n_t tiles (a group of G lanes per word), their popcounts
+// scanned (exclusive, carried across chunks of words), and every row's backup slot written:
+// ovf_slot[row] = its rank among overflow rows if below cap, else -1; ovf_rows[rank] = row;
+// *ovf_n = the number of overflow rows (may exceed cap).
+TW_DEV void ovf_scan_block(const uint32_t *__restrict__ bits, int n_t, int words, int R, int cap,
+                           int32_t *ovf_n, int32_t *ovf_rows, int32_t *ovf_slot) {
+  __shared__ uint32_t fw[1024];
+  __shared__ int pre[1024];
+  __shared__ int wsum[16];
+  __shared__ int carry_s;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int G = 1;
+  while (G < 64 && G * 2 * min(words, 1024) <= 1024) G *= 2;
+  const int wpc = 1024 / G;                       // words per chunk
+  if (tid == 0) carry_s = 0;
+  __syncthreads();
+  for (int base = 0; base < words; base += wpc) {
+    const int wi = tid / G, sub = tid % G;
+    const int w = base + wi;
+    uint32_t f = 0;
+    if (w < words) {
+      for (int k = sub; k < n_t; k += G) f |= bits[(size_t)k * words + w];
+    }
+    for (int off = 1; off < G; off <<= 1) f |= (uint32_t)__shfl_xor((int)f, off, 64);
+    // one value per word: lanes with sub == 0 hold it
+    const int c = (sub == 0 && w < words) ? __popc(f) : 0;
+    int tot;
+    const int ex = wave_excl_scan(c, &tot);
+    if (lane == 0) wsum[wave] = tot;
+    __syncthreads();
+    int wpre = 0, chunk_tot = 0;
+    for (int i = 0; i < 16; ++i) {
+      if (i < wave) wpre += wsum[i];
+      chunk_tot += wsum[i];
+    }
+    const int carry = carry_s;
+    if (sub == 0) {
+      fw[wi] = f;
+      pre[wi] = carry + wpre + ex;
+    }
+    __syncthreads();
+    const int nrows = min(wpc * 32, R - base * 32);
+    for (int i = tid; i < nrows; i += 1024) {
+      const int row = base * 32 + i;
+      const uint32_t ff = fw[i >> 5];
+      const int bit = i & 31;
+      int slot = -1;
+      if ((ff >> bit) & 1u) {
+        const int p = pre[i >> 5] + __popc(ff & ((1u << bit) - 1u));
+        if (p < cap) {
+          slot = p;
+          ovf_rows[p] = row;
+        }
+      }
+      ovf_slot[row] = slot;
+    }
+    __syncthreads();
+    if (tid == 0) carry_s = carry + chunk_tot;
+    __syncthreads();
+  }
+  if (tid == 0) *ovf_n = carry_s;
+}
+
+}  // namespace tw

@@ -155,7 +155,7 @@ def leg_c3(steps, warmup):
         def down():
             i = it[0] % 3
             it[0] += 1
-            tw.twell_down(hs[i], copies[i][1], y=y)
+            tw.twell_fwd_down(hs[i], copies[i][1], y=y)
 
         def gemm():
             i = it[0] % 3
@@ -238,7 +238,7 @@ def leg_c5(steps, warmup):
     cap = 1024
     h = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.float32, dev)
     y = torch.empty((T, d), device=dev)
-    ws = torch.empty((tw.twell_ffn_bwd_workspace_bytes(T, d, f, h),), dtype=torch.uint8, device=dev)
+    ws = torch.empty((tw.twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype),), dtype=torch.uint8, device=dev)
 
     def step():
         tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y)
@@ -312,7 +312,7 @@ def main():
         if ev is not None:
             ev.record()
         tw.twell_up_finish(x, w1t, b1, h)
-        tw.twell_down(h, w2, y=y)
+        tw.twell_fwd_down(h, w2, y=y)
 
     warm(step, a.warmup)
     E = lambda: torch.cuda.Event(enable_timing=True)  # noqa: E731
@@ -332,9 +332,7 @@ def main():
     ovf_n = int(h.ovf_n.item())
 
     # the monolithic entry point, same work (sanity: equal time within noise)
-    for _ in range(3):
-        tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, a.ovf_cap, h=h, y=y)
-    torch.cuda.synchronize()
+    warm(lambda: tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, a.ovf_cap, h=h, y=y), a.warmup)
     t0.record()
     for _ in range(a.steps):
         tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, a.ovf_cap, h=h, y=y)

@@ -72,8 +72,8 @@ typedef enum {
  *                                   inside one call; contents on return are unspecified
  *   row_nnz[R]                      library scratch: entries of each row's compact list
  *   row_list[R][C/tile_w * slots]   library scratch: compact (int32 column, fp32 value)
- *                                   pairs of each row, written by the consumers of the
- *                                   matrix (down projection, backward) before use
+ *                                   pairs of each row, written by twell_up_finish and by
+ *                                   twell_down before use
  *
  * A row overflows iff some tile of it holds more than `slots` nonzeros. A (row, tile)
  * keeps its first min(count, slots) nonzeros in ascending column order. "Nonzero" is
@@ -137,19 +137,30 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
 
 /*
  * Stages of twell_ffn_fwd, callable one by one (twell_ffn_fwd enqueues exactly
- * twell_up_gemm, twell_up_finish, twell_down, in that order, on its stream):
+ * twell_up_gemm, twell_up_finish, twell_fwd_down, in that order, on its stream):
  *   twell_up_gemm   — the up-projection MFMA GEMM with the fused bias + ReLU + TwELL
  *                     epilogue: writes counts, col_idx, vals and ovf_bits only.
  *   twell_up_finish — the overflow bookkeeping ("Formato Híbrido para Treinamento"): the
  *                     ordered overflow list, ovf_slot, *ovf_n, and ovf_dense recomputed by
- *                     the same GEMM for the listed rows. Must follow twell_up_gemm on the
- *                     same h. After both, h is the complete TwELL of ReLU(x W1 + b1).
- * Same arguments, checks and errors as twell_ffn_fwd.
+ *                     the same GEMM for the listed rows; in the same launch as the
+ *                     overflow scan it also fills the row lists (row_nnz, row_list) that
+ *                     the down projection walks. Must follow twell_up_gemm on the same h.
+ *                     After both, h is the complete TwELL of ReLU(x W1 + b1).
+ * Same arguments, checks and errors as twell_ffn_fwd (twell_up_finish also needs row_nnz
+ * and row_list).
  */
 int twell_up_gemm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
                   int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream);
 int twell_up_finish(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
                     int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream);
+
+/*
+ * twell_fwd_down — the last stage of twell_ffn_fwd: twell_down without rebuilding the row
+ * lists, which twell_up_finish left in h on the same stream. Arguments, checks and errors
+ * as twell_down. Use twell_down for a TwELL from any other producer.
+ */
+int twell_fwd_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model,
+                   void *y, int32_t y_dtype, void *stream);
 
 /*
  * twell_down — y[t] = sum over the nonzero h[t, j] of h[t, j] * w2[j] for an existing
@@ -168,8 +179,14 @@ int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t i
                       int32_t T, int32_t d_model, int32_t d_ff, void *h, int32_t h_dtype,
                       void *stream);
 
-/* Bytes of device workspace twell_ffn_bwd needs for this problem. */
-size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff,
+/*
+ * Bytes of device workspace twell_ffn_bwd needs for this problem (in_dtype as passed to
+ * twell_ffn_bwd; 0 for invalid arguments). Grows with the entry capacity of h
+ * (T * (d_ff / tile_w) * slots + min(ovf_cap, T) * d_ff) times roughly 32 + 4 * d_model / 128
+ * bytes (bf16; d_model / 64 chunks for fp32): the per-column-chunk partial dot products of
+ * the SDDMM are kept so that every XCD reads only its own slices of W2.
+ */
+size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, int32_t in_dtype,
                                      const twell_matrix_t *h);
 
 /*
@@ -184,6 +201,9 @@ size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff,
  *   db1  = sum_t dz                 [f]     fp32 (may be NULL)
  * x, w1t, w2, dy have in_dtype. Requires every overflow row to have a backup slot
  * (*ovf_n <= ovf_cap); rows without one contribute through their slots only.
+ * d_ff <= 16384 (a unit bit mask per 32-token block is built in LDS), else
+ * TWELL_ERR_UNSUPPORTED; workspace_bytes below twell_ffn_bwd_workspace_bytes gives
+ * TWELL_ERR_WORKSPACE.
  */
 int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dtype,
                   int32_t T, int32_t d_model, int32_t d_ff, const twell_matrix_t *h,

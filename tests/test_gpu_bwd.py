@@ -124,7 +124,7 @@ def test_bwd_workspace_too_small():
     f = w1t.shape[0]
     out = [torch.empty(s, dtype=torch.float32, device="cuda") for s in [(T, d), (f, d), (f, d), (f,)]]
     ws = torch.empty(4096, dtype=torch.uint8, device="cuda")
-    need = tw.twell_ffn_bwd_workspace_bytes(T, d, f, h)
+    need = tw.twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype)
     assert need > 4096
     m = h.c()
     st = tw.lib().twell_ffn_bwd(x.data_ptr(), w1t.data_ptr(), w2.data_ptr(), 0, T, d, f, ctypes.byref(m),
