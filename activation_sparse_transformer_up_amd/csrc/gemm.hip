@@ -53,13 +53,13 @@ template <> struct MfmaOps<float> {
   }
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int EPIW>
+template <int BM_, int BN_, int WM_, int WN_, int EPIW, int NS_ = 4>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32;
   static constexpr int RB = 64;                           // bytes of a row per K step
-  static constexpr int NS = 4;                            // pipeline stages
+  static constexpr int NS = NS_;                          // pipeline stages
   static constexpr int STAGE = (BM + BN) * RB;            // bytes per stage (A rows, then B rows)
   static constexpr int LDS_BYTES = NS * STAGE;
   static constexpr int LPW = (BM + BN) / 16 / NW;         // 1 KB wave-loads per wave per stage
@@ -83,6 +83,13 @@ constexpr int epi_wave_bytes(int rs, int tpw, int vbytes) {
 typedef Tile<256, 256, 64, 128, epi_wave_bytes(64, 2, 4)> TileL8;
 typedef Tile<256, 256, 128, 128, epi_wave_bytes(128, 2, 4)> TileL;
 typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4)> TileS;
+// Decode (at most 64 tokens): one wave owns a 64 x 128 tile over half of K with its own
+// 6-stage ring (TileD); two such waves form a workgroup and their partial tiles are added
+// (first half + second half). The weight stream then has twice the loads in flight per
+// workgroup; the K split changes the summation order, so the dense path uses the same split
+// for the same token count.
+typedef Tile<64, 128, 64, 128, epi_wave_bytes(128, 2, 4), 6> TileD;
+constexpr int kDecodeMaxT = 64;
 
 typedef __attribute__((address_space(3))) void lds_void_t;
 
@@ -110,6 +117,9 @@ TW_DEV void block_barrier_lds() {
 // A operand row r of the tile reads global row arow[m0 + r] (if arow) or m0 + r; rows at or
 // beyond a_rows are zero. B operand rows at or beyond b_rows are zero. a_total rows exist
 // in A (bounds of the buffer resource). Operands must be smaller than 2 GiB.
+// K split: the loop covers k in [kofs, kofs + K) of rows that are lda elements long (lda = 0:
+// lda = K); vwave >= 0 makes the calling wave act as wave vwave of G (a wave running its
+// own one-wave tile with its own smem ring passes 0).
 //
 // Software pipeline of one K step (two half-steps u = 0, 1 of 16 (bf16) k each):
 //   read fragments (kt, u=1)    | MFMAs on fragments (kt, u=0)
@@ -122,20 +132,21 @@ TW_DEV void block_barrier_lds() {
 template <typename T, class G>
 TW_DEV void mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, int a_rows, int a_total,
                      const T *__restrict__ B, int b_rows, int K, int m0, int n0,
-                     f32x16_t (&acc)[G::MB][G::NB], char *smem) {
+                     f32x16_t (&acc)[G::MB][G::NB], char *smem, int lda = 0, int kofs = 0, int vwave = -1) {
   static_assert(G::NS >= 3, "stages");
   constexpr int EPC = 16 / sizeof(T);                     // elements per 16-byte chunk
   constexpr int KPT = G::RB / sizeof(T);                  // k per stage
   constexpr int NMMA = G::MB * G::NB;
   constexpr uint32_t OOB = 0x80000000u;
   const int tid = threadIdx.x, lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wave = vwave >= 0 ? vwave : __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave / G::NWN, wn = wave % G::NWN;
-  const size_t row_bytes = (size_t)K * sizeof(T);
+  const size_t row_bytes = (size_t)(lda ? lda : K) * sizeof(T);
+  const size_t shift = (size_t)kofs * sizeof(T);
   const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)A, (short)0, (int)((size_t)a_total * row_bytes), 0x00020000);
+      (void *)(A + kofs), (short)0, (int)((size_t)a_total * row_bytes - shift), 0x00020000);
   const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc(
-      (void *)B, (short)0, (int)((size_t)b_rows * row_bytes), 0x00020000);
+      (void *)(B + kofs), (short)0, (int)((size_t)b_rows * row_bytes - shift), 0x00020000);
 
   // This lane's part of each of its wave-loads: LDS row lr16 = l / 4 of a 16-row block,
   // physical chunk l % 4 holding logical chunk c.
@@ -448,6 +459,95 @@ __global__ __launch_bounds__(G::NT) void k_up_dense(const T *__restrict__ x, con
   epi_dense<G>(acc, b1, rows, N, m0, n0, out, out_bf16, relu);
 }
 
+
+// ------------------------------------------------------------------ decode (K split)
+
+// Two waves of TileD: wave w covers k in [w K / 2, (w + 1) K / 2) through its own ring; after
+// the loop wave 1 leaves its partial tile in LDS and wave 0 adds it (first half + second
+// half). K is a multiple of two stages (the launchers check), so both waves run the same
+// number of loop steps and barriers.
+template <typename T>
+TW_DEV void decode_mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, int a_rows, int a_total,
+                            const T *__restrict__ B, int N, int K, int n0,
+                            f32x16_t (&acc)[TileD::MB][TileD::NB], char *smem) {
+  typedef TileD G;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kh = K / 2;
+  mainloop<T, G>(A, arow, a_rows, a_total, B, N, kh, 0, n0, acc, smem + w * G::LDS_BYTES, K, w * kh, 0);
+  block_barrier();                          // both rings are done; wave 0's ring takes the partial
+  const int lane = threadIdx.x & 63;
+  float *red = (float *)smem;
+  if (w == 1) {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) red[((mb * G::NB + nb) * 16 + r) * 64 + lane] = acc[mb][nb][r];
+  }
+  block_barrier();
+  if (w == 0) {
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) acc[mb][nb][r] += red[((mb * G::NB + nb) * 16 + r) * 64 + lane];
+  }
+}
+
+constexpr int kDecodeSmem = 2 * TileD::LDS_BYTES > TileD::EPI_WAVE ? 2 * TileD::LDS_BYTES : TileD::EPI_WAVE;
+static_assert(kDecodeSmem <= 160 * 1024, "LDS");
+
+template <typename T, int W, typename VT>
+__global__ __launch_bounds__(128) void k_up_twell_dec(const T *__restrict__ x, const T *__restrict__ w1t,
+                                                      const float *__restrict__ b1, int M, int N, int K,
+                                                      TwellOut o) {
+  __shared__ __attribute__((aligned(16))) char smem[kDecodeSmem];
+  const int n0 = blockIdx.x * TileD::BN;
+  float nbias[TileD::NB];
+#pragma unroll
+  for (int nb = 0; nb < TileD::NB; ++nb) {
+    const int col = n0 + nb * 32 + (threadIdx.x & 31);
+    nbias[nb] = col < N ? -b1[col] : 0.f;
+  }
+  f32x16_t acc[TileD::MB][TileD::NB];
+#pragma unroll
+  for (int mb = 0; mb < TileD::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < TileD::NB; ++nb) acc[mb][nb] = f32x16_t{};
+  decode_mainloop<T>(x, nullptr, M, M, w1t, N, K, n0, acc, smem);
+  if (threadIdx.x >= 64) return;            // wave 0 holds the sum and writes the TwELL
+  epi_twell<TileD, W, VT>(acc, nbias, M, N, 0, n0, o, smem);
+}
+
+template <typename T>
+__global__ __launch_bounds__(128) void k_up_dense_dec(const T *__restrict__ x, const T *__restrict__ w1t,
+                                                      const float *__restrict__ b1, int M, int N, int K, int x_rows,
+                                                      const int32_t *__restrict__ arow,
+                                                      const int32_t *__restrict__ n_rows_dev, void *out,
+                                                      int out_bf16, int relu) {
+  __shared__ __attribute__((aligned(16))) char smem[2 * TileD::LDS_BYTES];
+  const int n0 = blockIdx.x * TileD::BN;
+  int rows = M;
+  if (n_rows_dev) rows = min(rows, *n_rows_dev);
+  if (rows <= 0) return;
+  f32x16_t acc[TileD::MB][TileD::NB];
+#pragma unroll
+  for (int mb = 0; mb < TileD::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < TileD::NB; ++nb) acc[mb][nb] = f32x16_t{};
+  decode_mainloop<T>(x, arow, rows, x_rows, w1t, N, K, n0, acc, smem);
+  if (threadIdx.x >= 64) return;
+  epi_dense<TileD>(acc, b1, rows, N, 0, n0, out, out_bf16, relu);
+}
+
+// The decode kernels apply to at most 64 tokens and K a multiple of two stages.
+template <typename T> static bool use_decode(int T_tokens, int K) {
+  constexpr int KPT = TileD::RB / (int)sizeof(T);
+  return T_tokens <= kDecodeMaxT && K % (2 * KPT) == 0;
+}
+
 // ------------------------------------------------------------------ host launchers
 
 template <typename T, class G>
@@ -467,8 +567,26 @@ static hipError_t launch_twell_t(const T *x, const T *w1t, const float *b1, int 
 
 static bool use_large(int M, int N) { return M >= 512 && N >= 1024; }
 
+template <typename T>
+static hipError_t launch_twell_dec(const T *x, const T *w1t, const float *b1, int M, int N, int K, const TwellOut &o,
+                                   int W, hipStream_t s) {
+  const dim3 grid((N + TileD::BN - 1) / TileD::BN);
+  if (o.val_bf16) {
+    if (W == 64) hipLaunchKernelGGL((k_up_twell_dec<T, 64, uint16_t>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, o);
+    else hipLaunchKernelGGL((k_up_twell_dec<T, 128, uint16_t>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, o);
+  } else {
+    if (W == 64) hipLaunchKernelGGL((k_up_twell_dec<T, 64, float>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, o);
+    else hipLaunchKernelGGL((k_up_twell_dec<T, 128, float>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, o);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N,
                            int K, const TwellOut &o, int W, hipStream_t s) {
+  if (bf16 && use_decode<uint16_t>(M, K))
+    return launch_twell_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
+  if (!bf16 && use_decode<float>(M, K))
+    return launch_twell_dec<float>((const float *)x, (const float *)w1t, b1, M, N, K, o, W, s);
   if (bf16) {
     if (use_large(M, N) && (TileL8::WN / W) * o.S <= 64)
       return launch_twell_t<uint16_t, TileL8>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
@@ -489,9 +607,27 @@ static hipError_t launch_dense_t(const T *x, const T *w1t, const float *b1, int 
   return hipGetLastError();
 }
 
+template <typename T>
+static hipError_t launch_dense_dec(const T *x, const T *w1t, const float *b1, int M, int N, int K, int x_rows,
+                                   const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
+                                   hipStream_t s) {
+  const dim3 grid((N + TileD::BN - 1) / TileD::BN);
+  hipLaunchKernelGGL((k_up_dense_dec<T>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, x_rows, arow, n_rows_dev, out,
+                     out_bf16, relu);
+  return hipGetLastError();
+}
+
+// x_rows is the token count of the problem (for the overflow-row recompute it exceeds M): the
+// K split is chosen by it, as in launch_up_twell, so both paths sum in the same order.
 hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
                            int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16,
                            int relu, hipStream_t s) {
+  if (bf16 && use_decode<uint16_t>(x_rows, K))
+    return launch_dense_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
+                                      n_rows_dev, out, out_bf16, relu, s);
+  if (!bf16 && use_decode<float>(x_rows, K))
+    return launch_dense_dec<float>((const float *)x, (const float *)w1t, b1, M, N, K, x_rows, arow, n_rows_dev, out,
+                                   out_bf16, relu, s);
   if (bf16) {
     if (use_large(M, N) && !arow)
       return launch_dense_t<uint16_t, TileL8>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
