@@ -4,11 +4,25 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+#include <utility>
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 typedef float f32x16_t __attribute__((ext_vector_type(16)));
 
 #define TW_DEV __device__ __forceinline__
+
+// f(std::integral_constant<int, 0>()), ..., f(std::integral_constant<int, N - 1>()): the
+// index is a constant expression inside f, whatever the inliner and unroller do (register
+// arrays indexed by it stay in registers).
+template <typename F, int... J>
+TW_DEV void static_for_impl(F &&f, std::integer_sequence<int, J...>) {
+  (f(std::integral_constant<int, J>()), ...);
+}
+template <int N, typename F> TW_DEV void static_for(F &&f) {
+  static_for_impl(f, std::make_integer_sequence<int, N>());
+}
 
 // bf16 is carried as its raw 16-bit pattern in memory.
 TW_DEV float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }

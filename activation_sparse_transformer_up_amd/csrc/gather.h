@@ -12,22 +12,9 @@
 // and all sixteen row loads are issued before the FMAs; the next round's pairs are loaded
 // meanwhile. Accumulation is fp32 in list order.
 #pragma once
-#include <type_traits>
-#include <utility>
-
 #include "common.h"
 
 namespace tw {
-
-// f(std::integral_constant<int, 0>()), ..., f(std::integral_constant<int, N - 1>()): the
-// index is a constant expression inside f, whatever the inliner and unroller do.
-template <typename F, int... J>
-TW_DEV void static_for_impl(F &&f, std::integer_sequence<int, J...>) {
-  (f(std::integral_constant<int, J>()), ...);
-}
-template <int N, typename F> TW_DEV void static_for(F &&f) {
-  static_for_impl(f, std::make_integer_sequence<int, N>());
-}
 
 // Lane J of this lane's 16-lane row (DPP row broadcast).
 template <int J> TW_DEV uint32_t row_bcast(uint32_t v) {
