@@ -53,11 +53,15 @@ template <> struct MfmaOps<float> {
   }
 };
 
-template <int BM_, int BN_, int WM_, int WN_, int EPIW, int NS_ = 4>
+template <int BM_, int BN_, int WM_, int WN_, int EPIW, int NS_ = 4, int MI_ = 32>
 struct Tile {
   static constexpr int BM = BM_, BN = BN_, WM = WM_, WN = WN_;
   static constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN, NT = NW * 64;
   static constexpr int MB = WM / 32, NB = WN / 32;
+  // MFMA shape: 32 (v_mfma_f32_32x32x16_bf16 / 32x32x2_f32, f32x16_t accumulators per
+  // 32 x 32 block) or 16 (v_mfma_f32_16x16x32_bf16, f32x4_t per 16 x 16 block: FM x FN)
+  static constexpr int MI = MI_;
+  static constexpr int FM = WM / 16, FN = WN / 16;
   static constexpr int RB = 64;                           // bytes of a row per K step
   static constexpr int NS = NS_;                          // pipeline stages
   static constexpr int STAGE = (BM + BN) * RB;            // bytes per stage (A rows, then B rows)
@@ -80,9 +84,10 @@ constexpr int epi_wave_bytes(int rs, int tpw, int vbytes) {
 // up to 64 slots per row per wave. TileL (4 waves of 128 x 128) takes the larger slot
 // counts (W = 64 with S > 32). Few tokens: 64 x 128 tiles. Waves are 128 columns wide so
 // that a 64- or 128-wide TwELL tile never straddles two waves.
-typedef Tile<256, 256, 64, 128, epi_wave_bytes(64, 2, 4)> TileL8;
-typedef Tile<256, 256, 128, 128, epi_wave_bytes(128, 2, 4)> TileL;
-typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4)> TileS;
+typedef Tile<256, 256, 64, 128, epi_wave_bytes(64, 2, 4), 4, 16> TileL8;
+typedef Tile<256, 256, 128, 128, epi_wave_bytes(128, 2, 4), 4, 16> TileL;
+typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4), 4, 16> TileS;
+typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4)> TileSF;      // fp32 operands
 // Decode (at most 64 tokens): one wave owns a 64 x 128 tile over half of K with its own
 // 6-stage ring (TileD); two such waves form a workgroup and their partial tiles are added
 // (first half + second half). The weight stream then has twice the loads in flight per
@@ -249,6 +254,150 @@ TW_DEV void mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, 
   mma(a1, b1);
 }
 
+// The same operand staging with v_mfma_f32_16x16x32_bf16 (bf16 only; Tile::MI == 16). A
+// 16 x 16 x 32 MFMA takes a 16-row block of a whole stage (16 rows x 32 k: lane l reads row
+// l % 16, 16-byte chunk l / 16), so each stage is read as FM + FN fragments. Against the
+// 32 x 32 x 16 form the accumulator traffic per multiply-add halves, which lowers the power
+// of the loop and so raises the clock the chip sustains under it (the K loop is
+// power-limited on gfx950). One barrier per stage:
+//   wait for stage kt + 1's loads, barrier
+//   MFMAs on the fragments of stage kt, interleaved with the reads of stage kt + 1 (into
+//   the other fragment set) and with the loads of stage kt + NS - 1
+// The stage overwritten by those loads, (kt - 1) mod NS, was read during step kt - 2.
+template <class G>
+TW_DEV void mainloop16(const uint16_t *__restrict__ A, const int32_t *__restrict__ arow, int a_rows, int a_total,
+                       const uint16_t *__restrict__ B, int b_rows, int K, int m0, int n0,
+                       f32x4_t (&acc)[G::FM][G::FN], char *smem) {
+  static_assert(G::NS >= 3 && G::MI == 16, "stages / shape");
+  constexpr int KPT = G::RB / 2;                          // k per stage
+  constexpr int NM = G::FM * G::FN;                       // MFMAs per stage
+  constexpr int NR = G::FM + G::FN;                       // fragment reads per stage
+  constexpr int RI = NM / NR >= 2 ? NM / NR : 1;          // a read after every RI MFMAs
+  constexpr int DI = NM / G::LPW >= 1 ? NM / G::LPW : 1;  // a stage load after every DI MFMAs
+  constexpr uint32_t OOB = 0x80000000u;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm = wave / G::NWN, wn = wave % G::NWN;
+  const size_t row_bytes = (size_t)K * 2;
+  const __amdgpu_buffer_rsrc_t ra =
+      __builtin_amdgcn_make_buffer_rsrc((void *)A, (short)0, (int)((size_t)a_total * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)B, (short)0, (int)((size_t)b_rows * row_bytes), 0x00020000);
+  // stage loads: as in mainloop (LDS row lrow of a 16-row block, physical chunk cl)
+  const int lrow = lane >> 2;
+  const int cl = (lane & 3) ^ ((lrow >> 2) & 3);
+  uint32_t voff[G::LPW];
+  bool isA[G::LPW];
+  int ldsq[G::LPW];
+#pragma unroll
+  for (int i = 0; i < G::LPW; ++i) {
+    const int q = wave + G::NW * i;
+    const int r = q * 16 + lrow;
+    ldsq[i] = q * 1024;
+    isA[i] = q * 16 < G::BM;
+    if (isA[i]) {
+      const int gr = m0 + r;
+      voff[i] = gr < a_rows ? (uint32_t)((size_t)(arow ? arow[gr] : gr) * row_bytes) + cl * 16 : OOB;
+    } else {
+      const int gr = n0 + (r - G::BM);
+      voff[i] = gr < b_rows ? (uint32_t)((size_t)gr * row_bytes) + cl * 16 : OOB;
+    }
+  }
+  const int nk = (K + KPT - 1) / KPT;
+  const int kc = cl * 8;
+  auto issue1 = [&](int kt, int i) {
+    const int k0 = kt * KPT;
+    char *st = smem + (kt % G::NS) * G::STAGE;
+    const uint32_t vo = (k0 + kc < K) ? voff[i] : OOB;
+    lds_void_t *dst = (lds_void_t *)(st + ldsq[i]);
+    if (isA[i]) __builtin_amdgcn_raw_ptr_buffer_load_lds(ra, dst, 16, vo, k0 * 2, 0, 0);
+    else __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, dst, 16, vo, k0 * 2, 0, 0);
+  };
+  typedef u32x4_t FA[G::FM];
+  typedef u32x4_t FB[G::FN];
+  const int l16 = lane & 15, c4 = lane >> 4;
+  // fragment j of stage kt: j < FM the A block j, else the B block j - FM
+  auto read1 = [&](int kt, int j, FA &a, FB &b) {
+    const char *sa = smem + (kt % G::NS) * G::STAGE;
+    if (j < G::FM) {
+      const int r = wm * G::WM + j * 16 + l16;
+      a[j] = *(const u32x4_t *)(sa + r * G::RB + ((c4 ^ ((r >> 2) & 3)) << 4));
+    } else {
+      const int r = wn * G::WN + (j - G::FM) * 16 + l16;
+      b[j - G::FM] = *(const u32x4_t *)(sa + G::BM * G::RB + r * G::RB + ((c4 ^ ((r >> 2) & 3)) << 4));
+    }
+  };
+  auto mma = [&](int i, const FA &a, const FB &b) {
+    acc[i / G::FN][i % G::FN] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+        __builtin_bit_cast(bf16x8_t, a[i / G::FN]), __builtin_bit_cast(bf16x8_t, b[i % G::FN]),
+        acc[i / G::FN][i % G::FN], 0, 0, 0);
+  };
+  if (nk == 0) return;
+#pragma unroll
+  for (int st = 0; st < G::NS - 1; ++st)
+    if (st < nk)
+#pragma unroll
+      for (int i = 0; i < G::LPW; ++i) issue1(st, i);
+  if (nk >= G::NS - 1) wait_vmcnt<(G::NS - 2) * G::LPW>();
+  else wait_vmcnt<0>();
+  block_barrier();
+  FA a0, a1;
+  FB b0, b1;
+#pragma unroll
+  for (int j = 0; j < NR; ++j) read1(0, j, a0, b0);
+  // step kt < nk - 1: MFMAs on (ac, bc) = stage kt, reads of stage kt + 1 into (an, bn);
+  // LOAD: stage kt + NS - 1 exists and is loaded in this step
+  auto step = [&](int kt, const FA &ac, const FB &bc, FA &an, FB &bn, auto load_tag) {
+    constexpr bool LOAD = decltype(load_tag)::value;
+    if (LOAD) wait_vmcnt<(G::NS - 3) * G::LPW>();          // stage kt + 1 has landed
+    else wait_vmcnt<0>();
+    block_barrier_lds();
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      mma(i, ac, bc);
+      if constexpr (i % RI == 0 && i / RI < NR) read1(kt + 1, i / RI, an, bn);
+      if constexpr (LOAD && i % DI == DI - 1 && i / DI < G::LPW) issue1(kt + G::NS - 1, i / DI);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if constexpr (NM / RI < NR)
+#pragma unroll
+      for (int j = NM / RI; j < NR; ++j) read1(kt + 1, j, an, bn);
+    if constexpr (LOAD && NM / DI < G::LPW)
+#pragma unroll
+      for (int i = NM / DI; i < G::LPW; ++i) issue1(kt + G::NS - 1, i);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  const std::integral_constant<bool, true> ld;
+  const std::integral_constant<bool, false> nold;
+  auto settle = [&]() {                   // next fragment set -> current (tail steps only)
+#pragma unroll
+    for (int j = 0; j < G::FM; ++j) a0[j] = a1[j];
+#pragma unroll
+    for (int j = 0; j < G::FN; ++j) b0[j] = b1[j];
+  };
+  // Steps kt < nl load stage kt + NS - 1; the last NS - 2 steps (fewer if nk is small) do
+  // not. Loading steps run in pairs (the fragment sets alternate); an odd one and the
+  // non-loading ones copy the next set into the current one after the step.
+  const int nl = nk >= G::NS ? nk - G::NS + 1 : 0;
+  int kt = 0;
+  for (; kt + 1 < nl; kt += 2) {
+    step(kt, a0, b0, a1, b1, ld);
+    step(kt + 1, a1, b1, a0, b0, ld);
+  }
+  if (kt < nl) {
+    step(kt, a0, b0, a1, b1, ld);
+    settle();
+    ++kt;
+  }
+  for (; kt + 1 < nk; ++kt) {
+    step(kt, a0, b0, a1, b1, nold);
+    settle();
+  }
+#pragma unroll
+  for (int i = 0; i < NM; ++i) mma(i, a0, b0);
+}
+
 // Output position of accumulator register r of a 32x32 block, for this lane:
 //   row = 8 * (r / 4) + 4 * (lane / 32) + r % 4,   col = lane % 32.
 TW_DEV int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
@@ -379,6 +528,127 @@ TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB]
   }
 }
 
+// The TwELL epilogue on 16 x 16 accumulator blocks (Tile::MI == 16): register i of block
+// (fm, fn) holds row fm * 16 + 4 * (lane / 16) + i, column fn * 16 + lane % 16, so one
+// ballot covers 16 columns of four rows (lane group g = lane / 16 owns row 4 g + i). The
+// steps per 16-row block are those of epi_twell: pad the LDS slot block, scatter the active
+// (column, value) pairs into their slots, copy the block out with 16-byte stores. Overflow
+// bits are gathered per 32-row word over two 16-row blocks.
+template <class G, int W, typename VT>
+TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN], int M, int N, int m0,
+                        int n0, const TwellOut &o, char *smem) {
+  constexpr int BPT = W / 16;                   // 16-column blocks per TwELL tile
+  constexpr int TPW = G::WN / W;                // TwELL tiles per wave
+  static_assert(G::WN % W == 0 && G::FM % 2 == 0, "a TwELL tile must sit inside one wave");
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int wm = wave / G::NWN, wn = wave % G::NWN;
+  const int g = lane >> 4, li = lane & 15;
+  const int row0 = m0 + wm * G::WM, col0 = n0 + wn * G::WN;
+  const int S = o.S;
+  const int kt0 = col0 / W;
+  const int tiles = min(TPW, o.n_t - kt0);
+  if (tiles <= 0) return;
+  const int RS = TPW * S;
+  // wave-private LDS: idx [16][RS] + junk[64] | vals [16][RS] + junk[64] | counts [16][TPW] + junk[64]
+  char *base = smem + wave * G::EPI_WAVE;
+  int32_t *lidx = (int32_t *)base;
+  VT *lval = (VT *)(lidx + 16 * RS + 64);
+  int32_t *lcnt = (int32_t *)(base + ((4 * (16 * RS + 64) + (int)sizeof(VT) * (16 * RS + 64) + 15) & ~15));
+  const int JI = 16 * RS + lane;
+  const uint32_t below = (1u << li) - 1u;
+  const bool vec_ok = (S * (int)sizeof(VT)) % 16 == 0;
+  uint32_t ovfv[TPW];                            // overflow bits of this lane's rows, 32-row word
+#pragma unroll
+  for (int fm = 0; fm < G::FM; ++fm) {
+    const int rb0 = row0 + fm * 16;
+    if (rb0 >= M) break;                         // wave-uniform
+    if (fm % 2 == 0)
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) ovfv[q] = 0;
+    for (int i = lane; i < 16 * RS / 4; i += 64) ((int4 *)lidx)[i] = make_int4(-1, -1, -1, -1);
+    for (int i = lane; i < 16 * RS * (int)sizeof(VT) / 16; i += 64) ((int4 *)lval)[i] = make_int4(0, 0, 0, 0);
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int kt = kt0 + q;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int lrow = 4 * g + r;                           // row of this lane in the block
+        int pre = 0;
+#pragma unroll
+        for (int b = 0; b < BPT; ++b) {
+          const int nb = q * BPT + b;
+          const float zb = acc[fm][nb][r];
+          const bool on = zb > nbias[nb];
+          const uint64_t bal = ballot64(on);
+          if (bal == 0) continue;                             // wave-uniform
+          const uint32_t hm = (uint32_t)(bal >> (16 * g)) & 0xFFFFu;
+          const int slot = pre + __popc(hm & below);
+          const bool act = on && slot < S;
+          const int e = act ? lrow * RS + q * S + slot : JI;
+          lidx[e] = kt * W + b * 16 + li;
+          Elem<VT>::store(lval, e, zb - nbias[nb]);
+          pre += __popc(hm);
+        }
+        const int e = li == 0 ? lrow * TPW + q : 16 * TPW + lane;
+        lcnt[e] = pre;
+        ovfv[q] |= (pre > S ? 1u : 0u) << ((fm & 1) * 16 + lrow);
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    const int nrow = min(16, M - rb0);
+    const int relem = tiles * S;
+    if (vec_ok) {
+      const int ci = relem / 4, cv = relem * (int)sizeof(VT) / 16;
+      for (int i = lane; i < nrow * ci; i += 64) {
+        const int rr = i / ci, c = i - rr * ci;
+        const size_t gi = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
+        *(int4 *)(o.col_idx + gi + 4 * c) = *(const int4 *)(lidx + rr * RS + 4 * c);
+      }
+      constexpr int EV = 16 / sizeof(VT);
+      for (int i = lane; i < nrow * cv; i += 64) {
+        const int rr = i / cv, c = i - rr * cv;
+        const size_t gi = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
+        *(int4 *)((VT *)o.vals + gi + EV * c) = *(const int4 *)(lval + rr * RS + EV * c);
+      }
+    } else {
+      for (int i = lane; i < nrow * relem; i += 64) {
+        const int rr = i / relem, c = i - rr * relem;
+        const size_t gi = ((size_t)(rb0 + rr) * o.n_t + kt0) * S + c;
+        o.col_idx[gi] = lidx[rr * RS + c];
+        ((VT *)o.vals)[gi] = lval[rr * RS + c];
+      }
+    }
+    for (int i = lane; i < nrow * tiles; i += 64) {
+      const int rr = i / tiles, c = i - rr * tiles;
+      o.counts[(size_t)(rb0 + rr) * o.n_t + kt0 + c] = lcnt[rr * TPW + c];
+    }
+    // after the second 16-row block of a 32-row word (or the last block inside the matrix)
+    const bool last = fm == G::FM - 1 || rb0 + 16 >= M;
+    if (fm % 2 == 1 || last) {
+      const int wb0 = rb0 - (fm & 1) * 16;                    // first row of the word
+      const int nw = min(32, M - wb0);
+      const uint32_t valid = nw >= 32 ? 0xFFFFFFFFu : ((1u << nw) - 1u);
+#pragma unroll
+      for (int q = 0; q < TPW; ++q) {
+        const uint32_t word = (uint32_t)__builtin_amdgcn_readlane((int)ovfv[q], 0) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)ovfv[q], 16) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)ovfv[q], 32) |
+                              (uint32_t)__builtin_amdgcn_readlane((int)ovfv[q], 48);
+        if (q < tiles && lane == 0) o.ovf_bits[(size_t)(kt0 + q) * o.words + (wb0 >> 5)] = word & valid;
+      }
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  }
+}
+
 // ---------------------------------------------------------------- dense epilogue
 // out[orow][col] = ReLU(z + b1) (or z + b1 without ReLU), fp32 or bf16, orow = tile row.
 template <class G>
@@ -409,6 +679,35 @@ TW_DEV void epi_dense(f32x16_t (&acc)[G::MB][G::NB], const float *__restrict__ b
   }
 }
 
+// epi_dense on 16 x 16 accumulator blocks (Tile::MI == 16).
+template <class G>
+TW_DEV void epi_dense16(f32x4_t (&acc)[G::FM][G::FN], const float *__restrict__ b1, int rows_valid, int N,
+                        int m0, int n0, void *out, int out_bf16, int relu) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / G::NWN, wn = wave % G::NWN;
+  const int g = lane >> 4, li = lane & 15;
+  const int row0 = m0 + wm * G::WM, col0 = n0 + wn * G::WN;
+#pragma unroll
+  for (int fn = 0; fn < G::FN; ++fn) {
+    const int col = col0 + fn * 16 + li;
+    if (col >= N) continue;
+    const float bias = b1 ? b1[col] : 0.f;
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int row = row0 + fm * 16 + 4 * g + r;
+        if (row >= rows_valid) continue;
+        float z = acc[fm][fn][r] + bias;
+        if (relu) z = z > 0.f ? z : 0.f;
+        const size_t i = (size_t)row * N + col;
+        if (out_bf16) ((uint16_t *)out)[i] = (uint16_t)f32_to_bf16(z);
+        else ((float *)out)[i] = z;
+      }
+    }
+  }
+}
+
 // ------------------------------------------------------------------------ kernels
 
 template <typename T, class G, int W, typename VT>
@@ -417,24 +716,40 @@ __global__ __launch_bounds__(G::NT) void k_up_twell(const T *__restrict__ x, con
                                                     TwellOut o) {
   __shared__ __attribute__((aligned(16))) char smem[G::SMEM];
   const int n0 = blockIdx.x * G::BN, m0 = blockIdx.y * G::BM;
-  // -b1 of this lane's columns, fetched before the K loop so its latency is hidden
-  float nbias[G::NB];
-  {
-    const int wn = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % G::NWN;
+  const int wn = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) % G::NWN;
+  if constexpr (G::MI == 16) {
+    static_assert(std::is_same<T, uint16_t>::value, "16x16x32 MFMA tiles take bf16 operands");
+    // -b1 of this lane's columns, fetched before the K loop so its latency is hidden
+    float nbias[G::FN];
+#pragma unroll
+    for (int fn = 0; fn < G::FN; ++fn) {
+      const int col = n0 + wn * G::WN + fn * 16 + (threadIdx.x & 15);
+      nbias[fn] = col < N ? -b1[col] : 0.f;
+    }
+    f32x4_t acc[G::FM][G::FN];
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < G::FN; ++fn) acc[fm][fn] = f32x4_t{};
+    mainloop16<G>(x, nullptr, M, M, w1t, N, K, m0, n0, acc, smem);
+    block_barrier();                    // every wave is done reading the operand stages
+    epi_twell16<G, W, VT>(acc, nbias, M, N, m0, n0, o, smem);
+  } else {
+    float nbias[G::NB];
 #pragma unroll
     for (int nb = 0; nb < G::NB; ++nb) {
       const int col = n0 + wn * G::WN + nb * 32 + (threadIdx.x & 31);
       nbias[nb] = col < N ? -b1[col] : 0.f;
     }
+    f32x16_t acc[G::MB][G::NB];
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x16_t{};
+    mainloop<T, G>(x, nullptr, M, M, w1t, N, K, m0, n0, acc, smem);
+    block_barrier();
+    epi_twell<G, W, VT>(acc, nbias, M, N, m0, n0, o, smem);
   }
-  f32x16_t acc[G::MB][G::NB];
-#pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
-#pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x16_t{};
-  mainloop<T, G>(x, nullptr, M, M, w1t, N, K, m0, n0, acc, smem);
-  block_barrier();                      // every wave is done reading the operand stages
-  epi_twell<G, W, VT>(acc, nbias, M, N, m0, n0, o, smem);
 }
 
 // Dense ReLU(x W1 + b1). With arow != NULL the A rows are gathered: tile row i reads x row
@@ -450,13 +765,24 @@ __global__ __launch_bounds__(G::NT) void k_up_dense(const T *__restrict__ x, con
   int rows = M;
   if (n_rows_dev) rows = min(rows, *n_rows_dev);
   if (m0 >= rows) return;
-  f32x16_t acc[G::MB][G::NB];
+  if constexpr (G::MI == 16) {
+    static_assert(std::is_same<T, uint16_t>::value, "16x16x32 MFMA tiles take bf16 operands");
+    f32x4_t acc[G::FM][G::FN];
 #pragma unroll
-  for (int mb = 0; mb < G::MB; ++mb)
+    for (int fm = 0; fm < G::FM; ++fm)
 #pragma unroll
-    for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x16_t{};
-  mainloop<T, G>(x, arow, rows, x_rows, w1t, N, K, m0, n0, acc, smem);
-  epi_dense<G>(acc, b1, rows, N, m0, n0, out, out_bf16, relu);
+      for (int fn = 0; fn < G::FN; ++fn) acc[fm][fn] = f32x4_t{};
+    mainloop16<G>(x, arow, rows, x_rows, w1t, N, K, m0, n0, acc, smem);
+    epi_dense16<G>(acc, b1, rows, N, m0, n0, out, out_bf16, relu);
+  } else {
+    f32x16_t acc[G::MB][G::NB];
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x16_t{};
+    mainloop<T, G>(x, arow, rows, x_rows, w1t, N, K, m0, n0, acc, smem);
+    epi_dense<G>(acc, b1, rows, N, m0, n0, out, out_bf16, relu);
+  }
 }
 
 
@@ -594,7 +920,7 @@ hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float
       return launch_twell_t<uint16_t, TileL>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
     return launch_twell_t<uint16_t, TileS>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
   }
-  return launch_twell_t<float, TileS>((const float *)x, (const float *)w1t, b1, M, N, K, o, W, s);
+  return launch_twell_t<float, TileSF>((const float *)x, (const float *)w1t, b1, M, N, K, o, W, s);
 }
 
 template <typename T, class G>
@@ -635,7 +961,7 @@ hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float
     return launch_dense_t<uint16_t, TileS>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
                                            n_rows_dev, out, out_bf16, relu, s);
   }
-  return launch_dense_t<float, TileS>((const float *)x, (const float *)w1t, b1, M, N, K, x_rows, arow, n_rows_dev,
+  return launch_dense_t<float, TileSF>((const float *)x, (const float *)w1t, b1, M, N, K, x_rows, arow, n_rows_dev,
                                       out, out_bf16, relu, s);
 }
 
