@@ -24,6 +24,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "stage.h"
 
 namespace tw {
 
@@ -95,29 +96,6 @@ typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4)> TileSF;      // fp32 o
 // for the same token count.
 typedef Tile<64, 128, 64, 128, epi_wave_bytes(128, 2, 4), 6> TileD;
 constexpr int kDecodeMaxT = 64;
-
-typedef __attribute__((address_space(3))) void lds_void_t;
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
-template <int N> TW_DEV void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt");
-  __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
-}
-
-TW_DEV void block_barrier() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
-
-// Barrier after this wave's LDS reads have completed (lgkmcnt(0)), so that no read of a
-// stage can still be pending when another wave's loads overwrite it.
-TW_DEV void block_barrier_lds() {
-  asm volatile("" ::: "memory");
-  __builtin_amdgcn_s_waitcnt(0xF | (7 << 4) | (0 << 8) | (3 << 14));
-  __builtin_amdgcn_s_barrier();
-  asm volatile("" ::: "memory");
-}
 
 // A operand row r of the tile reads global row arow[m0 + r] (if arow) or m0 + r; rows at or
 // beyond a_rows are zero. B operand rows at or beyond b_rows are zero. a_total rows exist
@@ -448,9 +426,7 @@ TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB]
     // 1. pad pattern
     for (int i = lane; i < 32 * RS / 4; i += 64) ((int4 *)lidx)[i] = make_int4(-1, -1, -1, -1);
     for (int i = lane; i < 32 * RS * (int)sizeof(VT) / 16; i += 64) ((int4 *)lval)[i] = make_int4(0, 0, 0, 0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_order();
     // 2. active units -> slots
     uint32_t ovfv[TPW];                          // rows of this lane's half that overflow
 #pragma unroll
@@ -482,9 +458,7 @@ TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB]
         ovfv[q] |= (pre > S ? 1u : 0u) << lrow;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_order();
     // 3. copy out rows rb0 .. rb0 + 31: row r's slots of tiles kt0 .. kt0 + tiles - 1 are
     //    contiguous in the output (tiles * S elements at (row * n_t + kt0) * S)
     const int nrow = min(32, M - rb0);
@@ -522,9 +496,7 @@ TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB]
                             (uint32_t)__builtin_amdgcn_readlane((int)ovfv[q], 32);
       if (q < tiles && lane == 0) o.ovf_bits[(size_t)(kt0 + q) * o.words + (rb0 >> 5)] = word & valid;
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_order();
   }
 }
 
@@ -568,9 +540,7 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
       for (int q = 0; q < TPW; ++q) ovfv[q] = 0;
     for (int i = lane; i < 16 * RS / 4; i += 64) ((int4 *)lidx)[i] = make_int4(-1, -1, -1, -1);
     for (int i = lane; i < 16 * RS * (int)sizeof(VT) / 16; i += 64) ((int4 *)lval)[i] = make_int4(0, 0, 0, 0);
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_order();
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
       const int kt = kt0 + q;
@@ -598,9 +568,7 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
         ovfv[q] |= (pre > S ? 1u : 0u) << ((fm & 1) * 16 + lrow);
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_order();
     const int nrow = min(16, M - rb0);
     const int relem = tiles * S;
     if (vec_ok) {
@@ -643,9 +611,7 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
         if (q < tiles && lane == 0) o.ovf_bits[(size_t)(kt0 + q) * o.words + (wb0 >> 5)] = word & valid;
       }
     }
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    wave_lds_order();
   }
 }
 
