@@ -28,7 +28,6 @@
 
 namespace tw {
 
-typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 template <typename T> struct MfmaOps;
 

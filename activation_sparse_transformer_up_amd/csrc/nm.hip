@@ -8,6 +8,7 @@
 // back to dense bf16 in LDS and multiplies on MFMA (only the activation bytes shrink).
 #include "common.h"
 #include "launch.h"
+#include "stage.h"
 
 namespace tw {
 
@@ -162,151 +163,218 @@ hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, 
 }
 
 // ------------------------------------------------------------------- nm_ffn_down
-// y[t][c] = sum_k H[t][k] w2t[c][k] with H expanded from (vals, idx) per K step. Tile 256 x
-// 256, 4 waves of 128 x 128, 32x32x16 bf16 MFMA, K step 32. B (w2t rows) is staged by
-// buffer_load ... lds; A is built by the threads: zero the step's 32 columns of a row, then
-// write its N kept values (two groups per row for M = 16, one for M = 32). Two LDS stages:
-// the packed data of step k+1 is loaded into registers while step k is multiplied.
-// Patterns: 8:16 and 16:32 (M must be a multiple of 8 for the 16-byte zero fill).
-typedef uint32_t u32x4n_t __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) void nm_lds_t;
+// y[t][c] = sum_k H[t][k] w2t[c][k] with H expanded from (vals, idx) per 32-column stage.
+// Tile 256 tokens x 256 output columns, 4 waves of 128 x 128, v_mfma_f32_16x16x32_bf16, a
+// ring of four stages of 64-byte rows (A: 256 expanded H rows, B: 256 w2t rows), read as in
+// the up GEMM (16-row fragments, XOR-swizzled 16-byte chunks).
+//  - B arrives by buffer_load ... lds three stages ahead of its use.
+//  - A: thread r owns tile row r. A stage of a row holds 32 N / M = 16 kept entries (8:16
+//    and 16:32): 32 bytes of values and 16 bytes of indices, loaded into registers one step
+//    before the stage is built. Building writes zeros over the row's 64 bytes, then each
+//    kept value at its column (one thread's LDS writes execute in order).
+// Step kt: wait for stage kt + 1, barrier; load the packed A of stage kt + 4; the MFMAs of
+// stage kt with the fragment reads of stage kt + 1 and the B loads of stage kt + 3 between
+// them; then build the A of stage kt + 3 from the registers loaded in step kt - 1. Stage
+// kt + 3 reuses the buffer of stage kt - 1, whose fragments were read in step kt - 2.
+// Patterns: 8:16 and 16:32 (d_ff a multiple of 32).
+struct NmPack {
+  uint4 v0, v1, ix;                              // 16 values (bf16) and 16 indices (u8)
+};
 
 template <int N, int M>
 __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ vals, const uint8_t *__restrict__ idx,
                                                  int T, int f, const uint16_t *__restrict__ w2t, int d,
                                                  void *__restrict__ y, int y_bf16) {
-  constexpr int BM = 256, BN = 256, RB = 64, STAGE = (BM + BN) * RB;
-  constexpr int GPR = 32 / M;                    // groups of a row per K step
-  constexpr int GPT = BM * GPR / 256;            // groups per thread per K step
-  __shared__ __attribute__((aligned(16))) char smem[2 * STAGE];
+  static_assert(32 % M == 0 && 32 / M * N == 16, "16 kept entries per 32 columns");
+  constexpr int BM = 256, BN = 256, RB = 64, NS = 4, STAGE = (BM + BN) * RB;
+  constexpr int WM = 128, WN = 128, FM = WM / 16, FN = WN / 16;
+  constexpr int NM = FM * FN, NR = FM + FN;
+  constexpr int LPW = BN / 16 / 4;               // B wave-loads per wave per stage
+  constexpr int LA = 3;                          // packed-A loads per thread per stage
+  __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
-  const int G = f / M;                           // groups per row
   const int nk = f / 32;
-  // B operand via LDS DMA: 16 wave-loads of 16 rows per stage, 4 per wave
+  const size_t E = (size_t)f / M * N;            // kept entries per row
+
+  // B: stage rows of w2t through LDS DMA (16-row blocks q = wave + 4 i of the B half)
   constexpr uint32_t OOB = 0x80000000u;
   const size_t row_bytes = (size_t)f * 2;
-  const __amdgpu_buffer_rsrc_t rb = __builtin_amdgcn_make_buffer_rsrc((void *)w2t, (short)0,
-                                                                      (int)((size_t)d * row_bytes), 0x00020000);
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)w2t, (short)0, (int)((size_t)d * row_bytes), 0x00020000);
   const int lrow = lane >> 2, cl = (lane & 3) ^ ((lrow >> 2) & 3);
-  uint32_t voff[4];
+  uint32_t voff[LPW];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int q = wave + 4 * i;
-    const int gr = n0 + q * 16 + lrow;
+  for (int i = 0; i < LPW; ++i) {
+    const int gr = n0 + (wave + 4 * i) * 16 + lrow;
     voff[i] = gr < d ? (uint32_t)((size_t)gr * row_bytes) + cl * 16 : OOB;
   }
-  auto issue_b = [&](int kt) {
-    char *st = smem + (kt & 1) * STAGE + BM * RB;
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (nm_lds_t *)(st + (wave + 4 * i) * 1024), 16, voff[i],
-                                               kt * 64, 0, 0);
+  auto issue_b = [&](int kt, int i) {
+    char *st = smem + (kt % NS) * STAGE + BM * RB;
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + (wave + 4 * i) * 1024), 16, voff[i], kt * 64,
+                                             0, 0);
   };
-  // A operand: thread -> (row, group-in-step) pairs
-  uint4 pv[GPT][(N * 2 + 15) / 16];
-  uint32_t pi[GPT][(N + 3) / 4];
-  auto load_a = [&](int kt) {
+  // A: this thread's row (rows past T read row T - 1 and are built as zeros)
+  const bool trow = m0 + tid < T;
+  const size_t prow = (size_t)min(m0 + tid, T - 1) * E;
+  const uint4 *pv = (const uint4 *)(vals + prow);
+  const uint4 *pi = (const uint4 *)(idx + prow);
+  auto load_a = [&](int kt, NmPack &p) {
+    p.v0 = pv[2 * kt];
+    p.v1 = pv[2 * kt + 1];
+    p.ix = pi[kt];
+  };
+  // The stores are inline assembly: the compiler cannot tell them apart from the B ring's
+  // pending LDS DMA and would wait for all of it (vmcnt(0)) before each build. They write
+  // the A half of stage kt, which no DMA targets; the LDS wait before every barrier covers
+  // them.
+  const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t *)smem;
+  const int swz = (tid >> 2) & 3;
+  auto a_row = [&](int kt) { return lds0 + (uint32_t)((kt % NS) * STAGE + tid * RB); };
+  auto build_zero = [&](uint32_t row) {
+    const u32x4_t z = {0u, 0u, 0u, 0u};
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %1 offset:16\n\t"
+                 "ds_write_b128 %0, %1 offset:32\n\tds_write_b128 %0, %1 offset:48" ::"v"(row), "v"(z));
+  };
+  auto build_entry = [&](uint32_t row, const NmPack &p, int e) {
+    const uint32_t iw = e < 4 ? p.ix.x : e < 8 ? p.ix.y : e < 12 ? p.ix.z : p.ix.w;
+    const uint32_t vw = e < 8 ? (e < 2 ? p.v0.x : e < 4 ? p.v0.y : e < 6 ? p.v0.z : p.v0.w)
+                              : (e < 10 ? p.v1.x : e < 12 ? p.v1.y : e < 14 ? p.v1.z : p.v1.w);
+    const int col = (e / N) * M + (int)((iw >> (8 * (e % 4))) & (M - 1));
+    const uint32_t v = trow ? (vw >> (16 * (e & 1))) & 0xFFFFu : 0u;
+    const uint32_t a = row + (uint32_t)((((col >> 3) ^ swz) << 4) + (col & 7) * 2);
+    asm volatile("ds_write_b16 %0, %1" ::"v"(a), "v"(v));
+  };
+  auto build_a = [&](int kt, const NmPack &p) {
+    const uint32_t row = a_row(kt);
+    build_zero(row);
 #pragma unroll
-    for (int u = 0; u < GPT; ++u) {
-      const int q = tid + 256 * u;
-      const int r = q / GPR, gi = q % GPR;
-      const int t = m0 + r;
-      const int gg = kt * GPR + gi;
-      if (t < T) {
-        const size_t base = ((size_t)t * G + gg) * N;
-#pragma unroll
-        for (int v = 0; v < (N * 2 + 15) / 16; ++v) pv[u][v] = ((const uint4 *)(vals + base))[v];
-#pragma unroll
-        for (int v = 0; v < (N + 3) / 4; ++v) pi[u][v] = ((const uint32_t *)(idx + base))[v];
-      } else {
-#pragma unroll
-        for (int v = 0; v < (N * 2 + 15) / 16; ++v) pv[u][v] = make_uint4(0, 0, 0, 0);
-#pragma unroll
-        for (int v = 0; v < (N + 3) / 4; ++v) pi[u][v] = 0;
-      }
+    for (int e = 0; e < 16; ++e) build_entry(row, p, e);
+  };
+  // fragments (as in the up GEMM's 16 x 16 x 32 loop)
+  typedef u32x4_t FA[FM];
+  typedef u32x4_t FB[FN];
+  const int l16 = lane & 15, c4 = lane >> 4;
+  auto read1 = [&](int kt, int j, FA &a, FB &b) {
+    const char *sa = smem + (kt % NS) * STAGE;
+    if (j < FM) {
+      const int r = wm * WM + j * 16 + l16;
+      a[j] = *(const u32x4_t *)(sa + r * RB + ((c4 ^ ((r >> 2) & 3)) << 4));
+    } else {
+      const int r = wn * WN + (j - FM) * 16 + l16;
+      b[j - FM] = *(const u32x4_t *)(sa + BM * RB + r * RB + ((c4 ^ ((r >> 2) & 3)) << 4));
     }
   };
-  auto store_a = [&](int kt) {
-    char *sa = smem + (kt & 1) * STAGE;
+  f32x4_t acc[FM][FN];
 #pragma unroll
-    for (int u = 0; u < GPT; ++u) {
-      const int q = tid + 256 * u;
-      const int r = q / GPR, gi = q % GPR;
-      // zero the group's M columns (M / 8 chunks of 16 bytes)
+  for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int c = 0; c < M / 8; ++c) {
-        const int lc = gi * (M / 8) + c;
-        *(uint4 *)(sa + r * RB + ((lc ^ ((r >> 2) & 3)) << 4)) = make_uint4(0, 0, 0, 0);
-      }
-#pragma unroll
-      for (int e = 0; e < N; ++e) {
-        const uint32_t w = ((const uint32_t *)pv[u])[e / 2];
-        const uint16_t v = (uint16_t)((w >> (16 * (e & 1))) & 0xFFFFu);
-        const int k = gi * M + ((pi[u][e / 4] >> (8 * (e & 3))) & 0xFF);
-        const int lc = k >> 3;
-        *(uint16_t *)(sa + r * RB + ((lc ^ ((r >> 2) & 3)) << 4) + (k & 7) * 2) = v;
-      }
-    }
+    for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{};
+  auto mma = [&](int i, const FA &a, const FB &b) {
+    acc[i / FN][i % FN] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i / FN]),
+                                                                  __builtin_bit_cast(bf16x8_t, b[i % FN]),
+                                                                  acc[i / FN][i % FN], 0, 0, 0);
   };
-  f32x16_t acc[4][4];
+  // prologue: stages 0 .. 2 built and loaded, the packed A of stage 3 in registers
+  NmPack pa0, pa1;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = f32x16_t{};
-  const int lr = lane & 31, lh = lane >> 5;
-  load_a(0);
-  issue_b(0);
-  for (int kt = 0; kt < nk; ++kt) {
-    // stage kt & 1 was last read by compute(kt - 2), finished before the previous barrier
-    store_a(kt);
-    __builtin_amdgcn_s_waitcnt((0) | (7 << 4) | (15 << 8));      // B of step kt landed
-    asm volatile("" ::: "memory");
-    __syncthreads();
-    if (kt + 1 < nk) {
-      issue_b(kt + 1);                             // its stage was last read by compute(kt - 1)
-      load_a(kt + 1);
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk) {
+      load_a(st, pa0);
+      build_a(st, pa0);
     }
-    const char *sa = smem + (kt & 1) * STAGE;
-    const char *sb = sa + BM * RB;
+  if (NS - 1 < nk) load_a(NS - 1, pa1);
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int c = 2 * u + lh;
-      u32x4n_t a[4], b[4];
+  for (int st = 0; st < NS - 1; ++st)
+    if (st < nk)
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb) {
-        const int r = wm * 128 + mb * 32 + lr;
-        a[mb] = *(const u32x4n_t *)(sa + r * RB + ((c ^ ((r >> 2) & 3)) << 4));
-      }
+      for (int i = 0; i < LPW; ++i) issue_b(st, i);
+  wait_vmcnt<0>();
+  block_barrier_lds();
+  FA a0, a1;
+  FB b0, b1;
 #pragma unroll
-      for (int nb = 0; nb < 4; ++nb) {
-        const int r = wn * 128 + nb * 32 + lr;
-        b[nb] = *(const u32x4n_t *)(sb + r * RB + ((c ^ ((r >> 2) & 3)) << 4));
-      }
+  for (int j = 0; j < NR; ++j) read1(0, j, a0, b0);
+
+  // A step of the steady state (kt + 4 < nk): packed loads of stage kt + 4 into pl, build of
+  // stage kt + 3 from pb. Issue order per step: packed loads, then B loads, so that at the
+  // start of step kt the loads issued after stage kt + 1's B are step kt - 1's (LA + LPW),
+  // and at the build those issued after stage kt + 3's packed loads are 2 LPW + LA.
+  constexpr int RI = NM / NR;                    // a fragment read after every RI MFMAs
+  constexpr int DI = NM / LPW;                   // a B load after every DI MFMAs
+  // A step of the steady state (kt + 4 < nk). Issue order: the packed loads of stage kt + 4,
+  // then (between the MFMAs of stage kt, with the fragment reads of stage kt + 1) the B loads
+  // of stage kt + 3; after the MFMAs the A of stage kt + 3 is built from the registers
+  // loaded in step kt - 1. So at the start of step kt the loads issued after stage kt + 1's B
+  // are step kt - 1's (LA + LPW), and at the build those issued after stage kt + 3's packed
+  // loads are 2 LPW + LA. (Interleaving the build with the MFMAs measured slower: with one
+  // wave per SIMD its VALU work delays the MFMA issue.)
+  auto step = [&](int kt, const FA &ac, const FB &bc, FA &an, FB &bn, NmPack &pl, const NmPack &pb) {
+    wait_vmcnt<LA + LPW>();
+    block_barrier_lds();
+    load_a(kt + 4, pl);
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      mma(i, ac, bc);
+      if constexpr (i % RI == 0 && i / RI < NR) read1(kt + 1, i / RI, an, bn);
+      if constexpr (i % DI == DI - 1) issue_b(kt + 3, i / DI);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    wait_vmcnt<2 * LPW + LA>();
+    build_a(kt + 3, pb);
+    __builtin_amdgcn_sched_barrier(0);
+  };
+  // The last steps (kt + 4 >= nk): what exists is issued, waits are complete ones, and the
+  // next fragment set and packed registers are copied into the current ones afterwards.
+  auto tail_step = [&](int kt) {
+    wait_vmcnt<0>();
+    block_barrier_lds();
+    if (kt + 4 < nk) load_a(kt + 4, pa0);
+    static_for<NM>([&](auto I) {
+      constexpr int i = decltype(I)::value;
+      mma(i, a0, b0);
+      if constexpr (i % RI == 0 && i / RI < NR) read1(kt + 1, i / RI, a1, b1);
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (kt + 3 < nk) {
 #pragma unroll
-      for (int mb = 0; mb < 4; ++mb)
-#pragma unroll
-        for (int nb = 0; nb < 4; ++nb)
-          acc[mb][nb] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, a[mb]),
-                                                                __builtin_bit_cast(bf16x8_t, b[nb]), acc[mb][nb], 0, 0, 0);
+      for (int i = 0; i < LPW; ++i) issue_b(kt + 3, i);
+      build_a(kt + 3, pa1);
     }
+    wait_vmcnt<0>();
+#pragma unroll
+    for (int j = 0; j < FM; ++j) a0[j] = a1[j];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) b0[j] = b1[j];
+    pa1 = pa0;
+  };
+  int kt = 0;
+  for (; kt + 5 < nk; kt += 2) {
+    step(kt, a0, b0, a1, b1, pa0, pa1);          // loads stage kt + 4 (even parity) into pa0
+    step(kt + 1, a1, b1, a0, b0, pa1, pa0);      // builds stage kt + 4 from pa0
   }
-  // epilogue: y[row][col]
+  for (; kt + 1 < nk; ++kt) tail_step(kt);
 #pragma unroll
-  for (int nb = 0; nb < 4; ++nb) {
-    const int col = n0 + wn * 128 + nb * 32 + lr;
+  for (int i = 0; i < NM; ++i) mma(i, a0, b0);
+
+  // epilogue: y[row][col], register r of block (fm, fn): row 16 fm + 4 (lane / 16) + r,
+  // column 16 fn + lane % 16
+#pragma unroll
+  for (int fn = 0; fn < FN; ++fn) {
+    const int col = n0 + wn * WN + fn * 16 + l16;
     if (col >= d) continue;
 #pragma unroll
-    for (int mb = 0; mb < 4; ++mb)
+    for (int fm = 0; fm < FM; ++fm)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int row = m0 + wm * 128 + mb * 32 + 8 * (r >> 2) + 4 * lh + (r & 3);
+      for (int r = 0; r < 4; ++r) {
+        const int row = m0 + wm * WM + fm * 16 + 4 * c4 + r;
         if (row >= T) continue;
         const size_t o = (size_t)row * d + col;
-        if (y_bf16) ((uint16_t *)y)[o] = (uint16_t)f32_to_bf16(acc[mb][nb][r]);
-        else ((float *)y)[o] = acc[mb][nb][r];
+        if (y_bf16) ((uint16_t *)y)[o] = (uint16_t)f32_to_bf16(acc[fm][fn][r]);
+        else ((float *)y)[o] = acc[fm][fn][r];
       }
   }
 }

@@ -7,6 +7,7 @@
 namespace tw {
 
 typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(3))) char lds_char_t;
 
 // s_waitcnt with only the vector-memory counter constrained (gfx9 encoding).
 template <int N> TW_DEV void wait_vmcnt() {
