@@ -12,13 +12,15 @@ namespace tw {
 
 // row_list[t][0 .. row_nnz[t]) = (column, fp32 value bits) of the stored slots of row t in
 // ascending column order (an overflow row gets its truncated slots; consumers take such
-// rows from the dense backup instead). One wave. Lane k holds the count of tile k0 + k;
-// then each 16-lane group copies the slots of one tile per round (lane = slot), and all
-// sixteen rounds' loads are issued before any store, so a row costs two memory latencies
-// (counts, then slots) rather than one per slot.
+// rows from the dense backup instead). One wave, 64 tiles at a time: lane k holds the
+// count of tile k0 + k and its exclusive prefix off[k]; then lane e takes list entry e of
+// the chunk (e, e + 64, ...), finds its tile as the last k with off[k] <= e by a binary
+// search over the wave (ds_bpermute), and copies slot e - off[k]. A row costs a few wave
+// loads and one coalesced 8-byte store per 64 entries, instead of one wave load per tile
+// group and slot.
 template <typename VT>
 TW_DEV void row_list_wave(const TwellIn &h, int t) {
-  const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
+  const int lane = lane_id();
   const int S = h.S;
   const size_t stride = (size_t)h.n_t * S;
   uint2 *out = h.row_list + (size_t)t * stride;
@@ -29,33 +31,21 @@ TW_DEV void row_list_wave(const TwellIn &h, int t) {
     const int m = k < h.n_t ? min(h.counts[(size_t)t * h.n_t + k], S) : 0;
     int tot;
     const int off = wave_excl_scan(m, &tot);
-    for (int s0 = 0; s0 < S; s0 += 16) {
-      const int s = s0 + gl;
-      // row base of tile k0 (wave-uniform) + 32-bit lane offsets: one VGPR per load address
-      const size_t rb = ((size_t)t * h.n_t + k0) * S;
-      const char *ci_row = (const char *)(h.col_idx + rb);
-      const char *cv_row = (const char *)(vals + rb);
-      uint32_t ci[16], cv[16];
-      int dst[16];
-      // Loads are unconditional (lanes without a slot re-read slot 0 of tile k0): a load
-      // under a divergent branch makes the compiler wait for every earlier load first.
+    const size_t rb = ((size_t)t * h.n_t + k0) * S;   // slot 0 of tile k0
+    for (int e0 = 0; e0 < tot; e0 += 64) {
+      const int e = e0 + lane;
+      int lo = 0;                                     // last tile with off <= e (off[0] = 0)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int kk = 4 * r + g;                     // tile k0 + kk (count 0 past n_t)
-        const int mk = __shfl(m, kk, 64), ok = __shfl(off, kk, 64);
-        const bool on = s < mk;
-        const uint32_t e = on ? (uint32_t)(kk * S + s) : 0u;
-        ci[r] = *(const uint32_t *)(ci_row + 4u * e);
-        cv[r] = __float_as_uint(Elem<VT>::load((const VT *)(cv_row + (uint32_t)sizeof(VT) * e), 0));
-        dst[r] = on ? n + ok + s : -1;
+      for (int step = 32; step > 0; step >>= 1) {
+        const int o = __shfl(off, lo + step, 64);
+        lo = (lo + step < 64 && o <= e) ? lo + step : lo;
       }
-      // keep every load above the (branchy) stores: the compiler would otherwise sink a
-      // round's loads into its store branch, behind a wait
-#pragma unroll
-      for (int r = 0; r < 16; ++r) asm volatile("" ::"v"(ci[r]), "v"(cv[r]));
-#pragma unroll
-      for (int r = 0; r < 16; ++r)
-        if (dst[r] >= 0) out[dst[r]] = make_uint2(ci[r], cv[r]);
+      const int base = __shfl(off, lo, 64);
+      const bool on = e < tot;
+      const size_t si = rb + (on ? (size_t)lo * S + (e - base) : 0);
+      const uint32_t ci = (uint32_t)h.col_idx[si];
+      const uint32_t cv = __float_as_uint(Elem<VT>::load(vals, si));
+      if (on) out[n + e] = make_uint2(ci, cv);
     }
     n += tot;
   }
