@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--ovf-cap", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
-    ap.add_argument("--legs", default="c3,c4,c5",
+    ap.add_argument("--legs", default="pack,c3,c4,c5",
                     help="extra workloads measured after the headline (comma list, or 'none')")
     return ap.parse_args()
 
@@ -223,6 +223,47 @@ def leg_c4(steps, warmup):
     return out
 
 
+def leg_pack(steps, warmup):
+    """Standalone TwELL pack of a dense ReLU output at c2 (HBM-bound), and the unfused forward
+    (dense ReLU GEMM to HBM, pack, gather) beside the fused one: what the GEMM epilogue saves."""
+    import torch
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+    w = synth.C2
+    dev = torch.device("cuda:0")
+    g = synth.generate(w)
+    x, w1t, w2 = _up(g["x"], "bf16", dev), _up(g["w1t"], "bf16", dev), _up(g["w2"], "bf16", dev)
+    b1 = _up(g["b1"], "f32", dev)
+    T, f, d = w.T, w.f, w.d
+    n_t = f // w.tile_w
+    cap = 64
+    out = {}
+    for name, dt in (("fp32", torch.float32), ("bf16", torch.bfloat16)):
+        h = tw.ffn_up_relu_dense(x, w1t, b1, dt)
+        m = tw.twell_pack(h, w.tile_w, w.slots, cap)
+        ms = _time(lambda: tw.twell_pack(h, w.tile_w, w.slots, cap, out=m), steps, warmup)
+        eb = h.element_size()
+        nbytes = T * f * eb + T * n_t * 4 + T * n_t * w.slots * (4 + eb)
+        out[f"pack_{name}"] = {"ms": ms, "algorithmic_bytes": nbytes,
+                               "GB_per_s": nbytes / (ms * 1e-3) / 1e9,
+                               "frac_hbm_peak": nbytes / (ms * 1e-3) / 1e9 / PEAK_HBM_GBS}
+        del h, m
+    hb = torch.empty((T, f), dtype=torch.bfloat16, device=dev)
+    mb = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.bfloat16, dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+
+    def unfused():
+        tw.ffn_up_relu_dense(x, w1t, b1, torch.bfloat16, out=hb)
+        tw.twell_pack(hb, w.tile_w, w.slots, cap, out=mb)
+        tw.twell_down(mb, w2, y=y)
+    mf = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.float32, dev)
+    out["unfused_fwd_ms"] = _time(unfused, steps, warmup)
+    out["fused_fwd_ms"] = _time(lambda: tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=mf, y=y),
+                                steps, warmup)
+    out["unfused"] = "ffn_up_relu_dense (bf16 h to HBM) + twell_pack + twell_down"
+    return out
+
+
 def leg_c5(steps, warmup):
     """Training step (forward + backward with the L1 term) vs the dense bf16 FFN's
     forward + backward through autograd (the same six GEMMs a dense layer needs)."""
@@ -389,7 +430,7 @@ def main():
         torch.cuda.empty_cache()
         out["legs"] = {}
         for leg in legs:
-            fn = {"c3": leg_c3, "c4": leg_c4, "c5": leg_c5}.get(leg)
+            fn = {"c3": leg_c3, "c4": leg_c4, "c5": leg_c5, "pack": leg_pack}.get(leg)
             if fn is None:
                 continue
             try:
