@@ -86,6 +86,43 @@ def gather_rows(h: np.ndarray, w2: np.ndarray) -> np.ndarray:
     return y
 
 
+# ------------------------------------------------------------------- gated feed-forward
+
+def gated_ffn_fwd(x: np.ndarray, wgt: np.ndarray, bg: np.ndarray, wut: np.ndarray, w2: np.ndarray):
+    """y = (ReLU(x . Wg + bg) * (x . Wu)) . W2, elementwise product of gate and up.
+
+    [SFL] "Formato de Dados TwELL": the sparse format is produced by the dense product that
+    computes the gate activations; "Kernels de Inferência": one kernel fuses the up and the
+    down projections, iterating over the active units only (a dot product for the up
+    projection, then the multiply-add with the unit's down row).
+    Readings taken where the pages are silent: the gate is ReLU of its pre-activation with
+    a bias (the bias is what makes the synthetic layers sparse); the up projection has no
+    bias and no activation; a unit contributes gate * up; wgt / wut row j hold unit j's
+    input weights (like w1t) and w2 row j its output weights. Returns (zg, g, u, h, y).
+    """
+    zg = preact(x, wgt, bg)
+    g = relu(zg)
+    u = x @ wut.T
+    h = g * u
+    return zg, g, u, h, h @ w2
+
+
+def gated_gather(g: np.ndarray, x: np.ndarray, wut: np.ndarray, w2: np.ndarray) -> np.ndarray:
+    """The same y in the fused kernel's order: per token, for each active gate unit j in
+    ascending order, u = x[t] . wut[j] and y[t] += (g[t, j] * u) * w2[j] (fp64).
+
+    [SFL] "Kernels de Inferência". A unit with g = 0 adds nothing, so this equals
+    ``gated_ffn_fwd`` up to the order of the fp64 sums.
+    """
+    T = g.shape[0]
+    y = np.zeros((T, w2.shape[1]))
+    for t in range(T):
+        for j in np.flatnonzero(g[t]):
+            u = float(x[t] @ wut[j])
+            y[t] += (g[t, j] * u) * w2[j]
+    return y
+
+
 # ------------------------------------------------------------------------ TwELL format
 
 def twell_pack(h: np.ndarray, tile_w: int, slots: int, ovf_cap: int) -> dict:
