@@ -57,6 +57,9 @@ struct BwdArgs {
 size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf16);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 
+// gated.hip
+hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int bf16, int d, hipStream_t s);
+
 // nm.hip
 hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, void *vals, uint8_t *idx,
                            hipStream_t s);

@@ -171,6 +171,33 @@ int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t
                void *y, int32_t y_dtype, void *stream);
 
 /*
+ * Gated feed-forward ("Sparser, Faster, Lighter Transformer Language Models", section
+ * "2. Metodologia", blocks "Formato de Dados TwELL" and "Kernels de Inferência"): the TwELL
+ * holds the gate activations g = ReLU(x . Wg + bg), and only the active units take the up
+ * projection u = x . Wu (no bias) before the down product:
+ *   y = (g * u) . W2     (elementwise gate * up; rows of w_up_t as in w1t).
+ *
+ * twell_gate_up — the up stage: for every entry (j, g) of every row list in h, and every
+ * nonzero of every stored dense backup row, g <- g * (x[t] . w_up_t[j]) (fp32 sum; bf16
+ * products by v_dot2_f32_bf16). Call after twell_up_finish on the same h and stream (the
+ * gate GEMM built the lists); then twell_fwd_down yields y. The TwELL slots (counts,
+ * col_idx, vals) keep the gate; row_list values and ovf_dense rows hold g * u afterwards.
+ * x [T][d_model] and w_up_t [d_ff][d_model] in in_dtype, 16-byte aligned; d_model a
+ * multiple of 8. Errors as twell_ffn_fwd.
+ */
+int twell_gate_up(twell_matrix_t *h, const void *x, const void *w_up_t, int32_t in_dtype,
+                  int32_t T, int32_t d_model, int32_t d_ff, void *stream);
+
+/*
+ * twell_gated_ffn_fwd — the whole gated forward: twell_up_gemm and twell_up_finish on the
+ * gate weights (w_gate_t, b_gate), twell_gate_up with w_up_t, then twell_fwd_down with w2,
+ * in that order on the stream. Arguments, checks and errors as twell_ffn_fwd plus w_up_t.
+ */
+int twell_gated_ffn_fwd(const void *x, const void *w_gate_t, const float *b_gate, const void *w_up_t,
+                        const void *w2, int32_t in_dtype, int32_t T, int32_t d_model, int32_t d_ff,
+                        twell_matrix_t *h, void *y, int32_t y_dtype, void *stream);
+
+/*
  * ffn_up_relu_dense — h = ReLU(x . W1 + b1) written densely ([T][d_ff], h_dtype = fp32 or
  * bf16). Same MFMA kernel and accumulation order as the fused TwELL path, so the fp32
  * output is bit-identical to the values the TwELL epilogue sees.

@@ -137,6 +137,14 @@ def generate(w: Workload, T: int | None = None) -> dict:
             "dtype": w.dtype, "workload": w}
 
 
+def up_weights(w: Workload) -> np.ndarray:
+    """The up-projection weights of the gated variant of workload ``w``: [f][d] with the same
+    scaling as w1t (N(0, 1/d)), from a generator of their own (seed + 1000), so the plain
+    workload's draws are unchanged."""
+    rng = np.random.default_rng(w.seed + 1000)
+    return _normal(rng, (w.f, w.d), 1.0 / math.sqrt(w.d), w.dtype)
+
+
 def integer_grid(T: int, d: int, f: int, seed: int, dtype: str = BF16,
                  active: float = 0.05) -> dict:
     """Inputs on a coarse binary grid: every product and every partial sum is exactly

@@ -27,7 +27,8 @@ def test_header_declares_expected_entry_points():
     for n in ["twell_pack", "twell_ffn_fwd", "twell_ffn_bwd", "nm_prune", "twell_abi_version",
               "twell_status_str", "twell_sync_status", "nm_ffn_down", "ffn_up_relu_dense",
               "twell_down", "twell_ffn_bwd_workspace_bytes", "twell_ovf_bits_words",
-              "twell_row_list_bytes", "twell_up_gemm", "twell_up_finish", "twell_fwd_down"]:
+              "twell_row_list_bytes", "twell_up_gemm", "twell_up_finish", "twell_fwd_down",
+              "twell_gate_up", "twell_gated_ffn_fwd"]:
         assert n in names, n
 
 
