@@ -22,7 +22,6 @@ namespace tw {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGateEnt = 4;      // list entries per wave and round
-constexpr int kGatePieces = 8;   // 16-byte pieces per lane held at once (bf16: 4096 columns)
 
 template <typename XT> TW_DEV float dot16(uint4 a, uint4 b, float acc) {
   if constexpr (sizeof(XT) == 2) {
@@ -40,7 +39,9 @@ template <typename XT> TW_DEV float dot16(uint4 a, uint4 b, float acc) {
 }
 
 // u[k] = x_row . wu[col[k]] for k < ENT (col[k] < 0: no entry, u = 0), summed over the wave.
-template <typename XT>
+// NP 16-byte pieces per lane are in flight at once (NP = 4 covers 2048 bf16 columns; fewer
+// registers than needed for larger rows would cost occupancy for nothing at small d).
+template <typename XT, int NP>
 TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, int d, const int (&col)[kGateEnt],
                       float (&u)[kGateEnt]) {
   constexpr int EPL = 16 / sizeof(XT);
@@ -48,10 +49,10 @@ TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, in
   const int npc = (d + 64 * EPL - 1) / (64 * EPL);
 #pragma unroll
   for (int k = 0; k < kGateEnt; ++k) u[k] = 0.f;
-  for (int c0 = 0; c0 < npc; c0 += kGatePieces) {
-    uint4 xv[kGatePieces], wv[kGateEnt][kGatePieces];
+  for (int c0 = 0; c0 < npc; c0 += NP) {
+    uint4 xv[NP], wv[kGateEnt][NP];
 #pragma unroll
-    for (int q = 0; q < kGatePieces; ++q) {
+    for (int q = 0; q < NP; ++q) {
       const int i = ((c0 + q) * 64 + lane) * EPL;
       const bool ok = i < d;                                    // d is a multiple of EPL
       xv[q] = ok ? *(const uint4 *)(xrow + i) : make_uint4(0, 0, 0, 0);
@@ -60,7 +61,7 @@ TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, in
         wv[k][q] = (ok && col[k] >= 0) ? *(const uint4 *)(wu + (size_t)col[k] * d + i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
-    for (int q = 0; q < kGatePieces; ++q)
+    for (int q = 0; q < NP; ++q)
 #pragma unroll
       for (int k = 0; k < kGateEnt; ++k) u[k] = dot16<XT>(xv[q], wv[k][q], u[k]);
   }
@@ -71,7 +72,7 @@ TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, in
 // Row lists: workgroup (t, p) of 4 waves; wave w takes the entry groups p * 4 + w,
 // p * 4 + w + 4 P, ... of ENT entries each. Overflow rows are skipped (their backup row
 // carries them).
-template <typename XT>
+template <typename XT, int NP>
 __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restrict__ x, const XT *__restrict__ wu,
                                                   int d, int P) {
   const int t = blockIdx.x / P, p = blockIdx.x % P;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
 #pragma unroll
     for (int k = 0; k < kGateEnt; ++k) col[k] = e0 + k < nnz ? (int)lst[e0 + k].x : -1;
     float u[kGateEnt];
-    wave_dots<XT>(xrow, wu, d, col, u);
+    wave_dots<XT, NP>(xrow, wu, d, col, u);
     if (lane == 0)
 #pragma unroll
       for (int k = 0; k < kGateEnt; ++k)
@@ -116,7 +117,7 @@ __global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__
       m &= m ? m - 1 : 0;
     }
     float u[kGateEnt];
-    wave_dots<XT>(x + (size_t)t * d, wu, d, col, u);
+    wave_dots<XT, 8>(x + (size_t)t * d, wu, d, col, u);
 #pragma unroll
     for (int k = 0; k < kGateEnt; ++k) {
       const float gk = __shfl(g, col[k] & 63, 64);
@@ -136,14 +137,16 @@ hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int b
   const dim3 gridb((unsigned)((nb + 3) / 4));
   if (bf16) {
     const uint16_t *xx = (const uint16_t *)x, *ww = (const uint16_t *)wu;
-    hipLaunchKernelGGL((k_gate_dot<uint16_t>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    if (d <= 2048) hipLaunchKernelGGL((k_gate_dot<uint16_t, 4>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    else hipLaunchKernelGGL((k_gate_dot<uint16_t, 8>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     if (nb) {
       if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
       else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d);
     }
   } else {
     const float *xx = (const float *)x, *ww = (const float *)wu;
-    hipLaunchKernelGGL((k_gate_dot<float>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    if (d <= 1024) hipLaunchKernelGGL((k_gate_dot<float, 4>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    else hipLaunchKernelGGL((k_gate_dot<float, 8>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     if (nb) {
       if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
       else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d);

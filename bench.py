@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--ovf-cap", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
-    ap.add_argument("--legs", default="pack,c3,c4,c5",
+    ap.add_argument("--legs", default="pack,c3,c4,c5,gated",
                     help="extra workloads measured after the headline (comma list, or 'none')")
     return ap.parse_args()
 
@@ -264,6 +264,54 @@ def leg_pack(steps, warmup):
     return out
 
 
+def leg_gated(steps, warmup):
+    """The gated layer y = (ReLU(x Wg + bg) * (x Wu)) W2 at c2 and at c3's decode sizes: the
+    TwELL path (gate GEMM + TwELL, up dot products over the active units, down gather)
+    against the dense bf16 layer (three GEMMs). The up stage's own time is the difference
+    from the plain forward on the same gate; at decode its algorithmic bytes are the unique
+    up rows read."""
+    import torch
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+    dev = torch.device("cuda:0")
+    out = {}
+    for w, Ts in ((synth.C2, (synth.C2.T,)), (synth.C3, (1, 8, 64))):
+        g = synth.generate(w)
+        x_all = _up(g["x"], "bf16", dev)
+        wgt, w2 = _up(g["w1t"], "bf16", dev), _up(g["w2"], "bf16", dev)
+        wut = _up(synth.up_weights(w), "bf16", dev)
+        bg = _up(g["b1"], "f32", dev)
+        bgb = bg.to(torch.bfloat16)
+        for T in Ts:
+            x = x_all[:T].contiguous()
+            h = tw.TwellMatrix(T, w.f, w.tile_w, w.slots, 16, torch.float32, dev)
+            y = torch.empty((T, w.d), dtype=torch.float32, device=dev)
+            ms = _time(lambda: tw.twell_gated_ffn_fwd(x, wgt, bg, wut, w2, w.tile_w, w.slots, 16, h=h, y=y),
+                       steps, warmup)
+            ms_plain = _time(lambda: tw.twell_ffn_fwd(x, wgt, bg, w2, w.tile_w, w.slots, 16, h=h, y=y),
+                             steps, warmup)
+
+            def dense():
+                return (torch.relu(torch.addmm(bgb, x, wgt.t())) * (x @ wut.t())) @ w2
+            dms = _time(dense, steps, warmup)
+            rec = {"ms": ms, "dense_ms": dms, "speedup_vs_dense": dms / ms,
+                   "up_stage_ms": ms - ms_plain}
+            if w is synth.C3:
+                cols = h.col_idx.clamp(min=0).view(-1)
+                act = torch.zeros(w.f, dtype=torch.bool, device=dev)
+                act[cols[(h.col_idx.view(-1) >= 0)]] = True
+                uniq = int(act.sum().item())
+                nbytes = uniq * w.d * 2
+                rec["up_stage_unique_rows"] = uniq
+                if rec["up_stage_ms"] > 0:
+                    rec["up_stage_frac_hbm_peak"] = nbytes / (rec["up_stage_ms"] * 1e-3) / 1e9 / PEAK_HBM_GBS
+            out[f"{'c2' if w is synth.C2 else 'c3'}_T{T}"] = rec
+            del h, y
+        del x_all, wgt, w2, wut
+        torch.cuda.empty_cache()
+    return out
+
+
 def leg_c5(steps, warmup):
     """Training step (forward + backward with the L1 term) vs the dense bf16 FFN's
     forward + backward through autograd (the same six GEMMs a dense layer needs)."""
@@ -430,7 +478,7 @@ def main():
         torch.cuda.empty_cache()
         out["legs"] = {}
         for leg in legs:
-            fn = {"c3": leg_c3, "c4": leg_c4, "c5": leg_c5, "pack": leg_pack}.get(leg)
+            fn = {"c3": leg_c3, "c4": leg_c4, "c5": leg_c5, "pack": leg_pack, "gated": leg_gated}.get(leg)
             if fn is None:
                 continue
             try:
