@@ -39,7 +39,7 @@ def parse():
     ap.add_argument("--ovf-cap", type=int, default=64)
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device copy (reference for the HBM byte counters)")
-    ap.add_argument("--legs", default="pack,c3,c4,c5,gated",
+    ap.add_argument("--legs", default="pack,c3,c4,c5,gated,decode_graph",
                     help="extra workloads measured after the headline (comma list, or 'none')")
     return ap.parse_args()
 
@@ -312,6 +312,63 @@ def leg_gated(steps, warmup):
     return out
 
 
+def leg_decode_graph(steps, warmup):
+    """A decode loop over 4 layers of c3's shape (per-layer densities 0.5 / 1 / 2 / 3 %),
+    eager and captured in a HIP graph, beside the dense bf16 layers run the same way; T = 1
+    and 8 tokens. Between layers each token is normalised to unit RMS (torch, fp32 -> bf16),
+    the stand-in for the rest of a transformer block, the same for both paths."""
+    import torch
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+    dev = torch.device("cuda:0")
+    w = synth.C3
+    out = {}
+    x_bits, layers = synth.decode_layers(4, 8)
+    L = [(_up(a["w1t"], "bf16", dev), _up(a["b1"], "f32", dev), _up(a["w2"], "bf16", dev)) for a in layers]
+    x_all = _up(x_bits, "bf16", dev)
+    for T in (1, 8):
+        x0 = x_all[:T].contiguous()
+        hs = [tw.TwellMatrix(T, w.f, w.tile_w, w.slots, 4, torch.float32, dev) for _ in L]
+        ys = [torch.empty((T, w.d), dtype=torch.bfloat16, device=dev) for _ in L]
+        xs = [torch.empty((T, w.d), dtype=torch.bfloat16, device=dev) for _ in L]
+
+        def norm(y, out):
+            yf = y.float()
+            out.copy_(yf * torch.rsqrt(yf.square().mean(dim=1, keepdim=True)))
+            return out
+
+        def run():
+            x = x0
+            for l, ((w1t, b1, w2), h, y) in enumerate(zip(L, hs, ys)):
+                tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, 4, h=h, y=y, y_dtype=torch.bfloat16)
+                x = norm(y, xs[l])
+
+        def dense():
+            x = x0
+            for l, (w1t, b1, w2) in enumerate(L):
+                x = norm(torch.relu(torch.addmm(b1.to(torch.bfloat16), x, w1t.t())) @ w2, xs[l])
+            return x
+        eager_ms = _time(run, steps, warmup)
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            run()
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run()
+        graph_ms = _time(graph.replay, steps, warmup)
+        dense_ms = _time(dense, steps, warmup)
+        dens = [float((hh.counts.clamp(max=w.slots).sum() / (T * w.f)).item()) for hh in hs]
+        out[f"T{T}"] = {"layers": len(L), "layer_density": dens, "eager_ms": eager_ms, "graph_ms": graph_ms,
+                        "graph_speedup": eager_ms / graph_ms, "dense_eager_ms": dense_ms,
+                        "speedup_vs_dense": dense_ms / graph_ms,
+                        "tokens_per_s": T / (graph_ms * 1e-3)}
+        del hs, ys, graph
+    return out
+
+
 def leg_c5(steps, warmup):
     """Training step (forward + backward with the L1 term) vs the dense bf16 FFN's
     forward + backward through autograd (the same six GEMMs a dense layer needs)."""
@@ -478,7 +535,8 @@ def main():
         torch.cuda.empty_cache()
         out["legs"] = {}
         for leg in legs:
-            fn = {"c3": leg_c3, "c4": leg_c4, "c5": leg_c5, "pack": leg_pack, "gated": leg_gated}.get(leg)
+            fn = {"c3": leg_c3, "c4": leg_c4, "c5": leg_c5, "pack": leg_pack, "gated": leg_gated,
+                  "decode_graph": leg_decode_graph}.get(leg)
             if fn is None:
                 continue
             try:

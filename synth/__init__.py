@@ -145,6 +145,25 @@ def up_weights(w: Workload) -> np.ndarray:
     return _normal(rng, (w.f, w.d), 1.0 / math.sqrt(w.d), w.dtype)
 
 
+def decode_layers(n: int, T: int, densities=(0.005, 0.01, 0.02, 0.03)):
+    """``n`` decode-size layers of c3's shape (d=4096, f=14336, bf16) for a multi-layer
+    decode loop: layer l draws its weights from seed 2 + 100 (l + 1) (c3's scalings) and has
+    the constant bias Phi^-1(p_l) for p_l = densities[l % len(densities)] (per-layer density
+    skew). Layers expect unit-RMS inputs; a decode loop normalises each token's output
+    before the next layer, as a transformer does between its blocks.
+    Returns (x of the first layer [T, d], [per-layer dicts with w1t, b1, w2, p])."""
+    layers = []
+    x = None
+    for l in range(n):
+        p = densities[l % len(densities)]
+        w = C3.with_(seed=2 + 100 * (l + 1), bias=float(ndtri(np.array([p]))[0]))
+        g = generate(w, T=T)
+        if x is None:
+            x = g["x"]
+        layers.append({"w1t": g["w1t"], "b1": g["b1"], "w2": g["w2"], "p": p})
+    return x, layers
+
+
 def integer_grid(T: int, d: int, f: int, seed: int, dtype: str = BF16,
                  active: float = 0.05) -> dict:
     """Inputs on a coarse binary grid: every product and every partial sum is exactly
