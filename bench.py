@@ -394,6 +394,27 @@ def leg_c5(steps, warmup):
     ms_fwd = _time(lambda: tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y), steps, warmup)
     ovf = int(h.ovf_n.item())
     dens = float(h.counts.sum().item()) / (T * f)
+    # Activation memory kept for the backward ("Formato Híbrido para Treinamento"): counts,
+    # slots (int32 index + fp32 value) and the fp32 backup rows of the overflow rows, against
+    # a dense h. For a per-step choice of the slot count (the dynamic N_nz of the hybrid) the
+    # same bytes are evaluated on this step's true counts for other S; the smallest stash
+    # whose overflow rows fit the backup capacity is reported.
+    n_t = f // w.tile_w
+    rowmax = h.counts.max(dim=1).values
+    dense_bf16 = T * f * 2
+
+    def stash(S):
+        n_ovf = int((rowmax > S).sum().item())
+        return n_ovf, T * n_t * 4 + T * n_t * S * 8 + n_ovf * f * 4 + T * 4
+    per_s = {}
+    for S in (4, 6, 8, 12, 16, 24, 32):
+        n_ovf, b = stash(S)
+        per_s[str(S)] = {"overflow_rows": n_ovf, "bytes": b, "frac_of_dense_bf16": b / dense_bf16}
+    fit = [int(k) for k, v in per_s.items() if v["overflow_rows"] <= cap]
+    best = min(fit, key=lambda k: per_s[str(k)]["bytes"]) if fit else None
+    mem = {"dense_h_bf16_bytes": dense_bf16, "dense_h_fp32_bytes": 2 * dense_bf16,
+           "stash_bytes": stash(w.slots)[1], "stash_frac_of_dense_bf16": stash(w.slots)[1] / dense_bf16,
+           "per_slots": per_s, "best_slots_within_cap": best, "cap": cap}
     del ws
     torch.cuda.empty_cache()
     xd = x.clone().requires_grad_(True)
@@ -411,7 +432,7 @@ def leg_c5(steps, warmup):
     ms_dense = _time(dense_step, steps, warmup)
     return {"tokens_per_s": T / (ms * 1e-3), "ms_fwd_bwd": ms, "ms_fwd": ms_fwd, "ms_bwd": ms - ms_fwd,
             "dense_ms_fwd_bwd": ms_dense, "speedup_vs_dense": ms_dense / ms, "density": dens,
-            "overflow_rows": ovf, "slots": w.slots, "tile_w": w.tile_w}
+            "overflow_rows": ovf, "slots": w.slots, "tile_w": w.tile_w, "activation_memory": mem}
 
 
 def main():
