@@ -116,3 +116,29 @@ def test_pack_and_down_reject():
     assert L.ffn_up_relu_dense(FAKE, FAKE, None, 1, 4, 256, 512, FAKE, 0, None) == ARG
     assert L.ffn_up_relu_dense(FAKE, FAKE, FAKE, 1, 4, 250, 512, FAKE, 0, None) == ALIGN
     assert L.twell_sync_status(None, None) == ARG
+
+
+@pytestmark_nogpu
+def test_gated_entry_points_reject():
+    L = tw.lib()
+    m = mat()
+    # twell_gate_up(h, x, w_up_t, dtype, T, d, f, stream)
+    assert L.twell_gate_up(None, FAKE, FAKE, 1, 64, 256, 512, None) == ARG
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, None, 1, 64, 256, 512, None) == ARG
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 7, 64, 256, 512, None) == ARG
+    assert L.twell_gate_up(ctypes.byref(m), MIS, FAKE, 1, 64, 256, 512, None) == ALIGN
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 64, 100, 512, None) == ALIGN
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 32, 256, 512, None) == SHAPE
+    assert L.twell_gate_up(ctypes.byref(mat(row_list=None)), FAKE, FAKE, 1, 64, 256, 512, None) == ARG
+
+    def gfwd(**kw):
+        a = dict(x=FAKE, wg=FAKE, bg=FAKE, wu=FAKE, w2=FAKE, dt=1, T=64, d=256, f=512, y=FAKE, ydt=0)
+        a.update(kw)
+        return L.twell_gated_ffn_fwd(a["x"], a["wg"], a["bg"], a["wu"], a["w2"], a["dt"], a["T"], a["d"], a["f"],
+                                     ctypes.byref(m), a["y"], a["ydt"], None)
+    assert gfwd(wu=None) == ARG
+    assert gfwd(w2=None) == ARG
+    assert gfwd(bg=None) == ARG
+    assert gfwd(ydt=4) == ARG
+    assert gfwd(wu=MIS) == ALIGN
+    assert gfwd(f=1024) == SHAPE
