@@ -24,6 +24,8 @@ F32, BF16 = 0, 1
 STATUS = {0: "TWELL_OK", -1: "TWELL_ERR_ARG", -2: "TWELL_ERR_SHAPE", -3: "TWELL_ERR_ALIGN",
           -4: "TWELL_ERR_WORKSPACE", -5: "TWELL_ERR_OVF_CAPACITY", -6: "TWELL_ERR_HIP",
           -7: "TWELL_ERR_UNSUPPORTED"}
+# token count up to which the up GEMM takes its decode kernels (include/twell.h, row_list)
+DECODE_MAX_T = 64
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libtwell.so")
 
 _c = ctypes
@@ -138,7 +140,10 @@ class TwellMatrix:
         self.ovf_bits = torch.empty((max(words, 1),), **i32)
         self.row_nnz = torch.empty((max(rows, 1),), **i32)
         lb = lib().twell_row_list_bytes(rows, cols, tile_w, slots)
-        self.row_list = torch.empty((max(lb // 8, 2),), dtype=torch.int64, device=device)
+        # up to DECODE_MAX_T rows the scratch also holds the decode GEMM's tickets, which must
+        # start at zero (every call leaves them zero)
+        alloc = torch.zeros if rows <= DECODE_MAX_T else torch.empty
+        self.row_list = alloc((max(lb // 8, 2),), dtype=torch.int64, device=device)
 
     def c(self) -> TwellMatrixC:
         return TwellMatrixC(self.rows, self.cols, self.tile_w, self.slots, self.ovf_cap,

@@ -42,12 +42,23 @@ int check_matrix(const twell_matrix_t *m, bool need_ovf_bits, bool need_rows = f
   return TWELL_OK;
 }
 
+size_t list_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots) {
+  return (size_t)rows * (size_t)(cols / tile_w) * (size_t)slots * 8;
+}
+
 TwellOut out_of(const twell_matrix_t *m) {
   TwellOut o;
   o.counts = m->counts;
   o.col_idx = m->col_idx;
   o.vals = m->vals;
   o.ovf_bits = m->ovf_bits;
+  o.dec_part = nullptr;
+  o.dec_ticket = nullptr;
+  if (m->row_list && m->rows <= kDecodeMaxT) {
+    char *ws = (char *)m->row_list + align256(list_bytes(m->rows, m->cols, m->tile_w, m->slots));
+    o.dec_part = (float *)ws;
+    o.dec_ticket = (uint32_t *)(ws + dec_tiles(m->cols) * 2 * kDecHalfBytes);
+  }
   o.n_t = m->cols / m->tile_w;
   o.S = m->slots;
   o.words = (m->rows + 31) / 32;
@@ -103,7 +114,8 @@ size_t twell_ovf_bits_words(int32_t rows, int32_t cols, int32_t tile_w) {
 
 size_t twell_row_list_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots) {
   if (rows < 0 || cols <= 0 || tile_w <= 0 || slots <= 0) return 0;
-  return (size_t)rows * (size_t)(cols / tile_w) * (size_t)slots * 8;
+  const size_t lists = list_bytes(rows, cols, tile_w, slots);
+  return rows <= kDecodeMaxT ? align256(lists) + dec_ws_bytes(cols) : lists;
 }
 
 int twell_pack(const void *h, int32_t h_dtype, twell_matrix_t *out, void *stream) {
@@ -145,6 +157,7 @@ static int check_up_args(const void *x, const void *w1t, const float *b1, int32_
   st = check_matrix(h, true);
   if (st) return st;
   if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
+  if (T > 0 && T <= kDecodeMaxT && !h->row_list) return TWELL_ERR_ARG;   // decode workspace
   if (!al4(b1)) return TWELL_ERR_ALIGN;
   return TWELL_OK;
 }

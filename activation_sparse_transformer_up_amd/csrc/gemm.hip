@@ -88,13 +88,9 @@ typedef Tile<256, 256, 64, 128, epi_wave_bytes(64, 2, 4), 4, 16> TileL8;
 typedef Tile<256, 256, 128, 128, epi_wave_bytes(128, 2, 4), 4, 16> TileL;
 typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4), 4, 16> TileS;
 typedef Tile<64, 128, 32, 128, epi_wave_bytes(128, 2, 4)> TileSF;      // fp32 operands
-// Decode (at most 64 tokens): one wave owns a 64 x 128 tile over half of K with its own
-// 6-stage ring (TileD); two such waves form a workgroup and their partial tiles are added
-// (first half + second half). The weight stream then has twice the loads in flight per
-// workgroup; the K split changes the summation order, so the dense path uses the same split
-// for the same token count.
+// Decode (at most 64 tokens): one wave owns a 64 x 128 tile over a quarter of K with its
+// own 6-stage ring (TileD); the quarters are added in a fixed order (decode section below).
 typedef Tile<64, 128, 64, 128, epi_wave_bytes(128, 2, 4), 6> TileD;
-constexpr int kDecodeMaxT = 64;
 
 // A operand row r of the tile reads global row arow[m0 + r] (if arow) or m0 + r; rows at or
 // beyond a_rows are zero. B operand rows at or beyond b_rows are zero. a_total rows exist
@@ -751,51 +747,106 @@ __global__ __launch_bounds__(G::NT) void k_up_dense(const T *__restrict__ x, con
 }
 
 
-// ------------------------------------------------------------------ decode (K split)
+// ------------------------------------------------------------------ decode (K in quarters)
 
-// Two waves of TileD: wave w covers k in [w K / 2, (w + 1) K / 2) through its own ring; after
-// the loop wave 1 leaves its partial tile in LDS and wave 0 adds it (first half + second
-// half). K is a multiple of two stages (the launchers check), so both waves run the same
-// number of loop steps and barriers.
-template <typename T>
-TW_DEV void decode_mainloop(const T *__restrict__ A, const int32_t *__restrict__ arow, int a_rows, int a_total,
-                            const T *__restrict__ B, int N, int K, int n0,
-                            f32x16_t (&acc)[TileD::MB][TileD::NB], char *smem) {
-  typedef TileD G;
-  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int kh = K / 2;
-  mainloop<T, G>(A, arow, a_rows, a_total, B, N, kh, 0, n0, acc, smem + w * G::LDS_BYTES, K, w * kh, 0);
-  block_barrier();                          // both rings are done; wave 0's ring takes the partial
+// Decode (at most 64 tokens) is bound by the weight stream, and the stream rate grows with the
+// number of CUs that keep loads in flight. The sum over K is taken in four quarters,
+//   z = (q0 + q1) + (q2 + q3),   q_i over k in [i K / 4, (i + 1) K / 4),
+// each quarter by one wave through its own ring:
+//  - k_up_twell_dec spreads a 128-column tile over two workgroups of two waves (quarters
+//    0-1 and 2-3): twice the workgroups of one per tile. The halves meet in a workspace: each
+//    workgroup stores its half sum and takes a ticket; the second to arrive adds the other
+//    half and runs the TwELL epilogue.
+//  - k_up_dense_dec keeps one workgroup of four waves per tile (no workspace).
+// fp32 addition is commutative, so both add the same halves to the same bits whichever
+// workgroup arrives last, and the dense path equals the TwELL path bit for bit.
+
+// Fp32 of one wave's 64 x 128 accumulator tile, in register order: element r of block
+// (mb, nb) of lane l at ((mb * NB + nb) * 16 + r) * 64 + l.
+constexpr int kDecTileF = TileD::MB * TileD::NB * 16 * 64;
+static_assert(kDecTileF * 4 == (int)kDecHalfBytes, "workspace layout");
+
+TW_DEV void acc_to_lds(const f32x16_t (&acc)[TileD::MB][TileD::NB], float *red) {
   const int lane = threadIdx.x & 63;
-  float *red = (float *)smem;
-  if (w == 1) {
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
+  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
 #pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
+    for (int r = 0; r < 16; ++r) red[(i * 16 + r) * 64 + lane] = acc[i / TileD::NB][i % TileD::NB][r];
+}
+
+TW_DEV void acc_add_lds(f32x16_t (&acc)[TileD::MB][TileD::NB], const float *red) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) red[((mb * G::NB + nb) * 16 + r) * 64 + lane] = acc[mb][nb][r];
-  }
-  block_barrier();
-  if (w == 0) {
+  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
 #pragma unroll
-    for (int mb = 0; mb < G::MB; ++mb)
+    for (int r = 0; r < 16; ++r) acc[i / TileD::NB][i % TileD::NB][r] += red[(i * 16 + r) * 64 + lane];
+}
+
+// Rows of register group g (registers 4g .. 4g + 3) of block row mb: mb * 32 + 8 g + 0..7. A
+// group whose first row is at or beyond M holds only padding rows and is skipped as a whole
+// (a uniform branch, so the loads of the kept groups are all issued before any wait).
+TW_DEV bool dec_group_live(int mb, int g, int M) { return mb * 32 + 8 * g < M; }
+
+// Cross-workgroup hand-over of the half sums. Every access to the workspace is an atomic of
+// agent scope: such accesses are coherent across the XCDs' separate L2 caches on their own
+// (stores write through, loads do not hit a stale line). The half sum is stored, its stores
+// are waited for (vmcnt(0)) and only then is the ticket taken, so a workgroup that draws
+// ticket 1 reads a completely stored other half: its loads are issued after the ticket's
+// value has returned. An agent-scope release/acquire pair would add an L2 write-back and
+// invalidate per workgroup (several microseconds per launch) that only plain stores need.
+// The second arriver resets the ticket for the next launch; tickets start at zero.
+TW_DEV bool dec_handover(f32x16_t (&acc)[TileD::MB][TileD::NB], int M, float *mine, const float *other,
+                         uint32_t *ticket) {
+  const int lane = threadIdx.x & 63;
 #pragma unroll
-      for (int nb = 0; nb < G::NB; ++nb)
+  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) acc[mb][nb][r] += red[((mb * G::NB + nb) * 16 + r) * 64 + lane];
-  }
+    for (int g = 0; g < 4; ++g)
+      if (dec_group_live(i / TileD::NB, g, M))
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          __hip_atomic_store(mine + (i * 16 + 4 * g + q) * 64 + lane, acc[i / TileD::NB][i % TileD::NB][4 * g + q],
+                             __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmcnt<0>();
+  uint32_t t = 0;
+  if (lane == 0) t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  t = (uint32_t)__builtin_amdgcn_readfirstlane((int)t);
+  if (t == 0) return false;
+  if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  float ov[TileD::MB * TileD::NB][16];
+#pragma unroll
+  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
+#pragma unroll
+    for (int g = 0; g < 4; ++g)
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        ov[i][4 * g + q] = dec_group_live(i / TileD::NB, g, M)
+                               ? __hip_atomic_load(other + (i * 16 + 4 * g + q) * 64 + lane, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT)
+                               : 0.f;
+#pragma unroll
+  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) acc[i / TileD::NB][i % TileD::NB][r] += ov[i][r];
+  return true;
 }
 
 constexpr int kDecodeSmem = 2 * TileD::LDS_BYTES > TileD::EPI_WAVE ? 2 * TileD::LDS_BYTES : TileD::EPI_WAVE;
 static_assert(kDecodeSmem <= 160 * 1024, "LDS");
 
+// Grid: 2 * ceil(N / 128) workgroups of 128 threads; workgroup b takes tile b % n_tiles and
+// half b / n_tiles (quarters 2 half, 2 half + 1). Workspace o.dec_part [n_tiles][2][kDecTileF]
+// fp32 and o.dec_ticket [n_tiles] (zero between launches).
 template <typename T, int W, typename VT>
 __global__ __launch_bounds__(128) void k_up_twell_dec(const T *__restrict__ x, const T *__restrict__ w1t,
                                                       const float *__restrict__ b1, int M, int N, int K,
                                                       TwellOut o) {
   __shared__ __attribute__((aligned(16))) char smem[kDecodeSmem];
-  const int n0 = blockIdx.x * TileD::BN;
+  const int n_tiles = (N + TileD::BN - 1) / TileD::BN;
+  const int tile = blockIdx.x % n_tiles, half = blockIdx.x / n_tiles;
+  const int n0 = tile * TileD::BN;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kq = K / 4;
   float nbias[TileD::NB];
 #pragma unroll
   for (int nb = 0; nb < TileD::NB; ++nb) {
@@ -807,36 +858,60 @@ __global__ __launch_bounds__(128) void k_up_twell_dec(const T *__restrict__ x, c
   for (int mb = 0; mb < TileD::MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < TileD::NB; ++nb) acc[mb][nb] = f32x16_t{};
-  decode_mainloop<T>(x, nullptr, M, M, w1t, N, K, n0, acc, smem);
-  if (threadIdx.x >= 64) return;            // wave 0 holds the sum and writes the TwELL
+  mainloop<T, TileD>(x, nullptr, M, M, w1t, N, kq, 0, n0, acc, smem + w * TileD::LDS_BYTES, K, (2 * half + w) * kq, 0);
+  block_barrier_lds();                      // both rings are drained; ring 0 takes wave 1's quarter
+  float *red = (float *)smem;
+  if (w == 1) acc_to_lds(acc, red);
+  block_barrier_lds();
+  if (w == 1) return;
+  acc_add_lds(acc, red);                    // q_2h + q_2h+1
+  float *part = o.dec_part + (size_t)tile * 2 * kDecTileF;
+  if (!dec_handover(acc, M, part + half * kDecTileF, part + (1 - half) * kDecTileF, o.dec_ticket + tile))
+    return;
   epi_twell<TileD, W, VT>(acc, nbias, M, N, 0, n0, o, smem);
 }
 
+// Four waves of TileDQ (3-stage rings, 36 KB each), wave w on quarter w; then
+// (q0 + q1) + (q2 + q3) through LDS and the dense epilogue by wave 0.
+typedef Tile<64, 128, 64, 128, 0, 3> TileDQ;
+static_assert(4 * TileDQ::LDS_BYTES <= 160 * 1024 && 2 * kDecTileF * 4 <= 4 * TileDQ::LDS_BYTES, "LDS");
+
 template <typename T>
-__global__ __launch_bounds__(128) void k_up_dense_dec(const T *__restrict__ x, const T *__restrict__ w1t,
+__global__ __launch_bounds__(256) void k_up_dense_dec(const T *__restrict__ x, const T *__restrict__ w1t,
                                                       const float *__restrict__ b1, int M, int N, int K, int x_rows,
                                                       const int32_t *__restrict__ arow,
                                                       const int32_t *__restrict__ n_rows_dev, void *out,
                                                       int out_bf16, int relu) {
-  __shared__ __attribute__((aligned(16))) char smem[2 * TileD::LDS_BYTES];
-  const int n0 = blockIdx.x * TileD::BN;
+  __shared__ __attribute__((aligned(16))) char smem[4 * TileDQ::LDS_BYTES];
+  const int n0 = blockIdx.x * TileDQ::BN;
   int rows = M;
   if (n_rows_dev) rows = min(rows, *n_rows_dev);
   if (rows <= 0) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kq = K / 4;
   f32x16_t acc[TileD::MB][TileD::NB];
 #pragma unroll
   for (int mb = 0; mb < TileD::MB; ++mb)
 #pragma unroll
     for (int nb = 0; nb < TileD::NB; ++nb) acc[mb][nb] = f32x16_t{};
-  decode_mainloop<T>(x, arow, rows, x_rows, w1t, N, K, n0, acc, smem);
-  if (threadIdx.x >= 64) return;
+  mainloop<T, TileDQ>(x, arow, rows, x_rows, w1t, N, kq, 0, n0, acc, smem + w * TileDQ::LDS_BYTES, K, w * kq, 0);
+  block_barrier_lds();
+  float *red = (float *)smem;
+  if (w & 1) acc_to_lds(acc, red + (w >> 1) * kDecTileF);
+  block_barrier_lds();
+  if (!(w & 1)) acc_add_lds(acc, red + (w >> 1) * kDecTileF);   // waves 0, 2: q0 + q1, q2 + q3
+  block_barrier_lds();
+  if (w == 2) acc_to_lds(acc, red);
+  block_barrier_lds();
+  if (w != 0) return;
+  acc_add_lds(acc, red);
   epi_dense<TileD>(acc, b1, rows, N, 0, n0, out, out_bf16, relu);
 }
 
-// The decode kernels apply to at most 64 tokens and K a multiple of two stages.
+// The decode kernels apply to at most 64 tokens and K a multiple of four stages.
 template <typename T> static bool use_decode(int T_tokens, int K) {
   constexpr int KPT = TileD::RB / (int)sizeof(T);
-  return T_tokens <= kDecodeMaxT && K % (2 * KPT) == 0;
+  return T_tokens <= kDecodeMaxT && K % (4 * KPT) == 0;
 }
 
 // ------------------------------------------------------------------ host launchers
@@ -861,7 +936,7 @@ static bool use_large(int M, int N) { return M >= 512 && N >= 1024; }
 template <typename T>
 static hipError_t launch_twell_dec(const T *x, const T *w1t, const float *b1, int M, int N, int K, const TwellOut &o,
                                    int W, hipStream_t s) {
-  const dim3 grid((N + TileD::BN - 1) / TileD::BN);
+  const dim3 grid(2 * ((N + TileD::BN - 1) / TileD::BN));
   if (o.val_bf16) {
     if (W == 64) hipLaunchKernelGGL((k_up_twell_dec<T, 64, uint16_t>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, o);
     else hipLaunchKernelGGL((k_up_twell_dec<T, 128, uint16_t>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, o);
@@ -874,6 +949,8 @@ static hipError_t launch_twell_dec(const T *x, const T *w1t, const float *b1, in
 
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N,
                            int K, const TwellOut &o, int W, hipStream_t s) {
+  if ((bf16 ? use_decode<uint16_t>(M, K) : use_decode<float>(M, K)) && (!o.dec_part || !o.dec_ticket))
+    return hipErrorInvalidValue;
   if (bf16 && use_decode<uint16_t>(M, K))
     return launch_twell_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
   if (!bf16 && use_decode<float>(M, K))
@@ -902,8 +979,8 @@ template <typename T>
 static hipError_t launch_dense_dec(const T *x, const T *w1t, const float *b1, int M, int N, int K, int x_rows,
                                    const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
                                    hipStream_t s) {
-  const dim3 grid((N + TileD::BN - 1) / TileD::BN);
-  hipLaunchKernelGGL((k_up_dense_dec<T>), grid, dim3(128), 0, s, x, w1t, b1, M, N, K, x_rows, arow, n_rows_dev, out,
+  const dim3 grid((N + TileDQ::BN - 1) / TileDQ::BN);
+  hipLaunchKernelGGL((k_up_dense_dec<T>), grid, dim3(256), 0, s, x, w1t, b1, M, N, K, x_rows, arow, n_rows_dev, out,
                      out_bf16, relu);
   return hipGetLastError();
 }

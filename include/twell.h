@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 1
+#define TWELL_ABI_VERSION 2
 
 typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype_t;
 
@@ -73,7 +73,13 @@ typedef enum {
  *   row_nnz[R]                      library scratch: entries of each row's compact list
  *   row_list[R][C/tile_w * slots]   library scratch: compact (int32 column, fp32 value)
  *                                   pairs of each row, written by twell_up_finish and by
- *                                   twell_down before use
+ *                                   twell_down before use; twell_row_list_bytes bytes.
+ *                                   For R <= 64 it also holds the decode workspace of the
+ *                                   up GEMM (after the lists): fp32 half sums of the K split
+ *                                   and one uint32 ticket per 128 columns. The tickets must
+ *                                   be zero when the buffer is first used (allocate it
+ *                                   zero-filled); every call leaves them zero. Calls that
+ *                                   overlap on one h race.
  *
  * A row overflows iff some tile of it holds more than `slots` nonzeros. A (row, tile)
  * keeps its first min(count, slots) nonzeros in ascending column order. "Nonzero" is
@@ -108,7 +114,9 @@ const char *twell_status_str(int status);
 /* Number of uint32 words that twell_matrix_t.ovf_bits must hold. */
 size_t twell_ovf_bits_words(int32_t rows, int32_t cols, int32_t tile_w);
 
-/* Bytes that twell_matrix_t.row_list must hold (8 bytes per slot of the matrix). */
+/* Bytes that twell_matrix_t.row_list must hold: 8 bytes per slot of the matrix, plus, for
+ * rows <= 64, the decode workspace (256-byte aligned after the lists; 64 KB per 128
+ * columns and the tickets). */
 size_t twell_row_list_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots);
 
 /*
@@ -147,7 +155,12 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
  *                     the down projection walks. Must follow twell_up_gemm on the same h.
  *                     After both, h is the complete TwELL of ReLU(x W1 + b1).
  * Same arguments, checks and errors as twell_ffn_fwd (twell_up_finish also needs row_nnz
- * and row_list).
+ * and row_list; twell_up_gemm needs row_list when 0 < T <= 64, for the decode workspace,
+ * else TWELL_ERR_ARG).
+ *
+ * Up to 64 tokens the GEMM sums K in four quarters, (q0 + q1) + (q2 + q3), and spreads each
+ * 128-column tile over two workgroups (quarters 0-1 and 2-3) that meet in the decode
+ * workspace of row_list; ffn_up_relu_dense sums the same quarters in the same order.
  */
 int twell_up_gemm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
                   int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream);

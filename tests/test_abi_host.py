@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tw.twell_abi_version() == 1
+    assert tw.twell_abi_version() == 2
     L = tw.lib()
     for code in [0, -1, -2, -3, -4, -5, -6, -7]:
         s = L.twell_status_str(code).decode()
@@ -47,6 +47,18 @@ def test_version_and_status_strings():
     assert L.twell_status_str(12345).decode() == "TWELL_UNKNOWN_STATUS"
     assert L.twell_ovf_bits_words(100, 1024, 64) == 16 * 4
     assert L.twell_ovf_bits_words(-1, 1024, 64) == 0
+
+
+def test_row_list_bytes_with_decode_workspace():
+    L = tw.lib()
+    # above 64 rows: the lists only (8 bytes per slot)
+    assert L.twell_row_list_bytes(65, 14336, 128, 16) == 65 * 112 * 16 * 8
+    assert L.twell_row_list_bytes(4096, 1024, 64, 8) == 4096 * 16 * 8 * 8
+    # up to 64 rows: lists rounded up to 256 bytes, then two 64 x 128 fp32 half sums and a
+    # uint32 ticket per 128 columns (the tickets rounded up to 256 bytes)
+    assert L.twell_row_list_bytes(64, 14336, 128, 16) == 64 * 112 * 16 * 8 + 112 * 65536 + 512
+    assert L.twell_row_list_bytes(1, 1984, 64, 3) == 768 + 16 * 65536 + 256     # 15.5 tiles -> 16
+    assert L.twell_row_list_bytes(0, 512, 128, 8) == 0 + 4 * 65536 + 256
 
 
 def gpu_present():
@@ -130,6 +142,10 @@ def test_gated_entry_points_reject():
     assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 64, 100, 512, None) == ALIGN
     assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 32, 256, 512, None) == SHAPE
     assert L.twell_gate_up(ctypes.byref(mat(row_list=None)), FAKE, FAKE, 1, 64, 256, 512, None) == ARG
+    # the up GEMM alone needs row_list at decode sizes (its K-split workspace), not above
+    up = lambda m, T: L.twell_up_gemm(FAKE, FAKE, FAKE, 1, T, 256, 512, ctypes.byref(m), None)
+    assert up(mat(rows=4, row_list=None), 4) == ARG
+    assert up(mat(rows=64, row_list=None), 64) == ARG
 
     def gfwd(**kw):
         a = dict(x=FAKE, wg=FAKE, bg=FAKE, wu=FAKE, w2=FAKE, dt=1, T=64, d=256, f=512, y=FAKE, ydt=0)

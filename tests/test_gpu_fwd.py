@@ -165,6 +165,42 @@ def test_fwd_c3(T):
     say("c3", T, "flips", flips, "err", err)
 
 
+def decode_tickets(h):
+    """The per-128-column tickets of the decode K split, at the end of h's row_list scratch."""
+    lists = h.rows * (h.cols // h.tile_w) * h.slots * 8
+    tiles = (h.cols + 127) // 128
+    off = ((lists + 255) // 256 * 256 + tiles * 2 * 64 * 128 * 4) // 4
+    return h.row_list.view(torch.int32)[off:off + tiles]
+
+
+@pytest.mark.parametrize("T,f,W,S,seed", [(1, 1984, 64, 3, 21), (37, 2048, 128, 8, 22), (64, 1984, 64, 4, 23),
+                                          (64, 2048, 128, 2, 24)])
+def test_fwd_decode_split(T, f, W, S, seed):
+    """Up to 64 tokens the up GEMM splits every 128-column tile over two workgroups that add
+    their halves of K through the row_list workspace. f = 1984 ends in a half tile. The TwELL
+    equals the dense path's packing bit for bit (which sums the same quarters in one
+    workgroup), the tickets are zero after every call, and repeated calls on one h give the
+    same bits. S = 2 at T = 64 makes rows overflow, so the backup rows (dense path, rows
+    gathered by index) are exercised too."""
+    say("fwd decode split", T, f, W, S)
+    w = synth.C3.with_(d=1024, f=f, tile_w=W, slots=S, seed=seed)
+    g = synth.generate(w, T=T)
+    got, flips, err = check_forward(g, W, S, 64)
+    x, w1t, b1, w2 = dev_inputs(g)
+    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, 64)
+    torch.cuda.synchronize()
+    assert int(decode_tickets(h).abs().sum()) == 0
+    c1 = twell_host(h)
+    y2, _ = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, 64, h=h)
+    torch.cuda.synchronize()
+    assert int(decode_tickets(h).abs().sum()) == 0
+    assert torch.equal(y1, y2)
+    assert_twell_equal(twell_host(h), c1)
+    assert_twell_equal(c1, got)
+    if S == 2:
+        assert got["ovf_n"] > 0
+
+
 def test_fwd_hot_tokens_and_capacity():
     say("fwd hot tokens")
     w = synth.C5.with_(T=600, d=512, f=2048, slots=8, hot_every=64)
