@@ -17,7 +17,7 @@ __all__ = [
     "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
     "twell_down", "twell_fwd_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense",
     "twell_gate_up", "twell_gated_ffn_fwd", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
-    "nm_prune", "nm_ffn_down", "twell_sync_status", "F32", "BF16",
+    "nm_prune", "ffn_up_relu_nm", "nm_ffn_down", "twell_sync_status", "F32", "BF16",
 ]
 
 F32, BF16 = 0, 1
@@ -62,6 +62,7 @@ _SIGS = {
     "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
     "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
     "nm_prune": ([_P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
+    "ffn_up_relu_nm": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "nm_ffn_down": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P], _I),
     "twell_sync_status": ([_P, _P], _I),
 }
@@ -297,6 +298,20 @@ def nm_prune(h: torch.Tensor, n: int, m: int):
     idx = torch.empty((T, f // m, n), dtype=torch.uint8, device=h.device)
     _check(lib().nm_prune(_ptr(h), _dt(h.dtype), T, f, n, m, _ptr(vals), _ptr(idx), _stream(h.device)),
            "nm_prune")
+    return vals, idx
+
+
+def ffn_up_relu_nm(x, w1t, b1, n: int, m: int, vals=None, idx=None):
+    """N:M-pruned h = ReLU(x W1 + b1) from the up GEMM's epilogue: (vals [T][f/m][n] in x's
+    dtype, idx [T][f/m][n] uint8)."""
+    T, d = x.shape
+    f = w1t.shape[0]
+    if vals is None:
+        vals = torch.empty((T, f // m, n), dtype=x.dtype, device=x.device)
+    if idx is None:
+        idx = torch.empty((T, f // m, n), dtype=torch.uint8, device=x.device)
+    _check(lib().ffn_up_relu_nm(_ptr(x), _ptr(w1t), _ptr(b1), _dt(x.dtype), T, d, f, n, m, _ptr(vals),
+                                _ptr(idx), _stream(x.device)), "ffn_up_relu_nm")
     return vals, idx
 
 

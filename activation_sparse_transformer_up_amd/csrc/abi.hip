@@ -345,6 +345,20 @@ int nm_prune(const void *h, int32_t dtype, int32_t T, int32_t d_ff, int32_t n, i
   return TWELL_OK;
 }
 
+int ffn_up_relu_nm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T, int32_t d_model,
+                   int32_t d_ff, int32_t n, int32_t m, void *vals, uint8_t *idx, void *stream) {
+  if (!b1 || (T > 0 && (!vals || !idx))) return TWELL_ERR_ARG;
+  int st = check_ffn_args(x, w1t, nullptr, in_dtype, T, d_model, d_ff);
+  if (st) return st;
+  if (!((n == 2 && m == 4) || (n == 4 && m == 8) || (n == 8 && m == 16) || (n == 16 && m == 32)))
+    return TWELL_ERR_SHAPE;
+  if (d_ff % m) return TWELL_ERR_SHAPE;
+  if (!al4(b1) || !al16(vals) || !al16(idx)) return TWELL_ERR_ALIGN;
+  if (T == 0) return TWELL_OK;
+  TW_TRY(launch_up_nm(in_dtype == TWELL_BF16, x, w1t, b1, T, d_ff, d_model, n, m, vals, idx, S(stream)));
+  return TWELL_OK;
+}
+
 int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, int32_t d_ff, int32_t n,
                 int32_t m, const void *w2t, int32_t d_model, void *y, int32_t y_dtype, void *stream) {
   if (!w2t || (T > 0 && (!vals || !idx || !y))) return TWELL_ERR_ARG;

@@ -24,6 +24,7 @@
 
 #include "common.h"
 #include "launch.h"
+#include "nmsel.h"
 #include "stage.h"
 
 namespace tw {
@@ -669,6 +670,133 @@ TW_DEV void epi_dense16(f32x4_t (&acc)[G::FM][G::FN], const float *__restrict__ 
   }
 }
 
+// ---------------------------------------------------------------- N:M epilogue
+// "Motivating Next-Gen Accelerators with Flexible (N:M) Activation Sparsity ...", section
+// "2. Metodologia": the activations are pruned to N:M by magnitude. Fused here into the up
+// GEMM so that the dense h never goes to HBM: the workgroup's tile of h = ReLU(z + b1) is
+// rounded to the output type and staged in LDS ([BM][BN], rows padded by 16 bytes), then
+// every thread takes whole blocks of M columns, selects with nm_keep, compacts the kept
+// (value, index) pairs in place over the block's own LDS bytes and copies them out. h is
+// formed exactly as the dense epilogue forms it, so the result equals the standalone
+// pruning of ffn_up_relu_dense's output bit for bit.
+template <typename HT> TW_DEV void put_h(char *p, float z) {
+  z = z > 0.f ? z : 0.f;
+  if constexpr (sizeof(HT) == 2) *(uint16_t *)p = (uint16_t)f32_to_bf16(z);
+  else *(float *)p = z;
+}
+
+template <class G, typename HT> constexpr int nm_row_bytes() { return G::BN * (int)sizeof(HT) + 16; }
+template <class G, typename HT> constexpr int nm_stage_bytes() { return G::BM * nm_row_bytes<G, HT>(); }
+
+// 16 x 16 accumulator blocks: register i of block (fm, fn) is row fm * 16 + 4 (lane / 16) + i,
+// column fn * 16 + lane % 16 of the wave's sub-tile.
+template <class G, typename HT>
+TW_DEV void stage_h16(const f32x4_t (&acc)[G::FM][G::FN], const float *__restrict__ b1, int N, int n0, char *lds) {
+  constexpr int RS = nm_row_bytes<G, HT>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / G::NWN, wn = wave % G::NWN;
+  const int g = lane >> 4, li = lane & 15;
+#pragma unroll
+  for (int fn = 0; fn < G::FN; ++fn) {
+    const int ct = wn * G::WN + fn * 16 + li;
+    const float bias = n0 + ct < N ? b1[n0 + ct] : 0.f;
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+      for (int r = 0; r < 4; ++r)
+        put_h<HT>(lds + (wm * G::WM + fm * 16 + 4 * g + r) * RS + ct * (int)sizeof(HT), acc[fm][fn][r] + bias);
+  }
+}
+
+// 32 x 32 accumulator blocks (register r of block (mb, nb): row acc_row(r, lane / 32), column
+// lane % 32).
+template <class G, typename HT>
+TW_DEV void stage_h32(const f32x16_t (&acc)[G::MB][G::NB], const float *__restrict__ b1, int N, int n0, char *lds) {
+  constexpr int RS = nm_row_bytes<G, HT>();
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int wm = wave / G::NWN, wn = wave % G::NWN;
+  const int lh = lane >> 5, li = lane & 31;
+#pragma unroll
+  for (int nb = 0; nb < G::NB; ++nb) {
+    const int ct = wn * G::WN + nb * 32 + li;
+    const float bias = n0 + ct < N ? b1[n0 + ct] : 0.f;
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        put_h<HT>(lds + (wm * G::WM + mb * 32 + acc_row(r, lh)) * RS + ct * (int)sizeof(HT), acc[mb][nb][r] + bias);
+  }
+}
+
+// Copy NB bytes (a power of two, both sides NB-aligned up to 16) with the widest accesses.
+template <int NB> TW_DEV void copy_bytes(char *dst, const char *src) {
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) ((uint4 *)dst)[i] = ((const uint4 *)src)[i];
+  } else if constexpr (NB == 8) {
+    *(uint2 *)dst = *(const uint2 *)src;
+  } else if constexpr (NB == 4) {
+    *(uint32_t *)dst = *(const uint32_t *)src;
+  } else {
+    static_assert(NB == 2, "size");
+    *(uint16_t *)dst = *(const uint16_t *)src;
+  }
+}
+
+// Select the blocks of the staged tile (rows m0 .., columns n0 ..; rows at or beyond
+// rows_valid and columns at or beyond N are skipped; N is a multiple of M). Outputs
+// vals / idx [rows][N / M][NK]. Consecutive threads take consecutive blocks of a row, so the
+// copies of a wave are contiguous.
+template <typename HT, int NK, int M, int BM, int BN, int NT>
+TW_DEV void nm_tile(char *lds, int rows_valid, int N, int m0, int n0, HT *__restrict__ vals,
+                    uint8_t *__restrict__ idx) {
+  constexpr int RS = BN * (int)sizeof(HT) + 16;
+  constexpr int GPR = BN / M;                       // blocks per tile row
+  constexpr int GB = M * (int)sizeof(HT);           // bytes of a block
+  constexpr int VB = NK * (int)sizeof(HT);          // bytes of its kept values (= GB / 2)
+  static_assert(BN % M == 0 && 2 * NK == M, "blocks");
+  const int bpr = N / M;
+  for (int gi = threadIdx.x; gi < BM * GPR; gi += NT) {
+    const int r = gi / GPR, q = gi - r * GPR;
+    const int row = m0 + r, col = n0 + q * M;
+    if (row >= rows_valid || col >= N) continue;
+    char *p = lds + r * RS + q * GB;
+    uint32_t w[GB / 4];
+    if constexpr (GB % 16 == 0) {
+#pragma unroll
+      for (int v = 0; v < GB / 16; ++v) {
+        const uint4 u = ((const uint4 *)p)[v];
+        w[4 * v] = u.x; w[4 * v + 1] = u.y; w[4 * v + 2] = u.z; w[4 * v + 3] = u.w;
+      }
+    } else {
+      const uint2 u = *(const uint2 *)p;
+      w[0] = u.x; w[1] = u.y;
+    }
+    uint32_t bits[M];
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if constexpr (sizeof(HT) == 2) bits[i] = (w[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+      else bits[i] = w[i];
+    }
+    bool keep[M];
+    nm_keep<(int)sizeof(HT), NK, M>(bits, keep);
+    // in place: entry i moves to position pos <= i, so nothing unread is overwritten
+    int pos = 0;
+#pragma unroll
+    for (int i = 0; i < M; ++i) {
+      if (keep[i]) {
+        if constexpr (sizeof(HT) == 2) ((uint16_t *)p)[pos] = (uint16_t)bits[i];
+        else ((uint32_t *)p)[pos] = bits[i];
+        ((uint8_t *)p)[VB + pos] = (uint8_t)i;
+        ++pos;
+      }
+    }
+    const size_t o = ((size_t)row * bpr + col / M) * NK;
+    copy_bytes<VB>((char *)(vals + o), p);
+    copy_bytes<NK>((char *)(idx + o), p + VB);
+  }
+}
+
 // ------------------------------------------------------------------------ kernels
 
 template <typename T, class G, int W, typename VT>
@@ -908,6 +1036,74 @@ __global__ __launch_bounds__(256) void k_up_dense_dec(const T *__restrict__ x, c
   epi_dense<TileD>(acc, b1, rows, N, 0, n0, out, out_bf16, relu);
 }
 
+// h = ReLU(x W1 + b1) pruned to NK:M inside the up GEMM (N:M epilogue above). The tiles,
+// loops and accumulation order are those of k_up_dense for the same problem, so z is the
+// same bit for bit.
+template <typename T, class G, int NK, int M>
+__global__ __launch_bounds__(G::NT) void k_up_nm(const T *__restrict__ x, const T *__restrict__ w1t,
+                                                 const float *__restrict__ b1, int Mr, int N, int K,
+                                                 T *__restrict__ vals, uint8_t *__restrict__ idx) {
+  constexpr int SM = G::LDS_BYTES > nm_stage_bytes<G, T>() ? G::LDS_BYTES : nm_stage_bytes<G, T>();
+  static_assert(SM <= 160 * 1024, "LDS");
+  __shared__ __attribute__((aligned(16))) char smem[SM];
+  const int n0 = blockIdx.x * G::BN, m0 = blockIdx.y * G::BM;
+  if constexpr (G::MI == 16) {
+    static_assert(std::is_same<T, uint16_t>::value, "16x16x32 MFMA tiles take bf16 operands");
+    f32x4_t acc[G::FM][G::FN];
+#pragma unroll
+    for (int fm = 0; fm < G::FM; ++fm)
+#pragma unroll
+      for (int fn = 0; fn < G::FN; ++fn) acc[fm][fn] = f32x4_t{};
+    mainloop16<G>(x, nullptr, Mr, Mr, w1t, N, K, m0, n0, acc, smem);
+    block_barrier();                    // every wave is done reading the operand stages
+    stage_h16<G, T>(acc, b1, N, n0, smem);
+  } else {
+    f32x16_t acc[G::MB][G::NB];
+#pragma unroll
+    for (int mb = 0; mb < G::MB; ++mb)
+#pragma unroll
+      for (int nb = 0; nb < G::NB; ++nb) acc[mb][nb] = f32x16_t{};
+    mainloop<T, G>(x, nullptr, Mr, Mr, w1t, N, K, m0, n0, acc, smem);
+    block_barrier();
+    stage_h32<G, T>(acc, b1, N, n0, smem);
+  }
+  block_barrier_lds();
+  nm_tile<T, NK, M, G::BM, G::BN, G::NT>(smem, Mr, N, m0, n0, vals, idx);
+}
+
+// Decode form: the quarters of k_up_dense_dec, summed the same way by wave 0, then all four
+// waves select.
+template <typename T, int NK, int M>
+__global__ __launch_bounds__(256) void k_up_nm_dec(const T *__restrict__ x, const T *__restrict__ w1t,
+                                                   const float *__restrict__ b1, int Mr, int N, int K,
+                                                   T *__restrict__ vals, uint8_t *__restrict__ idx) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * TileDQ::LDS_BYTES];
+  static_assert(nm_stage_bytes<TileD, T>() <= 4 * TileDQ::LDS_BYTES, "LDS");
+  const int n0 = blockIdx.x * TileDQ::BN;
+  if (Mr <= 0) return;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int kq = K / 4;
+  f32x16_t acc[TileD::MB][TileD::NB];
+#pragma unroll
+  for (int mb = 0; mb < TileD::MB; ++mb)
+#pragma unroll
+    for (int nb = 0; nb < TileD::NB; ++nb) acc[mb][nb] = f32x16_t{};
+  mainloop<T, TileDQ>(x, nullptr, Mr, Mr, w1t, N, kq, 0, n0, acc, smem + w * TileDQ::LDS_BYTES, K, w * kq, 0);
+  block_barrier_lds();
+  float *red = (float *)smem;
+  if (w & 1) acc_to_lds(acc, red + (w >> 1) * kDecTileF);
+  block_barrier_lds();
+  if (!(w & 1)) acc_add_lds(acc, red + (w >> 1) * kDecTileF);   // waves 0, 2: q0 + q1, q2 + q3
+  block_barrier_lds();
+  if (w == 2) acc_to_lds(acc, red);
+  block_barrier_lds();
+  if (w == 0) acc_add_lds(acc, red);
+  block_barrier_lds();                  // the partial sums are read before the tile overwrites them
+  if (w == 0) stage_h32<TileD, T>(acc, b1, N, n0, smem);
+  block_barrier_lds();
+  nm_tile<T, NK, M, TileD::BM, TileD::BN, 256>(smem, Mr, N, 0, n0, vals, idx);
+}
+
 // The decode kernels apply to at most 64 tokens and K a multiple of four stages.
 template <typename T> static bool use_decode(int T_tokens, int K) {
   constexpr int KPT = TileD::RB / (int)sizeof(T);
@@ -1005,6 +1201,55 @@ hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float
   }
   return launch_dense_t<float, TileSF>((const float *)x, (const float *)w1t, b1, M, N, K, x_rows, arow, n_rows_dev,
                                       out, out_bf16, relu, s);
+}
+
+// ------------------------------------------------------------------ up GEMM + N:M pruning
+
+template <typename T, class G, int NK, int M>
+static void launch_nm_one(const T *x, const T *w1t, const float *b1, int Mr, int N, int K, T *vals, uint8_t *idx,
+                          hipStream_t s) {
+  dim3 grid((N + G::BN - 1) / G::BN, (Mr + G::BM - 1) / G::BM);
+  hipLaunchKernelGGL((k_up_nm<T, G, NK, M>), grid, dim3(G::NT), 0, s, x, w1t, b1, Mr, N, K, vals, idx);
+}
+
+template <typename T, class G>
+static hipError_t launch_nm_t(const T *x, const T *w1t, const float *b1, int Mr, int N, int K, int n, int m,
+                              T *vals, uint8_t *idx, hipStream_t s) {
+  if (n == 2 && m == 4) launch_nm_one<T, G, 2, 4>(x, w1t, b1, Mr, N, K, vals, idx, s);
+  else if (n == 4 && m == 8) launch_nm_one<T, G, 4, 8>(x, w1t, b1, Mr, N, K, vals, idx, s);
+  else if (n == 8 && m == 16) launch_nm_one<T, G, 8, 16>(x, w1t, b1, Mr, N, K, vals, idx, s);
+  else if (n == 16 && m == 32) launch_nm_one<T, G, 16, 32>(x, w1t, b1, Mr, N, K, vals, idx, s);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+template <typename T>
+static hipError_t launch_nm_dec(const T *x, const T *w1t, const float *b1, int Mr, int N, int K, int n, int m,
+                                T *vals, uint8_t *idx, hipStream_t s) {
+  const dim3 grid((N + TileDQ::BN - 1) / TileDQ::BN), blk(256);
+  if (n == 2 && m == 4) hipLaunchKernelGGL((k_up_nm_dec<T, 2, 4>), grid, blk, 0, s, x, w1t, b1, Mr, N, K, vals, idx);
+  else if (n == 4 && m == 8) hipLaunchKernelGGL((k_up_nm_dec<T, 4, 8>), grid, blk, 0, s, x, w1t, b1, Mr, N, K, vals, idx);
+  else if (n == 8 && m == 16) hipLaunchKernelGGL((k_up_nm_dec<T, 8, 16>), grid, blk, 0, s, x, w1t, b1, Mr, N, K, vals, idx);
+  else if (n == 16 && m == 32) hipLaunchKernelGGL((k_up_nm_dec<T, 16, 32>), grid, blk, 0, s, x, w1t, b1, Mr, N, K, vals, idx);
+  else return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+// The same kernel choice as launch_up_dense without gathered rows (x_rows = M), so the fused
+// and the two-step results agree bit for bit.
+hipError_t launch_up_nm(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K, int n,
+                        int m, void *vals, uint8_t *idx, hipStream_t s) {
+  if (bf16) {
+    const uint16_t *xb = (const uint16_t *)x, *wb = (const uint16_t *)w1t;
+    uint16_t *vb = (uint16_t *)vals;
+    if (use_decode<uint16_t>(M, K)) return launch_nm_dec<uint16_t>(xb, wb, b1, M, N, K, n, m, vb, idx, s);
+    if (use_large(M, N)) return launch_nm_t<uint16_t, TileL8>(xb, wb, b1, M, N, K, n, m, vb, idx, s);
+    return launch_nm_t<uint16_t, TileS>(xb, wb, b1, M, N, K, n, m, vb, idx, s);
+  }
+  const float *xf = (const float *)x, *wf = (const float *)w1t;
+  float *vf = (float *)vals;
+  if (use_decode<float>(M, K)) return launch_nm_dec<float>(xf, wf, b1, M, N, K, n, m, vf, idx, s);
+  return launch_nm_t<float, TileSF>(xf, wf, b1, M, N, K, n, m, vf, idx, s);
 }
 
 }  // namespace tw

@@ -47,6 +47,9 @@ hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float
 hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
                            int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
                            hipStream_t s);
+// h = ReLU(x W1 + b1) pruned to n:m in the GEMM epilogue (vals in the operand type)
+hipError_t launch_up_nm(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K, int n,
+                        int m, void *vals, uint8_t *idx, hipStream_t s);
 
 // pack.hip
 hipError_t launch_pack(const void *h, int h_bf16, int R, int C, const TwellOut &o, int W, hipStream_t s);

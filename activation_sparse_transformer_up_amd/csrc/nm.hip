@@ -8,43 +8,18 @@
 // back to dense bf16 in LDS and multiplies on MFMA (only the activation bytes shrink).
 #include "common.h"
 #include "launch.h"
+#include "nmsel.h"
 #include "stage.h"
 
 namespace tw {
 
 // ------------------------------------------------------------------------ nm_prune
-// One thread per block of M. Entry i is kept iff its rank
-//   rank_i = #{k : |h_k| > |h_i|} + #{k < i : |h_k| == |h_i|}
-// is below N (magnitudes compared as sign-cleared bit patterns: exact and monotone for
-// finite values, +-0 equal); output position = kept entries of lower index.
-// bf16: the ranks are those of the unique keys (magnitude << log2 M) | (M - 1 - i); every
-// supported pattern keeps N = M / 2, and the N largest keys are found by sorting each half
-// of the block (bitonic network, descending) and taking c_i = max(a_i, b_{N-1-i}), whose
-// minimum is the N-th largest key. fp32 (31-bit magnitudes) counts the ranks directly.
-// Outputs are staged in LDS per wave and written with 16-byte stores.
-
-// Bitonic sort of L keys, descending; every index is a compile-time constant.
-template <int L> TW_DEV void bitonic_desc(uint32_t (&a)[L]) {
-  static_for<31 - __builtin_clz(L)>([&](auto KS) {              // k = 2, 4, ..., L
-    constexpr int k = 2 << decltype(KS)::value;
-    static_for<decltype(KS)::value + 1>([&](auto JS) {          // j = k/2, ..., 1
-      constexpr int j = (k >> 1) >> decltype(JS)::value;
-      static_for<L>([&](auto IS) {
-        constexpr int i = decltype(IS)::value, l = i ^ j;
-        if constexpr (l > i) {
-          const uint32_t x = a[i], y = a[l];
-          const uint32_t hi = x > y ? x : y, lo = x > y ? y : x;
-          if constexpr ((i & k) == 0) { a[i] = hi; a[l] = lo; }
-          else { a[i] = lo; a[l] = hi; }
-        }
-      });
-    });
-  });
-}
+// One thread per block of M; the kept set is chosen by nm_keep (nmsel.h), and the kept
+// positions are emitted in ascending order with their signed values. Outputs are staged in
+// LDS per wave and written with 16-byte stores.
 template <typename HT, int N, int M>
 __global__ __launch_bounds__(256) void k_nm_prune(const HT *__restrict__ h, size_t groups, HT *__restrict__ vals,
                                                   uint8_t *__restrict__ idx) {
-  constexpr uint32_t MAGMASK = sizeof(HT) == 2 ? 0x7FFFu : 0x7FFFFFFFu;
   __shared__ __attribute__((aligned(16))) HT sv[4][64 * N];
   __shared__ __attribute__((aligned(16))) uint8_t si[4][64 * N];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
@@ -82,39 +57,7 @@ __global__ __launch_bounds__(256) void k_nm_prune(const HT *__restrict__ h, size
     for (int i = 0; i < M; ++i) bits[i] = 0;
   }
   bool keep[M];
-  if constexpr (sizeof(HT) == 2) {
-    static_assert(2 * N == M, "bf16 path keeps half of each block");
-    constexpr int LOGM = 31 - __builtin_clz(M);
-    uint32_t key[M], a[N], b[N];
-    static_for<M>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      key[i] = ((bits[i] & MAGMASK) << LOGM) | (uint32_t)(M - 1 - i);
-      if constexpr (i < N) a[i] = key[i];
-      else b[i - N] = key[i];
-    });
-    bitonic_desc<N>(a);
-    bitonic_desc<N>(b);
-    uint32_t th = 0xFFFFFFFFu;
-    static_for<N>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const uint32_t c = a[i] > b[N - 1 - i] ? a[i] : b[N - 1 - i];
-      th = c < th ? c : th;
-    });
-    static_for<M>([&](auto I) { keep[decltype(I)::value] = key[decltype(I)::value] >= th; });
-  } else {
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const uint32_t mi = bits[i] & MAGMASK;
-      int rank = 0;
-#pragma unroll
-      for (int k = 0; k < M; ++k) {
-        if (k == i) continue;
-        const uint32_t mk = bits[k] & MAGMASK;
-        rank += (k < i) ? (mk >= mi) : (mk > mi);
-      }
-      keep[i] = rank < N;
-    }
-  }
+  nm_keep<(int)sizeof(HT), N, M>(bits, keep);
   int pos = 0;
 #pragma unroll
   for (int i = 0; i < M; ++i) {

@@ -215,9 +215,16 @@ def leg_c4(steps, warmup):
         y = torch.empty((T, d), device=dev)
         ms_d = _time(lambda: tw.nm_ffn_down(vals, idx, n, m, w2t, y=y), steps, warmup)
         pbytes = T * f * 2 + T * (f // m) * n * 3
+        # the same pruning inside the up GEMM's epilogue (the dense h never reaches HBM)
+        fv, fi = tw.ffn_up_relu_nm(x, w1t, b1, n, m)
+        ms_f = _time(lambda: tw.ffn_up_relu_nm(x, w1t, b1, n, m, vals=fv, idx=fi), steps, warmup)
+        up_flop = 2.0 * T * d * f
         out[f"{n}:{m}"] = {
             "prune_ms": ms_p, "prune_GB_per_s": pbytes / (ms_p * 1e-3) / 1e9,
             "prune_frac_hbm_peak": pbytes / (ms_p * 1e-3) / 1e9 / PEAK_HBM_GBS,
+            "fused_up_nm_ms": ms_f, "unfused_up_nm_ms": out["up_relu_dense_ms"] + ms_p,
+            "fused_vs_unfused": (out["up_relu_dense_ms"] + ms_p) / ms_f,
+            "fused_up_nm_frac_mfma_peak": up_flop / (ms_f * 1e-3) / 1e12 / PEAK_BF16_TFLOPS,
             "nm_down_ms": ms_d, "nm_down_TFLOPs": 2.0 * T * f * d / (ms_d * 1e-3) / 1e12,
             "nm_down_vs_dense_down": out["dense_down_ms"] / ms_d}
     return out

@@ -263,6 +263,21 @@ int nm_prune(const void *h, int32_t dtype, int32_t T, int32_t d_ff, int32_t n, i
              void *vals, uint8_t *idx, void *stream);
 
 /*
+ * ffn_up_relu_nm — the up projection with N:M pruning in its epilogue ("Motivating Next-Gen
+ * Accelerators with Flexible (N:M) Activation Sparsity ...", "2. Metodologia", criterion
+ * ACT, applied to h = ReLU(x . W1 + b1)). The dense h is never written: each workgroup
+ * rounds its tile of h to in_dtype in LDS and prunes it there. The result is bit-identical
+ * to nm_prune(n, m) applied to ffn_up_relu_dense(..., h_dtype = in_dtype):
+ *   vals [T][d_ff/m][n]  in_dtype (the kept values of h, ascending index in the block)
+ *   idx  [T][d_ff/m][n]  uint8
+ * Arguments and checks as ffn_up_relu_dense and nm_prune: (n, m) in (2,4), (4,8), (8,16),
+ * (16,32) and d_ff % m == 0, else TWELL_ERR_SHAPE; vals, idx 16-byte aligned.
+ */
+int ffn_up_relu_nm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
+                   int32_t d_model, int32_t d_ff, int32_t n, int32_t m, void *vals, uint8_t *idx,
+                   void *stream);
+
+/*
  * nm_ffn_down — y = H_nm . W2 for N:M-packed activations (vals, idx from nm_prune, bf16).
  * gfx950 has no N:M matrix instruction, so each block is expanded to dense bf16 in LDS and
  * multiplied on MFMA; only the activation bytes shrink. The down weight is given as

@@ -187,3 +187,18 @@ def integer_grid(T: int, d: int, f: int, seed: int, dtype: str = BF16,
     conv = (lambda a: f32_to_bf16_bits(a.astype(np.float32))) if dtype == BF16 else (lambda a: a.astype(np.float32))
     return {"x": conv(x), "w1t": conv(w1t), "b1": b1, "w2": conv(w2), "dy": conv(rng.integers(-8, 9, size=(T, d)) / 8.0),
             "p": None, "dtype": dtype, "workload": None}
+
+
+def nm_grid(T: int, d: int, f: int, seed: int, dtype: str = BF16) -> dict:
+    """Inputs whose pre-activations are exact in bf16 as well as fp32 (for N:M pruning of
+    ReLU(x W1 + b1) stored in bf16): x in {-1, 0, 1}/2, w1t in {-1, 0, 1}/8, b1 in
+    {-4..4}/16, so z = k/16 with |k| <= d + 4 <= 256 (d <= 252) in any summation order.
+    About half of the pre-activations are positive, and equal magnitudes are frequent.
+    """
+    assert d <= 252
+    rng = np.random.default_rng(seed)
+    x = rng.integers(-1, 2, size=(T, d)) / 2.0
+    w1t = rng.integers(-1, 2, size=(f, d)) / 8.0
+    b1 = (rng.integers(-4, 5, size=f) / 16.0).astype(np.float32)
+    conv = (lambda a: f32_to_bf16_bits(a.astype(np.float32))) if dtype == BF16 else (lambda a: a.astype(np.float32))
+    return {"x": conv(x), "w1t": conv(w1t), "b1": b1, "dtype": dtype}

@@ -28,7 +28,7 @@ def test_header_declares_expected_entry_points():
               "twell_status_str", "twell_sync_status", "nm_ffn_down", "ffn_up_relu_dense",
               "twell_down", "twell_ffn_bwd_workspace_bytes", "twell_ovf_bits_words",
               "twell_row_list_bytes", "twell_up_gemm", "twell_up_finish", "twell_fwd_down",
-              "twell_gate_up", "twell_gated_ffn_fwd"]:
+              "twell_gate_up", "twell_gated_ffn_fwd", "ffn_up_relu_nm"]:
         assert n in names, n
 
 
@@ -158,3 +158,28 @@ def test_gated_entry_points_reject():
     assert gfwd(ydt=4) == ARG
     assert gfwd(wu=MIS) == ALIGN
     assert gfwd(f=1024) == SHAPE
+
+
+@pytestmark_nogpu
+def test_up_nm_rejects():
+    L = tw.lib()
+
+    def up_nm(**kw):
+        a = dict(x=FAKE, w1t=FAKE, b1=FAKE, dt=1, T=64, d=256, f=512, n=8, m=16, vals=FAKE, idx=FAKE)
+        a.update(kw)
+        return L.ffn_up_relu_nm(a["x"], a["w1t"], a["b1"], a["dt"], a["T"], a["d"], a["f"], a["n"], a["m"],
+                                a["vals"], a["idx"], None)
+    assert up_nm(b1=None) == ARG
+    assert up_nm(vals=None) == ARG
+    assert up_nm(idx=None) == ARG
+    assert up_nm(w1t=None) == ARG
+    assert up_nm(dt=3) == ARG
+    assert up_nm(n=3) == SHAPE
+    assert up_nm(n=8, m=32) == SHAPE
+    assert up_nm(f=520) == SHAPE                  # d_ff not a multiple of m
+    assert up_nm(T=-1) == SHAPE
+    assert up_nm(d=100) == ALIGN
+    assert up_nm(vals=MIS) == ALIGN
+    assert up_nm(idx=MIS) == ALIGN
+    assert up_nm(b1=MIS + 2) == ALIGN
+    assert up_nm(T=0, vals=None, idx=None) == 0   # nothing to do, nothing touched
