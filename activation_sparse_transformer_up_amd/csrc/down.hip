@@ -324,6 +324,75 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
   }
 }
 
+// Medium token counts at wide rows: a workgroup of 4 waves owns one (token, chunk of 64
+// lanes x 16 bytes: 512 bf16 or 256 fp32 columns), so every W2 row piece is one contiguous
+// 1 KB wave load. Chunk c runs on XCD c % 8 as in the other decompositions. Wave w takes
+// entries [64 k + 16 w, 64 k + 16 w + 16) of the token's list, k = 0, 1, ...: lanes 0-15
+// load the sixteen pairs (the first ones speculatively with the count, the next round's while
+// the rows are in flight) and readlane broadcasts them, so the row addresses are scalar.
+// The four wave sums are added in wave order through LDS. A backup row is taken by the
+// four waves as four 16-lane chunks (backup_row).
+template <typename WT, typename VT, typename YT>
+__global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restrict__ w2, int d,
+                                                   YT *__restrict__ y, int nchunk) {
+  constexpr int E = Vec16<WT>::N;
+  constexpr int CW = 64 * E;
+  __shared__ uint2 lst[4][64];
+  __shared__ float red[3][64 * E];
+  const int T = h.rows;
+  const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
+  const int c = xcd + 8 * (i / T), t = i % T;
+  if (c >= nchunk) return;                                  // uniform for the workgroup
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int cap = h.n_t * h.S;
+  const uint2 *src = h.row_list + (size_t)t * cap;
+  const int e0 = 16 * wave + lane;
+  uint2 pn = (lane < 16 && e0 < cap) ? src[e0] : make_uint2(0, 0);
+  const int slot = h.ovf_slot[t];
+  if (slot >= 0) {
+    const int cn = 4 * c + wave;                            // this wave's 16-lane chunk
+    if (cn * 16 * E < d) backup_row<WT, VT, YT>(h, w2, d, y, slot, cn, lst[wave]);
+    return;
+  }
+  const int col = c * CW + lane * E;
+  const bool cv = col < d;
+  const int nnz = h.row_nnz[t];
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int base = 16 * wave; base < nnz; base += 64) {
+    const uint2 q = pn;
+    const int nb = base + 64;
+    if (nb < nnz) pn = (lane < 16 && nb + lane < nnz) ? src[nb + lane] : make_uint2(0, 0);
+    uint4 raw[16];
+    float vv[16];
+    static_for<16>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)q.x, j);
+      const float vj = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)q.y, j));
+      const bool ok = base + j < nnz;
+      vv[j] = ok ? vj : 0.f;
+      raw[j] = make_uint4(0, 0, 0, 0);
+      if (ok && cv) raw[j] = *(const uint4 *)(w2 + (size_t)ij * d + col);
+    });
+#pragma unroll
+    for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
+  }
+  if (wave > 0)
+#pragma unroll
+    for (int q = 0; q < E; ++q) red[wave - 1][lane * E + q] = acc[q];
+  __syncthreads();
+  if (wave == 0 && cv) {
+#pragma unroll
+    for (int w = 0; w < 3; ++w)
+#pragma unroll
+      for (int q = 0; q < E; ++q) acc[q] += red[w][lane * E + q];
+    const size_t o = (size_t)t * d + col;
+#pragma unroll
+    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+  }
+}
+
 // Token-count thresholds between the three decompositions (measured at d = 2048 and 4096).
 constexpr int kRows4MinT = 512, kSplitMaxT = 16;
 
@@ -343,6 +412,10 @@ static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, bool buil
   } else if (h.rows <= kSplitMaxT) {
     hipLaunchKernelGGL((k_down_split<WT, VT, YT>), dim3((unsigned)(8 * per_xcd_chunks * h.rows)), dim3(256), 0, s,
                        h, w2, d, y, nchunk);
+  } else if ((d + 64 * Vec16<WT>::N - 1) / (64 * Vec16<WT>::N) >= 8) {
+    const int nwide = (d + 64 * Vec16<WT>::N - 1) / (64 * Vec16<WT>::N);
+    hipLaunchKernelGGL((k_down_wide<WT, VT, YT>), dim3((unsigned)(8 * ((nwide + 7) / 8) * h.rows)), dim3(256), 0, s,
+                       h, w2, d, y, nwide);
   } else {
     hipLaunchKernelGGL((k_twell_down<WT, VT, YT>), dim3((unsigned)(8 * per_xcd_chunks * h.rows)), dim3(64), 0, s,
                        h, w2, d, y, nchunk);

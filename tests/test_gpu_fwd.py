@@ -201,6 +201,24 @@ def test_fwd_decode_split(T, f, W, S, seed):
         assert got["ovf_n"] > 0
 
 
+@pytest.mark.parametrize("T,d,f,W,S,dt,seed", [(100, 4160, 1024, 128, 2, "bf16", 31),
+                                                 (40, 2112, 512, 64, 2, "f32", 32),
+                                                 (200, 4096, 1024, 128, 16, "bf16", 33)])
+def test_fwd_wide_gather(T, d, f, W, S, dt, seed):
+    """Between 17 and 511 tokens with rows of at least 8 chunks of 64 lanes x 16 bytes the
+    down projection runs one (token, 1 KB-wide chunk) per workgroup. d = 4160 and 2112 end in
+    a partial chunk; S = 2 sends many rows to the dense backup (taken by the four waves as
+    16-lane chunks)."""
+    say("fwd wide gather", T, d, f, W, S, dt)
+    base = synth.C3 if dt == "bf16" else synth.C1
+    w = base.with_(d=d, f=f, tile_w=W, slots=S, seed=seed)
+    g = synth.generate(w, T=T)
+    got, flips, err = check_forward(g, W, S, T)
+    say("wide", T, d, "flips", flips, "err", err, "ovf", got["ovf_n"])
+    if S == 2:
+        assert got["ovf_n"] > 0
+
+
 def test_fwd_hot_tokens_and_capacity():
     say("fwd hot tokens")
     w = synth.C5.with_(T=600, d=512, f=2048, slots=8, hot_every=64)
