@@ -17,7 +17,8 @@ __all__ = [
     "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
     "twell_down", "twell_fwd_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense",
     "twell_gate_up", "twell_gated_ffn_fwd", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
-    "nm_prune", "ffn_up_relu_nm", "nm_ffn_down", "twell_sync_status", "F32", "BF16",
+    "nm_prune", "ffn_up_relu_nm", "nm_ffn_down", "twell_sync_status", "twell_row_max_histogram",
+    "twell_stash_bytes", "twell_choose_slots", "F32", "BF16",
 ]
 
 F32, BF16 = 0, 1
@@ -65,6 +66,9 @@ _SIGS = {
     "ffn_up_relu_nm": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "nm_ffn_down": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P], _I),
     "twell_sync_status": ([_P, _P], _I),
+    "twell_row_max_histogram": ([_P, _P, _P], _I),
+    "twell_stash_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
+    "twell_choose_slots": ([_P, _I, _I, _I, _I, _I, _P], _I),
 }
 
 _LIB = None
@@ -329,3 +333,30 @@ def nm_ffn_down(vals, idx, n: int, m: int, w2t: torch.Tensor, y_dtype=torch.floa
 def twell_sync_status(h: TwellMatrix) -> int:
     m = h.c()
     return lib().twell_sync_status(_c.byref(m), _stream(h.counts.device))
+
+
+def twell_row_max_histogram(h: TwellMatrix, hist: torch.Tensor | None = None) -> torch.Tensor:
+    """Device int32 [tile_w + 1]: rows of h by their largest per-tile true count."""
+    if hist is None:
+        hist = torch.empty((h.tile_w + 1,), dtype=torch.int32, device=h.counts.device)
+    m = h.c()
+    _check(lib().twell_row_max_histogram(_c.byref(m), _ptr(hist), _stream(h.counts.device)),
+           "twell_row_max_histogram")
+    return hist
+
+
+def twell_stash_bytes(rows: int, cols: int, tile_w: int, slots: int, n_ovf: int,
+                      val_dtype=torch.float32) -> int:
+    return lib().twell_stash_bytes(rows, cols, tile_w, slots, n_ovf, _dt(val_dtype))
+
+
+def twell_choose_slots(hist, tile_w: int, rows: int, cols: int, ovf_cap: int, val_dtype=torch.float32):
+    """(S, stash bytes) from a host copy of the histogram (numpy or CPU tensor); raises
+    TwellError (TWELL_ERR_OVF_CAPACITY) if no slot count fits ovf_cap."""
+    import numpy as np
+    hh = np.ascontiguousarray(np.asarray(hist.cpu() if hasattr(hist, "cpu") else hist), dtype=np.int32)
+    out = _c.c_size_t(0)
+    s = lib().twell_choose_slots(hh.ctypes.data_as(_c.c_void_p), tile_w, rows, cols, ovf_cap, _dt(val_dtype),
+                                 _c.byref(out))
+    _check(s if s < 0 else 0, "twell_choose_slots")
+    return s, out.value

@@ -376,6 +376,46 @@ int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, 
   return TWELL_OK;
 }
 
+int twell_row_max_histogram(const twell_matrix_t *h, int32_t *hist, void *stream) {
+  if (!hist) return TWELL_ERR_ARG;
+  int st = check_matrix(h, false);
+  if (st) return st;
+  if (!al4(hist)) return TWELL_ERR_ALIGN;
+  TW_TRY(launch_rowmax_hist(h->counts, h->rows, h->cols / h->tile_w, h->tile_w, hist, S(stream)));
+  return TWELL_OK;
+}
+
+size_t twell_stash_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots, int32_t n_ovf,
+                         int32_t val_dtype) {
+  if (rows < 0 || cols <= 0 || tile_w <= 0 || cols % tile_w || slots <= 0 || n_ovf < 0 || !dtype_ok(val_dtype))
+    return 0;
+  const size_t vb = val_dtype == TWELL_BF16 ? 2 : 4;
+  const size_t cells = (size_t)rows * (size_t)(cols / tile_w);
+  return cells * 4 + cells * (size_t)slots * (4 + vb) + (size_t)rows * 4 + (size_t)n_ovf * (4 + (size_t)cols * vb);
+}
+
+int twell_choose_slots(const int32_t *hist, int32_t tile_w, int32_t rows, int32_t cols, int32_t ovf_cap,
+                       int32_t val_dtype, size_t *stash_bytes) {
+  if (!hist || !dtype_ok(val_dtype)) return TWELL_ERR_ARG;
+  if ((tile_w != 64 && tile_w != 128) || rows < 0 || cols <= 0 || cols % tile_w || ovf_cap < 0)
+    return TWELL_ERR_SHAPE;
+  int best = TWELL_ERR_OVF_CAPACITY;
+  size_t best_bytes = 0;
+  const int smax = tile_w < 64 ? tile_w : 64;
+  for (int S = 1; S <= smax; ++S) {
+    long long n_ovf = 0;
+    for (int m = S + 1; m <= tile_w; ++m) n_ovf += hist[m];
+    if (n_ovf > ovf_cap) continue;
+    const size_t b = twell_stash_bytes(rows, cols, tile_w, S, (int32_t)n_ovf, val_dtype);
+    if (best < 0 || b < best_bytes) {
+      best = S;
+      best_bytes = b;
+    }
+  }
+  if (stash_bytes) *stash_bytes = best > 0 ? best_bytes : 0;
+  return best;
+}
+
 int twell_sync_status(const twell_matrix_t *h, void *stream) {
   if (!h || !h->ovf_n) return TWELL_ERR_ARG;
   if (hipStreamSynchronize(S(stream)) != hipSuccess) return TWELL_ERR_HIP;

@@ -58,6 +58,8 @@ hipError_t launch_ovf_scan(const uint32_t *bits, int n_t, int words, int R, int 
 hipError_t launch_ovf_copy(const void *h, int h_bf16, int R, int C, const int32_t *ovf_n, const int32_t *ovf_rows,
                            int cap, void *dense, int dense_bf16, hipStream_t s);
 hipError_t launch_set_int(int32_t *p, int v, hipStream_t s);
+// hist[0 .. W] <- histogram of the per-row maximum tile count
+hipError_t launch_rowmax_hist(const int32_t *counts, int rows, int n_t, int W, int32_t *hist, hipStream_t s);
 
 // bwd.hip
 struct BwdArgs {

@@ -133,6 +133,44 @@ hipError_t launch_ovf_copy(const void *h, int h_bf16, int R, int C, const int32_
   return hipGetLastError();
 }
 
+// Row-maximum histogram of a TwELL's true counts ("Formato Híbrido para Treinamento": the
+// compact width is chosen from the data, and rows beyond it go to the dense backup).
+// hist[m] = number of rows whose largest per-tile count is m (0 <= m <= W). A wave reduces
+// one row's n_t counts at a time; each workgroup gathers its rows in an LDS histogram and
+// adds its nonzero bins to hist with integer atomics (exact and order-free).
+__global__ __launch_bounds__(256) void k_zero_i32(int32_t *__restrict__ p, int n) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i < n) p[i] = 0;
+}
+
+__global__ __launch_bounds__(256) void k_rowmax_hist(const int32_t *__restrict__ counts, int rows, int n_t, int W,
+                                                     int32_t *__restrict__ hist) {
+  __shared__ int32_t lh[129];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i <= W; i += 256) lh[i] = 0;
+  __syncthreads();
+  for (int row = blockIdx.x * 4 + wave; row < rows; row += gridDim.x * 4) {
+    const int32_t *c = counts + (size_t)row * n_t;
+    int m = 0;
+    for (int k = lane; k < n_t; k += 64) m = max(m, c[k]);
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) m = max(m, __shfl_xor(m, o, 64));
+    if (lane == 0) atomicAdd(&lh[min(max(m, 0), W)], 1);
+  }
+  __syncthreads();
+  for (int i = tid; i <= W; i += 256)
+    if (lh[i]) atomicAdd(&hist[i], lh[i]);
+}
+
+hipError_t launch_rowmax_hist(const int32_t *counts, int rows, int n_t, int W, int32_t *hist, hipStream_t s) {
+  hipLaunchKernelGGL(k_zero_i32, dim3((W + 1 + 255) / 256), dim3(256), 0, s, hist, W + 1);
+  if (rows > 0) {
+    const int grid = min((rows + 3) / 4, 1024);
+    hipLaunchKernelGGL(k_rowmax_hist, dim3(grid), dim3(256), 0, s, counts, rows, n_t, W, hist);
+  }
+  return hipGetLastError();
+}
+
 hipError_t launch_set_int(int32_t *p, int v, hipStream_t s) {
   hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, s, p, v);
   return hipGetLastError();

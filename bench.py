@@ -403,25 +403,25 @@ def leg_c5(steps, warmup):
     dens = float(h.counts.sum().item()) / (T * f)
     # Activation memory kept for the backward ("Formato Híbrido para Treinamento"): counts,
     # slots (int32 index + fp32 value) and the fp32 backup rows of the overflow rows, against
-    # a dense h. For a per-step choice of the slot count (the dynamic N_nz of the hybrid) the
-    # same bytes are evaluated on this step's true counts for other S; the smallest stash
-    # whose overflow rows fit the backup capacity is reported.
-    n_t = f // w.tile_w
-    rowmax = h.counts.max(dim=1).values
+    # a dense h. The dynamic width of the hybrid: the library's row-maximum histogram of this
+    # step's true counts gives the overflow rows for every S, and twell_choose_slots the
+    # smallest stash whose overflow rows fit the backup capacity (the S of the next step).
     dense_bf16 = T * f * 2
-
-    def stash(S):
-        n_ovf = int((rowmax > S).sum().item())
-        return n_ovf, T * n_t * 4 + T * n_t * S * 8 + n_ovf * f * 4 + T * 4
+    hist_dev = tw.twell_row_max_histogram(h)
+    ms_hist = _time(lambda: tw.twell_row_max_histogram(h, hist_dev), steps, warmup)
+    hist = hist_dev.cpu().numpy()
     per_s = {}
     for S in (4, 6, 8, 12, 16, 24, 32):
-        n_ovf, b = stash(S)
+        n_ovf = int(hist[S + 1:].sum())
+        b = tw.twell_stash_bytes(T, f, w.tile_w, S, n_ovf)
         per_s[str(S)] = {"overflow_rows": n_ovf, "bytes": b, "frac_of_dense_bf16": b / dense_bf16}
-    fit = [int(k) for k, v in per_s.items() if v["overflow_rows"] <= cap]
-    best = min(fit, key=lambda k: per_s[str(k)]["bytes"]) if fit else None
+    best, best_bytes = tw.twell_choose_slots(hist, w.tile_w, T, f, cap)
+    stash = tw.twell_stash_bytes(T, f, w.tile_w, w.slots, ovf)
     mem = {"dense_h_bf16_bytes": dense_bf16, "dense_h_fp32_bytes": 2 * dense_bf16,
-           "stash_bytes": stash(w.slots)[1], "stash_frac_of_dense_bf16": stash(w.slots)[1] / dense_bf16,
-           "per_slots": per_s, "best_slots_within_cap": best, "cap": cap}
+           "stash_bytes": stash, "stash_frac_of_dense_bf16": stash / dense_bf16,
+           "per_slots": per_s, "chosen_slots": best, "chosen_stash_bytes": best_bytes,
+           "chosen_frac_of_dense_bf16": best_bytes / dense_bf16, "cap": cap,
+           "row_max_histogram_ms": ms_hist}
     del ws
     torch.cuda.empty_cache()
     xd = x.clone().requires_grad_(True)

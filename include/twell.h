@@ -289,6 +289,37 @@ int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, 
                 int32_t y_dtype, void *stream);
 
 /*
+ * Dynamic slot count ("Sparser, Faster, Lighter Transformer Language Models", "2. Metodologia",
+ * block "Formato Híbrido para Treinamento": the compact width follows the data; rows beyond
+ * it go to the dense backup). A training loop takes the histogram of one step's TwELL and
+ * chooses the slot count of the next.
+ *
+ * twell_row_max_histogram — hist[m] = number of rows of h whose largest per-tile true count
+ * is m, for m = 0 .. tile_w (hist: device int32 [tile_w + 1], overwritten; enqueued on
+ * `stream`). Only h's shape fields and counts are read. For any S, sum over m > S of hist[m]
+ * is the number of rows that overflow S slots.
+ */
+int twell_row_max_histogram(const twell_matrix_t *h, int32_t *hist, void *stream);
+
+/*
+ * twell_stash_bytes — bytes of a TwELL with `slots` slots and n_ovf backup rows as kept for
+ * the backward: counts and ovf_slot (int32), col_idx (int32) and vals per slot, ovf_rows
+ * (int32) and one backup row of vals per overflow row. 0 for invalid arguments.
+ */
+size_t twell_stash_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots, int32_t n_ovf,
+                         int32_t val_dtype);
+
+/*
+ * twell_choose_slots — host function; hist is a HOST copy of the histogram above. Returns the
+ * slot count S in 1 .. min(tile_w, 64) with the smallest twell_stash_bytes among those whose
+ * overflow rows fit ovf_cap (the smaller S on equal bytes), and stores its bytes in
+ * *stash_bytes (may be NULL). TWELL_ERR_OVF_CAPACITY if no S fits; TWELL_ERR_ARG /
+ * TWELL_ERR_SHAPE for invalid arguments.
+ */
+int twell_choose_slots(const int32_t *hist, int32_t tile_w, int32_t rows, int32_t cols, int32_t ovf_cap,
+                       int32_t val_dtype, size_t *stash_bytes);
+
+/*
  * twell_sync_status — waits for `stream`, then reads *ovf_n: TWELL_ERR_OVF_CAPACITY if it
  * exceeds ovf_cap, TWELL_OK otherwise (TWELL_ERR_HIP if the wait or copy fails).
  */

@@ -185,6 +185,47 @@ def twell_unpack(tw: dict) -> np.ndarray:
     return h
 
 
+def row_max_histogram(counts: np.ndarray, tile_w: int) -> np.ndarray:
+    """hist[m] = number of rows whose largest per-tile count is m, m = 0 .. tile_w.
+
+    [SFL] "Formato Híbrido para Treinamento": the compact part holds rows up to some width
+    and the rest go to the dense backup; with the per-(row, tile) layout a row fits S slots
+    iff its largest tile count is at most S, so the overflow rows for S are the rows counted
+    in hist[S + 1 ..]. Pinned against the packer's own overflow count for every S.
+    """
+    R = counts.shape[0]
+    hist = np.zeros(tile_w + 1, np.int64)
+    if R == 0:
+        return hist
+    for m in counts.max(axis=1):
+        hist[int(m)] += 1
+    return hist
+
+
+def stash_bytes(rows: int, cols: int, tile_w: int, slots: int, n_ovf: int, val_bytes: int) -> int:
+    """Bytes of the TwELL kept for the backward: counts and ovf_slot (int32 per row-tile /
+    row), one int32 index and one value per slot, and per overflow row its int32 row id and
+    a dense row of values (the layout of ``twell_pack``; pinned against its array sizes)."""
+    cells = rows * (cols // tile_w)
+    return cells * 4 + cells * slots * (4 + val_bytes) + rows * 4 + n_ovf * (4 + cols * val_bytes)
+
+
+def choose_slots(hist: np.ndarray, tile_w: int, rows: int, cols: int, ovf_cap: int, val_bytes: int):
+    """The dynamic width of the hybrid format ([SFL] "Formato Híbrido para Treinamento"),
+    read as: among S = 1 .. min(tile_w, 64) whose overflow rows fit the backup capacity,
+    take the one with the smallest stash (the smaller S on equal bytes). Returns (S, bytes)
+    or (None, None) if no S fits."""
+    best = (None, None)
+    for S in range(1, min(tile_w, 64) + 1):
+        n_ovf = int(hist[S + 1:].sum())
+        if n_ovf > ovf_cap:
+            continue
+        b = stash_bytes(rows, cols, tile_w, S, n_ovf, val_bytes)
+        if best[1] is None or b < best[1]:
+            best = (S, b)
+    return best
+
+
 # --------------------------------------------------------------------- N:M activations
 
 def nm_prune(h: np.ndarray, n: int, m: int):
