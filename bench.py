@@ -209,6 +209,7 @@ def leg_c4(steps, warmup):
     T, f, d = w.T, w.f, w.d
     out = {"dense_down_ms": _time(lambda: h @ w2, steps, warmup)}
     out["up_relu_dense_ms"] = _time(lambda: tw.ffn_up_relu_dense(x, w1t, b1, torch.bfloat16, out=h), steps, warmup)
+    out["up_relu_dense_frac_mfma_peak"] = 2.0 * T * d * f / (out["up_relu_dense_ms"] * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
     for n, m in w.nm:
         vals, idx = tw.nm_prune(h, n, m)
         ms_p = _time(lambda: tw.nm_prune(h, n, m), steps, warmup)
@@ -399,6 +400,10 @@ def leg_c5(steps, warmup):
 
     ms = _time(step, steps, warmup)
     ms_fwd = _time(lambda: tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y), steps, warmup)
+    # the up GEMM with its TwELL epilogue alone (the forward's first stage), against bf16 peak
+    ms_up = _time(lambda: tw.twell_up_gemm(x, w1t, b1, h), steps, warmup)
+    up_frac = 2.0 * T * d * f / (ms_up * 1e-3) / 1e12 / PEAK_BF16_TFLOPS
+    tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y)
     ovf = int(h.ovf_n.item())
     dens = float(h.counts.sum().item()) / (T * f)
     # Activation memory kept for the backward ("Formato Híbrido para Treinamento"): counts,
@@ -439,6 +444,7 @@ def leg_c5(steps, warmup):
     ms_dense = _time(dense_step, steps, warmup)
     return {"tokens_per_s": T / (ms * 1e-3), "ms_fwd_bwd": ms, "ms_fwd": ms_fwd, "ms_bwd": ms - ms_fwd,
             "dense_ms_fwd_bwd": ms_dense, "speedup_vs_dense": ms_dense / ms, "density": dens,
+            "up_gemm_ms": ms_up, "up_gemm_frac_mfma_peak": up_frac,
             "overflow_rows": ovf, "slots": w.slots, "tile_w": w.tile_w, "activation_memory": mem}
 
 
