@@ -1104,6 +1104,240 @@ __global__ __launch_bounds__(256) void k_up_nm_dec(const T *__restrict__ x, cons
   nm_tile<T, NK, M, TileD::BM, TileD::BN, 256>(smem, Mr, N, 0, n0, vals, idx);
 }
 
+// ------------------------------------------------------------------ decode GEMV (T <= 2, bf16)
+// With a handful of tokens the up projection is a stream of W1 with a few dot products per
+// row. The tile kernels above fetch each W1 row in 64-byte pieces per stage; here every wave
+// load is one contiguous kilobyte of a row. Lane l holds the 16-byte pieces
+//   k = k0 + 8 (64 p + l),  p = 0 .. np - 1   (np = K / 1024 per half of K)
+// of x (all tokens, in registers) and of the rows it streams. A 128-unit tile is summed in
+// two halves of K; a half runs on 8 waves of 16 units (4 rows in flight per lane). Each
+// (unit, token) partial is accumulated over the lane's pieces in order with v_dot2_f32_bf16,
+// then over the 64 lanes by a fixed xor butterfly whose lane-0 value is kept:
+//   z = half_0 + half_1.
+// k_up_gemv_twell runs the halves on two workgroups that meet in the decode workspace (the
+// second to arrive adds the other half and packs the TwELL); k_up_gemv_dense runs both halves
+// one after the other in one workgroup (no workspace) and writes h densely or N:M-pruned.
+// fp32 addition is commutative, so all of them see the same z bit for bit.
+constexpr int kGemvMaxT = 2, kGemvNP = 4, kGemvUnits = 128, kGemvWaves = 8;
+constexpr int kGemvUPW = kGemvUnits / kGemvWaves;           // units per wave
+static_assert(kGemvMaxT * kGemvUnits * 4 <= (int)kDecHalfBytes, "decode workspace");
+
+typedef __bf16 bf16x2g_t __attribute__((ext_vector_type(2)));
+TW_DEV float dot8_bf16(uint4 a, uint4 b, float c) {
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2g_t, a.x), __builtin_bit_cast(bf16x2g_t, b.x), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2g_t, a.y), __builtin_bit_cast(bf16x2g_t, b.y), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2g_t, a.z), __builtin_bit_cast(bf16x2g_t, b.z), c, false);
+  c = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2g_t, a.w), __builtin_bit_cast(bf16x2g_t, b.w), c, false);
+  return c;
+}
+
+// Half `half` of K for the 16 units of wave wv of the tile at n0: zs[u * TT + t] (u < 128,
+// t < TT) for token slot t = x row (arow ? arow[t] : t), t < rows (others are zero).
+template <int TT>
+TW_DEV void gemv_half(const uint16_t *__restrict__ x, const int32_t *__restrict__ arow, int rows,
+                      const uint16_t *__restrict__ w1t, int N, int K, int n0, int half, int wv, float *zs) {
+  const int lane = threadIdx.x & 63;
+  const int np = K / 1024;
+  const size_t k0 = (size_t)half * (K / 2) + 8 * lane;
+  // addresses are clamped into the operands (row 0, piece 0) before the predicate is applied,
+  // so no load can leave them whatever the compiler hoists
+  uint4 xr[TT][kGemvNP];
+#pragma unroll
+  for (int t = 0; t < TT; ++t) {
+    const int tr = t < rows ? t : 0;
+    const uint16_t *xp = x + (size_t)(arow ? arow[tr] : tr) * K + k0;
+#pragma unroll
+    for (int p = 0; p < kGemvNP; ++p) {
+      xr[t][p] = make_uint4(0, 0, 0, 0);
+      if (p < np) {
+        const uint4 v = *(const uint4 *)(xp + 512 * p);
+        if (t < rows) xr[t][p] = v;
+      }
+    }
+  }
+  // four groups of four units; the next group's rows are loaded before the current group is
+  // reduced (two groups in flight)
+  auto load = [&](int g, uint4 (&wr)[4][kGemvNP]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = n0 + wv * kGemvUPW + 4 * g + i;
+      const uint16_t *wp = w1t + (size_t)(u < N ? u : 0) * K + k0;
+#pragma unroll
+      for (int p = 0; p < kGemvNP; ++p) {
+        wr[i][p] = make_uint4(0, 0, 0, 0);
+        if (p < np) {
+          const uint4 v = *(const uint4 *)(wp + 512 * p);
+          if (u < N) wr[i][p] = v;
+        }
+      }
+    }
+  };
+  auto reduce = [&](int g, const uint4 (&wr)[4][kGemvNP]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        float s = 0.f;
+#pragma unroll
+        for (int p = 0; p < kGemvNP; ++p) s = dot8_bf16(xr[t][p], wr[i][p], s);
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
+        if (lane == 0) zs[(wv * kGemvUPW + 4 * g + i) * TT + t] = s;
+      }
+  };
+  static_assert(kGemvUPW == 16, "four groups of four units");
+  uint4 wa[4][kGemvNP], wb[4][kGemvNP];
+  load(0, wa);
+  load(1, wb);
+  reduce(0, wa);
+  load(2, wa);
+  reduce(1, wb);
+  load(3, wb);
+  reduce(2, wa);
+  reduce(3, wb);
+}
+
+// TwELL of the token rows t < M for the tile's units from z (LDS zs[u * TT + t]); wave t packs
+// token t. W = 128: lane l holds units 2l, 2l + 1 (one TwELL tile); W = 64: units l and 64 + l
+// (two tiles). Slot order is ascending column (ballot prefix), pads (-1, +0.0), true counts,
+// and the tile's overflow word (rows < 32) is assembled in LDS.
+template <int TT, int W, typename VT>
+TW_DEV void gemv_twell_epi(const float *zs, const float *__restrict__ b1, int M, int N, int n0, const TwellOut &o,
+                           uint32_t *ovf_flag) {
+  constexpr int Q = 128 / W;                                  // TwELL tiles of the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, t = tid >> 6;
+  const int S = o.S;
+  if (t < M) {
+#pragma unroll
+    for (int q = 0; q < Q; ++q) {
+      const int kt = n0 / W + q;
+      if (kt >= o.n_t) break;
+      constexpr int V = W / 64;                               // units per lane in this tile
+      int u[V];
+      bool on[V];
+      float v[V];
+      uint64_t m[V];
+      int cnt = 0, before = 0;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        u[e] = q * W + V * lane + e;
+        const int col = n0 + u[e];
+        const float nb = col < N ? -b1[col] : 0.f;
+        const float z = zs[u[e] * TT + t];
+        on[e] = col < N && z > nb;
+        v[e] = z - nb;
+        m[e] = ballot64(on[e]);
+        cnt += __popcll(m[e]);
+        before += mbcnt64(m[e]);
+      }
+      const size_t base = ((size_t)t * o.n_t + kt) * (size_t)S;
+      int slot = before;
+#pragma unroll
+      for (int e = 0; e < V; ++e) {
+        if (on[e]) {
+          if (slot < S) {
+            o.col_idx[base + slot] = n0 + u[e];
+            Elem<VT>::store((VT *)o.vals, base + slot, v[e]);
+          }
+          ++slot;
+        }
+      }
+      for (int s2 = min(cnt, S) + lane; s2 < S; s2 += 64) {
+        o.col_idx[base + s2] = -1;
+        Elem<VT>::store((VT *)o.vals, base + s2, 0.f);
+      }
+      if (lane == 0) {
+        o.counts[(size_t)t * o.n_t + kt] = cnt;
+        ovf_flag[q * kGemvMaxT + t] = cnt > S ? 1u : 0u;
+      }
+    }
+  }
+  __syncthreads();
+  if (tid < Q && n0 / W + tid < o.n_t) {
+    uint32_t word = 0;
+    for (int r = 0; r < M; ++r) word |= ovf_flag[tid * kGemvMaxT + r] << r;
+    o.ovf_bits[(size_t)(n0 / W + tid) * o.words] = word;
+  }
+}
+
+// Grid: 2 * ceil(N / 128) workgroups of 512 threads; workgroup b takes tile b % n_tiles and
+// half b / n_tiles of K. Workspace as k_up_twell_dec (o.dec_part, o.dec_ticket zero between
+// launches).
+template <int TT, int W, typename VT>
+__global__ __launch_bounds__(512) void k_up_gemv_twell(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w1t,
+                                                       const float *__restrict__ b1, int M, int N, int K, TwellOut o) {
+  __shared__ float zs[kGemvUnits * TT];
+  __shared__ uint32_t flag[2 * kGemvMaxT];
+  __shared__ int last;
+  const int n_tiles = (N + kGemvUnits - 1) / kGemvUnits;
+  const int tile = blockIdx.x % n_tiles, half = blockIdx.x / n_tiles;
+  const int n0 = tile * kGemvUnits, tid = threadIdx.x;
+  gemv_half<TT>(x, nullptr, M, w1t, N, K, n0, half, tid >> 6, zs);
+  __syncthreads();
+  float *part = o.dec_part + (size_t)tile * 2 * kDecTileF;
+  for (int i = tid; i < kGemvUnits * TT; i += 512)
+    __hip_atomic_store(part + half * kDecTileF + i, zs[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  wait_vmcnt<0>();
+  __syncthreads();                       // every half-sum store of this workgroup has completed
+  if (tid == 0) {
+    const uint32_t tk = __hip_atomic_fetch_add(o.dec_ticket + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last = tk != 0;
+    if (tk != 0) __hip_atomic_store(o.dec_ticket + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+  __syncthreads();
+  if (!last) return;
+  for (int i = tid; i < kGemvUnits * TT; i += 512)
+    zs[i] += __hip_atomic_load(part + (1 - half) * kDecTileF + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  __syncthreads();
+  gemv_twell_epi<TT, W, VT>(zs, b1, M, N, n0, o, flag);
+}
+
+// Both halves in one workgroup of 512 threads, then (NK == 0) out[i][col] = ReLU(z + b1) in
+// fp32 or bf16 for token slots i < rows (x row arow[i] if arow), or (NK > 0) h rounded to bf16
+// and pruned NK:MM into vals / idx ([rows][N / MM][NK]).
+template <int TT, int NK, int MM>
+__global__ __launch_bounds__(512) void k_up_gemv_dense(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w1t,
+                                                       const float *__restrict__ b1, int M, int N, int K,
+                                                       const int32_t *__restrict__ arow,
+                                                       const int32_t *__restrict__ n_rows_dev, void *out, int out_bf16,
+                                                       int relu, uint8_t *__restrict__ idx) {
+  __shared__ float zs[2][kGemvUnits * TT];
+  __shared__ __attribute__((aligned(16))) char hs[NK > 0 ? TT * (kGemvUnits * 2 + 16) : 16];
+  const int n0 = blockIdx.x * kGemvUnits, tid = threadIdx.x;
+  int rows = M;
+  if (n_rows_dev) rows = min(rows, *n_rows_dev);
+  if (rows <= 0) return;
+  gemv_half<TT>(x, arow, rows, w1t, N, K, n0, 0, tid >> 6, zs[0]);
+  gemv_half<TT>(x, arow, rows, w1t, N, K, n0, 1, tid >> 6, zs[1]);
+  __syncthreads();
+  if constexpr (NK == 0) {
+    for (int i = tid; i < kGemvUnits * TT; i += 512) {
+      const int t = i / kGemvUnits, u = i % kGemvUnits, col = n0 + u;
+      if (t >= rows || col >= N) continue;
+      float z = zs[0][u * TT + t] + zs[1][u * TT + t] + b1[col];
+      if (relu) z = z > 0.f ? z : 0.f;
+      const size_t o = (size_t)t * N + col;
+      if (out_bf16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16(z);
+      else ((float *)out)[o] = z;
+    }
+  } else {
+    constexpr int RS = kGemvUnits * 2 + 16;
+    for (int i = tid; i < kGemvUnits * TT; i += 512) {
+      const int t = i / kGemvUnits, u = i % kGemvUnits, col = n0 + u;
+      put_h<uint16_t>(hs + t * RS + u * 2, zs[0][u * TT + t] + zs[1][u * TT + t] + (col < N ? b1[col] : 0.f));
+    }
+    __syncthreads();
+    nm_tile<uint16_t, NK, MM, TT, kGemvUnits, 512>(hs, rows, N, 0, n0, (uint16_t *)out, idx);
+  }
+}
+
+// bf16, 1 or 2 tokens (at c3 sizes: 26 / 28 us against 30 us for the tile kernel; from 3 tokens
+// on the per-row dot products make it slower: 35 us at 3-4 tokens, 50 us at 8), K in
+// {1024, 2048, 4096} (K / 2 in whole kilobyte pieces per lane).
+static bool use_gemv(int bf16, int T_tokens, int K) {
+  return bf16 && T_tokens >= 1 && T_tokens <= kGemvMaxT && (K == 1024 || K == 2048 || K == 4096);
+}
+
 // The decode kernels apply to at most 64 tokens and K a multiple of four stages.
 template <typename T> static bool use_decode(int T_tokens, int K) {
   constexpr int KPT = TileD::RB / (int)sizeof(T);
@@ -1143,10 +1377,44 @@ static hipError_t launch_twell_dec(const T *x, const T *w1t, const float *b1, in
   return hipGetLastError();
 }
 
+template <int TT>
+static hipError_t launch_gemv_twell_t(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
+                                      const TwellOut &o, int W, hipStream_t s) {
+  const dim3 grid(2 * ((N + kGemvUnits - 1) / kGemvUnits)), blk(512);
+  if (o.val_bf16) {
+    if (W == 64) hipLaunchKernelGGL((k_up_gemv_twell<TT, 64, uint16_t>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
+    else hipLaunchKernelGGL((k_up_gemv_twell<TT, 128, uint16_t>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
+  } else {
+    if (W == 64) hipLaunchKernelGGL((k_up_gemv_twell<TT, 64, float>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
+    else hipLaunchKernelGGL((k_up_gemv_twell<TT, 128, float>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
+  }
+  return hipGetLastError();
+}
+
+template <int NK, int MM>
+static hipError_t launch_gemv_dense_t(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
+                                      int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out,
+                                      int out_bf16, int relu, uint8_t *idx, hipStream_t s) {
+  const dim3 grid((N + kGemvUnits - 1) / kGemvUnits), blk(512);
+  if (x_rows <= 1)
+    hipLaunchKernelGGL((k_up_gemv_dense<1, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
+  else
+    hipLaunchKernelGGL((k_up_gemv_dense<2, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
+  return hipGetLastError();
+}
+
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N,
                            int K, const TwellOut &o, int W, hipStream_t s) {
-  if ((bf16 ? use_decode<uint16_t>(M, K) : use_decode<float>(M, K)) && (!o.dec_part || !o.dec_ticket))
+  if ((bf16 ? use_decode<uint16_t>(M, K) || use_gemv(bf16, M, K) : use_decode<float>(M, K)) &&
+      (!o.dec_part || !o.dec_ticket))
     return hipErrorInvalidValue;
+  if (use_gemv(bf16, M, K)) {
+    const uint16_t *xb = (const uint16_t *)x, *wb = (const uint16_t *)w1t;
+    if (M <= 1) return launch_gemv_twell_t<1>(xb, wb, b1, M, N, K, o, W, s);
+    return launch_gemv_twell_t<2>(xb, wb, b1, M, N, K, o, W, s);
+  }
   if (bf16 && use_decode<uint16_t>(M, K))
     return launch_twell_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
   if (!bf16 && use_decode<float>(M, K))
@@ -1186,6 +1454,9 @@ static hipError_t launch_dense_dec(const T *x, const T *w1t, const float *b1, in
 hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
                            int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16,
                            int relu, hipStream_t s) {
+  if (use_gemv(bf16, x_rows, K))
+    return launch_gemv_dense_t<0, 0>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow, n_rows_dev,
+                                     out, out_bf16, relu, nullptr, s);
   if (bf16 && use_decode<uint16_t>(x_rows, K))
     return launch_dense_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
                                       n_rows_dev, out, out_bf16, relu, s);
@@ -1242,6 +1513,14 @@ hipError_t launch_up_nm(int bf16, const void *x, const void *w1t, const float *b
   if (bf16) {
     const uint16_t *xb = (const uint16_t *)x, *wb = (const uint16_t *)w1t;
     uint16_t *vb = (uint16_t *)vals;
+    if (use_gemv(bf16, M, K)) {
+      if (n == 2 && m == 4) return launch_gemv_dense_t<2, 4>(xb, wb, b1, M, N, K, M, nullptr, nullptr, vb, 1, 1, idx, s);
+      if (n == 4 && m == 8) return launch_gemv_dense_t<4, 8>(xb, wb, b1, M, N, K, M, nullptr, nullptr, vb, 1, 1, idx, s);
+      if (n == 8 && m == 16) return launch_gemv_dense_t<8, 16>(xb, wb, b1, M, N, K, M, nullptr, nullptr, vb, 1, 1, idx, s);
+      if (n == 16 && m == 32)
+        return launch_gemv_dense_t<16, 32>(xb, wb, b1, M, N, K, M, nullptr, nullptr, vb, 1, 1, idx, s);
+      return hipErrorInvalidValue;
+    }
     if (use_decode<uint16_t>(M, K)) return launch_nm_dec<uint16_t>(xb, wb, b1, M, N, K, n, m, vb, idx, s);
     if (use_large(M, N)) return launch_nm_t<uint16_t, TileL8>(xb, wb, b1, M, N, K, n, m, vb, idx, s);
     return launch_nm_t<uint16_t, TileS>(xb, wb, b1, M, N, K, n, m, vb, idx, s);

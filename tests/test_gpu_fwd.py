@@ -219,6 +219,35 @@ def test_fwd_wide_gather(T, d, f, W, S, dt, seed):
         assert got["ovf_n"] > 0
 
 
+@pytest.mark.parametrize("T,d,f,W,S,seed", [(1, 4096, 1024, 128, 16, 51), (2, 1024, 1984, 64, 2, 52),
+                                             (2, 2048, 2048, 128, 2, 53), (3, 4096, 1536, 64, 3, 54),
+                                             (1, 1024, 384, 128, 1, 55)])
+def test_fwd_decode_gemv(T, d, f, W, S, seed):
+    """For 1 or 2 tokens (bf16, d_model 1024 / 2048 / 4096) the up projection is a W1 stream: each
+    128-unit tile is summed in two halves of K on two workgroups that meet in the row_list
+    workspace. The TwELL equals the dense path's packing bit for bit (that path sums the same
+    halves in one workgroup), the tickets are zero after every call, repeated calls give the
+    same bits, and small S sends rows to the dense backup (recomputed the same way). 3 tokens
+    take the tile kernel (K in quarters)."""
+    say("fwd decode gemv", T, d, f, W, S)
+    w = synth.C3.with_(d=d, f=f, tile_w=W, slots=S, seed=seed)
+    g = synth.generate(w, T=T)
+    got, flips, err = check_forward(g, W, S, T)
+    x, w1t, b1, w2 = dev_inputs(g)
+    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, T)
+    torch.cuda.synchronize()
+    assert int(decode_tickets(h).abs().sum()) == 0
+    c1 = twell_host(h)
+    y2, _ = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, T, h=h)
+    torch.cuda.synchronize()
+    assert int(decode_tickets(h).abs().sum()) == 0
+    assert torch.equal(y1, y2)
+    assert_twell_equal(twell_host(h), c1)
+    assert_twell_equal(c1, got)
+    if S <= 2:
+        assert got["ovf_n"] > 0
+
+
 def test_fwd_hot_tokens_and_capacity():
     say("fwd hot tokens")
     w = synth.C5.with_(T=600, d=512, f=2048, slots=8, hot_every=64)
