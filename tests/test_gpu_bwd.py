@@ -131,3 +131,66 @@ def test_bwd_workspace_too_small():
                                 dy.data_ptr(), 0.0, *[o.data_ptr() for o in out], ws.data_ptr(), 4096, None)
     assert st == -4
     torch.cuda.synchronize()
+
+
+def test_c5_full_sampled():
+    """c5 at full size in the bench's launch configuration (T=16384, d=4096, f=14336, bf16,
+    W=128, S=8, backup capacity 1024, fp32 values, l1 2e-5), checked on samples:
+      - the TwELL rows of 12 random tokens and 4 overflow rows equal the oracle's packing of
+        the GPU's own activations bit for bit (overflow rows: backup slot holds the full row);
+      - those activations are within the fp32 error bound of the oracle's, pattern flips only
+        where |z| <= bound; y and dx of those rows against the oracle;
+      - dW1t, dW2 and db1 of 8 random and the 4 most active units over all 16384 tokens. The
+        units separate in the backward, so the oracle's own backward runs on the sampled units'
+        weights with every token and the GPU's pattern."""
+    say("c5 full sampled")
+    w = synth.C5
+    g = synth.generate(w)
+    dt, W, S, cap, lam = "bf16", w.tile_w, w.slots, 1024, w.l1_coef
+    x, w1t, w2, dy = (to_dev(g[k], dt) for k in ("x", "w1t", "w2", "dy"))
+    b1 = to_dev(g["b1"], "f32")
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, cap)
+    dx, dw1t, dw2, db1 = tw.twell_ffn_bwd(x, w1t, w2, h, dy, lam)
+    hz = tw.ffn_up_relu_dense(x, w1t, b1, torch.float32)
+    torch.cuda.synchronize()
+    assert tw.twell_sync_status(h) == 0
+    n_ovf = int(h.ovf_n.item())
+    assert n_ovf > 0
+    rng = np.random.default_rng(7)
+    ovf = from_dev(h.ovf_rows)[:n_ovf]
+    rows = np.unique(np.concatenate([rng.choice(w.T, 12, replace=False), ovf[:4]]))
+    rt = torch.from_numpy(rows).cuda()
+    hs = from_dev(hz[rt])
+    want = orc.twell_pack(hs, W, S, len(rows))
+    assert np.array_equal(from_dev(h.counts[rt]), want["counts"])
+    assert np.array_equal(from_dev(h.col_idx[rt]), want["col_idx"])
+    assert np.array_equal(from_dev(h.vals[rt]), want["vals"])
+    slot = from_dev(h.ovf_slot[rt])
+    assert np.array_equal(slot >= 0, np.isin(rows, ovf))
+    for i in np.flatnonzero(slot >= 0):
+        assert np.array_equal(from_dev(h.ovf_dense[int(slot[i])]), hs[i])
+    say("c5 full: TwELL rows exact")
+    x64, w1r, w2r, dy64 = (orc.widen(g[k], dt) for k in ("x", "w1t", "w2", "dy"))
+    b1r = g["b1"].astype(np.float64)
+    z = orc.preact(x64[rows], w1r, b1r)
+    beta = orc.z_error_bound(x64[rows], w1r, b1r)
+    assert np.all(np.abs(hs - orc.relu(z)) <= beta)
+    flip = (hs > 0) != (z > 0)
+    assert np.all(np.abs(z[flip]) <= beta[flip])
+    e_y = rel_err(from_dev(y[rt]), orc.relu(z) @ w2r)
+    assert e_y <= TOL["bf16"], e_y
+    ref_r = orc.ffn_bwd(x64[rows], w1r, w2r, dy64[rows], lam, hs)
+    e_dx = rel_err(from_dev(dx[rt]), ref_r["dx"])
+    assert e_dx <= TOL["bf16"], e_dx
+    active = (hz > 0).sum(dim=0)
+    top = torch.topk(active, 4).indices.cpu().numpy()
+    units = np.unique(np.concatenate([rng.choice(w.f, 8, replace=False), top]))
+    ut = torch.from_numpy(units).cuda()
+    hu = from_dev(hz[:, ut])
+    ref_u = orc.ffn_bwd(x64, w1r[units], w2r[units], dy64, lam, hu)
+    e_w1 = rel_err(from_dev(dw1t[ut]), ref_u["dw1t"])
+    e_w2 = rel_err(from_dev(dw2[ut]), ref_u["dw2"])
+    e_b = rel_err(from_dev(db1[ut]), ref_u["db1"])
+    say("c5 full errs: y", e_y, "dx", e_dx, "dw1t", e_w1, "dw2", e_w2, "db1", e_b, "flips", int(flip.sum()),
+        "overflow rows", n_ovf)
+    assert max(e_w1, e_w2, e_b) <= TOL["bf16"]
