@@ -100,3 +100,30 @@ def test_gated_stages_equal_one_call():
     y2 = tw.twell_fwd_down(h, w2)
     torch.cuda.synchronize()
     assert torch.equal(y1, y2)
+
+
+def test_gated_c2_full_sampled():
+    """The gated layer at the c2 size as the bench runs it (T=4096, d=2048, f=8192, bf16,
+    W=128, S=16, backup capacity 16): the gate's TwELL rows of 16 sampled tokens equal the
+    oracle's packing of the GPU's gate activations bit for bit, and y of those rows is within
+    tolerance of the oracle's gated layer."""
+    say("gated c2 full sampled")
+    w = synth.C2
+    g, wut_bits = gated_case(w)
+    x, wgt, w2 = (to_dev(g[k], "bf16") for k in ("x", "w1t", "w2"))
+    bg, wut = to_dev(g["b1"], "f32"), to_dev(wut_bits, "bf16")
+    y, h = tw.twell_gated_ffn_fwd(x, wgt, bg, wut, w2, w.tile_w, w.slots, 16)
+    hz = tw.ffn_up_relu_dense(x, wgt, bg, torch.float32)
+    torch.cuda.synchronize()
+    rows = np.sort(np.random.default_rng(13).choice(w.T, 16, replace=False))
+    rt = torch.from_numpy(rows).cuda()
+    hs = from_dev(hz[rt])
+    want = orc.twell_pack(hs, w.tile_w, w.slots, len(rows))
+    assert np.array_equal(from_dev(h.counts[rt]), want["counts"])
+    assert np.array_equal(from_dev(h.col_idx[rt]), want["col_idx"])
+    xr = orc.widen(g["x"][rows], "bf16")
+    y_ref = orc.gated_ffn_fwd(xr, orc.widen(g["w1t"], "bf16"), g["b1"].astype(np.float64),
+                              orc.widen(wut_bits, "bf16"), orc.widen(g["w2"], "bf16"))[4]
+    err = rel_err(from_dev(y[rt]), y_ref)
+    say("gated c2 full err", err)
+    assert err <= TOL["bf16"], err

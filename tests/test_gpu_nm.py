@@ -115,3 +115,27 @@ def test_nm_rejects():
     with pytest.raises(tw.TwellError) as e:
         tw.nm_ffn_down(v, i, 2, 4, torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == -7
+
+
+def test_nm_down_c4_full_sampled():
+    """c4 at full size as the bench runs it (T=4096, d=4096, f=14336, bf16, b1 = 0): N:M from
+    the up GEMM's epilogue, then the packed down projection; 16 sampled rows of y against the
+    oracle's product of the unpacked N:M activations with W2 (the pruned entries are checked
+    bit-exact against the oracle by the up + N:M tests)."""
+    say("nm_down c4 full sampled")
+    w = synth.C4
+    g = synth.generate(w)
+    x, w1t, w2 = (to_dev(g[k], "bf16") for k in ("x", "w1t", "w2"))
+    b1 = to_dev(g["b1"], "f32")
+    w2t = w2.t().contiguous()
+    rows = np.sort(np.random.default_rng(11).choice(w.T, 16, replace=False))
+    rt = torch.from_numpy(rows).cuda()
+    w2r = orc.widen(g["w2"], "bf16")
+    for n, m in w.nm:
+        vals, idx = tw.ffn_up_relu_nm(x, w1t, b1, n, m)
+        y = tw.nm_ffn_down(vals, idx, n, m, w2t)
+        torch.cuda.synchronize()
+        ref = orc.nm_unpack(from_dev(vals[rt]), from_dev(idx[rt]), m) @ w2r
+        err = rel_err(from_dev(y[rt]), ref)
+        say("nm_down c4", n, m, "err", err)
+        assert err <= 2e-3
