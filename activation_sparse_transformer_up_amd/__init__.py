@@ -16,7 +16,8 @@ import torch
 __all__ = [
     "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
     "twell_down", "twell_fwd_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense",
-    "twell_gate_up", "twell_gated_ffn_fwd", "twell_ffn_bwd", "twell_ffn_bwd_workspace_bytes",
+    "twell_gate_up", "twell_gated_ffn_fwd", "twell_gate_up_workspace_bytes", "twell_ffn_bwd",
+    "twell_ffn_bwd_workspace_bytes",
     "nm_prune", "ffn_up_relu_nm", "nm_ffn_down", "twell_sync_status", "twell_row_max_histogram",
     "twell_stash_bytes", "twell_choose_slots", "F32", "BF16",
 ]
@@ -58,8 +59,9 @@ _SIGS = {
     "twell_up_gemm": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "twell_up_finish": ([_P, _P, _P, _I, _I, _I, _I, _P, _P], _I),
     "ffn_up_relu_dense": ([_P, _P, _P, _I, _I, _I, _I, _P, _I, _P], _I),
-    "twell_gate_up": ([_P, _P, _P, _I, _I, _I, _I, _P], _I),
-    "twell_gated_ffn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
+    "twell_gate_up_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
+    "twell_gate_up": ([_P, _P, _P, _I, _I, _I, _I, _P, _Z, _P], _I),
+    "twell_gated_ffn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _Z, _P], _I),
     "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
     "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
     "nm_prune": ([_P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
@@ -192,11 +194,24 @@ def twell_ffn_fwd(x, w1t, b1, w2, tile_w: int, slots: int, ovf_cap: int,
     return y, h
 
 
+def twell_gate_up_workspace_bytes(T: int, d: int, f: int, h: TwellMatrix, dtype=torch.bfloat16) -> int:
+    m = h.c()
+    return lib().twell_gate_up_workspace_bytes(T, d, f, _dt(dtype), _c.byref(m))
+
+
+def _gate_ws(T, d, f, h, dtype, device, workspace):
+    need = twell_gate_up_workspace_bytes(T, d, f, h, dtype)
+    if need and (workspace is None or workspace.numel() < need):
+        workspace = torch.empty((need,), dtype=torch.uint8, device=device)
+    return workspace
+
+
 def twell_gated_ffn_fwd(x, wgt, bg, wut, w2, tile_w: int, slots: int, ovf_cap: int,
                         val_dtype=torch.float32, y_dtype=torch.float32, h: TwellMatrix | None = None,
-                        y: torch.Tensor | None = None):
+                        y: torch.Tensor | None = None, workspace: torch.Tensor | None = None):
     """y = (ReLU(x wgt^T + bg) * (x wut^T)) w2 with the gate activations packed in TwELL.
-    Returns (y, h); h's slots hold the gate, its row lists the gated products."""
+    Returns (y, h); h's slots hold the gate, its row lists the gated products. From 512 tokens
+    on the up stage needs a workspace (allocated here unless a large enough one is given)."""
     T, d = x.shape
     f = wgt.shape[0]
     if wgt.dtype != x.dtype or wut.dtype != x.dtype or w2.dtype != x.dtype:
@@ -207,18 +222,23 @@ def twell_gated_ffn_fwd(x, wgt, bg, wut, w2, tile_w: int, slots: int, ovf_cap: i
         h = TwellMatrix(T, f, tile_w, slots, ovf_cap, val_dtype, x.device)
     if y is None:
         y = torch.empty((T, d), dtype=y_dtype, device=x.device)
+    workspace = _gate_ws(T, d, f, h, x.dtype, x.device, workspace)
     m = h.c()
     _check(lib().twell_gated_ffn_fwd(_ptr(x), _ptr(wgt), _ptr(bg), _ptr(wut), _ptr(w2), _dt(x.dtype), T, d, f,
-                                     _c.byref(m), _ptr(y), _dt(y.dtype), _stream(x.device)), "twell_gated_ffn_fwd")
+                                     _c.byref(m), _ptr(y), _dt(y.dtype), _ptr(workspace),
+                                     workspace.numel() if workspace is not None else 0, _stream(x.device)),
+           "twell_gated_ffn_fwd")
     return y, h
 
 
-def twell_gate_up(h: TwellMatrix, x, wut) -> TwellMatrix:
+def twell_gate_up(h: TwellMatrix, x, wut, workspace: torch.Tensor | None = None) -> TwellMatrix:
     """The up stage of the gated forward: row-list and backup values g <- g * (x[t] . wut[j])."""
     T, d = x.shape
+    workspace = _gate_ws(T, d, wut.shape[0], h, x.dtype, x.device, workspace)
     m = h.c()
-    _check(lib().twell_gate_up(_c.byref(m), _ptr(x), _ptr(wut), _dt(x.dtype), T, d, wut.shape[0],
-                               _stream(x.device)), "twell_gate_up")
+    _check(lib().twell_gate_up(_c.byref(m), _ptr(x), _ptr(wut), _dt(x.dtype), T, d, wut.shape[0], _ptr(workspace),
+                               workspace.numel() if workspace is not None else 0, _stream(x.device)),
+           "twell_gate_up")
     return h
 
 

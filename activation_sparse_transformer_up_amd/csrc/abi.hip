@@ -249,22 +249,42 @@ int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t
   return TWELL_OK;
 }
 
+size_t twell_gate_up_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, int32_t in_dtype,
+                                     const twell_matrix_t *h) {
+  if (!h || T < 0 || d_model <= 0 || d_ff <= 0 || h->tile_w <= 0 || h->slots <= 0) return 0;
+  if (!dtype_ok(in_dtype)) return 0;
+  return gate_up_workspace_bytes(T, d_model, d_ff / h->tile_w, h->slots, in_dtype == TWELL_BF16);
+}
+
+// The workspace the up products need for this h (checked before anything is enqueued).
+static int gate_ws_check(const twell_matrix_t *h, int32_t in_dtype, int32_t d_model, const void *ws,
+                         size_t ws_bytes) {
+  const size_t need = gate_up_workspace_bytes(h->rows, d_model, h->cols / h->tile_w, h->slots, in_dtype == TWELL_BF16);
+  if (need == 0) return TWELL_OK;
+  if (!ws || ws_bytes < need) return TWELL_ERR_WORKSPACE;
+  if (!al16(ws)) return TWELL_ERR_ALIGN;
+  return TWELL_OK;
+}
+
 int twell_gate_up(twell_matrix_t *h, const void *x, const void *w_up_t, int32_t in_dtype, int32_t T,
-                  int32_t d_model, int32_t d_ff, void *stream) {
+                  int32_t d_model, int32_t d_ff, void *workspace, size_t workspace_bytes, void *stream) {
   if (!h) return TWELL_ERR_ARG;
   int st = check_ffn_args(x, w_up_t, nullptr, in_dtype, T, d_model, d_ff);
   if (st) return st;
   st = check_matrix(h, false, true);
   if (st) return st;
   if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
+  st = gate_ws_check(h, in_dtype, d_model, workspace, workspace_bytes);
+  if (st) return st;
   if (T == 0) return TWELL_OK;
-  TW_TRY(launch_gate_up(in_of(h), x, w_up_t, in_dtype == TWELL_BF16, d_model, S(stream)));
+  TW_TRY(launch_gate_up(in_of(h), x, w_up_t, in_dtype == TWELL_BF16, d_model, (float *)workspace, S(stream)));
   return TWELL_OK;
 }
 
 int twell_gated_ffn_fwd(const void *x, const void *w_gate_t, const float *b_gate, const void *w_up_t,
                         const void *w2, int32_t in_dtype, int32_t T, int32_t d_model, int32_t d_ff,
-                        twell_matrix_t *h, void *y, int32_t y_dtype, void *stream) {
+                        twell_matrix_t *h, void *y, int32_t y_dtype, void *workspace, size_t workspace_bytes,
+                        void *stream) {
   if (!w2 || !w_up_t || (T > 0 && !y)) return TWELL_ERR_ARG;
   if (!dtype_ok(y_dtype)) return TWELL_ERR_ARG;
   int st = check_up_args(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h);
@@ -272,12 +292,14 @@ int twell_gated_ffn_fwd(const void *x, const void *w_gate_t, const float *b_gate
   st = check_matrix(h, true, true);
   if (st) return st;
   if (!al16(w2) || !al16(y) || !al16(w_up_t)) return TWELL_ERR_ALIGN;
+  st = gate_ws_check(h, in_dtype, d_model, workspace, workspace_bytes);
+  if (st) return st;
   hipStream_t s = S(stream);
   st = up_gemm(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h, s);
   if (st) return st;
   st = up_finish(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h, s);
   if (st || T == 0) return st;
-  TW_TRY(launch_gate_up(in_of(h), x, w_up_t, in_dtype == TWELL_BF16, d_model, s));
+  TW_TRY(launch_gate_up(in_of(h), x, w_up_t, in_dtype == TWELL_BF16, d_model, (float *)workspace, s));
   TW_TRY(launch_twell_down(in_of(h), w2, in_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, false, s));
   return TWELL_OK;
 }

@@ -164,23 +164,6 @@ TW_DEV float dot16(const uint4 &x, const uint4 &y) {
   return acc;
 }
 
-// v[0..16) of the 16 lanes of a group summed across the group, one sum per lane: at step m
-// (8, 4, 2, 1) a lane keeps the half of its remaining values selected by bit m of its lane
-// index and adds the partner's (lane ^ m) copy of that half. Lane l ends with entry l.
-TW_DEV float group16_transpose_sum(float (&v)[16], int gl) {
-  static_for<4>([&](auto S) {
-    constexpr int m = 8 >> decltype(S)::value, half = m;   // values left: 2 * m
-    const bool hi = gl & m;
-    static_for<half>([&](auto K) {
-      constexpr int k = decltype(K)::value;
-      const float keep = hi ? v[k + half] : v[k];
-      const float send = hi ? v[k] : v[k + half];
-      v[k] = keep + __shfl_xor(send, m, 64);
-    });
-  });
-  return v[0];
-}
-
 // part[c][e] = dy[t][chunk c] . w2[col[e]][chunk c] for the entries e of token t. Block b
 // runs on XCD b % 8 with chunk b % 8 + 8 * ((b / 8) / ntb) and token block (b / 8) % ntb of
 // 16 tokens (taken in the order perm), one per 16-lane group; lane l holds 16 bytes of

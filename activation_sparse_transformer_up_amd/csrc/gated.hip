@@ -9,12 +9,18 @@
 // (j, g) of a token's row list g <- g * (x[t] . w_up[j]), and the same for every nonzero
 // of a dense backup row. The gather then sums (g u)_j w2[j].
 //
-// A wave takes ENT list entries at a time. Lane l holds 16-byte pieces l, l + 64, ... of
-// x[t] (8 bf16 or 4 fp32 per piece), loads the same pieces of the ENT up rows before any
-// arithmetic, and accumulates with v_dot2_f32_bf16 (bf16; two products per instruction,
-// fp32 accumulation) or fp32 FMAs; the ENT sums are reduced across the wave and lane 0
-// rewrites the entries' values.
+// Few tokens (k_gate_dot): a wave takes ENT list entries at a time. Lane l holds 16-byte
+// pieces l, l + 64, ... of x[t] (8 bf16 or 4 fp32 per piece), loads the same pieces of the
+// ENT up rows before any arithmetic, and accumulates with v_dot2_f32_bf16 (bf16; two products
+// per instruction, fp32 accumulation) or fp32 FMAs; the ENT sums are reduced across the wave
+// and lane 0 rewrites the entries' values.
+// Many tokens (k_gate_part + k_gate_sum): the products of all tokens read the whole of w_up
+// from every XCD, so each XCD would fetch it from the shared last-level cache. As in the
+// backward's SDDMM, the dot products are cut into 16-lane column chunks instead: chunk c runs
+// on XCD c % 8, whose L2 then holds only its slices of w_up and x, and writes one partial per
+// (entry, chunk) to the workspace; a second kernel adds the partials in chunk order.
 #include "common.h"
+#include "gather.h"
 #include "launch.h"
 
 namespace tw {
@@ -126,8 +132,107 @@ __global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__
   }
 }
 
-hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int bf16, int d, hipStream_t s) {
+// part[c][t][e] = x[t][chunk c] . wu[col][chunk c] for the entries e of token t's row list
+// (normal rows; a backup row has row_nnz < 0 and is done by k_gate_dot_backup). Block b runs on
+// XCD b % 8 with chunk b % 8 + 8 * ((b / 8) / ntb) and token block (b / 8) % ntb of 16
+// tokens, one per 16-lane group; lane l holds 16 bytes of x[t]. Per round the group loads its
+// next 16 pairs (coalesced), broadcasts the columns, issues the 16 up-row loads, and sums the
+// 16 per-lane dot products across the group so that lane l stores entry l.
+template <typename XT>
+__global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk, int ntb, const XT *__restrict__ x,
+                                                   const XT *__restrict__ wu, float *__restrict__ part) {
+  constexpr int E = Vec16<XT>::N;
+  constexpr int CW = 16 * E;
+  const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
+  const int c = xcd + 8 * (i / ntb), tb = i % ntb;
+  if (c >= nchunk) return;
+  const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
+  const int t = tb * 16 + (threadIdx.x >> 6) * 4 + g;
+  const int colo = c * CW + gl * E;
+  const bool cv = colo < d;
+  const size_t cap = (size_t)h.n_t * h.S;
+  int n = t < h.rows ? h.row_nnz[t] : 0;
+  if (n < 0) n = 0;
+  int nw = max(n, __shfl_xor(n, 16, 64));
+  nw = max(nw, __shfl_xor(nw, 32, 64));
+  const int tt = t < h.rows ? t : 0;
+  const uint4 a = (t < h.rows && cv) ? *(const uint4 *)(x + (size_t)tt * d + colo) : make_uint4(0, 0, 0, 0);
+  const uint2 *lp = h.row_list + (size_t)tt * cap;
+  float *out = part + ((size_t)c * h.rows + tt) * cap;
+  int jn = gl < n ? (int)lp[gl].x : 0;
+  for (int base = 0; base < nw; base += 16) {
+    const int jq = jn;
+    if (base + 16 < nw) jn = base + 16 + gl < n ? (int)lp[base + 16 + gl].x : 0;
+    uint4 raw[16];
+    static_for<16>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      const uint32_t jj = row_bcast<j>((uint32_t)jq);
+      raw[j] = make_uint4(0, 0, 0, 0);
+      if (base + j < n && cv) raw[j] = *(const uint4 *)(wu + (size_t)jj * d + colo);
+    });
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = dot16<XT>(a, raw[j], 0.f);
+    const float tot = group16_transpose_sum(v, gl);
+    if (base + gl < n) out[base + gl] = tot;
+  }
+}
+
+// Row list entry e of token t: g <- g * (sum over chunks c of part[c][t][e], in chunk order).
+// One wave per token, lanes over the entries.
+__global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const float *__restrict__ part) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= h.rows) return;
+  const int n = h.row_nnz[t];
+  const size_t cap = (size_t)h.n_t * h.S, plane = (size_t)h.rows * cap;
+  uint2 *lp = h.row_list + (size_t)t * cap;
+  const float *pp = part + (size_t)t * cap;
+  for (int e = lane_id(); e < n; e += 64) {
+    float u = 0.f;
+    for (int c = 0; c < nchunk; ++c) u += pp[c * plane + e];
+    const uint2 q = lp[e];
+    lp[e].y = __float_as_uint(__uint_as_float(q.y) * u);
+  }
+}
+
+static int gate_chunks(int d, int bf16) {
+  const int cw = bf16 ? 128 : 64;
+  return (d + cw - 1) / cw;
+}
+
+size_t gate_up_workspace_bytes(int T, int d, int n_t, int S, int bf16) {
+  if (T < kGateChunkMinT) return 0;
+  return (size_t)gate_chunks(d, bf16) * (size_t)T * (size_t)n_t * (size_t)S * 4;
+}
+
+hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int bf16, int d, float *ws,
+                          hipStream_t s) {
   if (h.rows == 0) return hipSuccess;
+  if (h.rows >= kGateChunkMinT) {
+    if (!ws) return hipErrorInvalidValue;
+    const int nchunk = gate_chunks(d, bf16);
+    const int ntb = (h.rows + 15) / 16;
+    const dim3 grid((unsigned)(8 * (size_t)ntb * ((nchunk + 7) / 8))), rows4((h.rows + 3) / 4);
+    const size_t nb = (size_t)h.cap * ((h.cols + 63) / 64);
+    const dim3 gridb((unsigned)((nb + 3) / 4));
+    if (bf16) {
+      const uint16_t *xx = (const uint16_t *)x, *ww = (const uint16_t *)wu;
+      hipLaunchKernelGGL((k_gate_part<uint16_t>), grid, dim3(256), 0, s, h, d, nchunk, ntb, xx, ww, ws);
+      if (nb) {
+        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
+        else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d);
+      }
+    } else {
+      const float *xx = (const float *)x, *ww = (const float *)wu;
+      hipLaunchKernelGGL((k_gate_part<float>), grid, dim3(256), 0, s, h, d, nchunk, ntb, xx, ww, ws);
+      if (nb) {
+        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
+        else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d);
+      }
+    }
+    hipLaunchKernelGGL(k_gate_sum, rows4, dim3(256), 0, s, h, nchunk, ws);
+    return hipGetLastError();
+  }
   // enough workgroups to keep every CU busy at few tokens, without more entry groups per
   // token than a full list has
   const int groups = (h.n_t * h.S + 4 * kGateEnt - 1) / (4 * kGateEnt);

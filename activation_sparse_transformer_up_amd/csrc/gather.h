@@ -72,6 +72,23 @@ TW_DEV float gather_list16(const uint2 *__restrict__ p, int n, int nw, const WT 
   return vs;
 }
 
+// v[0..16) of the 16 lanes of a group summed across the group, one sum per lane: at step m
+// (8, 4, 2, 1) a lane keeps the half of its remaining values selected by bit m of its lane
+// index and adds the partner's (lane ^ m) copy of that half. Lane l ends with entry l.
+TW_DEV float group16_transpose_sum(float (&v)[16], int gl) {
+  static_for<4>([&](auto S) {
+    constexpr int m = 8 >> decltype(S)::value, half = m;   // values left: 2 * m
+    const bool hi = gl & m;
+    static_for<half>([&](auto K) {
+      constexpr int k = decltype(K)::value;
+      const float keep = hi ? v[k + half] : v[k];
+      const float send = hi ? v[k] : v[k + half];
+      v[k] = keep + __shfl_xor(send, m, 64);
+    });
+  });
+  return v[0];
+}
+
 // Sum over the 16 lanes of a group.
 TW_DEV float group16_sum(float v) {
   v += __shfl_xor(v, 1, 64);

@@ -74,7 +74,12 @@ size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf1
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 
 // gated.hip
-hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int bf16, int d, hipStream_t s);
+// From kGateChunkMinT tokens on the up products are chunked per XCD and need a workspace of
+// gate_up_workspace_bytes (0 below that size).
+constexpr int kGateChunkMinT = 512;
+size_t gate_up_workspace_bytes(int T, int d, int n_t, int S, int bf16);
+hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int bf16, int d, float *ws,
+                          hipStream_t s);
 
 // nm.hip
 hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, void *vals, uint8_t *idx,

@@ -294,8 +294,10 @@ def leg_gated(steps, warmup):
             x = x_all[:T].contiguous()
             h = tw.TwellMatrix(T, w.f, w.tile_w, w.slots, 16, torch.float32, dev)
             y = torch.empty((T, w.d), dtype=torch.float32, device=dev)
-            ms = _time(lambda: tw.twell_gated_ffn_fwd(x, wgt, bg, wut, w2, w.tile_w, w.slots, 16, h=h, y=y),
-                       steps, warmup)
+            ws = torch.empty((max(tw.twell_gate_up_workspace_bytes(T, w.d, w.f, h), 16),), dtype=torch.uint8,
+                             device=dev)
+            ms = _time(lambda: tw.twell_gated_ffn_fwd(x, wgt, bg, wut, w2, w.tile_w, w.slots, 16, h=h, y=y,
+                                                      workspace=ws), steps, warmup)
             ms_plain = _time(lambda: tw.twell_ffn_fwd(x, wgt, bg, w2, w.tile_w, w.slots, 16, h=h, y=y),
                              steps, warmup)
 

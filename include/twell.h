@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 2
+#define TWELL_ABI_VERSION 3
 
 typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype_t;
 
@@ -196,19 +196,28 @@ int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t
  * gate GEMM built the lists); then twell_fwd_down yields y. The TwELL slots (counts,
  * col_idx, vals) keep the gate; row_list values and ovf_dense rows hold g * u afterwards.
  * x [T][d_model] and w_up_t [d_ff][d_model] in in_dtype, 16-byte aligned; d_model a
- * multiple of 8. Errors as twell_ffn_fwd.
+ * multiple of 8. From 512 tokens on, the dot products of the row lists are cut into
+ * per-XCD column chunks whose partial sums go to `workspace` (device, caller-owned, 16-byte
+ * aligned, at least twell_gate_up_workspace_bytes; contents need not be initialised);
+ * below 512 tokens no workspace is used (it may be NULL). Too small a workspace gives
+ * TWELL_ERR_WORKSPACE before anything is enqueued; other errors as twell_ffn_fwd.
  */
+size_t twell_gate_up_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, int32_t in_dtype,
+                                     const twell_matrix_t *h);
 int twell_gate_up(twell_matrix_t *h, const void *x, const void *w_up_t, int32_t in_dtype,
-                  int32_t T, int32_t d_model, int32_t d_ff, void *stream);
+                  int32_t T, int32_t d_model, int32_t d_ff, void *workspace, size_t workspace_bytes,
+                  void *stream);
 
 /*
  * twell_gated_ffn_fwd — the whole gated forward: twell_up_gemm and twell_up_finish on the
- * gate weights (w_gate_t, b_gate), twell_gate_up with w_up_t, then twell_fwd_down with w2,
- * in that order on the stream. Arguments, checks and errors as twell_ffn_fwd plus w_up_t.
+ * gate weights (w_gate_t, b_gate), twell_gate_up with w_up_t (and the workspace), then
+ * twell_fwd_down with w2, in that order on the stream. Arguments, checks and errors as
+ * twell_ffn_fwd plus w_up_t and the workspace of twell_gate_up.
  */
 int twell_gated_ffn_fwd(const void *x, const void *w_gate_t, const float *b_gate, const void *w_up_t,
                         const void *w2, int32_t in_dtype, int32_t T, int32_t d_model, int32_t d_ff,
-                        twell_matrix_t *h, void *y, int32_t y_dtype, void *stream);
+                        twell_matrix_t *h, void *y, int32_t y_dtype, void *workspace,
+                        size_t workspace_bytes, void *stream);
 
 /*
  * ffn_up_relu_dense — h = ReLU(x . W1 + b1) written densely ([T][d_ff], h_dtype = fp32 or

@@ -13,7 +13,7 @@ HEADER = os.path.join(ROOT, "include", "twell.h")
 
 import activation_sparse_transformer_up_amd as tw  # noqa: E402
 
-ARG, SHAPE, ALIGN, UNSUP = -1, -2, -3, -7
+ARG, SHAPE, ALIGN, WS, UNSUP = -1, -2, -3, -4, -7
 
 
 def declared_functions():
@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tw.twell_abi_version() == 2
+    assert tw.twell_abi_version() == 3
     L = tw.lib()
     for code in [0, -1, -2, -3, -4, -5, -6, -7]:
         s = L.twell_status_str(code).decode()
@@ -134,30 +134,41 @@ def test_pack_and_down_reject():
 def test_gated_entry_points_reject():
     L = tw.lib()
     m = mat()
-    # twell_gate_up(h, x, w_up_t, dtype, T, d, f, stream)
-    assert L.twell_gate_up(None, FAKE, FAKE, 1, 64, 256, 512, None) == ARG
-    assert L.twell_gate_up(ctypes.byref(m), FAKE, None, 1, 64, 256, 512, None) == ARG
-    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 7, 64, 256, 512, None) == ARG
-    assert L.twell_gate_up(ctypes.byref(m), MIS, FAKE, 1, 64, 256, 512, None) == ALIGN
-    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 64, 100, 512, None) == ALIGN
-    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 32, 256, 512, None) == SHAPE
-    assert L.twell_gate_up(ctypes.byref(mat(row_list=None)), FAKE, FAKE, 1, 64, 256, 512, None) == ARG
+    # twell_gate_up(h, x, w_up_t, dtype, T, d, f, workspace, workspace_bytes, stream)
+    assert L.twell_gate_up(None, FAKE, FAKE, 1, 64, 256, 512, None, 0, None) == ARG
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, None, 1, 64, 256, 512, None, 0, None) == ARG
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 7, 64, 256, 512, None, 0, None) == ARG
+    assert L.twell_gate_up(ctypes.byref(m), MIS, FAKE, 1, 64, 256, 512, None, 0, None) == ALIGN
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 64, 100, 512, None, 0, None) == ALIGN
+    assert L.twell_gate_up(ctypes.byref(m), FAKE, FAKE, 1, 32, 256, 512, None, 0, None) == SHAPE
+    assert L.twell_gate_up(ctypes.byref(mat(row_list=None)), FAKE, FAKE, 1, 64, 256, 512, None, 0, None) == ARG
+    # from 512 tokens on the up products need the workspace (16 column chunks x 512 x 4 x 8 floats)
+    big = mat(rows=512)
+    need = L.twell_gate_up_workspace_bytes(512, 2048, 512, 1, ctypes.byref(big))
+    assert need == 16 * 512 * 4 * 8 * 4
+    assert L.twell_gate_up_workspace_bytes(511, 2048, 512, 1, ctypes.byref(mat(rows=511))) == 0
+    assert L.twell_gate_up(ctypes.byref(big), FAKE, FAKE, 1, 512, 2048, 512, None, 0, None) == WS
+    assert L.twell_gate_up(ctypes.byref(big), FAKE, FAKE, 1, 512, 2048, 512, FAKE, need - 16, None) == WS
+    assert L.twell_gate_up(ctypes.byref(big), FAKE, FAKE, 1, 512, 2048, 512, MIS, need, None) == ALIGN
     # the up GEMM alone needs row_list at decode sizes (its K-split workspace), not above
     up = lambda m, T: L.twell_up_gemm(FAKE, FAKE, FAKE, 1, T, 256, 512, ctypes.byref(m), None)
     assert up(mat(rows=4, row_list=None), 4) == ARG
     assert up(mat(rows=64, row_list=None), 64) == ARG
 
-    def gfwd(**kw):
-        a = dict(x=FAKE, wg=FAKE, bg=FAKE, wu=FAKE, w2=FAKE, dt=1, T=64, d=256, f=512, y=FAKE, ydt=0)
+    def gfwd(mm=m, **kw):
+        a = dict(x=FAKE, wg=FAKE, bg=FAKE, wu=FAKE, w2=FAKE, dt=1, T=64, d=256, f=512, y=FAKE, ydt=0, ws=None,
+                 wsb=0)
         a.update(kw)
         return L.twell_gated_ffn_fwd(a["x"], a["wg"], a["bg"], a["wu"], a["w2"], a["dt"], a["T"], a["d"], a["f"],
-                                     ctypes.byref(m), a["y"], a["ydt"], None)
+                                     ctypes.byref(mm), a["y"], a["ydt"], a["ws"], a["wsb"], None)
     assert gfwd(wu=None) == ARG
     assert gfwd(w2=None) == ARG
     assert gfwd(bg=None) == ARG
     assert gfwd(ydt=4) == ARG
     assert gfwd(wu=MIS) == ALIGN
     assert gfwd(f=1024) == SHAPE
+    assert gfwd(mm=big, T=512, d=2048) == WS
+    assert gfwd(mm=big, T=512, d=2048, ws=FAKE, wsb=need - 1) == WS
 
 
 @pytestmark_nogpu
