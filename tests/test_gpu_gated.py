@@ -79,6 +79,19 @@ def test_gated_c2_shapes(T, bias, W, S, cap):
         assert n > 0
 
 
+@pytest.mark.parametrize("T,bias,S", [(17, -2.326, 16), (64, -1.0, 4), (200, -2.326, 2)])
+def test_gated_wide_rows(T, bias, S):
+    # d_model 4096 with 17-200 tokens (the wide-row down gather; f = 2048 keeps the oracle
+    # fast); small S sends rows to the backup
+    say("gated wide rows", T, bias, S)
+    w = synth.C3.with_(f=2048)
+    g, wut = gated_case(w, T=T, bias=bias)
+    n, err = check_gated(g, wut, 128, S, T)
+    say("ovf", n, "err", err)
+    if S <= 4:
+        assert n > 0
+
+
 def test_gated_c3_T8():
     say("gated c3 T=8")
     w = synth.C3
