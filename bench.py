@@ -453,7 +453,7 @@ def leg_c5(steps, warmup):
 def main():
     a = parse()
     if a.gpus != 1:
-        print(json.dumps({"error": "this build runs on one GPU only; --gpus must be 1",
+        print(json.dumps({"error": "this library runs on one GPU; --gpus must be 1",
                           "n_gpus": a.gpus}))
         sys.exit(2)
     import numpy as np
