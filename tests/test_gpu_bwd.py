@@ -194,3 +194,47 @@ def test_c5_full_sampled():
     say("c5 full errs: y", e_y, "dx", e_dx, "dw1t", e_w1, "dw2", e_w2, "db1", e_b, "flips", int(flip.sum()),
         "overflow rows", n_ovf)
     assert max(e_w1, e_w2, e_b) <= TOL["bf16"]
+
+
+@pytest.mark.parametrize("dt", ["bf16", "f32"])
+def test_degenerate_none_and_all_active(dt):
+    """The method's two degenerate cases through forward and backward. No unit active (bias
+    -1e4): every count is 0, every slot a pad, y and all gradients exactly zero (db1 too: no
+    L1 term without active entries). Every unit active (bias +1e4, S < W): every row
+    overflows to the dense backup (capacity T), and y and the gradients follow the oracle."""
+    say("degenerate", dt)
+    T, d, f, W, S = 70, 256, 512, 64, 4
+    base = synth.C1 if dt == "f32" else synth.C2
+    for bias in (-1e4, 1e4):
+        w = base.with_(T=T, d=d, f=f, tile_w=W, slots=S, bias=bias, with_dy=True, seed=61)
+        g = synth.generate(w)
+        h, got = run(g, W, S, T, 2e-5)
+        host = twell_host(h)
+        if bias < 0:
+            assert host["counts"].sum() == 0 and np.all(host["col_idx"] == -1) and host["ovf_n"] == 0
+            assert all(not np.any(a) for a in got), "gradients must be exactly zero"
+        else:
+            assert host["ovf_n"] == T and np.array_equal(host["ovf_rows"], np.arange(T))
+            ref, h64, (xr, w1r, b1r) = reference(g, h, 2e-5)
+            assert np.all(h64 > 0)
+            check_close(got, ref, TOL[dt] if dt == "f32" else TOL["bf16"])
+
+
+def test_fwd_degenerate_y():
+    """Forward only: no active unit gives y = 0 exactly; all active (every row in the backup)
+    gives the dense product within tolerance."""
+    T, d, f, W, S = 33, 512, 1024, 128, 8
+    for bias in (-1e4, 1e4):
+        w = synth.C2.with_(T=T, d=d, f=f, tile_w=W, slots=S, bias=bias, seed=62)
+        g = synth.generate(w)
+        x, w1t, b1, w2 = (to_dev(g["x"], "bf16"), to_dev(g["w1t"], "bf16"), to_dev(g["b1"], "f32"),
+                          to_dev(g["w2"], "bf16"))
+        y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, T)
+        torch.cuda.synchronize()
+        if bias < 0:
+            assert int(torch.count_nonzero(y)) == 0
+        else:
+            xr, w1r, b1r, w2r, _ = inputs64(g)
+            y_ref = orc.relu(orc.preact(xr, w1r, b1r)) @ w2r
+            assert rel_err(from_dev(y), y_ref) <= TOL["bf16"]
+            assert int(h.ovf_n.item()) == T
