@@ -99,3 +99,25 @@ template <> struct Vec16<float> {
     o[0] = u.x; o[1] = u.y; o[2] = u.z; o[3] = u.w;
   }
 };
+
+// One lane's E consecutive fp32 results written as fp32 or bf16 (round to nearest even) with
+// nontemporal 16-byte (or 8-byte) stores: outputs that the writing kernel never reads again
+// should not displace the operand lines it keeps in L2. o must be a multiple of E.
+template <typename YT, int E> TW_DEV void store_out_nt(YT *y, size_t o, const float (&a)[E]) {
+  static_assert(E == 4 || E == 8, "vector width");
+  if constexpr (std::is_same<YT, float>::value) {
+#pragma unroll
+    for (int q = 0; q < E; q += 4)
+      __builtin_nontemporal_store(f32x4_t{a[q], a[q + 1], a[q + 2], a[q + 3]}, (f32x4_t *)(y + o + q));
+  } else {
+    uint32_t w[E / 2];
+#pragma unroll
+    for (int i = 0; i < E / 2; ++i) w[i] = f32_to_bf16(a[2 * i]) | (f32_to_bf16(a[2 * i + 1]) << 16);
+    if constexpr (E == 8) {
+      __builtin_nontemporal_store(u32x4_t{w[0], w[1], w[2], w[3]}, (u32x4_t *)(y + o));
+    } else {
+      typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+      __builtin_nontemporal_store(u32x2_t{w[0], w[1]}, (u32x2_t *)(y + o));
+    }
+  }
+}

@@ -138,8 +138,7 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
   }
   if (g == 0 && cv) {
     const size_t o = (size_t)t * d + col;
-#pragma unroll
-    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+    store_out_nt<YT, E>(y, o, acc);
   }
 }
 
@@ -201,8 +200,7 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
   }
   if (g == 0 && cv) {
     const size_t o = (size_t)t * d + col;
-#pragma unroll
-    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+    store_out_nt<YT, E>(y, o, acc);
   }
 }
 
@@ -243,8 +241,7 @@ __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restr
   gather_list16<WT>(lp, nnz, n, w2, d, col, cv, acc);
   if (normal && t < h.rows && cv) {
     const size_t o = (size_t)t * d + col;
-#pragma unroll
-    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+    store_out_nt<YT, E>(y, o, acc);
   }
 }
 
@@ -319,8 +316,7 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
 #pragma unroll
       for (int q = 0; q < E; ++q) acc[q] += red[w][lane * E + q];
     const size_t o = (size_t)t * d + col;
-#pragma unroll
-    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+    store_out_nt<YT, E>(y, o, acc);
   }
 }
 
@@ -388,8 +384,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
 #pragma unroll
       for (int q = 0; q < E; ++q) acc[q] += red[w][lane * E + q];
     const size_t o = (size_t)t * d + col;
-#pragma unroll
-    for (int q = 0; q < E; ++q) Elem<YT>::store(y, o + q, acc[q]);
+    store_out_nt<YT, E>(y, o, acc);
   }
 }
 

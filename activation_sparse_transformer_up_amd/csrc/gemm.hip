@@ -372,6 +372,13 @@ TW_DEV void mainloop16(const uint16_t *__restrict__ A, const int32_t *__restrict
   for (int i = 0; i < NM; ++i) mma(i, a0, b0);
 }
 
+// 16-byte copy from LDS to global memory with a nontemporal store (the TwELL output is not
+// read again by this kernel, so it should not displace operand lines in L2).
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+TW_DEV void st_nt16(void *dst, const void *src) {
+  __builtin_nontemporal_store(*(const i32x4_t *)src, (i32x4_t *)dst);
+}
+
 // Output position of accumulator register r of a 32x32 block, for this lane:
 //   row = 8 * (r / 4) + 4 * (lane / 32) + r % 4,   col = lane % 32.
 TW_DEV int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
@@ -464,13 +471,13 @@ TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB]
       for (int i = lane; i < nrow * ci; i += 64) {
         const int rr = i / ci, c = i - rr * ci;
         const size_t g = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
-        *(int4 *)(o.col_idx + g + 4 * c) = *(const int4 *)(lidx + rr * RS + 4 * c);
+        st_nt16(o.col_idx + g + 4 * c, lidx + rr * RS + 4 * c);
       }
       constexpr int EV = 16 / sizeof(VT);
       for (int i = lane; i < nrow * cv; i += 64) {
         const int rr = i / cv, c = i - rr * cv;
         const size_t g = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
-        *(int4 *)((VT *)o.vals + g + EV * c) = *(const int4 *)(lval + rr * RS + EV * c);
+        st_nt16((VT *)o.vals + g + EV * c, lval + rr * RS + EV * c);
       }
     } else {
       for (int i = lane; i < nrow * relem; i += 64) {
@@ -572,13 +579,13 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
       for (int i = lane; i < nrow * ci; i += 64) {
         const int rr = i / ci, c = i - rr * ci;
         const size_t gi = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
-        *(int4 *)(o.col_idx + gi + 4 * c) = *(const int4 *)(lidx + rr * RS + 4 * c);
+        st_nt16(o.col_idx + gi + 4 * c, lidx + rr * RS + 4 * c);
       }
       constexpr int EV = 16 / sizeof(VT);
       for (int i = lane; i < nrow * cv; i += 64) {
         const int rr = i / cv, c = i - rr * cv;
         const size_t gi = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
-        *(int4 *)((VT *)o.vals + gi + EV * c) = *(const int4 *)(lval + rr * RS + EV * c);
+        st_nt16((VT *)o.vals + gi + EV * c, lval + rr * RS + EV * c);
       }
     } else {
       for (int i = lane; i < nrow * relem; i += 64) {
