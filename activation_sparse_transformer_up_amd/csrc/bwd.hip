@@ -295,8 +295,7 @@ __global__ __launch_bounds__(256) void k_gather_csr4(int R, int d, int nchunk, i
   const float vs = gather_list16<MT>(pairs + start, n, nw, M, d, col, cv, acc);
   if (r < R && cv) {
     const size_t o = (size_t)r * d + col;
-#pragma unroll
-    for (int q = 0; q < E; q += 4) *(float4 *)(out + o + q) = make_float4(acc[q], acc[q + 1], acc[q + 2], acc[q + 3]);
+    store_out_nt<float, E>(out, o, acc);
   }
   if (rowsum && c == 0) {                        // uniform for the block
     const float sv = group16_sum(vs);
