@@ -107,33 +107,38 @@ hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, 
 
 // ------------------------------------------------------------------- nm_ffn_down
 // y[t][c] = sum_k H[t][k] w2t[c][k] with H expanded from (vals, idx) per 32-column stage.
-// Tile 256 tokens x 256 output columns, 4 waves of 128 x 128, v_mfma_f32_16x16x32_bf16, a
-// ring of four stages of 64-byte rows (A: 256 expanded H rows, B: 256 w2t rows), read as in
-// the up GEMM (16-row fragments, XOR-swizzled 16-byte chunks).
+// Tile 256 tokens x 256 output columns, 8 waves of 64 x 128 (two per SIMD, so one wave's
+// expansion and loads overlap the other's MFMAs), v_mfma_f32_16x16x32_bf16, a ring of four
+// stages of 64-byte rows (A: 256 expanded H rows, B: 256 w2t rows), read as in the up GEMM
+// (16-row fragments, XOR-swizzled 16-byte chunks).
 //  - B arrives by buffer_load ... lds three stages ahead of its use.
-//  - A: thread r owns tile row r. A stage of a row holds 32 N / M = 16 kept entries (8:16
-//    and 16:32): 32 bytes of values and 16 bytes of indices, loaded into registers one step
-//    before the stage is built. Building writes zeros over the row's 64 bytes, then each
-//    kept value at its column (one thread's LDS writes execute in order).
-// Step kt: wait for stage kt + 1, barrier; load the packed A of stage kt + 4; the MFMAs of
+//  - A: tile row r is built by the neighbouring lanes 2r and 2r + 1. A stage of a row holds
+//    32 N / M = 16 kept entries (8:16 and 16:32): each lane loads 8 values and 8 indices
+//    (16 + 8 bytes), clears its 32-byte half of the row, then writes its values at their
+//    columns, which may lie in either half. The two lanes are in one wave, whose LDS writes
+//    execute in issue order, so both clears precede every value.
+// Step kt: wait for stage kt + 1, barrier; load the packed A of stage kt + 3; the MFMAs of
 // stage kt with the fragment reads of stage kt + 1 and the B loads of stage kt + 3 between
-// them; then build the A of stage kt + 3 from the registers loaded in step kt - 1. Stage
-// kt + 3 reuses the buffer of stage kt - 1, whose fragments were read in step kt - 2.
+// them; then build the A of stage kt + 3. Stage kt + 3 reuses the buffer of stage kt - 1,
+// whose fragments were read in step kt - 2. (With 4 waves of 128 x 128 and the packed A
+// loaded a step earlier the kernel took 0.56 / 0.57 ms at c4 instead of 0.48 / 0.49 ms.)
 // Patterns: 8:16 and 16:32 (d_ff a multiple of 32).
+// One thread's half of a row's packed stage: 8 values (bf16) and 8 indices (u8).
 struct NmPack {
-  uint4 v0, v1, ix;                              // 16 values (bf16) and 16 indices (u8)
+  uint4 v;
+  uint2 ix;
 };
 
 template <int N, int M>
-__global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ vals, const uint8_t *__restrict__ idx,
+__global__ __launch_bounds__(512) void k_nm_down(const uint16_t *__restrict__ vals, const uint8_t *__restrict__ idx,
                                                  int T, int f, const uint16_t *__restrict__ w2t, int d,
                                                  void *__restrict__ y, int y_bf16) {
   static_assert(32 % M == 0 && 32 / M * N == 16, "16 kept entries per 32 columns");
   constexpr int BM = 256, BN = 256, RB = 64, NS = 4, STAGE = (BM + BN) * RB;
-  constexpr int WM = 128, WN = 128, FM = WM / 16, FN = WN / 16;
+  constexpr int WM = 64, WN = 128, FM = WM / 16, FN = WN / 16;
   constexpr int NM = FM * FN, NR = FM + FN;
-  constexpr int LPW = BN / 16 / 4;               // B wave-loads per wave per stage
-  constexpr int LA = 3;                          // packed-A loads per thread per stage
+  constexpr int LPW = BN / 16 / 8;               // B wave-loads per wave per stage
+  constexpr int LA = 2;                          // packed-A loads per thread per stage
   __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -142,7 +147,7 @@ __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ va
   const int nk = f / 32;
   const size_t E = (size_t)f / M * N;            // kept entries per row
 
-  // B: stage rows of w2t through LDS DMA (16-row blocks q = wave + 4 i of the B half)
+  // B: stage rows of w2t through LDS DMA (16-row blocks q = wave + 8 i of the B half)
   constexpr uint32_t OOB = 0x80000000u;
   const size_t row_bytes = (size_t)f * 2;
   const __amdgpu_buffer_rsrc_t rb =
@@ -151,41 +156,46 @@ __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ va
   uint32_t voff[LPW];
 #pragma unroll
   for (int i = 0; i < LPW; ++i) {
-    const int gr = n0 + (wave + 4 * i) * 16 + lrow;
+    const int gr = n0 + (wave + 8 * i) * 16 + lrow;
     voff[i] = gr < d ? (uint32_t)((size_t)gr * row_bytes) + cl * 16 : OOB;
   }
   auto issue_b = [&](int kt, int i) {
     char *st = smem + (kt % NS) * STAGE + BM * RB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + (wave + 4 * i) * 1024), 16, voff[i], kt * 64,
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + (wave + 8 * i) * 1024), 16, voff[i], kt * 64,
                                              0, 0);
   };
-  // A: this thread's row (rows past T read row T - 1 and are built as zeros)
-  const bool trow = m0 + tid < T;
-  const size_t prow = (size_t)min(m0 + tid, T - 1) * E;
+  // A: tile row tid / 2, whose 16 kept entries per stage this thread shares with its
+  // neighbour lane: half hf = tid % 2 takes entries 8 hf .. 8 hf + 7 (rows past T read row
+  // T - 1 and are built as zeros)
+  const int arow = tid >> 1, hf = tid & 1;
+  const bool trow = m0 + arow < T;
+  const size_t prow = (size_t)min(m0 + arow, T - 1) * E;
   const uint4 *pv = (const uint4 *)(vals + prow);
-  const uint4 *pi = (const uint4 *)(idx + prow);
+  const uint2 *pi = (const uint2 *)(idx + prow);
   auto load_a = [&](int kt, NmPack &p) {
-    p.v0 = pv[2 * kt];
-    p.v1 = pv[2 * kt + 1];
-    p.ix = pi[kt];
+    p.v = pv[2 * kt + hf];
+    p.ix = pi[2 * kt + hf];
   };
   // The stores are inline assembly: the compiler cannot tell them apart from the B ring's
   // pending LDS DMA and would wait for all of it (vmcnt(0)) before each build. They write
   // the A half of stage kt, which no DMA targets; the LDS wait before every barrier covers
   // them.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t *)smem;
-  const int swz = (tid >> 2) & 3;
-  auto a_row = [&](int kt) { return lds0 + (uint32_t)((kt % NS) * STAGE + tid * RB); };
+  const int swz = (arow >> 2) & 3;
+  auto a_row = [&](int kt) { return lds0 + (uint32_t)((kt % NS) * STAGE + arow * RB); };
+  // each thread clears its 32-byte half of the row, then writes its 8 entries anywhere in the
+  // row: the two halves' threads are neighbouring lanes of one wave, whose LDS writes execute
+  // in issue order, so both clears precede every entry write
   auto build_zero = [&](uint32_t row) {
     const u32x4_t z = {0u, 0u, 0u, 0u};
-    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %1 offset:16\n\t"
-                 "ds_write_b128 %0, %1 offset:32\n\tds_write_b128 %0, %1 offset:48" ::"v"(row), "v"(z));
+    const uint32_t h = row + 32u * (uint32_t)hf;
+    asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %1 offset:16" ::"v"(h), "v"(z));
   };
-  auto build_entry = [&](uint32_t row, const NmPack &p, int e) {
-    const uint32_t iw = e < 4 ? p.ix.x : e < 8 ? p.ix.y : e < 12 ? p.ix.z : p.ix.w;
-    const uint32_t vw = e < 8 ? (e < 2 ? p.v0.x : e < 4 ? p.v0.y : e < 6 ? p.v0.z : p.v0.w)
-                              : (e < 10 ? p.v1.x : e < 12 ? p.v1.y : e < 14 ? p.v1.z : p.v1.w);
-    const int col = (e / N) * M + (int)((iw >> (8 * (e % 4))) & (M - 1));
+  auto build_entry = [&](uint32_t row, const NmPack &p, int e) {     // entry 8 hf + e of the stage
+    const uint32_t iw = e < 4 ? p.ix.x : p.ix.y;
+    const uint32_t vw = e < 2 ? p.v.x : e < 4 ? p.v.y : e < 6 ? p.v.z : p.v.w;
+    const int ee = 8 * hf + e;
+    const int col = (ee / N) * M + (int)((iw >> (8 * (e % 4))) & (M - 1));
     const uint32_t v = trow ? (vw >> (16 * (e & 1))) & 0xFFFFu : 0u;
     const uint32_t a = row + (uint32_t)((((col >> 3) ^ swz) << 4) + (col & 7) * 2);
     asm volatile("ds_write_b16 %0, %1" ::"v"(a), "v"(v));
@@ -194,7 +204,7 @@ __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ va
     const uint32_t row = a_row(kt);
     build_zero(row);
 #pragma unroll
-    for (int e = 0; e < 16; ++e) build_entry(row, p, e);
+    for (int e = 0; e < 8; ++e) build_entry(row, p, e);
   };
   // fragments (as in the up GEMM's 16 x 16 x 32 loop)
   typedef u32x4_t FA[FM];
@@ -220,15 +230,14 @@ __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ va
                                                                   __builtin_bit_cast(bf16x8_t, b[i % FN]),
                                                                   acc[i / FN][i % FN], 0, 0, 0);
   };
-  // prologue: stages 0 .. 2 built and loaded, the packed A of stage 3 in registers
-  NmPack pa0, pa1;
+  // prologue: stages 0 .. 2 built and loaded
+  NmPack pa;
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk) {
-      load_a(st, pa0);
-      build_a(st, pa0);
+      load_a(st, pa);
+      build_a(st, pa);
     }
-  if (NS - 1 < nk) load_a(NS - 1, pa1);
 #pragma unroll
   for (int st = 0; st < NS - 1; ++st)
     if (st < nk)
@@ -241,23 +250,18 @@ __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ va
 #pragma unroll
   for (int j = 0; j < NR; ++j) read1(0, j, a0, b0);
 
-  // A step of the steady state (kt + 4 < nk): packed loads of stage kt + 4 into pl, build of
-  // stage kt + 3 from pb. Issue order per step: packed loads, then B loads, so that at the
-  // start of step kt the loads issued after stage kt + 1's B are step kt - 1's (LA + LPW),
-  // and at the build those issued after stage kt + 3's packed loads are 2 LPW + LA.
   constexpr int RI = NM / NR;                    // a fragment read after every RI MFMAs
   constexpr int DI = NM / LPW;                   // a B load after every DI MFMAs
-  // A step of the steady state (kt + 4 < nk). Issue order: the packed loads of stage kt + 4,
-  // then (between the MFMAs of stage kt, with the fragment reads of stage kt + 1) the B loads
-  // of stage kt + 3; after the MFMAs the A of stage kt + 3 is built from the registers
-  // loaded in step kt - 1. So at the start of step kt the loads issued after stage kt + 1's B
-  // are step kt - 1's (LA + LPW), and at the build those issued after stage kt + 3's packed
-  // loads are 2 LPW + LA. (Interleaving the build with the MFMAs measured slower: with one
-  // wave per SIMD its VALU work delays the MFMA issue.)
-  auto step = [&](int kt, const FA &ac, const FB &bc, FA &an, FB &bn, NmPack &pl, const NmPack &pb) {
+  // A step of the steady state (kt + 3 < nk): the packed loads of stage kt + 3, then (between
+  // the MFMAs of stage kt, with the fragment reads of stage kt + 1) the B loads of stage
+  // kt + 3; after the MFMAs the A of stage kt + 3 is built from those packed registers, whose
+  // loads are the ones issued before the LPW B loads. At the start of step kt the loads issued
+  // after stage kt + 1's B are step kt - 1's (LA + LPW). Stage kt + 3 reuses the buffer of
+  // stage kt - 1, whose fragments were read in step kt - 2.
+  auto step = [&](int kt, const FA &ac, const FB &bc, FA &an, FB &bn) {
     wait_vmcnt<LA + LPW>();
     block_barrier_lds();
-    load_a(kt + 4, pl);
+    load_a(kt + 3, pa);
     __builtin_amdgcn_sched_barrier(0);
     static_for<NM>([&](auto I) {
       constexpr int i = decltype(I)::value;
@@ -266,16 +270,16 @@ __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ va
       if constexpr (i % DI == DI - 1) issue_b(kt + 3, i / DI);
       __builtin_amdgcn_sched_barrier(0);
     });
-    wait_vmcnt<2 * LPW + LA>();
-    build_a(kt + 3, pb);
+    wait_vmcnt<LPW>();
+    build_a(kt + 3, pa);
     __builtin_amdgcn_sched_barrier(0);
   };
-  // The last steps (kt + 4 >= nk): what exists is issued, waits are complete ones, and the
-  // next fragment set and packed registers are copied into the current ones afterwards.
+  // The last steps (kt + 3 >= nk for the second of a pair or later): what exists is issued,
+  // waits are complete ones, and the next fragment set is copied into the current one.
   auto tail_step = [&](int kt) {
     wait_vmcnt<0>();
     block_barrier_lds();
-    if (kt + 4 < nk) load_a(kt + 4, pa0);
+    if (kt + 3 < nk) load_a(kt + 3, pa);
     static_for<NM>([&](auto I) {
       constexpr int i = decltype(I)::value;
       mma(i, a0, b0);
@@ -285,19 +289,18 @@ __global__ __launch_bounds__(256) void k_nm_down(const uint16_t *__restrict__ va
     if (kt + 3 < nk) {
 #pragma unroll
       for (int i = 0; i < LPW; ++i) issue_b(kt + 3, i);
-      build_a(kt + 3, pa1);
+      build_a(kt + 3, pa);
     }
     wait_vmcnt<0>();
 #pragma unroll
     for (int j = 0; j < FM; ++j) a0[j] = a1[j];
 #pragma unroll
     for (int j = 0; j < FN; ++j) b0[j] = b1[j];
-    pa1 = pa0;
   };
   int kt = 0;
-  for (; kt + 5 < nk; kt += 2) {
-    step(kt, a0, b0, a1, b1, pa0, pa1);          // loads stage kt + 4 (even parity) into pa0
-    step(kt + 1, a1, b1, a0, b0, pa1, pa0);      // builds stage kt + 4 from pa0
+  for (; kt + 4 < nk; kt += 2) {
+    step(kt, a0, b0, a1, b1);
+    step(kt + 1, a1, b1, a0, b0);
   }
   for (; kt + 1 < nk; ++kt) tail_step(kt);
 #pragma unroll
@@ -327,8 +330,8 @@ hipError_t launch_nm_down(const void *vals, const uint8_t *idx, int T, int f, in
   if (T == 0) return hipSuccess;
   const dim3 grid((d + 255) / 256, (T + 255) / 256);
   const uint16_t *v = (const uint16_t *)vals, *w = (const uint16_t *)w2t;
-  if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_down<8, 16>), grid, dim3(256), 0, s, v, idx, T, f, w, d, y, y_bf16);
-  else hipLaunchKernelGGL((k_nm_down<16, 32>), grid, dim3(256), 0, s, v, idx, T, f, w, d, y, y_bf16);
+  if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_down<8, 16>), grid, dim3(512), 0, s, v, idx, T, f, w, d, y, y_bf16);
+  else hipLaunchKernelGGL((k_nm_down<16, 32>), grid, dim3(512), 0, s, v, idx, T, f, w, d, y, y_bf16);
   return hipGetLastError();
 }
 
