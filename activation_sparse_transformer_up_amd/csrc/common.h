@@ -121,3 +121,14 @@ template <typename YT, int E> TW_DEV void store_out_nt(YT *y, size_t o, const fl
     }
   }
 }
+
+// Rows of a matrix read through a buffer resource: a scalar descriptor plus a 32-bit byte
+// offset per lane (every operand is below 2 GiB). Offsets at or above 2^31 (e.g. from a
+// negative index) read as zeros.
+TW_DEV __amdgpu_buffer_rsrc_t rows_rsrc(const void *p) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, 0x7FFFFFFF, 0x00020000);
+}
+template <typename WT> TW_DEV uint4 ld16(__amdgpu_buffer_rsrc_t rs, uint32_t elem) {
+  const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(elem * (uint32_t)sizeof(WT)), 0, 0);
+  return make_uint4(v.x, v.y, v.z, v.w);
+}

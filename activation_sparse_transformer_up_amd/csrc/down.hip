@@ -70,6 +70,7 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -85,7 +86,7 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
       if (e < n) {
         const uint2 p = lst[e];
         vv[j] = __uint_as_float(p.y);
-        if (cv) raw[j] = *(const uint4 *)(w2 + (size_t)p.x * d + col);
+        if (cv) raw[j] = ld16<WT>(rs, p.x * (uint32_t)d + (uint32_t)col);
       }
     }
 #pragma unroll
@@ -162,6 +163,7 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
   const bool cv = col < d;
   const int t = h.ovf_rows[r];
   const VT *row = (const VT *)h.ovf_dense + (size_t)r * h.cols;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -185,7 +187,7 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
         if (e < n) {
           const uint2 p = lst[e];
           vv[k] = __uint_as_float(p.y);
-          if (cv) raw[k] = *(const uint4 *)(w2 + (size_t)p.x * d + col);
+          if (cv) raw[k] = ld16<WT>(rs, p.x * (uint32_t)d + (uint32_t)col);
         }
       }
 #pragma unroll
@@ -265,6 +267,7 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
   const int G = wave * 4 + (lane >> 4), gl = lane & 15;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
   const int cap = h.n_t * h.S;
   const uint2 *src = h.row_list + (size_t)t * cap;
   if (tid < LW) lst[tid] = tid < cap ? src[tid] : make_uint2(0, 0);
@@ -295,7 +298,7 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
       if (e < n) {
         const uint2 p = lst[e];
         vv[j] = __uint_as_float(p.y);
-        if (cv) raw[j] = *(const uint4 *)(w2 + (size_t)p.x * d + col);
+        if (cv) raw[j] = ld16<WT>(rs, p.x * (uint32_t)d + (uint32_t)col);
       }
     }
 #pragma unroll
@@ -352,6 +355,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   }
   const int col = c * CW + lane * E;
   const bool cv = col < d;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
   const int nnz = h.row_nnz[t];
   float acc[E];
 #pragma unroll
@@ -369,7 +373,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
       const bool ok = base + j < nnz;
       vv[j] = ok ? vj : 0.f;
       raw[j] = make_uint4(0, 0, 0, 0);
-      if (ok && cv) raw[j] = *(const uint4 *)(w2 + (size_t)ij * d + col);
+      if (ok && cv) raw[j] = ld16<WT>(rs, ij * (uint32_t)d + (uint32_t)col);
     });
 #pragma unroll
     for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);

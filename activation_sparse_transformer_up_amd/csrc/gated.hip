@@ -150,6 +150,7 @@ __global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk,
   const int t = tb * 16 + (threadIdx.x >> 6) * 4 + g;
   const int colo = c * CW + gl * E;
   const bool cv = colo < d;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(wu);
   const size_t cap = (size_t)h.n_t * h.S;
   int n = t < h.rows ? h.row_nnz[t] : 0;
   if (n < 0) n = 0;
@@ -168,7 +169,7 @@ __global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk,
       constexpr int j = decltype(J)::value;
       const uint32_t jj = row_bcast<j>((uint32_t)jq);
       raw[j] = make_uint4(0, 0, 0, 0);
-      if (base + j < n && cv) raw[j] = *(const uint4 *)(wu + (size_t)jj * d + colo);
+      if (base + j < n && cv) raw[j] = ld16<XT>(rs, jj * (uint32_t)d + (uint32_t)colo);
     });
     float v[16];
 #pragma unroll

@@ -50,9 +50,7 @@ TW_DEV float gather_list16(const uint2 *__restrict__ p, int n, int nw, const WT 
                            bool cv, float (&acc)[Vec16<WT>::N]) {
   constexpr int E = Vec16<WT>::N;
   const int gl = lane_id() & 15;
-  // row pieces by buffer loads: a scalar resource plus a 32-bit byte offset per lane (every
-  // operand is below 2 GiB)
-  const __amdgpu_buffer_rsrc_t rs = __builtin_amdgcn_make_buffer_rsrc((void *)M, (short)0, 0x7FFFFFFF, 0x00020000);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(M);            // row pieces by buffer loads
   float vs = 0.f;
   uint2 pn = gl < n ? p[gl] : make_uint2(0, 0);
   for (int base = 0; base < nw; base += 16) {
@@ -67,10 +65,7 @@ TW_DEV float gather_list16(const uint2 *__restrict__ p, int n, int nw, const WT 
       const bool ok = base + j < n;
       vv[j] = ok ? __uint_as_float(vj) : 0.f;
       raw[j] = make_uint4(0, 0, 0, 0);
-      if (ok && cv) {
-        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)((ij * (uint32_t)d + (uint32_t)col) * sizeof(WT)), 0, 0);
-        raw[j] = make_uint4(v.x, v.y, v.z, v.w);
-      }
+      if (ok && cv) raw[j] = ld16<WT>(rs, ij * (uint32_t)d + (uint32_t)col);
     });
 #pragma unroll
     for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
