@@ -53,6 +53,7 @@ TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, in
   constexpr int EPL = 16 / sizeof(XT);
   const int lane = lane_id();
   const int npc = (d + 64 * EPL - 1) / (64 * EPL);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(wu);
 #pragma unroll
   for (int k = 0; k < kGateEnt; ++k) u[k] = 0.f;
   for (int c0 = 0; c0 < npc; c0 += NP) {
@@ -64,7 +65,7 @@ TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, in
       xv[q] = ok ? *(const uint4 *)(xrow + i) : make_uint4(0, 0, 0, 0);
 #pragma unroll
       for (int k = 0; k < kGateEnt; ++k)
-        wv[k][q] = (ok && col[k] >= 0) ? *(const uint4 *)(wu + (size_t)col[k] * d + i) : make_uint4(0, 0, 0, 0);
+        wv[k][q] = (ok && col[k] >= 0) ? ld16<XT>(rs, (uint32_t)col[k] * (uint32_t)d + (uint32_t)i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < NP; ++q)

@@ -1164,6 +1164,7 @@ TW_DEV void gemv_half(const uint16_t *__restrict__ x, const int32_t *__restrict_
   }
   // four groups of four units; the next group's rows are loaded before the current group is
   // reduced (two groups in flight)
+  const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w1t);
   auto load = [&](int g, uint4 (&wr)[4][kGemvNP]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -1173,7 +1174,7 @@ TW_DEV void gemv_half(const uint16_t *__restrict__ x, const int32_t *__restrict_
       for (int p = 0; p < kGemvNP; ++p) {
         wr[i][p] = make_uint4(0, 0, 0, 0);
         if (p < np) {
-          const uint4 v = *(const uint4 *)(wp + 512 * p);
+          const uint4 v = ld16<uint16_t>(rw, (uint32_t)(wp - w1t) + 512u * p);
           if (u < N) wr[i][p] = v;
         }
       }
