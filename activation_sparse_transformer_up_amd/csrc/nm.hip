@@ -14,9 +14,9 @@
 namespace tw {
 
 // ------------------------------------------------------------------------ nm_prune
-// One thread per block of M; the kept set is chosen by nm_keep (nmsel.h), and the kept
-// positions are emitted in ascending order with their signed values. Outputs are staged in
-// LDS per wave and written with 16-byte stores.
+// fp32 blocks: one thread per block of M; the kept set is chosen by nm_keep (nmsel.h), and
+// the kept positions are emitted in ascending order with their signed values. Outputs are
+// staged in LDS per wave and written with 16-byte stores.
 template <typename HT, int N, int M>
 __global__ __launch_bounds__(256) void k_nm_prune(const HT *__restrict__ h, size_t groups, HT *__restrict__ vals,
                                                   uint8_t *__restrict__ idx) {
@@ -87,13 +87,114 @@ __global__ __launch_bounds__(256) void k_nm_prune(const HT *__restrict__ h, size
   }
 }
 
+// bf16 blocks. A wave owns 64 consecutive blocks, one per lane: 128 M contiguous bytes,
+// staged through LDS with coalesced loads. Each lane reads its block back, takes the kept
+// set as a mask (nm_kept_mask) and walks it with count-leading-zeros, which yields the kept
+// entries in ascending order; each value is re-read from the staged block and each index
+// packed into bytes, so nothing branches on the data.
+template <int N, int M>
+__global__ __launch_bounds__(256) void k_nm_prune16(const uint16_t *__restrict__ h, size_t groups,
+                                                    uint16_t *__restrict__ vals, uint8_t *__restrict__ idx) {
+  constexpr int RB = 2 * M;                      // bytes per block
+  constexpr int CH = RB >= 16 ? 16 : 8;          // bytes per staged load
+  constexpr int CPL = RB / CH;                   // loads per lane
+  constexpr int NV = N / 2, NI = (N + 3) / 4;    // packed value words, index words
+  __shared__ __attribute__((aligned(16))) uint32_t raw[4][64 * RB / 4];
+  __shared__ __attribute__((aligned(16))) uint32_t sv[4][64 * NV];
+  __shared__ __attribute__((aligned(16))) uint8_t si[4][64 * N];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const size_t g0 = ((size_t)blockIdx.x * 4 + wave) * 64;
+  if (g0 >= groups) return;
+  const size_t ng = groups - g0 < 64 ? groups - g0 : 64;
+  const char *src = (const char *)(h + g0 * M);
+  char *rw = (char *)raw[wave];
+  const int nch = (int)ng * CPL;                 // loads that fall inside this wave's blocks
+  if constexpr (CH == 16) {
+    uint4 u[CPL];
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = c * 64 + lane;
+      u[c] = *(const uint4 *)(src + (size_t)(ch < nch ? ch : 0) * 16);
+    }
+#pragma unroll
+    for (int c = 0; c < CPL; ++c) {
+      const int ch = c * 64 + lane;
+      *(uint4 *)(rw + ch * 16) = ch < nch ? u[c] : make_uint4(0, 0, 0, 0);
+    }
+  } else {
+    const uint2 u = *(const uint2 *)(src + (size_t)(lane < nch ? lane : 0) * 8);
+    *(uint2 *)(rw + lane * 8) = lane < nch ? u : make_uint2(0, 0);
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const char *row = rw + lane * RB;
+  uint32_t w[RB / 4];
+  if constexpr (CH == 16) {
+#pragma unroll
+    for (int v = 0; v < RB / 16; ++v) {
+      const uint4 u = *(const uint4 *)(row + v * 16);
+      w[4 * v] = u.x; w[4 * v + 1] = u.y; w[4 * v + 2] = u.z; w[4 * v + 3] = u.w;
+    }
+  } else {
+    const uint2 u = *(const uint2 *)row;
+    w[0] = u.x; w[1] = u.y;
+  }
+  uint32_t bits[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) bits[i] = (w[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
+  uint32_t km = nm_kept_mask<N, M>(bits);
+  const uint16_t *rowh = (const uint16_t *)row;
+  uint32_t vw[NV], iw[NI];
+  static_for<N>([&](auto J) {
+    constexpr int j = decltype(J)::value;
+    const uint32_t e = (uint32_t)__builtin_clz(km);   // km holds N - j set bits here
+    km ^= 0x80000000u >> e;
+    const uint32_t v = rowh[e];
+    if constexpr (j & 1) vw[j / 2] |= v << 16;
+    else vw[j / 2] = v;
+    if constexpr (j % 4 == 0) iw[j / 4] = e;
+    else iw[j / 4] |= e << (8 * (j % 4));
+  });
+#pragma unroll
+  for (int q = 0; q < NV; ++q) sv[wave][lane * NV + q] = vw[q];
+  if constexpr (N >= 4) {
+#pragma unroll
+    for (int q = 0; q < NI; ++q) ((uint32_t *)si[wave])[lane * NI + q] = iw[q];
+  } else {
+    ((uint16_t *)si[wave])[lane] = (uint16_t)iw[0];
+  }
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+  const size_t vbytes = ng * N * 2, ibytes = ng * N;
+  char *dv = (char *)(vals + g0 * N);
+  char *di = (char *)(idx + g0 * N);
+  const char *lv = (const char *)sv[wave];
+  const char *li = (const char *)si[wave];
+  if (ng == 64) {
+    for (size_t o = (size_t)lane * 16; o < vbytes; o += 64 * 16) *(uint4 *)(dv + o) = *(const uint4 *)(lv + o);
+    for (size_t o = (size_t)lane * 8; o < ibytes; o += 64 * 8) *(uint2 *)(di + o) = *(const uint2 *)(li + o);
+  } else {
+    for (size_t o = lane; o < vbytes; o += 64) dv[o] = lv[o];
+    for (size_t o = lane; o < ibytes; o += 64) di[o] = li[o];
+  }
+}
+
 template <typename HT>
 static hipError_t prune_t(const HT *h, size_t groups, int n, int m, HT *vals, uint8_t *idx, hipStream_t s) {
   const dim3 grid((unsigned)((groups + 255) / 256));
-  if (n == 2 && m == 4) hipLaunchKernelGGL((k_nm_prune<HT, 2, 4>), grid, dim3(256), 0, s, h, groups, vals, idx);
-  else if (n == 4 && m == 8) hipLaunchKernelGGL((k_nm_prune<HT, 4, 8>), grid, dim3(256), 0, s, h, groups, vals, idx);
-  else if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_prune<HT, 8, 16>), grid, dim3(256), 0, s, h, groups, vals, idx);
-  else hipLaunchKernelGGL((k_nm_prune<HT, 16, 32>), grid, dim3(256), 0, s, h, groups, vals, idx);
+  if constexpr (sizeof(HT) == 2) {
+    if (n == 2 && m == 4) hipLaunchKernelGGL((k_nm_prune16<2, 4>), grid, dim3(256), 0, s, h, groups, vals, idx);
+    else if (n == 4 && m == 8) hipLaunchKernelGGL((k_nm_prune16<4, 8>), grid, dim3(256), 0, s, h, groups, vals, idx);
+    else if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_prune16<8, 16>), grid, dim3(256), 0, s, h, groups, vals, idx);
+    else hipLaunchKernelGGL((k_nm_prune16<16, 32>), grid, dim3(256), 0, s, h, groups, vals, idx);
+  } else {
+    if (n == 2 && m == 4) hipLaunchKernelGGL((k_nm_prune<HT, 2, 4>), grid, dim3(256), 0, s, h, groups, vals, idx);
+    else if (n == 4 && m == 8) hipLaunchKernelGGL((k_nm_prune<HT, 4, 8>), grid, dim3(256), 0, s, h, groups, vals, idx);
+    else if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_prune<HT, 8, 16>), grid, dim3(256), 0, s, h, groups, vals, idx);
+    else hipLaunchKernelGGL((k_nm_prune<HT, 16, 32>), grid, dim3(256), 0, s, h, groups, vals, idx);
+  }
   return hipGetLastError();
 }
 

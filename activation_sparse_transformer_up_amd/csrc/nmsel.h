@@ -12,19 +12,27 @@
 
 namespace tw {
 
-// Bitonic sort of L keys, descending; every index is a compile-time constant.
-template <int L> TW_DEV void bitonic_desc(uint32_t (&a)[L]) {
-  static_for<31 - __builtin_clz(L)>([&](auto KS) {              // k = 2, 4, ..., L
-    constexpr int k = 2 << decltype(KS)::value;
-    static_for<decltype(KS)::value + 1>([&](auto JS) {          // j = k/2, ..., 1
-      constexpr int j = (k >> 1) >> decltype(JS)::value;
-      static_for<L>([&](auto IS) {
-        constexpr int i = decltype(IS)::value, l = i ^ j;
-        if constexpr (l > i) {
-          const uint32_t x = a[i], y = a[l];
-          const uint32_t hi = x > y ? x : y, lo = x > y ? y : x;
-          if constexpr ((i & k) == 0) { a[i] = hi; a[l] = lo; }
-          else { a[i] = lo; a[l] = hi; }
+// Sorting network for L keys (L a power of two), descending: Batcher's odd-even merge sort
+// (K. E. Batcher, "Sorting networks and their applications", 1968). It takes 5, 19 and 63
+// compare-exchanges for 4, 8 and 16 keys, against 6, 24 and 80 for the bitonic network.
+// Every index is a compile-time constant. Stage p merges sorted runs of length p into runs
+// of 2p; within it, pass k compares i + j with i + j + k where both lie in one 2p-run.
+template <int L> TW_DEV void oddeven_desc(uint32_t (&a)[L]) {
+  static_for<31 - __builtin_clz(L)>([&](auto PS) {              // p = 1, 2, ..., L/2
+    constexpr int p = 1 << decltype(PS)::value;
+    static_for<decltype(PS)::value + 1>([&](auto KS) {           // k = p, p/2, ..., 1
+      constexpr int k = p >> decltype(KS)::value;
+      static_for<L>([&](auto JS) {                                // j = k mod p + 2k t
+        constexpr int j = decltype(JS)::value;
+        if constexpr (j >= k % p && (j - k % p) % (2 * k) == 0 && j + k < L) {
+          static_for<k>([&](auto IS) {
+            constexpr int lo = j + decltype(IS)::value, hi = lo + k;
+            if constexpr (hi < L && lo / (2 * p) == hi / (2 * p)) {
+              const uint32_t x = a[lo], y = a[hi];
+              a[lo] = x > y ? x : y;
+              a[hi] = x > y ? y : x;
+            }
+          });
         }
       });
     });
@@ -47,8 +55,8 @@ template <int BYTES, int N, int M> TW_DEV void nm_keep(const uint32_t (&bits)[M]
       if constexpr (i < N) a[i] = key[i];
       else b[i - N] = key[i];
     });
-    bitonic_desc<N>(a);
-    bitonic_desc<N>(b);
+    oddeven_desc<N>(a);
+    oddeven_desc<N>(b);
     uint32_t th = 0xFFFFFFFFu;
     static_for<N>([&](auto I) {
       constexpr int i = decltype(I)::value;
@@ -70,6 +78,31 @@ template <int BYTES, int N, int M> TW_DEV void nm_keep(const uint32_t (&bits)[M]
       keep[i] = rank < N;
     }
   }
+}
+
+// bf16 only: the kept set of one block as a mask, bit 31 - i set iff entry i is kept (so
+// count-leading-zeros walks the kept entries in ascending order). With the unique keys of
+// nm_keep and both halves sorted, c_i = max(a_i, b_{N-1-i}) (i < N) are exactly the N
+// largest keys, and each names its entry in its low log2 M bits.
+template <int N, int M> TW_DEV uint32_t nm_kept_mask(const uint32_t (&bits)[M]) {
+  static_assert(2 * N == M, "bf16 selection keeps half of each block");
+  constexpr int LOGM = 31 - __builtin_clz(M);
+  uint32_t a[N], b[N];
+  static_for<M>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const uint32_t key = ((bits[i] & 0x7FFFu) << LOGM) | (uint32_t)(M - 1 - i);
+    if constexpr (i < N) a[i] = key;
+    else b[i - N] = key;
+  });
+  oddeven_desc<N>(a);
+  oddeven_desc<N>(b);
+  uint32_t mask = 0;
+  static_for<N>([&](auto I) {
+    constexpr int i = decltype(I)::value;
+    const uint32_t c = a[i] > b[N - 1 - i] ? a[i] : b[N - 1 - i];
+    mask |= 1u << (c & (uint32_t)(M - 1));                       // bit M - 1 - entry
+  });
+  return mask << (32 - M);
 }
 
 }  // namespace tw

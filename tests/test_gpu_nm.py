@@ -55,6 +55,21 @@ def test_nm_prune_bit_exact(n, m, dt, kind):
     assert np.array_equal(np.signbit(gv), np.signbit(want_v))
 
 
+@pytest.mark.parametrize("n,m", PATTERNS)
+@pytest.mark.parametrize("groups", [1, 63, 65, 257])
+def test_nm_prune_small_group_counts(n, m, groups):
+    """One block, one short wave, one wave plus one block, a ragged last workgroup."""
+    say("nm_prune small", n, m, groups)
+    store, h64 = rand_h(1, groups * m, groups * 7 + m, "bf16", "ties")
+    vals, idx = tw.nm_prune(to_dev(store, "bf16"), n, m)
+    torch.cuda.synchronize()
+    want_v, want_i = orc.nm_prune(h64, n, m)
+    assert np.array_equal(from_dev(idx), want_i)
+    gv = from_dev(vals)
+    assert np.array_equal(gv, want_v)
+    assert np.array_equal(np.signbit(gv), np.signbit(want_v))
+
+
 def test_nm_prune_c4_full_bit_exact():
     """c4: h = ReLU(x W1) on the GPU (b1 = 0, about half active), pruned 8:16 and 16:32."""
     say("nm_prune c4 full")
