@@ -682,10 +682,12 @@ TW_DEV void epi_dense16(f32x4_t (&acc)[G::FM][G::FN], const float *__restrict__ 
 // "2. Metodologia": the activations are pruned to N:M by magnitude. Fused here into the up
 // GEMM so that the dense h never goes to HBM: the workgroup's tile of h = ReLU(z + b1) is
 // rounded to the output type and staged in LDS ([BM][BN], rows padded by 16 bytes), then
-// every thread takes whole blocks of M columns, selects with nm_keep, compacts the kept
-// (value, index) pairs in place over the block's own LDS bytes and copies them out. h is
-// formed exactly as the dense epilogue forms it, so the result equals the standalone
-// pruning of ffn_up_relu_dense's output bit for bit.
+// every thread takes whole blocks of M columns. bf16 blocks: the kept set comes as a mask
+// (nm_kept_mask), walked in ascending order by count-leading-zeros; the kept values are
+// re-read from LDS and stored with the packed indices straight from registers. fp32 blocks:
+// nm_keep, then the kept (value, index) pairs are compacted in place over the block's own
+// LDS bytes and copied out. h is formed exactly as the dense epilogue forms it, so the
+// result equals the standalone pruning of ffn_up_relu_dense's output bit for bit.
 template <typename HT> TW_DEV void put_h(char *p, float z) {
   z = z > 0.f ? z : 0.f;
   if constexpr (sizeof(HT) == 2) *(uint16_t *)p = (uint16_t)f32_to_bf16(z);
@@ -750,6 +752,21 @@ template <int NB> TW_DEV void copy_bytes(char *dst, const char *src) {
   }
 }
 
+// Store NB bytes (a power of two, dst NB-aligned up to 16) from packed words.
+template <int NB, int NW> TW_DEV void store_words(char *dst, const uint32_t (&w)[NW]) {
+  if constexpr (NB % 16 == 0) {
+#pragma unroll
+    for (int i = 0; i < NB / 16; ++i) ((uint4 *)dst)[i] = make_uint4(w[4 * i], w[4 * i + 1], w[4 * i + 2], w[4 * i + 3]);
+  } else if constexpr (NB == 8) {
+    *(uint2 *)dst = make_uint2(w[0], w[1]);
+  } else if constexpr (NB == 4) {
+    *(uint32_t *)dst = w[0];
+  } else {
+    static_assert(NB == 2, "size");
+    *(uint16_t *)dst = (uint16_t)w[0];
+  }
+}
+
 // Select the blocks of the staged tile (rows m0 .., columns n0 ..; rows at or beyond
 // rows_valid and columns at or beyond N are skipped; N is a multiple of M). Outputs
 // vals / idx [rows][N / M][NK]. Consecutive threads take consecutive blocks of a row, so the
@@ -785,22 +802,39 @@ TW_DEV void nm_tile(char *lds, int rows_valid, int N, int m0, int n0, HT *__rest
       if constexpr (sizeof(HT) == 2) bits[i] = (w[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
       else bits[i] = w[i];
     }
-    bool keep[M];
-    nm_keep<(int)sizeof(HT), NK, M>(bits, keep);
-    // in place: entry i moves to position pos <= i, so nothing unread is overwritten
-    int pos = 0;
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      if (keep[i]) {
-        if constexpr (sizeof(HT) == 2) ((uint16_t *)p)[pos] = (uint16_t)bits[i];
-        else ((uint32_t *)p)[pos] = bits[i];
-        ((uint8_t *)p)[VB + pos] = (uint8_t)i;
-        ++pos;
-      }
-    }
     const size_t o = ((size_t)row * bpr + col / M) * NK;
-    copy_bytes<VB>((char *)(vals + o), p);
-    copy_bytes<NK>((char *)(idx + o), p + VB);
+    if constexpr (sizeof(HT) == 2) {
+      uint32_t km = nm_kept_mask<NK, M>(bits);
+      const uint16_t *ph = (const uint16_t *)p;
+      uint32_t vw[(NK + 1) / 2], iw[(NK + 3) / 4];
+      static_for<NK>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        const uint32_t e = (uint32_t)__builtin_clz(km);   // km holds NK - j set bits here
+        km ^= 0x80000000u >> e;
+        const uint32_t v = ph[e];
+        if constexpr (j & 1) vw[j / 2] |= v << 16;
+        else vw[j / 2] = v;
+        if constexpr (j % 4 == 0) iw[j / 4] = e;
+        else iw[j / 4] |= e << (8 * (j % 4));
+      });
+      store_words<VB>((char *)(vals + o), vw);
+      store_words<NK>((char *)(idx + o), iw);
+    } else {
+      bool keep[M];
+      nm_keep<(int)sizeof(HT), NK, M>(bits, keep);
+      // in place: entry i moves to position pos <= i, so nothing unread is overwritten
+      int pos = 0;
+#pragma unroll
+      for (int i = 0; i < M; ++i) {
+        if (keep[i]) {
+          ((uint32_t *)p)[pos] = bits[i];
+          ((uint8_t *)p)[VB + pos] = (uint8_t)i;
+          ++pos;
+        }
+      }
+      copy_bytes<VB>((char *)(vals + o), p);
+      copy_bytes<NK>((char *)(idx + o), p + VB);
+    }
   }
 }
 
