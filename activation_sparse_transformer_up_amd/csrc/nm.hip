@@ -4,8 +4,10 @@
 // "2. Metodologia": in every block of M consecutive activations keep the N of largest
 // magnitude (criterion ACT); patterns 2:4, 4:8, 8:16 and 16:32. Section "5. Significado e
 // Implicações": without hardware that executes the N:M format the products are not
-// reduced; gfx950 has no N:M matrix instruction, so the down projection expands each block
-// back to dense bf16 in LDS and multiplies on MFMA (only the activation bytes shrink).
+// reduced. gfx950's sparse matrix instructions (v_smfmac) take only a 2:4 structure, at
+// most two nonzeros in every four consecutive entries, which 8:16 and 16:32 blocks do not
+// have; so the down projection expands each block back to dense bf16 in LDS and multiplies
+// on MFMA (only the activation bytes shrink).
 #include "common.h"
 #include "launch.h"
 #include "nmsel.h"

@@ -288,8 +288,9 @@ int ffn_up_relu_nm(const void *x, const void *w1t, const float *b1, int32_t in_d
 
 /*
  * nm_ffn_down — y = H_nm . W2 for N:M-packed activations (vals, idx from nm_prune, bf16).
- * gfx950 has no N:M matrix instruction, so each block is expanded to dense bf16 in LDS and
- * multiplied on MFMA; only the activation bytes shrink. The down weight is given as
+ * gfx950's sparse matrix instructions take only a 2:4 structure (at most two nonzeros in
+ * every four consecutive entries), which 8:16 and 16:32 blocks do not have, so each block is
+ * expanded to dense bf16 in LDS and multiplied on MFMA; only the activation bytes shrink. The down weight is given as
  * w2t [d_model][d_ff] (nn.Linear(d_ff, d_model).weight), the K-contiguous layout the MFMA
  * operand loads want. y: [T][d_model], y_dtype fp32 or bf16.
  */
