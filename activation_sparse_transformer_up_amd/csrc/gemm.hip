@@ -399,13 +399,15 @@ TW_DEV int acc_row(int r, int lh) { return 8 * (r >> 2) + 4 * lh + (r & 3); }
 // block out with 16-byte stores. Blocks whose ballot is empty are skipped (a scalar test).
 template <class G, int W, typename VT>
 TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB], int M, int N,
-                      int m0, int n0, const TwellOut &o, char *smem) {
+                      int m0, int n0, const TwellOut &o, char *smem, int only_mb = -1) {
   constexpr int BPT = W / 32;                   // 32-column blocks per TwELL tile
   constexpr int TPW = G::WN / W;                // TwELL tiles per wave
   static_assert(G::WN % W == 0, "a TwELL tile must sit inside one wave");
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  const int wm = wave / G::NWN, wn = wave % G::NWN;
+  // only_mb >= 0: this wave packs only 32-row block only_mb of a one-wave-wide tile (the
+  // tile's other blocks are packed by other waves), in its own LDS area
+  const int wm = only_mb >= 0 ? 0 : wave / G::NWN, wn = only_mb >= 0 ? 0 : wave % G::NWN;
   const int lh = lane >> 5, li = lane & 31;
   const int row0 = m0 + wm * G::WM, col0 = n0 + wn * G::WN;
   const int S = o.S;
@@ -424,6 +426,7 @@ TW_DEV void epi_twell(f32x16_t (&acc)[G::MB][G::NB], const float (&nbias)[G::NB]
   const bool vec_ok = (S * (int)sizeof(VT)) % 16 == 0;
 #pragma unroll
   for (int mb = 0; mb < G::MB; ++mb) {
+    if (only_mb >= 0 && mb != only_mb) continue;  // wave-uniform
     const int rb0 = row0 + mb * 32;
     if (rb0 >= M) break;                         // wave-uniform
     // 1. pad pattern
@@ -925,7 +928,7 @@ __global__ __launch_bounds__(G::NT) void k_up_dense(const T *__restrict__ x, con
 //  - k_up_twell_dec spreads a 128-column tile over two workgroups of two waves (quarters
 //    0-1 and 2-3): twice the workgroups of one per tile. The halves meet in a workspace: each
 //    workgroup stores its half sum and takes a ticket; the second to arrive adds the other
-//    half and runs the TwELL epilogue.
+//    half and runs the TwELL epilogue, its two waves on one 32-row block each.
 //  - k_up_dense_dec keeps one workgroup of four waves per tile (no workspace).
 // fp32 addition is commutative, so both add the same halves to the same bits whichever
 // workgroup arrives last, and the dense path equals the TwELL path bit for bit.
@@ -956,52 +959,76 @@ TW_DEV void acc_add_lds(f32x16_t (&acc)[TileD::MB][TileD::NB], const float *red)
 // (a uniform branch, so the loads of the kept groups are all issued before any wait).
 TW_DEV bool dec_group_live(int mb, int g, int M) { return mb * 32 + 8 * g < M; }
 
-// Cross-workgroup hand-over of the half sums. Every access to the workspace is an atomic of
+constexpr int kDecodeSmem = 2 * TileD::LDS_BYTES > TileD::EPI_WAVE ? 2 * TileD::LDS_BYTES : TileD::EPI_WAVE;
+static_assert(kDecodeSmem <= 160 * 1024, "LDS");
+
+// The TwELL decode kernel splits the tail of a tile by 32-row block: wave w of a workgroup
+// keeps block row w (rows 32 w .. 32 w + 31). kDecRowF floats hold one wave's block row in
+// register order: element r of block nb of lane l at (nb * 16 + r) * 64 + l.
+constexpr int kDecRowF = TileD::NB * 16 * 64;
+constexpr int kDecTicketOff = kDecodeSmem - 16;   // LDS word that shares the ticket
+static_assert(2 * kDecRowF * 4 <= kDecTicketOff && 2 * TileD::EPI_WAVE <= kDecTicketOff, "decode LDS layout");
+
+TW_DEV void row_to_lds(const f32x16_t (&a)[TileD::NB], float *red) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int nb = 0; nb < TileD::NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) red[(nb * 16 + r) * 64 + lane] = a[nb][r];
+}
+
+TW_DEV void row_add_lds(f32x16_t (&a)[TileD::NB], const float *red) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int nb = 0; nb < TileD::NB; ++nb)
+#pragma unroll
+    for (int r = 0; r < 16; ++r) a[nb][r] += red[(nb * 16 + r) * 64 + lane];
+}
+
+// Cross-workgroup hand-over of the half sums (k_up_twell_dec). Every access to the workspace is an atomic of
 // agent scope: such accesses are coherent across the XCDs' separate L2 caches on their own
 // (stores write through, loads do not hit a stale line). The half sum is stored, its stores
 // are waited for (vmcnt(0)) and only then is the ticket taken, so a workgroup that draws
 // ticket 1 reads a completely stored other half: its loads are issued after the ticket's
 // value has returned. An agent-scope release/acquire pair would add an L2 write-back and
 // invalidate per workgroup (several microseconds per launch) that only plain stores need.
-// The second arriver resets the ticket for the next launch; tickets start at zero.
-TW_DEV bool dec_handover(f32x16_t (&acc)[TileD::MB][TileD::NB], int M, float *mine, const float *other,
-                         uint32_t *ticket) {
+// The second arriver resets the ticket for the next launch; tickets start at zero. Both
+// waves of a workgroup store (and later load) their own block rows; wave 0 takes the one
+// ticket after a barrier that follows both waves' store waits.
+// Half sum of block row MB to the workspace (element r of block (MB, nb) of lane l at
+// ((MB * NB + nb) * 16 + r) * 64 + l), agent-scope stores of the live row groups only.
+template <int MB> TW_DEV void dec_store_row(const f32x16_t (&acc)[TileD::MB][TileD::NB], int M, float *mine) {
   const int lane = threadIdx.x & 63;
 #pragma unroll
-  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
+  for (int nb = 0; nb < TileD::NB; ++nb)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
-      if (dec_group_live(i / TileD::NB, g, M))
+      if (dec_group_live(MB, g, M))
 #pragma unroll
         for (int q = 0; q < 4; ++q)
-          __hip_atomic_store(mine + (i * 16 + 4 * g + q) * 64 + lane, acc[i / TileD::NB][i % TileD::NB][4 * g + q],
+          __hip_atomic_store(mine + ((MB * TileD::NB + nb) * 16 + 4 * g + q) * 64 + lane, acc[MB][nb][4 * g + q],
                              __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_vmcnt<0>();
-  uint32_t t = 0;
-  if (lane == 0) t = __hip_atomic_fetch_add(ticket, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  t = (uint32_t)__builtin_amdgcn_readfirstlane((int)t);
-  if (t == 0) return false;
-  if (lane == 0) __hip_atomic_store(ticket, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  float ov[TileD::MB * TileD::NB][16];
+}
+
+// acc[MB] += the other half's block row MB (all loads issued before the adds).
+template <int MB> TW_DEV void dec_add_row(f32x16_t (&acc)[TileD::MB][TileD::NB], int M, const float *other) {
+  const int lane = threadIdx.x & 63;
+  float ov[TileD::NB][16];
 #pragma unroll
-  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
+  for (int nb = 0; nb < TileD::NB; ++nb)
 #pragma unroll
     for (int g = 0; g < 4; ++g)
 #pragma unroll
       for (int q = 0; q < 4; ++q)
-        ov[i][4 * g + q] = dec_group_live(i / TileD::NB, g, M)
-                               ? __hip_atomic_load(other + (i * 16 + 4 * g + q) * 64 + lane, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT)
-                               : 0.f;
+        ov[nb][4 * g + q] = dec_group_live(MB, g, M)
+                                ? __hip_atomic_load(other + ((MB * TileD::NB + nb) * 16 + 4 * g + q) * 64 + lane,
+                                                    __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT)
+                                : 0.f;
 #pragma unroll
-  for (int i = 0; i < TileD::MB * TileD::NB; ++i)
+  for (int nb = 0; nb < TileD::NB; ++nb)
 #pragma unroll
-    for (int r = 0; r < 16; ++r) acc[i / TileD::NB][i % TileD::NB][r] += ov[i][r];
-  return true;
+    for (int r = 0; r < 16; ++r) acc[MB][nb][r] += ov[nb][r];
 }
-
-constexpr int kDecodeSmem = 2 * TileD::LDS_BYTES > TileD::EPI_WAVE ? 2 * TileD::LDS_BYTES : TileD::EPI_WAVE;
-static_assert(kDecodeSmem <= 160 * 1024, "LDS");
 
 // Grid: 2 * ceil(N / 128) workgroups of 128 threads; workgroup b takes tile b % n_tiles and
 // half b / n_tiles (quarters 2 half, 2 half + 1). Workspace o.dec_part [n_tiles][2][kDecTileF]
@@ -1028,16 +1055,34 @@ __global__ __launch_bounds__(128) void k_up_twell_dec(const T *__restrict__ x, c
 #pragma unroll
     for (int nb = 0; nb < TileD::NB; ++nb) acc[mb][nb] = f32x16_t{};
   mainloop<T, TileD>(x, nullptr, M, M, w1t, N, kq, 0, n0, acc, smem + w * TileD::LDS_BYTES, K, (2 * half + w) * kq, 0);
-  block_barrier_lds();                      // both rings are drained; ring 0 takes wave 1's quarter
+  // Wave w keeps block row w: it passes the other block row to the other wave through LDS
+  // and adds the one it receives (q_2h + q_2h+1; fp32 addition is commutative, so either
+  // wave's order gives the same bits).
+  block_barrier_lds();                      // both rings are drained
   float *red = (float *)smem;
-  if (w == 1) acc_to_lds(acc, red);
+  if (w == 0) row_to_lds(acc[1], red + kDecRowF);
+  else row_to_lds(acc[0], red);
   block_barrier_lds();
-  if (w == 1) return;
-  acc_add_lds(acc, red);                    // q_2h + q_2h+1
+  if (w == 0) row_add_lds(acc[0], red);
+  else row_add_lds(acc[1], red + kDecRowF);
+  // Hand-over of the half sums (one ticket per workgroup):
+  // both waves store their block rows and wait for the stores; after the barrier wave 0
+  // takes the ticket and shares it through LDS.
   float *part = o.dec_part + (size_t)tile * 2 * kDecTileF;
-  if (!dec_handover(acc, M, part + half * kDecTileF, part + (1 - half) * kDecTileF, o.dec_ticket + tile))
-    return;
-  epi_twell<TileD, W, VT>(acc, nbias, M, N, 0, n0, o, smem);
+  if (w == 0) dec_store_row<0>(acc, M, part + half * kDecTileF);
+  else dec_store_row<1>(acc, M, part + half * kDecTileF);
+  wait_vmcnt<0>();
+  block_barrier_lds();
+  uint32_t *tk = (uint32_t *)(smem + kDecTicketOff);
+  const int lane = threadIdx.x & 63;
+  if (w == 0 && lane == 0) *tk = __hip_atomic_fetch_add(o.dec_ticket + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  block_barrier_lds();
+  const uint32_t t = (uint32_t)__builtin_amdgcn_readfirstlane((int)*tk);
+  if (t == 0) return;                       // first to arrive: the other workgroup finishes
+  if (w == 0 && lane == 0) __hip_atomic_store(o.dec_ticket + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (w == 0) dec_add_row<0>(acc, M, part + (1 - half) * kDecTileF);
+  else dec_add_row<1>(acc, M, part + (1 - half) * kDecTileF);
+  epi_twell<TileD, W, VT>(acc, nbias, M, N, 0, n0, o, smem, w);
 }
 
 // Four waves of TileDQ (3-stage rings, 36 KB each), wave w on quarter w; then
