@@ -76,28 +76,38 @@ TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, in
   for (int k = 0; k < kGateEnt; ++k) u[k] = wave_sumf(u[k]);
 }
 
-// Row lists: workgroup (t, p) of 4 waves; wave w takes the entry groups p * 4 + w,
-// p * 4 + w + 4 P, ... of ENT entries each. Overflow rows are skipped (their backup row
-// carries them).
+// Row lists: workgroup (t, p) of 4 waves, numbered p * rows + t; wave w takes the entry
+// groups p * 4 + w, p * 4 + w + 4 P, ... of ENT entries each. Slot p of every token comes
+// before slot p + 1 of any, so the workgroups that have entries (small p; P is sized for
+// the longest possible list) are dispatched first and the empty ones last. Overflow rows
+// are skipped (their backup row carries them).
 template <typename XT, int NP>
 __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restrict__ x, const XT *__restrict__ wu,
                                                   int d, int P) {
-  const int t = blockIdx.x / P, p = blockIdx.x % P;
-  if (t >= h.rows || h.ovf_slot[t] >= 0) return;
+  const int t = blockIdx.x % h.rows, p = blockIdx.x / h.rows;
+  if (p >= P) return;
+  // the overflow flag and the list length in one round trip, each entry's (column, gate)
+  // pair in one load: the gate is kept for the final product instead of being re-read
+  const int oslot = h.ovf_slot[t], nnz = h.row_nnz[t];
+  if (oslot >= 0) return;
   const int wave = threadIdx.x >> 6, lane = lane_id();
-  const int nnz = h.row_nnz[t];
   uint2 *lst = h.row_list + (size_t)t * h.n_t * h.S;
   const XT *xrow = x + (size_t)t * d;
   for (int e0 = (p * 4 + wave) * kGateEnt; e0 < nnz; e0 += P * 4 * kGateEnt) {
     int col[kGateEnt];
+    float gv[kGateEnt];
 #pragma unroll
-    for (int k = 0; k < kGateEnt; ++k) col[k] = e0 + k < nnz ? (int)lst[e0 + k].x : -1;
+    for (int k = 0; k < kGateEnt; ++k) {
+      const uint2 en = e0 + k < nnz ? lst[e0 + k] : make_uint2(0xFFFFFFFFu, 0u);
+      col[k] = (int)en.x;
+      gv[k] = __uint_as_float(en.y);
+    }
     float u[kGateEnt];
     wave_dots<XT, NP>(xrow, wu, d, col, u);
     if (lane == 0)
 #pragma unroll
       for (int k = 0; k < kGateEnt; ++k)
-        if (col[k] >= 0) lst[e0 + k].y = __float_as_uint(__uint_as_float(lst[e0 + k].y) * u[k]);
+        if (col[k] >= 0) lst[e0 + k].y = __float_as_uint(gv[k] * u[k]);
   }
 }
 
