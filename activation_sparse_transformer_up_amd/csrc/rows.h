@@ -17,7 +17,11 @@ namespace tw {
 // the chunk (e, e + 64, ...), finds its tile as the last k with off[k] <= e by a binary
 // search over the wave (ds_bpermute), and copies slot e - off[k]. A row costs a few wave
 // loads and one coalesced 8-byte store per 64 entries, instead of one wave load per tile
-// group and slot.
+// group and slot. The row is a chain of dependent memory round trips, so the next chunk's
+// counts are loaded before this chunk's stores, and the slot loads of up to kListRounds
+// rounds of 64 entries are all issued before their stores.
+constexpr int kListRounds = 4;
+
 template <typename VT>
 TW_DEV void row_list_wave(const TwellIn &h, int t) {
   const int lane = lane_id();
@@ -25,27 +29,37 @@ TW_DEV void row_list_wave(const TwellIn &h, int t) {
   const size_t stride = (size_t)h.n_t * S;
   uint2 *out = h.row_list + (size_t)t * stride;
   const VT *vals = (const VT *)h.vals;
+  const int32_t *cnt = h.counts + (size_t)t * h.n_t;
   int n = 0;
+  int cnext = h.n_t > 0 ? cnt[lane < h.n_t ? lane : h.n_t - 1] : 0;
   for (int k0 = 0; k0 < h.n_t; k0 += 64) {
     const int k = k0 + lane;
-    const int m = k < h.n_t ? min(h.counts[(size_t)t * h.n_t + k], S) : 0;
+    const int m = k < h.n_t ? min(cnext, S) : 0;
+    if (k0 + 64 < h.n_t) cnext = cnt[k + 64 < h.n_t ? k + 64 : h.n_t - 1];
     int tot;
     const int off = wave_excl_scan(m, &tot);
     const size_t rb = ((size_t)t * h.n_t + k0) * S;   // slot 0 of tile k0
-    for (int e0 = 0; e0 < tot; e0 += 64) {
-      const int e = e0 + lane;
-      int lo = 0;                                     // last tile with off <= e (off[0] = 0)
+    for (int e0 = 0; e0 < tot; e0 += kListRounds * 64) {
+      uint32_t ci[kListRounds], cv[kListRounds];
 #pragma unroll
-      for (int step = 32; step > 0; step >>= 1) {
-        const int o = __shfl(off, lo + step, 64);
-        lo = (lo + step < 64 && o <= e) ? lo + step : lo;
+      for (int r = 0; r < kListRounds; ++r) {
+        const int e = e0 + r * 64 + lane;
+        int lo = 0;                                   // last tile with off <= e (off[0] = 0)
+#pragma unroll
+        for (int step = 32; step > 0; step >>= 1) {
+          const int o = __shfl(off, lo + step, 64);
+          lo = (lo + step < 64 && o <= e) ? lo + step : lo;
+        }
+        const int base = __shfl(off, lo, 64);
+        const size_t si = rb + (e < tot ? (size_t)lo * S + (e - base) : 0);
+        ci[r] = (uint32_t)h.col_idx[si];
+        cv[r] = __float_as_uint(Elem<VT>::load(vals, si));
       }
-      const int base = __shfl(off, lo, 64);
-      const bool on = e < tot;
-      const size_t si = rb + (on ? (size_t)lo * S + (e - base) : 0);
-      const uint32_t ci = (uint32_t)h.col_idx[si];
-      const uint32_t cv = __float_as_uint(Elem<VT>::load(vals, si));
-      if (on) out[n + e] = make_uint2(ci, cv);
+#pragma unroll
+      for (int r = 0; r < kListRounds; ++r) {
+        const int e = e0 + r * 64 + lane;
+        if (e < tot) out[n + e] = make_uint2(ci[r], cv[r]);
+      }
     }
     n += tot;
   }

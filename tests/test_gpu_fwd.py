@@ -174,10 +174,12 @@ def decode_tickets(h):
 
 
 @pytest.mark.parametrize("T,f,W,S,seed", [(1, 1984, 64, 3, 21), (37, 2048, 128, 8, 22), (64, 1984, 64, 4, 23),
-                                          (64, 2048, 128, 2, 24)])
+                                          (64, 2048, 128, 2, 24), (33, 1984, 64, 4, 25)])
 def test_fwd_decode_split(T, f, W, S, seed):
     """Up to 64 tokens the up GEMM splits every 128-column tile over two workgroups that add
-    their halves of K through the row_list workspace. f = 1984 ends in a half tile. The TwELL
+    their halves of K through the row_list workspace; the finishing workgroup's two waves
+    take one 32-row block each (T = 33: the second block holds one row). f = 1984 ends in a
+    half tile. The TwELL
     equals the dense path's packing bit for bit (which sums the same quarters in one
     workgroup), the tickets are zero after every call, and repeated calls on one h give the
     same bits. S = 2 at T = 64 makes rows overflow, so the backup rows (dense path, rows
