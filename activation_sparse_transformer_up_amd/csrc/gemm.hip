@@ -688,7 +688,7 @@ TW_DEV void epi_dense16(f32x4_t (&acc)[G::FM][G::FN], const float *__restrict__ 
 // every thread takes whole blocks of M columns. bf16 blocks: the kept set comes as a mask
 // (nm_kept_mask), walked in ascending order by count-leading-zeros; the kept values are
 // re-read from LDS and stored with the packed indices straight from registers. fp32 blocks:
-// nm_keep, then the kept (value, index) pairs are compacted in place over the block's own
+// nm_keep32, then the kept (value, index) pairs are compacted in place over the block's own
 // LDS bytes and copied out. h is formed exactly as the dense epilogue forms it, so the
 // result equals the standalone pruning of ffn_up_relu_dense's output bit for bit.
 template <typename HT> TW_DEV void put_h(char *p, float z) {
@@ -824,7 +824,7 @@ TW_DEV void nm_tile(char *lds, int rows_valid, int N, int m0, int n0, HT *__rest
       store_words<NK>((char *)(idx + o), iw);
     } else {
       bool keep[M];
-      nm_keep<(int)sizeof(HT), NK, M>(bits, keep);
+      nm_keep32<NK, M>(bits, keep);
       // in place: entry i moves to position pos <= i, so nothing unread is overwritten
       int pos = 0;
 #pragma unroll

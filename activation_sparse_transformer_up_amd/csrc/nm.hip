@@ -16,56 +16,38 @@
 namespace tw {
 
 // ------------------------------------------------------------------------ nm_prune
-// fp32 blocks: one thread per block of M; the kept set is chosen by nm_keep (nmsel.h), and
-// the kept positions are emitted in ascending order with their signed values. Outputs are
-// staged in LDS per wave and written with 16-byte stores.
-template <typename HT, int N, int M>
-__global__ __launch_bounds__(256) void k_nm_prune(const HT *__restrict__ h, size_t groups, HT *__restrict__ vals,
-                                                  uint8_t *__restrict__ idx) {
-  __shared__ __attribute__((aligned(16))) HT sv[4][64 * N];
+// fp32 blocks: one thread per block of M (M words, read as 16-byte vectors); the kept set
+// is chosen by nm_keep32 (nmsel.h), and the kept positions are emitted in ascending order with
+// their signed values. Outputs are staged in LDS per wave and written with 16-byte stores.
+template <int N, int M>
+__global__ __launch_bounds__(256) void k_nm_prune32(const float *__restrict__ h, size_t groups,
+                                                    float *__restrict__ vals, uint8_t *__restrict__ idx) {
+  static_assert(M % 4 == 0, "whole 16-byte vectors per block");
+  __shared__ __attribute__((aligned(16))) uint32_t sv[4][64 * N];
   __shared__ __attribute__((aligned(16))) uint8_t si[4][64 * N];
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const size_t g0 = ((size_t)blockIdx.x * 4 + wave) * 64;
   if (g0 >= groups) return;
   const size_t g = g0 + lane;
-  const bool gv = g < groups;
   uint32_t bits[M];
-  if (gv) {
-    // M values = W32 words, fetched with the widest aligned vector loads
-    constexpr int W32 = M * (int)sizeof(HT) / 4;
-    uint32_t w[W32];
-    if constexpr (W32 % 4 == 0) {
-      const uint4 *src = (const uint4 *)(h + g * M);
+  if (g < groups) {
+    const uint4 *src = (const uint4 *)(h + g * M);
 #pragma unroll
-      for (int v = 0; v < W32 / 4; ++v) {
-        const uint4 u = src[v];
-        w[4 * v] = u.x; w[4 * v + 1] = u.y; w[4 * v + 2] = u.z; w[4 * v + 3] = u.w;
-      }
-    } else {
-      const uint2 *src = (const uint2 *)(h + g * M);
-#pragma unroll
-      for (int v = 0; v < W32 / 2; ++v) {
-        const uint2 u = src[v];
-        w[2 * v] = u.x; w[2 * v + 1] = u.y;
-      }
-    }
-#pragma unroll
-    for (int i = 0; i < M; ++i) {
-      if constexpr (sizeof(HT) == 2) bits[i] = (w[i / 2] >> (16 * (i & 1))) & 0xFFFFu;
-      else bits[i] = w[i];
+    for (int v = 0; v < M / 4; ++v) {
+      const uint4 u = src[v];
+      bits[4 * v] = u.x; bits[4 * v + 1] = u.y; bits[4 * v + 2] = u.z; bits[4 * v + 3] = u.w;
     }
   } else {
 #pragma unroll
     for (int i = 0; i < M; ++i) bits[i] = 0;
   }
   bool keep[M];
-  nm_keep<(int)sizeof(HT), N, M>(bits, keep);
+  nm_keep32<N, M>(bits, keep);
   int pos = 0;
 #pragma unroll
   for (int i = 0; i < M; ++i) {
     if (keep[i]) {
-      if constexpr (sizeof(HT) == 2) ((uint16_t *)sv[wave])[lane * N + pos] = (uint16_t)bits[i];
-      else ((uint32_t *)sv[wave])[lane * N + pos] = bits[i];
+      sv[wave][lane * N + pos] = bits[i];
       si[wave][lane * N + pos] = (uint8_t)i;
       ++pos;
     }
@@ -75,7 +57,7 @@ __global__ __launch_bounds__(256) void k_nm_prune(const HT *__restrict__ h, size
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
   // copy out this wave's 64 groups (contiguous in the outputs)
   const size_t ng = groups - g0 < 64 ? groups - g0 : 64;
-  const size_t vbytes = ng * N * sizeof(HT), ibytes = ng * N;
+  const size_t vbytes = ng * N * 4, ibytes = ng * N;
   char *dv = (char *)(vals + g0 * N);
   char *di = (char *)(idx + g0 * N);
   const char *lv = (const char *)sv[wave];
@@ -183,29 +165,24 @@ __global__ __launch_bounds__(256) void k_nm_prune16(const uint16_t *__restrict__
   }
 }
 
-template <typename HT>
-static hipError_t prune_t(const HT *h, size_t groups, int n, int m, HT *vals, uint8_t *idx, hipStream_t s) {
+template <int N, int M>
+static void prune_launch(const void *h, size_t groups, void *vals, uint8_t *idx, int bf16, hipStream_t s) {
   const dim3 grid((unsigned)((groups + 255) / 256));
-  if constexpr (sizeof(HT) == 2) {
-    if (n == 2 && m == 4) hipLaunchKernelGGL((k_nm_prune16<2, 4>), grid, dim3(256), 0, s, h, groups, vals, idx);
-    else if (n == 4 && m == 8) hipLaunchKernelGGL((k_nm_prune16<4, 8>), grid, dim3(256), 0, s, h, groups, vals, idx);
-    else if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_prune16<8, 16>), grid, dim3(256), 0, s, h, groups, vals, idx);
-    else hipLaunchKernelGGL((k_nm_prune16<16, 32>), grid, dim3(256), 0, s, h, groups, vals, idx);
-  } else {
-    if (n == 2 && m == 4) hipLaunchKernelGGL((k_nm_prune<HT, 2, 4>), grid, dim3(256), 0, s, h, groups, vals, idx);
-    else if (n == 4 && m == 8) hipLaunchKernelGGL((k_nm_prune<HT, 4, 8>), grid, dim3(256), 0, s, h, groups, vals, idx);
-    else if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_prune<HT, 8, 16>), grid, dim3(256), 0, s, h, groups, vals, idx);
-    else hipLaunchKernelGGL((k_nm_prune<HT, 16, 32>), grid, dim3(256), 0, s, h, groups, vals, idx);
-  }
-  return hipGetLastError();
+  if (bf16)
+    hipLaunchKernelGGL((k_nm_prune16<N, M>), grid, dim3(256), 0, s, (const uint16_t *)h, groups, (uint16_t *)vals, idx);
+  else
+    hipLaunchKernelGGL((k_nm_prune32<N, M>), grid, dim3(256), 0, s, (const float *)h, groups, (float *)vals, idx);
 }
 
 hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, void *vals, uint8_t *idx,
                            hipStream_t s) {
   const size_t groups = (size_t)T * (f / m);
   if (groups == 0) return hipSuccess;
-  if (bf16) return prune_t<uint16_t>((const uint16_t *)h, groups, n, m, (uint16_t *)vals, idx, s);
-  return prune_t<float>((const float *)h, groups, n, m, (float *)vals, idx, s);
+  if (n == 2 && m == 4) prune_launch<2, 4>(h, groups, vals, idx, bf16, s);
+  else if (n == 4 && m == 8) prune_launch<4, 8>(h, groups, vals, idx, bf16, s);
+  else if (n == 8 && m == 16) prune_launch<8, 16>(h, groups, vals, idx, bf16, s);
+  else prune_launch<16, 32>(h, groups, vals, idx, bf16, s);
+  return hipGetLastError();
 }
 
 // ------------------------------------------------------------------- nm_ffn_down

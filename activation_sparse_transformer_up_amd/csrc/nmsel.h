@@ -39,50 +39,28 @@ template <int L> TW_DEV void oddeven_desc(uint32_t (&a)[L]) {
   });
 }
 
-// keep[i] for the M raw bit patterns of one block (bf16 in the low 16 bits, or fp32).
-// bf16: the ranks are those of the unique keys (magnitude << log2 M) | (M - 1 - i); every
-// supported pattern keeps N = M / 2, and the N largest keys are found by sorting each half
-// of the block (descending) and taking c_i = max(a_i, b_{N-1-i}), whose minimum is the
-// N-th largest key. fp32 (31-bit magnitudes) counts the ranks directly.
-template <int BYTES, int N, int M> TW_DEV void nm_keep(const uint32_t (&bits)[M], bool (&keep)[M]) {
-  if constexpr (BYTES == 2) {
-    static_assert(2 * N == M, "bf16 selection keeps half of each block");
-    constexpr int LOGM = 31 - __builtin_clz(M);
-    uint32_t key[M], a[N], b[N];
-    static_for<M>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      key[i] = ((bits[i] & 0x7FFFu) << LOGM) | (uint32_t)(M - 1 - i);
-      if constexpr (i < N) a[i] = key[i];
-      else b[i - N] = key[i];
-    });
-    oddeven_desc<N>(a);
-    oddeven_desc<N>(b);
-    uint32_t th = 0xFFFFFFFFu;
-    static_for<N>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      const uint32_t c = a[i] > b[N - 1 - i] ? a[i] : b[N - 1 - i];
-      th = c < th ? c : th;
-    });
-    static_for<M>([&](auto I) { keep[decltype(I)::value] = key[decltype(I)::value] >= th; });
-  } else {
+// fp32: keep[i] for the M raw bit patterns of one block, by counting each entry's rank
+// directly on the 31-bit magnitudes (M^2 comparisons; fp32 blocks are not the bandwidth-
+// critical case).
+template <int N, int M> TW_DEV void nm_keep32(const uint32_t (&bits)[M], bool (&keep)[M]) {
 #pragma unroll
-    for (int i = 0; i < M; ++i) {
-      const uint32_t mi = bits[i] & 0x7FFFFFFFu;
-      int rank = 0;
+  for (int i = 0; i < M; ++i) {
+    const uint32_t mi = bits[i] & 0x7FFFFFFFu;
+    int rank = 0;
 #pragma unroll
-      for (int k = 0; k < M; ++k) {
-        if (k == i) continue;
-        const uint32_t mk = bits[k] & 0x7FFFFFFFu;
-        rank += (k < i) ? (mk >= mi) : (mk > mi);
-      }
-      keep[i] = rank < N;
+    for (int k = 0; k < M; ++k) {
+      if (k == i) continue;
+      const uint32_t mk = bits[k] & 0x7FFFFFFFu;
+      rank += (k < i) ? (mk >= mi) : (mk > mi);
     }
+    keep[i] = rank < N;
   }
 }
 
-// bf16 only: the kept set of one block as a mask, bit 31 - i set iff entry i is kept (so
-// count-leading-zeros walks the kept entries in ascending order). With the unique keys of
-// nm_keep and both halves sorted, c_i = max(a_i, b_{N-1-i}) (i < N) are exactly the N
+// bf16: the kept set of one block as a mask, bit 31 - i set iff entry i is kept (so
+// count-leading-zeros walks the kept entries in ascending order). The keys are unique,
+// (magnitude << log2 M) | (M - 1 - i), so their order is the rank order with ties to the
+// lower index; every supported pattern keeps N = M / 2, and with both halves sorted c_i = max(a_i, b_{N-1-i}) (i < N) are exactly the N
 // largest keys, and each names its entry in its low log2 M bits.
 template <int N, int M> TW_DEV uint32_t nm_kept_mask(const uint32_t (&bits)[M]) {
   static_assert(2 * N == M, "bf16 selection keeps half of each block");
