@@ -111,34 +111,42 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
   }
 }
 
-// Backup rows: one wave per (overflow row r < min(ovf_n, cap), 64-column block); the
-// block's nonzero gates are taken ENT at a time in ascending column order.
+// Backup rows: wave (r0, blk) takes the 64-column block blk of the overflow rows r0,
+// r0 + rstep, ... below min(ovf_n, cap); the block's nonzero gates are taken ENT at a time
+// in ascending column order. The grid covers rstep = min(cap, kGateBackupRows) rows, not the
+// whole capacity: the overflow count is only known on the device, and it is usually zero, so
+// most of a capacity-sized grid would start only to exit.
+constexpr int kGateBackupRows = 8;
+
 template <typename XT, typename VT>
 __global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__restrict__ x,
-                                                         const XT *__restrict__ wu, int d) {
+                                                         const XT *__restrict__ wu, int d, int rstep) {
   const int wave_g = blockIdx.x * 4 + (threadIdx.x >> 6);
   const int nblk = (h.cols + 63) / 64;
-  const int r = wave_g / nblk, blk = wave_g % nblk;
-  if (r >= min(*h.ovf_n, h.cap)) return;                        // wave-uniform
+  const int r0 = wave_g / nblk, blk = wave_g % nblk;
+  if (r0 >= rstep) return;                                      // past the grid's rows
+  const int nr = min(*h.ovf_n, h.cap);
   const int lane = lane_id();
-  const int t = h.ovf_rows[r];
-  VT *row = (VT *)h.ovf_dense + (size_t)r * h.cols;
   const int j = blk * 64 + lane;
-  const float g = j < h.cols ? Elem<VT>::load(row, j) : 0.f;
-  uint64_t m = ballot64(g != 0.f);
-  while (m) {
-    int col[kGateEnt];
+  for (int r = r0; r < nr; r += rstep) {                        // wave-uniform
+    const int t = h.ovf_rows[r];
+    VT *row = (VT *)h.ovf_dense + (size_t)r * h.cols;
+    const float g = j < h.cols ? Elem<VT>::load(row, j) : 0.f;
+    uint64_t m = ballot64(g != 0.f);
+    while (m) {
+      int col[kGateEnt];
 #pragma unroll
-    for (int k = 0; k < kGateEnt; ++k) {
-      col[k] = m ? blk * 64 + (int)__builtin_ctzll(m) : -1;
-      m &= m ? m - 1 : 0;
-    }
-    float u[kGateEnt];
-    wave_dots<XT, 8>(x + (size_t)t * d, wu, d, col, u);
+      for (int k = 0; k < kGateEnt; ++k) {
+        col[k] = m ? blk * 64 + (int)__builtin_ctzll(m) : -1;
+        m &= m ? m - 1 : 0;
+      }
+      float u[kGateEnt];
+      wave_dots<XT, 8>(x + (size_t)t * d, wu, d, col, u);
 #pragma unroll
-    for (int k = 0; k < kGateEnt; ++k) {
-      const float gk = __shfl(g, col[k] & 63, 64);
-      if (lane == 0 && col[k] >= 0) Elem<VT>::store(row, col[k], gk * u[k]);
+      for (int k = 0; k < kGateEnt; ++k) {
+        const float gk = __shfl(g, col[k] & 63, 64);
+        if (lane == 0 && col[k] >= 0) Elem<VT>::store(row, col[k], gk * u[k]);
+      }
     }
   }
 }
@@ -225,21 +233,22 @@ hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int b
     const int nchunk = gate_chunks(d, bf16);
     const int ntb = (h.rows + 15) / 16;
     const dim3 grid((unsigned)(8 * (size_t)ntb * ((nchunk + 7) / 8))), rows4((h.rows + 3) / 4);
-    const size_t nb = (size_t)h.cap * ((h.cols + 63) / 64);
+    const int rstep = min(h.cap, kGateBackupRows);
+    const size_t nb = (size_t)rstep * ((h.cols + 63) / 64);
     const dim3 gridb((unsigned)((nb + 3) / 4));
     if (bf16) {
       const uint16_t *xx = (const uint16_t *)x, *ww = (const uint16_t *)wu;
       hipLaunchKernelGGL((k_gate_part<uint16_t>), grid, dim3(256), 0, s, h, d, nchunk, ntb, xx, ww, ws);
       if (nb) {
-        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
-        else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d);
+        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+        else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
       }
     } else {
       const float *xx = (const float *)x, *ww = (const float *)wu;
       hipLaunchKernelGGL((k_gate_part<float>), grid, dim3(256), 0, s, h, d, nchunk, ntb, xx, ww, ws);
       if (nb) {
-        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
-        else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d);
+        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+        else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
       }
     }
     hipLaunchKernelGGL(k_gate_sum, rows4, dim3(256), 0, s, h, nchunk, ws);
@@ -250,23 +259,24 @@ hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int b
   const int groups = (h.n_t * h.S + 4 * kGateEnt - 1) / (4 * kGateEnt);
   const int P = max(1, min(groups, (2048 + h.rows - 1) / h.rows));
   const dim3 grid((unsigned)((size_t)h.rows * P));
-  const size_t nb = (size_t)h.cap * ((h.cols + 63) / 64);
+  const int rstep = min(h.cap, kGateBackupRows);
+  const size_t nb = (size_t)rstep * ((h.cols + 63) / 64);
   const dim3 gridb((unsigned)((nb + 3) / 4));
   if (bf16) {
     const uint16_t *xx = (const uint16_t *)x, *ww = (const uint16_t *)wu;
     if (d <= 2048) hipLaunchKernelGGL((k_gate_dot<uint16_t, 4>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     else hipLaunchKernelGGL((k_gate_dot<uint16_t, 8>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     if (nb) {
-      if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
-      else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d);
+      if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+      else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
     }
   } else {
     const float *xx = (const float *)x, *ww = (const float *)wu;
     if (d <= 1024) hipLaunchKernelGGL((k_gate_dot<float, 4>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     else hipLaunchKernelGGL((k_gate_dot<float, 8>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     if (nb) {
-      if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d);
-      else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d);
+      if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+      else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
     }
   }
   return hipGetLastError();
