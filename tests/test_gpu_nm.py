@@ -70,6 +70,29 @@ def test_nm_prune_small_group_counts(n, m, groups):
     assert np.array_equal(np.signbit(gv), np.signbit(want_v))
 
 
+@pytest.mark.parametrize("n,m", PATTERNS)
+def test_nm_prune_extreme_bf16_patterns(n, m):
+    """Infinities, the largest finite value, the smallest subnormal and both zeros, mixed with
+    ordinary values: magnitudes compare as sign-cleared bit patterns (monotone for these), and
+    the kept set, order and signs equal the oracle's."""
+    say("nm_prune extreme", n, m)
+    rng = np.random.default_rng(m * 13 + n)
+    special = np.array([0x7F80, 0xFF80, 0x7F7F, 0xFF7F, 0x0001, 0x8001, 0x0000, 0x8000, 0x3F80, 0xBF80],
+                       dtype=np.uint16)
+    bits = rng.choice(special, size=(9, 64 * m)).astype(np.uint16)
+    ordinary = synth.f32_to_bf16_bits(rng.standard_normal((9, 64 * m)).astype(np.float32))
+    mix = rng.random((9, 64 * m)) < 0.4
+    bits = np.where(mix, ordinary, bits).astype(np.uint16)
+    h64 = orc.widen(bits, "bf16")
+    vals, idx = tw.nm_prune(to_dev(bits, "bf16"), n, m)
+    torch.cuda.synchronize()
+    want_v, want_i = orc.nm_prune(h64, n, m)
+    assert np.array_equal(from_dev(idx), want_i)
+    gv = from_dev(vals)
+    assert np.array_equal(gv, want_v)
+    assert np.array_equal(np.signbit(gv), np.signbit(want_v))
+
+
 def test_nm_prune_c4_full_bit_exact():
     """c4: h = ReLU(x W1) on the GPU (b1 = 0, about half active), pruned 8:16 and 16:32."""
     say("nm_prune c4 full")
