@@ -108,8 +108,10 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
     }
   };
 
-  if (h.ovf_slot[t] < 0) {
-    const int nnz = h.row_nnz[t];
+  // the overflow slot and the list length in one round trip
+  const int slot0 = h.ovf_slot[t], nnz0 = h.row_nnz[t];
+  if (slot0 < 0) {
+    const int nnz = nnz0;
     const uint2 *src = h.row_list + (size_t)t * h.n_t * h.S;
     for (int base = 0; base < nnz; base += 64) {
       const int n = min(64, nnz - base);
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
       __syncthreads();
     }
   } else {
-    const VT *row = (const VT *)h.ovf_dense + (size_t)h.ovf_slot[t] * h.cols;
+    const VT *row = (const VT *)h.ovf_dense + (size_t)slot0 * h.cols;
     for (int c0 = 0; c0 < h.cols; c0 += 64) {
       const int j = c0 + lane;
       const float v = j < h.cols ? ldv(row, j) : 0.f;
@@ -232,8 +234,10 @@ __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restr
   const int t = tb * 16 + wave * 4 + g;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
-  const bool normal = t < h.rows && h.ovf_slot[t] < 0;
-  const int nnz = normal ? h.row_nnz[t] : 0;
+  const int tc = t < h.rows ? t : 0;                       // slot and length in one round trip
+  const int slot0 = h.ovf_slot[tc], nnz0 = h.row_nnz[tc];
+  const bool normal = t < h.rows && slot0 < 0;
+  const int nnz = normal ? nnz0 : 0;
   int n = max(nnz, __shfl_xor(nnz, 16, 64));
   n = max(n, __shfl_xor(n, 32, 64));
   const uint2 *lp = h.row_list + (size_t)(t < h.rows ? t : 0) * h.n_t * h.S;
@@ -271,7 +275,7 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
   const int cap = h.n_t * h.S;
   const uint2 *src = h.row_list + (size_t)t * cap;
   if (tid < LW) lst[tid] = tid < cap ? src[tid] : make_uint2(0, 0);
-  const int slot = h.ovf_slot[t];
+  const int slot = h.ovf_slot[t], nnz = h.row_nnz[t];      // one round trip with the list
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -279,7 +283,6 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
     if (wave == 0) backup_row<WT, VT, YT>(h, w2, d, y, slot, c, lst);
     return;
   }
-  const int nnz = h.row_nnz[t];
   __syncthreads();
   for (int base = 0; base < nnz; base += LW) {
     if (base > 0) {
@@ -347,7 +350,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   const uint2 *src = h.row_list + (size_t)t * cap;
   const int e0 = 16 * wave + lane;
   uint2 pn = (lane < 16 && e0 < cap) ? src[e0] : make_uint2(0, 0);
-  const int slot = h.ovf_slot[t];
+  const int slot = h.ovf_slot[t], nnz = h.row_nnz[t];      // one round trip with the list
   if (slot >= 0) {
     const int cn = 4 * c + wave;                            // this wave's 16-lane chunk
     if (cn * 16 * E < d) backup_row<WT, VT, YT>(h, w2, d, y, slot, cn, lst[wave]);
@@ -356,7 +359,6 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   const int col = c * CW + lane * E;
   const bool cv = col < d;
   const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
-  const int nnz = h.row_nnz[t];
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
