@@ -36,6 +36,21 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 // ------------------------------------------------------------------ 1. counts / scan
 
+// A dense backup row is walked by one wave, 64 columns per step; the loads of kDenseBatch
+// steps are issued before any is used (addresses clamped into the row; columns past the
+// row read as zero), so the walk waits for memory once per batch rather than once per step.
+constexpr int kDenseBatch = 8;
+
+template <typename VT>
+TW_DEV void dense_batch(const VT *row, int cols, int j0, float (&v)[kDenseBatch]) {
+#pragma unroll
+  for (int u = 0; u < kDenseBatch; ++u) {
+    const int j = j0 + u * 64;
+    const float x = Elem<VT>::load(row, j < cols ? j : cols - 1);
+    v[u] = j < cols ? x : 0.f;
+  }
+}
+
 // nnz[t] = entries of row t: the nonzeros of its backup row (counted in that row, so the
 // fill below writes exactly this many), else the stored slots.
 // Also clears tot[0 .. f] (the per-unit totals k_col_mask accumulates into).
@@ -50,7 +65,12 @@ __global__ __launch_bounds__(256) void k_row_nnz(TwellIn h, int32_t *__restrict_
   int s = 0;
   if (slot >= 0) {
     const VT *row = (const VT *)h.ovf_dense + (size_t)slot * h.cols;
-    for (int j = lane; j < h.cols; j += 64) s += Elem<VT>::load(row, j) != 0.f;
+    for (int j0 = 0; j0 < h.cols; j0 += 64 * kDenseBatch) {
+      float v[kDenseBatch];
+      dense_batch<VT>(row, h.cols, j0 + lane, v);
+#pragma unroll
+      for (int u = 0; u < kDenseBatch; ++u) s += v[u] != 0.f;
+    }
   } else {
     for (int k = lane; k < h.n_t; k += 64) s += min(h.counts[(size_t)t * h.n_t + k], h.S);
   }
@@ -112,17 +132,21 @@ __global__ __launch_bounds__(256) void k_csr_fill(TwellIn h, const int32_t *__re
   int n = 0;
   if (slot >= 0) {
     const VT *row = (const VT *)h.ovf_dense + (size_t)slot * h.cols;
-    for (int c0 = 0; c0 < h.cols; c0 += 64) {
-      const int j = c0 + lane;
-      const float v = j < h.cols ? Elem<VT>::load(row, j) : 0.f;
-      const bool nz = v != 0.f;
-      const uint64_t m = ballot64(nz);
-      const int pos = base + n + (int)mbcnt64(m);
-      if (nz && pos < lim) {
-        col[pos] = j;
-        hval[pos] = v;
+    for (int c0 = 0; c0 < h.cols; c0 += 64 * kDenseBatch) {
+      float v[kDenseBatch];
+      dense_batch<VT>(row, h.cols, c0 + lane, v);
+#pragma unroll
+      for (int u = 0; u < kDenseBatch; ++u) {
+        const int j = c0 + u * 64 + lane;
+        const bool nz = v[u] != 0.f;
+        const uint64_t m = ballot64(nz);
+        const int pos = base + n + (int)mbcnt64(m);
+        if (nz && pos < lim) {
+          col[pos] = j;
+          hval[pos] = v[u];
+        }
+        n += __popcll(m);
       }
-      n += __popcll(m);
     }
   } else {
     for (int k0 = 0; k0 < h.n_t; k0 += 64) {
