@@ -380,6 +380,8 @@ __global__ __launch_bounds__(1024) void k_col_off(int NB, int f, const int32_t *
   }
 }
 
+constexpr int kCscBatch = 4;
+
 // Every CSR entry (t, j) goes to position off[t/32][j] + popc(mask[t/32][j] & lower bits)
 // of the unit-major lists: (t, h) for dw2, (t, dz) for dw1t.
 __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32_t *__restrict__ row_ptr,
@@ -393,12 +395,32 @@ __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32
   const int b = t >> 5, bit = t & 31;
   const uint32_t lower = (1u << bit) - 1u;
   const int s = row_ptr[t], e = row_ptr[t + 1];
-  for (int k = s + lane; k < e; k += 64) {
-    const int j = col[k];
-    const size_t bj = (size_t)b * f + j;
-    const int pos = off[bj] + __popc(mask[bj] & lower);
-    th[pos] = make_uint2((uint32_t)t, __float_as_uint(hval[k]));
-    tdz[pos] = make_uint2((uint32_t)t, dz[k].y);
+  // kCscBatch rounds of 64 entries: their loads (clamped to entry s) are all issued before
+  // the scattered stores, which would otherwise hold back the next round's loads
+  for (int k0 = s; k0 < e; k0 += 64 * kCscBatch) {
+    int j[kCscBatch];
+    uint32_t hv[kCscBatch], dv[kCscBatch];
+#pragma unroll
+    for (int u = 0; u < kCscBatch; ++u) {
+      const int k = k0 + u * 64 + lane;
+      const int kc = k < e ? k : s;
+      j[u] = col[kc];
+      hv[u] = __float_as_uint(hval[kc]);
+      dv[u] = dz[kc].y;
+    }
+    int pos[kCscBatch];
+#pragma unroll
+    for (int u = 0; u < kCscBatch; ++u) {
+      const size_t bj = (size_t)b * f + j[u];
+      pos[u] = off[bj] + __popc(mask[bj] & lower);
+    }
+#pragma unroll
+    for (int u = 0; u < kCscBatch; ++u) {
+      if (k0 + u * 64 + lane < e) {
+        th[pos[u]] = make_uint2((uint32_t)t, hv[u]);
+        tdz[pos[u]] = make_uint2((uint32_t)t, dv[u]);
+      }
+    }
   }
 }
 
