@@ -147,10 +147,9 @@ class TwellMatrix:
         self.ovf_bits = torch.empty((max(words, 1),), **i32)
         self.row_nnz = torch.empty((max(rows, 1),), **i32)
         lb = lib().twell_row_list_bytes(rows, cols, tile_w, slots)
-        # up to DECODE_MAX_T rows the scratch also holds the decode GEMM's tickets, which must
-        # start at zero (every call leaves them zero)
-        alloc = torch.zeros if rows <= DECODE_MAX_T else torch.empty
-        self.row_list = alloc((max(lb // 8, 2),), dtype=torch.int64, device=device)
+        # up to DECODE_MAX_T rows the scratch also holds the decode GEMM's workspace and
+        # tickets; none of it needs initialising
+        self.row_list = torch.empty((max(lb // 8, 2),), dtype=torch.int64, device=device)
 
     def c(self) -> TwellMatrixC:
         return TwellMatrixC(self.rows, self.cols, self.tile_w, self.slots, self.ovf_cap,

@@ -57,7 +57,7 @@ TwellOut out_of(const twell_matrix_t *m) {
   if (m->row_list && m->rows <= kDecodeMaxT) {
     char *ws = (char *)m->row_list + align256(list_bytes(m->rows, m->cols, m->tile_w, m->slots));
     o.dec_part = (float *)ws;
-    o.dec_ticket = (uint32_t *)(ws + dec_tiles(m->cols) * 2 * kDecHalfBytes);
+    o.dec_ticket = (uint64_t *)(ws + dec_tiles(m->cols) * 2 * kDecHalfBytes);
   }
   o.n_t = m->cols / m->tile_w;
   o.S = m->slots;
@@ -226,6 +226,10 @@ static int down_args(const twell_matrix_t *h, const void *w2, int32_t w_dtype, i
   if (d_model <= 0) return TWELL_ERR_SHAPE;
   if (d_model % 8) return TWELL_ERR_ALIGN;
   if (!al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
+  // the gathers address W2 rows (and y) with 32-bit byte offsets
+  const size_t wb = w_dtype == TWELL_BF16 ? 2 : 4, yb = y_dtype == TWELL_BF16 ? 2 : 4;
+  if ((size_t)h->cols * d_model * wb >= ((size_t)1 << 31) || (size_t)h->rows * d_model * yb >= ((size_t)1 << 31))
+    return TWELL_ERR_UNSUPPORTED;
   return TWELL_OK;
 }
 

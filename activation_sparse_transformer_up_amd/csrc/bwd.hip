@@ -424,6 +424,24 @@ __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32
   }
 }
 
+// More overflow rows than backup slots (*ovf_n > cap): the rows beyond the backup kept only
+// their first S entries per tile, so their gradients cannot be formed. Every output is then
+// overwritten with a quiet NaN, so that the condition cannot pass unnoticed; otherwise the
+// kernel exits at once (one scalar load per workgroup).
+__global__ __launch_bounds__(256) void k_bwd_poison(const int32_t *__restrict__ ovf_n, int cap, float *dx, size_t ndx,
+                                                    float *dw1t, float *dw2, size_t ndw, float *db1, size_t ndb) {
+  if (*ovf_n <= cap) return;
+  const float qnan = __uint_as_float(0x7FC00000u);
+  const size_t stride = (size_t)gridDim.x * 256;
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < ndw; i += stride) {
+    dw1t[i] = qnan;
+    dw2[i] = qnan;
+    if (i < ndx) dx[i] = qnan;
+    if (db1 && i < ndb) db1[i] = qnan;
+  }
+  for (size_t i = ndw + (size_t)blockIdx.x * 256 + threadIdx.x; i < ndx; i += stride) dx[i] = qnan;
+}
+
 __global__ __launch_bounds__(256) void k_fill_zero(int32_t *p, int n) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i < n) p[i] = 0;
@@ -518,6 +536,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   hipLaunchKernelGGL(k_order_by_len, dim3(1), dim3(1024), 0, s, f, col_ptr, perm_u);
   gather(f, col_ptr, perm_u, th, a.dy, a.dw2, nullptr);
   gather(f, col_ptr, perm_u, tdz, a.x, a.dw1t, a.db1);
+  hipLaunchKernelGGL(k_bwd_poison, dim3(256), dim3(256), 0, s, h.ovf_n, a.cap, a.dx, (size_t)T * d, a.dw1t, a.dw2,
+                     (size_t)f * d, a.db1, (size_t)f);
   return hipGetLastError();
 }
 

@@ -985,16 +985,32 @@ TW_DEV void row_add_lds(f32x16_t (&a)[TileD::NB], const float *red) {
     for (int r = 0; r < 16; ++r) a[nb][r] += red[(nb * 16 + r) * 64 + lane];
 }
 
-// Cross-workgroup hand-over of the half sums (k_up_twell_dec). Every access to the workspace is an atomic of
-// agent scope: such accesses are coherent across the XCDs' separate L2 caches on their own
-// (stores write through, loads do not hit a stale line). The half sum is stored, its stores
-// are waited for (vmcnt(0)) and only then is the ticket taken, so a workgroup that draws
-// ticket 1 reads a completely stored other half: its loads are issued after the ticket's
-// value has returned. An agent-scope release/acquire pair would add an L2 write-back and
-// invalidate per workgroup (several microseconds per launch) that only plain stores need.
-// The second arriver resets the ticket for the next launch; tickets start at zero. Both
-// waves of a workgroup store (and later load) their own block rows; wave 0 takes the one
-// ticket after a barrier that follows both waves' store waits.
+// Cross-workgroup hand-over of the half sums (k_up_twell_dec, k_up_gemv_twell). Every access
+// to the workspace is an atomic of agent scope: such accesses are coherent across the XCDs'
+// separate L2 caches on their own (stores write through, loads do not hit a stale line). The
+// half sum is stored, its stores are waited for (vmcnt(0)) and only then is the ticket taken,
+// so the workgroup that arrives second reads a completely stored other half: its loads are
+// issued after the ticket's value has returned. An agent-scope release/acquire pair would
+// add an L2 write-back and invalidate per workgroup (several microseconds per launch) that
+// only plain stores need.
+//
+// The ticket is a 64-bit word that each of the tile's two workgroups swaps for its own tag
+// (an arbitrary 64-bit constant per half). The workgroup that gets back the other half's tag
+// arrived second: it zeroes the word and finishes the tile. Any other value it gets back
+// (zero after an earlier launch, or whatever an uninitialised buffer holds) means it arrived
+// first. So the workspace needs no initialisation; only a word that happens to hold one of
+// the two tags before the first launch would mislead a tile (one chance in 2^63). Both waves
+// of a workgroup store (and later load) their own block rows; wave 0 takes the one ticket
+// after a barrier that follows both waves' store waits.
+TW_DEV uint64_t dec_tag(int half) { return half ? 0xBB67AE8584CAA73Bull : 0x6A09E667F3BCC908ull; }
+
+// true if this workgroup (half `half` of the tile) arrived second; then the ticket is zeroed.
+TW_DEV bool dec_meet(uint64_t *ticket, int half) {
+  const uint64_t old = __hip_atomic_exchange(ticket, dec_tag(half), __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  const bool second = old == dec_tag(1 - half);
+  if (second) __hip_atomic_store(ticket, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  return second;
+}
 // Half sum of block row MB to the workspace (element r of block (MB, nb) of lane l at
 // ((MB * NB + nb) * 16 + r) * 64 + l), agent-scope stores of the live row groups only.
 template <int MB> TW_DEV void dec_store_row(const f32x16_t (&acc)[TileD::MB][TileD::NB], int M, float *mine) {
@@ -1032,7 +1048,7 @@ template <int MB> TW_DEV void dec_add_row(f32x16_t (&acc)[TileD::MB][TileD::NB],
 
 // Grid: 2 * ceil(N / 128) workgroups of 128 threads; workgroup b takes tile b % n_tiles and
 // half b / n_tiles (quarters 2 half, 2 half + 1). Workspace o.dec_part [n_tiles][2][kDecTileF]
-// fp32 and o.dec_ticket [n_tiles] (zero between launches).
+// fp32 and o.dec_ticket [n_tiles] (see dec_meet).
 template <typename T, int W, typename VT>
 __global__ __launch_bounds__(128) void k_up_twell_dec(const T *__restrict__ x, const T *__restrict__ w1t,
                                                       const float *__restrict__ b1, int M, int N, int K,
@@ -1075,11 +1091,10 @@ __global__ __launch_bounds__(128) void k_up_twell_dec(const T *__restrict__ x, c
   block_barrier_lds();
   uint32_t *tk = (uint32_t *)(smem + kDecTicketOff);
   const int lane = threadIdx.x & 63;
-  if (w == 0 && lane == 0) *tk = __hip_atomic_fetch_add(o.dec_ticket + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  if (w == 0 && lane == 0) *tk = dec_meet(o.dec_ticket + tile, half) ? 1u : 0u;
   block_barrier_lds();
   const uint32_t t = (uint32_t)__builtin_amdgcn_readfirstlane((int)*tk);
   if (t == 0) return;                       // first to arrive: the other workgroup finishes
-  if (w == 0 && lane == 0) __hip_atomic_store(o.dec_ticket + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   if (w == 0) dec_add_row<0>(acc, M, part + (1 - half) * kDecTileF);
   else dec_add_row<1>(acc, M, part + (1 - half) * kDecTileF);
   epi_twell<TileD, W, VT>(acc, nbias, M, N, 0, n0, o, smem, w);
@@ -1348,8 +1363,7 @@ TW_DEV void gemv_twell_epi(const float *zs, const float *__restrict__ b1, int M,
 }
 
 // Grid: 2 * ceil(N / 128) workgroups of 512 threads; workgroup b takes tile b % n_tiles and
-// half b / n_tiles of K. Workspace as k_up_twell_dec (o.dec_part, o.dec_ticket zero between
-// launches).
+// half b / n_tiles of K. Workspace as k_up_twell_dec (o.dec_part, o.dec_ticket; see dec_meet).
 template <int TT, int W, typename VT>
 __global__ __launch_bounds__(512) void k_up_gemv_twell(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w1t,
                                                        const float *__restrict__ b1, int M, int N, int K, TwellOut o) {
@@ -1366,11 +1380,7 @@ __global__ __launch_bounds__(512) void k_up_gemv_twell(const uint16_t *__restric
     __hip_atomic_store(part + half * kDecTileF + i, zs[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   wait_vmcnt<0>();
   __syncthreads();                       // every half-sum store of this workgroup has completed
-  if (tid == 0) {
-    const uint32_t tk = __hip_atomic_fetch_add(o.dec_ticket + tile, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    last = tk != 0;
-    if (tk != 0) __hip_atomic_store(o.dec_ticket + tile, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  }
+  if (tid == 0) last = dec_meet(o.dec_ticket + tile, half);
   __syncthreads();
   if (!last) return;
   for (int i = tid; i < kGemvUnits * TT; i += 512)

@@ -8,13 +8,14 @@
 namespace tw {
 
 // The up GEMM of at most kDecodeMaxT tokens splits each 128-column tile over two workgroups
-// that meet in a workspace: two fp32 half sums of 64 x 128 per tile, then one uint32 ticket
-// per tile (zero between launches). It sits in the row-list scratch, after the lists.
+// that meet in a workspace: two fp32 half sums of 64 x 128 per tile, then one 64-bit ticket
+// per tile. It sits in the row-list scratch, after the lists. A ticket may hold any value
+// before a launch (see dec_meet in gemm.hip); every launch leaves it zero.
 constexpr int kDecodeMaxT = 64;
 constexpr size_t kDecHalfBytes = 64 * 128 * 4;
 inline size_t dec_tiles(int cols) { return (size_t)(cols + 127) / 128; }
 inline size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
-inline size_t dec_ws_bytes(int cols) { return dec_tiles(cols) * 2 * kDecHalfBytes + align256(dec_tiles(cols) * 4); }
+inline size_t dec_ws_bytes(int cols) { return dec_tiles(cols) * 2 * kDecHalfBytes + align256(dec_tiles(cols) * 8); }
 
 // Output side of a TwELL-producing kernel (see twell_matrix_t in include/twell.h).
 struct TwellOut {
@@ -23,7 +24,7 @@ struct TwellOut {
   void *vals;
   uint32_t *ovf_bits;
   float *dec_part;        // decode workspace (rows <= kDecodeMaxT): [tiles][2][64 x 128] fp32
-  uint32_t *dec_ticket;   // [tiles]
+  uint64_t *dec_ticket;   // [tiles]
   int n_t, S, words, val_bf16;
 };
 

@@ -67,9 +67,29 @@ def cpu_baseline(g, w, T_sample: int, min_seconds: float = 10.0) -> dict:
         t_total += time.perf_counter() - t0
         reps += 1
     return {"value": T_sample * reps / t_total, "unit": "tokens/s", "cores": int(threads),
-            "kind": "oracle",
+            "kind": "oracle", "nproc": os.cpu_count(), "affinity_cpus": _affinity(),
+            "cpu_model": _cpu_model(),
             "sample": f"{T_sample} tokens of the {w.name} workload x {reps} repetitions "
-                      f"(fp64 numpy forward + TwELL pack, {t_total:.1f} s)"}
+                      f"(fp64 numpy forward + TwELL pack, {t_total:.1f} s; 'cores' is the BLAS "
+                      f"thread count numpy used)"}
+
+
+def _cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    import platform
+    return platform.processor() or "unknown"
+
+
+def _affinity():
+    try:
+        return len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        return None
 
 
 def counter_traffic(workload: str):
@@ -444,10 +464,46 @@ def leg_c5(steps, warmup):
         xd.grad = w1d.grad = w2d.grad = bd.grad = None
 
     ms_dense = _time(dense_step, steps, warmup)
+    del xd, w1d, w2d, bd, x, w1t, w2, dy, b1, h, y
+    torch.cuda.empty_cache()
+    # hot tokens (every 1024th token's x scaled by 4, so those rows overflow) at S = 8 and 16
+    variants = {f"hot1024_S{S}": c5_variant(w.with_(slots=S, hot_every=1024), cap, steps, warmup)
+                for S in (8, 16)}
+    achieved = 2.0 * T * d * f / (ms_up * 1e-3) / 1e12
     return {"tokens_per_s": T / (ms * 1e-3), "ms_fwd_bwd": ms, "ms_fwd": ms_fwd, "ms_bwd": ms - ms_fwd,
             "dense_ms_fwd_bwd": ms_dense, "speedup_vs_dense": ms_dense / ms, "density": dens,
             "up_gemm_ms": ms_up, "up_gemm_frac_mfma_peak": up_frac,
-            "overflow_rows": ovf, "slots": w.slots, "tile_w": w.tile_w, "activation_memory": mem}
+            "roofline": {"kernel": "k_up_twell (up GEMM + fused ReLU/TwELL epilogue)", "bound": "mfma",
+                         "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                         "frac": achieved / PEAK_BF16_TFLOPS, "traffic": None,
+                         "per_launch_flop": 2.0 * T * d * f, "avg_launch_ms": ms_up},
+            "overflow_rows": ovf, "slots": w.slots, "tile_w": w.tile_w, "activation_memory": mem,
+            "variants": variants}
+
+
+def c5_variant(w, cap, steps, warmup):
+    """Forward + backward time of one c5 variant (hot tokens, slot count)."""
+    import torch
+    import activation_sparse_transformer_up_amd as tw
+    import synth
+    dev = torch.device("cuda:0")
+    g = synth.generate(w)
+    x, w1t, w2, dy = (_up(g[k], "bf16", dev) for k in ("x", "w1t", "w2", "dy"))
+    b1 = _up(g["b1"], "f32", dev)
+    T, f, d = w.T, w.f, w.d
+    h = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.float32, dev)
+    y = torch.empty((T, d), device=dev)
+    ws = torch.empty((tw.twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype),), dtype=torch.uint8, device=dev)
+
+    def step():
+        tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y)
+        tw.twell_ffn_bwd(x, w1t, w2, h, dy, w.l1_coef, workspace=ws)
+
+    ms = _time(step, steps, warmup)
+    ms_fwd = _time(lambda: tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y), steps, warmup)
+    return {"slots": w.slots, "hot_every": w.hot_every, "ms_fwd_bwd": ms, "ms_fwd": ms_fwd,
+            "tokens_per_s": T / (ms * 1e-3), "overflow_rows": int(h.ovf_n.item()),
+            "capacity_ok": tw.twell_sync_status(h) == 0}
 
 
 def main():

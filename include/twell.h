@@ -38,7 +38,7 @@
 extern "C" {
 #endif
 
-#define TWELL_ABI_VERSION 3
+#define TWELL_ABI_VERSION 4
 
 typedef enum { TWELL_F32 = 0, TWELL_BF16 = 1 } twell_dtype_t;
 
@@ -76,9 +76,11 @@ typedef enum {
  *                                   twell_down before use; twell_row_list_bytes bytes.
  *                                   For R <= 64 it also holds the decode workspace of the
  *                                   up GEMM (after the lists): fp32 half sums of the K split
- *                                   and one uint32 ticket per 128 columns. The tickets must
- *                                   be zero when the buffer is first used (allocate it
- *                                   zero-filled); every call leaves them zero. Calls that
+ *                                   and one 64-bit ticket per 128 columns. No part of
+ *                                   row_list needs initialising: the two workgroups of a
+ *                                   tile meet by swapping the ticket for their own tag
+ *                                   constant, and any other previous value (an earlier
+ *                                   call leaves zero) reads as "arrived first". Calls that
  *                                   overlap on one h race.
  *
  * A row overflows iff some tile of it holds more than `slots` nonzeros. A (row, tile)
@@ -116,7 +118,7 @@ size_t twell_ovf_bits_words(int32_t rows, int32_t cols, int32_t tile_w);
 
 /* Bytes that twell_matrix_t.row_list must hold: 8 bytes per slot of the matrix, plus, for
  * rows <= 64, the decode workspace (256-byte aligned after the lists; 64 KB per 128
- * columns and the tickets). */
+ * columns, then 8 bytes of ticket per 128 columns rounded up to 256 bytes). */
 size_t twell_row_list_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slots);
 
 /*
@@ -179,6 +181,9 @@ int twell_fwd_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int
  * twell_down — y[t] = sum over the nonzero h[t, j] of h[t, j] * w2[j] for an existing
  * TwELL h (rows = T, cols = d_ff; ovf_slot must be valid), fp32 accumulation.
  * "Kernels de Inferência": only the active units' rows of W2 are read.
+ * Errors: TWELL_ERR_ARG (null, dtype), TWELL_ERR_SHAPE (d_model <= 0), TWELL_ERR_ALIGN
+ * (d_model % 8, w2 or y not 16-byte aligned), TWELL_ERR_UNSUPPORTED (w2 or y of 2 GiB or
+ * more: rows are addressed with 32-bit byte offsets).
  */
 int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model,
                void *y, int32_t y_dtype, void *stream);
@@ -248,8 +253,10 @@ size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, i
  *   dw1t = dz^T . x                 [f][d]  fp32
  *   dw2  = h^T . dy                 [f][d]  fp32
  *   db1  = sum_t dz                 [f]     fp32 (may be NULL)
- * x, w1t, w2, dy have in_dtype. Requires every overflow row to have a backup slot
- * (*ovf_n <= ovf_cap); rows without one contribute through their slots only.
+ * x, w1t, w2, dy have in_dtype. Every overflow row needs a backup slot (*ovf_n <= ovf_cap):
+ * a row beyond the capacity kept only its first slots per tile, so its gradients cannot be
+ * formed, and then every output (dx, dw1t, dw2 and db1) is overwritten with quiet NaN on the
+ * device, so the condition cannot pass unnoticed (twell_sync_status also reports it).
  * d_ff <= 16384 (a unit bit mask per 32-token block is built in LDS), else
  * TWELL_ERR_UNSUPPORTED; workspace_bytes below twell_ffn_bwd_workspace_bytes gives
  * TWELL_ERR_WORKSPACE.

@@ -49,9 +49,11 @@ def twell_host(h) -> dict:
     """Device TwellMatrix -> dict shaped like the oracle's twell_pack output."""
     cap = h.ovf_cap
     n = int(from_dev(h.ovf_n)[0])
+    k = min(n, cap)
+    # only the stored backup rows: the rest of ovf_dense is uninitialised memory
     return {"counts": from_dev(h.counts), "col_idx": from_dev(h.col_idx), "vals": from_dev(h.vals),
-            "ovf_n": n, "ovf_rows": from_dev(h.ovf_rows)[: min(n, cap)],
-            "ovf_slot": from_dev(h.ovf_slot), "ovf_dense": from_dev(h.ovf_dense)[:cap],
+            "ovf_n": n, "ovf_rows": from_dev(h.ovf_rows)[:k],
+            "ovf_slot": from_dev(h.ovf_slot), "ovf_dense": from_dev(h.ovf_dense[:k]),
             "tile_w": h.tile_w, "slots": h.slots, "ovf_cap": cap, "shape": (h.rows, h.cols)}
 
 

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol():
 
 
 def test_version_and_status_strings():
-    assert tw.twell_abi_version() == 3
+    assert tw.twell_abi_version() == 4
     L = tw.lib()
     for code in [0, -1, -2, -3, -4, -5, -6, -7]:
         s = L.twell_status_str(code).decode()
@@ -55,8 +55,8 @@ def test_row_list_bytes_with_decode_workspace():
     assert L.twell_row_list_bytes(65, 14336, 128, 16) == 65 * 112 * 16 * 8
     assert L.twell_row_list_bytes(4096, 1024, 64, 8) == 4096 * 16 * 8 * 8
     # up to 64 rows: lists rounded up to 256 bytes, then two 64 x 128 fp32 half sums and a
-    # uint32 ticket per 128 columns (the tickets rounded up to 256 bytes)
-    assert L.twell_row_list_bytes(64, 14336, 128, 16) == 64 * 112 * 16 * 8 + 112 * 65536 + 512
+    # 64-bit ticket per 128 columns (the tickets rounded up to 256 bytes)
+    assert L.twell_row_list_bytes(64, 14336, 128, 16) == 64 * 112 * 16 * 8 + 112 * 65536 + 1024
     assert L.twell_row_list_bytes(1, 1984, 64, 3) == 768 + 16 * 65536 + 256     # 15.5 tiles -> 16
     assert L.twell_row_list_bytes(0, 512, 128, 8) == 0 + 4 * 65536 + 256
 
@@ -125,6 +125,11 @@ def test_pack_and_down_reject():
     assert L.twell_down(ctypes.byref(m), FAKE, 1, 100, FAKE, 0, None) == ALIGN
     assert L.twell_down(ctypes.byref(m), None, 1, 256, FAKE, 0, None) == ARG
     assert L.twell_down(ctypes.byref(m), FAKE, 1, 0, FAKE, 0, None) == SHAPE
+    # W2 rows are addressed with 32-bit byte offsets: 2 GiB of w2 (or of y) is refused
+    wide = mat(rows=64, cols=65536)
+    assert L.twell_down(ctypes.byref(wide), FAKE, 1, 16384, FAKE, 0, None) == UNSUP
+    assert L.twell_fwd_down(ctypes.byref(wide), FAKE, 0, 8192, FAKE, 0, None) == UNSUP
+    assert L.twell_down(ctypes.byref(mat(rows=1 << 17, cols=512)), FAKE, 1, 4096, FAKE, 0, None) == UNSUP
     assert L.ffn_up_relu_dense(FAKE, FAKE, None, 1, 4, 256, 512, FAKE, 0, None) == ARG
     assert L.ffn_up_relu_dense(FAKE, FAKE, FAKE, 1, 4, 250, 512, FAKE, 0, None) == ALIGN
     assert L.twell_sync_status(None, None) == ARG

@@ -113,6 +113,29 @@ def test_bwd_deterministic_and_dy_zero():
     assert np.allclose(from_dev(db1), lam * P.sum(0), rtol=1e-6)
 
 
+def test_bwd_capacity_exceeded_poisons_gradients():
+    """More overflow rows than backup slots: the rows beyond the capacity lost entries, so the
+    backward cannot form their gradients; it must not return numbers that look valid. Every
+    output is NaN, and twell_sync_status reports the capacity error. With enough capacity the
+    same inputs give finite gradients."""
+    w = synth.C5.with_(T=300, d=256, f=1024, hot_every=16)
+    g = synth.generate(w)
+    x, w1t, b1, w2 = (to_dev(g["x"], "bf16"), to_dev(g["w1t"], "bf16"), to_dev(g["b1"], "f32"), to_dev(g["w2"], "bf16"))
+    dy = to_dev(g["dy"], "bf16")
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 8, 2)
+    outs = tw.twell_ffn_bwd(x, w1t, w2, h, dy, 2e-5)
+    torch.cuda.synchronize()
+    assert tw.twell_sync_status(h) == -5
+    for t in outs:
+        assert bool(torch.isnan(t).all())
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 8, 300)
+    outs = tw.twell_ffn_bwd(x, w1t, w2, h, dy, 2e-5)
+    torch.cuda.synchronize()
+    assert tw.twell_sync_status(h) == 0
+    for t in outs:
+        assert bool(torch.isfinite(t).all())
+
+
 def test_bwd_workspace_too_small():
     import ctypes
     w = synth.C1.with_(with_dy=True)
@@ -133,9 +156,12 @@ def test_bwd_workspace_too_small():
     torch.cuda.synchronize()
 
 
-def test_c5_full_sampled():
+@pytest.mark.parametrize("S,hot", [(8, 0), (8, 1024), (16, 1024)])
+def test_c5_full_sampled(S, hot):
     """c5 at full size in the bench's launch configuration (T=16384, d=4096, f=14336, bf16,
-    W=128, S=8, backup capacity 1024, fp32 values, l1 2e-5), checked on samples:
+    W=128, backup capacity 1024, fp32 values, l1 2e-5) with S = 8, and with hot tokens (every
+    1024th token's x scaled by 4: about 28% of a hot token's units fire, so every hot row
+    overflows) at S = 8 and S = 16, checked on samples:
       - the TwELL rows of 12 random tokens and 4 overflow rows equal the oracle's packing of
         the GPU's own activations bit for bit (overflow rows: backup slot holds the full row);
       - those activations are within the fp32 error bound of the oracle's, pattern flips only
@@ -143,10 +169,10 @@ def test_c5_full_sampled():
       - dW1t, dW2 and db1 of 8 random and the 4 most active units over all 16384 tokens. The
         units separate in the backward, so the oracle's own backward runs on the sampled units'
         weights with every token and the GPU's pattern."""
-    say("c5 full sampled")
-    w = synth.C5
+    say("c5 full sampled", S, hot)
+    w = synth.C5.with_(slots=S, hot_every=hot)
     g = synth.generate(w)
-    dt, W, S, cap, lam = "bf16", w.tile_w, w.slots, 1024, w.l1_coef
+    dt, W, cap, lam = "bf16", w.tile_w, 1024, w.l1_coef
     x, w1t, w2, dy = (to_dev(g[k], dt) for k in ("x", "w1t", "w2", "dy"))
     b1 = to_dev(g["b1"], "f32")
     y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, cap)
@@ -158,7 +184,9 @@ def test_c5_full_sampled():
     assert n_ovf > 0
     rng = np.random.default_rng(7)
     ovf = from_dev(h.ovf_rows)[:n_ovf]
-    rows = np.unique(np.concatenate([rng.choice(w.T, 12, replace=False), ovf[:4]]))
+    hot_rows = np.arange(0, w.T, hot) if hot else np.zeros(0, np.int64)
+    assert set(hot_rows.tolist()) <= set(ovf.tolist())
+    rows = np.unique(np.concatenate([rng.choice(w.T, 12, replace=False), ovf[:4], hot_rows[1:3]]))
     rt = torch.from_numpy(rows).cuda()
     hs = from_dev(hz[rt])
     want = orc.twell_pack(hs, W, S, len(rows))

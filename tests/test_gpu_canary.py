@@ -48,7 +48,7 @@ def guarded_matrix(T, f, W, S, cap, vdt=torch.float32):
     for name in ("counts", "col_idx", "vals", "ovf_n", "ovf_rows", "ovf_slot", "ovf_dense", "ovf_bits",
                  "row_nnz", "row_list"):
         t = getattr(h, name)
-        g = Guarded(tuple(t.shape), t.dtype, zero=(name in ("row_list", "ovf_n")))
+        g = Guarded(tuple(t.shape), t.dtype, zero=(name == "ovf_n"))   # scratch keeps the fill bytes
         setattr(h, name, g.t)
         gs[name] = g
     return h, gs
@@ -66,10 +66,10 @@ def all_intact(gs):
     assert not bad, bad
 
 
-# (T, d, f, W, S, dtype, hot): large tiles with overflow rows, 64 x 128 tiles, the decode
-# K split, the one-token W1 stream, fp32 tiles
-FWD = [(600, 256, 1024, 128, 4, "bf16", 64), (100, 256, 640, 64, 2, "bf16", 0), (40, 512, 1024, 128, 3, "bf16", 8),
-       (1, 2048, 512, 64, 16, "bf16", 0), (70, 256, 512, 64, 4, "f32", 16)]
+# (T, d, f, W, S, dtype, hot): large tiles with overflow rows, the 4-wave large tiles (W = 64,
+# S > 32), 64 x 128 tiles, the decode K split, the one-token W1 stream, fp32 tiles
+FWD = [(600, 256, 1024, 128, 4, "bf16", 64), (600, 256, 1024, 64, 40, "bf16", 64), (100, 256, 640, 64, 2, "bf16", 0),
+       (40, 512, 1024, 128, 3, "bf16", 8), (1, 2048, 512, 64, 16, "bf16", 0), (70, 256, 512, 64, 4, "f32", 16)]
 
 
 @pytest.mark.parametrize("T,d,f,W,S,dt,hot", FWD)

@@ -93,18 +93,30 @@ def test_pack_bit_exact(R, C, W, S, cap, dens, dt, vdt):
 
 # ------------------------------------------------------------------ fused forward
 
-def check_forward(g, W, S, cap, y_dtype="f32", ambiguity=True):
+def round_bf16(a: np.ndarray) -> np.ndarray:
+    """float64 values that are exact in fp32 -> the nearest bf16 (ties to even), as float64."""
+    return orc.widen(synth.f32_to_bf16_bits(a.astype(np.float32)), "bf16")
+
+
+def check_forward(g, W, S, cap, y_dtype="f32", ambiguity=True, val_dtype="f32"):
     dt = g["dtype"]
     x, w1t, b1, w2 = dev_inputs(g)
     T, f = x.shape[0], w1t.shape[0]
     ydt = torch.float32 if y_dtype == "f32" else torch.bfloat16
-    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, cap, torch.float32, ydt)
+    vdt = torch.float32 if val_dtype == "f32" else torch.bfloat16
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, cap, vdt, ydt)
     hz = tw.ffn_up_relu_dense(x, w1t, b1, torch.float32)
     torch.cuda.synchronize()
     got = twell_host(h)
     h_gpu = from_dev(hz)
     # 1. the TwELL equals the oracle's packing of the GPU's own activations, bit for bit
-    assert_twell_equal(got, orc.twell_pack(h_gpu, W, S, cap))
+    #    (bf16 values: the pattern and counts of the fp32 activations, each stored value and
+    #    backup row rounded to bf16)
+    want = orc.twell_pack(h_gpu, W, S, cap)
+    if val_dtype == "bf16":
+        want["vals"] = round_bf16(want["vals"])
+        want["ovf_dense"] = round_bf16(want["ovf_dense"])
+    assert_twell_equal(got, want)
     # 2. the GPU activations are within the fp32 error bound of the oracle's
     xr, w1r, b1r, w2r, _ = inputs64(g)
     z = orc.preact(xr, w1r, b1r)
@@ -166,11 +178,23 @@ def test_fwd_c3(T):
 
 
 def decode_tickets(h):
-    """The per-128-column tickets of the decode K split, at the end of h's row_list scratch."""
+    """The per-128-column 64-bit tickets of the decode K split, at the end of h's row_list."""
     lists = h.rows * (h.cols // h.tile_w) * h.slots * 8
     tiles = (h.cols + 127) // 128
-    off = ((lists + 255) // 256 * 256 + tiles * 2 * 64 * 128 * 4) // 4
-    return h.row_list.view(torch.int32)[off:off + tiles]
+    off = ((lists + 255) // 256 * 256 + tiles * 2 * 64 * 128 * 4) // 8
+    return h.row_list[off:off + tiles]
+
+
+def garbage_matrix(T, f, W, S, cap, seed):
+    """A TwellMatrix whose scratch (row lists, decode half sums and tickets) holds random bits,
+    as a fresh allocation may: the library must not depend on its contents."""
+    h = tw.TwellMatrix(T, f, W, S, cap)
+    gen = torch.Generator(device="cuda").manual_seed(seed)
+    h.row_list.random_(generator=gen)
+    h.row_nnz.random_(generator=gen)
+    h.ovf_bits.random_(generator=gen)
+    assert int(decode_tickets(h).ne(0).sum()) > 0
+    return h
 
 
 @pytest.mark.parametrize("T,f,W,S,seed", [(1, 1984, 64, 3, 21), (37, 2048, 128, 8, 22), (64, 1984, 64, 4, 23),
@@ -189,7 +213,8 @@ def test_fwd_decode_split(T, f, W, S, seed):
     g = synth.generate(w, T=T)
     got, flips, err = check_forward(g, W, S, 64)
     x, w1t, b1, w2 = dev_inputs(g)
-    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, 64)
+    h = garbage_matrix(T, f, W, S, 64, seed)
+    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, 64, h=h)
     torch.cuda.synchronize()
     assert int(decode_tickets(h).abs().sum()) == 0
     c1 = twell_host(h)
@@ -236,7 +261,8 @@ def test_fwd_decode_gemv(T, d, f, W, S, seed):
     g = synth.generate(w, T=T)
     got, flips, err = check_forward(g, W, S, T)
     x, w1t, b1, w2 = dev_inputs(g)
-    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, T)
+    h = garbage_matrix(T, f, W, S, T, seed)
+    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, W, S, T, h=h)
     torch.cuda.synchronize()
     assert int(decode_tickets(h).abs().sum()) == 0
     c1 = twell_host(h)
@@ -277,6 +303,56 @@ def test_fwd_bf16_output_and_bf16_vals():
     bf = orc.widen(synth.f32_to_bf16_bits(a["vals"].astype(np.float32)), "bf16")
     assert np.array_equal(b["vals"], bf)
     assert rel_err(from_dev(y16), from_dev(y32)) < 2 ** -7
+
+
+@pytest.mark.parametrize("T,d,f,W,S,dt,hot,seed", [(600, 512, 2048, 128, 8, "bf16", 64, 71),
+                                                    (8, 1024, 1024, 128, 4, "bf16", 0, 72),
+                                                    (70, 256, 512, 64, 4, "f32", 16, 73),
+                                                    (520, 256, 1024, 64, 40, "bf16", 0, 74)])
+def test_fwd_bf16_vals_against_oracle(T, d, f, W, S, dt, hot, seed):
+    """bf16 TwELL values with an fp32 y, against the oracle: the slots and backup rows equal the
+    oracle's packing of the GPU's own activations rounded to bf16 (nearest, ties to even), and
+    y is within the bf16-input tolerance of the oracle's dense fp64 y. Hot tokens make rows
+    overflow, so bf16 backup rows are compared too; the last case takes the 4-wave 128 x 128
+    large tiles (W = 64, S > 32)."""
+    say("fwd bf16 vals", T, d, f, W, S, dt, hot)
+    base = synth.C2 if dt == "bf16" else synth.C1
+    w = base.with_(T=T, d=d, f=f, tile_w=W, slots=S, seed=seed, hot_every=hot)
+    g = synth.generate(w)
+    got, flips, err = check_forward(g, W, S, T, val_dtype="bf16")
+    say("bf16 vals", T, d, f, "flips", flips, "err", err, "ovf", got["ovf_n"])
+    assert err <= TOL["bf16"]
+    if hot:
+        assert got["ovf_n"] > 0
+
+
+@pytest.mark.parametrize("T,d,f,S,active,seed", [(600, 256, 1024, 40, 0.5, 81), (517, 128, 1536, 48, 0.6, 82),
+                                                 (1024, 256, 1024, 33, 0.4, 83)])
+def test_fwd_large_slot_tiles_exact(T, d, f, S, active, seed):
+    """From 512 tokens and 1024 units on, W = 64 with S > 32 takes the 4-wave 128 x 128 tile
+    variant of the up GEMM (its epilogue keeps up to 128 slots per row per wave). On integer-
+    grid inputs every value is exact, so the TwELL equals the oracle's own packing bit for bit;
+    40-60% of the units are active, so some row-tiles exceed S and their rows go to the dense
+    backup (recomputed by the 64 x 128 tiles, which sum in the same order). Products and
+    partial sums are multiples of 2^-14 below 2^10, so y is exact too."""
+    say("fwd large-slot tiles", T, d, f, S, active)
+    g = synth.integer_grid(T, d, f, seed=seed, dtype="bf16", active=active)
+    got, flips, err = check_forward(g, 64, S, T, ambiguity=False)
+    xr, w1r, b1r, w2r, _ = inputs64(g)
+    h_ref = orc.relu(orc.preact(xr, w1r, b1r))
+    assert_twell_equal(got, orc.twell_pack(h_ref, 64, S, T))
+    assert 0 < got["ovf_n"] < T
+    assert err == 0.0
+
+
+def test_fwd_large_slot_tiles_normal():
+    """The same tile variant on normal inputs (T = 640, W = 64, S = 36, b1 = -0.5: about 31% of
+    the units active): bit-exact against the oracle's packing of the GPU's activations, y
+    within the bf16-input tolerance."""
+    w = synth.C2.with_(T=640, d=512, f=2048, tile_w=64, slots=36, bias=-0.5, seed=84)
+    g = synth.generate(w)
+    got, flips, err = check_forward(g, 64, 36, 640)
+    say("large-slot normal flips", flips, "err", err, "ovf", got["ovf_n"])
 
 
 def test_down_from_pack_matches_fused():
