@@ -129,11 +129,21 @@ def check_forward(g, W, S, cap, y_dtype="f32", ambiguity=True, val_dtype="f32"):
         assert np.all(np.abs(z[flip]) <= beta[flip])
     else:
         assert not flip.any()
-    # 4. y within tolerance of the oracle's dense y
+    # 4. y within tolerance of the oracle's dense y. With bf16 TwELL values the kernel
+    #    multiplies the activations rounded to bf16 (relative error up to 2^-8 each), an extra
+    #    rounding the 2e-3 budget of bf16 inputs does not cover: then y is compared with the
+    #    oracle's product of those rounded values at the tolerance, and with the exact y within
+    #    the bound that rounding implies, 2^-8 * sum_j |h_j w2_j| (+ 1e-5 max|y| for the fp32 sums).
     y_ref = h_ref @ w2r
-    err = rel_err(from_dev(y), y_ref)
+    yg = from_dev(y)
     tol = TOL[dt] if y_dtype == "f32" else max(TOL[dt], 2 ** -8)
-    assert err <= tol, err
+    if val_dtype == "bf16":
+        assert rel_err(yg, round_bf16(h_gpu) @ w2r) <= tol
+        bound = 2.0 ** -8 * (np.abs(h_gpu) @ np.abs(w2r)) + 1e-5 * np.abs(y_ref).max()
+        assert np.all(np.abs(yg - y_ref) <= bound)
+    err = rel_err(yg, y_ref)
+    if val_dtype != "bf16":
+        assert err <= tol, err
     return got, int(flip.sum()), err
 
 
@@ -311,17 +321,18 @@ def test_fwd_bf16_output_and_bf16_vals():
                                                     (520, 256, 1024, 64, 40, "bf16", 0, 74)])
 def test_fwd_bf16_vals_against_oracle(T, d, f, W, S, dt, hot, seed):
     """bf16 TwELL values with an fp32 y, against the oracle: the slots and backup rows equal the
-    oracle's packing of the GPU's own activations rounded to bf16 (nearest, ties to even), and
-    y is within the bf16-input tolerance of the oracle's dense fp64 y. Hot tokens make rows
-    overflow, so bf16 backup rows are compared too; the last case takes the 4-wave 128 x 128
-    large tiles (W = 64, S > 32)."""
+    oracle's packing of the GPU's own activations rounded to bf16 (nearest, ties to even); y is
+    within the bf16-input tolerance of the oracle's product of those rounded activations, and
+    within the rounding's own bound of the exact dense y (the rounding alone can use the whole
+    2e-3: 2.03e-3 was measured on the first case, which is why fp32 values are the default).
+    Hot tokens make rows overflow, so bf16 backup rows are compared too; the last case takes
+    the 4-wave 128 x 128 large tiles (W = 64, S > 32)."""
     say("fwd bf16 vals", T, d, f, W, S, dt, hot)
     base = synth.C2 if dt == "bf16" else synth.C1
     w = base.with_(T=T, d=d, f=f, tile_w=W, slots=S, seed=seed, hot_every=hot)
     g = synth.generate(w)
     got, flips, err = check_forward(g, W, S, T, val_dtype="bf16")
-    say("bf16 vals", T, d, f, "flips", flips, "err", err, "ovf", got["ovf_n"])
-    assert err <= TOL["bf16"]
+    say("bf16 vals", T, d, f, "flips", flips, "err against the exact y", err, "ovf", got["ovf_n"])
     if hot:
         assert got["ovf_n"] > 0
 
