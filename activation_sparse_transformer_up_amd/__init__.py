@@ -17,7 +17,7 @@ __all__ = [
     "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
     "twell_down", "twell_fwd_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense",
     "twell_gate_up", "twell_gated_ffn_fwd", "twell_gate_up_workspace_bytes", "twell_ffn_bwd",
-    "twell_ffn_bwd_workspace_bytes",
+    "twell_ffn_bwd_workspace_bytes", "twell_ffn_bwd_noalloc",
     "nm_prune", "ffn_up_relu_nm", "nm_ffn_down", "twell_sync_status", "twell_row_max_histogram",
     "twell_stash_bytes", "twell_choose_slots", "F32", "BF16",
 ]
@@ -64,6 +64,7 @@ _SIGS = {
     "twell_gated_ffn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _Z, _P], _I),
     "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
     "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
+    "twell_ffn_bwd_noalloc": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P], _I),
     "nm_prune": ([_P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "ffn_up_relu_nm": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "nm_ffn_down": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P], _I),
@@ -312,6 +313,29 @@ def twell_ffn_bwd(x, w1t, w2, h: TwellMatrix, dy, l1_coef: float, want_db1: bool
     _check(lib().twell_ffn_bwd(_ptr(x), _ptr(w1t), _ptr(w2), _dt(x.dtype), T, d, f, _c.byref(m),
                                _ptr(dy), float(l1_coef), _ptr(dx), _ptr(dw1t), _ptr(dw2), _ptr(db1),
                                _ptr(workspace), workspace.numel(), _stream(dev)), "twell_ffn_bwd")
+    return dx, dw1t, dw2, db1
+
+
+# bytes of the fixed device scratch behind twell_ffn_bwd_noalloc (include/twell.h)
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def twell_ffn_bwd_noalloc(x, w1t, w2, h: TwellMatrix, dy, l1_coef: float, out=None):
+    """twell_ffn_bwd on the library's fixed per-GPU scratch (no workspace). ``out``: optional
+    (dx, dw1t, dw2, db1) tensors to write (db1 may be None); allocated here if not given."""
+    T, d = x.shape
+    f = w1t.shape[0]
+    dev = x.device
+    if out is None:
+        out = (torch.empty((T, d), dtype=torch.float32, device=dev),
+               torch.empty((f, d), dtype=torch.float32, device=dev),
+               torch.empty((f, d), dtype=torch.float32, device=dev),
+               torch.empty((f,), dtype=torch.float32, device=dev))
+    dx, dw1t, dw2, db1 = out
+    m = h.c()
+    _check(lib().twell_ffn_bwd_noalloc(_ptr(x), _ptr(w1t), _ptr(w2), _dt(x.dtype), T, d, f, _c.byref(m),
+                                       _ptr(dy), float(l1_coef), _ptr(dx), _ptr(dw1t), _ptr(dw2), _ptr(db1),
+                                       _stream(dev)), "twell_ffn_bwd_noalloc")
     return dx, dw1t, dw2, db1
 
 

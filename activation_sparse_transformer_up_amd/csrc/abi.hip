@@ -2,10 +2,39 @@
 // Declarations, layouts and error contract: include/twell.h.
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/twell.h"
 #include "launch.h"
 
 using namespace tw;
+
+// Device scratch of twell_ffn_bwd_noalloc, for callers that cannot allocate: one copy per GPU
+// (at its own address on each), held for the life of the process. In host code `scratch`
+// names a host-side stand-in, not device memory: only the address hipGetSymbolAddress returns
+// for the current device may be handed to kernels.
+static __device__ __align__(256) char scratch[TWELL_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void *scratch_ptr[kMaxDevices];
+
+// The current device's address of `scratch` (looked up once per device), or NULL on error.
+void *scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return nullptr;
+    scratch_ptr[dev] = p;
+  }
+  return scratch_ptr[dev];
+}
+
+}  // namespace
 
 namespace {
 
@@ -356,6 +385,21 @@ int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dty
   a.cap = h->ovf_cap;
   TW_TRY(launch_bwd(a, S(stream)));
   return TWELL_OK;
+}
+
+int twell_ffn_bwd_noalloc(const void *x, const void *w1t, const void *w2, int32_t in_dtype, int32_t T,
+                          int32_t d_model, int32_t d_ff, const twell_matrix_t *h, const void *dy, float l1_coef,
+                          float *dx, float *dw1t, float *dw2, float *db1, void *stream) {
+  if (!h) return TWELL_ERR_ARG;
+  // the size check comes first, so that a problem beyond the fixed scratch is refused before
+  // any device lookup
+  if (T >= 0 && d_model > 0 && d_ff > 0 && dtype_ok(in_dtype) && h->tile_w > 0 && h->slots > 0 && h->ovf_cap >= 0 &&
+      twell_ffn_bwd_workspace_bytes(T, d_model, d_ff, in_dtype, h) > (size_t)TWELL_NOALLOC_SCRATCH_BYTES)
+    return TWELL_ERR_WORKSPACE;
+  void *ws = scratch_on_current_device();
+  if (!ws) return TWELL_ERR_HIP;
+  return twell_ffn_bwd(x, w1t, w2, in_dtype, T, d_model, d_ff, h, dy, l1_coef, dx, dw1t, dw2, db1, ws,
+                       (size_t)TWELL_NOALLOC_SCRATCH_BYTES, stream);
 }
 
 int nm_prune(const void *h, int32_t dtype, int32_t T, int32_t d_ff, int32_t n, int32_t m, void *vals,

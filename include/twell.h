@@ -267,6 +267,25 @@ int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dty
                   float *db1, void *workspace, size_t workspace_bytes, void *stream);
 
 /*
+ * twell_ffn_bwd_noalloc — twell_ffn_bwd without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops, harnesses that
+ * forbid hipMalloc). The scratch is a fixed array of TWELL_NOALLOC_SCRATCH_BYTES inside the
+ * library, one per GPU, held until the process ends; nothing is allocated or freed by the
+ * call (the array's device address is looked up once per device, on the first call there).
+ * Same arguments, kernels, results and errors as twell_ffn_bwd, except: a problem whose
+ * twell_ffn_bwd_workspace_bytes exceeds TWELL_NOALLOC_SCRATCH_BYTES returns
+ * TWELL_ERR_WORKSPACE before anything is enqueued, and TWELL_ERR_HIP if the scratch cannot be
+ * located on the current device. Every call on one GPU shares that GPU's scratch: calls
+ * that overlap in time on one GPU (different streams or threads) race and must be ordered by
+ * the caller. The scratch needs no initialisation (the backward writes before it reads).
+ */
+#define TWELL_NOALLOC_SCRATCH_BYTES (64u << 20)
+int twell_ffn_bwd_noalloc(const void *x, const void *w1t, const void *w2, int32_t in_dtype,
+                          int32_t T, int32_t d_model, int32_t d_ff, const twell_matrix_t *h,
+                          const void *dy, float l1_coef, float *dx, float *dw1t, float *dw2,
+                          float *db1, void *stream);
+
+/*
  * nm_prune — N:M activation pruning by magnitude ("Motivating Next-Gen Accelerators ...",
  * "2. Metodologia", criterion ACT): in every block of m consecutive entries of a row of
  * h [T][d_ff] keep the n of largest |h| (ties to the lower index), emitted in ascending
