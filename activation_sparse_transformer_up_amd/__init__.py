@@ -16,7 +16,7 @@ import torch
 __all__ = [
     "TwellError", "TwellMatrix", "lib", "twell_abi_version", "twell_pack", "twell_ffn_fwd",
     "twell_down", "twell_fwd_down", "twell_up_gemm", "twell_up_finish", "ffn_up_relu_dense",
-    "twell_gate_up", "twell_gated_ffn_fwd", "twell_gate_up_workspace_bytes", "twell_ffn_bwd",
+    "twell_gate_up", "twell_gated_ffn_fwd", "twell_gated_ffn_infer", "twell_gate_up_workspace_bytes", "twell_ffn_bwd",
     "twell_ffn_bwd_workspace_bytes", "twell_ffn_bwd_noalloc",
     "nm_prune", "ffn_up_relu_nm", "nm_ffn_down", "twell_sync_status", "twell_row_max_histogram",
     "twell_stash_bytes", "twell_choose_slots", "F32", "BF16",
@@ -62,6 +62,7 @@ _SIGS = {
     "twell_gate_up_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
     "twell_gate_up": ([_P, _P, _P, _I, _I, _I, _I, _P, _Z, _P], _I),
     "twell_gated_ffn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _Z, _P], _I),
+    "twell_gated_ffn_infer": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
     "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
     "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
     "twell_ffn_bwd_noalloc": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P], _I),
@@ -228,6 +229,27 @@ def twell_gated_ffn_fwd(x, wgt, bg, wut, w2, tile_w: int, slots: int, ovf_cap: i
                                      _c.byref(m), _ptr(y), _dt(y.dtype), _ptr(workspace),
                                      workspace.numel() if workspace is not None else 0, _stream(x.device)),
            "twell_gated_ffn_fwd")
+    return y, h
+
+
+def twell_gated_ffn_infer(x, wgt, bg, wut, w2, tile_w: int, slots: int, val_dtype=torch.float32,
+                          y_dtype=torch.float32, h: TwellMatrix | None = None, y: torch.Tensor | None = None):
+    """Decode-size gated forward (T <= 64): the gate GEMM, then one fused kernel over the active
+    units (up dot product and down multiply-add). Returns (y, h); h holds the gate's TwELL."""
+    T, d = x.shape
+    f = wgt.shape[0]
+    if wgt.dtype != x.dtype or wut.dtype != x.dtype or w2.dtype != x.dtype:
+        raise TypeError("x, wgt, wut and w2 must share a dtype")
+    if bg.dtype != torch.float32:
+        raise TypeError("bg must be float32")
+    if h is None:
+        h = TwellMatrix(T, f, tile_w, slots, 0, val_dtype, x.device)
+    if y is None:
+        y = torch.empty((T, d), dtype=y_dtype, device=x.device)
+    m = h.c()
+    _check(lib().twell_gated_ffn_infer(_ptr(x), _ptr(wgt), _ptr(bg), _ptr(wut), _ptr(w2), _dt(x.dtype), T, d, f,
+                                       _c.byref(m), _ptr(y), _dt(y.dtype), _stream(x.device)),
+           "twell_gated_ffn_infer")
     return y, h
 
 

@@ -337,6 +337,27 @@ int twell_gated_ffn_fwd(const void *x, const void *w_gate_t, const float *b_gate
   return TWELL_OK;
 }
 
+int twell_gated_ffn_infer(const void *x, const void *w_gate_t, const float *b_gate, const void *w_up_t,
+                          const void *w2, int32_t in_dtype, int32_t T, int32_t d_model, int32_t d_ff,
+                          twell_matrix_t *h, void *y, int32_t y_dtype, void *stream) {
+  if (!w2 || !w_up_t || (T > 0 && !y)) return TWELL_ERR_ARG;
+  if (!dtype_ok(y_dtype)) return TWELL_ERR_ARG;
+  int st = check_up_args(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h);
+  if (st) return st;
+  st = check_matrix(h, true, true);
+  if (st) return st;
+  if (!al16(w2) || !al16(y) || !al16(w_up_t)) return TWELL_ERR_ALIGN;
+  if (T > kDecodeMaxT || d_ff / h->tile_w > 256) return TWELL_ERR_UNSUPPORTED;
+  if (T == 0) return TWELL_OK;
+  hipStream_t s = S(stream);
+  st = up_gemm(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h, s);
+  if (st) return st;
+  const TwellOut o = out_of(h);           // o.dec_part: the dense scratch rows [T][d_ff] fp32
+  TW_TRY(launch_gated_fused(in_of(h), x, w_gate_t, b_gate, w_up_t, w2, in_dtype == TWELL_BF16, d_model, y,
+                            y_dtype == TWELL_BF16, o.dec_part, s));
+  return TWELL_OK;
+}
+
 int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
                       int32_t d_model, int32_t d_ff, void *h, int32_t h_dtype, void *stream) {
   if (!b1 || (T > 0 && !h)) return TWELL_ERR_ARG;

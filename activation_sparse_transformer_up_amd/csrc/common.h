@@ -74,10 +74,12 @@ template <typename T> struct Elem;
 template <> struct Elem<float> {
   static TW_DEV float load(const float *p, size_t i) { return p[i]; }
   static TW_DEV void store(float *p, size_t i, float v) { p[i] = v; }
+  static TW_DEV float load_rounded(float v) { return v; }     // v as this type stores it
 };
 template <> struct Elem<uint16_t> {
   static TW_DEV float load(const uint16_t *p, size_t i) { return bf16_to_f32(p[i]); }
   static TW_DEV void store(uint16_t *p, size_t i, float v) { p[i] = (uint16_t)f32_to_bf16(v); }
+  static TW_DEV float load_rounded(float v) { return bf16_to_f32(f32_to_bf16(v)); }
 };
 
 // 16-byte vector of row elements, widened to fp32: 8 bf16 or 4 fp32.

@@ -22,6 +22,8 @@
 #include "common.h"
 #include "gather.h"
 #include "launch.h"
+#include "rows.h"
+#include "stage.h"
 
 namespace tw {
 
@@ -213,6 +215,301 @@ __global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const f
     const uint2 q = lp[e];
     lp[e].y = __float_as_uint(__uint_as_float(q.y) * u);
   }
+}
+
+// ------------------------------------------------------------ fused inference kernel
+// "Kernels de Inferência": after the gate GEMM has written the TwELL of the gate, a single
+// kernel walks each token's active units, takes the up dot product u = x[t] . w_up[j] and
+// multiplies-adds (g u) w2[j] into y[t]. It runs in one launch and two kinds of work item:
+//   up items (t, group of 4 tiles), claimed in batches from a work counter: for every active
+//     slot (j, g) of the tiles, u = x[t] . w_up[j] and the pair (j, g u) is written to the
+//     slot's place in row_list (read as [t][tile][S]); a tile holding more than S active
+//     units lost units in its slots, so its gate pre-activations are recomputed
+//     (x[t] . w_gate[j] + b[j], rounded to the value type as the TwELL stores it) and g u
+//     (0 where inactive) goes to the token's dense row in the scratch. Each finished item
+//     counts on its token;
+//   down items (t, 512-column chunk), four waves of 128 columns: when every up item of token
+//     t has finished, the token's pairs (from its slots and dense tiles, ascending column
+//     order) are staged in LDS 256 at a time and the waves multiply-add the W2 row pieces.
+// A workgroup takes down items only after the work counter has run past the last up item, so
+// every up item it may wait for has been claimed by a running workgroup: no waiting depends
+// on which workgroups are resident (no cooperative launch, no grid barrier).
+// Values handed between work items (pairs, dense rows, counters) are written and read with
+// agent-scope atomic accesses, which are coherent across the XCDs' L2 caches by themselves.
+// Scratch: the decode workspace of the row-list scratch (free once the gate GEMM has ended):
+// dense rows [T][f] fp32, and the state words at its end (fused_prepare).
+constexpr int kFusedTilesPerItem = 1;
+constexpr int kFusedUpBatch = 4;             // up items per claim (one per wave)
+constexpr int kFusedGroups = 8;              // work counters: up items split in 8 ranges
+constexpr uint64_t kFusedReady = 0x3C6EF372FE94F82Bull;
+constexpr uint64_t kFusedInit = 0xA54FF53A5F1D36F1ull;
+
+// State words: [0] readiness, [2] retired workgroups, [16 + 16 g] work counter of up-item range
+// g (one 128-byte line each), [160 ..] per-token count of finished up items (uint32,
+// kDecodeMaxT of them). The last workgroup to retire zeroes every counter and leaves [0] at
+// kFusedReady. A readiness word holding anything else (a buffer this
+// kernel never used) is claimed by one workgroup with a compare-and-swap; it zeroes the
+// counters and publishes kFusedReady while the others wait for it (it is running, so the wait
+// ends). Only a word that held kFusedInit or kFusedReady by chance before the first launch
+// would mislead it (one chance in 2^63).
+struct FusedState {
+  uint64_t *w;
+  TW_DEV uint32_t *done() const { return (uint32_t *)(w + 160); }
+  TW_DEV uint64_t *ctr(int g) const { return w + 16 + 16 * g; }
+};
+constexpr int kFusedStateBytes = 160 * 8 + kDecodeMaxT * 4;
+
+TW_DEV void fused_zero_counters(const FusedState &st, int T) {
+  __hip_atomic_store(st.w + 2, (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int g = 0; g < kFusedGroups; ++g) __hip_atomic_store(st.ctr(g), (uint64_t)0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  for (int i = 0; i < T; ++i) __hip_atomic_store(st.done() + i, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+TW_DEV void fused_prepare(const FusedState &st) {
+  if (threadIdx.x == 0) {
+    uint64_t r = __hip_atomic_load(st.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    if (r != kFusedReady) {
+      if (r != kFusedInit &&
+          __hip_atomic_compare_exchange_strong(st.w, &r, kFusedInit, __ATOMIC_RELAXED, __ATOMIC_RELAXED,
+                                               __HIP_MEMORY_SCOPE_AGENT)) {
+        fused_zero_counters(st, kDecodeMaxT);
+        wait_vmcnt<0>();
+        __hip_atomic_store(st.w, kFusedReady, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        while (__hip_atomic_load(st.w, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != kFusedReady)
+          __builtin_amdgcn_s_sleep(2);
+      }
+    }
+  }
+  __syncthreads();
+}
+
+TW_DEV uint64_t ld_coh64(const void *p) {
+  return __hip_atomic_load((const uint64_t *)p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+TW_DEV float ld_cohf(const float *p) { return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); }
+
+// One up item by one wave: the active units of tiles [k0, k0 + 4) of token t.
+template <typename XT, typename VT, int NP>
+TW_DEV void fused_up_item(const TwellIn &h, const XT *__restrict__ x, const XT *__restrict__ wg,
+                          const float *__restrict__ bg, const XT *__restrict__ wu, int d, float *__restrict__ dense,
+                          int t, int k0) {
+  const int lane = lane_id();
+  const XT *xrow = x + (size_t)t * d;
+  const VT *vals = (const VT *)h.vals;
+  for (int k = k0; k < min(k0 + kFusedTilesPerItem, h.n_t); ++k) {
+    const size_t sb = ((size_t)t * h.n_t + k) * h.S;
+    const int c = h.counts[(size_t)t * h.n_t + k];
+    if (c <= h.S) {
+      for (int s0 = 0; s0 < c; s0 += kGateEnt) {
+        int col[kGateEnt];
+        float gv[kGateEnt];
+#pragma unroll
+        for (int q = 0; q < kGateEnt; ++q) {
+          const bool ok = s0 + q < c;
+          col[q] = ok ? h.col_idx[sb + s0 + q] : -1;
+          gv[q] = ok ? Elem<VT>::load(vals, sb + s0 + q) : 0.f;
+        }
+        float u[kGateEnt];
+        wave_dots<XT, NP>(xrow, wu, d, col, u);
+        if (lane == 0)
+#pragma unroll
+          for (int q = 0; q < kGateEnt; ++q)
+            if (col[q] >= 0)
+              __hip_atomic_store((uint64_t *)(h.row_list + sb + s0 + q),
+                                 (uint64_t)(uint32_t)col[q] | ((uint64_t)__float_as_uint(gv[q] * u[q]) << 32),
+                                 __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      }
+    } else {
+      float *drow = dense + (size_t)t * h.cols;
+      for (int j0 = k * h.W; j0 < (k + 1) * h.W; j0 += kGateEnt) {
+        int col[kGateEnt];
+#pragma unroll
+        for (int q = 0; q < kGateEnt; ++q) col[q] = j0 + q;
+        float z[kGateEnt];
+        wave_dots<XT, NP>(xrow, wg, d, col, z);
+        int ucol[kGateEnt];
+        float g[kGateEnt];
+#pragma unroll
+        for (int q = 0; q < kGateEnt; ++q) {
+          const float zz = z[q] + bg[col[q]];
+          g[q] = zz > 0.f ? Elem<VT>::load_rounded(zz) : 0.f;
+          ucol[q] = g[q] != 0.f ? col[q] : -1;
+        }
+        float u[kGateEnt];
+        wave_dots<XT, NP>(xrow, wu, d, ucol, u);
+        if (lane == 0)
+#pragma unroll
+          for (int q = 0; q < kGateEnt; ++q)
+            __hip_atomic_store(drow + col[q], ucol[q] >= 0 ? g[q] * u[q] : 0.f, __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+      }
+    }
+  }
+}
+
+template <typename XT, typename VT, typename YT, int NP>
+__global__ __launch_bounds__(256) void k_gated_fused(TwellIn h, const XT *__restrict__ x, const XT *__restrict__ wg,
+                                                     const float *__restrict__ bg, const XT *__restrict__ wu,
+                                                     const XT *__restrict__ w2, int d, YT *__restrict__ y,
+                                                     float *__restrict__ dense, FusedState st) {
+  constexpr int E = Vec16<XT>::N;
+  constexpr int CW = 16 * E;                   // columns of one wave in a down item
+  __shared__ int claim_s;
+  __shared__ int pre_s[257];
+  __shared__ uint2 lst_s[256];
+  __shared__ int wsum_s[4];
+  const int T = h.rows;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ngrp = (h.n_t + kFusedTilesPerItem - 1) / kFusedTilesPerItem;   // up items per token
+  const int U = T * ngrp;
+  fused_prepare(st);
+
+  // up items: range g = [g U / 8, (g + 1) U / 8) has its own counter; a workgroup starts on
+  // range blockIdx % 8 and moves on to the others when it runs dry, so it reaches the down
+  // items only once every up item has been claimed
+  for (int gi = 0; gi < kFusedGroups; ++gi) {
+    const int g = (blockIdx.x + gi) % kFusedGroups;
+    const int r0 = (int)((long long)U * g / kFusedGroups), r1 = (int)((long long)U * (g + 1) / kFusedGroups);
+    for (;;) {
+      if (tid == 0)
+        claim_s = r0 + (int)__hip_atomic_fetch_add(st.ctr(g), (uint64_t)kFusedUpBatch, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      __syncthreads();
+      const int base = claim_s;
+      __syncthreads();
+      if (base >= r1) break;
+      const int i = base + wave;
+      if (i >= min(base + kFusedUpBatch, r1)) continue;
+      const int t = i / ngrp, k0 = (i % ngrp) * kFusedTilesPerItem;
+      fused_up_item<XT, VT, NP>(h, x, wg, bg, wu, d, dense, t, k0);
+      wait_vmcnt<0>();                                          // this item's stores have completed
+      if (lane == 0) __hip_atomic_fetch_add(st.done() + t, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    }
+  }
+
+  // down items (t, chunk of 4 * CW columns), statically spread over the workgroups
+  const int nch = (d + 4 * CW - 1) / (4 * CW);
+  const int g = lane >> 4, gl = lane & 15;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
+  for (int it = blockIdx.x; it < T * nch; it += gridDim.x) {
+    const int t = it / nch, c = it % nch;
+    const int colo = (c * 4 + wave) * CW + gl * E;
+    const bool cv = colo < d;
+    if (tid == 0)
+      while (__hip_atomic_load(st.done() + t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) < (uint32_t)ngrp)
+        __builtin_amdgcn_s_sleep(1);
+    // entries per tile: its stored slots, or all W columns of a recomputed (dense) tile
+    int m = 0;
+    if (tid < h.n_t) {
+      const int cnt = h.counts[(size_t)t * h.n_t + tid];
+      m = cnt <= h.S ? cnt : h.W;
+    }
+    int wt;
+    const int ex = wave_excl_scan(m, &wt);
+    if (lane == 0) wsum_s[wave] = wt;
+    __syncthreads();                                           // also: the up items of t are done
+    int wpre = 0, N = 0;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      wpre += w < wave ? wsum_s[w] : 0;
+      N += wsum_s[w];
+    }
+    pre_s[tid] = tid < h.n_t ? wpre + ex : N;                  // pre_s[k]: first entry of tile k
+    if (tid == 0) pre_s[256] = N;
+    __syncthreads();
+    float acc[E];
+#pragma unroll
+    for (int q = 0; q < E; ++q) acc[q] = 0.f;
+    for (int base = 0; base < N; base += 256) {
+      const int e = base + tid;
+      uint2 p = make_uint2(0, 0);
+      if (e < N) {
+        int lo = 0;                                            // last tile with pre_s <= e
+#pragma unroll
+        for (int step = 128; step > 0; step >>= 1)
+          if (lo + step < h.n_t && pre_s[lo + step] <= e) lo += step;
+        const int s = e - pre_s[lo];
+        const size_t sb = ((size_t)t * h.n_t + lo) * h.S;
+        if (h.counts[(size_t)t * h.n_t + lo] <= h.S) {
+          const uint64_t en = ld_coh64(h.row_list + sb + s);
+          p = make_uint2((uint32_t)en, (uint32_t)(en >> 32));
+        } else {
+          const int j = lo * h.W + s;
+          p = make_uint2((uint32_t)j, __float_as_uint(ld_cohf(dense + (size_t)t * h.cols + j)));
+        }
+      }
+      __syncthreads();                                         // the previous round's reads are done
+      lst_s[tid] = p;
+      __syncthreads();
+      const int n = min(256, N - base);
+      for (int e0 = 0; e0 < n; e0 += 64) {                     // group g takes entries e0 + g + 4 q
+        uint4 raw[16];
+        float vv[16];
+#pragma unroll
+        for (int q = 0; q < 16; ++q) {
+          const int ee = e0 + g + 4 * q;
+          vv[q] = 0.f;
+          raw[q] = make_uint4(0, 0, 0, 0);
+          if (ee < n) {
+            const uint2 pp = lst_s[ee];
+            vv[q] = __uint_as_float(pp.y);
+            if (cv && vv[q] != 0.f) raw[q] = ld16<XT>(rs, pp.x * (uint32_t)d + (uint32_t)colo);
+          }
+        }
+#pragma unroll
+        for (int q = 0; q < 16; ++q) fma16<XT, E>(acc, vv[q], raw[q]);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < E; ++q) {
+      acc[q] += __shfl_xor(acc[q], 16, 64);
+      acc[q] += __shfl_xor(acc[q], 32, 64);
+    }
+    if (g == 0 && cv) store_out_nt<YT, E>(y, (size_t)t * d + colo, acc);
+    __syncthreads();                                           // pre_s, lst_s reused by the next item
+  }
+
+  // retire; the last workgroup zeroes the counters for the next launch
+  __syncthreads();
+  if (tid == 0 &&
+      __hip_atomic_fetch_add(st.w + 2, (uint64_t)1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) + 1 == gridDim.x)
+    fused_zero_counters(st, T);
+}
+
+template <typename XT, typename VT, typename YT>
+static hipError_t fused_t(const TwellIn &h, const XT *x, const XT *wg, const float *bg, const XT *wu, const XT *w2,
+                          int d, YT *y, float *dense, hipStream_t s) {
+  // a workgroup per CU: enough down items to keep them busy at 64 tokens (8 per token at
+  // d = 4096), and few enough that the work counter is not a point of contention
+  const int nwg = 256;
+  FusedState st;
+  st.w = (uint64_t *)((char *)dense + dec_tiles(h.cols) * 2 * kDecHalfBytes - 2048);
+  static_assert(kFusedStateBytes <= 2048, "fused state");
+  hipLaunchKernelGGL((k_gated_fused<XT, VT, YT, 8>), dim3(nwg), dim3(256), 0, s, h, x, wg, bg, wu, w2, d, y, dense, st);
+  return hipGetLastError();
+}
+
+hipError_t launch_gated_fused(const TwellIn &h, const void *x, const void *wg, const float *bg, const void *wu,
+                              const void *w2, int bf16, int d, void *y, int y_bf16, float *dense, hipStream_t s) {
+  if (h.rows == 0) return hipSuccess;
+  if (bf16) {
+    const uint16_t *X = (const uint16_t *)x, *G = (const uint16_t *)wg, *U = (const uint16_t *)wu,
+                   *D = (const uint16_t *)w2;
+    if (h.val_bf16) {
+      if (y_bf16) return fused_t<uint16_t, uint16_t, uint16_t>(h, X, G, bg, U, D, d, (uint16_t *)y, dense, s);
+      return fused_t<uint16_t, uint16_t, float>(h, X, G, bg, U, D, d, (float *)y, dense, s);
+    }
+    if (y_bf16) return fused_t<uint16_t, float, uint16_t>(h, X, G, bg, U, D, d, (uint16_t *)y, dense, s);
+    return fused_t<uint16_t, float, float>(h, X, G, bg, U, D, d, (float *)y, dense, s);
+  }
+  const float *X = (const float *)x, *G = (const float *)wg, *U = (const float *)wu, *D = (const float *)w2;
+  if (h.val_bf16) {
+    if (y_bf16) return fused_t<float, uint16_t, uint16_t>(h, X, G, bg, U, D, d, (uint16_t *)y, dense, s);
+    return fused_t<float, uint16_t, float>(h, X, G, bg, U, D, d, (float *)y, dense, s);
+  }
+  if (y_bf16) return fused_t<float, float, uint16_t>(h, X, G, bg, U, D, d, (uint16_t *)y, dense, s);
+  return fused_t<float, float, float>(h, X, G, bg, U, D, d, (float *)y, dense, s);
 }
 
 static int gate_chunks(int d, int bf16) {

@@ -82,6 +82,11 @@ size_t gate_up_workspace_bytes(int T, int d, int n_t, int S, int bf16);
 hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int bf16, int d, float *ws,
                           hipStream_t s);
 
+// One cooperative launch after the gate GEMM (rows <= kDecodeMaxT): row lists, up products,
+// down products; dense: [rows][cols] fp32 scratch (the decode workspace of row_list).
+hipError_t launch_gated_fused(const TwellIn &h, const void *x, const void *wg, const float *bg, const void *wu,
+                              const void *w2, int bf16, int d, void *y, int y_bf16, float *dense, hipStream_t s);
+
 // nm.hip
 hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, void *vals, uint8_t *idx,
                            hipStream_t s);

@@ -22,7 +22,9 @@ namespace tw {
 // rounds of 64 entries are all issued before their stores.
 constexpr int kListRounds = 4;
 
-template <typename VT>
+// COH: the lists and lengths are written with agent-scope atomic stores, which reach the
+// memory side directly, so that other XCDs can read them later in the same kernel.
+template <typename VT, bool COH = false>
 TW_DEV void row_list_wave(const TwellIn &h, int t) {
   const int lane = lane_id();
   const int S = h.S;
@@ -58,12 +60,21 @@ TW_DEV void row_list_wave(const TwellIn &h, int t) {
 #pragma unroll
       for (int r = 0; r < kListRounds; ++r) {
         const int e = e0 + r * 64 + lane;
-        if (e < tot) out[n + e] = make_uint2(ci[r], cv[r]);
+        if (e < tot) {
+          if constexpr (COH)
+            __hip_atomic_store((uint64_t *)(out + n + e), (uint64_t)ci[r] | ((uint64_t)cv[r] << 32), __ATOMIC_RELAXED,
+                               __HIP_MEMORY_SCOPE_AGENT);
+          else
+            out[n + e] = make_uint2(ci[r], cv[r]);
+        }
       }
     }
     n += tot;
   }
-  if (lane == 0) h.row_nnz[t] = n;
+  if (lane == 0) {
+    if constexpr (COH) __hip_atomic_store(h.row_nnz + t, n, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else h.row_nnz[t] = n;
+  }
 }
 
 // The overflow scan, by one workgroup of 1024 threads: the per-(tile, 32-row) overflow

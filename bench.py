@@ -326,6 +326,16 @@ def leg_gated(steps, warmup):
             dms = _time(dense, steps, warmup)
             rec = {"ms": ms, "dense_ms": dms, "speedup_vs_dense": dms / ms,
                    "up_stage_ms": ms - ms_plain}
+            if T <= 64:
+                # the fused inference path: gate GEMM, then one kernel over the active units
+                hi = tw.TwellMatrix(T, w.f, w.tile_w, w.slots, 0, torch.float32, dev)
+                ms_inf = _time(lambda: tw.twell_gated_ffn_infer(x, wgt, bg, wut, w2, w.tile_w, w.slots, h=hi, y=y),
+                               steps, warmup)
+                ms_gate = _time(lambda: tw.twell_up_gemm(x, wgt, bg, hi), steps, warmup)
+                rec.update({"fused_infer_ms": ms_inf, "fused_speedup_vs_dense": dms / ms_inf,
+                            "fused_vs_staged": ms / ms_inf, "gate_gemm_ms": ms_gate,
+                            "fused_kernel_ms": ms_inf - ms_gate})
+                del hi
             if w is synth.C3:
                 cols = h.col_idx.clamp(min=0).view(-1)
                 act = torch.zeros(w.f, dtype=torch.bool, device=dev)

@@ -225,6 +225,26 @@ int twell_gated_ffn_fwd(const void *x, const void *w_gate_t, const float *b_gate
                         size_t workspace_bytes, void *stream);
 
 /*
+ * twell_gated_ffn_infer — the gated forward of twell_gated_ffn_fwd for inference at decode
+ * sizes (0 <= T <= 64), as "Kernels de Inferência" describes it: after the gate GEMM (the
+ * same kernel as twell_up_gemm, writing the gate's TwELL into h) ONE kernel iterates over
+ * each token's active gate units, takes the up dot product u = x[t] . w_up_t[j] and
+ * multiplies-adds (g u) w2[j] into y[t]; no intermediate goes through a separate launch.
+ * A tile holding more than h->slots active units is recomputed inside that kernel (its gate
+ * pre-activations x[t] . w_gate_t[j] + b_gate[j], rounded to the value type), its gated
+ * products taken from a dense row of the scratch. So no hybrid backup is formed: ovf_n,
+ * ovf_rows, ovf_slot and ovf_dense are not written (ovf_cap may be 0). h keeps the gate's
+ * TwELL (counts, col_idx, vals); row_nnz and row_list are scratch and need no
+ * initialisation. The down products of a token are summed in a fixed order (same bits on
+ * every call). Calls that overlap on one h race. Arguments, layouts and errors as
+ * twell_gated_ffn_fwd without the workspace; T > 64 or more than 256 tiles per row returns
+ * TWELL_ERR_UNSUPPORTED (use twell_gated_ffn_fwd).
+ */
+int twell_gated_ffn_infer(const void *x, const void *w_gate_t, const float *b_gate, const void *w_up_t,
+                          const void *w2, int32_t in_dtype, int32_t T, int32_t d_model, int32_t d_ff,
+                          twell_matrix_t *h, void *y, int32_t y_dtype, void *stream);
+
+/*
  * ffn_up_relu_dense — h = ReLU(x . W1 + b1) written densely ([T][d_ff], h_dtype = fp32 or
  * bf16). Same MFMA kernel and accumulation order as the fused TwELL path, so the fp32
  * output is bit-identical to the values the TwELL epilogue sees.
