@@ -19,7 +19,8 @@ __all__ = [
     "twell_gate_up", "twell_gated_ffn_fwd", "twell_gated_ffn_infer", "twell_gate_up_workspace_bytes", "twell_ffn_bwd",
     "twell_ffn_bwd_workspace_bytes", "twell_ffn_bwd_noalloc",
     "nm_prune", "ffn_up_relu_nm", "nm_ffn_down", "twell_sync_status", "twell_row_max_histogram",
-    "twell_stash_bytes", "twell_choose_slots", "F32", "BF16",
+    "twell_stash_bytes", "twell_choose_slots", "twell_to_row_ell", "twell_row_nnz_histogram",
+    "twell_choose_row_ell_width", "F32", "BF16",
 ]
 
 F32, BF16 = 0, 1
@@ -64,12 +65,16 @@ _SIGS = {
     "twell_gated_ffn_fwd": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P, _Z, _P], _I),
     "twell_gated_ffn_infer": ([_P, _P, _P, _P, _P, _I, _I, _I, _I, _P, _P, _I, _P], _I),
     "twell_ffn_bwd_workspace_bytes": ([_I, _I, _I, _I, _P], _Z),
+    "twell_ffn_bwd_workspace_bytes_nnz": ([_I, _I, _I, _I, _P, _c.c_int64], _Z),
     "twell_ffn_bwd": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P, _Z, _P], _I),
     "twell_ffn_bwd_noalloc": ([_P, _P, _P, _I, _I, _I, _I, _P, _P, _F, _P, _P, _P, _P, _P], _I),
     "nm_prune": ([_P, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "ffn_up_relu_nm": ([_P, _P, _P, _I, _I, _I, _I, _I, _I, _P, _P, _P], _I),
     "nm_ffn_down": ([_P, _P, _I, _I, _I, _I, _I, _P, _I, _P, _I, _P], _I),
     "twell_sync_status": ([_P, _P], _I),
+    "twell_to_row_ell": ([_P, _P, _P], _I),
+    "twell_row_nnz_histogram": ([_P, _P, _I, _P], _I),
+    "twell_choose_row_ell_width": ([_P, _I, _I, _I, _I, _I, _P], _I),
     "twell_row_max_histogram": ([_P, _P, _P], _I),
     "twell_stash_bytes": ([_I, _I, _I, _I, _I, _I], _Z),
     "twell_choose_slots": ([_P, _I, _I, _I, _I, _I, _P], _I),
@@ -313,14 +318,21 @@ def ffn_up_relu_dense(x, w1t, b1, h_dtype=torch.float32, out=None) -> torch.Tens
     return out
 
 
-def twell_ffn_bwd_workspace_bytes(T: int, d: int, f: int, h: TwellMatrix, dtype=torch.bfloat16) -> int:
+def twell_ffn_bwd_workspace_bytes(T: int, d: int, f: int, h: TwellMatrix, dtype=torch.bfloat16,
+                                  nnz: int | None = None) -> int:
+    """Workspace bytes of twell_ffn_bwd: for all of h's entry capacity, or for ``nnz`` stored
+    entries (the step's actual count, e.g. from twell_row_nnz_histogram)."""
     m = h.c()
-    return lib().twell_ffn_bwd_workspace_bytes(T, d, f, _dt(dtype), _c.byref(m))
+    if nnz is None:
+        return lib().twell_ffn_bwd_workspace_bytes(T, d, f, _dt(dtype), _c.byref(m))
+    return lib().twell_ffn_bwd_workspace_bytes_nnz(T, d, f, _dt(dtype), _c.byref(m), int(nnz))
 
 
 def twell_ffn_bwd(x, w1t, w2, h: TwellMatrix, dy, l1_coef: float, want_db1: bool = True,
                   workspace: torch.Tensor | None = None):
-    """Gradients (dx, dw1t, dw2, db1) of <dy, y> + l1_coef * sum(h), fp32."""
+    """Gradients (dx, dw1t, dw2, db1) of <dy, y> + l1_coef * sum(h), fp32. A given workspace
+    may be smaller than the capacity size (twell_ffn_bwd_workspace_bytes with nnz): the call's
+    entries must fit, else the outputs are NaN."""
     T, d = x.shape
     f = w1t.shape[0]
     dev = x.device
@@ -328,8 +340,8 @@ def twell_ffn_bwd(x, w1t, w2, h: TwellMatrix, dy, l1_coef: float, want_db1: bool
     dw1t = torch.empty((f, d), dtype=torch.float32, device=dev)
     dw2 = torch.empty((f, d), dtype=torch.float32, device=dev)
     db1 = torch.empty((f,), dtype=torch.float32, device=dev) if want_db1 else None
-    nbytes = twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype)
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is None:
+        nbytes = twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype)
         workspace = torch.empty((max(nbytes, 16),), dtype=torch.uint8, device=dev)
     m = h.c()
     _check(lib().twell_ffn_bwd(_ptr(x), _ptr(w1t), _ptr(w2), _dt(x.dtype), T, d, f, _c.byref(m),
@@ -425,3 +437,40 @@ def twell_choose_slots(hist, tile_w: int, rows: int, cols: int, ovf_cap: int, va
                                  _c.byref(out))
     _check(s if s < 0 else 0, "twell_choose_slots")
     return s, out.value
+
+
+def twell_row_nnz_histogram(h: TwellMatrix, nbins: int | None = None,
+                            hist: torch.Tensor | None = None) -> torch.Tensor:
+    """Device int32 [nbins]: rows of h by their number of nonzeros (the last bin holds every
+    row of nbins - 1 or more; default nbins = cols + 1, exact)."""
+    nbins = nbins or h.cols + 1
+    if hist is None:
+        hist = torch.empty((nbins,), dtype=torch.int32, device=h.counts.device)
+    m = h.c()
+    _check(lib().twell_row_nnz_histogram(_c.byref(m), _ptr(hist), nbins, _stream(h.counts.device)),
+           "twell_row_nnz_histogram")
+    return hist
+
+
+def twell_choose_row_ell_width(hist, rows: int, cols: int, ovf_cap: int, val_dtype=torch.float32):
+    """(N, stash bytes) of the row-ELL from a host copy of a row-nonzero histogram; raises
+    TwellError (TWELL_ERR_OVF_CAPACITY) if no width fits ovf_cap."""
+    import numpy as np
+    hh = np.ascontiguousarray(np.asarray(hist.cpu() if hasattr(hist, "cpu") else hist), dtype=np.int32)
+    out = _c.c_size_t(0)
+    n = lib().twell_choose_row_ell_width(hh.ctypes.data_as(_c.c_void_p), len(hh), rows, cols, ovf_cap,
+                                         _dt(val_dtype), _c.byref(out))
+    _check(n if n < 0 else 0, "twell_choose_row_ell_width")
+    return n, out.value
+
+
+def twell_to_row_ell(src: TwellMatrix, width: int, ovf_cap: int, val_dtype: torch.dtype | None = None,
+                     out: TwellMatrix | None = None) -> TwellMatrix:
+    """The compact row-ELL (one tile per row, ``width`` slots, dense backup for wider rows) of
+    the TwELL src."""
+    if out is None:
+        out = TwellMatrix(src.rows, src.cols, src.cols, width, ovf_cap, val_dtype or src.val_dtype,
+                          src.counts.device)
+    ms, md = src.c(), out.c()
+    _check(lib().twell_to_row_ell(_c.byref(ms), _c.byref(md), _stream(src.counts.device)), "twell_to_row_ell")
+    return out

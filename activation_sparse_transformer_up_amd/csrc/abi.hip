@@ -50,14 +50,23 @@ inline int hip_status(hipError_t e) { return e == hipSuccess ? TWELL_OK : TWELL_
     if (e_ != hipSuccess) return TWELL_ERR_HIP;    \
   } while (0)
 
-// Shape and pointer checks of a TwELL struct used as output (writable) or input.
-int check_matrix(const twell_matrix_t *m, bool need_ovf_bits, bool need_rows = false) {
+// A TwELL whose single tile spans the row: the compact row-ELL of the hybrid format.
+inline bool is_row_ell(const twell_matrix_t *m) { return m->tile_w == m->cols && m->tile_w != 64 && m->tile_w != 128; }
+
+// Shape and pointer checks of a TwELL struct used as output (writable) or input. row_ell:
+// the consumer also takes the row-ELL form (tile_w == cols, 1 <= slots <= cols <= 16384).
+int check_matrix(const twell_matrix_t *m, bool need_ovf_bits, bool need_rows = false, bool row_ell = false) {
   if (!m) return TWELL_ERR_ARG;
   if (!dtype_ok(m->val_dtype)) return TWELL_ERR_ARG;
   if (m->rows < 0 || m->cols <= 0 || m->ovf_cap < 0) return TWELL_ERR_SHAPE;
-  if (m->tile_w != 64 && m->tile_w != 128) return TWELL_ERR_UNSUPPORTED;
-  if (m->cols % m->tile_w) return TWELL_ERR_SHAPE;
-  if (m->slots < 1 || m->slots > m->tile_w || m->slots > 64) return TWELL_ERR_SHAPE;
+  if (row_ell && is_row_ell(m)) {
+    if (m->cols > 16384) return TWELL_ERR_UNSUPPORTED;
+    if (m->slots < 1 || m->slots > m->cols) return TWELL_ERR_SHAPE;
+  } else {
+    if (m->tile_w != 64 && m->tile_w != 128) return TWELL_ERR_UNSUPPORTED;
+    if (m->cols % m->tile_w) return TWELL_ERR_SHAPE;
+    if (m->slots < 1 || m->slots > m->tile_w || m->slots > 64) return TWELL_ERR_SHAPE;
+  }
   if (!m->ovf_n) return TWELL_ERR_ARG;
   if (m->rows > 0) {
     if (!m->counts || !m->col_idx || !m->vals || !m->ovf_slot) return TWELL_ERR_ARG;
@@ -247,10 +256,10 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
 }
 
 static int down_args(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model, const void *y,
-                     int32_t y_dtype) {
+                     int32_t y_dtype, bool row_ell = false) {
   if (!h || !w2 || !y) return TWELL_ERR_ARG;
   if (!dtype_ok(w_dtype) || !dtype_ok(y_dtype)) return TWELL_ERR_ARG;
-  int st = check_matrix(h, false, true);
+  int st = check_matrix(h, false, true, row_ell);
   if (st) return st;
   if (d_model <= 0) return TWELL_ERR_SHAPE;
   if (d_model % 8) return TWELL_ERR_ALIGN;
@@ -274,7 +283,7 @@ int twell_fwd_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int
 
 int twell_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model, void *y,
                int32_t y_dtype, void *stream) {
-  int st = down_args(h, w2, w_dtype, d_model, y, y_dtype);
+  int st = down_args(h, w2, w_dtype, d_model, y, y_dtype, true);
   if (st) return st;
   if (h->rows == 0) return TWELL_OK;
   TW_TRY(launch_twell_down(in_of(h), w2, w_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, true,
@@ -375,7 +384,17 @@ size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, i
                                      const twell_matrix_t *h) {
   if (!h || T < 0 || d_model <= 0 || d_ff <= 0 || h->tile_w <= 0 || h->slots <= 0 || h->ovf_cap < 0) return 0;
   if (!dtype_ok(in_dtype)) return 0;
-  return bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap, in_dtype == TWELL_BF16);
+  const size_t nz = bwd_entry_capacity(T, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap);
+  return bwd_workspace_bytes(T, d_model, d_ff, nz, in_dtype == TWELL_BF16);
+}
+
+size_t twell_ffn_bwd_workspace_bytes_nnz(int32_t T, int32_t d_model, int32_t d_ff, int32_t in_dtype,
+                                         const twell_matrix_t *h, int64_t nnz) {
+  if (!h || T < 0 || d_model <= 0 || d_ff <= 0 || h->tile_w <= 0 || h->slots <= 0 || h->ovf_cap < 0 || nnz < 0)
+    return 0;
+  if (!dtype_ok(in_dtype)) return 0;
+  const size_t cap = bwd_entry_capacity(T, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap);
+  return bwd_workspace_bytes(T, d_model, d_ff, (size_t)nnz < cap ? (size_t)nnz : cap, in_dtype == TWELL_BF16);
 }
 
 int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dtype, int32_t T,
@@ -386,16 +405,19 @@ int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dty
   if (T > 0 && (!dy || !dx)) return TWELL_ERR_ARG;
   int st = check_ffn_args(x, w1t, w2, in_dtype, T, d_model, d_ff);
   if (st) return st;
-  st = check_matrix(h, false);
+  st = check_matrix(h, false, false, true);
   if (st) return st;
   if (h->rows != T || h->cols != d_ff) return TWELL_ERR_SHAPE;
   if (!al16(dy) || !al16(dx) || !al16(dw1t) || !al16(dw2) || !al4(db1) || !al16(workspace)) return TWELL_ERR_ALIGN;
   // unit masks of a 32-token block live in LDS (4 bytes per unit)
   if (d_ff > 16384) return TWELL_ERR_UNSUPPORTED;
-  const size_t need =
-      bwd_workspace_bytes(T, d_model, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap, in_dtype == TWELL_BF16);
-  if (workspace_bytes < need) return TWELL_ERR_WORKSPACE;
+  // the workspace holds `nz` entries (all of h's capacity if it is that large); whether the
+  // call's actual entries fit is checked on the device
+  const size_t cap = bwd_entry_capacity(T, d_ff, d_ff / h->tile_w, h->slots, h->ovf_cap);
+  const size_t nz = bwd_fit_entries(T, d_model, d_ff, workspace_bytes, cap, in_dtype == TWELL_BF16);
+  if (nz == SIZE_MAX) return TWELL_ERR_WORKSPACE;
   BwdArgs a;
+  a.nz = nz;
   a.h = in_of(h);
   a.x = x; a.w1t = w1t; a.w2 = w2; a.dy = dy;
   a.l1 = l1_coef;
@@ -469,7 +491,7 @@ int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, 
 
 int twell_row_max_histogram(const twell_matrix_t *h, int32_t *hist, void *stream) {
   if (!hist) return TWELL_ERR_ARG;
-  int st = check_matrix(h, false);
+  int st = check_matrix(h, false, false, true);
   if (st) return st;
   if (!al4(hist)) return TWELL_ERR_ALIGN;
   TW_TRY(launch_rowmax_hist(h->counts, h->rows, h->cols / h->tile_w, h->tile_w, hist, S(stream)));
@@ -505,6 +527,52 @@ int twell_choose_slots(const int32_t *hist, int32_t tile_w, int32_t rows, int32_
   }
   if (stash_bytes) *stash_bytes = best > 0 ? best_bytes : 0;
   return best;
+}
+
+int twell_row_nnz_histogram(const twell_matrix_t *h, int32_t *hist, int32_t nbins, void *stream) {
+  if (!hist) return TWELL_ERR_ARG;
+  int st = check_matrix(h, false, false, true);
+  if (st) return st;
+  if (nbins < 2) return TWELL_ERR_SHAPE;
+  if (!al4(hist)) return TWELL_ERR_ALIGN;
+  TW_TRY(launch_row_nnz_hist(h->counts, h->rows, h->cols / h->tile_w, nbins, hist, S(stream)));
+  return TWELL_OK;
+}
+
+int twell_choose_row_ell_width(const int32_t *hist, int32_t nbins, int32_t rows, int32_t cols, int32_t ovf_cap,
+                               int32_t val_dtype, size_t *stash_bytes) {
+  if (!hist || !dtype_ok(val_dtype)) return TWELL_ERR_ARG;
+  if (nbins < 3 || rows < 0 || cols <= 0 || ovf_cap < 0) return TWELL_ERR_SHAPE;
+  // rows with more than N entries overflow; the last bin holds every row of nbins - 1 or more
+  int best = TWELL_ERR_OVF_CAPACITY;
+  size_t best_bytes = 0;
+  long long above = 0;
+  for (int m = 0; m < nbins; ++m) above += hist[m];
+  const int nmax = nbins - 2 < cols ? nbins - 2 : cols;
+  for (int N = 0; N <= nmax; ++N) {
+    above -= hist[N];                          // rows with more than N entries
+    if (N < 1 || above > ovf_cap) continue;
+    const size_t b = twell_stash_bytes(rows, cols, cols, N, (int32_t)above, val_dtype);
+    if (best < 0 || b < best_bytes) {
+      best = N;
+      best_bytes = b;
+    }
+  }
+  if (stash_bytes) *stash_bytes = best > 0 ? best_bytes : 0;
+  return best;
+}
+
+int twell_to_row_ell(const twell_matrix_t *src, twell_matrix_t *dst, void *stream) {
+  int st = check_matrix(src, false);
+  if (st) return st;
+  st = check_matrix(dst, true, false, true);
+  if (st) return st;
+  if (dst->rows != src->rows || dst->cols != src->cols || dst->tile_w != dst->cols) return TWELL_ERR_SHAPE;
+  if (src->val_dtype == TWELL_F32 && dst->val_dtype == TWELL_BF16) return TWELL_ERR_UNSUPPORTED;
+  if (dst->cols > 16384) return TWELL_ERR_UNSUPPORTED;
+  TW_TRY(launch_to_row_ell(in_of(src), out_of(dst), dst->slots, dst->ovf_cap, dst->ovf_n, dst->ovf_rows, dst->ovf_slot,
+                           dst->ovf_dense, S(stream)));
+  return TWELL_OK;
 }
 
 int twell_sync_status(const twell_matrix_t *h, void *stream) {

@@ -122,9 +122,9 @@ __global__ __launch_bounds__(1024) void k_scan_excl(const int32_t *in, int n, in
 
 template <typename VT>
 __global__ __launch_bounds__(256) void k_csr_fill(TwellIn h, const int32_t *__restrict__ row_ptr,
-                                                  int32_t *__restrict__ col, float *__restrict__ hval) {
+                                                  int32_t *__restrict__ col, float *__restrict__ hval, size_t nzcap) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= h.rows) return;
+  if (t >= h.rows || (size_t)row_ptr[h.rows] > nzcap) return;   // entries beyond the workspace
   const int lane = lane_id();
   const int base = row_ptr[t], lim = row_ptr[t + 1];
   const int slot = h.ovf_slot[t];
@@ -146,6 +146,17 @@ __global__ __launch_bounds__(256) void k_csr_fill(TwellIn h, const int32_t *__re
           hval[pos] = v[u];
         }
         n += __popcll(m);
+      }
+    }
+  } else if (h.n_t == 1) {
+    // one tile per row (the compact row-ELL): the lanes take the slots
+    const int m = min(h.counts[t], h.S);
+    const size_t sb = (size_t)t * h.S;
+    for (int s = lane; s < m; s += 64) {
+      const int pos = base + s;
+      if (pos < lim) {
+        col[pos] = h.col_idx[sb + s];
+        hval[pos] = Elem<VT>::load(vals, sb + s);
       }
     }
   } else {
@@ -205,7 +216,7 @@ __global__ __launch_bounds__(256) void k_sddmm_part(int T_rows, int d, int nchun
   constexpr int CW = 16 * E;
   const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
   const int c = xcd + 8 * (i / ntb), tb = i % ntb;
-  if (c >= nchunk) return;
+  if (c >= nchunk || (size_t)row_ptr[T_rows] > nz) return;     // nz: the workspace's entry capacity
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
   const int ti = tb * 16 + (threadIdx.x >> 6) * 4 + g;
   const int t = ti < T_rows ? perm[ti] : T_rows;
@@ -247,6 +258,7 @@ __global__ __launch_bounds__(256) void k_sddmm_sum(int T_rows, const int32_t *__
                                                    const int32_t *__restrict__ col, float l1,
                                                    uint2 *__restrict__ dz) {
   const size_t total = (size_t)row_ptr[T_rows];
+  if (total > nz) return;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
     float s = 0.f;
     for (int c = 0; c < nchunk; ++c) s += part[(size_t)c * nz + e];
@@ -295,12 +307,13 @@ __global__ __launch_bounds__(256) void k_gather_csr4(int R, int d, int nchunk, i
                                                      const int32_t *__restrict__ ptr,
                                                      const int32_t *__restrict__ perm,
                                                      const uint2 *__restrict__ pairs, const MT *__restrict__ M,
-                                                     float *__restrict__ out, float *__restrict__ rowsum) {
+                                                     float *__restrict__ out, float *__restrict__ rowsum,
+                                                     const int32_t *__restrict__ total, size_t nzcap) {
   constexpr int E = Vec16<MT>::N;
   constexpr int CW = 16 * E;
   const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
   const int c = xcd + 8 * (i / ntb), rb = i % ntb;
-  if (c >= nchunk) return;
+  if (c >= nchunk || (size_t)*total > nzcap) return;
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
   const int ri = rb * 16 + (threadIdx.x >> 6) * 4 + g;
   const int r = ri < R ? perm[ri] : R;
@@ -334,9 +347,10 @@ __global__ __launch_bounds__(256) void k_gather_csr4(int R, int d, int nchunk, i
 // independent of order). LDS holds the block's masks for all units.
 __global__ __launch_bounds__(256) void k_col_mask(int T_rows, int f, const int32_t *__restrict__ row_ptr,
                                                   const int32_t *__restrict__ col, uint32_t *__restrict__ mask,
-                                                  int32_t *__restrict__ cnt, int32_t *__restrict__ tot) {
+                                                  int32_t *__restrict__ cnt, int32_t *__restrict__ tot, size_t nzcap) {
   extern __shared__ uint32_t lm[];
   const int b = blockIdx.x, tid = threadIdx.x;
+  if ((size_t)row_ptr[T_rows] > nzcap) return;
   for (int j = tid; j < f; j += 256) lm[j] = 0u;
   __syncthreads();
   const int wave = tid >> 6, lane = tid & 63;
@@ -388,9 +402,9 @@ __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32
                                                   const int32_t *__restrict__ col, const float *__restrict__ hval,
                                                   const uint2 *__restrict__ dz, const uint32_t *__restrict__ mask,
                                                   const int32_t *__restrict__ off, uint2 *__restrict__ th,
-                                                  uint2 *__restrict__ tdz) {
+                                                  uint2 *__restrict__ tdz, size_t nzcap) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
-  if (t >= T_rows) return;
+  if (t >= T_rows || (size_t)row_ptr[T_rows] > nzcap) return;
   const int lane = lane_id();
   const int b = t >> 5, bit = t & 31;
   const uint32_t lower = (1u << bit) - 1u;
@@ -425,12 +439,15 @@ __global__ __launch_bounds__(256) void k_csc_fill(int T_rows, int f, const int32
 }
 
 // More overflow rows than backup slots (*ovf_n > cap): the rows beyond the backup kept only
-// their first S entries per tile, so their gradients cannot be formed. Every output is then
-// overwritten with a quiet NaN, so that the condition cannot pass unnoticed; otherwise the
-// kernel exits at once (one scalar load per workgroup).
-__global__ __launch_bounds__(256) void k_bwd_poison(const int32_t *__restrict__ ovf_n, int cap, float *dx, size_t ndx,
-                                                    float *dw1t, float *dw2, size_t ndw, float *db1, size_t ndb) {
-  if (*ovf_n <= cap) return;
+// their first S entries per tile, so their gradients cannot be formed. Or more entries than
+// the workspace holds (the kernels after the row scan then did nothing). In both cases every
+// output is overwritten with a quiet NaN, so that the condition cannot pass unnoticed;
+// otherwise the kernel exits at once (two scalar loads per workgroup).
+__global__ __launch_bounds__(256) void k_bwd_poison(const int32_t *__restrict__ ovf_n, int cap,
+                                                    const int32_t *__restrict__ total, size_t nzcap, float *dx,
+                                                    size_t ndx, float *dw1t, float *dw2, size_t ndw, float *db1,
+                                                    size_t ndb) {
+  if (*ovf_n <= cap && (size_t)*total <= nzcap) return;
   const float qnan = __uint_as_float(0x7FC00000u);
   const size_t stride = (size_t)gridDim.x * 256;
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < ndw; i += stride) {
@@ -456,8 +473,12 @@ static int sddmm_chunks(int d, int bf16) {
   return (d + cw - 1) / cw;
 }
 
-size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf16) {
-  const size_t NZ = (size_t)T * n_t * S + (size_t)(cap < T ? cap : T) * f;
+size_t bwd_entry_capacity(int T, int f, int n_t, int S, int cap) {
+  return (size_t)T * n_t * S + (size_t)(cap < T ? cap : T) * f;
+}
+
+// Workspace for at most NZ stored entries (slots in use plus nonzeros of the backup rows).
+size_t bwd_workspace_bytes(int T, int d, int f, size_t NZ, int bf16) {
   const size_t NB = ((size_t)T + 31) / 32;
   size_t b = 0;
   b += al256(4 * NZ * (size_t)sddmm_chunks(d, bf16));   // SDDMM partial dot products
@@ -471,10 +492,24 @@ size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf1
   return b;
 }
 
+// The largest entry count up to NZmax whose workspace fits in `bytes` (bytes grows with it);
+// SIZE_MAX if not even an empty one fits.
+size_t bwd_fit_entries(int T, int d, int f, size_t bytes, size_t NZmax, int bf16) {
+  if (bwd_workspace_bytes(T, d, f, 0, bf16) > bytes) return SIZE_MAX;
+  if (bwd_workspace_bytes(T, d, f, NZmax, bf16) <= bytes) return NZmax;
+  size_t lo = 0, hi = NZmax;                // fits(lo), !fits(hi)
+  while (hi - lo > 1) {
+    const size_t mid = lo + (hi - lo) / 2;
+    if (bwd_workspace_bytes(T, d, f, mid, bf16) <= bytes) lo = mid;
+    else hi = mid;
+  }
+  return lo;
+}
+
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   const TwellIn &h = a.h;
   const int T = h.rows, f = h.cols, d = a.d;
-  const size_t NZ = (size_t)T * h.n_t * h.S + (size_t)(a.cap < T ? a.cap : T) * f;
+  const size_t NZ = a.nz;                   // entry capacity of the workspace (checked on the device)
   const size_t NB = ((size_t)T + 31) / 32;
   const int nchunk = sddmm_chunks(d, a.bf16);
   char *p = (char *)a.ws;
@@ -500,8 +535,8 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
   }
   hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, row_ptr, T, row_ptr);
   if (T > 0) {
-    if (h.val_bf16) hipLaunchKernelGGL(k_csr_fill<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr, col, hval);
-    else hipLaunchKernelGGL(k_csr_fill<float>, rows4, dim3(256), 0, s, h, row_ptr, col, hval);
+    if (h.val_bf16) hipLaunchKernelGGL(k_csr_fill<uint16_t>, rows4, dim3(256), 0, s, h, row_ptr, col, hval, NZ);
+    else hipLaunchKernelGGL(k_csr_fill<float>, rows4, dim3(256), 0, s, h, row_ptr, col, hval, NZ);
     hipLaunchKernelGGL(k_order_by_len, dim3(1), dim3(1024), 0, s, T, row_ptr, perm_t);
     const int ntb = (T + 15) / 16;
     const size_t grid = 8 * (size_t)ntb * ((nchunk + 7) / 8);
@@ -509,7 +544,7 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
                                    (const uint16_t *)a.dy, (const uint16_t *)a.w2, row_ptr, perm_t, col, NZ, part);
     else hipLaunchKernelGGL((k_sddmm_part<float>), dim3((unsigned)grid), dim3(256), 0, s, T, d, nchunk, ntb,
                             (const float *)a.dy, (const float *)a.w2, row_ptr, perm_t, col, NZ, part);
-    const unsigned sum_grid = (unsigned)std::min<size_t>((NZ + 255) / 256, 4096);
+    const unsigned sum_grid = (unsigned)std::max<size_t>(1, std::min<size_t>((NZ + 255) / 256, 4096));
     hipLaunchKernelGGL(k_sddmm_sum, dim3(sum_grid), dim3(256), 0, s, T, row_ptr, NZ, nchunk, part, col, a.l1, dz);
   }
   auto gather = [&](int R, const int32_t *ptr, const int32_t *perm, const uint2 *pairs, const void *M, float *out,
@@ -517,27 +552,27 @@ hipError_t launch_bwd(const BwdArgs &a, hipStream_t s) {
     const int ntb = (R + 15) / 16;
     const size_t grid = 8 * (size_t)ntb * ((nchunk + 7) / 8);
     if (a.bf16) hipLaunchKernelGGL((k_gather_csr4<uint16_t>), dim3((unsigned)grid), dim3(256), 0, s, R, d, nchunk, ntb,
-                                   ptr, perm, pairs, (const uint16_t *)M, out, rowsum);
+                                   ptr, perm, pairs, (const uint16_t *)M, out, rowsum, row_ptr + T, NZ);
     else hipLaunchKernelGGL((k_gather_csr4<float>), dim3((unsigned)grid), dim3(256), 0, s, R, d, nchunk, ntb, ptr,
-                            perm, pairs, (const float *)M, out, rowsum);
+                            perm, pairs, (const float *)M, out, rowsum, row_ptr + T, NZ);
   };
   // dx = dz . w1t
   if (T > 0) gather(T, row_ptr, perm_t, dz, a.w1t, a.dx, nullptr);
   // CSC
   if (T > 0)
     hipLaunchKernelGGL(k_col_mask, dim3((unsigned)NB), dim3(256), (size_t)f * 4, s, T, f, row_ptr, col, mask, cnt,
-                       col_ptr);
+                       col_ptr, NZ);
   hipLaunchKernelGGL(k_scan_excl, dim3(1), dim3(1024), 0, s, col_ptr, f, col_ptr);
   if (T > 0) {
     hipLaunchKernelGGL(k_col_off, dim3((f + 63) / 64), dim3(1024), 0, s, (int)NB, f, col_ptr, cnt);
-    hipLaunchKernelGGL(k_csc_fill, rows4, dim3(256), 0, s, T, f, row_ptr, col, hval, dz, mask, cnt, th, tdz);
+    hipLaunchKernelGGL(k_csc_fill, rows4, dim3(256), 0, s, T, f, row_ptr, col, hval, dz, mask, cnt, th, tdz, NZ);
   }
   // dw2 = h^T dy, dw1t = dz^T x (every unit row written, zero if it has no entry), db1
   hipLaunchKernelGGL(k_order_by_len, dim3(1), dim3(1024), 0, s, f, col_ptr, perm_u);
   gather(f, col_ptr, perm_u, th, a.dy, a.dw2, nullptr);
   gather(f, col_ptr, perm_u, tdz, a.x, a.dw1t, a.db1);
-  hipLaunchKernelGGL(k_bwd_poison, dim3(256), dim3(256), 0, s, h.ovf_n, a.cap, a.dx, (size_t)T * d, a.dw1t, a.dw2,
-                     (size_t)f * d, a.db1, (size_t)f);
+  hipLaunchKernelGGL(k_bwd_poison, dim3(256), dim3(256), 0, s, h.ovf_n, a.cap, row_ptr + T, NZ, a.dx, (size_t)T * d,
+                     a.dw1t, a.dw2, (size_t)f * d, a.db1, (size_t)f);
   return hipGetLastError();
 }
 

@@ -59,6 +59,18 @@ hipError_t launch_ovf_scan(const uint32_t *bits, int n_t, int words, int R, int 
 hipError_t launch_ovf_copy(const void *h, int h_bf16, int R, int C, const int32_t *ovf_n, const int32_t *ovf_rows,
                            int cap, void *dense, int dense_bf16, hipStream_t s);
 hipError_t launch_set_int(int32_t *p, int v, hipStream_t s);
+hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t s);
+
+#define TW_TRY_HIP(expr)                 \
+  do {                                   \
+    hipError_t e_ = (expr);              \
+    if (e_ != hipSuccess) return e_;     \
+  } while (0)
+
+// rell.hip: the compact row-ELL (one tile per row) from a TwELL, and the row-nonzero histogram
+hipError_t launch_to_row_ell(const TwellIn &src, const TwellOut &dst, int N, int cap, int32_t *ovf_n,
+                             int32_t *ovf_rows, int32_t *ovf_slot, void *dense, hipStream_t s);
+hipError_t launch_row_nnz_hist(const int32_t *counts, int rows, int n_t, int nbins, int32_t *hist, hipStream_t s);
 // hist[0 .. W] <- histogram of the per-row maximum tile count
 hipError_t launch_rowmax_hist(const int32_t *counts, int rows, int n_t, int W, int32_t *hist, hipStream_t s);
 
@@ -69,9 +81,12 @@ struct BwdArgs {
   float l1;
   float *dx, *dw1t, *dw2, *db1;
   void *ws;
+  size_t nz;              // entries the workspace holds (bwd_fit_entries)
   int d, bf16, cap;
 };
-size_t bwd_workspace_bytes(int T, int d, int f, int n_t, int S, int cap, int bf16);
+size_t bwd_entry_capacity(int T, int f, int n_t, int S, int cap);
+size_t bwd_workspace_bytes(int T, int d, int f, size_t NZ, int bf16);
+size_t bwd_fit_entries(int T, int d, int f, size_t bytes, size_t NZmax, int bf16);
 hipError_t launch_bwd(const BwdArgs &a, hipStream_t s);
 
 // gated.hip

@@ -171,6 +171,11 @@ hipError_t launch_rowmax_hist(const int32_t *counts, int rows, int n_t, int W, i
   return hipGetLastError();
 }
 
+hipError_t launch_zero_i32(int32_t *p, int n, hipStream_t s) {
+  if (n > 0) hipLaunchKernelGGL(k_zero_i32, dim3((n + 255) / 256), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
 hipError_t launch_set_int(int32_t *p, int v, hipStream_t s) {
   hipLaunchKernelGGL(k_set_int, dim3(1), dim3(1), 0, s, p, v);
   return hipGetLastError();

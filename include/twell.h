@@ -254,14 +254,23 @@ int ffn_up_relu_dense(const void *x, const void *w1t, const float *b1, int32_t i
                       void *stream);
 
 /*
- * Bytes of device workspace twell_ffn_bwd needs for this problem (in_dtype as passed to
- * twell_ffn_bwd; 0 for invalid arguments). Grows with the entry capacity of h
- * (T * (d_ff / tile_w) * slots + min(ovf_cap, T) * d_ff) times roughly 32 + 4 * d_model / 128
- * bytes (bf16; d_model / 64 chunks for fp32): the per-column-chunk partial dot products of
- * the SDDMM are kept so that every XCD reads only its own slices of W2.
+ * Workspace of twell_ffn_bwd. It grows with the number of entries it can hold, about
+ * 36 + 4 * d_model / 128 bytes each (bf16; d_model / 64 column chunks for fp32: the SDDMM keeps
+ * one partial dot product per entry and chunk so that every XCD reads only its own slices of
+ * W2), plus 8 bytes per (32-token block, unit) and small per-token and per-unit arrays.
+ *   twell_ffn_bwd_workspace_bytes      — room for every entry h can hold, T * (d_ff / tile_w)
+ *                                        * slots + min(ovf_cap, T) * d_ff: always enough.
+ *   twell_ffn_bwd_workspace_bytes_nnz  — room for nnz entries (at most that capacity): the
+ *                                        stored entries of the call, i.e. the sum over rows of
+ *                                        the row's nonzeros (slots in use, or the nonzeros of
+ *                                        its backup row), which a caller knows from
+ *                                        twell_row_nnz_histogram (sum of m * hist[m]).
+ * 0 for invalid arguments. in_dtype as passed to twell_ffn_bwd.
  */
 size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, int32_t in_dtype,
                                      const twell_matrix_t *h);
+size_t twell_ffn_bwd_workspace_bytes_nnz(int32_t T, int32_t d_model, int32_t d_ff, int32_t in_dtype,
+                                         const twell_matrix_t *h, int64_t nnz);
 
 /*
  * twell_ffn_bwd — gradients of <dy, y> + l1_coef * sum(h) for the forward above.
@@ -278,8 +287,11 @@ size_t twell_ffn_bwd_workspace_bytes(int32_t T, int32_t d_model, int32_t d_ff, i
  * formed, and then every output (dx, dw1t, dw2 and db1) is overwritten with quiet NaN on the
  * device, so the condition cannot pass unnoticed (twell_sync_status also reports it).
  * d_ff <= 16384 (a unit bit mask per 32-token block is built in LDS), else
- * TWELL_ERR_UNSUPPORTED; workspace_bytes below twell_ffn_bwd_workspace_bytes gives
- * TWELL_ERR_WORKSPACE.
+ * TWELL_ERR_UNSUPPORTED. The workspace may be smaller than twell_ffn_bwd_workspace_bytes:
+ * the call uses it for as many entries as fit, and if the call's entries do not fit (checked
+ * on the device) every output is overwritten with quiet NaN; a workspace too small for even
+ * zero entries gives TWELL_ERR_WORKSPACE before anything is enqueued. Contents need not be
+ * initialised.
  */
 int twell_ffn_bwd(const void *x, const void *w1t, const void *w2, int32_t in_dtype,
                   int32_t T, int32_t d_model, int32_t d_ff, const twell_matrix_t *h,
@@ -374,6 +386,45 @@ size_t twell_stash_bytes(int32_t rows, int32_t cols, int32_t tile_w, int32_t slo
  */
 int twell_choose_slots(const int32_t *hist, int32_t tile_w, int32_t rows, int32_t cols, int32_t ovf_cap,
                        int32_t val_dtype, size_t *stash_bytes);
+
+/*
+ * The compact row-ELL of the hybrid training format ("Formato Híbrido para Treinamento": rows
+ * with few nonzeros in a compact ELL whose width follows the data, the rest in a dense
+ * backup). It is a twell_matrix_t whose single tile spans the row: tile_w == cols, slots = the
+ * width N (1 <= N <= cols <= 16384), counts [R][1] = the row's nonzeros, col_idx / vals
+ * [R][N] its first min(count, N) entries in ascending column order (pad -1, +0.0), and the
+ * same ordered dense backup for the rows with more than N entries. twell_down,
+ * twell_ffn_bwd (and _noalloc), twell_row_max_histogram, twell_row_nnz_histogram and
+ * twell_sync_status take it; the GEMM producers and twell_pack make tile_w 64 or 128 only.
+ *
+ * twell_to_row_ell — the row-ELL `dst` (shape fields and buffers from the caller: rows and
+ * cols of src, tile_w = cols, slots = N, ovf_cap, val_dtype; ovf_bits as
+ * twell_ovf_bits_words) of a TwELL `src` whose backup bookkeeping is complete (after
+ * twell_up_finish / twell_ffn_fwd or twell_pack). Values are copied bit for bit (bf16 ->
+ * fp32 widening is exact; fp32 -> bf16 is refused). A src row beyond src's backup capacity
+ * lost entries: then dst's *ovf_n is raised above dst's ovf_cap, so the capacity error
+ * follows the data. Errors: TWELL_ERR_ARG, TWELL_ERR_SHAPE (dst not a row-ELL of src's
+ * shape), TWELL_ERR_UNSUPPORTED.
+ */
+int twell_to_row_ell(const twell_matrix_t *src, twell_matrix_t *dst, void *stream);
+
+/*
+ * twell_row_nnz_histogram — hist[min(n_t, nbins - 1)] = number of rows t of h with n_t
+ * nonzeros (the sum of the row's true tile counts, also for backup rows), nbins >= 2; hist:
+ * device int32 [nbins], overwritten. sum over m of m * hist[m] (with nbins above the widest
+ * row) is the number of entries the backward stores for h.
+ */
+int twell_row_nnz_histogram(const twell_matrix_t *h, int32_t *hist, int32_t nbins, void *stream);
+
+/*
+ * twell_choose_row_ell_width — host function; hist is a HOST copy of a row-nonzero histogram
+ * (nbins >= 3). Returns the width N in 1 .. min(nbins - 2, cols) whose row-ELL has the
+ * smallest twell_stash_bytes (tile_w = cols) among those whose rows with more than N entries
+ * fit ovf_cap (the smaller N on equal bytes), its bytes in *stash_bytes (may be NULL).
+ * TWELL_ERR_OVF_CAPACITY if none fits.
+ */
+int twell_choose_row_ell_width(const int32_t *hist, int32_t nbins, int32_t rows, int32_t cols,
+                               int32_t ovf_cap, int32_t val_dtype, size_t *stash_bytes);
 
 /*
  * twell_sync_status — waits for `stream`, then reads *ovf_n: TWELL_ERR_OVF_CAPACITY if it

@@ -226,6 +226,38 @@ def choose_slots(hist: np.ndarray, tile_w: int, rows: int, cols: int, ovf_cap: i
     return best
 
 
+def row_nnz_histogram(counts: np.ndarray, nbins: int) -> np.ndarray:
+    """hist[min(n_t, nbins - 1)] = number of rows t with n_t nonzeros (the sum of the row's
+    true tile counts).
+
+    [SFL] "Formato Híbrido para Treinamento": the compact ELL keeps a row's entries up to a
+    width chosen from the data, and wider rows go to the dense backup; with a single tile per
+    row a row fits N slots iff it has at most N nonzeros, so the rows above N are counted in
+    hist[N + 1 ..]. Pinned against the packer's own overflow count with tile_w = cols.
+    """
+    hist = np.zeros(nbins, np.int64)
+    for n in counts.sum(axis=1):
+        hist[min(int(n), nbins - 1)] += 1
+    return hist
+
+
+def choose_row_ell_width(hist: np.ndarray, rows: int, cols: int, ovf_cap: int, val_bytes: int):
+    """The width N of the compact row-ELL ([SFL] "Formato Híbrido para Treinamento"), read as
+    for the slot count: among N = 1 .. min(len(hist) - 2, cols) whose rows with more than N
+    nonzeros fit the backup capacity, the one with the smallest stash (one tile per row:
+    ``stash_bytes`` with tile_w = cols), the smaller N on equal bytes. Returns (N, bytes) or
+    (None, None)."""
+    best = (None, None)
+    for N in range(1, min(len(hist) - 2, cols) + 1):
+        n_ovf = int(hist[N + 1:].sum())
+        if n_ovf > ovf_cap:
+            continue
+        b = stash_bytes(rows, cols, cols, N, n_ovf, val_bytes)
+        if best[1] is None or b < best[1]:
+            best = (N, b)
+    return best
+
+
 # --------------------------------------------------------------------- N:M activations
 
 def nm_prune(h: np.ndarray, n: int, m: int):

@@ -118,3 +118,54 @@ def test_library_choose_slots_no_fit_and_rejects():
     assert L.twell_choose_slots(hist.ctypes.data_as(ctypes.c_void_p), 64, 5, 250, 5, 0, None) == -2
     assert L.twell_stash_bytes(5, 250, 64, 8, 0, 0) == 0
     assert L.twell_row_max_histogram(None, None, None) == -1
+
+
+# ------------------------------------------------------------ the compact row-ELL width
+
+def test_row_nnz_histogram_tail_is_the_row_ell_overflow_count():
+    R, C = 90, 768
+    h = skewed_h(R, C, 11)
+    counts = orc.twell_pack(h, 128, 1, R)["counts"]
+    hist = orc.row_nnz_histogram(counts, C + 1)
+    assert hist.sum() == R
+    assert int((hist * np.arange(C + 1)).sum()) == int((h != 0).sum())
+    for N in (1, 5, 20, 60, C):
+        assert orc.twell_pack(h, C, N, R)["ovf_n"] == int(hist[N + 1:].sum()), N
+    # a last bin below the widest row collects every wider row
+    short = orc.row_nnz_histogram(counts, 10)
+    assert short.sum() == R and short[9] == int((hist[9:]).sum())
+
+
+def test_choose_row_ell_width_brute_force():
+    R, C = 60, 384
+    h = skewed_h(R, C, 12)
+    hist = orc.row_nnz_histogram(orc.twell_pack(h, 64, 1, R)["counts"], C + 1)
+    for cap in (0, 2, 9, R):
+        best = (None, None)
+        for N in range(1, C + 1):
+            tw = orc.twell_pack(h, C, N, R)
+            n = tw["ovf_n"]
+            if n > cap:
+                continue
+            b = (tw["counts"].size + tw["col_idx"].size + tw["vals"].size + R + n + n * C) * 4
+            if best[1] is None or b < best[1]:
+                best = (N, b)
+        assert orc.choose_row_ell_width(hist, R, C, cap, 4) == best, cap
+
+
+@pytest.mark.parametrize("R,C,cap,seed", [(16384, 14336, 1024, 1), (300, 1024, 0, 2), (500, 4096, 20, 3)])
+def test_library_row_ell_width_matches_oracle(R, C, cap, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    hist = np.zeros(C + 1, np.int64)
+    np.add.at(hist, np.minimum(rng.poisson(0.0125 * C, size=R) + (rng.random(R) < 0.01) * C // 4, C), 1)
+    for nbins in (C + 1, 200):
+        hb = hist if nbins == C + 1 else np.concatenate([hist[:nbins - 1], [hist[nbins - 1:].sum()]])
+        for vdt, vb in ((torch.float32, 4), (torch.bfloat16, 2)):
+            N, b = orc.choose_row_ell_width(hb, R, C, cap, vb)
+            if N is None:
+                with pytest.raises(tw.TwellError) as e:
+                    tw.twell_choose_row_ell_width(hb, R, C, cap, vdt)
+                assert e.value.status == -5
+                continue
+            assert tw.twell_choose_row_ell_width(hb, R, C, cap, vdt) == (N, b)
