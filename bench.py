@@ -411,7 +411,19 @@ def leg_decode_graph(steps, warmup):
 
 def leg_c5(steps, warmup):
     """Training step (forward + backward with the L1 term) vs the dense bf16 FFN's
-    forward + backward through autograd (the same six GEMMs a dense layer needs)."""
+    forward + backward through autograd (the same six GEMMs a dense layer needs).
+
+    Two flows of the hybrid format ("Formato Híbrido para Treinamento"):
+      twell : the forward's TwELL (W=128, S=8) is the stash, the backward workspace sized for
+              the whole entry capacity (no host round trip; the headline ms_fwd_bwd);
+      rowell: after the forward, the row-nonzero histogram goes to the host, which picks the
+              compact row-ELL width of this step (twell_choose_row_ell_width) and the exact
+              entry count; the TwELL is converted into the row-ELL stash and freed, and the
+              backward runs on the row-ELL with a workspace sized for the step's entries.
+    Peak memory: device bytes allocated during one step above what was allocated before it
+    (inputs and weights), outputs included (y, dx, dW1, dW2, db1; the dense layer's autograd
+    keeps bf16 gradients, ours are fp32)."""
+    import numpy as np
     import torch
     import activation_sparse_transformer_up_amd as tw
     import synth
@@ -421,10 +433,11 @@ def leg_c5(steps, warmup):
     x, w1t, w2, dy = (_up(g[k], "bf16", dev) for k in ("x", "w1t", "w2", "dy"))
     b1 = _up(g["b1"], "f32", dev)
     T, f, d = w.T, w.f, w.d
-    cap = 1024
+    cap, cap_ell = 1024, 1024
     h = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.float32, dev)
     y = torch.empty((T, d), device=dev)
     ws = torch.empty((tw.twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype),), dtype=torch.uint8, device=dev)
+    ws_capacity_bytes = ws.numel()
 
     def step():
         tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y)
@@ -438,11 +451,9 @@ def leg_c5(steps, warmup):
     tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=h, y=y)
     ovf = int(h.ovf_n.item())
     dens = float(h.counts.sum().item()) / (T * f)
-    # Activation memory kept for the backward ("Formato Híbrido para Treinamento"): counts,
-    # slots (int32 index + fp32 value) and the fp32 backup rows of the overflow rows, against
-    # a dense h. The dynamic width of the hybrid: the library's row-maximum histogram of this
-    # step's true counts gives the overflow rows for every S, and twell_choose_slots the
-    # smallest stash whose overflow rows fit the backup capacity (the S of the next step).
+    # Activation memory kept for the backward: counts, slots (int32 index + fp32 value) and the
+    # fp32 backup rows, against a dense h; per slot count from the row-maximum histogram, and
+    # the slot count twell_choose_slots picks.
     dense_bf16 = T * f * 2
     hist_dev = tw.twell_row_max_histogram(h)
     ms_hist = _time(lambda: tw.twell_row_max_histogram(h, hist_dev), steps, warmup)
@@ -454,13 +465,59 @@ def leg_c5(steps, warmup):
         per_s[str(S)] = {"overflow_rows": n_ovf, "bytes": b, "frac_of_dense_bf16": b / dense_bf16}
     best, best_bytes = tw.twell_choose_slots(hist, w.tile_w, T, f, cap)
     stash = tw.twell_stash_bytes(T, f, w.tile_w, w.slots, ovf)
+    # the compact row-ELL of this step
+    nnz_hist = tw.twell_row_nnz_histogram(h).cpu().numpy()
+    nnz = int((nnz_hist * np.arange(len(nnz_hist))).sum())
+    width, ell_bytes = tw.twell_choose_row_ell_width(nnz_hist, T, f, cap_ell)
+    ws_entries_bytes = tw.twell_ffn_bwd_workspace_bytes(T, d, f, h, x.dtype, nnz=nnz)
     mem = {"dense_h_bf16_bytes": dense_bf16, "dense_h_fp32_bytes": 2 * dense_bf16,
            "stash_bytes": stash, "stash_frac_of_dense_bf16": stash / dense_bf16,
            "per_slots": per_s, "chosen_slots": best, "chosen_stash_bytes": best_bytes,
            "chosen_frac_of_dense_bf16": best_bytes / dense_bf16, "cap": cap,
-           "row_max_histogram_ms": ms_hist}
-    del ws
+           "row_max_histogram_ms": ms_hist, "stored_entries": nnz,
+           "row_ell_width": width, "row_ell_stash_bytes": ell_bytes,
+           "row_ell_frac_of_dense_bf16": ell_bytes / dense_bf16, "row_ell_cap": cap_ell,
+           "bwd_workspace_capacity_bytes": ws_capacity_bytes, "bwd_workspace_entries_bytes": ws_entries_bytes}
+    del ws, h, y
     torch.cuda.empty_cache()
+
+    def step_twell_entries():
+        hh = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.float32, dev)
+        yy, _ = tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=hh)
+        hist_h = tw.twell_row_nnz_histogram(hh).cpu().numpy()
+        n = int((hist_h * np.arange(len(hist_h))).sum())
+        wsb = torch.empty((tw.twell_ffn_bwd_workspace_bytes(T, d, f, hh, x.dtype, nnz=n),), dtype=torch.uint8,
+                          device=dev)
+        return yy, tw.twell_ffn_bwd(x, w1t, w2, hh, dy, w.l1_coef, workspace=wsb)
+
+    def step_rowell():
+        hh = tw.TwellMatrix(T, f, w.tile_w, w.slots, cap, torch.float32, dev)
+        yy, _ = tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, cap, h=hh)
+        hist_h = tw.twell_row_nnz_histogram(hh).cpu().numpy()
+        N, _ = tw.twell_choose_row_ell_width(hist_h, T, f, cap_ell)
+        n = int((hist_h * np.arange(len(hist_h))).sum())
+        e = tw.twell_to_row_ell(hh, N, cap_ell)
+        del hh                                   # the stash is the row-ELL from here on
+        wsb = torch.empty((tw.twell_ffn_bwd_workspace_bytes(T, d, f, e, x.dtype, nnz=n),), dtype=torch.uint8,
+                          device=dev)
+        return yy, tw.twell_ffn_bwd(x, w1t, w2, e, dy, w.l1_coef, workspace=wsb)
+
+    def peak_of(fn):
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        base = torch.cuda.memory_allocated()
+        torch.cuda.reset_peak_memory_stats()
+        out = fn()
+        torch.cuda.synchronize()
+        peak = torch.cuda.max_memory_allocated() - base
+        del out
+        torch.cuda.empty_cache()
+        return peak
+
+    ms_twell_entries = _time(step_twell_entries, steps, warmup)
+    ms_rowell = _time(step_rowell, steps, warmup)
+    peak_twell = peak_of(step_twell_entries)
+    peak_rowell = peak_of(step_rowell)
     xd = x.clone().requires_grad_(True)
     w1d = w1t.clone().requires_grad_(True)
     w2d = w2.clone().requires_grad_(True)
@@ -471,10 +528,23 @@ def leg_c5(steps, warmup):
         yy = hh @ w2d
         loss = (yy * dy).sum() + w.l1_coef * hh.float().sum()
         loss.backward()
+        grads = (xd.grad, w1d.grad, w2d.grad, bd.grad)
         xd.grad = w1d.grad = w2d.grad = bd.grad = None
+        return yy, grads
 
     ms_dense = _time(dense_step, steps, warmup)
-    del xd, w1d, w2d, bd, x, w1t, w2, dy, b1, h, y
+    peak_dense = peak_of(dense_step)
+    # the outputs each flow allocates: ours fp32 y, dx, dW1, dW2, db1; the dense layer bf16
+    out_ours = 4 * (2 * T * d + 2 * f * d + f)
+    out_dense = 2 * (2 * T * d + 2 * f * d + f)
+    mem.update({"peak_step_bytes_twell_stash": peak_twell, "peak_step_bytes_row_ell_stash": peak_rowell,
+                "peak_step_bytes_dense": peak_dense,
+                "peak_row_ell_vs_dense": peak_rowell / peak_dense, "peak_twell_vs_dense": peak_twell / peak_dense,
+                "outputs_bytes_ours_fp32": out_ours, "outputs_bytes_dense_bf16": out_dense,
+                "peak_minus_outputs_row_ell": peak_rowell - out_ours, "peak_minus_outputs_twell": peak_twell - out_ours,
+                "peak_minus_outputs_dense": peak_dense - out_dense,
+                "peak_minus_outputs_row_ell_vs_dense": (peak_rowell - out_ours) / max(1, peak_dense - out_dense)})
+    del xd, w1d, w2d, bd, x, w1t, w2, dy, b1
     torch.cuda.empty_cache()
     # hot tokens (every 1024th token's x scaled by 4, so those rows overflow) at S = 8 and 16
     variants = {f"hot1024_S{S}": c5_variant(w.with_(slots=S, hot_every=1024), cap, steps, warmup)
@@ -482,6 +552,7 @@ def leg_c5(steps, warmup):
     achieved = 2.0 * T * d * f / (ms_up * 1e-3) / 1e12
     return {"tokens_per_s": T / (ms * 1e-3), "ms_fwd_bwd": ms, "ms_fwd": ms_fwd, "ms_bwd": ms - ms_fwd,
             "dense_ms_fwd_bwd": ms_dense, "speedup_vs_dense": ms_dense / ms, "density": dens,
+            "ms_fwd_bwd_entry_workspace": ms_twell_entries, "ms_fwd_bwd_row_ell": ms_rowell,
             "up_gemm_ms": ms_up, "up_gemm_frac_mfma_peak": up_frac,
             "roofline": {"kernel": "k_up_twell (up GEMM + fused ReLU/TwELL epilogue)", "bound": "mfma",
                          "achieved": achieved, "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
