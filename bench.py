@@ -363,24 +363,37 @@ def leg_decode_graph(steps, warmup):
     dev = torch.device("cuda:0")
     w = synth.C3
     out = {}
-    x_bits, layers = synth.decode_layers(4, 8)
+    x_bits, layers = synth.decode_layers(4, 64)
     L = [(_up(a["w1t"], "bf16", dev), _up(a["b1"], "f32", dev), _up(a["w2"], "bf16", dev)) for a in layers]
     x_all = _up(x_bits, "bf16", dev)
-    for T in (1, 8):
+
+    def norm(y, out):
+        yf = y.float()
+        out.copy_(yf * torch.rsqrt(yf.square().mean(dim=1, keepdim=True)))
+        return out
+
+    # per-layer slot counts: each layer's row-maximum histogram on a 64-token calibration batch,
+    # the smallest stash with no row beyond S (twell_choose_slots, capacity 0)
+    hc = [tw.TwellMatrix(64, w.f, w.tile_w, w.slots, 4, torch.float32, dev) for _ in L]
+    xc = x_all
+    for (w1t, b1, w2), h in zip(L, hc):
+        yc, _ = tw.twell_ffn_fwd(xc, w1t, b1, w2, w.tile_w, w.slots, 4, h=h, y_dtype=torch.bfloat16)
+        xc = norm(yc, torch.empty_like(yc))
+    slots_cal = [tw.twell_choose_slots(tw.twell_row_max_histogram(h).cpu().numpy(), w.tile_w, 64, w.f, 0)[0]
+                 for h in hc]
+    del hc
+    out["per_layer_slots"] = slots_cal
+    for T, per_layer in ((1, False), (8, False), (1, True), (8, True)):
         x0 = x_all[:T].contiguous()
-        hs = [tw.TwellMatrix(T, w.f, w.tile_w, w.slots, 4, torch.float32, dev) for _ in L]
+        sl = slots_cal if per_layer else [w.slots] * len(L)
+        hs = [tw.TwellMatrix(T, w.f, w.tile_w, S, 4, torch.float32, dev) for S in sl]
         ys = [torch.empty((T, w.d), dtype=torch.bfloat16, device=dev) for _ in L]
         xs = [torch.empty((T, w.d), dtype=torch.bfloat16, device=dev) for _ in L]
-
-        def norm(y, out):
-            yf = y.float()
-            out.copy_(yf * torch.rsqrt(yf.square().mean(dim=1, keepdim=True)))
-            return out
 
         def run():
             x = x0
             for l, ((w1t, b1, w2), h, y) in enumerate(zip(L, hs, ys)):
-                tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, w.slots, 4, h=h, y=y, y_dtype=torch.bfloat16)
+                tw.twell_ffn_fwd(x, w1t, b1, w2, w.tile_w, h.slots, 4, h=h, y=y, y_dtype=torch.bfloat16)
                 x = norm(y, xs[l])
 
         def dense():
@@ -401,10 +414,12 @@ def leg_decode_graph(steps, warmup):
         graph_ms = _time(graph.replay, steps, warmup)
         dense_ms = _time(dense, steps, warmup)
         dens = [float((hh.counts.clamp(max=w.slots).sum() / (T * w.f)).item()) for hh in hs]
-        out[f"T{T}"] = {"layers": len(L), "layer_density": dens, "eager_ms": eager_ms, "graph_ms": graph_ms,
-                        "graph_speedup": eager_ms / graph_ms, "dense_eager_ms": dense_ms,
-                        "speedup_vs_dense": dense_ms / graph_ms,
-                        "tokens_per_s": T / (graph_ms * 1e-3)}
+        stash = sum(tw.twell_stash_bytes(T, w.f, w.tile_w, hh.slots, int(hh.ovf_n.item())) for hh in hs)
+        out[f"T{T}" + ("_per_layer_S" if per_layer else "")] = {
+            "layers": len(L), "slots": sl, "layer_density": dens, "eager_ms": eager_ms, "graph_ms": graph_ms,
+            "graph_speedup": eager_ms / graph_ms, "dense_eager_ms": dense_ms,
+            "speedup_vs_dense": dense_ms / graph_ms, "stash_bytes": stash,
+            "tokens_per_s": T / (graph_ms * 1e-3)}
         del hs, ys, graph
     return out
 
