@@ -396,13 +396,16 @@ def ffn_up_relu_nm(x, w1t, b1, n: int, m: int, vals=None, idx=None):
     return vals, idx
 
 
-def nm_ffn_down(vals, idx, n: int, m: int, w2t: torch.Tensor, y_dtype=torch.float32, y=None):
+def nm_ffn_down(vals, idx, n: int, m: int, w2: torch.Tensor, y_dtype=torch.float32, y=None):
+    """w2: [d_ff][d_model] bf16, the down weight the TwELL entry points take."""
     T, G, _ = vals.shape
     f = G * m
-    d = w2t.shape[0]
+    if w2.shape[0] != f:
+        raise ValueError(f"nm_ffn_down: w2 has {w2.shape[0]} rows, the activations {f} columns")
+    d = w2.shape[1]
     if y is None:
         y = torch.empty((T, d), dtype=y_dtype, device=vals.device)
-    _check(lib().nm_ffn_down(_ptr(vals), _ptr(idx), _dt(vals.dtype), T, f, n, m, _ptr(w2t), d, _ptr(y),
+    _check(lib().nm_ffn_down(_ptr(vals), _ptr(idx), _dt(vals.dtype), T, f, n, m, _ptr(w2), d, _ptr(y),
                              _dt(y.dtype), _stream(vals.device)), "nm_ffn_down")
     return y
 

@@ -473,8 +473,8 @@ int ffn_up_relu_nm(const void *x, const void *w1t, const float *b1, int32_t in_d
 }
 
 int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, int32_t d_ff, int32_t n,
-                int32_t m, const void *w2t, int32_t d_model, void *y, int32_t y_dtype, void *stream) {
-  if (!w2t || (T > 0 && (!vals || !idx || !y))) return TWELL_ERR_ARG;
+                int32_t m, const void *w2, int32_t d_model, void *y, int32_t y_dtype, void *stream) {
+  if (!w2 || (T > 0 && (!vals || !idx || !y))) return TWELL_ERR_ARG;
   if (!dtype_ok(dtype) || !dtype_ok(y_dtype)) return TWELL_ERR_ARG;
   if (T < 0 || d_ff <= 0 || d_model <= 0) return TWELL_ERR_SHAPE;
   if (!((n == 8 && m == 16) || (n == 16 && m == 32))) {
@@ -482,10 +482,10 @@ int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, 
     return TWELL_ERR_SHAPE;
   }
   if (dtype != TWELL_BF16) return TWELL_ERR_UNSUPPORTED;
-  if (d_ff % 32) return TWELL_ERR_SHAPE;
-  if (!al16(vals) || !al16(idx) || !al16(w2t) || !al16(y)) return TWELL_ERR_ALIGN;
-  if ((size_t)d_model * d_ff * 2 >= ((size_t)1 << 31)) return TWELL_ERR_UNSUPPORTED;
-  TW_TRY(launch_nm_down(vals, idx, T, d_ff, n, m, w2t, d_model, y, y_dtype == TWELL_BF16, S(stream)));
+  if (d_ff % 32 || d_model % 8) return TWELL_ERR_SHAPE;
+  if (!al16(vals) || !al16(idx) || !al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
+  if ((size_t)d_model * d_ff * 2 >= ((size_t)1 << 31) || d_ff >= (1 << 23)) return TWELL_ERR_UNSUPPORTED;
+  TW_TRY(launch_nm_down(vals, idx, T, d_ff, n, m, w2, d_model, y, y_dtype == TWELL_BF16, S(stream)));
   return TWELL_OK;
 }
 

@@ -105,7 +105,7 @@ hipError_t launch_gated_fused(const TwellIn &h, const void *x, const void *wg, c
 // nm.hip
 hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, void *vals, uint8_t *idx,
                            hipStream_t s);
-hipError_t launch_nm_down(const void *vals, const uint8_t *idx, int T, int f, int n, int m, const void *w2t, int d,
+hipError_t launch_nm_down(const void *vals, const uint8_t *idx, int T, int f, int n, int m, const void *w2, int d,
                           void *y, int y_bf16, hipStream_t s);
 
 // down.hip

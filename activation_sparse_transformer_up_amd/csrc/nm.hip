@@ -186,205 +186,234 @@ hipError_t launch_nm_prune(const void *h, int bf16, int T, int f, int n, int m, 
 }
 
 // ------------------------------------------------------------------- nm_ffn_down
-// y[t][c] = sum_k H[t][k] w2t[c][k] with H expanded from (vals, idx) per 32-column stage.
+// y[t][c] = sum_k H[t][k] w2[k][c] with H expanded from (vals, idx) per 32-column stage and
+// w2 [d_ff][d_model] (the down weight as the TwELL path reads it, so one copy serves both).
 // Tile 256 tokens x 256 output columns, 8 waves of 64 x 128 (two per SIMD, so one wave's
-// expansion and loads overlap the other's MFMAs), v_mfma_f32_16x16x32_bf16, a ring of four
-// stages of 64-byte rows (A: 256 expanded H rows, B: 256 w2t rows), read as in the up GEMM
-// (16-row fragments, XOR-swizzled 16-byte chunks).
-//  - B arrives by buffer_load ... lds three stages ahead of its use.
+// expansion and stores overlap the other's MFMAs), v_mfma_f32_16x16x32_bf16, a ring of four
+// LDS stages, each A: 256 expanded H rows of 64 bytes (16-row fragments read with 16-byte
+// loads from XOR-swizzled chunks, as in the up GEMM) and B: 32 rows of w2, 512 bytes each.
+//  - B: the MFMA wants 8 consecutive k of one column per lane, while w2 rows run along the
+//    columns, so its fragments are read with gfx950's transposing LDS load
+//    (ds_read_b64_tr_b16): in each 16-lane group, lane a + 4 e points at row k0 + e, columns
+//    4 a .. 4 a + 3, and lane i receives the four values of column i at rows k0 .. k0 + 3;
+//    two such loads give 8 k. Row k's 16-byte chunk j sits at chunk j ^ (key(k) << 1),
+//    key(k) = (k & 3) | ((k >> 3) & 3) << 2: the 16 rows one load touches (k = 8 q + e or
+//    8 q + 4 + e, q, e < 4) get distinct even chunk offsets, so its 32 chunks fall on
+//    distinct bank groups.
+//    B travels through registers (two 16-byte buffer loads per thread and stage, then
+//    16-byte LDS stores), not by buffer_load ... lds: the compiler cannot tell a transposing
+//    read from a write of a pending LDS DMA and would wait for every DMA in flight before
+//    each such read, which stalls the ring on the load just issued.
 //  - A: tile row r is built by the neighbouring lanes 2r and 2r + 1. A stage of a row holds
 //    32 N / M = 16 kept entries (8:16 and 16:32): each lane loads 8 values and 8 indices
-//    (16 + 8 bytes), clears its 32-byte half of the row, then writes its values at their
-//    columns, which may lie in either half. The two lanes are in one wave, whose LDS writes
-//    execute in issue order, so both clears precede every value.
-// Step kt: wait for stage kt + 1, barrier; load the packed A of stage kt + 3; the MFMAs of
-// stage kt with the fragment reads of stage kt + 1 and the B loads of stage kt + 3 between
-// them; then build the A of stage kt + 3. Stage kt + 3 reuses the buffer of stage kt - 1,
-// whose fragments were read in step kt - 2. (With 4 waves of 128 x 128 and the packed A
-// loaded a step earlier the kernel took 0.56 / 0.57 ms at c4 instead of 0.48 / 0.49 ms.)
+//    (16 + 8 bytes; rows past T load as zeros through the buffer's range check), clears its
+//    32-byte half of the row, then stores its values at their columns (which for 16:32 may
+//    lie in either half). The two lanes are in one wave, whose LDS writes execute in issue
+//    order, so both clears precede every value. The LDS byte of column c in row r is
+//    2 (c ^ 8 swz(r)), swz(r) = (r >> 2) & 3, so each index byte becomes a byte offset with
+//    one XOR and one shift per 4 indices, and a value's store address with one add.
+//    These value stores are the kernel's largest cost beyond the GEMM itself (about 40 %
+//    of its time at 4096 x 14336 x 4096): each takes one entry of 32 rows, and since the
+//    t-th kept column of every row lies near column 2 t, the lanes of rows in one 16-bank
+//    group meet in a bank (3.6 at a time on average). Stores of 4 or 8 rows with 16 or 8
+//    lanes per row meet 1 or 2 at a time, but need 2- and 4-byte loads per entry (4 to 8
+//    times the load instructions and twice the registers) or a pass through LDS; measured,
+//    each of those was slower.
+// Step kt: barrier (stage kt + 1 is in LDS, nobody reads stage kt - 1 any more); the A and
+// B loads of stage kt + 3 into registers; the MFMAs of stage kt in B-fragment order, each
+// B fragment reloaded with stage kt + 1 once its four MFMAs are issued, the A fragments of
+// stage kt + 1 read early into the other A set; then stage kt + 3's A is built and its B
+// stored into the buffer of stage kt - 1.
 // Patterns: 8:16 and 16:32 (d_ff a multiple of 32).
-// One thread's half of a row's packed stage: 8 values (bf16) and 8 indices (u8).
-struct NmPack {
-  uint4 v;
-  uint2 ix;
-};
+typedef short v4s_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) v4s_t lds_v4s_t;
+typedef unsigned u32x2_t __attribute__((ext_vector_type(2)));
+
+TW_DEV int nm_b_key(int k) { return (k & 3) | (((k >> 3) & 3) << 2); }
 
 template <int N, int M>
 __global__ __launch_bounds__(512) void k_nm_down(const uint16_t *__restrict__ vals, const uint8_t *__restrict__ idx,
-                                                 int T, int f, const uint16_t *__restrict__ w2t, int d,
+                                                 int T, int f, const uint16_t *__restrict__ w2, int d,
                                                  void *__restrict__ y, int y_bf16) {
   static_assert(32 % M == 0 && 32 / M * N == 16, "16 kept entries per 32 columns");
-  constexpr int BM = 256, BN = 256, RB = 64, NS = 4, STAGE = (BM + BN) * RB;
-  constexpr int WM = 64, WN = 128, FM = WM / 16, FN = WN / 16;
-  constexpr int NM = FM * FN, NR = FM + FN;
-  constexpr int LPW = BN / 16 / 8;               // B wave-loads per wave per stage
-  constexpr int LA = 2;                          // packed-A loads per thread per stage
+  constexpr int BM = 256, BN = 256, RB = 64, NS = 4;
+  constexpr int ASZ = BM * RB, BSZ = 32 * BN * 2, STAGE = ASZ + BSZ;
+  constexpr int WM = 64, WN = 128, FM = WM / 16, FN = WN / 16, NM = FM * FN;
   __shared__ __attribute__((aligned(16))) char smem[NS * STAGE];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int wm = wave >> 1, wn = wave & 1;
   const int n0 = blockIdx.x * BN, m0 = blockIdx.y * BM;
   const int nk = f / 32;
-  const size_t E = (size_t)f / M * N;            // kept entries per row
-
-  // B: stage rows of w2t through LDS DMA (16-row blocks q = wave + 8 i of the B half)
-  constexpr uint32_t OOB = 0x80000000u;
-  const size_t row_bytes = (size_t)f * 2;
-  const __amdgpu_buffer_rsrc_t rb =
-      __builtin_amdgcn_make_buffer_rsrc((void *)w2t, (short)0, (int)((size_t)d * row_bytes), 0x00020000);
-  const int lrow = lane >> 2, cl = (lane & 3) ^ ((lrow >> 2) & 3);
-  uint32_t voff[LPW];
-#pragma unroll
-  for (int i = 0; i < LPW; ++i) {
-    const int gr = n0 + (wave + 8 * i) * 16 + lrow;
-    voff[i] = gr < d ? (uint32_t)((size_t)gr * row_bytes) + cl * 16 : OOB;
-  }
-  auto issue_b = [&](int kt, int i) {
-    char *st = smem + (kt % NS) * STAGE + BM * RB;
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rb, (lds_void_t *)(st + (wave + 8 * i) * 1024), 16, voff[i], kt * 64,
-                                             0, 0);
-  };
-  // A: tile row tid / 2, whose 16 kept entries per stage this thread shares with its
-  // neighbour lane: half hf = tid % 2 takes entries 8 hf .. 8 hf + 7 (rows past T read row
-  // T - 1 and are built as zeros)
-  const int arow = tid >> 1, hf = tid & 1;
-  const bool trow = m0 + arow < T;
-  const size_t prow = (size_t)min(m0 + arow, T - 1) * E;
-  const uint4 *pv = (const uint4 *)(vals + prow);
-  const uint2 *pi = (const uint2 *)(idx + prow);
-  auto load_a = [&](int kt, NmPack &p) {
-    p.v = pv[2 * kt + hf];
-    p.ix = pi[2 * kt + hf];
-  };
-  // The stores are inline assembly: the compiler cannot tell them apart from the B ring's
-  // pending LDS DMA and would wait for all of it (vmcnt(0)) before each build. They write
-  // the A half of stage kt, which no DMA targets; the LDS wait before every barrier covers
-  // them.
   const uint32_t lds0 = (uint32_t)(uintptr_t)(lds_char_t *)smem;
+
+  // B: thread load i in {0, 1} of a stage is wave-load q = wave + 8 i, rows 2 q and 2 q + 1
+  // of the stage; lane l stores LDS chunk l % 32 of row 2 q + l / 32, which holds the row's
+  // global chunk (l % 32) ^ (key << 1). Columns past d read as zeros (range check).
+  constexpr uint32_t OOB = 0x80000000u;
+  const uint32_t wrow = (uint32_t)d * 2;
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void *)w2, (short)0, (int)((size_t)f * wrow), 0x00020000);
+  uint32_t gb[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k = 2 * (wave + 8 * i) + (lane >> 5);
+    const int col = n0 + 8 * ((lane & 31) ^ (nm_b_key(k) << 1));
+    gb[i] = col < d ? (uint32_t)k * wrow + (uint32_t)col * 2 : OOB;
+  }
+  typedef u32x4_t PB[2];
+  auto load_b = [&](int kt, PB &p) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) p[i] = __builtin_amdgcn_raw_buffer_load_b128(rb, gb[i], kt * 32 * (int)wrow, 0);
+  };
+  auto store_b = [&](int kt, const PB &p) {
+    const uint32_t base = lds0 + (uint32_t)((kt % NS) * STAGE + ASZ) + (uint32_t)lane * 16;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      asm volatile("ds_write_b128 %0, %1" ::"v"(base + (uint32_t)(wave + 8 * i) * 1024), "v"(p[i]));
+  };
+
+  // A: tile row tid / 2; half hf = tid % 2 takes entries 8 hf .. 8 hf + 7 of each stage.
+  const int arow = tid >> 1, hf = tid & 1;
+  const uint32_t E = (uint32_t)f / M * N;                 // kept entries per row
+  const uint32_t nrows = (uint32_t)min(BM, T - m0);
+  const __amdgpu_buffer_rsrc_t rv = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(vals + (size_t)m0 * E), (short)0, (int)(nrows * E * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ri = __builtin_amdgcn_make_buffer_rsrc(
+      (void *)(idx + (size_t)m0 * E), (short)0, (int)(nrows * E), 0x00020000);
+  const uint32_t gv = (uint32_t)arow * E * 2 + 16u * hf, gi = (uint32_t)arow * E + 8u * hf;
+  struct PA {
+    u32x4_t v;
+    u32x2_t ix;
+  };
+  auto load_a = [&](int kt, PA &p) {
+    p.v = __builtin_amdgcn_raw_buffer_load_b128(rv, gv, kt * 32, 0);
+    p.ix = __builtin_amdgcn_raw_buffer_load_b64(ri, gi, kt * 16, 0);
+  };
+  // column c of the row sits at byte 2 (c ^ 8 swz): for 8:16 the half's columns are 16 hf +
+  // idx, for 16:32 they are idx
   const int swz = (arow >> 2) & 3;
-  auto a_row = [&](int kt) { return lds0 + (uint32_t)((kt % NS) * STAGE + arow * RB); };
-  // each thread clears its 32-byte half of the row, then writes its 8 entries anywhere in the
-  // row: the two halves' threads are neighbouring lanes of one wave, whose LDS writes execute
-  // in issue order, so both clears precede every entry write
-  auto build_zero = [&](uint32_t row) {
+  const uint32_t xw = (M == 16 ? 8u * (uint32_t)(swz & 1) : 8u * (uint32_t)swz) * 0x01010101u;
+  const uint32_t hb = M == 16 ? 32u * (uint32_t)(hf ^ (swz >> 1)) : 0u;
+  constexpr uint32_t IM = (uint32_t)(M - 1) * 0x01010101u;
+  // The stores are inline assembly so that they stay in issue order after the clears; the
+  // LDS wait before every barrier covers them.
+  auto build_a = [&](int kt, const PA &p) {
+    const uint32_t row = lds0 + (uint32_t)((kt % NS) * STAGE + arow * RB);
     const u32x4_t z = {0u, 0u, 0u, 0u};
     const uint32_t h = row + 32u * (uint32_t)hf;
     asm volatile("ds_write_b128 %0, %1\n\tds_write_b128 %0, %1 offset:16" ::"v"(h), "v"(z));
-  };
-  auto build_entry = [&](uint32_t row, const NmPack &p, int e) {     // entry 8 hf + e of the stage
-    const uint32_t iw = e < 4 ? p.ix.x : p.ix.y;
-    const uint32_t vw = e < 2 ? p.v.x : e < 4 ? p.v.y : e < 6 ? p.v.z : p.v.w;
-    const int ee = 8 * hf + e;
-    const int col = (ee / N) * M + (int)((iw >> (8 * (e % 4))) & (M - 1));
-    const uint32_t v = trow ? (vw >> (16 * (e & 1))) & 0xFFFFu : 0u;
-    const uint32_t a = row + (uint32_t)((((col >> 3) ^ swz) << 4) + (col & 7) * 2);
-    asm volatile("ds_write_b16 %0, %1" ::"v"(a), "v"(v));
-  };
-  auto build_a = [&](int kt, const NmPack &p) {
-    const uint32_t row = a_row(kt);
-    build_zero(row);
+    const uint32_t base = row + hb;
+    const uint32_t w0 = ((p.ix.x & IM) ^ xw) << 1, w1 = ((p.ix.y & IM) ^ xw) << 1;
 #pragma unroll
-    for (int e = 0; e < 8; ++e) build_entry(row, p, e);
+    for (int e = 0; e < 8; ++e) {
+      const uint32_t w = e < 4 ? w0 : w1;
+      const uint32_t a = base + ((w >> (8 * (e & 3))) & 0xFFu);
+      const uint32_t v = p.v[e >> 1];
+      if (e & 1) asm volatile("ds_write_b16_d16_hi %0, %1" ::"v"(a), "v"(v));
+      else asm volatile("ds_write_b16 %0, %1" ::"v"(a), "v"(v));
+    }
   };
-  // fragments (as in the up GEMM's 16 x 16 x 32 loop)
+
+  // fragments
   typedef u32x4_t FA[FM];
   typedef u32x4_t FB[FN];
   const int l16 = lane & 15, c4 = lane >> 4;
-  auto read1 = [&](int kt, int j, FA &a, FB &b) {
-    const char *sa = smem + (kt % NS) * STAGE;
-    if (j < FM) {
-      const int r = wm * WM + j * 16 + l16;
-      a[j] = *(const u32x4_t *)(sa + r * RB + ((c4 ^ ((r >> 2) & 3)) << 4));
-    } else {
-      const int r = wn * WN + (j - FM) * 16 + l16;
-      b[j - FM] = *(const u32x4_t *)(sa + BM * RB + r * RB + ((c4 ^ ((r >> 2) & 3)) << 4));
-    }
+  auto read_a = [&](int kt, int j, FA &a) {
+    const int r = wm * WM + j * 16 + l16;
+    a[j] = *(const u32x4_t *)(smem + (kt % NS) * STAGE + r * RB + ((c4 ^ ((r >> 2) & 3)) << 4));
+  };
+  // transposing B reads: lane l (group q = l / 16, source lane s = l % 16: a = s % 4,
+  // e = s / 4) points at row 8 q + 4 half + e, columns 16 fn' + 4 a of the tile, fn' = wn *
+  // 8 + fn, i.e. chunk 2 fn' + (a >> 1) at its swizzled place, byte (a & 1) * 8
+  const int tq = lane >> 4, ta = lane & 3, te = (lane >> 2) & 3;
+  uint32_t boff[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh) {
+    const int k = 8 * tq + 4 * hh + te;
+    boff[hh] = (uint32_t)(k * 512 + (((ta >> 1) ^ (nm_b_key(k) << 1)) << 4) + (ta & 1) * 8);
+  }
+  auto read_b = [&](int kt, int fn, FB &b) {
+    // the stage offset sits above bit 13 and the fragment's chunk bits in bits 5 .. 8, so
+    // XORing after the add equals adding after the XOR; XORing last keeps the address tied
+    // to the stage, so it is formed at the read instead of held in a register per fragment
+    const uint32_t so = (uint32_t)((kt % NS) * STAGE + ASZ);
+    const uint32_t cx = (uint32_t)(2 * (wn * FN + fn)) << 4;
+    const v4s_t lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t *)(smem + ((so + boff[0]) ^ cx)));
+    const v4s_t hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_v4s_t *)(smem + ((so + boff[1]) ^ cx)));
+    const uint2 l2 = __builtin_bit_cast(uint2, lo), h2 = __builtin_bit_cast(uint2, hi);
+    b[fn] = u32x4_t{l2.x, l2.y, h2.x, h2.y};
   };
   f32x4_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
 #pragma unroll
     for (int j = 0; j < FN; ++j) acc[i][j] = f32x4_t{};
-  auto mma = [&](int i, const FA &a, const FB &b) {
-    acc[i / FN][i % FN] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[i / FN]),
-                                                                  __builtin_bit_cast(bf16x8_t, b[i % FN]),
-                                                                  acc[i / FN][i % FN], 0, 0, 0);
+  auto mma = [&](int fm, int fn, const FA &a, const FB &b) {
+    acc[fm][fn] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[fm]),
+                                                          __builtin_bit_cast(bf16x8_t, b[fn]), acc[fm][fn], 0, 0, 0);
   };
-  // prologue: stages 0 .. 2 built and loaded
-  NmPack pa;
+
+  // prologue: stages 0 .. 2 built and stored, stage 0's fragments read
+  {
+    PA pa[NS - 1];
+    PB pb[NS - 1];
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk) {
-      load_a(st, pa);
-      build_a(st, pa);
-    }
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < nk) {
+        load_a(st, pa[st]);
+        load_b(st, pb[st]);
+      }
 #pragma unroll
-  for (int st = 0; st < NS - 1; ++st)
-    if (st < nk)
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) issue_b(st, i);
-  wait_vmcnt<0>();
+    for (int st = 0; st < NS - 1; ++st)
+      if (st < nk) {
+        build_a(st, pa[st]);
+        store_b(st, pb[st]);
+      }
+  }
   block_barrier_lds();
   FA a0, a1;
-  FB b0, b1;
+  FB b;
 #pragma unroll
-  for (int j = 0; j < NR; ++j) read1(0, j, a0, b0);
+  for (int j = 0; j < FM; ++j) read_a(0, j, a0);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) read_b(0, j, b);
 
-  constexpr int RI = NM / NR;                    // a fragment read after every RI MFMAs
-  constexpr int DI = NM / LPW;                   // a B load after every DI MFMAs
-  // A step of the steady state (kt + 3 < nk): the packed loads of stage kt + 3, then (between
-  // the MFMAs of stage kt, with the fragment reads of stage kt + 1) the B loads of stage
-  // kt + 3; after the MFMAs the A of stage kt + 3 is built from those packed registers, whose
-  // loads are the ones issued before the LPW B loads. At the start of step kt the loads issued
-  // after stage kt + 1's B are step kt - 1's (LA + LPW). Stage kt + 3 reuses the buffer of
-  // stage kt - 1, whose fragments were read in step kt - 2.
-  auto step = [&](int kt, const FA &ac, const FB &bc, FA &an, FB &bn) {
-    wait_vmcnt<LA + LPW>();
+  // One step. LOAD: stage kt + 3 exists; NEXT: stage kt + 1 exists.
+  PA pa;
+  PB pb;
+  auto step = [&](int kt, const FA &ac, FA &an, bool load, bool next) {
     block_barrier_lds();
-    load_a(kt + 3, pa);
-    __builtin_amdgcn_sched_barrier(0);
-    static_for<NM>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      mma(i, ac, bc);
-      if constexpr (i % RI == 0 && i / RI < NR) read1(kt + 1, i / RI, an, bn);
-      if constexpr (i % DI == DI - 1) issue_b(kt + 3, i / DI);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    wait_vmcnt<LPW>();
-    build_a(kt + 3, pa);
-    __builtin_amdgcn_sched_barrier(0);
-  };
-  // The last steps (kt + 3 >= nk for the second of a pair or later): what exists is issued,
-  // waits are complete ones, and the next fragment set is copied into the current one.
-  auto tail_step = [&](int kt) {
-    wait_vmcnt<0>();
-    block_barrier_lds();
-    if (kt + 3 < nk) load_a(kt + 3, pa);
-    static_for<NM>([&](auto I) {
-      constexpr int i = decltype(I)::value;
-      mma(i, a0, b0);
-      if constexpr (i % RI == 0 && i / RI < NR) read1(kt + 1, i / RI, a1, b1);
-      __builtin_amdgcn_sched_barrier(0);
-    });
-    if (kt + 3 < nk) {
-#pragma unroll
-      for (int i = 0; i < LPW; ++i) issue_b(kt + 3, i);
-      build_a(kt + 3, pa);
+    if (load) {
+      load_a(kt + 3, pa);
+      load_b(kt + 3, pb);
     }
-    wait_vmcnt<0>();
-#pragma unroll
-    for (int j = 0; j < FM; ++j) a0[j] = a1[j];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) b0[j] = b1[j];
+    __builtin_amdgcn_sched_barrier(0);
+    static_for<NM>([&](auto I) {
+      constexpr int i = decltype(I)::value, fn = i / FM, fm = i % FM;
+      mma(fm, fn, ac, b);
+      if (next) {
+        if constexpr (fm == FM - 1) read_b(kt + 1, fn, b);
+        if constexpr (i % 2 == 0 && i / 2 < FM) read_a(kt + 1, i / 2, an);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+    });
+    if (load) {
+      build_a(kt + 3, pa);
+      store_b(kt + 3, pb);
+    }
+    __builtin_amdgcn_sched_barrier(0);
   };
   int kt = 0;
   for (; kt + 4 < nk; kt += 2) {
-    step(kt, a0, b0, a1, b1);
-    step(kt + 1, a1, b1, a0, b0);
+    step(kt, a0, a1, true, true);
+    step(kt + 1, a1, a0, true, true);
   }
-  for (; kt + 1 < nk; ++kt) tail_step(kt);
+  for (; kt < nk; ++kt) {
+    step(kt, a0, a1, kt + 3 < nk, kt + 1 < nk);
 #pragma unroll
-  for (int i = 0; i < NM; ++i) mma(i, a0, b0);
+    for (int j = 0; j < FM; ++j) a0[j] = a1[j];
+  }
 
   // epilogue: y[row][col], register r of block (fm, fn): row 16 fm + 4 (lane / 16) + r,
   // column 16 fn + lane % 16
@@ -405,11 +434,11 @@ __global__ __launch_bounds__(512) void k_nm_down(const uint16_t *__restrict__ va
   }
 }
 
-hipError_t launch_nm_down(const void *vals, const uint8_t *idx, int T, int f, int n, int m, const void *w2t, int d,
+hipError_t launch_nm_down(const void *vals, const uint8_t *idx, int T, int f, int n, int m, const void *w2, int d,
                           void *y, int y_bf16, hipStream_t s) {
   if (T == 0) return hipSuccess;
   const dim3 grid((d + 255) / 256, (T + 255) / 256);
-  const uint16_t *v = (const uint16_t *)vals, *w = (const uint16_t *)w2t;
+  const uint16_t *v = (const uint16_t *)vals, *w = (const uint16_t *)w2;
   if (n == 8 && m == 16) hipLaunchKernelGGL((k_nm_down<8, 16>), grid, dim3(512), 0, s, v, idx, T, f, w, d, y, y_bf16);
   else hipLaunchKernelGGL((k_nm_down<16, 32>), grid, dim3(512), 0, s, v, idx, T, f, w, d, y, y_bf16);
   return hipGetLastError();

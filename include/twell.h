@@ -348,12 +348,16 @@ int ffn_up_relu_nm(const void *x, const void *w1t, const float *b1, int32_t in_d
  * nm_ffn_down — y = H_nm . W2 for N:M-packed activations (vals, idx from nm_prune, bf16).
  * gfx950's sparse matrix instructions take only a 2:4 structure (at most two nonzeros in
  * every four consecutive entries), which 8:16 and 16:32 blocks do not have, so each block is
- * expanded to dense bf16 in LDS and multiplied on MFMA; only the activation bytes shrink. The down weight is given as
- * w2t [d_model][d_ff] (nn.Linear(d_ff, d_model).weight), the K-contiguous layout the MFMA
- * operand loads want. y: [T][d_model], y_dtype fp32 or bf16.
+ * expanded to dense bf16 in LDS and multiplied on MFMA; only the activation bytes shrink.
+ * w2: [d_ff][d_model] bf16, row-major, the same down weight twell_down and twell_ffn_fwd
+ * take, so one copy serves the TwELL and the N:M paths. y: [T][d_model], y_dtype fp32 or
+ * bf16. (n, m) in (8,16), (16,32) (2:4 and 4:8 give TWELL_ERR_UNSUPPORTED); d_ff % 32 == 0
+ * and d_model % 8 == 0, else TWELL_ERR_SHAPE; vals, idx, w2, y 16-byte aligned; w2 under
+ * 2 GiB and d_ff < 2^23 (256 rows of packed values under 2 GiB), else
+ * TWELL_ERR_UNSUPPORTED.
  */
 int nm_ffn_down(const void *vals, const uint8_t *idx, int32_t dtype, int32_t T, int32_t d_ff,
-                int32_t n, int32_t m, const void *w2t, int32_t d_model, void *y,
+                int32_t n, int32_t m, const void *w2, int32_t d_model, void *y,
                 int32_t y_dtype, void *stream);
 
 /*

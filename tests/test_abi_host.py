@@ -199,3 +199,27 @@ def test_up_nm_rejects():
     assert up_nm(idx=MIS) == ALIGN
     assert up_nm(b1=MIS + 2) == ALIGN
     assert up_nm(T=0, vals=None, idx=None) == 0   # nothing to do, nothing touched
+
+
+@pytestmark_nogpu
+def test_nm_down_rejects():
+    L = tw.lib()
+
+    def down(**kw):
+        # nm_ffn_down(vals, idx, dtype, T, d_ff, n, m, w2 [d_ff][d_model], d_model, y, y_dtype, stream)
+        a = dict(vals=FAKE, idx=FAKE, dt=1, T=64, f=512, n=8, m=16, w2=FAKE, d=256, y=FAKE, ydt=0)
+        a.update(kw)
+        return L.nm_ffn_down(a["vals"], a["idx"], a["dt"], a["T"], a["f"], a["n"], a["m"], a["w2"], a["d"],
+                             a["y"], a["ydt"], None)
+    assert down(w2=None) == ARG
+    assert down(vals=None) == ARG
+    assert down(ydt=5) == ARG
+    assert down(n=2, m=4) == UNSUP
+    assert down(n=3) == SHAPE
+    assert down(dt=0) == UNSUP                    # fp32 values
+    assert down(f=528) == SHAPE                   # d_ff not a multiple of 32
+    assert down(d=260) == SHAPE                   # d_model not a multiple of 8
+    assert down(w2=MIS) == ALIGN
+    assert down(y=MIS) == ALIGN
+    assert down(f=1 << 20, d=1024) == UNSUP       # w2 of 2 GiB
+    assert down(f=1 << 23, d=8) == UNSUP          # 256 rows of packed values of 2 GiB

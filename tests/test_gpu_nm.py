@@ -114,15 +114,14 @@ def test_nm_prune_c4_full_bit_exact():
 
 
 @pytest.mark.parametrize("n,m", [(8, 16), (16, 32)])
-@pytest.mark.parametrize("T,d,f", [(64, 256, 512), (300, 320, 1024), (513, 512, 2048)])
+@pytest.mark.parametrize("T,d,f", [(64, 256, 512), (300, 320, 1024), (513, 512, 2048), (77, 264, 544)])
 def test_nm_down(n, m, T, d, f):
     say("nm_down", n, m, T, d, f)
     rng = np.random.default_rng(T + d)
     hb = synth.f32_to_bf16_bits(np.maximum(rng.standard_normal((T, f)), 0).astype(np.float32))
     w2 = synth.f32_to_bf16_bits((rng.standard_normal((f, d)) / np.sqrt(f)).astype(np.float32))
-    w2t = np.ascontiguousarray(w2.T)
     vals, idx = tw.nm_prune(to_dev(hb, "bf16"), n, m)
-    y = tw.nm_ffn_down(vals, idx, n, m, to_dev(w2t, "bf16"))
+    y = tw.nm_ffn_down(vals, idx, n, m, to_dev(w2, "bf16"))
     torch.cuda.synchronize()
     hv, hi = orc.nm_prune(orc.widen(hb, "bf16"), n, m)
     ref = orc.nm_unpack(hv, hi, m) @ orc.widen(w2, "bf16")
@@ -137,7 +136,7 @@ def test_nm_down_integer_grid_exact():
     hb = synth.f32_to_bf16_bits(h.astype(np.float32))
     w2b = synth.f32_to_bf16_bits(w2.astype(np.float32))
     vals, idx = tw.nm_prune(to_dev(hb, "bf16"), 8, 16)
-    y = tw.nm_ffn_down(vals, idx, 8, 16, to_dev(np.ascontiguousarray(w2b.T), "bf16"))
+    y = tw.nm_ffn_down(vals, idx, 8, 16, to_dev(w2b, "bf16"))
     torch.cuda.synchronize()
     hv, hi = orc.nm_prune(h, 8, 16)
     assert np.array_equal(from_dev(y), orc.nm_unpack(hv, hi, 16) @ w2)
@@ -151,8 +150,11 @@ def test_nm_rejects():
         tw.nm_prune(h[:, :60].contiguous(), 8, 16)
     v, i = tw.nm_prune(h, 2, 4)
     with pytest.raises(tw.TwellError) as e:
-        tw.nm_ffn_down(v, i, 2, 4, torch.zeros((16, 64), dtype=torch.bfloat16, device="cuda"))
+        tw.nm_ffn_down(v, i, 2, 4, torch.zeros((64, 16), dtype=torch.bfloat16, device="cuda"))
     assert e.value.status == -7
+    v, i = tw.nm_prune(h, 8, 16)
+    with pytest.raises(tw.TwellError):  # d_model not a multiple of 8
+        tw.nm_ffn_down(v, i, 8, 16, torch.zeros((64, 12), dtype=torch.bfloat16, device="cuda"))
 
 
 def test_nm_down_c4_full_sampled():
@@ -165,13 +167,12 @@ def test_nm_down_c4_full_sampled():
     g = synth.generate(w)
     x, w1t, w2 = (to_dev(g[k], "bf16") for k in ("x", "w1t", "w2"))
     b1 = to_dev(g["b1"], "f32")
-    w2t = w2.t().contiguous()
     rows = np.sort(np.random.default_rng(11).choice(w.T, 16, replace=False))
     rt = torch.from_numpy(rows).cuda()
     w2r = orc.widen(g["w2"], "bf16")
     for n, m in w.nm:
         vals, idx = tw.ffn_up_relu_nm(x, w1t, b1, n, m)
-        y = tw.nm_ffn_down(vals, idx, n, m, w2t)
+        y = tw.nm_ffn_down(vals, idx, n, m, w2)
         torch.cuda.synchronize()
         ref = orc.nm_unpack(from_dev(vals[rt]), from_dev(idx[rt]), m) @ w2r
         err = rel_err(from_dev(y[rt]), ref)
