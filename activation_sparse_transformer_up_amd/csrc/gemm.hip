@@ -536,6 +536,14 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
   const int JI = 16 * RS + lane;
   const uint32_t below = (1u << li) - 1u;
   const bool vec_ok = (S * (int)sizeof(VT)) % 16 == 0;
+  // copy-out positions: the lane's first (row, 16-byte chunk) and the step between its
+  // chunks i and i + 64, divided once here (the chunk counts per row are runtime values)
+  const int relem = tiles * S;
+  const int ci = relem / 4, cv = relem * (int)sizeof(VT) / 16;   // 16-byte chunks per row
+  const int ri0 = vec_ok ? lane / ci : 0, ci0 = vec_ok ? lane - ri0 * ci : 0;
+  const int rq = vec_ok ? 64 / ci : 0, rm = vec_ok ? 64 - rq * ci : 0;
+  const int rv0 = vec_ok ? lane / cv : 0, cv0 = vec_ok ? lane - rv0 * cv : 0;
+  const int vq = vec_ok ? 64 / cv : 0, vm = vec_ok ? 64 - vq * cv : 0;
   uint32_t ovfv[TPW];                            // overflow bits of this lane's rows, 32-row word
 #pragma unroll
   for (int fm = 0; fm < G::FM; ++fm) {
@@ -576,19 +584,27 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
     }
     wave_lds_order();
     const int nrow = min(16, M - rb0);
-    const int relem = tiles * S;
     if (vec_ok) {
-      const int ci = relem / 4, cv = relem * (int)sizeof(VT) / 16;
-      for (int i = lane; i < nrow * ci; i += 64) {
-        const int rr = i / ci, c = i - rr * ci;
+      for (int i = lane, rr = ri0, c = ci0; i < nrow * ci; i += 64) {
         const size_t gi = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
         st_nt16(o.col_idx + gi + 4 * c, lidx + rr * RS + 4 * c);
+        rr += rq;
+        c += rm;
+        if (c >= ci) {
+          c -= ci;
+          ++rr;
+        }
       }
       constexpr int EV = 16 / sizeof(VT);
-      for (int i = lane; i < nrow * cv; i += 64) {
-        const int rr = i / cv, c = i - rr * cv;
+      for (int i = lane, rr = rv0, c = cv0; i < nrow * cv; i += 64) {
         const size_t gi = ((size_t)(rb0 + rr) * o.n_t + kt0) * S;
         st_nt16((VT *)o.vals + gi + EV * c, lval + rr * RS + EV * c);
+        rr += vq;
+        c += vm;
+        if (c >= cv) {
+          c -= cv;
+          ++rr;
+        }
       }
     } else {
       for (int i = lane; i < nrow * relem; i += 64) {
@@ -598,9 +614,13 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
         ((VT *)o.vals)[gi] = lval[rr * RS + c];
       }
     }
-    for (int i = lane; i < nrow * tiles; i += 64) {
-      const int rr = i / tiles, c = i - rr * tiles;
-      o.counts[(size_t)(rb0 + rr) * o.n_t + kt0 + c] = lcnt[rr * TPW + c];
+    if constexpr (TPW == 1) {
+      if (lane < nrow) o.counts[(size_t)(rb0 + lane) * o.n_t + kt0] = lcnt[lane];
+    } else {
+      for (int i = lane; i < nrow * tiles; i += 64) {
+        const int rr = i / tiles, c = i - rr * tiles;
+        o.counts[(size_t)(rb0 + rr) * o.n_t + kt0 + c] = lcnt[rr * TPW + c];
+      }
     }
     // after the second 16-row block of a 32-row word (or the last block inside the matrix)
     const bool last = fm == G::FM - 1 || rb0 + 16 >= M;
