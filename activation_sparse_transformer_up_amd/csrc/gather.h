@@ -12,14 +12,17 @@
 // and all sixteen row loads are issued before the FMAs; the next round's pairs are loaded
 // meanwhile. Accumulation is fp32 in list order.
 #pragma once
+#include <type_traits>
+
 #include "common.h"
 
 namespace tw {
 
-// Lane J of this lane's 16-lane row (DPP row broadcast).
+// Lane J of this lane's 16-lane row (DPP row broadcast). Every lane's source exists, so no
+// "old" value is needed (bound_ctrl), and the compiler emits no move before the broadcast.
 template <int J> TW_DEV uint32_t row_bcast(uint32_t v) {
   static_assert(J >= 0 && J < 16, "row lane");
-  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x150 + J, 0xF, 0xF, false);
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, 0x150 + J, 0xF, 0xF, true);
 }
 
 // acc[0..E) += v * the E elements in the 16 bytes raw (bf16 widened exactly to fp32).
@@ -49,26 +52,44 @@ template <typename WT>
 TW_DEV float gather_list16(const uint2 *__restrict__ p, int n, int nw, const WT *__restrict__ M, int d, int col,
                            bool cv, float (&acc)[Vec16<WT>::N]) {
   constexpr int E = Vec16<WT>::N;
+  constexpr uint32_t OOB = 0x80000000u;                      // beyond the range: reads zeros
   const int gl = lane_id() & 15;
   const __amdgpu_buffer_rsrc_t rs = rows_rsrc(M);            // row pieces by buffer loads
+  // byte offset of row i's piece: i * (row bytes) + this lane's column bytes, one 24-bit
+  // multiply-add (row indices and row bytes are below 2^24, the operand below 2 GiB)
+  const uint32_t rowb = (uint32_t)d * (uint32_t)sizeof(WT), colb = (uint32_t)col * (uint32_t)sizeof(WT);
   float vs = 0.f;
   uint2 pn = gl < n ? p[gl] : make_uint2(0, 0);
   for (int base = 0; base < nw; base += 16) {
     const uint2 q = pn;
     if (base + 16 < nw) pn = base + 16 + gl < n ? p[base + 16 + gl] : make_uint2(0, 0);
     vs += __uint_as_float(q.y);                 // zero for entries past n
-    uint4 raw[16];
-    float vv[16];
-    static_for<16>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      const uint32_t ij = row_bcast<j>(q.x), vj = row_bcast<j>(q.y);
-      const bool ok = base + j < n;
-      vv[j] = ok ? __uint_as_float(vj) : 0.f;
-      raw[j] = make_uint4(0, 0, 0, 0);
-      if (ok && cv) raw[j] = ld16<WT>(rs, ij * (uint32_t)d + (uint32_t)col);
-    });
-#pragma unroll
-    for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
+    // Entries up to the wave's longest list in this round (rem, wave-uniform) are issued
+    // without a per-lane branch: an entry past its own list (its pair, and so its value, is
+    // zero) or a column past the row reads zeros through the range check. Entries past rem
+    // are skipped by a scalar branch, loads and FMAs alike.
+    const int rem = nw - base;
+    auto round = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      uint4 raw[16];
+      float vv[16];
+      static_for<16>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if (!FULL && j >= rem) return;
+        const uint32_t ij = row_bcast<j>(q.x), vj = row_bcast<j>(q.y);
+        vv[j] = __uint_as_float(vj);
+        const uint32_t off = (base + j < n && cv) ? __umul24(ij, rowb) + colb : OOB;
+        const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+        raw[j] = make_uint4(v.x, v.y, v.z, v.w);
+      });
+      static_for<16>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if (!FULL && j >= rem) return;
+        fma16<WT, E>(acc, vv[j], raw[j]);
+      });
+    };
+    if (rem >= 16) round(std::true_type());
+    else round(std::false_type());
   }
   return vs;
 }
