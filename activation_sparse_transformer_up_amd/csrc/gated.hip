@@ -182,19 +182,38 @@ __global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk,
   const uint2 *lp = h.row_list + (size_t)tt * cap;
   float *out = part + ((size_t)c * h.rows + tt) * cap;
   int jn = gl < n ? (int)lp[gl].x : 0;
+  // as in gather_list16: one 24-bit multiply-add per row piece, loads issued without a
+  // per-lane branch (entries past the list and columns past the row read zeros through the
+  // range check), rounds bounded by the wave's longest list (scalar branch)
+  constexpr uint32_t OOB = 0x80000000u;
+  const uint32_t rowb = (uint32_t)d * (uint32_t)sizeof(XT), colb = (uint32_t)colo * (uint32_t)sizeof(XT);
   for (int base = 0; base < nw; base += 16) {
     const int jq = jn;
     if (base + 16 < nw) jn = base + 16 + gl < n ? (int)lp[base + 16 + gl].x : 0;
-    uint4 raw[16];
-    static_for<16>([&](auto J) {
-      constexpr int j = decltype(J)::value;
-      const uint32_t jj = row_bcast<j>((uint32_t)jq);
-      raw[j] = make_uint4(0, 0, 0, 0);
-      if (base + j < n && cv) raw[j] = ld16<XT>(rs, jj * (uint32_t)d + (uint32_t)colo);
-    });
+    const int rem = nw - base;
     float v[16];
-#pragma unroll
-    for (int j = 0; j < 16; ++j) v[j] = dot16<XT>(a, raw[j], 0.f);
+    auto round = [&](auto full_tag) {
+      constexpr bool FULL = decltype(full_tag)::value;
+      uint4 raw[16];
+      static_for<16>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if (!FULL && j >= rem) return;
+        const uint32_t jj = row_bcast<j>((uint32_t)jq);
+        const uint32_t off = (base + j < n && cv) ? __umul24(jj, rowb) + colb : OOB;
+        const u32x4_t r = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)off, 0, 0);
+        raw[j] = make_uint4(r.x, r.y, r.z, r.w);
+      });
+      static_for<16>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        if (!FULL && j >= rem) {
+          v[j] = 0.f;
+          return;
+        }
+        v[j] = dot16<XT>(a, raw[j], 0.f);
+      });
+    };
+    if (rem >= 16) round(std::true_type());
+    else round(std::false_type());
     const float tot = group16_transpose_sum(v, gl);
     if (base + gl < n) out[base + gl] = tot;
   }
