@@ -92,16 +92,31 @@ TwellOut out_of(const twell_matrix_t *m) {
   o.ovf_bits = m->ovf_bits;
   o.dec_part = nullptr;
   o.dec_ticket = nullptr;
+  o.dec_bytes = 0;
   if (m->row_list && m->rows <= kDecodeMaxT) {
     char *ws = (char *)m->row_list + align256(list_bytes(m->rows, m->cols, m->tile_w, m->slots));
     o.dec_part = (float *)ws;
     o.dec_ticket = (uint64_t *)(ws + dec_tiles(m->cols) * 2 * kDecHalfBytes);
+    o.dec_bytes = dec_tiles(m->cols) * 2 * kDecHalfBytes;
   }
   o.n_t = m->cols / m->tile_w;
   o.S = m->slots;
   o.words = (m->rows + 31) / 32;
   o.val_bf16 = m->val_dtype == TWELL_BF16;
   return o;
+}
+
+TwellFinish finish_of(twell_matrix_t *m, bool complete) {
+  TwellFinish f;
+  f.complete = complete;
+  f.row_nnz = m->row_nnz;
+  f.row_list = (uint2 *)m->row_list;
+  f.ovf_n = m->ovf_n;
+  f.ovf_rows = m->ovf_rows;
+  f.ovf_slot = m->ovf_slot;
+  f.ovf_dense = m->ovf_dense;
+  f.cap = m->ovf_cap;
+  return f;
 }
 
 TwellIn in_of(const twell_matrix_t *m) {
@@ -200,11 +215,20 @@ static int check_up_args(const void *x, const void *w1t, const float *b1, int32_
   return TWELL_OK;
 }
 
+// complete: let the GEMM stage also build the lists, the overflow scan and the backup rows
+// where it can do that itself (one or two tokens; see gemm_completes)
 static int up_gemm(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T, int32_t d_model,
-                   int32_t d_ff, twell_matrix_t *h, hipStream_t s) {
+                   int32_t d_ff, twell_matrix_t *h, hipStream_t s, bool complete = false) {
   if (T == 0) return TWELL_OK;
-  TW_TRY(launch_up_twell(in_dtype == TWELL_BF16, x, w1t, b1, T, d_ff, d_model, out_of(h), h->tile_w, s));
+  TW_TRY(launch_up_twell(in_dtype == TWELL_BF16, x, w1t, b1, T, d_ff, d_model, out_of(h), finish_of(h, complete),
+                         h->tile_w, s));
   return TWELL_OK;
+}
+
+// true if up_gemm(..., complete = true) completes the matrix (lists, overflow scan, backup
+// rows): then up_finish has nothing left to do
+static bool gemm_completes(int32_t in_dtype, int32_t T, int32_t d_model, twell_matrix_t *h) {
+  return T > 0 && up_twell_completes(in_dtype == TWELL_BF16, T, d_model, finish_of(h, true));
 }
 
 static int up_finish(const void *x, const void *w1t, const float *b1, int32_t in_dtype, int32_t T,
@@ -247,9 +271,9 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
   if (st) return st;
   if (!al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
   hipStream_t s = S(stream);
-  st = up_gemm(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);
+  st = up_gemm(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s, true);
   if (st) return st;
-  st = up_finish(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);
+  if (!gemm_completes(in_dtype, T, d_model, h)) st = up_finish(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);
   if (st || T == 0) return st;
   TW_TRY(launch_twell_down(in_of(h), w2, in_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, false, s));
   return TWELL_OK;
@@ -337,9 +361,9 @@ int twell_gated_ffn_fwd(const void *x, const void *w_gate_t, const float *b_gate
   st = gate_ws_check(h, in_dtype, d_model, workspace, workspace_bytes);
   if (st) return st;
   hipStream_t s = S(stream);
-  st = up_gemm(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h, s);
+  st = up_gemm(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h, s, true);
   if (st) return st;
-  st = up_finish(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h, s);
+  if (!gemm_completes(in_dtype, T, d_model, h)) st = up_finish(x, w_gate_t, b_gate, in_dtype, T, d_model, d_ff, h, s);
   if (st || T == 0) return st;
   TW_TRY(launch_gate_up(in_of(h), x, w_up_t, in_dtype == TWELL_BF16, d_model, (float *)workspace, s));
   TW_TRY(launch_twell_down(in_of(h), w2, in_dtype == TWELL_BF16, d_model, y, y_dtype == TWELL_BF16, false, s));

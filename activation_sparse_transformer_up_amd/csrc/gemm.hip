@@ -1005,7 +1005,7 @@ TW_DEV void row_add_lds(f32x16_t (&a)[TileD::NB], const float *red) {
     for (int r = 0; r < 16; ++r) a[nb][r] += red[(nb * 16 + r) * 64 + lane];
 }
 
-// Cross-workgroup hand-over of the half sums (k_up_twell_dec, k_up_gemv_twell). Every access
+// Cross-workgroup hand-over of the half sums (k_up_twell_dec). Every access
 // to the workspace is an atomic of agent scope: such accesses are coherent across the XCDs'
 // separate L2 caches on their own (stores write through, loads do not hit a stale line). The
 // half sum is stored, its stores are waited for (vmcnt(0)) and only then is the ticket taken,
@@ -1228,20 +1228,23 @@ __global__ __launch_bounds__(256) void k_up_nm_dec(const T *__restrict__ x, cons
 // ------------------------------------------------------------------ decode GEMV (T <= 2, bf16)
 // With a handful of tokens the up projection is a stream of W1 with a few dot products per
 // row. The tile kernels above fetch each W1 row in 64-byte pieces per stage; here every wave
-// load is one contiguous kilobyte of a row. Lane l holds the 16-byte pieces
+// load is one contiguous kilobyte of a row. A wave takes 16 units over one half of K; lane l
+// holds the 16-byte pieces
 //   k = k0 + 8 (64 p + l),  p = 0 .. np - 1   (np = K / 1024 per half of K)
-// of x (all tokens, in registers) and of the rows it streams. A 128-unit tile is summed in
-// two halves of K; a half runs on 8 waves of 16 units (4 rows in flight per lane). Each
-// (unit, token) partial is accumulated over the lane's pieces in order with v_dot2_f32_bf16,
-// then over the 64 lanes by a fixed xor butterfly whose lane-0 value is kept:
+// of x (all tokens, in registers) and of the rows it streams, four units at a time with three
+// (stream kernel) or two (dense kernel, whose waves have half the registers) groups of four
+// in flight. Each (unit, token) partial is accumulated over the lane's pieces
+// in order with v_dot2_f32_bf16, then the wave's 16 TT partials are summed over the 64 lanes
+// by one transposing butterfly (gemv_reduce):
 //   z = half_0 + half_1.
-// k_up_gemv_twell runs the halves on two workgroups that meet in the decode workspace (the
-// second to arrive adds the other half and packs the TwELL); k_up_gemv_dense runs both halves
-// one after the other in one workgroup (no workspace) and writes h densely or N:M-pruned.
-// fp32 addition is commutative, so all of them see the same z bit for bit.
-constexpr int kGemvMaxT = 2, kGemvNP = 4, kGemvUnits = 128, kGemvWaves = 8;
-constexpr int kGemvUPW = kGemvUnits / kGemvWaves;           // units per wave
-static_assert(kGemvMaxT * kGemvUnits * 4 <= (int)kDecHalfBytes, "decode workspace");
+// TwELL: k_up_gemv_z streams W1 on one-wave workgroups (every CU streams; no workgroup waits
+// for another) and stores the half sums in the decode workspace; k_gemv_finish, one
+// workgroup, packs the TwELL from them and completes the matrix (row lists, overflow scan,
+// dense backup rows). Dense and N:M: k_up_gemv_dense runs both halves of a 128-unit tile on
+// the 16 waves of one workgroup and adds them in LDS. fp32 addition is commutative, so all of
+// them see the same z bit for bit.
+constexpr int kGemvMaxT = 2, kGemvNP = 4, kGemvUnits = 128;
+constexpr int kGemvUPW = 16;                                // units per wave
 
 typedef __bf16 bf16x2g_t __attribute__((ext_vector_type(2)));
 TW_DEV float dot8_bf16(uint4 a, uint4 b, float c) {
@@ -1252,167 +1255,344 @@ TW_DEV float dot8_bf16(uint4 a, uint4 b, float c) {
   return c;
 }
 
-// Half `half` of K for the 16 units of wave wv of the tile at n0: zs[u * TT + t] (u < 128,
-// t < TT) for token slot t = x row (arow ? arow[t] : t), t < rows (others are zero).
-template <int TT>
-TW_DEV void gemv_half(const uint16_t *__restrict__ x, const int32_t *__restrict__ arow, int rows,
-                      const uint16_t *__restrict__ w1t, int N, int K, int n0, int half, int wv, float *zs) {
-  const int lane = threadIdx.x & 63;
-  const int np = K / 1024;
-  const size_t k0 = (size_t)half * (K / 2) + 8 * lane;
-  // addresses are clamped into the operands (row 0, piece 0) before the predicate is applied,
-  // so no load can leave them whatever the compiler hoists
-  uint4 xr[TT][kGemvNP];
+constexpr int ilog2(int v) { return v <= 1 ? 0 : 1 + ilog2(v / 2); }
+
+// Sum over the 64 lanes of each of the V values v[j] (V a power of two, at most 64). Step s
+// (m = 32 >> s) halves the set: a lane keeps the upper half of its values if bit m of its
+// lane index is set, else the lower half, and adds the partner's (lane ^ m) copy of that
+// half. After log2 V steps a lane holds one value, index gemv_value_index<V>(lane); the lanes
+// that hold the same index then add their partials by an xor butterfly over the low bits, so
+// every lane ends with its index's complete sum (identical bits in all of them: each addition
+// is commutative). V - 1 + log2(64 / V) exchanges instead of 6 per value.
+template <int V> TW_DEV float gemv_reduce(float (&v)[V]) {
+  constexpr int LV = ilog2(V);
+  static_assert((1 << LV) == V && V <= 64, "power of two");
+  const int lane = lane_id();
+  static_for<LV>([&](auto S) {
+    constexpr int st = decltype(S)::value, m = 32 >> st, half = V >> (st + 1);
+    const bool hi = lane & m;
+    static_for<half>([&](auto J) {
+      constexpr int k = decltype(J)::value;
+      const float keep = hi ? v[k + half] : v[k];
+      const float send = hi ? v[k] : v[k + half];
+      v[k] = keep + __shfl_xor(send, m, 64);
+    });
+  });
+  float r = v[0];
+#pragma unroll
+  for (int m = 32 >> LV; m > 0; m >>= 1) r += __shfl_xor(r, m, 64);
+  return r;
+}
+
+template <int V> TW_DEV int gemv_value_index(int lane) {
+  constexpr int LV = ilog2(V);
+  int j = 0;
+#pragma unroll
+  for (int st = 0; st < LV; ++st) j += ((lane >> (5 - st)) & 1) * (V >> (st + 1));
+  return j;
+}
+
+// One wave: units u0 .. u0 + 15 (rows at or beyond N read as zero) over half kh of K (NP =
+// K / 1024 pieces per lane), token slots t < TT (x row arow[t] if arow, else t; slots at or
+// beyond rows are zero). Returns the sum of value gemv_value_index<16 TT>(lane) = unit * TT +
+// slot (complete in every lane). Unit addresses are clamped into the operand (row 0) before
+// the predicate is applied, so no load can leave it whatever the compiler hoists.
+template <int TT, int NP, int NG>
+TW_DEV float gemv_wave(const uint16_t *__restrict__ x, const int32_t *__restrict__ arow, int rows,
+                       const uint16_t *__restrict__ w1t, int N, int K, int u0, int kh) {
+  const int lane = lane_id();
+  const size_t k0 = (size_t)kh * (K / 2) + 8 * lane;
+  uint4 xr[TT][NP];
 #pragma unroll
   for (int t = 0; t < TT; ++t) {
     const int tr = t < rows ? t : 0;
     const uint16_t *xp = x + (size_t)(arow ? arow[tr] : tr) * K + k0;
 #pragma unroll
-    for (int p = 0; p < kGemvNP; ++p) {
-      xr[t][p] = make_uint4(0, 0, 0, 0);
-      if (p < np) {
-        const uint4 v = *(const uint4 *)(xp + 512 * p);
-        if (t < rows) xr[t][p] = v;
-      }
+    for (int p = 0; p < NP; ++p) {
+      const uint4 v = *(const uint4 *)(xp + 512 * p);
+      xr[t][p] = t < rows ? v : make_uint4(0, 0, 0, 0);
     }
   }
-  // four groups of four units; the next group's rows are loaded before the current group is
-  // reduced (two groups in flight)
   const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w1t);
-  auto load = [&](int g, uint4 (&wr)[4][kGemvNP]) {
+  auto load = [&](int g, uint4 (&wr)[4][NP]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int u = n0 + wv * kGemvUPW + 4 * g + i;
-      const uint16_t *wp = w1t + (size_t)(u < N ? u : 0) * K + k0;
+      const int u = u0 + 4 * g + i;
+      const uint32_t wo = (uint32_t)((size_t)(u < N ? u : 0) * K + k0);
 #pragma unroll
-      for (int p = 0; p < kGemvNP; ++p) {
-        wr[i][p] = make_uint4(0, 0, 0, 0);
-        if (p < np) {
-          const uint4 v = ld16<uint16_t>(rw, (uint32_t)(wp - w1t) + 512u * p);
-          if (u < N) wr[i][p] = v;
-        }
+      for (int p = 0; p < NP; ++p) {
+        const uint4 v = ld16<uint16_t>(rw, wo + 512u * p);
+        wr[i][p] = u < N ? v : make_uint4(0, 0, 0, 0);
       }
     }
   };
-  auto reduce = [&](int g, const uint4 (&wr)[4][kGemvNP]) {
+  float part[16 * TT];
+  auto dot = [&](int g, const uint4 (&wr)[4][NP]) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int t = 0; t < TT; ++t) {
-        float s = 0.f;
+        float acc = 0.f;
 #pragma unroll
-        for (int p = 0; p < kGemvNP; ++p) s = dot8_bf16(xr[t][p], wr[i][p], s);
-#pragma unroll
-        for (int o = 32; o > 0; o >>= 1) s += __shfl_xor(s, o, 64);
-        if (lane == 0) zs[(wv * kGemvUPW + 4 * g + i) * TT + t] = s;
+        for (int p = 0; p < NP; ++p) acc = dot8_bf16(xr[t][p], wr[i][p], acc);
+        part[(4 * g + i) * TT + t] = acc;
       }
   };
-  static_assert(kGemvUPW == 16, "four groups of four units");
-  uint4 wa[4][kGemvNP], wb[4][kGemvNP];
-  load(0, wa);
-  load(1, wb);
-  reduce(0, wa);
-  load(2, wa);
-  reduce(1, wb);
-  load(3, wb);
-  reduce(2, wa);
-  reduce(3, wb);
+  static_assert(kGemvUPW == 16 && (NG == 2 || NG == 3), "four groups of four units, two or three in flight");
+  uint4 wa[4][NP], wb[4][NP];
+  if constexpr (NG == 3) {
+    uint4 wc[4][NP];
+    load(0, wa);
+    load(1, wb);
+    load(2, wc);
+    dot(0, wa);
+    load(3, wa);
+    dot(1, wb);
+    dot(2, wc);
+    dot(3, wa);
+  } else {
+    load(0, wa);
+    load(1, wb);
+    dot(0, wa);
+    load(2, wa);
+    dot(1, wb);
+    load(3, wb);
+    dot(2, wa);
+    dot(3, wb);
+  }
+  return gemv_reduce<16 * TT>(part);
 }
 
-// TwELL of the token rows t < M for the tile's units from z (LDS zs[u * TT + t]); wave t packs
-// token t. W = 128: lane l holds units 2l, 2l + 1 (one TwELL tile); W = 64: units l and 64 + l
-// (two tiles). Slot order is ascending column (ballot prefix), pads (-1, +0.0), true counts,
-// and the tile's overflow word (rows < 32) is assembled in LDS.
-template <int TT, int W, typename VT>
-TW_DEV void gemv_twell_epi(const float *zs, const float *__restrict__ b1, int M, int N, int n0, const TwellOut &o,
-                           uint32_t *ovf_flag) {
-  constexpr int Q = 128 / W;                                  // TwELL tiles of the workgroup
-  const int tid = threadIdx.x, lane = tid & 63, t = tid >> 6;
-  const int S = o.S;
-  if (t < M) {
+// Grid: 2 * ceil(N / 16) one-wave workgroups; workgroup b takes units 16 (b % nb) .. + 15 and
+// half b / nb of K, and stores its sums to zp[half][t][u] (fp32). With n_rows_dev the token
+// count is min(M, *n_rows_dev) (nothing to do at zero). ticket (optional): the decode
+// tickets of the matrix, unused on this path; like every call, it leaves them zero (plain
+// stores: they are next read by a later launch).
+template <int TT, int NP>
+__global__ __launch_bounds__(64) void k_up_gemv_z(const uint16_t *__restrict__ x, const int32_t *__restrict__ arow,
+                                                  const int32_t *__restrict__ n_rows_dev, int M,
+                                                  const uint16_t *__restrict__ w1t, int N, int K,
+                                                  float *__restrict__ zp, uint64_t *__restrict__ ticket) {
+  if (ticket && threadIdx.x == 0 && blockIdx.x < (N + kGemvUnits - 1) / kGemvUnits) ticket[blockIdx.x] = 0;
+  int rows = M;
+  if (n_rows_dev) rows = min(rows, *n_rows_dev);
+  if (rows <= 0) return;
+  const int nb = (N + kGemvUPW - 1) / kGemvUPW;
+  const int ub = blockIdx.x % nb, kh = blockIdx.x / nb;
+  const float z = gemv_wave<TT, NP, 3>(x, arow, rows, w1t, N, K, ub * kGemvUPW, kh);
+  const int lane = lane_id(), j = gemv_value_index<16 * TT>(lane);
+  const int u = ub * kGemvUPW + j / TT, t = j % TT;
+  if (lane % (64 / (16 * TT)) == 0 && u < N) zp[((size_t)kh * TT + t) * N + u] = z;
+}
+
+// TwELL of one tile kt (a wave; lane l holds units V l .. V l + V - 1 of it, V = W / 64) for
+// the TT token rows from z and nb = -b1 of those units: unit u is active iff z > nb, value
+// z - nb (the tile epilogues' arithmetic); a ballot per unit position, the count, the slots
+// in ascending column order (the first S active units), pads (-1, +0), the counts and the
+// tile's overflow word (rows < 32). Returns min(count, S) of row t in cnt[t];
+// stored(t, slot, col, v) sees every stored slot.
+template <int TT, int W, typename VT, class F>
+TW_DEV void gemv_pack_tile(const float (&z)[TT][W / 64], const float (&nb)[W / 64], int kt, const TwellOut &o,
+                           int (&cnt)[TT], bool (&ovf)[TT], F &&stored) {
+  constexpr int V = W / 64;
+  const int lane = lane_id(), S = o.S, n_t = o.n_t;
+  uint32_t word = 0;
 #pragma unroll
-    for (int q = 0; q < Q; ++q) {
-      const int kt = n0 / W + q;
-      if (kt >= o.n_t) break;
-      constexpr int V = W / 64;                               // units per lane in this tile
-      int u[V];
-      bool on[V];
-      float v[V];
-      uint64_t m[V];
-      int cnt = 0, before = 0;
+  for (int t = 0; t < TT; ++t) {
+    bool on[V];
+    uint64_t m[V];
+    int c = 0, before = 0;
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        u[e] = q * W + V * lane + e;
-        const int col = n0 + u[e];
-        const float nb = col < N ? -b1[col] : 0.f;
-        const float z = zs[u[e] * TT + t];
-        on[e] = col < N && z > nb;
-        v[e] = z - nb;
-        m[e] = ballot64(on[e]);
-        cnt += __popcll(m[e]);
-        before += mbcnt64(m[e]);
-      }
-      const size_t base = ((size_t)t * o.n_t + kt) * (size_t)S;
-      int slot = before;
+    for (int e = 0; e < V; ++e) {
+      on[e] = z[t][e] > nb[e];
+      m[e] = ballot64(on[e]);
+      c += __popcll(m[e]);
+      before += mbcnt64(m[e]);
+    }
+    const size_t base = ((size_t)t * n_t + kt) * S;
+    int slot = before;
 #pragma unroll
-      for (int e = 0; e < V; ++e) {
-        if (on[e]) {
-          if (slot < S) {
-            o.col_idx[base + slot] = n0 + u[e];
-            Elem<VT>::store((VT *)o.vals, base + slot, v[e]);
-          }
-          ++slot;
+    for (int e = 0; e < V; ++e) {
+      if (on[e]) {
+        if (slot < S) {
+          const int col = kt * W + V * lane + e;
+          const float v = z[t][e] - nb[e];
+          o.col_idx[base + slot] = col;
+          Elem<VT>::store((VT *)o.vals, base + slot, v);
+          stored(t, slot, col, v);
         }
-      }
-      for (int s2 = min(cnt, S) + lane; s2 < S; s2 += 64) {
-        o.col_idx[base + s2] = -1;
-        Elem<VT>::store((VT *)o.vals, base + s2, 0.f);
-      }
-      if (lane == 0) {
-        o.counts[(size_t)t * o.n_t + kt] = cnt;
-        ovf_flag[q * kGemvMaxT + t] = cnt > S ? 1u : 0u;
+        ++slot;
       }
     }
+    for (int s2 = min(c, S) + lane; s2 < S; s2 += 64) {
+      o.col_idx[base + s2] = -1;
+      Elem<VT>::store((VT *)o.vals, base + s2, 0.f);
+    }
+    word |= (c > S ? 1u : 0u) << t;
+    if (lane == 0) o.counts[(size_t)t * n_t + kt] = c;
+    cnt[t] = min(c, S);
+    ovf[t] = c > S;
   }
-  __syncthreads();
-  if (tid < Q && n0 / W + tid < o.n_t) {
-    uint32_t word = 0;
-    for (int r = 0; r < M; ++r) word |= ovf_flag[tid * kGemvMaxT + r] << r;
-    o.ovf_bits[(size_t)(n0 / W + tid) * o.words] = word;
-  }
+  if (lane == 0) o.ovf_bits[(size_t)kt * o.words] = word;
 }
 
-// Grid: 2 * ceil(N / 128) workgroups of 512 threads; workgroup b takes tile b % n_tiles and
-// half b / n_tiles of K. Workspace as k_up_twell_dec (o.dec_part, o.dec_ticket; see dec_meet).
+// The TwELL alone (no lists, scan or backup rows), one tile per wave: grid ceil(n_t / 16)
+// workgroups of 1024 threads.
 template <int TT, int W, typename VT>
-__global__ __launch_bounds__(512) void k_up_gemv_twell(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w1t,
-                                                       const float *__restrict__ b1, int M, int N, int K, TwellOut o) {
-  __shared__ float zs[kGemvUnits * TT];
-  __shared__ uint32_t flag[2 * kGemvMaxT];
-  __shared__ int last;
-  const int n_tiles = (N + kGemvUnits - 1) / kGemvUnits;
-  const int tile = blockIdx.x % n_tiles, half = blockIdx.x / n_tiles;
-  const int n0 = tile * kGemvUnits, tid = threadIdx.x;
-  gemv_half<TT>(x, nullptr, M, w1t, N, K, n0, half, tid >> 6, zs);
-  __syncthreads();
-  float *part = o.dec_part + (size_t)tile * 2 * kDecTileF;
-  for (int i = tid; i < kGemvUnits * TT; i += 512)
-    __hip_atomic_store(part + half * kDecTileF + i, zs[i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  wait_vmcnt<0>();
-  __syncthreads();                       // every half-sum store of this workgroup has completed
-  if (tid == 0) last = dec_meet(o.dec_ticket + tile, half);
-  __syncthreads();
-  if (!last) return;
-  for (int i = tid; i < kGemvUnits * TT; i += 512)
-    zs[i] += __hip_atomic_load(part + (1 - half) * kDecTileF + i, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  __syncthreads();
-  gemv_twell_epi<TT, W, VT>(zs, b1, M, N, n0, o, flag);
+__global__ __launch_bounds__(1024) void k_gemv_pack(const float *__restrict__ zp, const float *__restrict__ b1, int N,
+                                                    TwellOut o) {
+  constexpr int V = W / 64;
+  const int kt = blockIdx.x * 16 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (kt >= o.n_t) return;
+  float z[TT][V], nb[V];
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    const int u = kt * W + V * lane + e;
+    nb[e] = -b1[u];
+#pragma unroll
+    for (int t = 0; t < TT; ++t) z[t][e] = zp[(size_t)t * N + u] + zp[((size_t)TT + t) * N + u];
+  }
+  int cnt[TT];
+  bool ovf[TT];
+  gemv_pack_tile<TT, W, VT>(z, nb, kt, o, cnt, ovf, [](int, int, int, float) {});
 }
 
-// Both halves in one workgroup of 512 threads, then (NK == 0) out[i][col] = ReLU(z + b1) in
-// fp32 or bf16 for token slots i < rows (x row arow[i] if arow), or (NK > 0) h rounded to bf16
-// and pruned NK:MM into vals / idx ([rows][N / MM][NK]).
-template <int TT, int NK, int MM>
+// One workgroup of 1024 threads completes the TwELL of the TT token rows from the half sums
+// zp (z = zp[0][t][u] + zp[1][t][u]; unit u is active iff z > -b1[u], value z - (-b1[u]),
+// the tile epilogues' arithmetic), in chunks of CH tiles (as many as the LDS stage holds):
+//  1. per tile (one wave) the TwELL of gemv_pack_tile; the stored slots also go to an LDS
+//     stage as (column, fp32 value bits). A wave takes up to kFinB / TT tiles at once with
+//     every load issued first: the loads are the cost of this kernel;
+//  2. with lists: the exclusive prefix over the chunk's tiles of min(count, S) per row (plus
+//     the carry of earlier chunks) gives each tile's list offset, and the staged slots are
+//     copied to the row lists (the compact lists of the finish kernels);
+// then the overflow scan of the rows (rank among overflow rows, below cap) and the dense
+// backup row ReLU(z + b1) of each overflow row with a slot, formed as k_up_gemv_dense forms
+// it (so it equals the recompute bit for bit). Barriers wait for LDS only: nothing written to
+// global memory here is read back by this kernel.
+constexpr int kFinB = 8;                                     // tiles per batch of a wave, times TT
+constexpr int kFinStage = 12288;                             // LDS stage entries (96 KB)
+constexpr int kFinMaxCH = 1024;
+
+template <int TT, int W, typename VT>
+__global__ __launch_bounds__(1024) void k_gemv_finish(const float *__restrict__ zp, const float *__restrict__ b1,
+                                                      int N, TwellOut o, TwellFinish f) {
+  constexpr int V = W / 64, B = kFinB / TT;
+  __shared__ uint2 stage[kFinStage];
+  __shared__ int off_s[TT][kFinMaxCH], st_s[TT][kFinMaxCH];
+  __shared__ int wsum[TT][16];
+  __shared__ int carry_s[TT], ovf_s[TT], slot_s[TT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int S = o.S, n_t = o.n_t;
+  const int CH = min(kFinMaxCH, kFinStage / (TT * S));
+  if (tid < TT) {
+    carry_s[tid] = 0;
+    ovf_s[tid] = 0;
+  }
+  block_barrier_lds();
+  const bool lists = f.row_nnz && f.row_list;
+  const size_t lstride = (size_t)n_t * S;
+  for (int c0 = 0; c0 < n_t; c0 += CH) {
+    const int nc = min(CH, n_t - c0);
+    for (int q0 = wave; q0 < nc; q0 += 16 * B) {
+      float z[B][TT][V], nb[B][V];
+#pragma unroll
+      for (int bq = 0; bq < B; ++bq) {
+        const int q = q0 + 16 * bq < nc ? q0 + 16 * bq : q0;   // a valid tile for every load
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          const int u = (c0 + q) * W + V * lane + e;
+          nb[bq][e] = -b1[u];
+#pragma unroll
+          for (int t = 0; t < TT; ++t) z[bq][t][e] = zp[(size_t)t * N + u] + zp[((size_t)TT + t) * N + u];
+        }
+      }
+#pragma unroll
+      for (int bq = 0; bq < B; ++bq) {
+        const int q = q0 + 16 * bq;
+        if (q >= nc) break;                                    // wave-uniform
+        int cnt[TT];
+        bool ovf[TT];
+        gemv_pack_tile<TT, W, VT>(z[bq], nb[bq], c0 + q, o, cnt, ovf, [&](int t, int slot, int col, float v) {
+          stage[(t * CH + q) * S + slot] = make_uint2((uint32_t)col, __float_as_uint(Elem<VT>::load_rounded(v)));
+        });
+        if (lane == 0)
+#pragma unroll
+          for (int t = 0; t < TT; ++t) {
+            off_s[t][q] = cnt[t];
+            st_s[t][q] = cnt[t];
+            if (ovf[t]) ovf_s[t] = 1;
+          }
+      }
+    }
+    block_barrier_lds();
+    if (lists) {
+#pragma unroll
+      for (int t = 0; t < TT; ++t) {
+        const int c = tid < nc ? off_s[t][tid] : 0;
+        int tot;
+        const int ex = wave_excl_scan(c, &tot);
+        if (lane == 0) wsum[t][wave] = tot;
+        block_barrier_lds();
+        int pre = carry_s[t], all = 0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          if (i < wave) pre += wsum[t][i];
+          all += wsum[t][i];
+        }
+        if (tid < nc) off_s[t][tid] = pre + ex;
+        block_barrier_lds();                   // every thread has read carry_s[t]
+        if (tid == 0) carry_s[t] += all;
+      }
+      block_barrier_lds();
+      // copy: lane l of a wave takes slot l % S of tile q (64 / S tiles per pass when S <= 32)
+      const int per = S <= 32 ? 64 / S : 1;
+      const int sl = lane % S, sub = lane / S;
+      for (int p0 = wave * per; p0 < nc * TT; p0 += 16 * per) {
+        const int p = p0 + sub;                                // (t, q) = (p / nc, p % nc)
+        if (sub < per && p < nc * TT) {
+          const int t = p / nc, q = p - t * nc;
+          if (sl < st_s[t][q]) f.row_list[(size_t)t * lstride + off_s[t][q] + sl] = stage[(t * CH + q) * S + sl];
+        }
+      }
+    }
+    block_barrier_lds();               // the stage and the offsets are free for the next chunk
+  }
+  if (tid == 0) {
+    int r = 0;
+    for (int t = 0; t < TT; ++t) {
+      int sl = -1;
+      if (ovf_s[t]) {
+        if (r < f.cap) {
+          sl = r;
+          f.ovf_rows[r] = t;
+        }
+        ++r;
+      }
+      slot_s[t] = sl;
+      f.ovf_slot[t] = sl;
+      if (lists) f.row_nnz[t] = carry_s[t];
+    }
+    *f.ovf_n = r;
+  }
+  block_barrier_lds();
+  for (int t = 0; t < TT; ++t) {
+    const int sl = slot_s[t];
+    if (sl < 0) continue;                      // uniform
+    VT *row = (VT *)f.ovf_dense + (size_t)sl * N;
+    for (int u = tid; u < N; u += 1024) {
+      float h = zp[(size_t)t * N + u] + zp[((size_t)TT + t) * N + u] + b1[u];
+      h = h > 0.f ? h : 0.f;
+      Elem<VT>::store(row, u, h);
+    }
+  }
+}
+
+// One 128-unit tile per workgroup of 512 threads: wave w takes units 16 w .. 16 w + 15 over
+// both halves of K in turn, then (NK == 0) out[i][col] = ReLU(z + b1) (or z + b1) in fp32 or
+// bf16 for token slots i < rows (x row arow[i] if arow), or (NK > 0) h rounded to bf16 and
+// pruned NK:MM into vals / idx ([rows][N / MM][NK]).
+template <int TT, int NP, int NK, int MM>
 __global__ __launch_bounds__(512) void k_up_gemv_dense(const uint16_t *__restrict__ x, const uint16_t *__restrict__ w1t,
                                                        const float *__restrict__ b1, int M, int N, int K,
                                                        const int32_t *__restrict__ arow,
@@ -1424,18 +1604,24 @@ __global__ __launch_bounds__(512) void k_up_gemv_dense(const uint16_t *__restric
   int rows = M;
   if (n_rows_dev) rows = min(rows, *n_rows_dev);
   if (rows <= 0) return;
-  gemv_half<TT>(x, arow, rows, w1t, N, K, n0, 0, tid >> 6, zs[0]);
-  gemv_half<TT>(x, arow, rows, w1t, N, K, n0, 1, tid >> 6, zs[1]);
+  const int w = tid >> 6, lane = tid & 63;
+  const int vi = kGemvUPW * TT * w + gemv_value_index<16 * TT>(lane);
+  const bool own = lane % (64 / (16 * TT)) == 0;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const float z = gemv_wave<TT, NP, 2>(x, arow, rows, w1t, N, K, n0 + kGemvUPW * w, kh);
+    if (own) zs[kh][vi] = z;
+  }
   __syncthreads();
   if constexpr (NK == 0) {
     for (int i = tid; i < kGemvUnits * TT; i += 512) {
       const int t = i / kGemvUnits, u = i % kGemvUnits, col = n0 + u;
       if (t >= rows || col >= N) continue;
-      float z = zs[0][u * TT + t] + zs[1][u * TT + t] + b1[col];
-      if (relu) z = z > 0.f ? z : 0.f;
+      float h = zs[0][u * TT + t] + zs[1][u * TT + t] + b1[col];
+      if (relu) h = h > 0.f ? h : 0.f;
       const size_t o = (size_t)t * N + col;
-      if (out_bf16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16(z);
-      else ((float *)out)[o] = z;
+      if (out_bf16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16(h);
+      else ((float *)out)[o] = h;
     }
   } else {
     constexpr int RS = kGemvUnits * 2 + 16;
@@ -1494,43 +1680,72 @@ static hipError_t launch_twell_dec(const T *x, const T *w1t, const float *b1, in
   return hipGetLastError();
 }
 
+template <int TT, int W, typename VT>
+static void launch_gemv_tail(const float *b1, int N, const TwellOut &o, const TwellFinish &f, hipStream_t s) {
+  if (f.complete)
+    hipLaunchKernelGGL((k_gemv_finish<TT, W, VT>), dim3(1), dim3(1024), 0, s, o.dec_part, b1, N, o, f);
+  else
+    hipLaunchKernelGGL((k_gemv_pack<TT, W, VT>), dim3((o.n_t + 15) / 16), dim3(1024), 0, s, o.dec_part, b1, N, o);
+}
+
 template <int TT>
 static hipError_t launch_gemv_twell_t(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
-                                      const TwellOut &o, int W, hipStream_t s) {
-  const dim3 grid(2 * ((N + kGemvUnits - 1) / kGemvUnits)), blk(512);
+                                      const TwellOut &o, const TwellFinish &f, int W, hipStream_t s) {
+  const dim3 grid(2 * ((N + kGemvUPW - 1) / kGemvUPW));
+  if (K == 1024) hipLaunchKernelGGL((k_up_gemv_z<TT, 1>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket);
+  else if (K == 2048) hipLaunchKernelGGL((k_up_gemv_z<TT, 2>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket);
+  else hipLaunchKernelGGL((k_up_gemv_z<TT, 4>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket);
   if (o.val_bf16) {
-    if (W == 64) hipLaunchKernelGGL((k_up_gemv_twell<TT, 64, uint16_t>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
-    else hipLaunchKernelGGL((k_up_gemv_twell<TT, 128, uint16_t>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
+    if (W == 64) launch_gemv_tail<TT, 64, uint16_t>(b1, N, o, f, s);
+    else launch_gemv_tail<TT, 128, uint16_t>(b1, N, o, f, s);
   } else {
-    if (W == 64) hipLaunchKernelGGL((k_up_gemv_twell<TT, 64, float>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
-    else hipLaunchKernelGGL((k_up_gemv_twell<TT, 128, float>), grid, blk, 0, s, x, w1t, b1, M, N, K, o);
+    if (W == 64) launch_gemv_tail<TT, 64, float>(b1, N, o, f, s);
+    else launch_gemv_tail<TT, 128, float>(b1, N, o, f, s);
   }
   return hipGetLastError();
+}
+
+template <int TT, int NK, int MM>
+static void launch_gemv_dense_tt(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
+                                 const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
+                                 uint8_t *idx, hipStream_t s) {
+  const dim3 grid((N + kGemvUnits - 1) / kGemvUnits), blk(512);
+  if (K == 1024)
+    hipLaunchKernelGGL((k_up_gemv_dense<TT, 1, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
+  else if (K == 2048)
+    hipLaunchKernelGGL((k_up_gemv_dense<TT, 2, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
+  else
+    hipLaunchKernelGGL((k_up_gemv_dense<TT, 4, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
 }
 
 template <int NK, int MM>
 static hipError_t launch_gemv_dense_t(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
                                       int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out,
                                       int out_bf16, int relu, uint8_t *idx, hipStream_t s) {
-  const dim3 grid((N + kGemvUnits - 1) / kGemvUnits), blk(512);
-  if (x_rows <= 1)
-    hipLaunchKernelGGL((k_up_gemv_dense<1, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
-                       out_bf16, relu, idx);
-  else
-    hipLaunchKernelGGL((k_up_gemv_dense<2, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
-                       out_bf16, relu, idx);
+  if (x_rows <= 1) launch_gemv_dense_tt<1, NK, MM>(x, w1t, b1, M, N, K, arow, n_rows_dev, out, out_bf16, relu, idx, s);
+  else launch_gemv_dense_tt<2, NK, MM>(x, w1t, b1, M, N, K, arow, n_rows_dev, out, out_bf16, relu, idx, s);
   return hipGetLastError();
 }
 
+bool up_twell_completes(int bf16, int M, int K, const TwellFinish &f) {
+  return f.complete && f.row_nnz && f.row_list && use_gemv(bf16, M, K);
+}
+
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N,
-                           int K, const TwellOut &o, int W, hipStream_t s) {
+                           int K, const TwellOut &o, const TwellFinish &f, int W, hipStream_t s) {
   if ((bf16 ? use_decode<uint16_t>(M, K) || use_gemv(bf16, M, K) : use_decode<float>(M, K)) &&
       (!o.dec_part || !o.dec_ticket))
     return hipErrorInvalidValue;
   if (use_gemv(bf16, M, K)) {
+    if ((f.complete && (!f.ovf_n || !f.ovf_slot || (f.cap > 0 && (!f.ovf_rows || !f.ovf_dense)))) ||
+        (size_t)2 * M * N * 4 > o.dec_bytes)
+      return hipErrorInvalidValue;
     const uint16_t *xb = (const uint16_t *)x, *wb = (const uint16_t *)w1t;
-    if (M <= 1) return launch_gemv_twell_t<1>(xb, wb, b1, M, N, K, o, W, s);
-    return launch_gemv_twell_t<2>(xb, wb, b1, M, N, K, o, W, s);
+    if (M <= 1) return launch_gemv_twell_t<1>(xb, wb, b1, M, N, K, o, f, W, s);
+    return launch_gemv_twell_t<2>(xb, wb, b1, M, N, K, o, f, W, s);
   }
   if (bf16 && use_decode<uint16_t>(M, K))
     return launch_twell_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);

@@ -25,7 +25,20 @@ struct TwellOut {
   uint32_t *ovf_bits;
   float *dec_part;        // decode workspace (rows <= kDecodeMaxT): [tiles][2][64 x 128] fp32
   uint64_t *dec_ticket;   // [tiles]
+  size_t dec_bytes;       // bytes of dec_part
   int n_t, S, words, val_bf16;
+};
+
+// The rest of a TwELL matrix, which the one- and two-token up projection completes when asked
+// (complete): row lists (when row_nnz and row_list are given), overflow scan and dense backup
+// rows [cap][cols].
+struct TwellFinish {
+  int32_t *row_nnz;
+  uint2 *row_list;
+  int32_t *ovf_n, *ovf_rows, *ovf_slot;
+  void *ovf_dense;
+  int cap;
+  bool complete;
 };
 
 // Read side of a TwELL consumer.
@@ -44,7 +57,10 @@ struct TwellIn {
 
 // gemm.hip
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
-                           const TwellOut &o, int W, hipStream_t s);
+                           const TwellOut &o, const TwellFinish &f, int W, hipStream_t s);
+// true if launch_up_twell of M tokens with f also completes the matrix (lists, overflow scan,
+// backup rows): the finish step has nothing left to do
+bool up_twell_completes(int bf16, int M, int K, const TwellFinish &f);
 hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
                            int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
                            hipStream_t s);

@@ -77,11 +77,13 @@ typedef enum {
  *                                   For R <= 64 it also holds the decode workspace of the
  *                                   up GEMM (after the lists): fp32 half sums of the K split
  *                                   and one 64-bit ticket per 128 columns. No part of
- *                                   row_list needs initialising: the two workgroups of a
- *                                   tile meet by swapping the ticket for their own tag
- *                                   constant, and any other previous value (an earlier
- *                                   call leaves zero) reads as "arrived first". Calls that
- *                                   overlap on one h race.
+ *                                   row_list needs initialising: from 3 rows on, the two
+ *                                   workgroups of a tile meet by swapping the ticket for
+ *                                   their own tag constant, and any other previous value
+ *                                   (an earlier call leaves zero) reads as "arrived first";
+ *                                   with 1 or 2 rows the half sums are added by a later
+ *                                   kernel of the same call. Calls that overlap on one h
+ *                                   race.
  *
  * A row overflows iff some tile of it holds more than `slots` nonzeros. A (row, tile)
  * keeps its first min(count, slots) nonzeros in ascending column order. "Nonzero" is
