@@ -1238,11 +1238,11 @@ __global__ __launch_bounds__(256) void k_up_nm_dec(const T *__restrict__ x, cons
 // by one transposing butterfly (gemv_reduce):
 //   z = half_0 + half_1.
 // TwELL: k_up_gemv_z streams W1 on one-wave workgroups (every CU streams; no workgroup waits
-// for another) and stores the half sums in the decode workspace; k_gemv_finish, one
-// workgroup, packs the TwELL from them and completes the matrix (row lists, overflow scan,
-// dense backup rows). Dense and N:M: k_up_gemv_dense runs both halves of a 128-unit tile on
-// the 16 waves of one workgroup and adds them in LDS. fp32 addition is commutative, so all of
-// them see the same z bit for bit.
+// for another) and stores the half sums in the decode workspace; k_dec_finish (one workgroup
+// per token row) packs the TwELL from them and completes the matrix (row lists, overflow
+// scan, dense backup rows), or k_dec_pack packs the TwELL alone. Dense and N:M:
+// k_up_gemv_dense runs both halves of a 128-unit tile on the 8 waves of one workgroup and
+// adds them in LDS. fp32 addition is commutative, so all of them see the same z bit for bit.
 constexpr int kGemvMaxT = 2, kGemvNP = 4, kGemvUnits = 128;
 constexpr int kGemvUPW = 16;                                // units per wave
 
@@ -1364,16 +1364,19 @@ TW_DEV float gemv_wave(const uint16_t *__restrict__ x, const int32_t *__restrict
 }
 
 // Grid: 2 * ceil(N / 16) one-wave workgroups; workgroup b takes units 16 (b % nb) .. + 15 and
-// half b / nb of K, and stores its sums to zp[half][t][u] (fp32). With n_rows_dev the token
+// half b / nb of K, and stores its sums to zp[half][t][u] (fp32, t < M). With n_rows_dev the token
 // count is min(M, *n_rows_dev) (nothing to do at zero). ticket (optional): the decode
 // tickets of the matrix, unused on this path; like every call, it leaves them zero (plain
-// stores: they are next read by a later launch).
+// stores: they are next read by a later launch). ovf_words (optional): the first word of each
+// of the n_words tiles' overflow bits (stride words), zeroed for k_dec_pack.
 template <int TT, int NP>
 __global__ __launch_bounds__(64) void k_up_gemv_z(const uint16_t *__restrict__ x, const int32_t *__restrict__ arow,
                                                   const int32_t *__restrict__ n_rows_dev, int M,
                                                   const uint16_t *__restrict__ w1t, int N, int K,
-                                                  float *__restrict__ zp, uint64_t *__restrict__ ticket) {
+                                                  float *__restrict__ zp, uint64_t *__restrict__ ticket,
+                                                  uint32_t *__restrict__ ovf_words, int n_words, int words) {
   if (ticket && threadIdx.x == 0 && blockIdx.x < (N + kGemvUnits - 1) / kGemvUnits) ticket[blockIdx.x] = 0;
+  if (ovf_words && threadIdx.x == 0 && blockIdx.x < n_words) ovf_words[(size_t)blockIdx.x * words] = 0;
   int rows = M;
   if (n_rows_dev) rows = min(rows, *n_rows_dev);
   if (rows <= 0) return;
@@ -1382,210 +1385,350 @@ __global__ __launch_bounds__(64) void k_up_gemv_z(const uint16_t *__restrict__ x
   const float z = gemv_wave<TT, NP, 3>(x, arow, rows, w1t, N, K, ub * kGemvUPW, kh);
   const int lane = lane_id(), j = gemv_value_index<16 * TT>(lane);
   const int u = ub * kGemvUPW + j / TT, t = j % TT;
-  if (lane % (64 / (16 * TT)) == 0 && u < N) zp[((size_t)kh * TT + t) * N + u] = z;
+  if (lane % (64 / (16 * TT)) == 0 && u < N && t < M) zp[((size_t)kh * M + t) * N + u] = z;
 }
 
-// TwELL of one tile kt (a wave; lane l holds units V l .. V l + V - 1 of it, V = W / 64) for
-// the TT token rows from z and nb = -b1 of those units: unit u is active iff z > nb, value
-// z - nb (the tile epilogues' arithmetic); a ballot per unit position, the count, the slots
-// in ascending column order (the first S active units), pads (-1, +0), the counts and the
-// tile's overflow word (rows < 32). Returns min(count, S) of row t in cnt[t];
-// stored(t, slot, col, v) sees every stored slot.
-template <int TT, int W, typename VT, class F>
-TW_DEV void gemv_pack_tile(const float (&z)[TT][W / 64], const float (&nb)[W / 64], int kt, const TwellOut &o,
-                           int (&cnt)[TT], bool (&ovf)[TT], F &&stored) {
+// ------------------------------------------------------------ decode stream, 3 to 16 tokens
+// From three tokens on, the dot products of the W1 stream go to the matrix cores: a wave
+// still owns 16 units over one half of K, now as the A operand of v_mfma_f32_16x16x32_bf16
+// loaded straight from memory (16 rows x 64 bytes per wave load, no LDS), with x^T as the B
+// operand (token slots 0-15). kMsD steps of 32 k are in flight. The output stays the half
+// sums zp[half][t][u] of the one- and two-token stream, so the same packing kernels follow.
+constexpr int kMsMaxT = 16, kMsD = 16;
+
+// Units u0 .. u0 + 15 over half kh of K for token slots t < rows <= 16 (x row arow[t] if arow,
+// else t). Lane l loads the 16-byte piece l / 16 of every 32-k step of W1 row u0 + l % 16 and
+// of x row l % 16; rows at or beyond N and slots at or beyond rows take an out-of-range
+// offset and read zeros. Returns lane l's accumulators z[u0 + 4 (l / 16) + i][slot l % 16],
+// i < 4, each the sum over the half's steps in order. K = 1024 NP.
+template <int NP>
+TW_DEV f32x4_t mstream_wave(const uint16_t *__restrict__ x, const int32_t *__restrict__ arow, int rows,
+                            const uint16_t *__restrict__ w1t, int N, int K, int u0, int kh) {
+  constexpr uint32_t OOB = 0x80000000u;
+  constexpr int NS = 16 * NP;                                  // steps of the half (K = 1024 NP)
+  const int lane = lane_id(), r = lane & 15, c = lane >> 4;
+  const uint32_t rowb = (uint32_t)K * 2u, half = (uint32_t)kh * (uint32_t)K;   // bytes
+  const int u = u0 + r;
+  const uint32_t wo = u < N ? (uint32_t)u * rowb + half + 16u * (uint32_t)c : OOB;
+  const uint32_t xo = r < rows ? (uint32_t)(arow ? arow[r] : r) * rowb + half + 16u * (uint32_t)c : OOB;
+  const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w1t), rx = rows_rsrc(x);
+  // straight-line steps (fully unrolled), so that each MFMA waits for its own step's loads only
+  u32x4_t a[kMsD], b[kMsD];
+  static_for<kMsD>([&](auto D) {
+    constexpr int d = decltype(D)::value;
+    a[d] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wo + 64u * d), 0, 0);
+    b[d] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo + 64u * d), 0, 0);
+  });
+  __builtin_amdgcn_sched_barrier(0);            // the scheduler keeps the kMsD steps in flight
+  f32x4_t acc = f32x4_t{};
+  static_for<NS>([&](auto J) {
+    constexpr int j = decltype(J)::value, d = j % kMsD;
+    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a[d]), __builtin_bit_cast(bf16x8_t, b[d]),
+                                                 acc, 0, 0, 0);
+    if constexpr (j + kMsD < NS) {
+      a[d] = __builtin_amdgcn_raw_buffer_load_b128(rw, (int)(wo + 64u * (j + kMsD)), 0, 0);
+      b[d] = __builtin_amdgcn_raw_buffer_load_b128(rx, (int)(xo + 64u * (j + kMsD)), 0, 0);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+  });
+  return acc;
+}
+
+// Grid: 2 * ceil(N / 16) one-wave workgroups, as k_up_gemv_z: zp[half][t][u] (fp32, t < M).
+template <int NP>
+__global__ __launch_bounds__(64) void k_up_mstream_z(const uint16_t *__restrict__ x, const int32_t *__restrict__ arow,
+                                                     const int32_t *__restrict__ n_rows_dev, int M,
+                                                     const uint16_t *__restrict__ w1t, int N, int K,
+                                                     float *__restrict__ zp, uint64_t *__restrict__ ticket,
+                                                     uint32_t *__restrict__ ovf_words, int n_words, int words) {
+  if (ticket && threadIdx.x == 0 && blockIdx.x < (N + kGemvUnits - 1) / kGemvUnits) ticket[blockIdx.x] = 0;
+  if (ovf_words && threadIdx.x == 0 && blockIdx.x < n_words) ovf_words[(size_t)blockIdx.x * words] = 0;
+  int rows = M;
+  if (n_rows_dev) rows = min(rows, *n_rows_dev);
+  if (rows <= 0) return;
+  const int nb = (N + kGemvUPW - 1) / kGemvUPW;
+  const int ub = blockIdx.x % nb, kh = blockIdx.x / nb;
+  const f32x4_t z = mstream_wave<NP>(x, arow, rows, w1t, N, K, ub * kGemvUPW, kh);
+  const int lane = lane_id(), t = lane & 15;
+  if (t < M)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int u = ub * kGemvUPW + 4 * (lane >> 4) + i;
+      if (u < N) zp[((size_t)kh * M + t) * N + u] = z[i];
+    }
+}
+
+// TwELL of row t of one tile kt (a wave; lane l holds units V l .. V l + V - 1 of it, V = W / 64)
+// from z and nb = -b1 of those units: unit u is active iff z > nb, value z - nb (the tile
+// epilogues' arithmetic); a ballot per unit position, the count, the slots in ascending column
+// order (the first S active units), pads (-1, +0) and the count. Returns min(count, S);
+// *ovf = count > S; stored(slot, col, v) sees every stored slot.
+template <int W, typename VT, class F>
+TW_DEV int gemv_pack_row(const float (&z)[W / 64], const float (&nb)[W / 64], int t, int kt, const TwellOut &o,
+                         bool *ovf, F &&stored) {
   constexpr int V = W / 64;
   const int lane = lane_id(), S = o.S, n_t = o.n_t;
-  uint32_t word = 0;
+  bool on[V];
+  uint64_t m[V];
+  int c = 0, before = 0;
 #pragma unroll
-  for (int t = 0; t < TT; ++t) {
-    bool on[V];
-    uint64_t m[V];
-    int c = 0, before = 0;
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      on[e] = z[t][e] > nb[e];
-      m[e] = ballot64(on[e]);
-      c += __popcll(m[e]);
-      before += mbcnt64(m[e]);
-    }
-    const size_t base = ((size_t)t * n_t + kt) * S;
-    int slot = before;
-#pragma unroll
-    for (int e = 0; e < V; ++e) {
-      if (on[e]) {
-        if (slot < S) {
-          const int col = kt * W + V * lane + e;
-          const float v = z[t][e] - nb[e];
-          o.col_idx[base + slot] = col;
-          Elem<VT>::store((VT *)o.vals, base + slot, v);
-          stored(t, slot, col, v);
-        }
-        ++slot;
-      }
-    }
-    for (int s2 = min(c, S) + lane; s2 < S; s2 += 64) {
-      o.col_idx[base + s2] = -1;
-      Elem<VT>::store((VT *)o.vals, base + s2, 0.f);
-    }
-    word |= (c > S ? 1u : 0u) << t;
-    if (lane == 0) o.counts[(size_t)t * n_t + kt] = c;
-    cnt[t] = min(c, S);
-    ovf[t] = c > S;
+  for (int e = 0; e < V; ++e) {
+    on[e] = z[e] > nb[e];
+    m[e] = ballot64(on[e]);
+    c += __popcll(m[e]);
+    before += mbcnt64(m[e]);
   }
-  if (lane == 0) o.ovf_bits[(size_t)kt * o.words] = word;
+  const size_t base = ((size_t)t * n_t + kt) * S;
+  int slot = before;
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    if (on[e]) {
+      if (slot < S) {
+        const int col = kt * W + V * lane + e;
+        const float v = z[e] - nb[e];
+        o.col_idx[base + slot] = col;
+        Elem<VT>::store((VT *)o.vals, base + slot, v);
+        stored(slot, col, v);
+      }
+      ++slot;
+    }
+  }
+  for (int s2 = min(c, S) + lane; s2 < S; s2 += 64) {
+    o.col_idx[base + s2] = -1;
+    Elem<VT>::store((VT *)o.vals, base + s2, 0.f);
+  }
+  if (lane == 0) o.counts[(size_t)t * n_t + kt] = c;
+  *ovf = c > S;
+  return min(c, S);
 }
 
-// The TwELL alone (no lists, scan or backup rows), one tile per wave: grid ceil(n_t / 16)
-// workgroups of 1024 threads.
-template <int TT, int W, typename VT>
-__global__ __launch_bounds__(1024) void k_gemv_pack(const float *__restrict__ zp, const float *__restrict__ b1, int N,
-                                                    TwellOut o) {
+// The TwELL alone (no lists, scan or backup rows) of M <= 16 rows from the half sums
+// zp[half][t][u] (z = zp[0] + zp[1]): one (tile, row) per wave, grid ceil(M n_t / 16)
+// workgroups of 1024 threads. A row-tile above S slots sets its bit in the tile's overflow word
+// (rows < 32) with an atomic OR; the stream kernel of the same call zeroed the words.
+template <int W, typename VT>
+__global__ __launch_bounds__(1024) void k_dec_pack(const float *__restrict__ zp, const float *__restrict__ b1, int M,
+                                                   int N, TwellOut o) {
   constexpr int V = W / 64;
-  const int kt = blockIdx.x * 16 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
-  if (kt >= o.n_t) return;
-  float z[TT][V], nb[V];
+  const int wg = blockIdx.x * 16 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (wg >= M * o.n_t) return;
+  const int kt = wg % o.n_t, t = wg / o.n_t;
+  float z[V], z1[V], nb[V];
 #pragma unroll
   for (int e = 0; e < V; ++e) {
     const int u = kt * W + V * lane + e;
-    nb[e] = -b1[u];
-#pragma unroll
-    for (int t = 0; t < TT; ++t) z[t][e] = zp[(size_t)t * N + u] + zp[((size_t)TT + t) * N + u];
+    nb[e] = b1[u];
+    z[e] = zp[(size_t)t * N + u];
+    z1[e] = zp[((size_t)M + t) * N + u];
   }
-  int cnt[TT];
-  bool ovf[TT];
-  gemv_pack_tile<TT, W, VT>(z, nb, kt, o, cnt, ovf, [](int, int, int, float) {});
+  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+  for (int e = 0; e < V; ++e) {
+    nb[e] = -nb[e];
+    z[e] += z1[e];
+  }
+  bool ovf;
+  gemv_pack_row<W, VT>(z, nb, t, kt, o, &ovf, [](int, int, float) {});
+  if (ovf && lane == 0)
+    __hip_atomic_fetch_or(o.ovf_bits + (size_t)kt * o.words, 1u << t, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
-// One workgroup of 1024 threads completes the TwELL of the TT token rows from the half sums
-// zp (z = zp[0][t][u] + zp[1][t][u]; unit u is active iff z > -b1[u], value z - (-b1[u]),
-// the tile epilogues' arithmetic), in chunks of CH tiles (as many as the LDS stage holds):
-//  1. per tile (one wave) the TwELL of gemv_pack_tile; the stored slots also go to an LDS
-//     stage as (column, fp32 value bits). A wave takes up to kFinB / TT tiles at once with
-//     every load issued first: the loads are the cost of this kernel;
-//  2. with lists: the exclusive prefix over the chunk's tiles of min(count, S) per row (plus
-//     the carry of earlier chunks) gives each tile's list offset, and the staged slots are
-//     copied to the row lists (the compact lists of the finish kernels);
-// then the overflow scan of the rows (rank among overflow rows, below cap) and the dense
-// backup row ReLU(z + b1) of each overflow row with a slot, formed as k_up_gemv_dense forms
-// it (so it equals the recompute bit for bit). Barriers wait for LDS only: nothing written to
-// global memory here is read back by this kernel.
-constexpr int kFinB = 8;                                     // tiles per batch of a wave, times TT
+// The whole matrix of M <= 16 rows from the half sums: workgroup t (1024 threads) takes row t,
+// in chunks of CH tiles (as many as the LDS stage holds):
+//  1. per tile (one wave, up to kFinB tiles at once with every load issued first: the loads
+//     are the cost) the TwELL of gemv_pack_row; the stored slots also go to an LDS stage as
+//     (column, fp32 value bits);
+//  2. with lists: the exclusive prefix over the chunk's tiles of min(count, S) (plus the carry
+//     of earlier chunks) gives each tile's list offset, and the staged slots are copied to the
+//     row's list;
+// then the rows meet on one 64-bit word of the decode workspace (zeroed by the stream kernel of
+// the same call; a single row needs no meeting): each adds 1 plus its overflow flag at bit
+// 32 + t. The last to arrive has
+// every flag, runs the overflow scan (rank among overflow rows, below cap), writes the dense
+// backup row ReLU(z + b1) of each overflow row with a slot (formed as k_up_gemv_dense forms
+// it, so it equals the recompute bit for bit) and zeroes the word again. Barriers wait for
+// LDS only: nothing written to global memory is read back by this kernel.
+constexpr int kFinB = 8;                                     // tiles per batch of a wave
 constexpr int kFinStage = 12288;                             // LDS stage entries (96 KB)
 constexpr int kFinMaxCH = 1024;
 
-template <int TT, int W, typename VT>
-__global__ __launch_bounds__(1024) void k_gemv_finish(const float *__restrict__ zp, const float *__restrict__ b1,
-                                                      int N, TwellOut o, TwellFinish f) {
-  constexpr int V = W / 64, B = kFinB / TT;
+template <int W, typename VT>
+__global__ __launch_bounds__(1024) void k_dec_finish(const float *__restrict__ zp, const float *__restrict__ b1, int M,
+                                                     int N, TwellOut o, TwellFinish f) {
+  constexpr int V = W / 64;
   __shared__ uint2 stage[kFinStage];
-  __shared__ int off_s[TT][kFinMaxCH], st_s[TT][kFinMaxCH];
-  __shared__ int wsum[TT][16];
-  __shared__ int carry_s[TT], ovf_s[TT], slot_s[TT];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int off_s[kFinMaxCH], st_s[kFinMaxCH];
+  __shared__ int wsum[16];
+  __shared__ int carry_s, ovf_s, last_s;
+  __shared__ int slot_s[kMsMaxT];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6, t = blockIdx.x;
   const int S = o.S, n_t = o.n_t;
-  const int CH = min(kFinMaxCH, kFinStage / (TT * S));
-  if (tid < TT) {
-    carry_s[tid] = 0;
-    ovf_s[tid] = 0;
+  const int CH = min(kFinMaxCH, kFinStage / S);
+  if (tid == 0) {
+    carry_s = 0;
+    ovf_s = 0;
   }
   block_barrier_lds();
   const bool lists = f.row_nnz && f.row_list;
-  const size_t lstride = (size_t)n_t * S;
+  const float *z0 = zp + (size_t)t * N, *z1 = zp + ((size_t)M + t) * N;
+  uint2 *lrow = lists ? f.row_list + (size_t)t * n_t * S : nullptr;
   for (int c0 = 0; c0 < n_t; c0 += CH) {
     const int nc = min(CH, n_t - c0);
-    for (int q0 = wave; q0 < nc; q0 += 16 * B) {
-      float z[B][TT][V], nb[B][V];
+    for (int q0 = wave; q0 < nc; q0 += 16 * kFinB) {
+      float z[kFinB][V], zb[kFinB][V], nb[kFinB][V];
 #pragma unroll
-      for (int bq = 0; bq < B; ++bq) {
+      for (int bq = 0; bq < kFinB; ++bq) {
         const int q = q0 + 16 * bq < nc ? q0 + 16 * bq : q0;   // a valid tile for every load
 #pragma unroll
         for (int e = 0; e < V; ++e) {
           const int u = (c0 + q) * W + V * lane + e;
-          nb[bq][e] = -b1[u];
-#pragma unroll
-          for (int t = 0; t < TT; ++t) z[bq][t][e] = zp[(size_t)t * N + u] + zp[((size_t)TT + t) * N + u];
+          nb[bq][e] = b1[u];
+          z[bq][e] = z0[u];
+          zb[bq][e] = z1[u];
         }
       }
+      __builtin_amdgcn_sched_barrier(0);       // every load of the batch before the first sum
 #pragma unroll
-      for (int bq = 0; bq < B; ++bq) {
+      for (int bq = 0; bq < kFinB; ++bq)
+#pragma unroll
+        for (int e = 0; e < V; ++e) {
+          nb[bq][e] = -nb[bq][e];
+          z[bq][e] += zb[bq][e];
+        }
+#pragma unroll
+      for (int bq = 0; bq < kFinB; ++bq) {
         const int q = q0 + 16 * bq;
         if (q >= nc) break;                                    // wave-uniform
-        int cnt[TT];
-        bool ovf[TT];
-        gemv_pack_tile<TT, W, VT>(z[bq], nb[bq], c0 + q, o, cnt, ovf, [&](int t, int slot, int col, float v) {
-          stage[(t * CH + q) * S + slot] = make_uint2((uint32_t)col, __float_as_uint(Elem<VT>::load_rounded(v)));
+        bool ovf;
+        const int cnt = gemv_pack_row<W, VT>(z[bq], nb[bq], t, c0 + q, o, &ovf, [&](int slot, int col, float v) {
+          stage[q * S + slot] = make_uint2((uint32_t)col, __float_as_uint(Elem<VT>::load_rounded(v)));
         });
-        if (lane == 0)
-#pragma unroll
-          for (int t = 0; t < TT; ++t) {
-            off_s[t][q] = cnt[t];
-            st_s[t][q] = cnt[t];
-            if (ovf[t]) ovf_s[t] = 1;
-          }
+        if (lane == 0) {
+          off_s[q] = cnt;
+          st_s[q] = cnt;
+          if (ovf) ovf_s = 1;
+        }
       }
     }
     block_barrier_lds();
     if (lists) {
-#pragma unroll
-      for (int t = 0; t < TT; ++t) {
-        const int c = tid < nc ? off_s[t][tid] : 0;
-        int tot;
-        const int ex = wave_excl_scan(c, &tot);
-        if (lane == 0) wsum[t][wave] = tot;
-        block_barrier_lds();
-        int pre = carry_s[t], all = 0;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          if (i < wave) pre += wsum[t][i];
-          all += wsum[t][i];
-        }
-        if (tid < nc) off_s[t][tid] = pre + ex;
-        block_barrier_lds();                   // every thread has read carry_s[t]
-        if (tid == 0) carry_s[t] += all;
-      }
+      const int c = tid < nc ? off_s[tid] : 0;
+      int tot;
+      const int ex = wave_excl_scan(c, &tot);
+      if (lane == 0) wsum[wave] = tot;
       block_barrier_lds();
-      // copy: lane l of a wave takes slot l % S of tile q (64 / S tiles per pass when S <= 32)
+      int pre = carry_s, all = 0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < wave) pre += wsum[i];
+        all += wsum[i];
+      }
+      if (tid < nc) off_s[tid] = pre + ex;
+      block_barrier_lds();                     // every thread has read carry_s
+      if (tid == 0) carry_s += all;
+      // copy: lane l of a wave takes slot l % S of a tile (64 / S tiles per pass when S <= 32)
       const int per = S <= 32 ? 64 / S : 1;
       const int sl = lane % S, sub = lane / S;
-      for (int p0 = wave * per; p0 < nc * TT; p0 += 16 * per) {
-        const int p = p0 + sub;                                // (t, q) = (p / nc, p % nc)
-        if (sub < per && p < nc * TT) {
-          const int t = p / nc, q = p - t * nc;
-          if (sl < st_s[t][q]) f.row_list[(size_t)t * lstride + off_s[t][q] + sl] = stage[(t * CH + q) * S + sl];
-        }
+      for (int q0 = wave * per; q0 < nc; q0 += 16 * per) {
+        const int q = q0 + sub;
+        if (sub < per && q < nc && sl < st_s[q]) lrow[off_s[q] + sl] = stage[q * S + sl];
       }
     }
     block_barrier_lds();               // the stage and the offsets are free for the next chunk
   }
   if (tid == 0) {
-    int r = 0;
-    for (int t = 0; t < TT; ++t) {
-      int sl = -1;
-      if (ovf_s[t]) {
-        if (r < f.cap) {
-          sl = r;
-          f.ovf_rows[r] = t;
+    if (lists) f.row_nnz[t] = carry_s;
+    const uint64_t mine = 1ull | ((uint64_t)(ovf_s ? 1u : 0u) << (32 + t));
+    const uint64_t old = M == 1 ? 0ull : __hip_atomic_fetch_add(o.dec_ticket, mine, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    last_s = (int)(old & 0xFFFFFFFFull) == M - 1;
+    if (last_s) {
+      const uint32_t flags = (uint32_t)((old + mine) >> 32);
+      int r = 0;
+      for (int i = 0; i < M; ++i) {
+        int sl = -1;
+        if ((flags >> i) & 1u) {
+          if (r < f.cap) {
+            sl = r;
+            f.ovf_rows[r] = i;
+          }
+          ++r;
         }
-        ++r;
+        slot_s[i] = sl;
+        f.ovf_slot[i] = sl;
       }
-      slot_s[t] = sl;
-      f.ovf_slot[t] = sl;
-      if (lists) f.row_nnz[t] = carry_s[t];
+      *f.ovf_n = r;
+      if (M > 1) __hip_atomic_store(o.dec_ticket, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
-    *f.ovf_n = r;
   }
   block_barrier_lds();
-  for (int t = 0; t < TT; ++t) {
-    const int sl = slot_s[t];
+  if (!last_s) return;
+  for (int i = 0; i < M; ++i) {
+    const int sl = slot_s[i];
     if (sl < 0) continue;                      // uniform
     VT *row = (VT *)f.ovf_dense + (size_t)sl * N;
+    const float *a0 = zp + (size_t)i * N, *a1 = zp + ((size_t)M + i) * N;
     for (int u = tid; u < N; u += 1024) {
-      float h = zp[(size_t)t * N + u] + zp[((size_t)TT + t) * N + u] + b1[u];
+      float h = a0[u] + a1[u] + b1[u];
       h = h > 0.f ? h : 0.f;
       Elem<VT>::store(row, u, h);
     }
   }
+}
+
+// Dense or N:M output of one 128-unit tile from its two half sums zs[half][u * TT + t] (token
+// slots t < rows, columns n0 + u < N): (NK == 0) out[t][col] = ReLU(z + b1) (or z + b1) in fp32
+// or bf16; (NK > 0) h rounded to bf16 and pruned NK:MM into vals / idx ([rows][N / MM][NK]),
+// staged in hs.
+template <int TT, int NK, int MM, int NT>
+TW_DEV void gemv_dense_out(const float (&zs)[2][kGemvUnits * TT], char *hs, const float *__restrict__ b1, int rows,
+                           int N, int n0, void *out, int out_bf16, int relu, uint8_t *__restrict__ idx) {
+  const int tid = threadIdx.x;
+  if constexpr (NK == 0) {
+    for (int i = tid; i < kGemvUnits * TT; i += NT) {
+      const int t = i / kGemvUnits, u = i % kGemvUnits, col = n0 + u;
+      if (t >= rows || col >= N) continue;
+      float h = zs[0][u * TT + t] + zs[1][u * TT + t] + b1[col];
+      if (relu) h = h > 0.f ? h : 0.f;
+      const size_t o = (size_t)t * N + col;
+      if (out_bf16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16(h);
+      else ((float *)out)[o] = h;
+    }
+  } else {
+    constexpr int RS = kGemvUnits * 2 + 16;
+    for (int i = tid; i < kGemvUnits * TT; i += NT) {
+      const int t = i / kGemvUnits, u = i % kGemvUnits, col = n0 + u;
+      put_h<uint16_t>(hs + t * RS + u * 2, zs[0][u * TT + t] + zs[1][u * TT + t] + (col < N ? b1[col] : 0.f));
+    }
+    __syncthreads();
+    nm_tile<uint16_t, NK, MM, TT, kGemvUnits, NT>(hs, rows, N, 0, n0, (uint16_t *)out, idx);
+  }
+}
+
+// The dense and N:M forms for 3 to 16 tokens: one 128-unit tile per workgroup of 512 threads,
+// wave w takes units 16 w .. 16 w + 15 over both halves of K in turn (mstream_wave), then
+// gemv_dense_out with 16 token slots.
+template <int NP, int NK, int MM>
+__global__ __launch_bounds__(512) void k_up_mstream_dense(const uint16_t *__restrict__ x,
+                                                          const uint16_t *__restrict__ w1t, const float *__restrict__ b1,
+                                                          int M, int N, int K, const int32_t *__restrict__ arow,
+                                                          const int32_t *__restrict__ n_rows_dev, void *out,
+                                                          int out_bf16, int relu, uint8_t *__restrict__ idx) {
+  constexpr int TT = kMsMaxT;
+  __shared__ float zs[2][kGemvUnits * TT];
+  __shared__ __attribute__((aligned(16))) char hs[NK > 0 ? TT * (kGemvUnits * 2 + 16) : 16];
+  const int n0 = blockIdx.x * kGemvUnits, tid = threadIdx.x;
+  int rows = M;
+  if (n_rows_dev) rows = min(rows, *n_rows_dev);
+  if (rows <= 0) return;
+  const int w = tid >> 6, lane = tid & 63, t = lane & 15;
+#pragma unroll
+  for (int kh = 0; kh < 2; ++kh) {
+    const f32x4_t z = mstream_wave<NP>(x, arow, rows, w1t, N, K, n0 + kGemvUPW * w, kh);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) zs[kh][(kGemvUPW * w + 4 * (lane >> 4) + i) * TT + t] = z[i];
+  }
+  __syncthreads();
+  gemv_dense_out<TT, NK, MM, 512>(zs, hs, b1, rows, N, n0, out, out_bf16, relu, idx);
 }
 
 // One 128-unit tile per workgroup of 512 threads: wave w takes units 16 w .. 16 w + 15 over
@@ -1613,25 +1756,7 @@ __global__ __launch_bounds__(512) void k_up_gemv_dense(const uint16_t *__restric
     if (own) zs[kh][vi] = z;
   }
   __syncthreads();
-  if constexpr (NK == 0) {
-    for (int i = tid; i < kGemvUnits * TT; i += 512) {
-      const int t = i / kGemvUnits, u = i % kGemvUnits, col = n0 + u;
-      if (t >= rows || col >= N) continue;
-      float h = zs[0][u * TT + t] + zs[1][u * TT + t] + b1[col];
-      if (relu) h = h > 0.f ? h : 0.f;
-      const size_t o = (size_t)t * N + col;
-      if (out_bf16) ((uint16_t *)out)[o] = (uint16_t)f32_to_bf16(h);
-      else ((float *)out)[o] = h;
-    }
-  } else {
-    constexpr int RS = kGemvUnits * 2 + 16;
-    for (int i = tid; i < kGemvUnits * TT; i += 512) {
-      const int t = i / kGemvUnits, u = i % kGemvUnits, col = n0 + u;
-      put_h<uint16_t>(hs + t * RS + u * 2, zs[0][u * TT + t] + zs[1][u * TT + t] + (col < N ? b1[col] : 0.f));
-    }
-    __syncthreads();
-    nm_tile<uint16_t, NK, MM, TT, kGemvUnits, 512>(hs, rows, N, 0, n0, (uint16_t *)out, idx);
-  }
+  gemv_dense_out<TT, NK, MM, 512>(zs, hs, b1, rows, N, n0, out, out_bf16, relu, idx);
 }
 
 // bf16, 1 or 2 tokens (at c3 sizes: 26 / 28 us against 30 us for the tile kernel; from 3 tokens
@@ -1639,6 +1764,11 @@ __global__ __launch_bounds__(512) void k_up_gemv_dense(const uint16_t *__restric
 // {1024, 2048, 4096} (K / 2 in whole kilobyte pieces per lane).
 static bool use_gemv(int bf16, int T_tokens, int K) {
   return bf16 && T_tokens >= 1 && T_tokens <= kGemvMaxT && (K == 1024 || K == 2048 || K == 4096);
+}
+
+// bf16, 3 to 16 tokens, K in {1024, 2048, 4096} (the steps are unrolled per K).
+static bool use_mstream(int bf16, int T_tokens, int K) {
+  return bf16 && T_tokens > kGemvMaxT && T_tokens <= kMsMaxT && (K == 1024 || K == 2048 || K == 4096);
 }
 
 // The decode kernels apply to at most 64 tokens and K a multiple of four stages.
@@ -1680,28 +1810,57 @@ static hipError_t launch_twell_dec(const T *x, const T *w1t, const float *b1, in
   return hipGetLastError();
 }
 
-template <int TT, int W, typename VT>
-static void launch_gemv_tail(const float *b1, int N, const TwellOut &o, const TwellFinish &f, hipStream_t s) {
+// After a stream kernel: the whole matrix (complete) or the TwELL alone, from the half sums.
+template <int W, typename VT>
+static void launch_dec_tail(const float *b1, int M, int N, const TwellOut &o, const TwellFinish &f, hipStream_t s) {
   if (f.complete)
-    hipLaunchKernelGGL((k_gemv_finish<TT, W, VT>), dim3(1), dim3(1024), 0, s, o.dec_part, b1, N, o, f);
+    hipLaunchKernelGGL((k_dec_finish<W, VT>), dim3(M), dim3(1024), 0, s, o.dec_part, b1, M, N, o, f);
   else
-    hipLaunchKernelGGL((k_gemv_pack<TT, W, VT>), dim3((o.n_t + 15) / 16), dim3(1024), 0, s, o.dec_part, b1, N, o);
+    hipLaunchKernelGGL((k_dec_pack<W, VT>), dim3((M * o.n_t + 15) / 16), dim3(1024), 0, s, o.dec_part, b1, M, N, o);
 }
 
-template <int TT>
-static hipError_t launch_gemv_twell_t(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
+// 1 to 16 bf16 tokens: the W1 stream (k_up_gemv_z for 1 or 2, k_up_mstream_z from 3), then the
+// packing kernels.
+static hipError_t launch_stream_twell(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
                                       const TwellOut &o, const TwellFinish &f, int W, hipStream_t s) {
   const dim3 grid(2 * ((N + kGemvUPW - 1) / kGemvUPW));
-  if (K == 1024) hipLaunchKernelGGL((k_up_gemv_z<TT, 1>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket);
-  else if (K == 2048) hipLaunchKernelGGL((k_up_gemv_z<TT, 2>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket);
-  else hipLaunchKernelGGL((k_up_gemv_z<TT, 4>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket);
-  if (o.val_bf16) {
-    if (W == 64) launch_gemv_tail<TT, 64, uint16_t>(b1, N, o, f, s);
-    else launch_gemv_tail<TT, 128, uint16_t>(b1, N, o, f, s);
+  if (M > kGemvMaxT) {
+    if (K == 1024) hipLaunchKernelGGL((k_up_mstream_z<1>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
+    else if (K == 2048) hipLaunchKernelGGL((k_up_mstream_z<2>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
+    else hipLaunchKernelGGL((k_up_mstream_z<4>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
+  } else if (M == 1) {
+    if (K == 1024) hipLaunchKernelGGL((k_up_gemv_z<1, 1>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
+    else if (K == 2048) hipLaunchKernelGGL((k_up_gemv_z<1, 2>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
+    else hipLaunchKernelGGL((k_up_gemv_z<1, 4>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
   } else {
-    if (W == 64) launch_gemv_tail<TT, 64, float>(b1, N, o, f, s);
-    else launch_gemv_tail<TT, 128, float>(b1, N, o, f, s);
+    if (K == 1024) hipLaunchKernelGGL((k_up_gemv_z<2, 1>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
+    else if (K == 2048) hipLaunchKernelGGL((k_up_gemv_z<2, 2>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
+    else hipLaunchKernelGGL((k_up_gemv_z<2, 4>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
   }
+  if (o.val_bf16) {
+    if (W == 64) launch_dec_tail<64, uint16_t>(b1, M, N, o, f, s);
+    else launch_dec_tail<128, uint16_t>(b1, M, N, o, f, s);
+  } else {
+    if (W == 64) launch_dec_tail<64, float>(b1, M, N, o, f, s);
+    else launch_dec_tail<128, float>(b1, M, N, o, f, s);
+  }
+  return hipGetLastError();
+}
+
+template <int NK, int MM>
+static hipError_t launch_mstream_dense_t(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
+                                         const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16,
+                                         int relu, uint8_t *idx, hipStream_t s) {
+  const dim3 grid((N + kGemvUnits - 1) / kGemvUnits), blk(512);
+  if (K == 1024)
+    hipLaunchKernelGGL((k_up_mstream_dense<1, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
+  else if (K == 2048)
+    hipLaunchKernelGGL((k_up_mstream_dense<2, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
+  else
+    hipLaunchKernelGGL((k_up_mstream_dense<4, NK, MM>), grid, blk, 0, s, x, w1t, b1, M, N, K, arow, n_rows_dev, out,
+                       out_bf16, relu, idx);
   return hipGetLastError();
 }
 
@@ -1731,7 +1890,7 @@ static hipError_t launch_gemv_dense_t(const uint16_t *x, const uint16_t *w1t, co
 }
 
 bool up_twell_completes(int bf16, int M, int K, const TwellFinish &f) {
-  return f.complete && f.row_nnz && f.row_list && use_gemv(bf16, M, K);
+  return f.complete && f.row_nnz && f.row_list && (use_gemv(bf16, M, K) || use_mstream(bf16, M, K));
 }
 
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N,
@@ -1739,13 +1898,11 @@ hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float
   if ((bf16 ? use_decode<uint16_t>(M, K) || use_gemv(bf16, M, K) : use_decode<float>(M, K)) &&
       (!o.dec_part || !o.dec_ticket))
     return hipErrorInvalidValue;
-  if (use_gemv(bf16, M, K)) {
+  if (use_gemv(bf16, M, K) || use_mstream(bf16, M, K)) {
     if ((f.complete && (!f.ovf_n || !f.ovf_slot || (f.cap > 0 && (!f.ovf_rows || !f.ovf_dense)))) ||
         (size_t)2 * M * N * 4 > o.dec_bytes)
       return hipErrorInvalidValue;
-    const uint16_t *xb = (const uint16_t *)x, *wb = (const uint16_t *)w1t;
-    if (M <= 1) return launch_gemv_twell_t<1>(xb, wb, b1, M, N, K, o, f, W, s);
-    return launch_gemv_twell_t<2>(xb, wb, b1, M, N, K, o, f, W, s);
+    return launch_stream_twell((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, f, W, s);
   }
   if (bf16 && use_decode<uint16_t>(M, K))
     return launch_twell_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, o, W, s);
@@ -1789,6 +1946,9 @@ hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float
   if (use_gemv(bf16, x_rows, K))
     return launch_gemv_dense_t<0, 0>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow, n_rows_dev,
                                      out, out_bf16, relu, nullptr, s);
+  if (use_mstream(bf16, x_rows, K))
+    return launch_mstream_dense_t<0, 0>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, arow, n_rows_dev, out,
+                                        out_bf16, relu, nullptr, s);
   if (bf16 && use_decode<uint16_t>(x_rows, K))
     return launch_dense_dec<uint16_t>((const uint16_t *)x, (const uint16_t *)w1t, b1, M, N, K, x_rows, arow,
                                       n_rows_dev, out, out_bf16, relu, s);
@@ -1851,6 +2011,14 @@ hipError_t launch_up_nm(int bf16, const void *x, const void *w1t, const float *b
       if (n == 8 && m == 16) return launch_gemv_dense_t<8, 16>(xb, wb, b1, M, N, K, M, nullptr, nullptr, vb, 1, 1, idx, s);
       if (n == 16 && m == 32)
         return launch_gemv_dense_t<16, 32>(xb, wb, b1, M, N, K, M, nullptr, nullptr, vb, 1, 1, idx, s);
+      return hipErrorInvalidValue;
+    }
+    if (use_mstream(bf16, M, K)) {
+      if (n == 2 && m == 4) return launch_mstream_dense_t<2, 4>(xb, wb, b1, M, N, K, nullptr, nullptr, vb, 1, 1, idx, s);
+      if (n == 4 && m == 8) return launch_mstream_dense_t<4, 8>(xb, wb, b1, M, N, K, nullptr, nullptr, vb, 1, 1, idx, s);
+      if (n == 8 && m == 16) return launch_mstream_dense_t<8, 16>(xb, wb, b1, M, N, K, nullptr, nullptr, vb, 1, 1, idx, s);
+      if (n == 16 && m == 32)
+        return launch_mstream_dense_t<16, 32>(xb, wb, b1, M, N, K, nullptr, nullptr, vb, 1, 1, idx, s);
       return hipErrorInvalidValue;
     }
     if (use_decode<uint16_t>(M, K)) return launch_nm_dec<uint16_t>(xb, wb, b1, M, N, K, n, m, vb, idx, s);

@@ -258,14 +258,19 @@ def test_fwd_wide_gather(T, d, f, W, S, dt, seed):
 
 @pytest.mark.parametrize("T,d,f,W,S,seed", [(1, 4096, 1024, 128, 16, 51), (2, 1024, 1984, 64, 2, 52),
                                              (2, 2048, 2048, 128, 2, 53), (3, 4096, 1536, 64, 3, 54),
-                                             (1, 1024, 384, 128, 1, 55)])
+                                             (1, 1024, 384, 128, 1, 55), (5, 1024, 1984, 64, 2, 56),
+                                             (8, 2048, 2048, 128, 4, 57), (16, 4096, 1024, 128, 16, 58),
+                                             (12, 1024, 768, 64, 3, 59), (6, 1280, 1024, 128, 4, 60),
+                                             (9, 512, 1024, 128, 4, 61)])
 def test_fwd_decode_gemv(T, d, f, W, S, seed):
-    """For 1 or 2 tokens (bf16, d_model 1024 / 2048 / 4096) the up projection is a W1 stream: each
-    128-unit tile is summed in two halves of K on two workgroups that meet in the row_list
-    workspace. The TwELL equals the dense path's packing bit for bit (that path sums the same
-    halves in one workgroup), the tickets are zero after every call, repeated calls give the
-    same bits, and small S sends rows to the dense backup (recomputed the same way). 3 tokens
-    take the tile kernel (K in quarters)."""
+    """Up to 16 tokens (bf16; d_model 1024 / 2048 / 4096 for 1 or 2 tokens, a multiple of 1024 from
+    3 on) the up projection is a W1 stream on one-wave workgroups (v_dot2 for 1 or 2 tokens,
+    16x16x32 MFMA from 3) that stores the half sums of K in the row_list workspace; then one
+    workgroup per row packs the TwELL and completes the matrix. The TwELL equals the dense path's
+    packing bit for bit (that path sums the same halves in one workgroup), the tickets are zero
+    after every call, repeated calls give the same bits, and small S sends rows to the dense
+    backup (written from the same sums). d_model = 1280 or 512 (not a multiple of 1024) takes
+    the tile kernel (K in quarters)."""
     say("fwd decode gemv", T, d, f, W, S)
     w = synth.C3.with_(d=d, f=f, tile_w=W, slots=S, seed=seed)
     g = synth.generate(w, T=T)

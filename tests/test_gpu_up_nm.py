@@ -46,12 +46,14 @@ def normal_layer(T, d, f, seed, dt, bias):
 
 
 # (T, d, f, dtype): 256x256 bf16 tiles with a ragged last row tile; 64x128 bf16 tiles with
-# ragged rows and a partial column tile; the decode K split (bf16 and fp32); a K that is not
-# a multiple of the decode quarters at a decode token count; fp32 tiles; the W1 stream of
-# 1 or 2 bf16 tokens (d_model 1024 / 2048 / 4096, a partial 128-unit tile).
-SHAPES = [(1000, 256, 2048, "bf16"), (100, 256, 544, "bf16"), (8, 512, 640, "bf16"),
-          (64, 256, 384, "bf16"), (8, 264, 256, "bf16"), (130, 256, 512, "f32"), (8, 256, 256, "f32"),
-          (1, 4096, 256, "bf16"), (2, 1024, 640, "bf16"), (2, 2048, 384, "bf16")]
+# ragged rows and a partial column tile; the MFMA W1 stream of 3 to 16 bf16 tokens (d_model a
+# multiple of 1024); the decode K split (bf16 and fp32); a K that is not a multiple of the
+# decode quarters at a decode token count; fp32 tiles; the v_dot2 W1 stream of 1 or 2 bf16
+# tokens (d_model 1024 / 2048 / 4096, a partial 128-unit tile).
+SHAPES = [(1000, 256, 2048, "bf16"), (100, 256, 544, "bf16"), (8, 1024, 640, "bf16"), (16, 1024, 512, "bf16"),
+          (3, 2048, 384, "bf16"), (8, 512, 640, "bf16"), (64, 256, 384, "bf16"), (8, 264, 256, "bf16"),
+          (130, 256, 512, "f32"),
+          (8, 256, 256, "f32"), (1, 4096, 256, "bf16"), (2, 1024, 640, "bf16"), (2, 2048, 384, "bf16")]
 
 
 @pytest.mark.parametrize("n,m", PATTERNS)
