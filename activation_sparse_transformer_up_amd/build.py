@@ -14,7 +14,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libtwell.so")
-SOURCES = ["abi.hip", "gemm.hip", "pack.hip", "down.hip", "bwd.hip", "nm.hip", "gated.hip", "rell.hip"]
+SOURCES = ["abi.hip", "gemm.hip", "pack.hip", "down.hip", "decode.hip", "bwd.hip", "nm.hip", "gated.hip", "rell.hip"]
 
 ARCH = "gfx950"
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

@@ -271,6 +271,14 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
   if (st) return st;
   if (!al16(w2) || !al16(y)) return TWELL_ERR_ALIGN;
   hipStream_t s = S(stream);
+  if (T > 0 && in_dtype == TWELL_BF16 && up_stream_ok(1, T, d_model)) {
+    // up to 16 tokens: the W1 stream, then the TwELL, the overflow scan and y in one launch
+    const TwellOut o = out_of(h);
+    TW_TRY(launch_up_stream(x, w1t, T, d_ff, d_model, o, s));
+    TW_TRY(launch_dec_fused_down(b1, T, d_ff, o, finish_of(h, true), w2, d_model, y, y_dtype == TWELL_BF16, h->tile_w,
+                                 s));
+    return TWELL_OK;
+  }
   st = up_gemm(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s, true);
   if (st) return st;
   if (!gemm_completes(in_dtype, T, d_model, h)) st = up_finish(x, w1t, b1, in_dtype, T, d_model, d_ff, h, s);

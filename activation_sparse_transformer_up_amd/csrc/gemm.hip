@@ -1819,10 +1819,10 @@ static void launch_dec_tail(const float *b1, int M, int N, const TwellOut &o, co
     hipLaunchKernelGGL((k_dec_pack<W, VT>), dim3((M * o.n_t + 15) / 16), dim3(1024), 0, s, o.dec_part, b1, M, N, o);
 }
 
-// 1 to 16 bf16 tokens: the W1 stream (k_up_gemv_z for 1 or 2, k_up_mstream_z from 3), then the
-// packing kernels.
-static hipError_t launch_stream_twell(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
-                                      const TwellOut &o, const TwellFinish &f, int W, hipStream_t s) {
+// 1 to 16 bf16 tokens: the W1 stream (k_up_gemv_z for 1 or 2, k_up_mstream_z from 3) into the
+// half sums of o.dec_part.
+static void launch_stream_z(const uint16_t *x, const uint16_t *w1t, int M, int N, int K, const TwellOut &o,
+                            hipStream_t s) {
   const dim3 grid(2 * ((N + kGemvUPW - 1) / kGemvUPW));
   if (M > kGemvMaxT) {
     if (K == 1024) hipLaunchKernelGGL((k_up_mstream_z<1>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
@@ -1837,6 +1837,12 @@ static hipError_t launch_stream_twell(const uint16_t *x, const uint16_t *w1t, co
     else if (K == 2048) hipLaunchKernelGGL((k_up_gemv_z<2, 2>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
     else hipLaunchKernelGGL((k_up_gemv_z<2, 4>), grid, dim3(64), 0, s, x, nullptr, nullptr, M, w1t, N, K, o.dec_part, o.dec_ticket, o.ovf_bits, o.n_t, o.words);
   }
+}
+
+// The stream, then the packing kernels.
+static hipError_t launch_stream_twell(const uint16_t *x, const uint16_t *w1t, const float *b1, int M, int N, int K,
+                                      const TwellOut &o, const TwellFinish &f, int W, hipStream_t s) {
+  launch_stream_z(x, w1t, M, N, K, o, s);
   if (o.val_bf16) {
     if (W == 64) launch_dec_tail<64, uint16_t>(b1, M, N, o, f, s);
     else launch_dec_tail<128, uint16_t>(b1, M, N, o, f, s);
@@ -1886,6 +1892,14 @@ static hipError_t launch_gemv_dense_t(const uint16_t *x, const uint16_t *w1t, co
                                       int out_bf16, int relu, uint8_t *idx, hipStream_t s) {
   if (x_rows <= 1) launch_gemv_dense_tt<1, NK, MM>(x, w1t, b1, M, N, K, arow, n_rows_dev, out, out_bf16, relu, idx, s);
   else launch_gemv_dense_tt<2, NK, MM>(x, w1t, b1, M, N, K, arow, n_rows_dev, out, out_bf16, relu, idx, s);
+  return hipGetLastError();
+}
+
+bool up_stream_ok(int bf16, int M, int K) { return use_gemv(bf16, M, K) || use_mstream(bf16, M, K); }
+
+hipError_t launch_up_stream(const void *x, const void *w1t, int M, int N, int K, const TwellOut &o, hipStream_t s) {
+  if (!up_stream_ok(1, M, K) || !o.dec_part || (size_t)2 * M * N * 4 > o.dec_bytes) return hipErrorInvalidValue;
+  launch_stream_z((const uint16_t *)x, (const uint16_t *)w1t, M, N, K, o, s);
   return hipGetLastError();
 }
 

@@ -61,6 +61,16 @@ hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float
 // true if launch_up_twell of M tokens with f also completes the matrix (lists, overflow scan,
 // backup rows): the finish step has nothing left to do
 bool up_twell_completes(int bf16, int M, int K, const TwellFinish &f);
+// 1 to 16 bf16 tokens: true if the up projection runs as a W1 stream that leaves the half sums
+// in o.dec_part (launch_up_stream), which launch_dec_fused_down then turns into the TwELL, the
+// overflow scan, the backup rows and y
+bool up_stream_ok(int bf16, int M, int K);
+hipError_t launch_up_stream(const void *x, const void *w1t, int M, int N, int K, const TwellOut &o, hipStream_t s);
+
+// decode.hip: after launch_up_stream, the TwELL of the M <= 16 rows, the overflow scan, the
+// backup rows and y = h W2 (bf16 W2 [N][d]) in one launch
+hipError_t launch_dec_fused_down(const float *b1, int M, int N, const TwellOut &o, const TwellFinish &f, const void *w2,
+                                 int d, void *y, int y_bf16, int W, hipStream_t s);
 hipError_t launch_up_dense(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
                            int x_rows, const int32_t *arow, const int32_t *n_rows_dev, void *out, int out_bf16, int relu,
                            hipStream_t s);

@@ -291,6 +291,28 @@ def test_fwd_decode_gemv(T, d, f, W, S, seed):
         assert got["ovf_n"] > 0
 
 
+@pytest.mark.parametrize("T,f,bias,seed", [(1, 20480, -1.2, 71), (7, 20480, -1.2, 72), (3, 16512, -2.0, 73)])
+def test_fwd_decode_fused_long_lists(T, f, bias, seed):
+    """Up to 16 bf16 tokens the forward after the W1 stream is one kernel that rebuilds each
+    token's active list in LDS, a segment of 16384 units at a time, and gathers it in rounds of
+    256 entries. d_ff = 20480 takes two segments, and about 11 % active units give lists of
+    ~2300 entries: full rounds, entries carried from one segment to the next, and rows above
+    the slot budget (backup rows); d_ff = 16512 ends in a one-tile second segment with ~350
+    entries per row. The TwELL equals the oracle's packing of the GPU's own h, y matches the
+    oracle, and a repeated call gives the same bits."""
+    say("fwd decode fused long lists", T, f, bias)
+    w = synth.C3.with_(d=1024, f=f, tile_w=128, slots=16, seed=seed, bias=bias)
+    g = synth.generate(w, T=T)
+    got, flips, err = check_forward(g, 128, 16, T)
+    x, w1t, b1, w2 = dev_inputs(g)
+    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 16, T)
+    y2, _ = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 16, T, h=h)
+    torch.cuda.synchronize()
+    assert torch.equal(y1, y2)
+    assert_twell_equal(twell_host(h), got)
+    assert int(got["counts"].sum()) > 300 * T                 # more than one round per row
+
+
 def test_fwd_hot_tokens_and_capacity():
     say("fwd hot tokens")
     w = synth.C5.with_(T=600, d=512, f=2048, slots=8, hot_every=64)
