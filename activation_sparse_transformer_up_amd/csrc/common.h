@@ -125,10 +125,16 @@ template <typename YT, int E> TW_DEV void store_out_nt(YT *y, size_t o, const fl
 }
 
 // Rows of a matrix read through a buffer resource: a scalar descriptor plus a 32-bit byte
-// offset per lane (every operand is below 2 GiB). Offsets at or above 2^31 (e.g. from a
-// negative index) read as zeros.
-TW_DEV __amdgpu_buffer_rsrc_t rows_rsrc(const void *p) {
-  return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, 0x7FFFFFFF, 0x00020000);
+// offset per lane (every operand is below 2 GiB). Offsets at or above `bytes` (default 2^31 - 1;
+// e.g. from a negative index, or a row index read from a list that was never written) read as
+// zeros.
+TW_DEV __amdgpu_buffer_rsrc_t rows_rsrc(const void *p, uint32_t bytes = 0x7FFFFFFFu) {
+  return __builtin_amdgcn_make_buffer_rsrc((void *)p, (short)0, (int)bytes, 0x00020000);
+}
+// Byte extent of a [rows][d] matrix of T for rows_rsrc (capped at 2^31 - 1).
+template <typename T> TW_DEV uint32_t rows_bytes(int rows, int d) {
+  const size_t b = (size_t)rows * (size_t)d * sizeof(T);
+  return b < 0x7FFFFFFFu ? (uint32_t)b : 0x7FFFFFFFu;
 }
 template <typename WT> TW_DEV uint4 ld16(__amdgpu_buffer_rsrc_t rs, uint32_t elem) {
   const u32x4_t v = __builtin_amdgcn_raw_buffer_load_b128(rs, (int)(elem * (uint32_t)sizeof(WT)), 0, 0);

@@ -66,7 +66,7 @@ __global__ __launch_bounds__(kFdThreads) void k_dec_fused_down(const float *__re
   const int col = c * CW + gl * E;
   const bool cv = col < d;
   const bool writer = c == 0;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<WT>(N, d));
   const float *z0 = zp + (size_t)t * N, *z1 = zp + ((size_t)M + t) * N;
   const int S = o.S, n_t = o.n_t;
   if (tid == 0) ovf_s = 0;

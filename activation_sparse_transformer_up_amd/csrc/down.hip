@@ -70,7 +70,7 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<WT>(h.cols, d));
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(64) void k_twell_down(TwellIn h, const WT *__restri
   // the overflow slot and the list length in one round trip
   const int slot0 = h.ovf_slot[t], nnz0 = h.row_nnz[t];
   if (slot0 < 0) {
-    const int nnz = nnz0;
+    const int nnz = list_len(h, nnz0);
     const uint2 *src = h.row_list + (size_t)t * h.n_t * h.S;
     for (int base = 0; base < nnz; base += 64) {
       const int n = min(64, nnz - base);
@@ -165,7 +165,7 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
   const bool cv = col < d;
   const int t = h.ovf_rows[r];
   const VT *row = (const VT *)h.ovf_dense + (size_t)r * h.cols;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<WT>(h.cols, d));
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -237,14 +237,14 @@ __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restr
   const int tc = t < h.rows ? t : 0;                       // slot and length in one round trip
   const int slot0 = h.ovf_slot[tc], nnz0 = h.row_nnz[tc];
   const bool normal = t < h.rows && slot0 < 0;
-  const int nnz = normal ? nnz0 : 0;
+  const int nnz = normal ? list_len(h, nnz0) : 0;
   int n = max(nnz, __shfl_xor(nnz, 16, 64));
   n = max(n, __shfl_xor(n, 32, 64));
   const uint2 *lp = h.row_list + (size_t)(t < h.rows ? t : 0) * h.n_t * h.S;
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  gather_list16<WT>(lp, nnz, n, w2, d, col, cv, acc);
+  gather_list16<WT>(lp, nnz, n, w2, d, col, cv, acc, rows_bytes<WT>(h.cols, d));
   if (normal && t < h.rows && cv) {
     const size_t o = (size_t)t * d + col;
     store_out_nt<YT, E>(y, o, acc);
@@ -271,11 +271,11 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
   const int G = wave * 4 + (lane >> 4), gl = lane & 15;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<WT>(h.cols, d));
   const int cap = h.n_t * h.S;
   const uint2 *src = h.row_list + (size_t)t * cap;
   if (tid < LW) lst[tid] = tid < cap ? src[tid] : make_uint2(0, 0);
-  const int slot = h.ovf_slot[t], nnz = h.row_nnz[t];      // one round trip with the list
+  const int slot = h.ovf_slot[t], nnz = list_len(h, h.row_nnz[t]);   // one round trip with the list
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
@@ -350,7 +350,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   const uint2 *src = h.row_list + (size_t)t * cap;
   const int e0 = 16 * wave + lane;
   uint2 pn = (lane < 16 && e0 < cap) ? src[e0] : make_uint2(0, 0);
-  const int slot = h.ovf_slot[t], nnz = h.row_nnz[t];      // one round trip with the list
+  const int slot = h.ovf_slot[t], nnz = list_len(h, h.row_nnz[t]);   // one round trip with the list
   if (slot >= 0) {
     const int cn = 4 * c + wave;                            // this wave's 16-lane chunk
     if (cn * 16 * E < d) backup_row<WT, VT, YT>(h, w2, d, y, slot, cn, lst[wave]);
@@ -358,7 +358,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   }
   const int col = c * CW + lane * E;
   const bool cv = col < d;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<WT>(h.cols, d));
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;

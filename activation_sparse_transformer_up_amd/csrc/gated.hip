@@ -51,11 +51,11 @@ template <typename XT> TW_DEV float dot16(uint4 a, uint4 b, float acc) {
 // registers than needed for larger rows would cost occupancy for nothing at small d).
 template <typename XT, int NP>
 TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, int d, const int (&col)[kGateEnt],
-                      float (&u)[kGateEnt]) {
+                      float (&u)[kGateEnt], int rows) {
   constexpr int EPL = 16 / sizeof(XT);
   const int lane = lane_id();
   const int npc = (d + 64 * EPL - 1) / (64 * EPL);
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(wu);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(wu, rows_bytes<XT>(rows, d));
 #pragma unroll
   for (int k = 0; k < kGateEnt; ++k) u[k] = 0.f;
   for (int c0 = 0; c0 < npc; c0 += NP) {
@@ -90,7 +90,7 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
   if (p >= P) return;
   // the overflow flag and the list length in one round trip, each entry's (column, gate)
   // pair in one load: the gate is kept for the final product instead of being re-read
-  const int oslot = h.ovf_slot[t], nnz = h.row_nnz[t];
+  const int oslot = h.ovf_slot[t], nnz = list_len(h, h.row_nnz[t]);
   if (oslot >= 0) return;
   const int wave = threadIdx.x >> 6, lane = lane_id();
   uint2 *lst = h.row_list + (size_t)t * h.n_t * h.S;
@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
       gv[k] = __uint_as_float(en.y);
     }
     float u[kGateEnt];
-    wave_dots<XT, NP>(xrow, wu, d, col, u);
+    wave_dots<XT, NP>(xrow, wu, d, col, u, h.cols);
     if (lane == 0)
 #pragma unroll
       for (int k = 0; k < kGateEnt; ++k)
@@ -143,7 +143,7 @@ __global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__
         m &= m ? m - 1 : 0;
       }
       float u[kGateEnt];
-      wave_dots<XT, 8>(x + (size_t)t * d, wu, d, col, u);
+      wave_dots<XT, 8>(x + (size_t)t * d, wu, d, col, u, h.cols);
 #pragma unroll
       for (int k = 0; k < kGateEnt; ++k) {
         const float gk = __shfl(g, col[k] & 63, 64);
@@ -171,10 +171,9 @@ __global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk,
   const int t = tb * 16 + (threadIdx.x >> 6) * 4 + g;
   const int colo = c * CW + gl * E;
   const bool cv = colo < d;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(wu);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(wu, rows_bytes<XT>(h.cols, d));
   const size_t cap = (size_t)h.n_t * h.S;
-  int n = t < h.rows ? h.row_nnz[t] : 0;
-  if (n < 0) n = 0;
+  const int n = t < h.rows ? list_len(h, h.row_nnz[t]) : 0;
   int nw = max(n, __shfl_xor(n, 16, 64));
   nw = max(nw, __shfl_xor(nw, 32, 64));
   const int tt = t < h.rows ? t : 0;
@@ -224,7 +223,7 @@ __global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk,
 __global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const float *__restrict__ part) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= h.rows) return;
-  const int n = h.row_nnz[t];
+  const int n = list_len(h, h.row_nnz[t]);
   const size_t cap = (size_t)h.n_t * h.S, plane = (size_t)h.rows * cap;
   uint2 *lp = h.row_list + (size_t)t * cap;
   const float *pp = part + (size_t)t * cap;
@@ -330,7 +329,7 @@ TW_DEV void fused_up_item(const TwellIn &h, const XT *__restrict__ x, const XT *
           gv[q] = ok ? Elem<VT>::load(vals, sb + s0 + q) : 0.f;
         }
         float u[kGateEnt];
-        wave_dots<XT, NP>(xrow, wu, d, col, u);
+        wave_dots<XT, NP>(xrow, wu, d, col, u, h.cols);
         if (lane == 0)
 #pragma unroll
           for (int q = 0; q < kGateEnt; ++q)
@@ -346,7 +345,7 @@ TW_DEV void fused_up_item(const TwellIn &h, const XT *__restrict__ x, const XT *
 #pragma unroll
         for (int q = 0; q < kGateEnt; ++q) col[q] = j0 + q;
         float z[kGateEnt];
-        wave_dots<XT, NP>(xrow, wg, d, col, z);
+        wave_dots<XT, NP>(xrow, wg, d, col, z, h.cols);
         int ucol[kGateEnt];
         float g[kGateEnt];
 #pragma unroll
@@ -356,7 +355,7 @@ TW_DEV void fused_up_item(const TwellIn &h, const XT *__restrict__ x, const XT *
           ucol[q] = g[q] != 0.f ? col[q] : -1;
         }
         float u[kGateEnt];
-        wave_dots<XT, NP>(xrow, wu, d, ucol, u);
+        wave_dots<XT, NP>(xrow, wu, d, ucol, u, h.cols);
         if (lane == 0)
 #pragma unroll
           for (int q = 0; q < kGateEnt; ++q)
@@ -410,7 +409,7 @@ __global__ __launch_bounds__(256) void k_gated_fused(TwellIn h, const XT *__rest
   // down items (t, chunk of 4 * CW columns), statically spread over the workgroups
   const int nch = (d + 4 * CW - 1) / (4 * CW);
   const int g = lane >> 4, gl = lane & 15;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2);
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<XT>(h.cols, d));
   for (int it = blockIdx.x; it < T * nch; it += gridDim.x) {
     const int t = it / nch, c = it % nch;
     const int colo = (c * 4 + wave) * CW + gl * E;

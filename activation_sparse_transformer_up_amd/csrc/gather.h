@@ -50,11 +50,11 @@ TW_DEV void fma16(float (&acc)[E], float v, uint4 raw) {
 // adds entries l, l + 16, ...).
 template <typename WT>
 TW_DEV float gather_list16(const uint2 *__restrict__ p, int n, int nw, const WT *__restrict__ M, int d, int col,
-                           bool cv, float (&acc)[Vec16<WT>::N]) {
+                           bool cv, float (&acc)[Vec16<WT>::N], uint32_t mbytes = 0x7FFFFFFFu) {
   constexpr int E = Vec16<WT>::N;
   constexpr uint32_t OOB = 0x80000000u;                      // beyond the range: reads zeros
   const int gl = lane_id() & 15;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(M);            // row pieces by buffer loads
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(M, mbytes);    // row pieces by buffer loads
   // byte offset of row i's piece: i * (row bytes) + this lane's column bytes, one 24-bit
   // multiply-add (row indices and row bytes are below 2^24, the operand below 2 GiB)
   const uint32_t rowb = (uint32_t)d * (uint32_t)sizeof(WT), colb = (uint32_t)col * (uint32_t)sizeof(WT);

@@ -55,6 +55,11 @@ struct TwellIn {
   int rows, cols, n_t, S, W, val_bf16, cap;
 };
 
+// Length of row t's list as the gathers use it: row_nnz[t] clamped to [0, n_t S]. The lists
+// are scratch that only the finish step writes; a matrix whose lists are stale or were never
+// built then gives wrong sums, but no access outside its row of row_list.
+__device__ __forceinline__ int list_len(const TwellIn &h, int nnz) { return min(max(nnz, 0), h.n_t * h.S); }
+
 // gemm.hip
 hipError_t launch_up_twell(int bf16, const void *x, const void *w1t, const float *b1, int M, int N, int K,
                            const TwellOut &o, const TwellFinish &f, int W, hipStream_t s);

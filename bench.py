@@ -191,6 +191,10 @@ def leg_c3(steps, warmup):
             torch.relu(torch.addmm(bb, x, w1.t())) @ w2_
 
         ms = _time(fwd, steps * 4, warmup)
+        # the gather walks the row lists of the staged path (the fused decode forward leaves none)
+        for i in range(3):
+            tw.twell_up_gemm(x, copies[i][0], b1, hs[i])
+            tw.twell_up_finish(x, copies[i][0], b1, hs[i])
         ms_down = _time(down, steps * 4, warmup)
         ms_gemm = _time(gemm, steps * 4, warmup)
         ms_dense = _time(dense, steps * 4, warmup)

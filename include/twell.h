@@ -140,6 +140,10 @@ int twell_pack(const void *h, int32_t h_dtype, twell_matrix_t *out, void *stream
  * buffers from the caller, rows = T, cols = d_ff) is left for the backward pass.
  * in_dtype: TWELL_F32 (x, w1t, w2 fp32) or TWELL_BF16 (bf16, fp32 accumulation).
  * y_dtype: TWELL_F32 or TWELL_BF16. T == 0 is allowed (only *ovf_n is written).
+ * The row lists (row_nnz, row_list) are scratch: from 1 to 16 bf16 tokens with d_model 1024,
+ * 2048 or 4096 the forward packs
+ * the TwELL and gathers y in one kernel and leaves no lists in h; call twell_down (which
+ * rebuilds them), not twell_fwd_down, on such an h.
  * Errors: TWELL_ERR_ARG, TWELL_ERR_SHAPE (d, d_ff <= 0, T < 0, d_ff % tile_w, h_out shape
  * mismatch), TWELL_ERR_ALIGN (d % 8), TWELL_ERR_UNSUPPORTED.
  */
@@ -148,8 +152,10 @@ int twell_ffn_fwd(const void *x, const void *w1t, const float *b1, const void *w
                   twell_matrix_t *h_out, void *y, int32_t y_dtype, void *stream);
 
 /*
- * Stages of twell_ffn_fwd, callable one by one (twell_ffn_fwd enqueues exactly
- * twell_up_gemm, twell_up_finish, twell_fwd_down, in that order, on its stream):
+ * Stages of twell_ffn_fwd, callable one by one; run in this order on one stream they give
+ * the TwELL twell_ffn_fwd gives, bit for bit, and y within the sum-order rounding (at the
+ * decode sizes above twell_ffn_fwd runs its own fused kernels, elsewhere it enqueues exactly
+ * these three):
  *   twell_up_gemm   — the up-projection MFMA GEMM with the fused bias + ReLU + TwELL
  *                     epilogue: writes counts, col_idx, vals and ovf_bits only.
  *   twell_up_finish — the overflow bookkeeping ("Formato Híbrido para Treinamento"): the
@@ -172,9 +178,10 @@ int twell_up_finish(const void *x, const void *w1t, const float *b1, int32_t in_
                     int32_t d_model, int32_t d_ff, twell_matrix_t *h, void *stream);
 
 /*
- * twell_fwd_down — the last stage of twell_ffn_fwd: twell_down without rebuilding the row
- * lists, which twell_up_finish left in h on the same stream. Arguments, checks and errors
- * as twell_down. Use twell_down for a TwELL from any other producer.
+ * twell_fwd_down — the last stage: twell_down without rebuilding the row lists, which
+ * twell_up_finish left in h on the same stream. Arguments, checks and errors as twell_down.
+ * Use twell_down for a TwELL from any other producer (twell_ffn_fwd included). Stale lists
+ * give wrong sums but no access outside h's buffers (lengths are clamped to n_t S).
  */
 int twell_fwd_down(const twell_matrix_t *h, const void *w2, int32_t w_dtype, int32_t d_model,
                    void *y, int32_t y_dtype, void *stream);

@@ -261,7 +261,9 @@ def test_fwd_wide_gather(T, d, f, W, S, dt, seed):
                                              (1, 1024, 384, 128, 1, 55), (5, 1024, 1984, 64, 2, 56),
                                              (8, 2048, 2048, 128, 4, 57), (16, 4096, 1024, 128, 16, 58),
                                              (12, 1024, 768, 64, 3, 59), (6, 1280, 1024, 128, 4, 60),
-                                             (9, 512, 1024, 128, 4, 61)])
+                                             (9, 512, 1024, 128, 4, 61), (17, 4096, 1984, 64, 2, 62),
+                                             (64, 4096, 2048, 128, 2, 63), (40, 4352, 1024, 128, 4, 64),
+                                             (33, 4096, 1024, 128, 16, 65)])
 def test_fwd_decode_gemv(T, d, f, W, S, seed):
     """Up to 16 tokens (bf16; d_model 1024 / 2048 / 4096 for 1 or 2 tokens, a multiple of 1024 from
     3 on) the up projection is a W1 stream on one-wave workgroups (v_dot2 for 1 or 2 tokens,
@@ -270,7 +272,8 @@ def test_fwd_decode_gemv(T, d, f, W, S, seed):
     packing bit for bit (that path sums the same halves in one workgroup), the tickets are zero
     after every call, repeated calls give the same bits, and small S sends rows to the dense
     backup (written from the same sums). d_model = 1280 or 512 (not a multiple of 1024) takes
-    the tile kernel (K in quarters)."""
+    the tile kernel (K in quarters), as do 17 to 64 tokens, here with the wide gather (d_model
+    4096 and 4352, 8 and 9 chunks of 1 KB; T = 17 with f = 1984: a half last tile)."""
     say("fwd decode gemv", T, d, f, W, S)
     w = synth.C3.with_(d=d, f=f, tile_w=W, slots=S, seed=seed)
     g = synth.generate(w, T=T)
@@ -311,6 +314,24 @@ def test_fwd_decode_fused_long_lists(T, f, bias, seed):
     assert torch.equal(y1, y2)
     assert_twell_equal(twell_host(h), got)
     assert int(got["counts"].sum()) > 300 * T                 # more than one round per row
+
+
+@pytest.mark.parametrize("T,d,seed", [(1, 4096, 75), (8, 2048, 76)])
+def test_down_after_fused_forward(T, d, seed):
+    """At decode sizes twell_ffn_fwd leaves no row lists in h (they are scratch). twell_down
+    rebuilds them and gives y within rounding of the fused forward's; twell_fwd_down on the
+    never-written lists (random bits here) gives meaningless sums but stays inside h's buffers
+    and W2 (list lengths clamped to n_t S, W2 row reads range-checked)."""
+    say("down after fused fwd", T, d)
+    w = synth.C3.with_(d=d, f=4096, tile_w=128, slots=4, seed=seed)
+    g = synth.generate(w, T=T)
+    x, w1t, b1, w2 = dev_inputs(g)
+    h = garbage_matrix(T, w.f, 128, 4, T, seed)
+    y1, h = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 4, T, h=h)
+    tw.twell_fwd_down(h, w2)
+    y2 = tw.twell_down(h, w2)
+    torch.cuda.synchronize()
+    assert rel_err(from_dev(y2), from_dev(y1)) < 1e-5
 
 
 def test_fwd_hot_tokens_and_capacity():
