@@ -685,19 +685,29 @@ def main():
     ovf_n = int(h.ovf_n.item())
 
     flops_up = 2.0 * T * d * f
-    traffic = counter_traffic(w.name)
+    name = w.name.replace(f"_T{w.T}_", f"_T{T}_")
+    traffic = counter_traffic(name)
     peak = PEAK_BF16_TFLOPS if w.dtype == "bf16" else PEAK_F32_TFLOPS
     achieved = flops_up / (gemm_ms * 1e-3) / 1e12
+    roof = {"kernel": "k_up_twell (up GEMM + fused ReLU/TwELL epilogue)", "bound": "mfma",
+            "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
+            "traffic": traffic, "per_launch_flop": flops_up, "avg_launch_ms": gemm_ms}
+    if T <= 64:
+        # decode sizes: the up stage streams W1 once (plus x and the TwELL it writes)
+        n_t = f // w.tile_w
+        ubytes = f * d * (2 if w.dtype == "bf16" else 4) + T * d * 2 + T * n_t * (4 + 8 * w.slots)
+        gbs = ubytes / (gemm_ms * 1e-3) / 1e9
+        roof = {"kernel": "up stage at decode sizes (W1 stream or decode tile GEMM, then the TwELL pack)",
+                "bound": "hbm", "achieved": gbs, "peak": PEAK_HBM_GBS, "unit": "GB/s", "frac": gbs / PEAK_HBM_GBS,
+                "traffic": traffic, "per_launch_bytes": ubytes, "avg_launch_ms": gemm_ms}
     out = {
         "metric": "FFN tokens/sec at 1% density (TwELL forward), speedup vs dense bf16, % MFMA peak",
         "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": a.steps,
         "warmup": a.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": w.dtype, "data": "synthetic (seeded generator, random-init weights)",
-        "config": {"workload": w.name, "T": T, "d_model": d, "d_ff": f, "tile_w": w.tile_w,
+        "config": {"workload": name, "T": T, "d_model": d, "d_ff": f, "tile_w": w.tile_w,
                    "slots": w.slots, "bias": w.bias, "seed": w.seed, "parallelism": "single GPU"},
-        "roofline": {"kernel": "k_up_twell (up GEMM + fused ReLU/TwELL epilogue)", "bound": "mfma",
-                     "achieved": achieved, "peak": peak, "unit": "TFLOP/s", "frac": achieved / peak,
-                     "traffic": traffic, "per_launch_flop": flops_up, "avg_launch_ms": gemm_ms},
+        "roofline": roof,
         "measured_density": nnz / (T * f), "ovf_rows": ovf_n, "ms_per_step_staged": ms_staged,
     }
 
