@@ -326,21 +326,25 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
   }
 }
 
-// Medium token counts at wide rows: a workgroup of 4 waves owns one (token, chunk of 64
+// Medium token counts at wide rows: a workgroup of NW waves owns one (token, chunk of 64
 // lanes x 16 bytes: 512 bf16 or 256 fp32 columns), so every W2 row piece is one contiguous
 // 1 KB wave load. Chunk c runs on XCD c % 8 as in the other decompositions. Wave w takes
-// entries [64 k + 16 w, 64 k + 16 w + 16) of the token's list, k = 0, 1, ...: lanes 0-15
-// load the sixteen pairs (the first ones speculatively with the count, the next round's while
-// the rows are in flight) and readlane broadcasts them, so the row addresses are scalar.
-// The four wave sums are added in wave order through LDS. A backup row is taken by the
-// four waves as four 16-lane chunks (backup_row).
-template <typename WT, typename VT, typename YT>
-__global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restrict__ w2, int d,
-                                                   YT *__restrict__ y, int nchunk) {
+// entries [NW PE k + PE w, NW PE k + PE w + PE) of the token's list, k = 0, 1, ...: lanes
+// 0 .. PE-1 load the pairs (the first ones speculatively with the count, the next round's
+// while the rows are in flight) and readlane broadcasts them, so the row addresses are
+// scalar. The wave sums are added in wave order through LDS. A backup row is taken by the
+// first four waves as four 16-lane chunks (backup_row).
+constexpr int kWideNW = 8, kWidePE = 4;                 // measured at c3 T = 64, d = 4096
+
+template <typename WT, typename VT, typename YT, int NW, int PE>
+__global__ __launch_bounds__(64 * NW) void k_down_wide(TwellIn h, const WT *__restrict__ w2, int d,
+                                                        YT *__restrict__ y, int nchunk) {
   constexpr int E = Vec16<WT>::N;
   constexpr int CW = 64 * E;
+  constexpr int RW = NW * PE;                               // entries per round
+  static_assert(NW >= 4 && PE <= 64, "shape");
   __shared__ uint2 lst[4][64];
-  __shared__ float red[3][64 * E];
+  __shared__ float red[NW - 1][64 * E];
   const int T = h.rows;
   const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
   const int c = xcd + 8 * (i / T), t = i % T;
@@ -348,12 +352,14 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int cap = h.n_t * h.S;
   const uint2 *src = h.row_list + (size_t)t * cap;
-  const int e0 = 16 * wave + lane;
-  uint2 pn = (lane < 16 && e0 < cap) ? src[e0] : make_uint2(0, 0);
+  const int e0 = PE * wave + lane;
+  uint2 pn = (lane < PE && e0 < cap) ? src[e0] : make_uint2(0, 0);
   const int slot = h.ovf_slot[t], nnz = list_len(h, h.row_nnz[t]);   // one round trip with the list
   if (slot >= 0) {
-    const int cn = 4 * c + wave;                            // this wave's 16-lane chunk
-    if (cn * 16 * E < d) backup_row<WT, VT, YT>(h, w2, d, y, slot, cn, lst[wave]);
+    if (wave < 4) {
+      const int cn = 4 * c + wave;                          // this wave's 16-lane chunk
+      if (cn * 16 * E < d) backup_row<WT, VT, YT>(h, w2, d, y, slot, cn, lst[wave]);
+    }
     return;
   }
   const int col = c * CW + lane * E;
@@ -362,13 +368,13 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int base = 16 * wave; base < nnz; base += 64) {
+  for (int base = PE * wave; base < nnz; base += RW) {
     const uint2 q = pn;
-    const int nb = base + 64;
-    if (nb < nnz) pn = (lane < 16 && nb + lane < nnz) ? src[nb + lane] : make_uint2(0, 0);
-    uint4 raw[16];
-    float vv[16];
-    static_for<16>([&](auto J) {
+    const int nb = base + RW;
+    if (nb < nnz) pn = (lane < PE && nb + lane < nnz) ? src[nb + lane] : make_uint2(0, 0);
+    uint4 raw[PE];
+    float vv[PE];
+    static_for<PE>([&](auto J) {
       constexpr int j = decltype(J)::value;
       const uint32_t ij = (uint32_t)__builtin_amdgcn_readlane((int)q.x, j);
       const float vj = __uint_as_float((uint32_t)__builtin_amdgcn_readlane((int)q.y, j));
@@ -378,7 +384,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
       if (ok && cv) raw[j] = ld16<WT>(rs, ij * (uint32_t)d + (uint32_t)col);
     });
 #pragma unroll
-    for (int j = 0; j < 16; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
+    for (int j = 0; j < PE; ++j) fma16<WT, E>(acc, vv[j], raw[j]);
   }
   if (wave > 0)
 #pragma unroll
@@ -386,7 +392,7 @@ __global__ __launch_bounds__(256) void k_down_wide(TwellIn h, const WT *__restri
   __syncthreads();
   if (wave == 0 && cv) {
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
+    for (int w = 0; w < NW - 1; ++w)
 #pragma unroll
       for (int q = 0; q < E; ++q) acc[q] += red[w][lane * E + q];
     const size_t o = (size_t)t * d + col;
@@ -415,8 +421,8 @@ static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, bool buil
                        h, w2, d, y, nchunk);
   } else if ((d + 64 * Vec16<WT>::N - 1) / (64 * Vec16<WT>::N) >= 8) {
     const int nwide = (d + 64 * Vec16<WT>::N - 1) / (64 * Vec16<WT>::N);
-    hipLaunchKernelGGL((k_down_wide<WT, VT, YT>), dim3((unsigned)(8 * ((nwide + 7) / 8) * h.rows)), dim3(256), 0, s,
-                       h, w2, d, y, nwide);
+    hipLaunchKernelGGL((k_down_wide<WT, VT, YT, kWideNW, kWidePE>), dim3((unsigned)(8 * ((nwide + 7) / 8) * h.rows)),
+                       dim3(64 * kWideNW), 0, s, h, w2, d, y, nwide);
   } else {
     hipLaunchKernelGGL((k_twell_down<WT, VT, YT>), dim3((unsigned)(8 * per_xcd_chunks * h.rows)), dim3(64), 0, s,
                        h, w2, d, y, nchunk);
