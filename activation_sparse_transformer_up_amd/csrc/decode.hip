@@ -19,9 +19,9 @@ namespace tw {
 // A workgroup of kFdThreads threads; a thread holds kFdUPT consecutive units of a segment of
 // kFdThreads kFdUPT units (a whole row at d_ff up to 16384: one round trip for its half sums).
 constexpr int kFdThreads = 1024, kFdUPT = 16, kFdSeg = kFdThreads * kFdUPT;
-// Entries per gather round: the rounds of the split gather (k_down_split), so that a row's
-// products are summed in the same order as there.
-constexpr int kFdLW = 256;
+// Entries per gather round (as in the split gather, k_down_split) and the waves that gather
+// them: group G (16 lanes) of the first kFdGW waves takes entries G, G + 4 kFdGW, ...
+constexpr int kFdLW = 256, kFdGW = 8;
 
 // Grid: 8 ceil(nchunk / 8) M workgroups of kFdThreads threads; workgroup b runs on XCD b % 8 and
 // takes chunk c = b % 8 + 8 ((b / 8) / M) (CW = 16 E columns, E = 16 bytes of W2 elements) of
@@ -31,8 +31,8 @@ constexpr int kFdLW = 256;
 // first), marks the active ones (z > -b1, value z - (-b1) as the TwELL stores it, read back
 // in the value type) and a block scan of the per-thread counts places the active (unit,
 // value) entries, in ascending unit order, after the entries still pending in LDS. Every
-// complete round of kFdLW pending entries is gathered at once by the first four waves (group G
-// of 16 lanes takes entries G, G + 16, ..., all row loads issued before the FMAs), and the rest
+// complete round of kFdLW pending entries is gathered at once by the first kFdGW waves (group G
+// of 16 lanes takes entries G, G + 4 kFdGW, ..., all row loads issued before the FMAs), and the rest
 // moves to the front for the next segment. An overflow row (a tile above S) is gathered the same way from
 // all its active units: the products are those of its dense backup row.
 //
@@ -49,11 +49,11 @@ __global__ __launch_bounds__(kFdThreads) void k_dec_fused_down(const float *__re
                                                         int M, int N, TwellOut o, TwellFinish f,
                                                         const WT *__restrict__ w2, int d, YT *__restrict__ y,
                                                         int nchunk) {
-  constexpr int E = Vec16<WT>::N, CW = 16 * E, NG = 16, PER = kFdLW / NG;
+  constexpr int E = Vec16<WT>::N, CW = 16 * E, NG = 4 * kFdGW, PER = kFdLW / NG;
   constexpr int L = W / kFdUPT;                                // lanes of a tile
   static_assert(W % kFdUPT == 0 && 64 % L == 0 && kFdSeg % W == 0, "tile lanes");
   __shared__ uint2 lst[kFdLW + kFdSeg];
-  __shared__ float red[3][16 * E];
+  __shared__ float red[kFdGW - 1][16 * E];
   __shared__ int wsum[kFdThreads / 64];
   __shared__ int ovf_s, last_s;
   __shared__ int slot_s[16];
@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kFdThreads) void k_dec_fused_down(const float *__re
   const int c = xcd + 8 * (i / M), t = i % M;
   if (c >= nchunk) return;                                     // uniform for the workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const bool gatherer = wave < 4;                              // the 16 groups of the gather
+  const bool gatherer = wave < kFdGW;                          // the NG groups of the gather
   const int G = wave * 4 + (lane >> 4), gl = lane & 15;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
@@ -184,13 +184,13 @@ __global__ __launch_bounds__(kFdThreads) void k_dec_fused_down(const float *__re
     acc[q] += __shfl_xor(acc[q], 16, 64);
     acc[q] += __shfl_xor(acc[q], 32, 64);
   }
-  if (wave > 0 && wave < 4 && lane < 16)
+  if (wave > 0 && wave < kFdGW && lane < 16)
 #pragma unroll
     for (int q = 0; q < E; ++q) red[wave - 1][lane * E + q] = acc[q];
   __syncthreads();
   if (wave == 0 && lane < 16 && cv) {
 #pragma unroll
-    for (int w = 0; w < 3; ++w)
+    for (int w = 0; w < kFdGW - 1; ++w)
 #pragma unroll
       for (int q = 0; q < E; ++q) acc[q] += red[w][lane * E + q];
     store_out_nt<YT, E>(y, (size_t)t * d + col, acc);
