@@ -30,6 +30,7 @@ namespace tw {
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr int kGateEnt = 4;      // list entries per wave and round
+constexpr int kGateDotEnt = 2;   // the same for k_gate_dot (measured at c3 T = 64)
 
 template <typename XT> TW_DEV float dot16(uint4 a, uint4 b, float acc) {
   if constexpr (sizeof(XT) == 2) {
@@ -49,41 +50,42 @@ template <typename XT> TW_DEV float dot16(uint4 a, uint4 b, float acc) {
 // u[k] = x_row . wu[col[k]] for k < ENT (col[k] < 0: no entry, u = 0), summed over the wave.
 // NP 16-byte pieces per lane are in flight at once (NP = 4 covers 2048 bf16 columns; fewer
 // registers than needed for larger rows would cost occupancy for nothing at small d).
-template <typename XT, int NP>
-TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, int d, const int (&col)[kGateEnt],
-                      float (&u)[kGateEnt], int rows) {
+template <typename XT, int NP, int ENT = kGateEnt>
+TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, int d, const int (&col)[ENT],
+                      float (&u)[ENT], int rows) {
   constexpr int EPL = 16 / sizeof(XT);
   const int lane = lane_id();
   const int npc = (d + 64 * EPL - 1) / (64 * EPL);
   const __amdgpu_buffer_rsrc_t rs = rows_rsrc(wu, rows_bytes<XT>(rows, d));
 #pragma unroll
-  for (int k = 0; k < kGateEnt; ++k) u[k] = 0.f;
+  for (int k = 0; k < ENT; ++k) u[k] = 0.f;
   for (int c0 = 0; c0 < npc; c0 += NP) {
-    uint4 xv[NP], wv[kGateEnt][NP];
+    uint4 xv[NP], wv[ENT][NP];
 #pragma unroll
     for (int q = 0; q < NP; ++q) {
       const int i = ((c0 + q) * 64 + lane) * EPL;
       const bool ok = i < d;                                    // d is a multiple of EPL
       xv[q] = ok ? *(const uint4 *)(xrow + i) : make_uint4(0, 0, 0, 0);
 #pragma unroll
-      for (int k = 0; k < kGateEnt; ++k)
+      for (int k = 0; k < ENT; ++k)
         wv[k][q] = (ok && col[k] >= 0) ? ld16<XT>(rs, (uint32_t)col[k] * (uint32_t)d + (uint32_t)i) : make_uint4(0, 0, 0, 0);
     }
 #pragma unroll
     for (int q = 0; q < NP; ++q)
 #pragma unroll
-      for (int k = 0; k < kGateEnt; ++k) u[k] = dot16<XT>(xv[q], wv[k][q], u[k]);
+      for (int k = 0; k < ENT; ++k) u[k] = dot16<XT>(xv[q], wv[k][q], u[k]);
   }
 #pragma unroll
-  for (int k = 0; k < kGateEnt; ++k) u[k] = wave_sumf(u[k]);
+  for (int k = 0; k < ENT; ++k) u[k] = wave_sumf(u[k]);
 }
 
 // Row lists: workgroup (t, p) of 4 waves, numbered p * rows + t; wave w takes the entry
-// groups p * 4 + w, p * 4 + w + 4 P, ... of ENT entries each. Slot p of every token comes
+// groups p * 4 + w, p * 4 + w + 4 P, ... of ENT entries each (ENT = kGateDotEnt: two entries
+// keep 2 NP row pieces per lane in flight, up to 16, and twice as many waves busy as four). Slot p of every token comes
 // before slot p + 1 of any, so the workgroups that have entries (small p; P is sized for
 // the longest possible list) are dispatched first and the empty ones last. Overflow rows
 // are skipped (their backup row carries them).
-template <typename XT, int NP>
+template <typename XT, int NP, int ENT>
 __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restrict__ x, const XT *__restrict__ wu,
                                                   int d, int P) {
   const int t = blockIdx.x % h.rows, p = blockIdx.x / h.rows;
@@ -95,20 +97,20 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
   const int wave = threadIdx.x >> 6, lane = lane_id();
   uint2 *lst = h.row_list + (size_t)t * h.n_t * h.S;
   const XT *xrow = x + (size_t)t * d;
-  for (int e0 = (p * 4 + wave) * kGateEnt; e0 < nnz; e0 += P * 4 * kGateEnt) {
-    int col[kGateEnt];
-    float gv[kGateEnt];
+  for (int e0 = (p * 4 + wave) * ENT; e0 < nnz; e0 += P * 4 * ENT) {
+    int col[ENT];
+    float gv[ENT];
 #pragma unroll
-    for (int k = 0; k < kGateEnt; ++k) {
+    for (int k = 0; k < ENT; ++k) {
       const uint2 en = e0 + k < nnz ? lst[e0 + k] : make_uint2(0xFFFFFFFFu, 0u);
       col[k] = (int)en.x;
       gv[k] = __uint_as_float(en.y);
     }
-    float u[kGateEnt];
-    wave_dots<XT, NP>(xrow, wu, d, col, u, h.cols);
+    float u[ENT];
+    wave_dots<XT, NP, ENT>(xrow, wu, d, col, u, h.cols);
     if (lane == 0)
 #pragma unroll
-      for (int k = 0; k < kGateEnt; ++k)
+      for (int k = 0; k < ENT; ++k)
         if (col[k] >= 0) lst[e0 + k].y = __float_as_uint(gv[k] * u[k]);
   }
 }
@@ -571,7 +573,7 @@ hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int b
   }
   // enough workgroups to keep every CU busy at few tokens, without more entry groups per
   // token than a full list has
-  const int groups = (h.n_t * h.S + 4 * kGateEnt - 1) / (4 * kGateEnt);
+  const int groups = (h.n_t * h.S + 4 * kGateDotEnt - 1) / (4 * kGateDotEnt);
   const int P = max(1, min(groups, (2048 + h.rows - 1) / h.rows));
   const dim3 grid((unsigned)((size_t)h.rows * P));
   const int rstep = min(h.cap, kGateBackupRows);
@@ -579,16 +581,16 @@ hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int b
   const dim3 gridb((unsigned)((nb + 3) / 4));
   if (bf16) {
     const uint16_t *xx = (const uint16_t *)x, *ww = (const uint16_t *)wu;
-    if (d <= 2048) hipLaunchKernelGGL((k_gate_dot<uint16_t, 4>), grid, dim3(256), 0, s, h, xx, ww, d, P);
-    else hipLaunchKernelGGL((k_gate_dot<uint16_t, 8>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    if (d <= 2048) hipLaunchKernelGGL((k_gate_dot<uint16_t, 4, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    else hipLaunchKernelGGL((k_gate_dot<uint16_t, 8, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     if (nb) {
       if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
       else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
     }
   } else {
     const float *xx = (const float *)x, *ww = (const float *)wu;
-    if (d <= 1024) hipLaunchKernelGGL((k_gate_dot<float, 4>), grid, dim3(256), 0, s, h, xx, ww, d, P);
-    else hipLaunchKernelGGL((k_gate_dot<float, 8>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    if (d <= 1024) hipLaunchKernelGGL((k_gate_dot<float, 4, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    else hipLaunchKernelGGL((k_gate_dot<float, 8, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
     if (nb) {
       if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
       else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
