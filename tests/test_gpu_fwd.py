@@ -349,8 +349,11 @@ def test_fwd_hot_tokens_and_capacity():
     assert host["ovf_n"] == got["ovf_n"] and np.array_equal(host["ovf_rows"], got["ovf_rows"][:3])
 
 
-def test_fwd_bf16_output_and_bf16_vals():
-    w = synth.C2.with_(T=256)
+@pytest.mark.parametrize("T", [256, 6])
+def test_fwd_bf16_output_and_bf16_vals(T):
+    """bf16 y and bf16 TwELL values against the fp32 forward on the same inputs (256 tokens: the
+    tile GEMM and the row gather; 6 tokens: the W1 stream and the fused decode kernel)."""
+    w = synth.C2.with_(T=T)
     g = synth.generate(w)
     x, w1t, b1, w2 = dev_inputs(g)
     y32, h32 = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 16, 8)
@@ -366,15 +369,17 @@ def test_fwd_bf16_output_and_bf16_vals():
 @pytest.mark.parametrize("T,d,f,W,S,dt,hot,seed", [(600, 512, 2048, 128, 8, "bf16", 64, 71),
                                                     (8, 1024, 1024, 128, 4, "bf16", 0, 72),
                                                     (70, 256, 512, 64, 4, "f32", 16, 73),
-                                                    (520, 256, 1024, 64, 40, "bf16", 0, 74)])
+                                                    (520, 256, 1024, 64, 40, "bf16", 0, 74),
+                                                    (5, 2048, 2048, 64, 1, "bf16", 2, 75)])
 def test_fwd_bf16_vals_against_oracle(T, d, f, W, S, dt, hot, seed):
     """bf16 TwELL values with an fp32 y, against the oracle: the slots and backup rows equal the
     oracle's packing of the GPU's own activations rounded to bf16 (nearest, ties to even); y is
     within the bf16-input tolerance of the oracle's product of those rounded activations, and
     within the rounding's own bound of the exact dense y (the rounding alone can use the whole
     2e-3: 2.03e-3 was measured on the first case, which is why fp32 values are the default).
-    Hot tokens make rows overflow, so bf16 backup rows are compared too; the last case takes
-    the 4-wave 128 x 128 large tiles (W = 64, S > 32)."""
+    Hot tokens make rows overflow, so bf16 backup rows are compared too; the 520-token case
+    takes the 4-wave 128 x 128 large tiles (W = 64, S > 32), and the 5-token one the decode
+    forward's single kernel after the W1 stream (bf16 slots and backup rows written there)."""
     say("fwd bf16 vals", T, d, f, W, S, dt, hot)
     base = synth.C2 if dt == "bf16" else synth.C1
     w = base.with_(T=T, d=d, f=f, tile_w=W, slots=S, seed=seed, hot_every=hot)
