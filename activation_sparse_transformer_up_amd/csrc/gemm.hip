@@ -528,12 +528,19 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
   const int tiles = min(TPW, o.n_t - kt0);
   if (tiles <= 0) return;
   const int RS = TPW * S;
-  // wave-private LDS: idx [16][RS] + junk[64] | vals [16][RS] + junk[64] | counts [16][TPW] + junk[64]
+  // wave-private LDS at fixed offsets (so that a slot's value sits VOFF bytes after its column
+  // for fp32 values, one address for both stores): idx [16][RS] + junk[64] at 0 | vals
+  // [16][RS] + junk[64] at VOFF | counts [16][TPW] + junk[64] at 2 VOFF. RSX is the largest RS
+  // the wave's EPI_WAVE bytes hold (epi_wave_bytes(RSX / 2, 2, 4)); the host keeps RS <= RSX.
+  constexpr int RSX = (G::EPI_WAVE - 1024) / 128;
+  static_assert(epi_wave_bytes(RSX / 2, 2, 4) == G::EPI_WAVE, "epilogue LDS layout");
+  constexpr int VOFF = 4 * (16 * RSX + 64);
   char *base = smem + wave * G::EPI_WAVE;
   int32_t *lidx = (int32_t *)base;
-  VT *lval = (VT *)(lidx + 16 * RS + 64);
-  int32_t *lcnt = (int32_t *)(base + ((4 * (16 * RS + 64) + (int)sizeof(VT) * (16 * RS + 64) + 15) & ~15));
+  VT *lval = (VT *)(base + VOFF);
+  int32_t *lcnt = (int32_t *)(base + 2 * VOFF);
   const int JI = 16 * RS + lane;
+  const int jaddr = 4 * JI;                                    // this lane's junk word
   const uint32_t below = (1u << li) - 1u;
   const bool vec_ok = (S * (int)sizeof(VT)) % 16 == 0;
   // copy-out positions: the lane's first (row, 16-byte chunk) and the step between its
@@ -545,6 +552,11 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
   const int rv0 = vec_ok ? lane / cv : 0, cv0 = vec_ok ? lane - rv0 * cv : 0;
   const int vq = vec_ok ? 64 / cv : 0, vm = vec_ok ? 64 - vq * cv : 0;
   uint32_t ovfv[TPW];                            // overflow bits of this lane's rows, 32-row word
+  int colv[TPW][BPT];                            // this lane's column in each 16-column block
+#pragma unroll
+  for (int q = 0; q < TPW; ++q)
+#pragma unroll
+    for (int b = 0; b < BPT; ++b) colv[q][b] = (kt0 + q) * W + b * 16 + li;
 #pragma unroll
   for (int fm = 0; fm < G::FM; ++fm) {
     const int rb0 = row0 + fm * 16;
@@ -557,11 +569,13 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
     wave_lds_order();
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
-      const int kt = kt0 + q;
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int lrow = 4 * g + r;                           // row of this lane in the block
-        int pre = 0;
+        // the running slot counts from the word of slot 0 of (row, tile), so a slot's word is
+        // `slot` and the budget test compares with `lim`
+        const int row0w = lrow * RS + q * S, lim = row0w + S;
+        int pre = row0w;
 #pragma unroll
         for (int b = 0; b < BPT; ++b) {
           const int nb = q * BPT + b;
@@ -571,12 +585,13 @@ TW_DEV void epi_twell16(f32x4_t (&acc)[G::FM][G::FN], const float (&nbias)[G::FN
           if (bal == 0) continue;                             // wave-uniform
           const uint32_t hm = (uint32_t)(bal >> (16 * g)) & 0xFFFFu;
           const int slot = pre + __popc(hm & below);
-          const bool act = on && slot < S;
-          const int e = act ? lrow * RS + q * S + slot : JI;
-          lidx[e] = kt * W + b * 16 + li;
-          Elem<VT>::store(lval, e, zb - nbias[nb]);
+          const int a = (on && slot < lim) ? 4 * slot : jaddr;   // byte of the slot's column
+          *(int32_t *)(base + a) = colv[q][b];
+          if constexpr (sizeof(VT) == 4) *(float *)(base + VOFF + a) = zb - nbias[nb];
+          else *(uint16_t *)(base + VOFF + (a >> 1)) = (uint16_t)f32_to_bf16(zb - nbias[nb]);
           pre += __popc(hm);
         }
+        pre -= row0w;
         const int e = li == 0 ? lrow * TPW + q : 16 * TPW + lane;
         lcnt[e] = pre;
         ovfv[q] |= (pre > S ? 1u : 0u) << ((fm & 1) * 16 + lrow);
