@@ -33,10 +33,18 @@ namespace tw {
 
 template <typename VT> TW_DEV float ldv(const VT *p, size_t i) { return Elem<VT>::load(p, i); }
 
-// The compact list of every row (row_list_wave), 16 rows per workgroup.
+// Rows per workgroup of the list kernels: a row is one wave's chain of dependent round trips,
+// so the rows are spread over about one workgroup per CU (at most 16 rows, one per wave; the
+// other waves exit at once). At c3 T = 64 one row per workgroup instead of 16 took the finish
+// from five workgroups to 65 and the forward from 61.9-62.1 to 58.6-59.0 us (same box).
+inline int list_rows_per_wg(int rows) { return std::min(16, std::max(1, (rows + 255) / 256)); }
+
+// The compact list of every row (row_list_wave), rpw rows per workgroup.
 template <typename VT>
-__global__ __launch_bounds__(1024) void k_row_list(TwellIn h) {
-  const int t = blockIdx.x * 16 + (threadIdx.x >> 6);
+__global__ __launch_bounds__(1024) void k_row_list(TwellIn h, int rpw) {
+  const int w = threadIdx.x >> 6;
+  if (w >= rpw) return;
+  const int t = blockIdx.x * rpw + w;
   if (t < h.rows) row_list_wave<VT>(h, t);
 }
 
@@ -45,12 +53,14 @@ __global__ __launch_bounds__(1024) void k_row_list(TwellIn h) {
 // (consumers tell overflow rows by ovf_slot).
 template <typename VT>
 __global__ __launch_bounds__(1024) void k_lists_scan(TwellIn h, const uint32_t *__restrict__ bits, int words,
-                                                     int32_t *ovf_n, int32_t *ovf_rows, int32_t *ovf_slot) {
+                                                     int32_t *ovf_n, int32_t *ovf_rows, int32_t *ovf_slot, int rpw) {
   if (blockIdx.x == 0) {
     ovf_scan_block(bits, h.n_t, words, h.rows, h.cap, ovf_n, ovf_rows, ovf_slot);
     return;
   }
-  const int t = (blockIdx.x - 1) * 16 + (threadIdx.x >> 6);
+  const int w = threadIdx.x >> 6;
+  if (w >= rpw) return;
+  const int t = (blockIdx.x - 1) * rpw + w;
   if (t < h.rows) row_list_wave<VT>(h, t);
 }
 
@@ -409,7 +419,10 @@ static hipError_t down_t(const TwellIn &h, const WT *w2, int d, YT *y, bool buil
   const int nchunk = (d + CW - 1) / CW;
   const size_t per_xcd_chunks = (nchunk + 7) / 8;
   if (h.rows == 0) return hipSuccess;
-  if (build_lists) hipLaunchKernelGGL((k_row_list<VT>), dim3((h.rows + 15) / 16), dim3(1024), 0, s, h);
+  if (build_lists) {
+    const int rpw = list_rows_per_wg(h.rows);
+    hipLaunchKernelGGL((k_row_list<VT>), dim3((h.rows + rpw - 1) / rpw), dim3(1024), 0, s, h, rpw);
+  }
   if (h.rows >= kRows4MinT) {
     const int ntb = (h.rows + 15) / 16;
     const size_t nmain = 8 * per_xcd_chunks * (size_t)ntb;
@@ -452,9 +465,10 @@ hipError_t launch_twell_down(const TwellIn &h, const void *w2, int w_bf16, int d
 
 hipError_t launch_lists_scan(const TwellIn &h, const uint32_t *bits, int words, int32_t *ovf_n, int32_t *ovf_rows,
                             int32_t *ovf_slot, hipStream_t s) {
-  const dim3 grid(1 + (h.rows + 15) / 16);
-  if (h.val_bf16) hipLaunchKernelGGL((k_lists_scan<uint16_t>), grid, dim3(1024), 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot);
-  else hipLaunchKernelGGL((k_lists_scan<float>), grid, dim3(1024), 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot);
+  const int rpw = list_rows_per_wg(h.rows);
+  const dim3 grid(1 + (h.rows + rpw - 1) / rpw);
+  if (h.val_bf16) hipLaunchKernelGGL((k_lists_scan<uint16_t>), grid, dim3(1024), 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot, rpw);
+  else hipLaunchKernelGGL((k_lists_scan<float>), grid, dim3(1024), 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot, rpw);
   return hipGetLastError();
 }
 
