@@ -235,6 +235,10 @@ static int up_finish(const void *x, const void *w1t, const float *b1, int32_t in
                      int32_t d_model, int32_t d_ff, twell_matrix_t *h, hipStream_t s) {
   if (T == 0) return hip_status(launch_set_int(h->ovf_n, 0, s));
   const TwellOut o = out_of(h);
+  const hipError_t fe = launch_finish_dec(in_dtype == TWELL_BF16, in_of(h), h->ovf_bits, o.words, h->ovf_n,
+                                          h->ovf_rows, h->ovf_slot, x, w1t, b1, d_model, h->ovf_dense, s);
+  if (fe == hipSuccess) return TWELL_OK;
+  if (fe != hipErrorNotSupported) return hip_status(fe);
   TW_TRY(launch_lists_scan(in_of(h), h->ovf_bits, o.words, h->ovf_n, h->ovf_rows, h->ovf_slot, s));
   if (h->ovf_cap > 0) {
     const int M = h->ovf_cap < T ? h->ovf_cap : T;

@@ -33,12 +33,6 @@ namespace tw {
 
 template <typename VT> TW_DEV float ldv(const VT *p, size_t i) { return Elem<VT>::load(p, i); }
 
-// Rows per workgroup of the list kernels: a row is one wave's chain of dependent round trips,
-// so the rows are spread over about one workgroup per CU (at most 16 rows, one per wave; the
-// other waves exit at once). At c3 T = 64 one row per workgroup instead of 16 took the finish
-// from five workgroups to 65 and the forward from 61.9-62.1 to 58.6-59.0 us (same box).
-inline int list_rows_per_wg(int rows) { return std::min(16, std::max(1, (rows + 255) / 256)); }
-
 // The compact list of every row (row_list_wave), rpw rows per workgroup.
 template <typename VT>
 __global__ __launch_bounds__(1024) void k_row_list(TwellIn h, int rpw) {

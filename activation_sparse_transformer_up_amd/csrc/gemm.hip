@@ -25,6 +25,7 @@
 #include "common.h"
 #include "launch.h"
 #include "nmsel.h"
+#include "rows.h"
 #include "stage.h"
 
 namespace tw {
@@ -1140,17 +1141,13 @@ __global__ __launch_bounds__(128) void k_up_twell_dec(const T *__restrict__ x, c
 typedef Tile<64, 128, 64, 128, 0, 3> TileDQ;
 static_assert(4 * TileDQ::LDS_BYTES <= 160 * 1024 && 2 * kDecTileF * 4 <= 4 * TileDQ::LDS_BYTES, "LDS");
 
+// One 128-column tile of the dense rows arow[i], i < rows (x row arow[i] if arow, else i): four
+// waves, wave w on quarter w of K through its own ring, then (q0 + q1) + (q2 + q3) through LDS and
+// the dense epilogue by wave 0. Waves 4 and up of a larger workgroup must have exited.
 template <typename T>
-__global__ __launch_bounds__(256) void k_up_dense_dec(const T *__restrict__ x, const T *__restrict__ w1t,
-                                                      const float *__restrict__ b1, int M, int N, int K, int x_rows,
-                                                      const int32_t *__restrict__ arow,
-                                                      const int32_t *__restrict__ n_rows_dev, void *out,
-                                                      int out_bf16, int relu) {
-  __shared__ __attribute__((aligned(16))) char smem[4 * TileDQ::LDS_BYTES];
-  const int n0 = blockIdx.x * TileDQ::BN;
-  int rows = M;
-  if (n_rows_dev) rows = min(rows, *n_rows_dev);
-  if (rows <= 0) return;
+TW_DEV void dense_dec_tile(const T *__restrict__ x, const T *__restrict__ w1t, const float *__restrict__ b1, int rows,
+                           int N, int K, int x_rows, const int32_t *arow, int n0, void *out, int out_bf16, int relu,
+                           char *smem) {
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int kq = K / 4;
   f32x16_t acc[TileD::MB][TileD::NB];
@@ -1172,6 +1169,83 @@ __global__ __launch_bounds__(256) void k_up_dense_dec(const T *__restrict__ x, c
   epi_dense<TileD>(acc, b1, rows, N, 0, n0, out, out_bf16, relu);
 }
 
+template <typename T>
+__global__ __launch_bounds__(256) void k_up_dense_dec(const T *__restrict__ x, const T *__restrict__ w1t,
+                                                      const float *__restrict__ b1, int M, int N, int K, int x_rows,
+                                                      const int32_t *__restrict__ arow,
+                                                      const int32_t *__restrict__ n_rows_dev, void *out,
+                                                      int out_bf16, int relu) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * TileDQ::LDS_BYTES];
+  int rows = M;
+  if (n_rows_dev) rows = min(rows, *n_rows_dev);
+  if (rows <= 0) return;
+  dense_dec_tile<T>(x, w1t, b1, rows, N, K, x_rows, arow, blockIdx.x * TileDQ::BN, out, out_bf16, relu, smem);
+}
+
+// The finish of at most 64 rows after the decode tile GEMM, with the backup recompute in the
+// same launch, in workgroups of four waves. Every workgroup that needs them finds the overflow
+// rows from the overflow words itself (bit t % 32 of word t / 32 of any tile; at most 64 rows),
+// ranked in ascending row order and cut at cap, which is the order of the overflow scan
+// (ovf_scan_block). Workgroup 0 writes that scan (ovf_slot, ovf_rows, ovf_n); workgroups 1 ..
+// nlist build one row list each (row_list_wave); workgroup 1 + nlist + i recomputes tile i of the
+// backup rows ReLU(x W1 + b1) exactly as k_up_dense_dec does, so it waits for nothing, and with
+// no overflow row it exits after the one read of the words.
+template <typename T, typename VT>
+__global__ __launch_bounds__(256) void k_finish_dec(TwellIn h, const uint32_t *__restrict__ bits, int words,
+                                                    int32_t *ovf_n, int32_t *ovf_rows, int32_t *ovf_slot, int nlist,
+                                                    const T *__restrict__ x, const T *__restrict__ w1t,
+                                                    const float *__restrict__ b1, int K, void *dense, int dense_bf16) {
+  __shared__ __attribute__((aligned(16))) char smem[4 * TileDQ::LDS_BYTES];
+  __shared__ int32_t rows_s[64];
+  __shared__ uint32_t ow[2];
+  __shared__ int nr_s;
+  const int b = blockIdx.x, tid = threadIdx.x;
+  if (b >= 1 && b <= nlist) {
+    if (tid >= 64) return;
+    if (b - 1 < h.rows) row_list_wave<VT>(h, b - 1);
+    return;
+  }
+  if (b > nlist && h.cap <= 0) return;                         // uniform: no backup rows
+  // The words of all tiles, read as one flat run (word i belongs to row word i % words), OR-ed
+  // into ow: four clamped loads in flight per lane.
+  if (tid < 2) ow[tid] = 0u;
+  __syncthreads();
+  const int nw = h.n_t * words;
+  uint32_t f0 = 0, f1 = 0;
+  for (int i0 = tid; i0 < nw; i0 += 4 * 256) {
+    uint32_t v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = bits[min(i0 + u * 256, nw - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int i = i0 + u * 256;
+      if (i < nw && i % words == 0) f0 |= v[u];
+      if (i < nw && i % words == 1) f1 |= v[u];
+    }
+  }
+  if (f0) atomicOr(&ow[0], f0);
+  if (f1) atomicOr(&ow[1], f1);
+  __syncthreads();
+  if (tid < 64) {
+    const bool on = tid < h.rows && ((ow[tid >> 5] >> (tid & 31)) & 1u);
+    const uint64_t m = ballot64(on);
+    const int rank = __popcll(m & ((1ull << tid) - 1ull));
+    const int slot = on && rank < h.cap ? rank : -1;
+    if (slot >= 0) rows_s[slot] = tid;
+    if (tid == 0) nr_s = min(__popcll(m), h.cap);
+    if (b == 0) {                                              // the overflow scan's outputs
+      if (tid < h.rows) ovf_slot[tid] = slot;
+      if (slot >= 0) ovf_rows[slot] = tid;
+      if (tid == 0) *ovf_n = __popcll(m);
+    }
+  }
+  if (b == 0) return;
+  __syncthreads();
+  const int nr = nr_s;
+  if (nr == 0) return;                                         // uniform
+  dense_dec_tile<T>(x, w1t, b1, nr, h.cols, K, h.rows, rows_s, (b - 1 - nlist) * TileDQ::BN, dense, dense_bf16, 1,
+                    smem);
+}
 // h = ReLU(x W1 + b1) pruned to NK:M inside the up GEMM (N:M epilogue above). The tiles,
 // loops and accumulation order are those of k_up_dense for the same problem, so z is the
 // same bit for bit.
@@ -1964,6 +2038,37 @@ static hipError_t launch_dense_dec(const T *x, const T *w1t, const float *b1, in
   const dim3 grid((N + TileDQ::BN - 1) / TileDQ::BN);
   hipLaunchKernelGGL((k_up_dense_dec<T>), grid, dim3(256), 0, s, x, w1t, b1, M, N, K, x_rows, arow, n_rows_dev, out,
                      out_bf16, relu);
+  return hipGetLastError();
+}
+
+// The finish of at most 64 tokens after the decode tile GEMM (use_decode) in one launch, or
+// hipErrorNotSupported where the recompute would take another kernel (then the caller launches
+// the scan and the recompute separately).
+hipError_t launch_finish_dec(int bf16, const TwellIn &h, const uint32_t *bits, int words, int32_t *ovf_n,
+                             int32_t *ovf_rows, int32_t *ovf_slot, const void *x, const void *w1t, const float *b1,
+                             int K, void *dense, hipStream_t s) {
+  const int T = h.rows;
+  if (T < 1 || T > 64 || words > 2 || use_gemv(bf16, T, K) || use_mstream(bf16, T, K) ||
+      !(bf16 ? use_decode<uint16_t>(T, K) : use_decode<float>(T, K)))
+    return hipErrorNotSupported;
+  const int nlist = T;                                          // one row list per workgroup
+  const int n_tiles = (h.cols + TileDQ::BN - 1) / TileDQ::BN;
+  const dim3 grid(1 + nlist + n_tiles), blk(256);
+  if (bf16) {
+    if (h.val_bf16)
+      hipLaunchKernelGGL((k_finish_dec<uint16_t, uint16_t>), grid, blk, 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot,
+                         nlist, (const uint16_t *)x, (const uint16_t *)w1t, b1, K, dense, 1);
+    else
+      hipLaunchKernelGGL((k_finish_dec<uint16_t, float>), grid, blk, 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot,
+                         nlist, (const uint16_t *)x, (const uint16_t *)w1t, b1, K, dense, 0);
+  } else {
+    if (h.val_bf16)
+      hipLaunchKernelGGL((k_finish_dec<float, uint16_t>), grid, blk, 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot,
+                         nlist, (const float *)x, (const float *)w1t, b1, K, dense, 1);
+    else
+      hipLaunchKernelGGL((k_finish_dec<float, float>), grid, blk, 0, s, h, bits, words, ovf_n, ovf_rows, ovf_slot,
+                         nlist, (const float *)x, (const float *)w1t, b1, K, dense, 0);
+  }
   return hipGetLastError();
 }
 

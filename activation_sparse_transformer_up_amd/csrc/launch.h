@@ -145,5 +145,10 @@ hipError_t launch_twell_down(const TwellIn &h, const void *w2, int w_bf16, int d
 // overflow scan + row lists in one launch (the finish step of the fused forward)
 hipError_t launch_lists_scan(const TwellIn &h, const uint32_t *bits, int words, int32_t *ovf_n, int32_t *ovf_rows,
                              int32_t *ovf_slot, hipStream_t s);
+// gemm.hip: the same finish plus the backup recompute in one launch, for at most 64 tokens on
+// the decode tile GEMM; hipErrorNotSupported elsewhere
+hipError_t launch_finish_dec(int bf16, const TwellIn &h, const uint32_t *bits, int words, int32_t *ovf_n,
+                             int32_t *ovf_rows, int32_t *ovf_slot, const void *x, const void *w1t, const float *b1,
+                             int K, void *dense, hipStream_t s);
 
 }  // namespace tw

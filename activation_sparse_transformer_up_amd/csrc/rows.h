@@ -22,6 +22,12 @@ namespace tw {
 // rounds of 64 entries are all issued before their stores.
 constexpr int kListRounds = 4;
 
+// Rows per workgroup of the list kernels: a row is one wave's chain of dependent round trips,
+// so the rows are spread over about one workgroup per CU (at most 16 rows, one per wave; the
+// other waves exit at once). At c3 T = 64 one row per workgroup instead of 16 took the finish
+// from five workgroups to 65 and the forward from 61.9-62.1 to 58.6-59.0 us (same box).
+inline int list_rows_per_wg(int rows) { return rows < 256 ? 1 : (rows > 16 * 256 ? 16 : (rows + 255) / 256); }
+
 // COH: the lists and lengths are written with agent-scope atomic stores, which reach the
 // memory side directly, so that other XCDs can read them later in the same kernel.
 template <typename VT, bool COH = false>
