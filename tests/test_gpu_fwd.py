@@ -156,7 +156,8 @@ def test_fwd_c1():
 
 
 @pytest.mark.parametrize("T,d,f,W,S,dt", [(300, 256, 1024, 128, 4, "bf16"), (64, 128, 512, 64, 2, "f32"),
-                                          (777, 512, 2048, 128, 8, "bf16"), (5, 64, 256, 64, 3, "bf16")])
+                                          (777, 512, 2048, 128, 8, "bf16"), (5, 64, 256, 64, 3, "bf16"),
+                                          (200, 128, 640, 64, 2, "f32")])
 def test_fwd_integer_grid_exact(T, d, f, W, S, dt):
     say("fwd integer grid", T, d, f, W, S, dt)
     g = synth.integer_grid(T, d, f, seed=3 * T + 1, dtype=dt, active=0.05)
