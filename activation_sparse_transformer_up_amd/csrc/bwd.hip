@@ -252,7 +252,8 @@ __global__ __launch_bounds__(256) void k_sddmm_part(int T_rows, int d, int nchun
 }
 
 // dz[e] = (sum over chunks c of part[c][e], in chunk order) + l1, stored as (col[e], dz),
-// for the row_ptr[T] entries in use (grid-stride over a fixed grid).
+// for the row_ptr[T] entries in use (grid-stride over a fixed grid). Each thread has the loads
+// of 16 chunks in flight (clamped to valid addresses) before it adds them in order.
 __global__ __launch_bounds__(256) void k_sddmm_sum(int T_rows, const int32_t *__restrict__ row_ptr, size_t nz,
                                                    int nchunk, const float *__restrict__ part,
                                                    const int32_t *__restrict__ col, float l1,
@@ -261,7 +262,14 @@ __global__ __launch_bounds__(256) void k_sddmm_sum(int T_rows, const int32_t *__
   if (total > nz) return;
   for (size_t e = (size_t)blockIdx.x * 256 + threadIdx.x; e < total; e += (size_t)gridDim.x * 256) {
     float s = 0.f;
-    for (int c = 0; c < nchunk; ++c) s += part[(size_t)c * nz + e];
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = part[(size_t)min(c0 + j, nchunk - 1) * nz + e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (c0 + j < nchunk) s += v[j];
+    }
     dz[e] = make_uint2((uint32_t)col[e], __float_as_uint(s + l1));
   }
 }

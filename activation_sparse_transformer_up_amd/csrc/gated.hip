@@ -221,7 +221,8 @@ __global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk,
 }
 
 // Row list entry e of token t: g <- g * (sum over chunks c of part[c][t][e], in chunk order).
-// One wave per token, lanes over the entries.
+// One wave per token, lanes over the entries; each lane has the loads of 16 chunks in flight
+// (clamped to valid addresses) before it adds them in order.
 __global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const float *__restrict__ part) {
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= h.rows) return;
@@ -231,7 +232,14 @@ __global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const f
   const float *pp = part + (size_t)t * cap;
   for (int e = lane_id(); e < n; e += 64) {
     float u = 0.f;
-    for (int c = 0; c < nchunk; ++c) u += pp[c * plane + e];
+    for (int c0 = 0; c0 < nchunk; c0 += 16) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) v[j] = pp[(size_t)min(c0 + j, nchunk - 1) * plane + e];
+#pragma unroll
+      for (int j = 0; j < 16; ++j)
+        if (c0 + j < nchunk) u += v[j];
+    }
     const uint2 q = lp[e];
     lp[e].y = __float_as_uint(__uint_as_float(q.y) * u);
   }
