@@ -295,6 +295,30 @@ def test_fwd_decode_gemv(T, d, f, W, S, seed):
         assert got["ovf_n"] > 0
 
 
+@pytest.mark.parametrize("T,cap", [(40, 5), (64, 1)])
+def test_fwd_decode_capacity(T, cap):
+    """17 to 64 tokens on the decode tile path with more overflow rows than backup slots: the
+    one-launch finish keeps the first cap overflow rows in ascending row order, gives the others
+    no slot and reports the true count, and the kept backup rows equal those of a call with a
+    slot for every row (the same tile computes them)."""
+    say("fwd decode capacity", T, cap)
+    w = synth.C3.with_(d=1024, f=2048, tile_w=128, slots=2, seed=90 + T)
+    g = synth.generate(w, T=T)
+    got, flips, err = check_forward(g, 128, 2, T)
+    assert got["ovf_n"] > cap
+    x, w1t, b1, w2 = dev_inputs(g)
+    y, h = tw.twell_ffn_fwd(x, w1t, b1, w2, 128, 2, cap)
+    assert tw.twell_sync_status(h) == -5
+    host = twell_host(h)
+    assert host["ovf_n"] == got["ovf_n"]
+    assert np.array_equal(host["ovf_rows"], got["ovf_rows"][:cap])
+    want_slot = np.where(got["ovf_slot"] < cap, got["ovf_slot"], -1)
+    assert np.array_equal(host["ovf_slot"], want_slot)
+    assert np.array_equal(host["ovf_dense"], got["ovf_dense"][:cap])
+    for key in ("counts", "col_idx", "vals"):
+        assert np.array_equal(host[key], got[key])
+
+
 @pytest.mark.parametrize("T,f,bias,seed", [(1, 20480, -1.2, 71), (7, 20480, -1.2, 72), (3, 16512, -2.0, 73)])
 def test_fwd_decode_fused_long_lists(T, f, bias, seed):
     """Up to 16 bf16 tokens the forward after the W1 stream is one kernel that rebuilds each
