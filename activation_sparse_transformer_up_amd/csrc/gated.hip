@@ -86,9 +86,8 @@ TW_DEV void wave_dots(const XT *__restrict__ xrow, const XT *__restrict__ wu, in
 // the longest possible list) are dispatched first and the empty ones last. Overflow rows
 // are skipped (their backup row carries them).
 template <typename XT, int NP, int ENT>
-__global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restrict__ x, const XT *__restrict__ wu,
-                                                  int d, int P) {
-  const int t = blockIdx.x % h.rows, p = blockIdx.x / h.rows;
+TW_DEV void gate_dot_wg(const TwellIn &h, const XT *__restrict__ x, const XT *__restrict__ wu, int d, int P, int b) {
+  const int t = b % h.rows, p = b / h.rows;
   if (p >= P) return;
   // the overflow flag and the list length in one round trip, each entry's (column, gate)
   // pair in one load: the gate is kept for the final product instead of being re-read
@@ -115,6 +114,12 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
   }
 }
 
+template <typename XT, int NP, int ENT>
+__global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restrict__ x, const XT *__restrict__ wu,
+                                                  int d, int P) {
+  gate_dot_wg<XT, NP, ENT>(h, x, wu, d, P, blockIdx.x);
+}
+
 // Backup rows: wave (r0, blk) takes the 64-column block blk of the overflow rows r0,
 // r0 + rstep, ... below min(ovf_n, cap); the block's nonzero gates are taken ENT at a time
 // in ascending column order. The grid covers rstep = min(cap, kGateBackupRows) rows, not the
@@ -122,10 +127,9 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
 // most of a capacity-sized grid would start only to exit.
 constexpr int kGateBackupRows = 8;
 
-template <typename XT, typename VT>
-__global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__restrict__ x,
-                                                         const XT *__restrict__ wu, int d, int rstep) {
-  const int wave_g = blockIdx.x * 4 + (threadIdx.x >> 6);
+template <typename XT, typename VT, int NP, int ENT>
+TW_DEV void gate_backup_wave(const TwellIn &h, const XT *__restrict__ x, const XT *__restrict__ wu, int d, int rstep,
+                             int wave_g) {
   const int nblk = (h.cols + 63) / 64;
   const int r0 = wave_g / nblk, blk = wave_g % nblk;
   if (r0 >= rstep) return;                                      // past the grid's rows
@@ -138,21 +142,39 @@ __global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__
     const float g = j < h.cols ? Elem<VT>::load(row, j) : 0.f;
     uint64_t m = ballot64(g != 0.f);
     while (m) {
-      int col[kGateEnt];
+      int col[ENT];
 #pragma unroll
-      for (int k = 0; k < kGateEnt; ++k) {
+      for (int k = 0; k < ENT; ++k) {
         col[k] = m ? blk * 64 + (int)__builtin_ctzll(m) : -1;
         m &= m ? m - 1 : 0;
       }
-      float u[kGateEnt];
-      wave_dots<XT, 8>(x + (size_t)t * d, wu, d, col, u, h.cols);
+      float u[ENT];
+      wave_dots<XT, NP, ENT>(x + (size_t)t * d, wu, d, col, u, h.cols);
 #pragma unroll
-      for (int k = 0; k < kGateEnt; ++k) {
+      for (int k = 0; k < ENT; ++k) {
         const float gk = __shfl(g, col[k] & 63, 64);
         if (lane == 0 && col[k] >= 0) Elem<VT>::store(row, col[k], gk * u[k]);
       }
     }
   }
+}
+
+template <typename XT, typename VT>
+__global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__restrict__ x,
+                                                         const XT *__restrict__ wu, int d, int rstep) {
+  gate_backup_wave<XT, VT, 8, kGateEnt>(h, x, wu, d, rstep, blockIdx.x * 4 + (threadIdx.x >> 6));
+}
+
+// k_gate_dot and the backup rows in one launch: workgroups 0 .. nA - 1 run k_gate_dot, the
+// others the backup rows at k_gate_dot's shape (NP pieces per lane, ENT entries per round; the
+// per-entry sums do not depend on either), so the backup needs no launch of its own when, as
+// usual, no row overflowed.
+template <typename XT, int NP, int ENT, typename VT>
+__global__ __launch_bounds__(256) void k_gate_dot_all(TwellIn h, const XT *__restrict__ x, const XT *__restrict__ wu,
+                                                      int d, int P, int nA, int rstep) {
+  const int b = blockIdx.x;
+  if (b < nA) gate_dot_wg<XT, NP, ENT>(h, x, wu, d, P, b);
+  else gate_backup_wave<XT, VT, NP, ENT>(h, x, wu, d, rstep, (b - nA) * 4 + (threadIdx.x >> 6));
 }
 
 // part[c][t][e] = x[t][chunk c] . wu[col][chunk c] for the entries e of token t's row list
@@ -587,21 +609,47 @@ hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int b
   const int rstep = min(h.cap, kGateBackupRows);
   const size_t nb = (size_t)rstep * ((h.cols + 63) / 64);
   const dim3 gridb((unsigned)((nb + 3) / 4));
+  const int nA = (int)grid.x;
+  const dim3 gall((unsigned)(nA + gridb.x));
   if (bf16) {
     const uint16_t *xx = (const uint16_t *)x, *ww = (const uint16_t *)wu;
-    if (d <= 2048) hipLaunchKernelGGL((k_gate_dot<uint16_t, 4, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
-    else hipLaunchKernelGGL((k_gate_dot<uint16_t, 8, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
-    if (nb) {
-      if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
-      else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+    if (!nb) {
+      if (d <= 2048) hipLaunchKernelGGL((k_gate_dot<uint16_t, 4, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+      else hipLaunchKernelGGL((k_gate_dot<uint16_t, 8, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    } else if (d <= 2048) {
+      if (h.val_bf16)
+        hipLaunchKernelGGL((k_gate_dot_all<uint16_t, 4, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, xx, ww, d, P,
+                           nA, rstep);
+      else
+        hipLaunchKernelGGL((k_gate_dot_all<uint16_t, 4, kGateDotEnt, float>), gall, dim3(256), 0, s, h, xx, ww, d, P, nA,
+                           rstep);
+    } else {
+      if (h.val_bf16)
+        hipLaunchKernelGGL((k_gate_dot_all<uint16_t, 8, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, xx, ww, d, P,
+                           nA, rstep);
+      else
+        hipLaunchKernelGGL((k_gate_dot_all<uint16_t, 8, kGateDotEnt, float>), gall, dim3(256), 0, s, h, xx, ww, d, P, nA,
+                           rstep);
     }
   } else {
     const float *xx = (const float *)x, *ww = (const float *)wu;
-    if (d <= 1024) hipLaunchKernelGGL((k_gate_dot<float, 4, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
-    else hipLaunchKernelGGL((k_gate_dot<float, 8, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
-    if (nb) {
-      if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
-      else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+    if (!nb) {
+      if (d <= 1024) hipLaunchKernelGGL((k_gate_dot<float, 4, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+      else hipLaunchKernelGGL((k_gate_dot<float, 8, kGateDotEnt>), grid, dim3(256), 0, s, h, xx, ww, d, P);
+    } else if (d <= 1024) {
+      if (h.val_bf16)
+        hipLaunchKernelGGL((k_gate_dot_all<float, 4, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, xx, ww, d, P, nA,
+                           rstep);
+      else
+        hipLaunchKernelGGL((k_gate_dot_all<float, 4, kGateDotEnt, float>), gall, dim3(256), 0, s, h, xx, ww, d, P, nA,
+                           rstep);
+    } else {
+      if (h.val_bf16)
+        hipLaunchKernelGGL((k_gate_dot_all<float, 8, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, xx, ww, d, P, nA,
+                           rstep);
+      else
+        hipLaunchKernelGGL((k_gate_dot_all<float, 8, kGateDotEnt, float>), gall, dim3(256), 0, s, h, xx, ww, d, P, nA,
+                           rstep);
     }
   }
   return hipGetLastError();
