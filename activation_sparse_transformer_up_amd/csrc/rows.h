@@ -28,10 +28,74 @@ constexpr int kListRounds = 4;
 // from five workgroups to 65 and the forward from 61.9-62.1 to 58.6-59.0 us (same box).
 inline int list_rows_per_wg(int rows) { return rows < 256 ? 1 : (rows > 16 * 256 ? 16 : (rows + 255) / 256); }
 
+// Stores of one list entry and of the list length (COH: agent-scope atomic stores).
+template <bool COH> TW_DEV void list_store(uint2 *out, int e, uint32_t c, uint32_t v) {
+  if constexpr (COH)
+    __hip_atomic_store((uint64_t *)(out + e), (uint64_t)c | ((uint64_t)v << 32), __ATOMIC_RELAXED,
+                       __HIP_MEMORY_SCOPE_AGENT);
+  else
+    out[e] = make_uint2(c, v);
+}
+
+// The same list for rows of 65 to 128 tiles in one pass: both chunks' counts are loaded and
+// scanned together (lane k holds tiles k and 64 + k), and entries of both chunks share the
+// rounds of slot loads, so the second chunk's slots do not wait for the first chunk's.
+// Entry e < tot0 lies in chunk 0, the others in chunk 1; each lane searches its chunk's
+// prefix (both are shuffled at every step, the lane keeps its own).
+template <typename VT, bool COH>
+TW_DEV void row_list_wave2(const TwellIn &h, int t) {
+  const int lane = lane_id();
+  const int S = h.S, n_t = h.n_t;
+  uint2 *out = h.row_list + (size_t)t * n_t * S;
+  const VT *vals = (const VT *)h.vals;
+  const int32_t *cnt = h.counts + (size_t)t * n_t;
+  const int c0 = cnt[lane], c1 = cnt[64 + lane < n_t ? 64 + lane : n_t - 1];
+  const int m0 = min(c0, S), m1 = 64 + lane < n_t ? min(c1, S) : 0;
+  int tot0, tot1;
+  const int off0 = wave_excl_scan(m0, &tot0);
+  const int off1 = wave_excl_scan(m1, &tot1);
+  const int tot = tot0 + tot1;
+  const size_t rb = (size_t)t * n_t * S;                       // slot 0 of tile 0
+  for (int e0 = 0; e0 < tot; e0 += kListRounds * 64) {
+    uint32_t ci[kListRounds], cv[kListRounds];
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r) {
+      const int e = e0 + r * 64 + lane;
+      const bool in1 = e >= tot0;
+      const int ee = in1 ? e - tot0 : e;
+      int lo = 0;                                               // last tile of the chunk with off <= ee
+#pragma unroll
+      for (int step = 32; step > 0; step >>= 1) {
+        const int o0 = __shfl(off0, lo + step, 64), o1 = __shfl(off1, lo + step, 64);
+        const int o = in1 ? o1 : o0;
+        lo = (lo + step < 64 && o <= ee) ? lo + step : lo;
+      }
+      const int b0 = __shfl(off0, lo, 64), b1 = __shfl(off1, lo, 64);
+      const int tile = (in1 ? 64 : 0) + lo;
+      const size_t si = rb + (e < tot ? (size_t)tile * S + (ee - (in1 ? b1 : b0)) : 0);
+      ci[r] = (uint32_t)h.col_idx[si];
+      cv[r] = __float_as_uint(Elem<VT>::load(vals, si));
+    }
+#pragma unroll
+    for (int r = 0; r < kListRounds; ++r) {
+      const int e = e0 + r * 64 + lane;
+      if (e < tot) list_store<COH>(out, e, ci[r], cv[r]);
+    }
+  }
+  if (lane == 0) {
+    if constexpr (COH) __hip_atomic_store(h.row_nnz + t, tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    else h.row_nnz[t] = tot;
+  }
+}
+
 // COH: the lists and lengths are written with agent-scope atomic stores, which reach the
 // memory side directly, so that other XCDs can read them later in the same kernel.
 template <typename VT, bool COH = false>
 TW_DEV void row_list_wave(const TwellIn &h, int t) {
+  if (h.n_t > 64 && h.n_t <= 128) {                            // wave-uniform
+    row_list_wave2<VT, COH>(h, t);
+    return;
+  }
   const int lane = lane_id();
   const int S = h.S;
   const size_t stride = (size_t)h.n_t * S;

@@ -169,6 +169,23 @@ def test_fwd_integer_grid_exact(T, d, f, W, S, dt):
     assert got["ovf_n"] > 0
 
 
+@pytest.mark.parametrize("T,d,f,W,dt", [(100, 256, 12288, 128, "bf16"), (90, 128, 6144, 64, "f32")])
+def test_fwd_long_lists_two_chunks(T, d, f, W, dt):
+    """Rows of 65 to 128 tiles (96 here) are listed in one pass over both 64-tile chunks; at
+    5% density with S = 16 a row keeps 200 to 760 entries, up to three rounds of 256 that
+    cross the chunk boundary, and no row overflows, so the lists (not the backup rows) carry
+    y. Exact on the integer grid."""
+    say("fwd long lists", T, d, f, W, dt)
+    g = synth.integer_grid(T, d, f, seed=7 * T + 5, dtype=dt, active=0.05)
+    got, flips, err = check_forward(g, W, 16, T, ambiguity=False)
+    kept = np.minimum(got["counts"], 16).sum(axis=1)
+    normal = got["ovf_slot"] < 0
+    assert normal.sum() > T // 2 and kept[normal].max() > 256
+    xr, w1r, b1r, w2r, _ = inputs64(g)
+    h_ref = orc.relu(orc.preact(xr, w1r, b1r))
+    assert_twell_equal(got, orc.twell_pack(h_ref, W, 16, T))
+
+
 def test_fwd_c2_full():
     say("fwd c2 full")
     w = synth.C2
