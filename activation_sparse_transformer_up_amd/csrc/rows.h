@@ -19,7 +19,8 @@ namespace tw {
 // loads and one coalesced 8-byte store per 64 entries, instead of one wave load per tile
 // group and slot. The row is a chain of dependent memory round trips, so the next chunk's
 // counts are loaded before this chunk's stores, and the slot loads of up to kListRounds
-// rounds of 64 entries are all issued before their stores.
+// rounds of 64 entries are all issued before their stores. Rows of 65 to 128 tiles take both
+// chunks in one pass (row_list_wave2).
 constexpr int kListRounds = 4;
 
 // Rows per workgroup of the list kernels: a row is one wave's chain of dependent round trips,
