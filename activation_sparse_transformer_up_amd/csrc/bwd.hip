@@ -80,36 +80,43 @@ __global__ __launch_bounds__(256) void k_row_nnz(TwellIn h, int32_t *__restrict_
 
 // out[i] = in[0] + ... + in[i-1] for i <= n (out may alias in). One workgroup.
 __global__ __launch_bounds__(1024) void k_scan_excl(const int32_t *in, int n, int32_t *out) {
-  constexpr int IPT = 8;
+  // wave w of a chunk covers values base + w 1024 + i 64 + lane (i < 16): every load and store
+  // is one coalesced 256-byte row per wave; the 16 rows are scanned in order with a running
+  // carry. Every value of a chunk is read before the barrier that precedes its stores (in may
+  // be out).
+  constexpr int IPT = 16;
   __shared__ int wsum[16];
   __shared__ int carry_s;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   if (tid == 0) carry_s = 0;
   __syncthreads();
   for (int base = 0; base < n; base += 1024 * IPT) {
+    const int wb = base + wave * 64 * IPT;
     int v[IPT];
-    int local = 0;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      const int idx = base + tid * IPT + i;
+      const int idx = wb + i * 64 + lane;
       v[i] = idx < n ? in[idx] : 0;
-      local += v[i];
     }
-    int tot;
-    const int ex = wave_excl_scan(local, &tot);
-    if (lane == 0) wsum[wave] = tot;
+    int ex[IPT], run = 0;
+#pragma unroll
+    for (int i = 0; i < IPT; ++i) {
+      int tot;
+      ex[i] = run + wave_excl_scan(v[i], &tot);
+      run += tot;
+    }
+    if (lane == 0) wsum[wave] = run;
     __syncthreads();
     int wpre = 0, ctot = 0;
     for (int i = 0; i < 16; ++i) {
       if (i < wave) wpre += wsum[i];
       ctot += wsum[i];
     }
-    int run = carry_s + wpre + ex;
+    const int c = carry_s + wpre;
 #pragma unroll
     for (int i = 0; i < IPT; ++i) {
-      const int idx = base + tid * IPT + i;
-      if (idx < n) out[idx] = run;
-      run += v[i];
+      const int idx = wb + i * 64 + lane;
+      if (idx < n) out[idx] = c + ex[i];
     }
     __syncthreads();
     if (tid == 0) carry_s += ctot;
