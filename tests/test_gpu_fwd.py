@@ -169,12 +169,14 @@ def test_fwd_integer_grid_exact(T, d, f, W, S, dt):
     assert got["ovf_n"] > 0
 
 
-@pytest.mark.parametrize("T,d,f,W,dt", [(100, 256, 12288, 128, "bf16"), (90, 128, 6144, 64, "f32")])
+@pytest.mark.parametrize("T,d,f,W,dt", [(100, 256, 12288, 128, "bf16"), (90, 128, 6144, 64, "f32"),
+                                         (80, 128, 4160, 64, "bf16"), (50, 128, 16384, 128, "bf16")])
 def test_fwd_long_lists_two_chunks(T, d, f, W, dt):
-    """Rows of 65 to 128 tiles (96 here) are listed in one pass over both 64-tile chunks; at
-    5% density with S = 16 a row keeps 200 to 760 entries, up to three rounds of 256 that
-    cross the chunk boundary, and no row overflows, so the lists (not the backup rows) carry
-    y. Exact on the integer grid."""
+    """Rows of 65 to 128 tiles are listed in one pass over both 64-tile chunks (96 tiles; 65:
+    the second chunk is one tile; 128: both chunks full). At 5% density with S = 16 a row
+    keeps 130 to 1060 entries, up to five rounds of 256 that cross the chunk boundary, and
+    most rows do not overflow, so the lists (not the backup rows) carry y. Exact on the
+    integer grid."""
     say("fwd long lists", T, d, f, W, dt)
     g = synth.integer_grid(T, d, f, seed=7 * T + 5, dtype=dt, active=0.05)
     got, flips, err = check_forward(g, W, 16, T, ambiguity=False)
