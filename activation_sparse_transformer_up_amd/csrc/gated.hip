@@ -120,7 +120,8 @@ __global__ __launch_bounds__(256) void k_gate_dot(TwellIn h, const XT *__restric
   gate_dot_wg<XT, NP, ENT>(h, x, wu, d, P, blockIdx.x);
 }
 
-// Backup rows: wave (r0, blk) takes the 64-column block blk of the overflow rows r0,
+// Backup rows (gate_backup_wave, in the launch of k_gate_dot_all below 512 tokens and of
+// k_gate_sum_all from 512): wave (r0, blk) takes the 64-column block blk of the overflow rows r0,
 // r0 + rstep, ... below min(ovf_n, cap); the block's nonzero gates are taken ENT at a time
 // in ascending column order. The grid covers rstep = min(cap, kGateBackupRows) rows, not the
 // whole capacity: the overflow count is only known on the device, and it is usually zero, so
@@ -159,11 +160,6 @@ TW_DEV void gate_backup_wave(const TwellIn &h, const XT *__restrict__ x, const X
   }
 }
 
-template <typename XT, typename VT>
-__global__ __launch_bounds__(256) void k_gate_dot_backup(TwellIn h, const XT *__restrict__ x,
-                                                         const XT *__restrict__ wu, int d, int rstep) {
-  gate_backup_wave<XT, VT, 8, kGateEnt>(h, x, wu, d, rstep, blockIdx.x * 4 + (threadIdx.x >> 6));
-}
 
 // k_gate_dot and the backup rows in one launch: workgroups 0 .. nA - 1 run k_gate_dot, the
 // others the backup rows at k_gate_dot's shape (NP pieces per lane, ENT entries per round; the
@@ -178,7 +174,7 @@ __global__ __launch_bounds__(256) void k_gate_dot_all(TwellIn h, const XT *__res
 }
 
 // part[c][t][e] = x[t][chunk c] . wu[col][chunk c] for the entries e of token t's row list
-// (normal rows; a backup row has row_nnz < 0 and is done by k_gate_dot_backup). Block b runs on
+// (normal rows; a backup row has row_nnz < 0 and is done in k_gate_sum_all). Block b runs on
 // XCD b % 8 with chunk b % 8 + 8 * ((b / 8) / ntb) and token block (b / 8) % ntb of 16
 // tokens, one per 16-lane group; lane l holds 16 bytes of x[t]. Per round the group loads its
 // next 16 pairs (coalesced), broadcasts the columns, issues the 16 up-row loads, and sums the
@@ -245,8 +241,8 @@ __global__ __launch_bounds__(256) void k_gate_part(TwellIn h, int d, int nchunk,
 // Row list entry e of token t: g <- g * (sum over chunks c of part[c][t][e], in chunk order).
 // One wave per token, lanes over the entries; each lane has the loads of 16 chunks in flight
 // (clamped to valid addresses) before it adds them in order.
-__global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const float *__restrict__ part) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+TW_DEV void gate_sum_wg(const TwellIn &h, int nchunk, const float *__restrict__ part, int b) {
+  const int t = b * 4 + (threadIdx.x >> 6);
   if (t >= h.rows) return;
   const int n = list_len(h, h.row_nnz[t]);
   const size_t cap = (size_t)h.n_t * h.S, plane = (size_t)h.rows * cap;
@@ -265,6 +261,23 @@ __global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const f
     const uint2 q = lp[e];
     lp[e].y = __float_as_uint(__uint_as_float(q.y) * u);
   }
+}
+
+__global__ __launch_bounds__(256) void k_gate_sum(TwellIn h, int nchunk, const float *__restrict__ part) {
+  gate_sum_wg(h, nchunk, part, blockIdx.x);
+}
+
+// k_gate_sum and the backup rows' products in one launch (many tokens): workgroups
+// 0 .. nA - 1 add the partials, the others run the backup rows at k_gate_dot's shape (NP pieces
+// per lane, ENT entries per round; the per-entry sums do not depend on either). The two touch
+// disjoint data: list entries of normal rows, and the dense backup rows.
+template <typename XT, int NP, int ENT, typename VT>
+__global__ __launch_bounds__(256) void k_gate_sum_all(TwellIn h, int nchunk, const float *__restrict__ part,
+                                                      const XT *__restrict__ x, const XT *__restrict__ wu, int d,
+                                                      int nA, int rstep) {
+  const int b = blockIdx.x;
+  if (b < nA) gate_sum_wg(h, nchunk, part, b);
+  else gate_backup_wave<XT, VT, NP, ENT>(h, x, wu, d, rstep, (b - nA) * 4 + (threadIdx.x >> 6));
 }
 
 // ------------------------------------------------------------ fused inference kernel
@@ -583,22 +596,48 @@ hipError_t launch_gate_up(const TwellIn &h, const void *x, const void *wu, int b
     const int rstep = min(h.cap, kGateBackupRows);
     const size_t nb = (size_t)rstep * ((h.cols + 63) / 64);
     const dim3 gridb((unsigned)((nb + 3) / 4));
+    // the partial sums, then their sum with the backup rows' products in the same launch
+    const int nA = (int)rows4.x;
+    const dim3 gall((unsigned)(nA + gridb.x));
     if (bf16) {
       const uint16_t *xx = (const uint16_t *)x, *ww = (const uint16_t *)wu;
       hipLaunchKernelGGL((k_gate_part<uint16_t>), grid, dim3(256), 0, s, h, d, nchunk, ntb, xx, ww, ws);
-      if (nb) {
-        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
-        else hipLaunchKernelGGL((k_gate_dot_backup<uint16_t, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+      if (!nb) hipLaunchKernelGGL(k_gate_sum, rows4, dim3(256), 0, s, h, nchunk, ws);
+      else if (d <= 2048) {
+        if (h.val_bf16)
+          hipLaunchKernelGGL((k_gate_sum_all<uint16_t, 4, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, nchunk, ws,
+                             xx, ww, d, nA, rstep);
+        else
+          hipLaunchKernelGGL((k_gate_sum_all<uint16_t, 4, kGateDotEnt, float>), gall, dim3(256), 0, s, h, nchunk, ws, xx,
+                             ww, d, nA, rstep);
+      } else {
+        if (h.val_bf16)
+          hipLaunchKernelGGL((k_gate_sum_all<uint16_t, 8, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, nchunk, ws,
+                             xx, ww, d, nA, rstep);
+        else
+          hipLaunchKernelGGL((k_gate_sum_all<uint16_t, 8, kGateDotEnt, float>), gall, dim3(256), 0, s, h, nchunk, ws, xx,
+                             ww, d, nA, rstep);
       }
     } else {
       const float *xx = (const float *)x, *ww = (const float *)wu;
       hipLaunchKernelGGL((k_gate_part<float>), grid, dim3(256), 0, s, h, d, nchunk, ntb, xx, ww, ws);
-      if (nb) {
-        if (h.val_bf16) hipLaunchKernelGGL((k_gate_dot_backup<float, uint16_t>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
-        else hipLaunchKernelGGL((k_gate_dot_backup<float, float>), gridb, dim3(256), 0, s, h, xx, ww, d, rstep);
+      if (!nb) hipLaunchKernelGGL(k_gate_sum, rows4, dim3(256), 0, s, h, nchunk, ws);
+      else if (d <= 1024) {
+        if (h.val_bf16)
+          hipLaunchKernelGGL((k_gate_sum_all<float, 4, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, nchunk, ws, xx,
+                             ww, d, nA, rstep);
+        else
+          hipLaunchKernelGGL((k_gate_sum_all<float, 4, kGateDotEnt, float>), gall, dim3(256), 0, s, h, nchunk, ws, xx, ww,
+                             d, nA, rstep);
+      } else {
+        if (h.val_bf16)
+          hipLaunchKernelGGL((k_gate_sum_all<float, 8, kGateDotEnt, uint16_t>), gall, dim3(256), 0, s, h, nchunk, ws, xx,
+                             ww, d, nA, rstep);
+        else
+          hipLaunchKernelGGL((k_gate_sum_all<float, 8, kGateDotEnt, float>), gall, dim3(256), 0, s, h, nchunk, ws, xx, ww,
+                             d, nA, rstep);
       }
     }
-    hipLaunchKernelGGL(k_gate_sum, rows4, dim3(256), 0, s, h, nchunk, ws);
     return hipGetLastError();
   }
   // enough workgroups to keep every CU busy at few tokens, without more entry groups per
