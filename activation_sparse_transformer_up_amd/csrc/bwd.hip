@@ -39,7 +39,7 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 // A dense backup row is walked by one wave, 64 columns per step; the loads of kDenseBatch
 // steps are issued before any is used (addresses clamped into the row; columns past the
 // row read as zero), so the walk waits for memory once per batch rather than once per step.
-constexpr int kDenseBatch = 8;
+constexpr int kDenseBatch = 32;
 
 template <typename VT>
 TW_DEV void dense_batch(const VT *row, int cols, int j0, float (&v)[kDenseBatch]) {
