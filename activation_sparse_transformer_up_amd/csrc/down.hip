@@ -156,33 +156,35 @@ TW_DEV void wave_sync_lds() {
   __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
-// Backup row r of the overflow list, one chunk, by one wave: the dense row's nonzeros are
-// compacted 64 columns at a time into this wave's LDS batch; the four groups take every
-// fourth entry; the group sums are added and written by group 0.
-template <typename WT, typename VT, typename YT>
+// Backup row r of the overflow list, one chunk, by one wave: the dense row is read kBkSteps
+// steps of 64 columns at a time (every load before any use; addresses clamped into the row),
+// its nonzeros are appended to this wave's LDS list (CAP entries) in column order, and the list
+// is gathered whenever it might not take another full step, and at the end: the four groups
+// take every fourth entry, 16 entries per round. The group sums are added and written by
+// group 0. A row is then a few round trips per kBkSteps steps and per 16 entries, instead of
+// one per step for the row and one per step with a nonzero for W2.
+constexpr int kBkSteps = 8, kBkList = 192;            // list entries per wave
+
+template <typename WT, typename VT, typename YT, int CAP>
 TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *__restrict__ y, int r, int c,
                        uint2 *lst) {
+  static_assert(CAP >= 128, "a flush must leave room for a full step");
   constexpr int E = Vec16<WT>::N;
   constexpr int CW = 16 * E;
   const int lane = lane_id(), g = lane >> 4, gl = lane & 15;
   const int col = c * CW + gl * E;
   const bool cv = col < d;
   const int t = h.ovf_rows[r];
-  const VT *row = (const VT *)h.ovf_dense + (size_t)r * h.cols;
-  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<WT>(h.cols, d));
+  const int cols = h.cols;
+  const VT *row = (const VT *)h.ovf_dense + (size_t)r * cols;
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(w2, rows_bytes<WT>(cols, d));
   float acc[E];
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
-  for (int c0 = 0; c0 < h.cols; c0 += 64) {
-    const int j = c0 + lane;
-    const float v = j < h.cols ? ldv(row, j) : 0.f;
-    const bool nz = v != 0.f;
-    const uint64_t m = ballot64(nz);
-    if (m == 0) continue;
-    if (nz) lst[mbcnt64(m)] = make_uint2((uint32_t)j, __float_as_uint(v));
+  int cnt = 0;                                                 // pending list entries (uniform)
+  auto flush = [&]() {
     wave_sync_lds();
-    const int n = __popcll(m);
-    for (int e0 = 0; e0 < n; e0 += 16) {
+    for (int e0 = 0; e0 < cnt; e0 += 16) {
       uint4 raw[4];
       float vv[4];
 #pragma unroll
@@ -190,7 +192,7 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
         const int e = e0 + g + 4 * k;
         vv[k] = 0.f;
         raw[k] = make_uint4(0, 0, 0, 0);
-        if (e < n) {
+        if (e < cnt) {
           const uint2 p = lst[e];
           vv[k] = __uint_as_float(p.y);
           if (cv) raw[k] = ld16<WT>(rs, p.x * (uint32_t)d + (uint32_t)col);
@@ -200,7 +202,27 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
       for (int k = 0; k < 4; ++k) fma16<WT, E>(acc, vv[k], raw[k]);
     }
     wave_sync_lds();
+    cnt = 0;
+  };
+  for (int c0 = 0; c0 < cols; c0 += 64 * kBkSteps) {
+    float v[kBkSteps];
+#pragma unroll
+    for (int u = 0; u < kBkSteps; ++u) {
+      const int j = c0 + u * 64 + lane;
+      const float x = ldv(row, j < cols ? j : cols - 1);
+      v[u] = j < cols ? x : 0.f;
+    }
+#pragma unroll
+    for (int u = 0; u < kBkSteps; ++u) {
+      const bool nz = v[u] != 0.f;
+      const uint64_t m = ballot64(nz);
+      if (m == 0) continue;                                    // uniform
+      if (cnt > CAP - 64) flush();                             // uniform
+      if (nz) lst[cnt + (int)mbcnt64(m)] = make_uint2((uint32_t)(c0 + u * 64 + lane), __float_as_uint(v[u]));
+      cnt += (int)__popcll(m);
+    }
   }
+  if (cnt > 0) flush();
 #pragma unroll
   for (int q = 0; q < E; ++q) {
     acc[q] += __shfl_xor(acc[q], 16, 64);
@@ -219,7 +241,7 @@ TW_DEV void backup_row(const TwellIn &h, const WT *__restrict__ w2, int d, YT *_
 template <typename WT, typename VT, typename YT>
 __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restrict__ w2, int d,
                                                     YT *__restrict__ y, int nchunk, int ntb, int nmain) {
-  __shared__ uint2 lst[4][64];
+  __shared__ uint2 lst[4][kBkList];
   constexpr int E = Vec16<WT>::N;
   constexpr int CW = 16 * E;
   const int b = blockIdx.x;
@@ -228,7 +250,7 @@ __global__ __launch_bounds__(256) void k_down_rows4(TwellIn h, const WT *__restr
     const int i = b - nmain;
     const int c = i % nchunk, r = (i / nchunk) * 4 + wave;
     if (r >= min(*h.ovf_n, h.cap)) return;               // wave-uniform
-    backup_row<WT, VT, YT>(h, w2, d, y, r, c, lst[wave]);
+    backup_row<WT, VT, YT, kBkList>(h, w2, d, y, r, c, lst[wave]);
     return;
   }
   const int xcd = b & 7, i = b >> 3;
@@ -284,7 +306,7 @@ __global__ __launch_bounds__(256) void k_down_split(TwellIn h, const WT *__restr
 #pragma unroll
   for (int e = 0; e < E; ++e) acc[e] = 0.f;
   if (slot >= 0) {                                          // backup row: one wave does it
-    if (wave == 0) backup_row<WT, VT, YT>(h, w2, d, y, slot, c, lst);
+    if (wave == 0) backup_row<WT, VT, YT, LW>(h, w2, d, y, slot, c, lst);
     return;
   }
   __syncthreads();
@@ -347,7 +369,7 @@ __global__ __launch_bounds__(64 * NW) void k_down_wide(TwellIn h, const WT *__re
   constexpr int CW = 64 * E;
   constexpr int RW = NW * PE;                               // entries per round
   static_assert(NW >= 4 && PE <= 64, "shape");
-  __shared__ uint2 lst[4][64];
+  __shared__ uint2 lst[4][kBkList];
   __shared__ float red[NW - 1][64 * E];
   const int T = h.rows;
   const int b = blockIdx.x, xcd = b & 7, i = b >> 3;
@@ -362,7 +384,7 @@ __global__ __launch_bounds__(64 * NW) void k_down_wide(TwellIn h, const WT *__re
   if (slot >= 0) {
     if (wave < 4) {
       const int cn = 4 * c + wave;                          // this wave's 16-lane chunk
-      if (cn * 16 * E < d) backup_row<WT, VT, YT>(h, w2, d, y, slot, cn, lst[wave]);
+      if (cn * 16 * E < d) backup_row<WT, VT, YT, kBkList>(h, w2, d, y, slot, cn, lst[wave]);
     }
     return;
   }
